@@ -1,0 +1,130 @@
+/*
+ * attn_bwd.h -- C ABI of the MI355X (gfx950) scaled dot-product attention
+ * backward library (libattn_bwd.so).
+ *
+ * The operation (dense):
+ *   S  = scale * Q K^T (+ bias), masked;  P = row softmax(S);
+ *   dV = P^T dY;  dP = dY V^T;  dS = P * (dP - rowsum(P * dP)) * scale;
+ *   dQ = dS K;    dK = dS^T Q.
+ * as defined by docs.rs rlx-cpu 0.2.17, src/attention_bwd.rs
+ * (`backward_dense_head_all`, `attention_backward_all`, `apply_synthetic_mask`),
+ * with the strided layout and the numeric mask / wrt codes of docs.rs rlx-wgpu
+ * 0.2.1, src/kernels/attention_bwd.wgsl (`Params`, `mask_score`).
+ *
+ * The operation (paged): dK / dV of a grouped-query attention whose keys and
+ * values live in a page-permuted pool, given the per-row statistics
+ * (max, denominator, rowsum(P * dP)), as defined by docs.rs ruDNN 0.1.43,
+ * src/paged_attention/ordered_kernel.rs (`history_backward`).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named "device" are GPU memory the caller allocated; "host"
+ *     pointers are CPU memory.  The library never allocates, frees or keeps
+ *     any of them, and holds no state between calls.
+ *   - `stream` is a hipStream_t passed as void*.  Work is enqueued on it and the
+ *     call returns without synchronising: inputs must stay alive, and outputs
+ *     must not be read, until the stream has passed this point.
+ *   - Return value: ATTN_OK (0) or a negative status.  On a negative status
+ *     nothing was enqueued and attn_bwd_last_error() describes the problem.
+ *   - Outputs are fully determined by the inputs: no atomics, fixed reduction
+ *     orders, bit-identical from run to run.
+ *   - Calls on different streams may overlap; calls that share an output or a
+ *     workspace must be ordered by the caller.
+ */
+#ifndef ATTN_BWD_H
+#define ATTN_BWD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of Q, K, V, dY and of every gradient output. */
+enum { ATTN_F32 = 0, ATTN_BF16 = 1 };
+
+/* Which gradients to produce.  0..2 are the `wrt` codes of rlx-wgpu
+ * attention_bwd.wgsl (0 = dQ, 1 = dK, 2 = dV); 3 asks for all three from one
+ * score recompute, as rlx-cpu `attention_backward_all`. */
+enum { ATTN_WRT_Q = 0, ATTN_WRT_K = 1, ATTN_WRT_V = 2, ATTN_WRT_ALL = 3 };
+
+/* Mask kinds: the MaskKind codes of rlx-wgpu `mask_score`.
+ *   NONE   every key visible.
+ *   CAUSAL query i (absolute position a = max(Sk - Sq, 0) + i) sees keys j <= a
+ *          (rlx-cpu `apply_synthetic_mask`).
+ *   KEYPAD key j hidden when mask[b,h,i,j] < mask_threshold ("Custom").
+ *   WINDOW sees keys max(a - window, 0) <= j <= a ("SlidingWindow(w)").
+ *   BIAS   mask[b,h,i,j] is added to the scaled score ("Bias").
+ * Hidden keys are excluded from the softmax; a row with no visible key has
+ * P = 0, contributes nothing, and its dQ row is 0. */
+enum {
+  ATTN_MASK_NONE = 0,
+  ATTN_MASK_CAUSAL = 1,
+  ATTN_MASK_KEYPAD = 2,
+  ATTN_MASK_WINDOW = 3,
+  ATTN_MASK_BIAS = 4
+};
+/* mask_flags bit: also apply the causal rule, after KEYPAD or BIAS. */
+#define ATTN_MASK_FLAG_CAUSAL 0x1
+
+enum {
+  ATTN_OK = 0,
+  ATTN_E_INVALID = -1,     /* bad enum, size, pointer, stride, aliasing or plan */
+  ATTN_E_UNSUPPORTED = -2, /* head_dim not in {32, 64, 128}, d not contiguous, rows not 16-byte aligned */
+  ATTN_E_WORKSPACE = -3,   /* workspace missing or smaller than attn_bwd_workspace_bytes() */
+  ATTN_E_HIP = -4          /* the HIP runtime refused a launch */
+};
+
+/* Dense arguments.  Tensors are [B, S, H, D] in element strides (b, s, h) with
+ * d contiguous (stride 1); [B, H, S, D] is the same with other strides
+ * (rlx-wgpu `Params` carries per-tensor batch / head / seq strides). */
+typedef struct attn_bwd_args {
+  int32_t dtype;           /* ATTN_F32 or ATTN_BF16, for all seven tensors */
+  int32_t wrt;             /* ATTN_WRT_* */
+  int64_t B, H, Sq, Sk, D; /* D in {32, 64, 128}; Sq, Sk < 2^30 */
+  const void *q, *k, *v, *dy; /* device, read only. q, dy: [B,Sq,H,D]; k, v: [B,Sk,H,D] */
+  void *dq, *dk, *dv;         /* device outputs; required iff `wrt` asks for them, else ignored */
+  int64_t q_stride[3], k_stride[3], v_stride[3], dy_stride[3]; /* (b, s, h) element strides, >= 0 */
+  int64_t dq_stride[3], dk_stride[3], dv_stride[3];
+  int32_t mask_kind;       /* ATTN_MASK_* */
+  int32_t mask_flags;      /* 0 or ATTN_MASK_FLAG_CAUSAL (KEYPAD / BIAS only) */
+  int64_t window;          /* WINDOW only, >= 0: keeps window + 1 keys */
+  const float *mask;       /* device fp32, KEYPAD validity or BIAS values; else ignored */
+  int64_t mask_stride[4];  /* (b, h, i, j) element strides, 0 = broadcast ([B,Sk] padding: {Sk,0,0,1}) */
+  float mask_threshold;    /* KEYPAD: key hidden iff value < threshold */
+  float scale;             /* finite; callers usually pass (float)(1/sqrt(D)) */
+  void *workspace;         /* device, >= attn_bwd_workspace_bytes(B, H, Sq) bytes, 256-byte aligned */
+  size_t workspace_bytes;
+} attn_bwd_args;
+
+/* Bytes of device workspace attn_bwd needs: four fp32 planes of B*H*Sq row
+ * statistics, each padded to 256 bytes.  Plane 0 = row max m of the scaled
+ * scores, plane 1 = denominator l = sum exp(s - m), plane 2 = delta =
+ * rowsum(P * dP), plane 3 = internal (log2-domain log-sum-exp).  Row (b, h, i)
+ * sits at index (b * H + h) * Sq + i.  An empty row holds m = -inf, l = 0,
+ * delta = 0.  Returns 0 for negative sizes. */
+size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq);
+
+/* The whole dense backward: row statistics, then dK / dV, then dQ, as `wrt`
+ * asks.  Every element of every requested output is written (no pre-zeroing
+ * needed, as rlx-cpu `attention_backward_all`); no output may overlap any
+ * input, another output or the workspace.  B, H, Sq or Sk = 0 is valid: the
+ * requested outputs that have elements are then written with zeros. */
+int attn_bwd(const attn_bwd_args *a, void *stream);
+
+/* The three stages of attn_bwd, for callers that time or schedule them one by
+ * one.  They take the same arguments and validation.  Run them in this order
+ * on one stream: row_stats fills the workspace statistics; kv writes dK / dV
+ * (those `wrt` asks for) from them; dq writes dQ (if asked) from them. */
+int attn_bwd_row_stats(const attn_bwd_args *a, void *stream);
+int attn_bwd_kv(const attn_bwd_args *a, void *stream);
+int attn_bwd_dq(const attn_bwd_args *a, void *stream);
+
+/* Thread-local description of the last non-OK status returned on this thread. */
+const char *attn_bwd_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_BWD_H */

@@ -1,0 +1,144 @@
+"""MI355X (gfx950) scaled dot-product attention backward.
+
+A thin ctypes binding over ``libattn_bwd.so`` (C ABI in ``include/attn_bwd.h``).
+This module only marshals arguments: torch supplies device memory and the
+current stream, and every step of the computation runs in the HIP kernels.
+There is no CPU fallback: without the built library every call raises.
+
+    dq, dk, dv = attn_bwd(q, k, v, dy, mask_kind="causal")
+
+Tensors are ``[B, S, H, D]`` (any strides with ``D`` contiguous; pass
+``x.transpose(1, 2)`` for a ``[B, H, S, D]`` tensor), float32 or bfloat16, on the
+GPU.  The semantics are those of rlx-cpu 0.2.17 src/attention_bwd.rs
+(`attention_backward_all`) with the mask codes of rlx-wgpu 0.2.1
+attention_bwd.wgsl (`mask_score`).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+from ._abi import (ATTN_BF16, ATTN_F32, ATTN_MASK_BIAS, ATTN_MASK_CAUSAL,
+                   ATTN_MASK_FLAG_CAUSAL, ATTN_MASK_KEYPAD, ATTN_MASK_NONE, ATTN_MASK_WINDOW,
+                   ATTN_WRT_ALL, ATTN_WRT_K, ATTN_WRT_Q, ATTN_WRT_V, AttnBwdArgs, AttnError,
+                   load_library, library_path)
+
+__all__ = ["attn_bwd", "attn_bwd_stage", "workspace_bytes", "make_args", "AttnError",
+           "load_library", "library_path", "MASKS", "WRT"]
+
+MASKS = {"none": ATTN_MASK_NONE, "causal": ATTN_MASK_CAUSAL, "keypad": ATTN_MASK_KEYPAD,
+         "window": ATTN_MASK_WINDOW, "bias": ATTN_MASK_BIAS}
+WRT = {"q": ATTN_WRT_Q, "k": ATTN_WRT_K, "v": ATTN_WRT_V, "all": ATTN_WRT_ALL}
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def workspace_bytes(B: int, H: int, Sq: int) -> int:
+    return int(load_library().attn_bwd_workspace_bytes(B, H, Sq))
+
+
+def _strides3(t):
+    s = t.stride()
+    return (s[0], s[1], s[2])
+
+
+def make_args(q, k, v, dy, dq=None, dk=None, dv=None, *, wrt="all", mask_kind="none",
+              causal=False, window=0, mask=None, threshold=0.5, scale=None, workspace=None):
+    """Builds the attn_bwd_args struct for already-allocated tensors (no checks:
+    the library validates)."""
+    torch = _torch()
+    B, Sq, H, D = q.shape
+    Sk = k.shape[1]
+    a = AttnBwdArgs()
+    a.dtype = ATTN_BF16 if q.dtype == torch.bfloat16 else ATTN_F32
+    a.wrt = WRT[wrt] if isinstance(wrt, str) else int(wrt)
+    a.B, a.H, a.Sq, a.Sk, a.D = B, H, Sq, Sk, D
+    a.q, a.k, a.v, a.dy = q.data_ptr(), k.data_ptr(), v.data_ptr(), dy.data_ptr()
+    a.q_stride[:], a.k_stride[:] = _strides3(q), _strides3(k)
+    a.v_stride[:], a.dy_stride[:] = _strides3(v), _strides3(dy)
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is not None:
+            setattr(a, name, t.data_ptr())
+            getattr(a, name + "_stride")[:] = _strides3(t)
+    a.mask_kind = MASKS[mask_kind] if isinstance(mask_kind, str) else int(mask_kind)
+    a.mask_flags = ATTN_MASK_FLAG_CAUSAL if causal else 0
+    a.window = int(window or 0)
+    if mask is not None:
+        mv = mask.expand(B, H, Sq, Sk)
+        a.mask = mv.data_ptr()
+        a.mask_stride[:] = mv.stride()
+    a.mask_threshold = float(threshold)
+    a.scale = float(scale) if scale is not None else float(
+        torch.tensor(1.0 / math.sqrt(D), dtype=torch.float32))
+    if workspace is not None:
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+    return a
+
+
+def _check(rc):
+    if rc != 0:
+        msg = load_library().attn_bwd_last_error().decode(errors="replace")
+        raise AttnError(rc, msg)
+
+
+def _stream_handle(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def attn_bwd_stage(stage: str, args: AttnBwdArgs, stream=None):
+    """Runs one stage ("all", "row_stats", "kv" or "dq") of the backward on the
+    given (default: current) torch stream."""
+    lib = load_library()
+    fn = {"all": lib.attn_bwd, "row_stats": lib.attn_bwd_row_stats, "kv": lib.attn_bwd_kv,
+          "dq": lib.attn_bwd_dq}[stage]
+    _check(fn(ctypes.byref(args), _stream_handle(stream)))
+
+
+def attn_bwd(q, k, v, dy, *, wrt="all", mask_kind="none", causal=False, window=0, mask=None,
+             threshold=0.5, scale=None, out=None, workspace=None, stream=None,
+             return_workspace=False):
+    """Gradients of scaled dot-product attention.
+
+    mask_kind: "none", "causal", "keypad" (mask = key validity, hidden iff
+    < threshold), "window" (keeps [a - window, a] for query position a) or
+    "bias" (mask added to the scaled scores); ``causal=True`` adds the causal
+    rule to "keypad" / "bias".  ``mask`` is float32 and broadcasts to
+    [B, H, Sq, Sk] ([B, 1, 1, Sk] for per-batch padding).
+    Returns (dq, dk, dv); entries that ``wrt`` does not ask for are None.
+    """
+    torch = _torch()
+    B, Sq, H, D = q.shape
+    w = WRT[wrt] if isinstance(wrt, str) else int(wrt)
+    if out is None:
+        dq = torch.empty_like(q, memory_format=torch.contiguous_format) if w in (ATTN_WRT_Q, ATTN_WRT_ALL) else None
+        dk = torch.empty_like(k, memory_format=torch.contiguous_format) if w in (ATTN_WRT_K, ATTN_WRT_ALL) else None
+        dv = torch.empty_like(v, memory_format=torch.contiguous_format) if w in (ATTN_WRT_V, ATTN_WRT_ALL) else None
+    else:
+        dq, dk, dv = out
+    if workspace is None:
+        nbytes = workspace_bytes(B, H, Sq)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    args = make_args(q, k, v, dy, dq, dk, dv, wrt=w, mask_kind=mask_kind, causal=causal,
+                     window=window, mask=mask, threshold=threshold, scale=scale,
+                     workspace=workspace)
+    attn_bwd_stage("all", args, stream)
+    if return_workspace:
+        return (dq, dk, dv), workspace
+    return dq, dk, dv
+
+
+def row_stats_views(workspace, B, H, Sq):
+    """(m, l, delta) as float32 views [B, H, Sq] of a workspace filled by attn_bwd."""
+    plane = ((B * H * Sq * 4 + 255) // 256) * 256
+    f = workspace.view(_torch().uint8)
+    out = []
+    for i in range(3):
+        out.append(f[i * plane: i * plane + B * H * Sq * 4].view(_torch().float32).view(B, H, Sq))
+    return tuple(out)

@@ -1,0 +1,81 @@
+"""ctypes mirror of include/attn_bwd.h and the library loader.
+
+The loader never builds: if libattn_bwd.so is missing, every entry point raises
+(no CPU fallback exists).  Build it with ``python -m scaled_dot_product_bwd_amd.build``
+or ``__graft_entry__.build()``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+ATTN_F32, ATTN_BF16 = 0, 1
+ATTN_WRT_Q, ATTN_WRT_K, ATTN_WRT_V, ATTN_WRT_ALL = 0, 1, 2, 3
+ATTN_MASK_NONE, ATTN_MASK_CAUSAL, ATTN_MASK_KEYPAD, ATTN_MASK_WINDOW, ATTN_MASK_BIAS = 0, 1, 2, 3, 4
+ATTN_MASK_FLAG_CAUSAL = 0x1
+ATTN_OK, ATTN_E_INVALID, ATTN_E_UNSUPPORTED, ATTN_E_WORKSPACE, ATTN_E_HIP = 0, -1, -2, -3, -4
+
+STATUS_NAMES = {ATTN_E_INVALID: "ATTN_E_INVALID", ATTN_E_UNSUPPORTED: "ATTN_E_UNSUPPORTED",
+                ATTN_E_WORKSPACE: "ATTN_E_WORKSPACE", ATTN_E_HIP: "ATTN_E_HIP"}
+
+# Every symbol include/attn_bwd.h declares.
+EXPORTED = ["attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_row_stats", "attn_bwd_kv",
+            "attn_bwd_dq", "attn_bwd_last_error"]
+
+
+class AttnError(RuntimeError):
+    def __init__(self, code, message):
+        super().__init__(f"{STATUS_NAMES.get(code, code)}: {message}")
+        self.code = code
+
+
+_i64x3 = ctypes.c_int64 * 3
+_i64x4 = ctypes.c_int64 * 4
+
+
+class AttnBwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("wrt", ctypes.c_int32),
+        ("B", ctypes.c_int64), ("H", ctypes.c_int64), ("Sq", ctypes.c_int64),
+        ("Sk", ctypes.c_int64), ("D", ctypes.c_int64),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("dy", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+        ("q_stride", _i64x3), ("k_stride", _i64x3), ("v_stride", _i64x3), ("dy_stride", _i64x3),
+        ("dq_stride", _i64x3), ("dk_stride", _i64x3), ("dv_stride", _i64x3),
+        ("mask_kind", ctypes.c_int32), ("mask_flags", ctypes.c_int32),
+        ("window", ctypes.c_int64),
+        ("mask", ctypes.c_void_p), ("mask_stride", _i64x4),
+        ("mask_threshold", ctypes.c_float), ("scale", ctypes.c_float),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return os.path.join(HERE, "libattn_bwd.so")
+
+
+def load_library():
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m scaled_dot_product_bwd_amd.build` "
+                           "(the HIP library is required, there is no fallback)")
+    lib = ctypes.CDLL(path)
+    lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_bwd_workspace_bytes.argtypes = [ctypes.c_int64] * 3
+    for name in ("attn_bwd", "attn_bwd_row_stats", "attn_bwd_kv", "attn_bwd_dq"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.POINTER(AttnBwdArgs), ctypes.c_void_p]
+    lib.attn_bwd_last_error.restype = ctypes.c_char_p
+    lib.attn_bwd_last_error.argtypes = []
+    _lib = lib
+    return lib

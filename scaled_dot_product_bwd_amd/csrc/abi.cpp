@@ -1,0 +1,281 @@
+// abi.cpp -- the C ABI of libattn_bwd.so (declared in include/attn_bwd.h):
+// argument validation, workspace sizing and kernel dispatch for the dense path.
+//
+// Every check happens on the host before anything is enqueued, so a rejected
+// call leaves the stream untouched.  The pages' own interfaces have no error
+// path (rlx-cpu panics on a bad slice, rlx-metal `use_gpu` falls back to the
+// CPU, rlx-wgpu `attention_bwd` silently returns for head_dim > 128); here
+// every unsupported or inconsistent request is an explicit status.
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "attn_bwd.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t plane_bytes(int64_t B, int64_t H, int64_t Sq) {
+  return align256((size_t)B * (size_t)H * (size_t)Sq * sizeof(float));
+}
+
+// Byte range [lo, hi) covered by a [n0, n1, n2, n3] tensor with element strides
+// st[0..3] (last one for the innermost axis); empty if any extent is 0.
+struct Range {
+  uintptr_t lo = 0, hi = 0;
+  bool empty() const { return hi <= lo; }
+};
+
+Range extent(const void *p, const int64_t n[4], const int64_t st[4], size_t esize) {
+  Range r;
+  if (!p) return r;
+  int64_t last = 0;
+  for (int i = 0; i < 4; ++i) {
+    if (n[i] <= 0) return r;
+    last += (n[i] - 1) * st[i];
+  }
+  r.lo = (uintptr_t)p;
+  r.hi = r.lo + (uintptr_t)((last + 1) * (int64_t)esize);
+  return r;
+}
+
+bool overlap(const Range &a, const Range &b) {
+  return !a.empty() && !b.empty() && a.lo < b.hi && b.lo < a.hi;
+}
+
+struct Checked {
+  attn::DenseParams p;
+  bool bf16;
+  int D;
+  int mode;
+  bool want_q, want_k, want_v;
+  int nblk_q, nblk_k;
+};
+
+int validate(const attn_bwd_args *a, Checked &c) {
+  if (!a) return fail(ATTN_E_INVALID, "args is NULL");
+  if (a->dtype != ATTN_F32 && a->dtype != ATTN_BF16)
+    return fail(ATTN_E_INVALID, "dtype %d is not ATTN_F32 or ATTN_BF16", a->dtype);
+  if (a->wrt < ATTN_WRT_Q || a->wrt > ATTN_WRT_ALL)
+    return fail(ATTN_E_INVALID, "wrt %d is not one of ATTN_WRT_*", a->wrt);
+  if (a->mask_kind < ATTN_MASK_NONE || a->mask_kind > ATTN_MASK_BIAS)
+    return fail(ATTN_E_INVALID, "mask_kind %d is not one of ATTN_MASK_*", a->mask_kind);
+  if (a->mask_flags & ~ATTN_MASK_FLAG_CAUSAL)
+    return fail(ATTN_E_INVALID, "unknown mask_flags bits 0x%x", a->mask_flags);
+  if (a->mask_flags && a->mask_kind != ATTN_MASK_KEYPAD && a->mask_kind != ATTN_MASK_BIAS)
+    return fail(ATTN_E_INVALID, "mask_flags only combine with ATTN_MASK_KEYPAD or ATTN_MASK_BIAS");
+  if (a->B < 0 || a->H < 0 || a->Sq < 0 || a->Sk < 0)
+    return fail(ATTN_E_INVALID, "negative size (B=%lld H=%lld Sq=%lld Sk=%lld)", (long long)a->B,
+                (long long)a->H, (long long)a->Sq, (long long)a->Sk);
+  if (a->Sq >= (1 << 30) || a->Sk >= (1 << 30))
+    return fail(ATTN_E_INVALID, "sequence length must be below 2^30");
+  if (a->D != 32 && a->D != 64 && a->D != 128)
+    return fail(ATTN_E_UNSUPPORTED, "head_dim %lld is not 32, 64 or 128", (long long)a->D);
+  if (!std::isfinite(a->scale)) return fail(ATTN_E_INVALID, "scale is not finite");
+  if (a->mask_kind == ATTN_MASK_WINDOW && a->window < 0)
+    return fail(ATTN_E_INVALID, "window %lld is negative", (long long)a->window);
+  if (a->mask_kind == ATTN_MASK_KEYPAD && std::isnan(a->mask_threshold))
+    return fail(ATTN_E_INVALID, "mask_threshold is NaN");
+
+  const int64_t nblk_q = (a->Sq + 127) / 128, nblk_k = (a->Sk + 127) / 128;
+  const int64_t heads = a->B * a->H;
+  if (a->H > 0 && a->B > INT32_MAX / a->H) return fail(ATTN_E_INVALID, "B * H too large");
+  if (heads * (nblk_q > nblk_k ? nblk_q : nblk_k) > INT32_MAX)
+    return fail(ATTN_E_INVALID, "problem too large for one launch");
+
+  c.want_q = a->wrt == ATTN_WRT_Q || a->wrt == ATTN_WRT_ALL;
+  c.want_k = a->wrt == ATTN_WRT_K || a->wrt == ATTN_WRT_ALL;
+  c.want_v = a->wrt == ATTN_WRT_V || a->wrt == ATTN_WRT_ALL;
+  c.bf16 = a->dtype == ATTN_BF16;
+  c.D = (int)a->D;
+  c.nblk_q = (int)nblk_q;
+  c.nblk_k = (int)nblk_k;
+  const size_t es = c.bf16 ? 2 : 4;
+  const bool has_q = heads > 0 && a->Sq > 0, has_k = heads > 0 && a->Sk > 0;
+
+  struct T {
+    const char *name;
+    const void *ptr;
+    const int64_t *st;
+    int64_t S;
+    bool needed;
+    bool output;
+  } ts[7] = {
+      {"q", a->q, a->q_stride, a->Sq, has_q, false},
+      {"k", a->k, a->k_stride, a->Sk, has_k, false},
+      {"v", a->v, a->v_stride, a->Sk, has_k, false},
+      {"dy", a->dy, a->dy_stride, a->Sq, has_q, false},
+      {"dq", a->dq, a->dq_stride, a->Sq, has_q && c.want_q, true},
+      {"dk", a->dk, a->dk_stride, a->Sk, has_k && c.want_k, true},
+      {"dv", a->dv, a->dv_stride, a->Sk, has_k && c.want_v, true},
+  };
+  Range rng[7];
+  for (int i = 0; i < 7; ++i) {
+    if (!ts[i].needed) continue;
+    if (!ts[i].ptr) return fail(ATTN_E_INVALID, "%s is NULL", ts[i].name);
+    for (int j = 0; j < 3; ++j)
+      if (ts[i].st[j] < 0) return fail(ATTN_E_INVALID, "%s has a negative stride", ts[i].name);
+    if ((uintptr_t)ts[i].ptr % 16)
+      return fail(ATTN_E_UNSUPPORTED, "%s is not 16-byte aligned", ts[i].name);
+    for (int j = 0; j < 3; ++j)
+      if ((ts[i].st[j] * (int64_t)es) % 16)
+        return fail(ATTN_E_UNSUPPORTED, "%s stride %d is not a multiple of 16 bytes", ts[i].name, j);
+    const int64_t n[4] = {a->B, ts[i].S, a->H, a->D};
+    const int64_t st[4] = {ts[i].st[0], ts[i].st[1], ts[i].st[2], 1};
+    rng[i] = extent(ts[i].ptr, n, st, es);
+  }
+
+  const bool masked = a->mask_kind == ATTN_MASK_KEYPAD || a->mask_kind == ATTN_MASK_BIAS;
+  Range mrng;
+  if (masked && has_q && a->Sk > 0) {
+    if (!a->mask) return fail(ATTN_E_INVALID, "mask is NULL for mask_kind %d", a->mask_kind);
+    if ((uintptr_t)a->mask % 4) return fail(ATTN_E_INVALID, "mask is not 4-byte aligned");
+    for (int j = 0; j < 4; ++j)
+      if (a->mask_stride[j] < 0) return fail(ATTN_E_INVALID, "mask has a negative stride");
+    const int64_t n[4] = {a->B, a->H, a->Sq, a->Sk};
+    mrng = extent(a->mask, n, a->mask_stride, sizeof(float));
+  }
+
+  const size_t ws_need = attn_bwd_workspace_bytes(a->B, a->H, a->Sq);
+  Range wrng;
+  if (ws_need) {
+    if (!a->workspace) return fail(ATTN_E_WORKSPACE, "workspace is NULL (%zu bytes needed)", ws_need);
+    if ((uintptr_t)a->workspace % 256)
+      return fail(ATTN_E_WORKSPACE, "workspace is not 256-byte aligned");
+    if (a->workspace_bytes < ws_need)
+      return fail(ATTN_E_WORKSPACE, "workspace has %zu bytes, %zu needed", a->workspace_bytes, ws_need);
+    wrng.lo = (uintptr_t)a->workspace;
+    wrng.hi = wrng.lo + ws_need;
+  }
+
+  // No output may share memory with an input, another output or the workspace.
+  for (int i = 4; i < 7; ++i) {
+    if (!ts[i].needed) continue;
+    for (int j = 0; j < 7; ++j)
+      if (j != i && ts[j].needed && overlap(rng[i], rng[j]))
+        return fail(ATTN_E_INVALID, "%s overlaps %s", ts[i].name, ts[j].name);
+    if (overlap(rng[i], mrng)) return fail(ATTN_E_INVALID, "%s overlaps mask", ts[i].name);
+    if (overlap(rng[i], wrng)) return fail(ATTN_E_INVALID, "%s overlaps the workspace", ts[i].name);
+  }
+  if (overlap(wrng, mrng)) return fail(ATTN_E_INVALID, "workspace overlaps mask");
+  for (int j = 0; j < 4; ++j)
+    if (ts[j].needed && overlap(wrng, rng[j]))
+      return fail(ATTN_E_INVALID, "workspace overlaps %s", ts[j].name);
+
+  attn::DenseParams &p = c.p;
+  std::memset(&p, 0, sizeof p);
+  p.q = a->q; p.k = a->k; p.v = a->v; p.dy = a->dy;
+  p.dq = a->dq; p.dk = a->dk; p.dv = a->dv;
+  for (int j = 0; j < 3; ++j) {
+    p.qs[j] = a->q_stride[j]; p.ks[j] = a->k_stride[j]; p.vs[j] = a->v_stride[j];
+    p.dys[j] = a->dy_stride[j]; p.dqs[j] = a->dq_stride[j]; p.dks[j] = a->dk_stride[j];
+    p.dvs[j] = a->dv_stride[j];
+  }
+  p.mask = masked ? a->mask : nullptr;
+  for (int j = 0; j < 4; ++j) p.ms[j] = masked ? a->mask_stride[j] : 0;
+  p.thr = a->mask_threshold;
+  p.scale = a->scale;
+  p.scale_log2 = a->scale * attn::kLog2e;
+  p.B = (int)a->B; p.H = (int)a->H; p.Sq = (int)a->Sq; p.Sk = (int)a->Sk;
+  // Query i sits at absolute position max(Sk - Sq, 0) + i (rlx-cpu
+  // `apply_synthetic_mask`, saturating_sub).
+  const int64_t q_off = a->Sk > a->Sq ? a->Sk - a->Sq : 0;
+  const bool causal = a->mask_kind == ATTN_MASK_CAUSAL || a->mask_kind == ATTN_MASK_WINDOW ||
+                      (a->mask_flags & ATTN_MASK_FLAG_CAUSAL);
+  p.hi_off = causal ? (int)q_off : attn::kBig;
+  if (a->mask_kind == ATTN_MASK_WINDOW) {
+    const int64_t lo = q_off - a->window;
+    p.lo_off = lo < -(int64_t)attn::kBig ? -attn::kBig : (int)lo;
+  } else {
+    p.lo_off = -attn::kBig;
+  }
+  p.need_dk = c.want_k;
+  p.need_dv = c.want_v;
+  char *ws = (char *)a->workspace;
+  const size_t pb = plane_bytes(a->B, a->H, a->Sq);
+  p.st_m = (float *)ws;
+  p.st_l = (float *)(ws ? ws + pb : nullptr);
+  p.st_delta = (float *)(ws ? ws + 2 * pb : nullptr);
+  p.st_lse2 = (float *)(ws ? ws + 3 * pb : nullptr);
+  c.mode = a->mask_kind == ATTN_MASK_KEYPAD ? attn::MODE_KEYPAD
+           : a->mask_kind == ATTN_MASK_BIAS ? attn::MODE_BIAS
+                                            : attn::MODE_INDEX;
+  return ATTN_OK;
+}
+
+int run_stage(int stage, Checked &c, hipStream_t stream) {
+  attn::DenseParams p = c.p;
+  const int heads = p.B * p.H;
+  int nblocks = 0;
+  if (stage == attn::STAGE_ROW_STATS) {
+    if (p.Sq == 0 || !(c.want_q || c.want_k || c.want_v)) return ATTN_OK;
+    p.nblk = c.nblk_q;
+    nblocks = heads * c.nblk_q;
+  } else if (stage == attn::STAGE_KV) {
+    if (!(c.want_k || c.want_v) || p.Sk == 0) return ATTN_OK;
+    p.nblk = c.nblk_k;
+    nblocks = heads * c.nblk_k;
+  } else {
+    if (!c.want_q || p.Sq == 0) return ATTN_OK;
+    p.nblk = c.nblk_q;
+    nblocks = heads * c.nblk_q;
+  }
+  const hipError_t e = attn::launch_dense_stage(stage, c.bf16, c.D, c.mode, p, nblocks, stream);
+  if (e != hipSuccess)
+    return fail(ATTN_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+int run(const attn_bwd_args *a, void *stream, int first, int last) {
+  Checked c;
+  const int rc = validate(a, c);
+  if (rc != ATTN_OK) return rc;
+  for (int s = first; s <= last; ++s) {
+    const int r = run_stage(s, c, (hipStream_t)stream);
+    if (r != ATTN_OK) return r;
+  }
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq) {
+  if (B < 0 || H < 0 || Sq < 0) return 0;
+  return 4 * plane_bytes(B, H, Sq);
+}
+
+int attn_bwd(const attn_bwd_args *a, void *stream) {
+  return run(a, stream, attn::STAGE_ROW_STATS, attn::STAGE_DQ);
+}
+
+int attn_bwd_row_stats(const attn_bwd_args *a, void *stream) {
+  return run(a, stream, attn::STAGE_ROW_STATS, attn::STAGE_ROW_STATS);
+}
+
+int attn_bwd_kv(const attn_bwd_args *a, void *stream) {
+  return run(a, stream, attn::STAGE_KV, attn::STAGE_KV);
+}
+
+int attn_bwd_dq(const attn_bwd_args *a, void *stream) {
+  return run(a, stream, attn::STAGE_DQ, attn::STAGE_DQ);
+}
+
+const char *attn_bwd_last_error(void) { return g_err; }
+
+}  // extern "C"
