@@ -17,94 +17,164 @@
 // its `apply_synthetic_mask` and Custom / Bias branches.
 //
 // Every workgroup has 4 waves; wave w owns 32 consecutive rows of the block.
-// All five contractions run on 32x32 MFMA tiles (device_common.hpp).
+// All five contractions run on 32x32 MFMA tiles (device_common.hpp).  The
+// streamed operand (Q / dY chunks, or K / V chunks) is double-buffered in LDS:
+// while a chunk is consumed from one buffer, the next one is already in flight
+// from HBM into the other (bf16: direct global -> LDS loads), so each chunk
+// costs one barrier and no exposed load latency.
 #include "device_common.hpp"
 #include "launch.hpp"
 
 namespace attn {
 
+// Each kernel's chunk loop is unrolled by two over distinct LDS buffer objects,
+// and its body is a force-inlined step function whose buffers are __restrict__
+// parameters.  The scoped no-alias information this leaves on the LDS accesses
+// lets the compiler see that the direct-to-LDS loads filling the next buffer
+// never alias the reads of the current one, so reads do not wait on those
+// loads: the next chunk streams in while the current one is computed.
+
+// The last chunk index of a loop over [c_first, c_last], extended so that the
+// loop runs an even number of chunks (two unconditional steps per iteration;
+// a conditional second step would make the accumulators merge across paths,
+// which the compiler pays for with register copies).  The extra chunk lies
+// past the visible range -- past the end of the sequence, or past the
+// causal / window boundary -- so the index mask makes every element of it
+// invisible and it contributes nothing.
+__device__ __forceinline__ int last_chunk_even(int c_first, int c_last) {
+  const int n = c_last - c_first + 1;
+  return n <= 0 ? c_first - 1 : c_first + ((n + 1) & ~1) - 1;
+}
+
 // ---------------------------------------------------------------------------
+// Row statistics.
+template <typename T, int D> struct RowStatsState {
+  typedef MT<T> M;
+  static constexpr int NSD = D / M::KS, NT = D / 32;
+  typename M::frag qf[NSD];
+  f32x16 o[NT];
+  float m_run, l_run;
+  ChunkIO<T, D> io_k, io_v;
+  const T *kbase, *vbase;
+  int b, h, iw, qi, lane, l32, half, c_last;
+};
+
+template <typename T, int D, int MODE>
+__device__ __forceinline__ void row_stats_step(const DenseParams &p, RowStatsState<T, D> &S, int c,
+                                               const Tile<T, D> *__restrict__ Kc,
+                                               const Tile<T, D> *__restrict__ Vc,
+                                               Tile<T, D> *__restrict__ Kn,
+                                               Tile<T, D> *__restrict__ Vn) {
+  typedef MT<T> M;
+  constexpr int NSD = D / M::KS, NT = D / 32, CS = M::CSTEPS;
+  const int j0 = c * 32;
+  if (c < S.c_last) {
+    S.io_k.issue(S.kbase, p.ks[1], j0 + 32, p.Sk, *Kn);
+    S.io_v.issue(S.vbase, p.vs[1], j0 + 32, p.Sk, *Vn);
+  }
+  // Every chunk of the block's range is computed by every wave, also those no
+  // query of the wave sees (their P is 0): an unconditional body keeps the
+  // loop-carried accumulators in place.
+  const bool check = MODE != MODE_INDEX || !tile_all_visible(p, S.iw, j0);
+  // S^T = K Q^T: rows = keys (A from LDS), columns = this lane's query.
+  typename M::frag ka[NSD];
+#pragma unroll
+  for (int s = 0; s < NSD; ++s) ka[s] = Kc->frag(S.l32, s, S.half);
+  f32x16 sacc = f32x16{};
+#pragma unroll
+  for (int s = 0; s < NSD; ++s) sacc = M::mma(ka[s], S.qf[s], sacc);
+
+  float sc[16];
+  const int qi = S.qi, half = S.half;
+  scores16<MODE>(p, sacc, sc, S.b, S.h, check, [&](int) { return qi; },
+                 [&](int r) { return j0 + kr(r, half); });
+  float mloc = sc[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, sc[r]);
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+  const float m_new = fmaxf(S.m_run, mloc);
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;
+  const float alpha = fast_exp2(S.m_run - m_use);
+  float psum = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    sc[r] = fast_exp2(sc[r] - m_use);
+    psum += sc[r];
+  }
+  S.l_run = S.l_run * alpha + psum;
+  S.m_run = m_new;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) S.o[t] *= alpha;
+
+  // O^T += V^T P^T: A = V read transposed from LDS, B = P straight from the S^T tile.
+#pragma unroll
+  for (int st = 0; st < CS; ++st) {
+    const typename M::frag pf = creuse<T>(sc, st);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) S.o[t] = M::mma(Vc->tfrag(32 * t, st, S.lane), pf, S.o[t]);
+  }
+  if (c < S.c_last) {
+    S.io_k.complete(*Kn);
+    S.io_v.complete(*Vn);
+  }
+  __syncthreads();
+}
+
 template <typename T, int D, int MODE>
 __global__ __launch_bounds__(256) void k_row_stats(const DenseParams p) {
   typedef MT<T> M;
   constexpr int KS = M::KS, KL = M::KL, NSD = D / KS, NT = D / 32;
-  __shared__ RowTile<T, 32, D> Ks;
-  __shared__ typename CReuseSrc<T, 32, D>::tile Vs;
+  __shared__ Tile<T, D> Ks0, Ks1, Vs0, Vs1;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, half = lane >> 5;
+  RowStatsState<T, D> S;
+  const int tid = threadIdx.x, w = tid >> 6;
+  S.lane = tid & 63;
+  S.l32 = S.lane & 31;
+  S.half = S.lane >> 5;
   const int nb = p.nblk;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int blk = nb - 1 - (L % nb);  // the heaviest causal blocks first
-  const int h = (L / nb) % p.H, b = L / (nb * p.H);
-  const int i0 = blk * 128, iw = i0 + 32 * w, qi = iw + l32;
+  S.h = (L / nb) % p.H;
+  S.b = L / (nb * p.H);
+  const int i0 = blk * 128;
+  S.iw = i0 + 32 * w;
+  S.qi = S.iw + S.l32;
+  const int b = S.b, h = S.h, qi = S.qi, half = S.half;
   const bool qvalid = qi < p.Sq;
 
   const T *qrow = (const T *)p.q + b * p.qs[0] + (int64_t)(qvalid ? qi : 0) * p.qs[1] + h * p.qs[2];
-  typename M::frag qf[NSD];
 #pragma unroll
-  for (int s = 0; s < NSD; ++s) qf[s] = load_frag<T>(qrow, s * KS + half * KL, qvalid);
+  for (int s = 0; s < NSD; ++s) S.qf[s] = load_frag<T>(qrow, s * KS + half * KL, qvalid);
 
-  const T *kbase = (const T *)p.k + b * p.ks[0] + h * p.ks[2];
-  const T *vbase = (const T *)p.v + b * p.vs[0] + h * p.vs[2];
+  S.kbase = (const T *)p.k + b * p.ks[0] + h * p.ks[2];
+  S.vbase = (const T *)p.v + b * p.vs[0] + h * p.vs[2];
   const int ilast = min(i0 + 128, p.Sq) - 1;
   const int jlo = max(0, i0 + p.lo_off);
   const int jhi = min(p.Sk - 1, (int)min((int64_t)ilast + p.hi_off, (int64_t)kBig));
+  const int c_first = jlo >> 5;
+  S.c_last = last_chunk_even(c_first, jhi >= jlo ? jhi >> 5 : c_first - 1);
 
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x16 o[NT];
+  S.m_run = -INFINITY;
+  S.l_run = 0.f;
 #pragma unroll
-  for (int t = 0; t < NT; ++t) o[t] = f32x16{};
+  for (int t = 0; t < NT; ++t) S.o[t] = f32x16{};
 
-  for (int j0 = jlo & ~31; j0 <= jhi; j0 += 32) {
-    __syncthreads();
-    stage_rows<T, D>(kbase, p.ks[1], j0, p.Sk, Ks);
-    if constexpr (sizeof(T) == 2)
-      stage_cols<D>(vbase, p.vs[1], j0, p.Sk, Vs);  // V only transposed (A of O^T = V^T P^T)
-    else
-      stage_rows<T, D>(vbase, p.vs[1], j0, p.Sk, Vs);
-    __syncthreads();
-    if (MODE == MODE_INDEX && tile_none_visible(p, iw, j0)) continue;
-    const bool check = MODE != MODE_INDEX || !tile_all_visible(p, iw, j0);
-
-    // S^T = K Q^T: rows = keys (A from LDS), columns = this lane's query.
-    f32x16 sacc = f32x16{};
-#pragma unroll
-    for (int s = 0; s < NSD; ++s) sacc = M::mma(Ks.frag(l32, s, half), qf[s], sacc);
-
-    float sc[16];
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      sc[r] = masked_score<MODE>(p, sacc[r], b, h, qi, j0 + kr(r, half), check);
-      mloc = fmaxf(mloc, sc[r]);
-    }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    float psum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      sc[r] = fast_exp2(sc[r] - m_use);
-      psum += sc[r];
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) o[t] *= alpha;
-
-    // O^T += V^T P^T: A = V^T from LDS, B = P straight from the S^T tile.
-#pragma unroll
-    for (int st = 0; st < M::CSTEPS; ++st) {
-      const typename M::frag pf = creuse<T>(sc, st);
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-        o[t] = M::mma(CReuseSrc<T, 32, D>::frag(Vs, 32 * t + l32, st, half), pf, o[t]);
-    }
+  S.io_k.init();
+  S.io_v.init();
+  if (c_first <= S.c_last) {
+    S.io_k.issue(S.kbase, p.ks[1], c_first * 32, p.Sk, Ks0);
+    S.io_v.issue(S.vbase, p.vs[1], c_first * 32, p.Sk, Vs0);
+    S.io_k.complete(Ks0);
+    S.io_v.complete(Vs0);
+  }
+  __syncthreads();
+  for (int c = c_first; c <= S.c_last; c += 2) {
+    row_stats_step<T, D, MODE>(p, S, c, &Ks0, &Vs0, &Ks1, &Vs1);
+    row_stats_step<T, D, MODE>(p, S, c + 1, &Ks1, &Vs1, &Ks0, &Vs0);
   }
 
   // delta = dY . O / l  (O^T tile: lane holds its query, d = 32 t + kr(r, half)).
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = S.l_run + __shfl_xor(S.l_run, 32);
   const T *grow = (const T *)p.dy + b * p.dys[0] + (int64_t)(qvalid ? qi : 0) * p.dys[1] + h * p.dys[2];
   float dsum = 0.f;
   if (qvalid) {
@@ -114,113 +184,172 @@ __global__ __launch_bounds__(256) void k_row_stats(const DenseParams p) {
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * t + 8 * g + 4 * half;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dsum += (float)grow[d0 + e] * o[t][4 * g + e];
+        for (int e = 0; e < 4; ++e) dsum += (float)grow[d0 + e] * S.o[t][4 * g + e];
       }
   }
   dsum += __shfl_xor(dsum, 32);
   if (qvalid && half == 0) {
     const int64_t row = ((int64_t)b * p.H + h) * p.Sq + qi;
     const bool empty = !(l_tot > 0.f);
-    p.st_m[row] = empty ? -INFINITY : m_run * kLn2;
+    p.st_m[row] = empty ? -INFINITY : S.m_run * kLn2;
     p.st_l[row] = empty ? 0.f : l_tot;
     p.st_delta[row] = empty ? 0.f : dsum / l_tot;
-    p.st_lse2[row] = empty ? INFINITY : m_run + __log2f(l_tot);
+    p.st_lse2[row] = empty ? INFINITY : S.m_run + __log2f(l_tot);
   }
 }
 
 // ---------------------------------------------------------------------------
+// dK / dV, KV-block-major.
+template <typename T, int D> struct KvState {
+  typedef MT<T> M;
+  static constexpr int NSD = D / M::KS, NT = D / 32;
+  typename M::frag kf[NSD], vf[NSD];
+  f32x16 dk[NT], dv[NT];
+  ChunkIO<T, D> io_q, io_g;
+  const T *qbase, *gbase;
+  int64_t srow0;
+  int b, h, jw, kj, wave, lane, l32, half, c_last;
+};
+
+// Statistics of the 32 rows of chunk i0 into LDS [lse2 x 32 | delta x 32]: one
+// direct-to-LDS dword load from wave 0 (lane l < 32: lse2 of row i0 + l, lane
+// 32 + l: delta of that row).  Rows past Sq repeat the last row; the index
+// mask gives them P = 0 on every tile that holds one.
+__device__ __forceinline__ void issue_row_stats(const DenseParams &p, int64_t srow0, int i0,
+                                                float *st, int wave, int lane) {
+  if (wave == 0) {
+    const int row = min(i0 + (lane & 31), p.Sq - 1);
+    const float *src = (lane < 32 ? p.st_lse2 : p.st_delta) + srow0 + row;
+    __builtin_amdgcn_global_load_lds((const void *)src,
+                                     (__attribute__((address_space(3))) void *)st, 4, 0, 0);
+  }
+}
+
+template <typename T, int D, int MODE>
+__device__ __forceinline__ void kv_step(const DenseParams &p, KvState<T, D> &S, int c,
+                                        const Tile<T, D> *__restrict__ Qc,
+                                        const Tile<T, D> *__restrict__ Gc,
+                                        const float *__restrict__ st_c,
+                                        Tile<T, D> *__restrict__ Qn, Tile<T, D> *__restrict__ Gn,
+                                        float *__restrict__ st_n) {
+  typedef MT<T> M;
+  constexpr int NSD = D / M::KS, NT = D / 32, CS = M::CSTEPS;
+  const int i0 = c * 32;
+  if (c < S.c_last) {
+    S.io_q.issue(S.qbase, p.qs[1], i0 + 32, p.Sq, *Qn);
+    S.io_g.issue(S.gbase, p.dys[1], i0 + 32, p.Sq, *Gn);
+    issue_row_stats(p, S.srow0, i0 + 32, st_n, S.wave, S.lane);
+  }
+  // Unconditional body (see row_stats_step): invisible tiles contribute P = 0.
+  const bool check = MODE != MODE_INDEX || !tile_all_visible(p, i0, S.jw);
+  // S = Q K^T and dP = dY V^T: rows = queries (A from LDS), columns = this lane's key.
+  typename M::frag qa[NSD], ga[NSD];
+#pragma unroll
+  for (int s = 0; s < NSD; ++s) {
+    qa[s] = Qc->frag(S.l32, s, S.half);
+    ga[s] = Gc->frag(S.l32, s, S.half);
+  }
+  f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+  for (int s = 0; s < NSD; ++s) {
+    sacc = M::mma(qa[s], S.kf[s], sacc);
+    pacc = M::mma(ga[s], S.vf[s], pacc);
+  }
+  float sc[16];
+  const int kj = S.kj, half = S.half;
+  scores16<MODE>(p, sacc, sc, S.b, S.h, check, [&](int r) { return i0 + kr(r, half); },
+                 [&](int) { return kj; });
+  float pv[16], dsv[16];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const f32x4 lse4 = *reinterpret_cast<const f32x4 *>(&st_c[8 * g + 4 * half]);
+    const f32x4 del4 = *reinterpret_cast<const f32x4 *>(&st_c[32 + 8 * g + 4 * half]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * g + e;
+      const float pr = fast_exp2(sc[r] - lse4[e]);
+      pv[r] = pr;
+      dsv[r] = pr * (pacc[r] - del4[e]) * p.scale;
+    }
+  }
+  // dV^T += dY^T P and dK^T += Q^T dS: A = rows read transposed from LDS, B = C reuse.
+#pragma unroll
+  for (int st = 0; st < CS; ++st) {
+    const typename M::frag pf = creuse<T>(pv, st);
+    const typename M::frag sf = creuse<T>(dsv, st);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      S.dv[t] = M::mma(Gc->tfrag(32 * t, st, S.lane), pf, S.dv[t]);
+      S.dk[t] = M::mma(Qc->tfrag(32 * t, st, S.lane), sf, S.dk[t]);
+    }
+  }
+  if (c < S.c_last) {
+    S.io_q.complete(*Qn);
+    S.io_g.complete(*Gn);
+    wait_vmem();
+  }
+  __syncthreads();
+}
+
 template <typename T, int D, int MODE>
 __global__ __launch_bounds__(256) void k_kv_bwd(const DenseParams p) {
   typedef MT<T> M;
   constexpr int KS = M::KS, KL = M::KL, NSD = D / KS, NT = D / 32;
-  __shared__ RowTile<T, 32, D> Qs, Gs;
-  __shared__ TTile<32, (sizeof(T) == 2 ? D : 1)> Qt, Gt;  // bf16 only
-  __shared__ __attribute__((aligned(16))) float lse_s[32];
-  __shared__ __attribute__((aligned(16))) float del_s[32];
+  __shared__ Tile<T, D> Qs0, Qs1, Gs0, Gs1;
+  __shared__ __attribute__((aligned(16))) float st0[64], st1[64];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, half = lane >> 5;
+  KvState<T, D> S;
+  const int w = threadIdx.x >> 6;
+  S.wave = __builtin_amdgcn_readfirstlane(w);
+  S.lane = threadIdx.x & 63;
+  S.l32 = S.lane & 31;
+  S.half = S.lane >> 5;
   const int nb = p.nblk;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int blk = L % nb;  // key block 0 sees the most queries under a causal mask
-  const int h = (L / nb) % p.H, b = L / (nb * p.H);
-  const int j0b = blk * 128, jw = j0b + 32 * w, kj = jw + l32;
+  S.h = (L / nb) % p.H;
+  S.b = L / (nb * p.H);
+  const int j0b = blk * 128;
+  S.jw = j0b + 32 * w;
+  S.kj = S.jw + S.l32;
+  const int b = S.b, h = S.h, kj = S.kj, half = S.half;
   const bool kvalid = kj < p.Sk;
 
   const T *krow = (const T *)p.k + b * p.ks[0] + (int64_t)(kvalid ? kj : 0) * p.ks[1] + h * p.ks[2];
   const T *vrow = (const T *)p.v + b * p.vs[0] + (int64_t)(kvalid ? kj : 0) * p.vs[1] + h * p.vs[2];
-  typename M::frag kf[NSD], vf[NSD];
 #pragma unroll
   for (int s = 0; s < NSD; ++s) {
-    kf[s] = load_frag<T>(krow, s * KS + half * KL, kvalid);
-    vf[s] = load_frag<T>(vrow, s * KS + half * KL, kvalid);
+    S.kf[s] = load_frag<T>(krow, s * KS + half * KL, kvalid);
+    S.vf[s] = load_frag<T>(vrow, s * KS + half * KL, kvalid);
   }
 
-  const T *qbase = (const T *)p.q + b * p.qs[0] + h * p.qs[2];
-  const T *gbase = (const T *)p.dy + b * p.dys[0] + h * p.dys[2];
-  const int64_t srow0 = ((int64_t)b * p.H + h) * p.Sq;
+  S.qbase = (const T *)p.q + b * p.qs[0] + h * p.qs[2];
+  S.gbase = (const T *)p.dy + b * p.dys[0] + h * p.dys[2];
+  S.srow0 = ((int64_t)b * p.H + h) * p.Sq;
   const int jlast = min(j0b + 128, p.Sk) - 1;
   const int ilo = max(0, (int)max((int64_t)j0b - p.hi_off, (int64_t)0));
   const int ihi = min(p.Sq - 1, (int)min((int64_t)jlast - p.lo_off, (int64_t)kBig));
+  const int c_first = ilo >> 5;
+  S.c_last = last_chunk_even(c_first, ihi >= ilo ? ihi >> 5 : c_first - 1);
 
-  f32x16 dk[NT], dv[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) dk[t] = dv[t] = f32x16{};
+  for (int t = 0; t < NT; ++t) S.dk[t] = S.dv[t] = f32x16{};
 
-  for (int i0 = ilo & ~31; i0 <= ihi; i0 += 32) {
-    __syncthreads();
-    if constexpr (sizeof(T) == 2) {
-      stage_rows<T, D>(qbase, p.qs[1], i0, p.Sq, Qs, &Qt);
-      stage_rows<T, D>(gbase, p.dys[1], i0, p.Sq, Gs, &Gt);
-    } else {
-      stage_rows<T, D>(qbase, p.qs[1], i0, p.Sq, Qs);
-      stage_rows<T, D>(gbase, p.dys[1], i0, p.Sq, Gs);
-    }
-    if (tid < 32) {
-      const bool valid = i0 + tid < p.Sq;
-      lse_s[tid] = valid ? p.st_lse2[srow0 + i0 + tid] : INFINITY;
-      del_s[tid] = valid ? p.st_delta[srow0 + i0 + tid] : 0.f;
-    }
-    __syncthreads();
-    if (MODE == MODE_INDEX && tile_none_visible(p, i0, jw)) continue;
-    const bool check = MODE != MODE_INDEX || !tile_all_visible(p, i0, jw);
-
-    // S = Q K^T and dP = dY V^T: rows = queries (A from LDS), columns = this lane's key.
-    f32x16 sacc = f32x16{}, pacc = f32x16{};
-#pragma unroll
-    for (int s = 0; s < NSD; ++s) {
-      sacc = M::mma(Qs.frag(l32, s, half), kf[s], sacc);
-      pacc = M::mma(Gs.frag(l32, s, half), vf[s], pacc);
-    }
-    float pv[16], dsv[16];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const f32x4 lse4 = *reinterpret_cast<const f32x4 *>(&lse_s[8 * g + 4 * half]);
-      const f32x4 del4 = *reinterpret_cast<const f32x4 *>(&del_s[8 * g + 4 * half]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * g + e;
-        const float s2 = masked_score<MODE>(p, sacc[r], b, h, i0 + kr(r, half), kj, check);
-        const float pr = fast_exp2(s2 - lse4[e]);
-        pv[r] = pr;
-        dsv[r] = pr * (pacc[r] - del4[e]) * p.scale;
-      }
-    }
-    // dV^T += dY^T P and dK^T += Q^T dS: A = transposed rows from LDS, B = C reuse.
-#pragma unroll
-    for (int st = 0; st < M::CSTEPS; ++st) {
-      const typename M::frag pf = creuse<T>(pv, st);
-      const typename M::frag sf = creuse<T>(dsv, st);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        if constexpr (sizeof(T) == 2) {
-          dv[t] = M::mma(Gt.frag(32 * t + l32, st, half), pf, dv[t]);
-          dk[t] = M::mma(Qt.frag(32 * t + l32, st, half), sf, dk[t]);
-        } else {
-          dv[t] = M::mma(CReuseSrc<T, 32, D>::frag(Gs, 32 * t + l32, st, half), pf, dv[t]);
-          dk[t] = M::mma(CReuseSrc<T, 32, D>::frag(Qs, 32 * t + l32, st, half), sf, dk[t]);
-        }
-      }
-    }
+  S.io_q.init();
+  S.io_g.init();
+  if (c_first <= S.c_last) {
+    const int i0 = c_first * 32;
+    S.io_q.issue(S.qbase, p.qs[1], i0, p.Sq, Qs0);
+    S.io_g.issue(S.gbase, p.dys[1], i0, p.Sq, Gs0);
+    issue_row_stats(p, S.srow0, i0, st0, S.wave, S.lane);
+    S.io_q.complete(Qs0);
+    S.io_g.complete(Gs0);
+    wait_vmem();
+  }
+  __syncthreads();
+  for (int c = c_first; c <= S.c_last; c += 2) {
+    kv_step<T, D, MODE>(p, S, c, &Qs0, &Gs0, st0, &Qs1, &Gs1, st1);
+    kv_step<T, D, MODE>(p, S, c + 1, &Qs1, &Gs1, st1, &Qs0, &Gs0, st0);
   }
 
   if (!kvalid) return;
@@ -232,87 +361,131 @@ __global__ __launch_bounds__(256) void k_kv_bwd(const DenseParams p) {
     for (int g = 0; g < 4; ++g) {
       const int d0 = 32 * t + 8 * g + 4 * half;
       if (p.need_dk)
-        store4<T>(dkrow + d0, dk[t][4 * g], dk[t][4 * g + 1], dk[t][4 * g + 2], dk[t][4 * g + 3]);
+        store4<T>(dkrow + d0, S.dk[t][4 * g], S.dk[t][4 * g + 1], S.dk[t][4 * g + 2], S.dk[t][4 * g + 3]);
       if (p.need_dv)
-        store4<T>(dvrow + d0, dv[t][4 * g], dv[t][4 * g + 1], dv[t][4 * g + 2], dv[t][4 * g + 3]);
+        store4<T>(dvrow + d0, S.dv[t][4 * g], S.dv[t][4 * g + 1], S.dv[t][4 * g + 2], S.dv[t][4 * g + 3]);
     }
 }
 
 // ---------------------------------------------------------------------------
+// dQ, query-block-major.
+template <typename T, int D> struct DqState {
+  typedef MT<T> M;
+  static constexpr int NSD = D / M::KS, NT = D / 32;
+  typename M::frag qf[NSD], gf[NSD];
+  f32x16 dq[NT];
+  ChunkIO<T, D> io_k, io_v;
+  const T *kbase, *vbase;
+  float lse, del;
+  int b, h, iw, qi, lane, l32, half, c_last;
+};
+
+template <typename T, int D, int MODE>
+__device__ __forceinline__ void dq_step(const DenseParams &p, DqState<T, D> &S, int c,
+                                        const Tile<T, D> *__restrict__ Kc,
+                                        const Tile<T, D> *__restrict__ Vc,
+                                        Tile<T, D> *__restrict__ Kn, Tile<T, D> *__restrict__ Vn) {
+  typedef MT<T> M;
+  constexpr int NSD = D / M::KS, NT = D / 32, CS = M::CSTEPS;
+  const int j0 = c * 32;
+  if (c < S.c_last) {
+    S.io_k.issue(S.kbase, p.ks[1], j0 + 32, p.Sk, *Kn);
+    S.io_v.issue(S.vbase, p.vs[1], j0 + 32, p.Sk, *Vn);
+  }
+  // Unconditional body (see row_stats_step): invisible tiles contribute P = 0.
+  const bool check = MODE != MODE_INDEX || !tile_all_visible(p, S.iw, j0);
+  // S^T = K Q^T and dP^T = V dY^T: rows = keys, columns = this lane's query.
+  typename M::frag ka[NSD], va[NSD];
+#pragma unroll
+  for (int s = 0; s < NSD; ++s) {
+    ka[s] = Kc->frag(S.l32, s, S.half);
+    va[s] = Vc->frag(S.l32, s, S.half);
+  }
+  f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+  for (int s = 0; s < NSD; ++s) {
+    sacc = M::mma(ka[s], S.qf[s], sacc);
+    pacc = M::mma(va[s], S.gf[s], pacc);
+  }
+  float sc[16], dsv[16];
+  const int qi = S.qi, half = S.half;
+  scores16<MODE>(p, sacc, sc, S.b, S.h, check, [&](int) { return qi; },
+                 [&](int r) { return j0 + kr(r, half); });
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float pr = fast_exp2(sc[r] - S.lse);
+    dsv[r] = pr * (pacc[r] - S.del) * p.scale;
+  }
+  // dQ^T += K^T dS^T: A = K read transposed from LDS, B = dS straight from the tile.
+#pragma unroll
+  for (int st = 0; st < CS; ++st) {
+    const typename M::frag sf = creuse<T>(dsv, st);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) S.dq[t] = M::mma(Kc->tfrag(32 * t, st, S.lane), sf, S.dq[t]);
+  }
+  if (c < S.c_last) {
+    S.io_k.complete(*Kn);
+    S.io_v.complete(*Vn);
+  }
+  __syncthreads();
+}
+
 template <typename T, int D, int MODE>
 __global__ __launch_bounds__(256) void k_dq_bwd(const DenseParams p) {
   typedef MT<T> M;
   constexpr int KS = M::KS, KL = M::KL, NSD = D / KS, NT = D / 32;
-  __shared__ RowTile<T, 32, D> Ks, Vs;
-  __shared__ TTile<32, (sizeof(T) == 2 ? D : 1)> Kt;  // bf16 only
+  __shared__ Tile<T, D> Ks0, Ks1, Vs0, Vs1;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, half = lane >> 5;
+  DqState<T, D> S;
+  const int tid = threadIdx.x, w = tid >> 6;
+  S.lane = tid & 63;
+  S.l32 = S.lane & 31;
+  S.half = S.lane >> 5;
   const int nb = p.nblk;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int blk = nb - 1 - (L % nb);
-  const int h = (L / nb) % p.H, b = L / (nb * p.H);
-  const int i0 = blk * 128, iw = i0 + 32 * w, qi = iw + l32;
+  S.h = (L / nb) % p.H;
+  S.b = L / (nb * p.H);
+  const int i0 = blk * 128;
+  S.iw = i0 + 32 * w;
+  S.qi = S.iw + S.l32;
+  const int b = S.b, h = S.h, qi = S.qi, half = S.half;
   const bool qvalid = qi < p.Sq;
 
   const T *qrow = (const T *)p.q + b * p.qs[0] + (int64_t)(qvalid ? qi : 0) * p.qs[1] + h * p.qs[2];
   const T *grow = (const T *)p.dy + b * p.dys[0] + (int64_t)(qvalid ? qi : 0) * p.dys[1] + h * p.dys[2];
-  typename M::frag qf[NSD], gf[NSD];
 #pragma unroll
   for (int s = 0; s < NSD; ++s) {
-    qf[s] = load_frag<T>(qrow, s * KS + half * KL, qvalid);
-    gf[s] = load_frag<T>(grow, s * KS + half * KL, qvalid);
+    S.qf[s] = load_frag<T>(qrow, s * KS + half * KL, qvalid);
+    S.gf[s] = load_frag<T>(grow, s * KS + half * KL, qvalid);
   }
   const int64_t srow = ((int64_t)b * p.H + h) * p.Sq + (qvalid ? qi : 0);
-  const float lse = qvalid ? p.st_lse2[srow] : INFINITY;
-  const float del = qvalid ? p.st_delta[srow] : 0.f;
+  S.lse = qvalid ? p.st_lse2[srow] : INFINITY;
+  S.del = qvalid ? p.st_delta[srow] : 0.f;
 
-  const T *kbase = (const T *)p.k + b * p.ks[0] + h * p.ks[2];
-  const T *vbase = (const T *)p.v + b * p.vs[0] + h * p.vs[2];
+  S.kbase = (const T *)p.k + b * p.ks[0] + h * p.ks[2];
+  S.vbase = (const T *)p.v + b * p.vs[0] + h * p.vs[2];
   const int ilast = min(i0 + 128, p.Sq) - 1;
   const int jlo = max(0, i0 + p.lo_off);
   const int jhi = min(p.Sk - 1, (int)min((int64_t)ilast + p.hi_off, (int64_t)kBig));
+  const int c_first = jlo >> 5;
+  S.c_last = last_chunk_even(c_first, jhi >= jlo ? jhi >> 5 : c_first - 1);
 
-  f32x16 dq[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) dq[t] = f32x16{};
+  for (int t = 0; t < NT; ++t) S.dq[t] = f32x16{};
 
-  for (int j0 = jlo & ~31; j0 <= jhi; j0 += 32) {
-    __syncthreads();
-    if constexpr (sizeof(T) == 2)
-      stage_rows<T, D>(kbase, p.ks[1], j0, p.Sk, Ks, &Kt);
-    else
-      stage_rows<T, D>(kbase, p.ks[1], j0, p.Sk, Ks);
-    stage_rows<T, D>(vbase, p.vs[1], j0, p.Sk, Vs);
-    __syncthreads();
-    if (MODE == MODE_INDEX && tile_none_visible(p, iw, j0)) continue;
-    const bool check = MODE != MODE_INDEX || !tile_all_visible(p, iw, j0);
-
-    // S^T = K Q^T and dP^T = V dY^T: rows = keys, columns = this lane's query.
-    f32x16 sacc = f32x16{}, pacc = f32x16{};
-#pragma unroll
-    for (int s = 0; s < NSD; ++s) {
-      sacc = M::mma(Ks.frag(l32, s, half), qf[s], sacc);
-      pacc = M::mma(Vs.frag(l32, s, half), gf[s], pacc);
-    }
-    float dsv[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float s2 = masked_score<MODE>(p, sacc[r], b, h, qi, j0 + kr(r, half), check);
-      const float pr = fast_exp2(s2 - lse);
-      dsv[r] = pr * (pacc[r] - del) * p.scale;
-    }
-    // dQ^T += K^T dS^T: A = K^T from LDS, B = dS straight from the tile.
-#pragma unroll
-    for (int st = 0; st < M::CSTEPS; ++st) {
-      const typename M::frag sf = creuse<T>(dsv, st);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        if constexpr (sizeof(T) == 2)
-          dq[t] = M::mma(Kt.frag(32 * t + l32, st, half), sf, dq[t]);
-        else
-          dq[t] = M::mma(CReuseSrc<T, 32, D>::frag(Ks, 32 * t + l32, st, half), sf, dq[t]);
-      }
-    }
+  S.io_k.init();
+  S.io_v.init();
+  if (c_first <= S.c_last) {
+    S.io_k.issue(S.kbase, p.ks[1], c_first * 32, p.Sk, Ks0);
+    S.io_v.issue(S.vbase, p.vs[1], c_first * 32, p.Sk, Vs0);
+    S.io_k.complete(Ks0);
+    S.io_v.complete(Vs0);
+  }
+  __syncthreads();
+  for (int c = c_first; c <= S.c_last; c += 2) {
+    dq_step<T, D, MODE>(p, S, c, &Ks0, &Vs0, &Ks1, &Vs1);
+    dq_step<T, D, MODE>(p, S, c + 1, &Ks1, &Vs1, &Ks0, &Vs0);
   }
 
   if (!qvalid) return;
@@ -321,8 +494,8 @@ __global__ __launch_bounds__(256) void k_dq_bwd(const DenseParams p) {
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int g = 0; g < 4; ++g)
-      store4<T>(dqrow + 32 * t + 8 * g + 4 * half, dq[t][4 * g], dq[t][4 * g + 1], dq[t][4 * g + 2],
-                dq[t][4 * g + 3]);
+      store4<T>(dqrow + 32 * t + 8 * g + 4 * half, S.dq[t][4 * g], S.dq[t][4 * g + 1],
+                S.dq[t][4 * g + 2], S.dq[t][4 * g + 3]);
 }
 
 // ---------------------------------------------------------------------------

@@ -1,6 +1,6 @@
 // device_common.hpp -- shared device helpers for the gfx950 attention-backward
 // kernels: element types, 32x32 MFMA wrappers, fragment layouts, LDS tiles,
-// mask evaluation and the workgroup -> tile mapping.
+// the chunk prefetcher, mask evaluation and the workgroup -> tile mapping.
 //
 // Fragment conventions (wave64, 32x32 MFMA).  lane = 0..63, l32 = lane & 31,
 // half = lane >> 5.  One MFMA step contracts KS k-values; every lane holds
@@ -16,8 +16,9 @@
 // rows, with the rows permuted consistently on both operands: in bf16 step s,
 // element e of lane (n, half) stands for row kidx(s, half, e) =
 // 16 s + 8 (e / 4) + 4 half + e % 4 (which is kr(8 s + e, half)); in fp32 step
-// r the lane stands for row kr(r, half).  The matching A operand reads the same
-// rows from LDS.  No register shuffles are needed.
+// r the lane stands for row kr(r, half).  The matching A operand reads those
+// rows of one column from LDS: with ds_read_b64_tr_b16 (bf16) or a plain
+// element read (fp32).  No register shuffles are needed.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -28,6 +29,7 @@ namespace attn {
 typedef __bf16 bf16;
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -68,7 +70,6 @@ template <> struct MT<bf16> {
   __device__ __forceinline__ static f32x16 mma(frag a, frag b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
-  __device__ __forceinline__ static frag zero() { return frag{}; }
   // Steps needed to contract the 32 rows of one C tile.
   static constexpr int CSTEPS = 2;
 };
@@ -80,7 +81,6 @@ template <> struct MT<float> {
   __device__ __forceinline__ static f32x16 mma(frag a, frag b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
   }
-  __device__ __forceinline__ static frag zero() { return 0.f; }
   static constexpr int CSTEPS = 16;
 };
 
@@ -112,111 +112,138 @@ __device__ __forceinline__ float creuse<float>(const float *v, int st) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS tiles of ROWS rows x D columns.
+// LDS tile holding one 32-row chunk of a strided [S, D] matrix, row-major and
+// padded, so every fragment read of a lane is one base address plus a
+// compile-time offset.
 //
-// RowTile: row-major, padded so that the A-operand reads (32 lanes on 32 rows,
-// same columns) spread over all banks: +8 bf16 (16 B) or +1 float per row.
-// TTile (bf16 only): the same data transposed, [D][ROWS + 4], for the A operand
-// of a C-reuse product, which needs 4 consecutive rows of one column.
-template <typename T, int ROWS, int D> struct RowTile;
+// bf16: rows of D + 8 elements (D * 2 + 16 bytes).  The 16-byte pad shifts
+// consecutive rows by 4 banks, so the A-operand reads (8 rows x 16 bytes, same
+// columns) touch every bank once.  The tile is filled by direct global -> LDS
+// loads that write 1 KB segments linearly (see DirectLoader), so it is sized in
+// whole segments.
+//
+// fp32: rows of D + 1 floats; 32 lanes reading one column of 32 rows hit 32
+// different banks.
+template <typename T, int D> struct Tile;
 
-template <int ROWS, int D> struct RowTile<bf16, ROWS, D> {
-  static constexpr int LD = D + 8;
-  bf16 a[ROWS * LD];
-  // A operand of a contraction over columns: row `row`, step s.
-  __device__ __forceinline__ bf16x8 frag(int row, int s, int half) const {
-    return *reinterpret_cast<const bf16x8 *>(&a[row * LD + s * 16 + half * 8]);
+template <int D> struct Tile<bf16, D> {
+  static constexpr int LD = D + 8;                    // row stride, elements
+  static constexpr int CPR = LD / 8;                  // 16-byte slots per row (last = pad)
+  static constexpr int CH = D / 8;                    // 16-byte data chunks per row
+  static constexpr int NSEG = (32 * CPR + 63) / 64;   // 1 KB segments covering 32 rows
+  bf16 a[NSEG * 512];
+  // A operand of a contraction over columns: row r, step s.
+  __device__ __forceinline__ bf16x8 frag(int r, int s, int half) const {
+    return *reinterpret_cast<const bf16x8 *>(&a[r * LD + 16 * s + 8 * half]);
   }
-  __device__ __forceinline__ void put8(int row, int c0, bf16x8 x) {
-    *reinterpret_cast<bf16x8 *>(&a[row * LD + c0]) = x;
+  // A operand of a C-reuse product: column n0 + (lane's n), rows kidx(st, half, e).
+  // ds_read_b64_tr_b16 hands lane i of each 16-lane group element i % 4 of the
+  // 8 bytes addressed by lanes i / 4 + 4 e (e = 0..3); so lane i addresses row
+  // rowbase + i / 4, columns colbase + 4 (i % 4) .. + 3, and receives rows
+  // rowbase .. rowbase + 3 of column colbase + i.
+  __device__ __forceinline__ bf16x8 tfrag(int n0, int st, int lane) const {
+    const int i = lane & 15, g = lane >> 4, half = lane >> 5;
+    const int base = (4 * half + (i >> 2)) * LD + 16 * (g & 1) + 4 * (i & 3);
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4 *)(const_cast<bf16 *>(&a[base + 16 * st * LD + n0])));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4 *)(const_cast<bf16 *>(&a[base + (16 * st + 8) * LD + n0])));
+    const bf16x4 l = __builtin_bit_cast(bf16x4, lo), h = __builtin_bit_cast(bf16x4, hi);
+    return bf16x8{l[0], l[1], l[2], l[3], h[0], h[1], h[2], h[3]};
   }
 };
 
-template <int ROWS, int D> struct RowTile<float, ROWS, D> {
+template <int D> struct Tile<float, D> {
   static constexpr int LD = D + 1;
-  float a[ROWS * LD];
-  __device__ __forceinline__ float frag(int row, int s, int half) const {
-    return a[row * LD + 2 * s + half];
-  }
-  __device__ __forceinline__ float at(int row, int col) const { return a[row * LD + col]; }
-  __device__ __forceinline__ void put4(int row, int c0, f32x4 x) {
+  float a[32 * LD];
+  __device__ __forceinline__ void put(int r, int c, f32x4 x) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) a[row * LD + c0 + e] = x[e];
+    for (int e = 0; e < 4; ++e) a[r * LD + 4 * c + e] = x[e];
+  }
+  __device__ __forceinline__ float frag(int r, int s, int half) const {
+    return a[r * LD + 2 * s + half];
+  }
+  __device__ __forceinline__ float tfrag(int n0, int st, int lane) const {
+    return a[kr(st, lane >> 5) * LD + n0 + (lane & 31)];
   }
 };
 
-template <int ROWS, int D> struct TTile {
-  static constexpr int LD = ROWS + 4;
-  bf16 a[D * LD];
-  // A operand of a C-reuse product for column n, step s (rows kidx(s, half, e)).
-  __device__ __forceinline__ bf16x8 frag(int n, int s, int half) const {
-    const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(&a[n * LD + 16 * s + 4 * half]);
-    const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(&a[n * LD + 16 * s + 8 + 4 * half]);
-    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  }
-  __device__ __forceinline__ void put8(int row, int c0, bf16x8 x) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) a[(c0 + e) * LD + row] = x[e];
-  }
-};
+// Wait until this wave's outstanding global loads (and direct-to-LDS writes)
+// have landed: s_waitcnt vmcnt(0), other counters unconstrained.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// A operand of a C-reuse product (column n, step st) from the LDS copy of the
-// contracted rows: the transposed tile for bf16, the row-major tile for fp32.
-template <typename T, int ROWS, int D> struct CReuseSrc;
-template <int ROWS, int D> struct CReuseSrc<bf16, ROWS, D> {
-  typedef TTile<ROWS, D> tile;
-  __device__ __forceinline__ static bf16x8 frag(const tile &t, int n, int st, int half) {
-    return t.frag(n, st, half);
-  }
-};
-template <int ROWS, int D> struct CReuseSrc<float, ROWS, D> {
-  typedef RowTile<float, ROWS, D> tile;
-  __device__ __forceinline__ static float frag(const tile &t, int n, int st, int half) {
-    return t.at(kr(st, half), n);
-  }
-};
+// Streams 32-row chunks of a strided [S, D] matrix into a Tile.  issue() starts
+// the transfer of rows [r0, r0 + 32) (rows past the end repeat the last row, so
+// every tile element is finite and no lane branches); complete() must run
+// before the barrier that hands the tile to the other waves.
+//
+// bf16: gfx950 direct loads (global_load_lds_dwordx4): one instruction writes
+// the 16 bytes of lane i at LDS segment base + 16 i, so each wave fills whole
+// 1 KB segments and lane i fetches whichever row chunk belongs at that slot
+// (pad slots fetch a harmless duplicate).  No registers or LDS writes involved.
+// fp32: a register prefetch written to LDS in complete().
+template <typename T, int D> struct ChunkIO;
 
-// Stage 32 rows [r0, r0 + 32) of a strided [S, D] matrix into LDS, row-major and
-// (bf16, if `tt` is given) transposed.  Rows >= nrows are zero.  Thread t moves
-// 16 bytes of row t % 32 per pass, so each pass writes 32 different rows.
-template <typename T, int D>
-__device__ __forceinline__ void stage_rows(const T *base, int64_t row_stride, int r0, int nrows,
-                                           RowTile<T, 32, D> &rt, TTile<32, D> *tt = nullptr) {
-  constexpr int VEC = 16 / (int)sizeof(T);
-  constexpr int CH = D / VEC;  // 16-byte chunks per row
-  const int t = threadIdx.x;
-  const int row = t & 31;
-  const bool valid = r0 + row < nrows;
-  const T *src = base + (int64_t)(valid ? r0 + row : 0) * row_stride;
+template <int D> struct ChunkIO<bf16, D> {
+  typedef Tile<bf16, D> TileT;
+  static constexpr int MAXJ = (TileT::NSEG + 3) / 4;
+  int rloc[MAXJ], col[MAXJ];
+  int wave;
+  __device__ __forceinline__ void init() {
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int c = t >> 5; c < CH; c += 8) {
-    if constexpr (sizeof(T) == 2) {
-      const bf16x8 x = valid ? *reinterpret_cast<const bf16x8 *>(src + c * VEC) : bf16x8{};
-      rt.put8(row, c * VEC, x);
-      if (tt) tt->put8(row, c * VEC, x);
-    } else {
-      const f32x4 x = valid ? *reinterpret_cast<const f32x4 *>(src + c * VEC) : f32x4{};
-      rt.put4(row, c * VEC, x);
+    for (int j = 0; j < MAXJ; ++j) {
+      const int g = (wave + 4 * j) * 64 + lane;
+      int r = g / TileT::CPR, c = g % TileT::CPR;
+      if (c >= TileT::CH) c = 0;
+      if (r > 31) r = 31;
+      rloc[j] = r;
+      col[j] = 8 * c;
     }
   }
-}
-
-// Stage 32 rows [r0, r0 + 32) of a strided bf16 [S, D] matrix into LDS
-// transposed only.
-template <int D>
-__device__ __forceinline__ void stage_cols(const bf16 *base, int64_t row_stride, int r0, int nrows,
-                                           TTile<32, D> &tt) {
-  constexpr int VEC = 8, CH = D / VEC;
-  const int t = threadIdx.x;
-  const int row = t & 31;
-  const bool valid = r0 + row < nrows;
-  const bf16 *src = base + (int64_t)(valid ? r0 + row : 0) * row_stride;
+  __device__ __forceinline__ void issue(const bf16 *base, int64_t stride, int r0, int nrows,
+                                        TileT &t) {
 #pragma unroll
-  for (int c = t >> 5; c < CH; c += 8) {
-    const bf16x8 x = valid ? *reinterpret_cast<const bf16x8 *>(src + c * VEC) : bf16x8{};
-    tt.put8(row, c * VEC, x);
+    for (int j = 0; j < MAXJ; ++j) {
+      const int seg = wave + 4 * j;
+      if (seg < TileT::NSEG) {
+        const int row = min(r0 + rloc[j], nrows - 1);
+        const bf16 *src = base + (int64_t)row * stride + col[j];
+        __builtin_amdgcn_global_load_lds(
+            (const void *)src, (__attribute__((address_space(3))) void *)(&t.a[seg * 512]), 16, 0, 0);
+      }
+    }
   }
-}
+  __device__ __forceinline__ void complete(TileT &) { wait_vmem(); }
+};
+
+template <int D> struct ChunkIO<float, D> {
+  typedef Tile<float, D> TileT;
+  static constexpr int CH = D / 4;  // 16-byte chunks per row
+  static constexpr int PER = (32 * CH + 255) / 256;
+  f32x4 r[PER];
+  __device__ __forceinline__ void init() {}
+  __device__ __forceinline__ void issue(const float *base, int64_t stride, int r0, int nrows,
+                                        TileT &) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int id = threadIdx.x + 256 * j;
+      const int row = min(r0 + id / CH, nrows - 1), c = id % CH;
+      r[j] = (32 * CH % 256 == 0 || id < 32 * CH)
+                 ? *reinterpret_cast<const f32x4 *>(base + (int64_t)row * stride + 4 * c)
+                 : f32x4{};
+    }
+  }
+  __device__ __forceinline__ void complete(TileT &t) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int id = threadIdx.x + 256 * j;
+      if (32 * CH % 256 == 0 || id < 32 * CH) t.put(id / CH, id % CH, r[j]);
+    }
+  }
+};
 
 // Visibility of (query i, key j) by the index rule.
 __device__ __forceinline__ bool idx_visible(const DenseParams &p, int i, int j) {
@@ -236,31 +263,38 @@ __device__ __forceinline__ bool tile_none_visible(const DenseParams &p, int i0, 
   return i0 >= p.Sq || j0 >= p.Sk || j0 - (i0 + 31) > p.hi_off || (j0 + 31) - i0 < p.lo_off;
 }
 
-// log2-domain score of (i, j) from the raw dot product, with the mask applied:
-// -inf when hidden.  MODE_INDEX callers skip the per-element test on tiles that
-// are entirely visible.
-template <int MODE>
-__device__ __forceinline__ float masked_score(const DenseParams &p, float dot, int b, int h,
-                                              int i, int j, bool check) {
-  float s = dot * p.scale_log2;
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Turn the 16 raw dot products of a C tile into masked log2-domain scores.
+// Element r sits at (query qi(r), key kj(r)) as given by the functors.  The
+// index rule is only evaluated on tiles that need it (`check`, wave-uniform),
+// and then without branches.
+template <int MODE, typename QI, typename KJ>
+__device__ __forceinline__ void scores16(const DenseParams &p, const f32x16 &acc, float *s2, int b,
+                                         int h, bool check, QI qi, KJ kj) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s2[r] = acc[r] * p.scale_log2;
   if constexpr (MODE == MODE_INDEX) {
-    if (check && !idx_visible(p, i, j)) s = -INFINITY;
+    if (check) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s2[r] = idx_visible(p, qi(r), kj(r)) ? s2[r] : -INFINITY;
+    }
   } else {
-    if (!idx_visible(p, i, j)) {
-      s = -INFINITY;
-    } else {
-      const float mv = p.mask[b * p.ms[0] + h * p.ms[1] + (int64_t)i * p.ms[2] + (int64_t)j * p.ms[3]];
-      if constexpr (MODE == MODE_KEYPAD) {
-        if (mv < p.thr) s = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = qi(r), j = kj(r);
+      if (idx_visible(p, i, j)) {
+        const float mv = p.mask[b * p.ms[0] + h * p.ms[1] + (int64_t)i * p.ms[2] + (int64_t)j * p.ms[3]];
+        if constexpr (MODE == MODE_KEYPAD)
+          s2[r] = mv < p.thr ? -INFINITY : s2[r];
+        else
+          s2[r] = fmaf(mv, kLog2e, s2[r]);
       } else {
-        s = fmaf(mv, kLog2e, s);
+        s2[r] = -INFINITY;
       }
     }
   }
-  return s;
 }
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Workgroup id -> logical tile id.  The hardware hands workgroup i to XCD i % 8;
 // this gives every XCD a contiguous range of logical ids, so the tiles of one
