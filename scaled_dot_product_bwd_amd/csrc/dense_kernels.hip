@@ -18,32 +18,45 @@
 //
 // Every workgroup has 4 waves; wave w owns 32 consecutive rows of the block.
 // All five contractions run on 32x32 MFMA tiles (device_common.hpp).  The
-// streamed operand (Q / dY chunks, or K / V chunks) is double-buffered in LDS:
-// while a chunk is consumed from one buffer, the next one is already in flight
-// from HBM into the other (bf16: direct global -> LDS loads), so each chunk
-// costs one barrier and no exposed load latency.
+// streamed operand (Q / dY chunks, or K / V chunks) is triple-buffered in LDS:
+// while chunk c is consumed from one buffer, chunk c + 1 is landing in the
+// second and chunk c + 2 is being requested into the third (bf16: direct
+// global -> LDS loads), so each chunk costs one barrier and HBM / L2 latency
+// stays hidden behind two chunks of compute.
 #include "device_common.hpp"
 #include "launch.hpp"
 
 namespace attn {
 
-// Each kernel's chunk loop is unrolled by two over distinct LDS buffer objects,
-// and its body is a force-inlined step function whose buffers are __restrict__
-// parameters.  The scoped no-alias information this leaves on the LDS accesses
-// lets the compiler see that the direct-to-LDS loads filling the next buffer
-// never alias the reads of the current one, so reads do not wait on those
-// loads: the next chunk streams in while the current one is computed.
+// Each kernel's chunk loop runs in a force-inlined `*_run` function unrolled by
+// three, so every step has its LDS buffers fixed at compile time.  Steps are
+// unconditional (a conditional step would make the accumulators merge across
+// paths, which the compiler pays for with register copies); chunks no row of
+// a wave sees are computed like any other and contribute P = 0.
 
-// The last chunk index of a loop over [c_first, c_last], extended so that the
-// loop runs an even number of chunks (two unconditional steps per iteration;
-// a conditional second step would make the accumulators merge across paths,
-// which the compiler pays for with register copies).  The extra chunk lies
-// past the visible range -- past the end of the sequence, or past the
-// causal / window boundary -- so the index mask makes every element of it
-// invisible and it contributes nothing.
-__device__ __forceinline__ int last_chunk_even(int c_first, int c_last) {
-  const int n = c_last - c_first + 1;
-  return n <= 0 ? c_first - 1 : c_first + ((n + 1) & ~1) - 1;
+// After the compute of a step: make this wave's loads of the next chunk land
+// (leaving the `issued` loads of the chunk after it in flight), then hand the
+// buffers over.  fp32 tiles are written from registers in complete() instead.
+template <bool DIRECT, int PER_CHUNK>
+__device__ __forceinline__ void end_step(bool issued) {
+  if constexpr (DIRECT) {
+    if (issued)
+      wait_vmem_le<PER_CHUNK>();
+    else
+      wait_vmem();
+  }
+  __syncthreads();
+}
+
+// Statistics of the 32 rows of chunk i0 into LDS [lse2 x 32 | delta x 32]: one
+// direct-to-LDS dword load per wave (lane l < 32: lse2 of row i0 + l, lane
+// 32 + l: delta of that row; each wave writes its own copy, so every wave
+// issues the same number of loads).  Rows past Sq repeat the last row; the
+// index mask gives them P = 0 on every tile that holds one.
+__device__ __forceinline__ void issue_row_stats(const DenseParams &p, int64_t srow0, int i0,
+                                                float *st, int wave, int lane) {
+  const int row = min(i0 + (lane & 31), p.Sq - 1);
+  dma_lds4(st + 64 * wave, (lane < 32 ? p.st_lse2 : p.st_delta) + srow0 + row);
 }
 
 // ---------------------------------------------------------------------------
@@ -61,20 +74,16 @@ template <typename T, int D> struct RowStatsState {
 
 template <typename T, int D, int MODE>
 __device__ __forceinline__ void row_stats_step(const DenseParams &p, RowStatsState<T, D> &S, int c,
-                                               const Tile<T, D> *__restrict__ Kc,
-                                               const Tile<T, D> *__restrict__ Vc,
-                                               Tile<T, D> *__restrict__ Kn,
-                                               Tile<T, D> *__restrict__ Vn) {
+                                               const Tile<T, D> *Kc, const Tile<T, D> *Vc, int cn,
+                                               Tile<T, D> *Kn, Tile<T, D> *Vn) {
   typedef MT<T> M;
   constexpr int NSD = D / M::KS, NT = D / 32, CS = M::CSTEPS;
   const int j0 = c * 32;
-  if (c < S.c_last) {
-    S.io_k.issue(S.kbase, p.ks[1], j0 + 32, p.Sk, *Kn);
-    S.io_v.issue(S.vbase, p.vs[1], j0 + 32, p.Sk, *Vn);
+  const bool issued = cn <= S.c_last;
+  if (issued) {
+    S.io_k.issue(S.kbase, p.ks[1], cn * 32, p.Sk, *Kn);
+    S.io_v.issue(S.vbase, p.vs[1], cn * 32, p.Sk, *Vn);
   }
-  // Every chunk of the block's range is computed by every wave, also those no
-  // query of the wave sees (their P is 0): an unconditional body keeps the
-  // loop-carried accumulators in place.
   const bool check = MODE != MODE_INDEX || !tile_all_visible(p, S.iw, j0);
   // S^T = K Q^T: rows = keys (A from LDS), columns = this lane's query.
   typename M::frag ka[NSD];
@@ -113,18 +122,51 @@ __device__ __forceinline__ void row_stats_step(const DenseParams &p, RowStatsSta
 #pragma unroll
     for (int t = 0; t < NT; ++t) S.o[t] = M::mma(Vc->tfrag(32 * t, st, S.lane), pf, S.o[t]);
   }
-  if (c < S.c_last) {
+  if (issued) {
     S.io_k.complete(*Kn);
     S.io_v.complete(*Vn);
   }
-  __syncthreads();
+  end_step<ChunkIO<T, D>::DIRECT, 2 * ChunkIO<T, D>::LOADS>(issued);
 }
 
 template <typename T, int D, int MODE>
-__global__ __launch_bounds__(256) void k_row_stats(const DenseParams p) {
+__device__ __forceinline__ void row_stats_run(const DenseParams &p, RowStatsState<T, D> &S,
+                                              int c_first, Tile<T, D> *__restrict__ K0,
+                                              Tile<T, D> *__restrict__ K1,
+                                              Tile<T, D> *__restrict__ K2,
+                                              Tile<T, D> *__restrict__ V0,
+                                              Tile<T, D> *__restrict__ V1,
+                                              Tile<T, D> *__restrict__ V2) {
+  const int c_last = S.c_last;
+  if (c_first <= c_last) {
+    S.io_k.issue(S.kbase, p.ks[1], c_first * 32, p.Sk, *K0);
+    S.io_v.issue(S.vbase, p.vs[1], c_first * 32, p.Sk, *V0);
+    S.io_k.complete(*K0);
+    S.io_v.complete(*V0);
+  }
+  const bool second = c_first + 1 <= c_last;
+  if (second) {
+    S.io_k.issue(S.kbase, p.ks[1], (c_first + 1) * 32, p.Sk, *K1);
+    S.io_v.issue(S.vbase, p.vs[1], (c_first + 1) * 32, p.Sk, *V1);
+    S.io_k.complete(*K1);
+    S.io_v.complete(*V1);
+  }
+  end_step<ChunkIO<T, D>::DIRECT, 2 * ChunkIO<T, D>::LOADS>(second);
+  int c = c_first;
+  for (; c + 2 <= c_last; c += 3) {
+    row_stats_step<T, D, MODE>(p, S, c, K0, V0, c + 2, K2, V2);
+    row_stats_step<T, D, MODE>(p, S, c + 1, K1, V1, c + 3, K0, V0);
+    row_stats_step<T, D, MODE>(p, S, c + 2, K2, V2, c + 4, K1, V1);
+  }
+  if (c <= c_last) row_stats_step<T, D, MODE>(p, S, c, K0, V0, c + 2, K2, V2);
+  if (c + 1 <= c_last) row_stats_step<T, D, MODE>(p, S, c + 1, K1, V1, c + 3, K0, V0);
+}
+
+template <typename T, int D, int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_row_stats(const DenseParams p) {
   typedef MT<T> M;
   constexpr int KS = M::KS, KL = M::KL, NSD = D / KS, NT = D / 32;
-  __shared__ Tile<T, D> Ks0, Ks1, Vs0, Vs1;
+  __shared__ Tile<T, D> Ks0, Ks1, Ks2, Vs0, Vs1, Vs2;
 
   RowStatsState<T, D> S;
   const int tid = threadIdx.x, w = tid >> 6;
@@ -152,26 +194,19 @@ __global__ __launch_bounds__(256) void k_row_stats(const DenseParams p) {
   const int jlo = max(0, i0 + p.lo_off);
   const int jhi = min(p.Sk - 1, (int)min((int64_t)ilast + p.hi_off, (int64_t)kBig));
   const int c_first = jlo >> 5;
-  S.c_last = last_chunk_even(c_first, jhi >= jlo ? jhi >> 5 : c_first - 1);
+  S.c_last = jhi >= jlo ? jhi >> 5 : c_first - 1;
 
   S.m_run = -INFINITY;
   S.l_run = 0.f;
 #pragma unroll
   for (int t = 0; t < NT; ++t) S.o[t] = f32x16{};
-
   S.io_k.init();
   S.io_v.init();
-  if (c_first <= S.c_last) {
-    S.io_k.issue(S.kbase, p.ks[1], c_first * 32, p.Sk, Ks0);
-    S.io_v.issue(S.vbase, p.vs[1], c_first * 32, p.Sk, Vs0);
-    S.io_k.complete(Ks0);
-    S.io_v.complete(Vs0);
-  }
-  __syncthreads();
-  for (int c = c_first; c <= S.c_last; c += 2) {
-    row_stats_step<T, D, MODE>(p, S, c, &Ks0, &Vs0, &Ks1, &Vs1);
-    row_stats_step<T, D, MODE>(p, S, c + 1, &Ks1, &Vs1, &Ks0, &Vs0);
-  }
+  // Let the fragment loads above land before the first chunk load is issued,
+  // so the compiler knows they are complete inside the loop (otherwise it
+  // would wait for them there, and with them for the chunk loads in flight).
+  wait_vmem();
+  row_stats_run<T, D, MODE>(p, S, c_first, &Ks0, &Ks1, &Ks2, &Vs0, &Vs1, &Vs2);
 
   // delta = dY . O / l  (O^T tile: lane holds its query, d = 32 t + kr(r, half)).
   const float l_tot = S.l_run + __shfl_xor(S.l_run, 32);
@@ -211,36 +246,24 @@ template <typename T, int D> struct KvState {
   int b, h, jw, kj, wave, lane, l32, half, c_last;
 };
 
-// Statistics of the 32 rows of chunk i0 into LDS [lse2 x 32 | delta x 32]: one
-// direct-to-LDS dword load from wave 0 (lane l < 32: lse2 of row i0 + l, lane
-// 32 + l: delta of that row).  Rows past Sq repeat the last row; the index
-// mask gives them P = 0 on every tile that holds one.
-__device__ __forceinline__ void issue_row_stats(const DenseParams &p, int64_t srow0, int i0,
-                                                float *st, int wave, int lane) {
-  if (wave == 0) {
-    const int row = min(i0 + (lane & 31), p.Sq - 1);
-    const float *src = (lane < 32 ? p.st_lse2 : p.st_delta) + srow0 + row;
-    __builtin_amdgcn_global_load_lds((const void *)src,
-                                     (__attribute__((address_space(3))) void *)st, 4, 0, 0);
-  }
+template <typename T, int D, int MODE>
+__device__ __forceinline__ void kv_issue(const DenseParams &p, KvState<T, D> &S, int c,
+                                         Tile<T, D> *Q, Tile<T, D> *G, float *st) {
+  S.io_q.issue(S.qbase, p.qs[1], c * 32, p.Sq, *Q);
+  S.io_g.issue(S.gbase, p.dys[1], c * 32, p.Sq, *G);
+  issue_row_stats(p, S.srow0, c * 32, st, S.wave, S.lane);
 }
 
 template <typename T, int D, int MODE>
 __device__ __forceinline__ void kv_step(const DenseParams &p, KvState<T, D> &S, int c,
-                                        const Tile<T, D> *__restrict__ Qc,
-                                        const Tile<T, D> *__restrict__ Gc,
-                                        const float *__restrict__ st_c,
-                                        Tile<T, D> *__restrict__ Qn, Tile<T, D> *__restrict__ Gn,
-                                        float *__restrict__ st_n) {
+                                        const Tile<T, D> *Qc, const Tile<T, D> *Gc,
+                                        const float *st_c, int cn, Tile<T, D> *Qn, Tile<T, D> *Gn,
+                                        float *st_n) {
   typedef MT<T> M;
   constexpr int NSD = D / M::KS, NT = D / 32, CS = M::CSTEPS;
   const int i0 = c * 32;
-  if (c < S.c_last) {
-    S.io_q.issue(S.qbase, p.qs[1], i0 + 32, p.Sq, *Qn);
-    S.io_g.issue(S.gbase, p.dys[1], i0 + 32, p.Sq, *Gn);
-    issue_row_stats(p, S.srow0, i0 + 32, st_n, S.wave, S.lane);
-  }
-  // Unconditional body (see row_stats_step): invisible tiles contribute P = 0.
+  const bool issued = cn <= S.c_last;
+  if (issued) kv_issue<T, D, MODE>(p, S, cn, Qn, Gn, st_n);
   const bool check = MODE != MODE_INDEX || !tile_all_visible(p, i0, S.jw);
   // S = Q K^T and dP = dY V^T: rows = queries (A from LDS), columns = this lane's key.
   typename M::frag qa[NSD], ga[NSD];
@@ -283,20 +306,49 @@ __device__ __forceinline__ void kv_step(const DenseParams &p, KvState<T, D> &S, 
       S.dk[t] = M::mma(Qc->tfrag(32 * t, st, S.lane), sf, S.dk[t]);
     }
   }
-  if (c < S.c_last) {
+  if (issued) {
     S.io_q.complete(*Qn);
     S.io_g.complete(*Gn);
-    wait_vmem();
   }
-  __syncthreads();
+  end_step<ChunkIO<T, D>::DIRECT, 2 * ChunkIO<T, D>::LOADS + 1>(issued);
+}
+
+template <typename T, int D, int MODE>
+__device__ __forceinline__ void kv_run(const DenseParams &p, KvState<T, D> &S, int c_first,
+                                       Tile<T, D> *__restrict__ Q0, Tile<T, D> *__restrict__ Q1,
+                                       Tile<T, D> *__restrict__ Q2, Tile<T, D> *__restrict__ G0,
+                                       Tile<T, D> *__restrict__ G1, Tile<T, D> *__restrict__ G2,
+                                       float *__restrict__ s0, float *__restrict__ s1,
+                                       float *__restrict__ s2) {
+  const int c_last = S.c_last;
+  if (c_first <= c_last) {
+    kv_issue<T, D, MODE>(p, S, c_first, Q0, G0, s0);
+    S.io_q.complete(*Q0);
+    S.io_g.complete(*G0);
+  }
+  const bool second = c_first + 1 <= c_last;
+  if (second) {
+    kv_issue<T, D, MODE>(p, S, c_first + 1, Q1, G1, s1);
+    S.io_q.complete(*Q1);
+    S.io_g.complete(*G1);
+  }
+  end_step<ChunkIO<T, D>::DIRECT, 2 * ChunkIO<T, D>::LOADS + 1>(second);
+  int c = c_first;
+  for (; c + 2 <= c_last; c += 3) {
+    kv_step<T, D, MODE>(p, S, c, Q0, G0, s0, c + 2, Q2, G2, s2);
+    kv_step<T, D, MODE>(p, S, c + 1, Q1, G1, s1, c + 3, Q0, G0, s0);
+    kv_step<T, D, MODE>(p, S, c + 2, Q2, G2, s2, c + 4, Q1, G1, s1);
+  }
+  if (c <= c_last) kv_step<T, D, MODE>(p, S, c, Q0, G0, s0, c + 2, Q2, G2, s2);
+  if (c + 1 <= c_last) kv_step<T, D, MODE>(p, S, c + 1, Q1, G1, s1, c + 3, Q0, G0, s0);
 }
 
 template <typename T, int D, int MODE>
 __global__ __launch_bounds__(256) void k_kv_bwd(const DenseParams p) {
   typedef MT<T> M;
   constexpr int KS = M::KS, KL = M::KL, NSD = D / KS, NT = D / 32;
-  __shared__ Tile<T, D> Qs0, Qs1, Gs0, Gs1;
-  __shared__ __attribute__((aligned(16))) float st0[64], st1[64];
+  __shared__ Tile<T, D> Qs0, Qs1, Qs2, Gs0, Gs1, Gs2;
+  __shared__ __attribute__((aligned(16))) float st0[256], st1[256], st2[256];
 
   KvState<T, D> S;
   const int w = threadIdx.x >> 6;
@@ -330,27 +382,14 @@ __global__ __launch_bounds__(256) void k_kv_bwd(const DenseParams p) {
   const int ilo = max(0, (int)max((int64_t)j0b - p.hi_off, (int64_t)0));
   const int ihi = min(p.Sq - 1, (int)min((int64_t)jlast - p.lo_off, (int64_t)kBig));
   const int c_first = ilo >> 5;
-  S.c_last = last_chunk_even(c_first, ihi >= ilo ? ihi >> 5 : c_first - 1);
+  S.c_last = ihi >= ilo ? ihi >> 5 : c_first - 1;
 
 #pragma unroll
   for (int t = 0; t < NT; ++t) S.dk[t] = S.dv[t] = f32x16{};
-
   S.io_q.init();
   S.io_g.init();
-  if (c_first <= S.c_last) {
-    const int i0 = c_first * 32;
-    S.io_q.issue(S.qbase, p.qs[1], i0, p.Sq, Qs0);
-    S.io_g.issue(S.gbase, p.dys[1], i0, p.Sq, Gs0);
-    issue_row_stats(p, S.srow0, i0, st0, S.wave, S.lane);
-    S.io_q.complete(Qs0);
-    S.io_g.complete(Gs0);
-    wait_vmem();
-  }
-  __syncthreads();
-  for (int c = c_first; c <= S.c_last; c += 2) {
-    kv_step<T, D, MODE>(p, S, c, &Qs0, &Gs0, st0, &Qs1, &Gs1, st1);
-    kv_step<T, D, MODE>(p, S, c + 1, &Qs1, &Gs1, st1, &Qs0, &Gs0, st0);
-  }
+  wait_vmem();  // fragment loads complete before the loop (see k_row_stats)
+  kv_run<T, D, MODE>(p, S, c_first, &Qs0, &Qs1, &Qs2, &Gs0, &Gs1, &Gs2, st0, st1, st2);
 
   if (!kvalid) return;
   T *dkrow = (T *)p.dk + b * p.dks[0] + (int64_t)kj * p.dks[1] + h * p.dks[2];
@@ -382,17 +421,16 @@ template <typename T, int D> struct DqState {
 
 template <typename T, int D, int MODE>
 __device__ __forceinline__ void dq_step(const DenseParams &p, DqState<T, D> &S, int c,
-                                        const Tile<T, D> *__restrict__ Kc,
-                                        const Tile<T, D> *__restrict__ Vc,
-                                        Tile<T, D> *__restrict__ Kn, Tile<T, D> *__restrict__ Vn) {
+                                        const Tile<T, D> *Kc, const Tile<T, D> *Vc, int cn,
+                                        Tile<T, D> *Kn, Tile<T, D> *Vn) {
   typedef MT<T> M;
   constexpr int NSD = D / M::KS, NT = D / 32, CS = M::CSTEPS;
   const int j0 = c * 32;
-  if (c < S.c_last) {
-    S.io_k.issue(S.kbase, p.ks[1], j0 + 32, p.Sk, *Kn);
-    S.io_v.issue(S.vbase, p.vs[1], j0 + 32, p.Sk, *Vn);
+  const bool issued = cn <= S.c_last;
+  if (issued) {
+    S.io_k.issue(S.kbase, p.ks[1], cn * 32, p.Sk, *Kn);
+    S.io_v.issue(S.vbase, p.vs[1], cn * 32, p.Sk, *Vn);
   }
-  // Unconditional body (see row_stats_step): invisible tiles contribute P = 0.
   const bool check = MODE != MODE_INDEX || !tile_all_visible(p, S.iw, j0);
   // S^T = K Q^T and dP^T = V dY^T: rows = keys, columns = this lane's query.
   typename M::frag ka[NSD], va[NSD];
@@ -423,18 +461,48 @@ __device__ __forceinline__ void dq_step(const DenseParams &p, DqState<T, D> &S, 
 #pragma unroll
     for (int t = 0; t < NT; ++t) S.dq[t] = M::mma(Kc->tfrag(32 * t, st, S.lane), sf, S.dq[t]);
   }
-  if (c < S.c_last) {
+  if (issued) {
     S.io_k.complete(*Kn);
     S.io_v.complete(*Vn);
   }
-  __syncthreads();
+  end_step<ChunkIO<T, D>::DIRECT, 2 * ChunkIO<T, D>::LOADS>(issued);
 }
 
 template <typename T, int D, int MODE>
-__global__ __launch_bounds__(256) void k_dq_bwd(const DenseParams p) {
+__device__ __forceinline__ void dq_run(const DenseParams &p, DqState<T, D> &S, int c_first,
+                                       Tile<T, D> *__restrict__ K0, Tile<T, D> *__restrict__ K1,
+                                       Tile<T, D> *__restrict__ K2, Tile<T, D> *__restrict__ V0,
+                                       Tile<T, D> *__restrict__ V1, Tile<T, D> *__restrict__ V2) {
+  const int c_last = S.c_last;
+  if (c_first <= c_last) {
+    S.io_k.issue(S.kbase, p.ks[1], c_first * 32, p.Sk, *K0);
+    S.io_v.issue(S.vbase, p.vs[1], c_first * 32, p.Sk, *V0);
+    S.io_k.complete(*K0);
+    S.io_v.complete(*V0);
+  }
+  const bool second = c_first + 1 <= c_last;
+  if (second) {
+    S.io_k.issue(S.kbase, p.ks[1], (c_first + 1) * 32, p.Sk, *K1);
+    S.io_v.issue(S.vbase, p.vs[1], (c_first + 1) * 32, p.Sk, *V1);
+    S.io_k.complete(*K1);
+    S.io_v.complete(*V1);
+  }
+  end_step<ChunkIO<T, D>::DIRECT, 2 * ChunkIO<T, D>::LOADS>(second);
+  int c = c_first;
+  for (; c + 2 <= c_last; c += 3) {
+    dq_step<T, D, MODE>(p, S, c, K0, V0, c + 2, K2, V2);
+    dq_step<T, D, MODE>(p, S, c + 1, K1, V1, c + 3, K0, V0);
+    dq_step<T, D, MODE>(p, S, c + 2, K2, V2, c + 4, K1, V1);
+  }
+  if (c <= c_last) dq_step<T, D, MODE>(p, S, c, K0, V0, c + 2, K2, V2);
+  if (c + 1 <= c_last) dq_step<T, D, MODE>(p, S, c + 1, K1, V1, c + 3, K0, V0);
+}
+
+template <typename T, int D, int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_dq_bwd(const DenseParams p) {
   typedef MT<T> M;
   constexpr int KS = M::KS, KL = M::KL, NSD = D / KS, NT = D / 32;
-  __shared__ Tile<T, D> Ks0, Ks1, Vs0, Vs1;
+  __shared__ Tile<T, D> Ks0, Ks1, Ks2, Vs0, Vs1, Vs2;
 
   DqState<T, D> S;
   const int tid = threadIdx.x, w = tid >> 6;
@@ -469,24 +537,14 @@ __global__ __launch_bounds__(256) void k_dq_bwd(const DenseParams p) {
   const int jlo = max(0, i0 + p.lo_off);
   const int jhi = min(p.Sk - 1, (int)min((int64_t)ilast + p.hi_off, (int64_t)kBig));
   const int c_first = jlo >> 5;
-  S.c_last = last_chunk_even(c_first, jhi >= jlo ? jhi >> 5 : c_first - 1);
+  S.c_last = jhi >= jlo ? jhi >> 5 : c_first - 1;
 
 #pragma unroll
   for (int t = 0; t < NT; ++t) S.dq[t] = f32x16{};
-
   S.io_k.init();
   S.io_v.init();
-  if (c_first <= S.c_last) {
-    S.io_k.issue(S.kbase, p.ks[1], c_first * 32, p.Sk, Ks0);
-    S.io_v.issue(S.vbase, p.vs[1], c_first * 32, p.Sk, Vs0);
-    S.io_k.complete(Ks0);
-    S.io_v.complete(Vs0);
-  }
-  __syncthreads();
-  for (int c = c_first; c <= S.c_last; c += 2) {
-    dq_step<T, D, MODE>(p, S, c, &Ks0, &Vs0, &Ks1, &Vs1);
-    dq_step<T, D, MODE>(p, S, c + 1, &Ks1, &Vs1, &Ks0, &Vs0);
-  }
+  wait_vmem();  // fragment and statistics loads complete before the loop (see k_row_stats)
+  dq_run<T, D, MODE>(p, S, c_first, &Ks0, &Ks1, &Ks2, &Vs0, &Vs1, &Vs2);
 
   if (!qvalid) return;
   T *dqrow = (T *)p.dq + b * p.dqs[0] + (int64_t)qi * p.dqs[1] + h * p.dqs[2];

@@ -112,43 +112,52 @@ __device__ __forceinline__ float creuse<float>(const float *v, int st) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS tile holding one 32-row chunk of a strided [S, D] matrix, row-major and
-// padded, so every fragment read of a lane is one base address plus a
-// compile-time offset.
+// LDS tile holding one 32-row chunk of a strided [S, D] matrix.
 //
-// bf16: rows of D + 8 elements (D * 2 + 16 bytes).  The 16-byte pad shifts
-// consecutive rows by 4 banks, so the A-operand reads (8 rows x 16 bytes, same
-// columns) touch every bank once.  The tile is filled by direct global -> LDS
-// loads that write 1 KB segments linearly (see DirectLoader), so it is sized in
-// whole segments.
+// bf16: rows are laid out in groups of four, row r at byte offset
+// (r / 4) * G + (r % 4) * RS.  gfx950 LDS has 64 banks of 4 bytes; it serves a
+// ds_read_b128 16 lanes at a time and a ds_read_b64_tr_b16 32 lanes at a time.
+// The A-operand read (16 consecutive rows, same 16 bytes) is conflict-free iff
+// those rows start at 16 distinct multiples of 16 modulo 256; the C-reuse read
+// (4 consecutive rows of one group, 64 bytes each) iff the 4 rows start in 4
+// different 64-byte quarters modulo 256.  RS = 64 (mod 256) for D = 32,
+// 192 or 320 for D = 64 / 128 spreads a group's rows over the quarters, and
+// G = 16 (mod 64) shifts successive groups by 16 bytes: both patterns are
+// conflict-free, and each fragment read of a lane is one base address plus a
+// compile-time offset.  The tile is filled by direct global -> LDS loads that
+// write whole 1 KB segments (see ChunkIO), so it is sized in segments, a
+// multiple of 4 of them so that every wave issues the same number of loads.
 //
 // fp32: rows of D + 1 floats; 32 lanes reading one column of 32 rows hit 32
 // different banks.
 template <typename T, int D> struct Tile;
 
 template <int D> struct Tile<bf16, D> {
-  static constexpr int LD = D + 8;                    // row stride, elements
-  static constexpr int CPR = LD / 8;                  // 16-byte slots per row (last = pad)
-  static constexpr int CH = D / 8;                    // 16-byte data chunks per row
-  static constexpr int NSEG = (32 * CPR + 63) / 64;   // 1 KB segments covering 32 rows
+  static constexpr int RS = D == 128 ? 160 : (D == 64 ? 96 : 32);   // row stride in a group, elements
+  static constexpr int G = D == 128 ? 616 : (D == 64 ? 360 : 136);  // group stride, elements
+  static constexpr int SLOTS = 8 * G / 8;                            // 16-byte slots of 8 groups
+  static constexpr int NSEG = ((SLOTS + 63) / 64 + 3) / 4 * 4;       // 1 KB load segments
   bf16 a[NSEG * 512];
+  __device__ __forceinline__ static constexpr int row_off(int r) { return (r >> 2) * G + (r & 3) * RS; }
   // A operand of a contraction over columns: row r, step s.
   __device__ __forceinline__ bf16x8 frag(int r, int s, int half) const {
-    return *reinterpret_cast<const bf16x8 *>(&a[r * LD + 16 * s + 8 * half]);
+    return *reinterpret_cast<const bf16x8 *>(&a[row_off(r) + 16 * s + 8 * half]);
   }
   // A operand of a C-reuse product: column n0 + (lane's n), rows kidx(st, half, e).
   // ds_read_b64_tr_b16 hands lane i of each 16-lane group element i % 4 of the
   // 8 bytes addressed by lanes i / 4 + 4 e (e = 0..3); so lane i addresses row
   // rowbase + i / 4, columns colbase + 4 (i % 4) .. + 3, and receives rows
-  // rowbase .. rowbase + 3 of column colbase + i.
+  // rowbase .. rowbase + 3 of column colbase + i.  rowbase = 16 st + 4 half
+  // (+ 8) is a multiple of 4, so the row offset splits into a per-lane part and
+  // a compile-time group offset.
   __device__ __forceinline__ bf16x8 tfrag(int n0, int st, int lane) const {
     const int i = lane & 15, g = lane >> 4, half = lane >> 5;
-    const int base = (4 * half + (i >> 2)) * LD + 16 * (g & 1) + 4 * (i & 3);
+    const int base = half * G + (i >> 2) * RS + 16 * (g & 1) + 4 * (i & 3);
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_i16x4 *)(const_cast<bf16 *>(&a[base + 16 * st * LD + n0])));
+        (lds_i16x4 *)(const_cast<bf16 *>(&a[base + 4 * st * G + n0])));
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_i16x4 *)(const_cast<bf16 *>(&a[base + (16 * st + 8) * LD + n0])));
+        (lds_i16x4 *)(const_cast<bf16 *>(&a[base + (4 * st + 2) * G + n0])));
     const bf16x4 l = __builtin_bit_cast(bf16x4, lo), h = __builtin_bit_cast(bf16x4, hi);
     return bf16x8{l[0], l[1], l[2], l[3], h[0], h[1], h[2], h[3]};
   }
@@ -169,58 +178,88 @@ template <int D> struct Tile<float, D> {
   }
 };
 
-// Wait until this wave's outstanding global loads (and direct-to-LDS writes)
-// have landed: s_waitcnt vmcnt(0), other counters unconstrained.
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Direct global -> LDS loads (gfx950 global_load_lds_dword[x4]): every lane of
+// the wave reads `bytes` bytes at its own global address and the wave writes
+// them to LDS at lds + bytes * lane.  Issued as inline assembly on purpose: the
+// compiler then does not track them, so it neither waits for all of them at
+// every barrier nor before LDS reads it cannot prove independent of them.  The
+// kernels wait for exactly the loads they need with wait_vmem_le<N>() before
+// the barrier that publishes the data.  (Loads the compiler does not see can
+// only make its own in-order vmcnt waits stricter, never looser.)  No other
+// code here uses M0.
+__device__ __forceinline__ unsigned lds_addr(const void *p) {
+  return __builtin_amdgcn_readfirstlane(
+      (unsigned)(size_t)(__attribute__((address_space(3))) const void *)p);
+}
+__device__ __forceinline__ void dma_lds16(void *lds, const void *g) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds_addr(lds)), "v"(g)
+               : "memory");
+}
+__device__ __forceinline__ void dma_lds4(void *lds, const void *g) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               :
+               : "s"(lds_addr(lds)), "v"(g)
+               : "memory");
+}
+
+// s_waitcnt vmcnt(n), other counters unconstrained (n < 16).
+template <int N> __device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+__device__ __forceinline__ void wait_vmem() { wait_vmem_le<0>(); }
 
 // Streams 32-row chunks of a strided [S, D] matrix into a Tile.  issue() starts
 // the transfer of rows [r0, r0 + 32) (rows past the end repeat the last row, so
-// every tile element is finite and no lane branches); complete() must run
-// before the barrier that hands the tile to the other waves.
+// every tile element is finite and no lane branches).  The data must have
+// landed, in every wave, before the barrier that hands the tile over: for bf16
+// that is a vmcnt wait (LOADS = the number of loads one issue() leaves in
+// flight per wave), for fp32 it is complete(), which writes the registers.
 //
 // bf16: gfx950 direct loads (global_load_lds_dwordx4): one instruction writes
 // the 16 bytes of lane i at LDS segment base + 16 i, so each wave fills whole
 // 1 KB segments and lane i fetches whichever row chunk belongs at that slot
-// (pad slots fetch a harmless duplicate).  No registers or LDS writes involved.
-// fp32: a register prefetch written to LDS in complete().
+// (pad slots and the slack past the last row fetch a harmless duplicate).
+// No registers or LDS write instructions are involved.
+// fp32: a register prefetch written to LDS by complete().
 template <typename T, int D> struct ChunkIO;
 
 template <int D> struct ChunkIO<bf16, D> {
   typedef Tile<bf16, D> TileT;
-  static constexpr int MAXJ = (TileT::NSEG + 3) / 4;
-  int rloc[MAXJ], col[MAXJ];
+  static constexpr int LOADS = TileT::NSEG / 4;
+  static constexpr bool DIRECT = true;
+  int rloc[LOADS], col[LOADS];
   int wave;
   __device__ __forceinline__ void init() {
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int j = 0; j < MAXJ; ++j) {
-      const int g = (wave + 4 * j) * 64 + lane;
-      int r = g / TileT::CPR, c = g % TileT::CPR;
-      if (c >= TileT::CH) c = 0;
-      if (r > 31) r = 31;
-      rloc[j] = r;
-      col[j] = 8 * c;
+    for (int j = 0; j < LOADS; ++j) {
+      const int slot = (wave + 4 * j) * 64 + lane;  // 16-byte slot of the tile
+      const int grp = slot / (TileT::G / 8), o = slot % (TileT::G / 8);
+      const int q = o / (TileT::RS / 8), c = o % (TileT::RS / 8);
+      const bool data = grp < 8 && q < 4 && c < D / 8;
+      rloc[j] = data ? 4 * grp + q : 31;
+      col[j] = data ? 8 * c : 0;
     }
   }
   __device__ __forceinline__ void issue(const bf16 *base, int64_t stride, int r0, int nrows,
                                         TileT &t) {
 #pragma unroll
-    for (int j = 0; j < MAXJ; ++j) {
-      const int seg = wave + 4 * j;
-      if (seg < TileT::NSEG) {
-        const int row = min(r0 + rloc[j], nrows - 1);
-        const bf16 *src = base + (int64_t)row * stride + col[j];
-        __builtin_amdgcn_global_load_lds(
-            (const void *)src, (__attribute__((address_space(3))) void *)(&t.a[seg * 512]), 16, 0, 0);
-      }
+    for (int j = 0; j < LOADS; ++j) {
+      const int row = min(r0 + rloc[j], nrows - 1);
+      dma_lds16(&t.a[(wave + 4 * j) * 512], base + (int64_t)row * stride + col[j]);
     }
   }
-  __device__ __forceinline__ void complete(TileT &) { wait_vmem(); }
+  __device__ __forceinline__ void complete(TileT &) {}
 };
 
 template <int D> struct ChunkIO<float, D> {
   typedef Tile<float, D> TileT;
+  static constexpr int LOADS = 0;
+  static constexpr bool DIRECT = false;
   static constexpr int CH = D / 4;  // 16-byte chunks per row
   static constexpr int PER = (32 * CH + 255) / 256;
   f32x4 r[PER];
