@@ -48,17 +48,6 @@ __device__ __forceinline__ void end_step(bool issued) {
   __syncthreads();
 }
 
-// Statistics of the 32 rows of chunk i0 into LDS [lse2 x 32 | delta x 32]: one
-// direct-to-LDS dword load per wave (lane l < 32: lse2 of row i0 + l, lane
-// 32 + l: delta of that row; each wave writes its own copy, so every wave
-// issues the same number of loads).  Rows past Sq repeat the last row; the
-// index mask gives them P = 0 on every tile that holds one.
-__device__ __forceinline__ void issue_row_stats(const DenseParams &p, int64_t srow0, int i0,
-                                                float *st, int wave, int lane) {
-  const int row = min(i0 + (lane & 31), p.Sq - 1);
-  dma_lds4(st + 64 * wave, (lane < 32 ? p.st_lse2 : p.st_delta) + srow0 + row);
-}
-
 // ---------------------------------------------------------------------------
 // Row statistics.
 template <typename T, int D> struct RowStatsState {
@@ -234,13 +223,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ---------------------------------------------------------------------------
-// dK / dV, KV-block-major.
+// dK / dV, KV-block-major.  A step covers ROWS = 32 * NSUB queries as NSUB
+// independent 32-row sub-tiles (two for bf16): their chains of MFMA and VALU
+// work interleave within the wave, and the step's barrier is shared.
+template <typename T> struct KvShape {
+  static constexpr int NSUB = sizeof(T) == 2 ? 2 : 1;
+  static constexpr int ROWS = 32 * NSUB;
+};
+
+// Statistics of the ROWS rows of chunk i0 into LDS, [lse2 x ROWS | delta x ROWS]
+// per wave copy: direct-to-LDS dword loads, each wave writing its own copy so
+// that every wave issues the same number of loads (STAT_LOADS).  Rows past Sq
+// repeat the last row; the index mask gives them P = 0.
+template <int ROWS>
+__device__ __forceinline__ void issue_row_stats(const DenseParams &p, int64_t srow0, int i0,
+                                                float *st, int wave, int lane) {
+  float *dst = st + 2 * ROWS * wave;
+  if constexpr (ROWS == 32) {
+    const int row = min(i0 + (lane & 31), p.Sq - 1);
+    dma_lds4(dst, (lane < 32 ? p.st_lse2 : p.st_delta) + srow0 + row);
+  } else {
+    const int row = min(i0 + lane, p.Sq - 1);
+    dma_lds4(dst, p.st_lse2 + srow0 + row);
+    dma_lds4(dst + 64, p.st_delta + srow0 + row);
+  }
+}
+template <int ROWS> constexpr int stat_loads() { return ROWS == 32 ? 1 : 2; }
+
 template <typename T, int D> struct KvState {
   typedef MT<T> M;
-  static constexpr int NSD = D / M::KS, NT = D / 32;
+  static constexpr int NSD = D / M::KS, NT = D / 32, ROWS = KvShape<T>::ROWS;
   typename M::frag kf[NSD], vf[NSD];
   f32x16 dk[NT], dv[NT];
-  ChunkIO<T, D> io_q, io_g;
+  ChunkIO<T, D, ROWS> io_q, io_g;
   const T *qbase, *gbase;
   int64_t srow0;
   int b, h, jw, kj, wave, lane, l32, half, c_last;
@@ -248,78 +263,104 @@ template <typename T, int D> struct KvState {
 
 template <typename T, int D, int MODE>
 __device__ __forceinline__ void kv_issue(const DenseParams &p, KvState<T, D> &S, int c,
-                                         Tile<T, D> *Q, Tile<T, D> *G, float *st) {
-  S.io_q.issue(S.qbase, p.qs[1], c * 32, p.Sq, *Q);
-  S.io_g.issue(S.gbase, p.dys[1], c * 32, p.Sq, *G);
-  issue_row_stats(p, S.srow0, c * 32, st, S.wave, S.lane);
+                                         Tile<T, D, KvShape<T>::ROWS> *Q,
+                                         Tile<T, D, KvShape<T>::ROWS> *G, float *st) {
+  constexpr int ROWS = KvShape<T>::ROWS;
+  S.io_q.issue(S.qbase, p.qs[1], c * ROWS, p.Sq, *Q);
+  S.io_g.issue(S.gbase, p.dys[1], c * ROWS, p.Sq, *G);
+  issue_row_stats<ROWS>(p, S.srow0, c * ROWS, st, S.wave, S.lane);
 }
 
 template <typename T, int D, int MODE>
 __device__ __forceinline__ void kv_step(const DenseParams &p, KvState<T, D> &S, int c,
-                                        const Tile<T, D> *Qc, const Tile<T, D> *Gc,
-                                        const float *st_c, int cn, Tile<T, D> *Qn, Tile<T, D> *Gn,
-                                        float *st_n) {
+                                        const Tile<T, D, KvShape<T>::ROWS> *Qc,
+                                        const Tile<T, D, KvShape<T>::ROWS> *Gc,
+                                        const float *st_c, int cn,
+                                        Tile<T, D, KvShape<T>::ROWS> *Qn,
+                                        Tile<T, D, KvShape<T>::ROWS> *Gn, float *st_n) {
   typedef MT<T> M;
   constexpr int NSD = D / M::KS, NT = D / 32, CS = M::CSTEPS;
-  const int i0 = c * 32;
+  constexpr int NSUB = KvShape<T>::NSUB, ROWS = KvShape<T>::ROWS;
+  constexpr int PER_CHUNK = 2 * ChunkIO<T, D, ROWS>::LOADS + stat_loads<ROWS>();
+  const int i0 = c * ROWS;
   const bool issued = cn <= S.c_last;
   if (issued) kv_issue<T, D, MODE>(p, S, cn, Qn, Gn, st_n);
-  const bool check = MODE != MODE_INDEX || !tile_all_visible(p, i0, S.jw);
-  // S = Q K^T and dP = dY V^T: rows = queries (A from LDS), columns = this lane's key.
-  typename M::frag qa[NSD], ga[NSD];
-#pragma unroll
-  for (int s = 0; s < NSD; ++s) {
-    qa[s] = Qc->frag(S.l32, s, S.half);
-    ga[s] = Gc->frag(S.l32, s, S.half);
-  }
-  f32x16 sacc = f32x16{}, pacc = f32x16{};
-#pragma unroll
-  for (int s = 0; s < NSD; ++s) {
-    sacc = M::mma(qa[s], S.kf[s], sacc);
-    pacc = M::mma(ga[s], S.vf[s], pacc);
-  }
-  float sc[16];
   const int kj = S.kj, half = S.half;
-  scores16<MODE>(p, sacc, sc, S.b, S.h, check, [&](int r) { return i0 + kr(r, half); },
-                 [&](int) { return kj; });
-  float pv[16], dsv[16];
+
+  // S = Q K^T and dP = dY V^T per sub-tile: rows = queries (A from LDS),
+  // columns = this lane's key.
+  f32x16 sacc[NSUB], pacc[NSUB];
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const f32x4 lse4 = *reinterpret_cast<const f32x4 *>(&st_c[8 * g + 4 * half]);
-    const f32x4 del4 = *reinterpret_cast<const f32x4 *>(&st_c[32 + 8 * g + 4 * half]);
+  for (int u = 0; u < NSUB; ++u) {
+    typename M::frag qa[NSD], ga[NSD];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 4 * g + e;
-      const float pr = fast_exp2(sc[r] - lse4[e]);
-      pv[r] = pr;
-      dsv[r] = pr * (pacc[r] - del4[e]) * p.scale;
+    for (int s = 0; s < NSD; ++s) {
+      qa[s] = Qc->frag(32 * u + S.l32, s, S.half);
+      ga[s] = Gc->frag(32 * u + S.l32, s, S.half);
+    }
+    sacc[u] = f32x16{};
+    pacc[u] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < NSD; ++s) {
+      sacc[u] = M::mma(qa[s], S.kf[s], sacc[u]);
+      pacc[u] = M::mma(ga[s], S.vf[s], pacc[u]);
+    }
+  }
+  // P and dS (the statistics of wave 0's copy).
+  typename M::frag pf[NSUB][CS], sf[NSUB][CS];
+#pragma unroll
+  for (int u = 0; u < NSUB; ++u) {
+    const bool check = MODE != MODE_INDEX || !tile_all_visible(p, i0 + 32 * u, S.jw);
+    float sc[16], pv[16], dsv[16];
+    scores16<MODE>(p, sacc[u], sc, S.b, S.h, check,
+                   [&](int r) { return i0 + 32 * u + kr(r, half); }, [&](int) { return kj; });
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 lse4 = *reinterpret_cast<const f32x4 *>(&st_c[32 * u + 8 * g + 4 * half]);
+      const f32x4 del4 = *reinterpret_cast<const f32x4 *>(&st_c[ROWS + 32 * u + 8 * g + 4 * half]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * g + e;
+        const float pr = fast_exp2(sc[r] - lse4[e]);
+        pv[r] = pr;
+        dsv[r] = pr * (pacc[u][r] - del4[e]) * p.scale;
+      }
+    }
+#pragma unroll
+    for (int st = 0; st < CS; ++st) {
+      pf[u][st] = creuse<T>(pv, st);
+      sf[u][st] = creuse<T>(dsv, st);
     }
   }
   // dV^T += dY^T P and dK^T += Q^T dS: A = rows read transposed from LDS, B = C reuse.
 #pragma unroll
-  for (int st = 0; st < CS; ++st) {
-    const typename M::frag pf = creuse<T>(pv, st);
-    const typename M::frag sf = creuse<T>(dsv, st);
+  for (int u = 0; u < NSUB; ++u)
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      S.dv[t] = M::mma(Gc->tfrag(32 * t, st, S.lane), pf, S.dv[t]);
-      S.dk[t] = M::mma(Qc->tfrag(32 * t, st, S.lane), sf, S.dk[t]);
-    }
-  }
+    for (int st = 0; st < CS; ++st)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        S.dv[t] = M::mma(Gc->tfrag(32 * t, st, S.lane, 32 * u), pf[u][st], S.dv[t]);
+        S.dk[t] = M::mma(Qc->tfrag(32 * t, st, S.lane, 32 * u), sf[u][st], S.dk[t]);
+      }
   if (issued) {
     S.io_q.complete(*Qn);
     S.io_g.complete(*Gn);
   }
-  end_step<ChunkIO<T, D>::DIRECT, 2 * ChunkIO<T, D>::LOADS + 1>(issued);
+  end_step<ChunkIO<T, D, ROWS>::DIRECT, PER_CHUNK>(issued);
 }
 
 template <typename T, int D, int MODE>
 __device__ __forceinline__ void kv_run(const DenseParams &p, KvState<T, D> &S, int c_first,
-                                       Tile<T, D> *__restrict__ Q0, Tile<T, D> *__restrict__ Q1,
-                                       Tile<T, D> *__restrict__ Q2, Tile<T, D> *__restrict__ G0,
-                                       Tile<T, D> *__restrict__ G1, Tile<T, D> *__restrict__ G2,
+                                       Tile<T, D, KvShape<T>::ROWS> *__restrict__ Q0,
+                                       Tile<T, D, KvShape<T>::ROWS> *__restrict__ Q1,
+                                       Tile<T, D, KvShape<T>::ROWS> *__restrict__ Q2,
+                                       Tile<T, D, KvShape<T>::ROWS> *__restrict__ G0,
+                                       Tile<T, D, KvShape<T>::ROWS> *__restrict__ G1,
+                                       Tile<T, D, KvShape<T>::ROWS> *__restrict__ G2,
                                        float *__restrict__ s0, float *__restrict__ s1,
                                        float *__restrict__ s2) {
+  constexpr int ROWS = KvShape<T>::ROWS;
+  constexpr int PER_CHUNK = 2 * ChunkIO<T, D, ROWS>::LOADS + stat_loads<ROWS>();
   const int c_last = S.c_last;
   if (c_first <= c_last) {
     kv_issue<T, D, MODE>(p, S, c_first, Q0, G0, s0);
@@ -332,7 +373,7 @@ __device__ __forceinline__ void kv_run(const DenseParams &p, KvState<T, D> &S, i
     S.io_q.complete(*Q1);
     S.io_g.complete(*G1);
   }
-  end_step<ChunkIO<T, D>::DIRECT, 2 * ChunkIO<T, D>::LOADS + 1>(second);
+  end_step<ChunkIO<T, D, ROWS>::DIRECT, PER_CHUNK>(second);
   int c = c_first;
   for (; c + 2 <= c_last; c += 3) {
     kv_step<T, D, MODE>(p, S, c, Q0, G0, s0, c + 2, Q2, G2, s2);
@@ -346,9 +387,9 @@ __device__ __forceinline__ void kv_run(const DenseParams &p, KvState<T, D> &S, i
 template <typename T, int D, int MODE>
 __global__ __launch_bounds__(256) void k_kv_bwd(const DenseParams p) {
   typedef MT<T> M;
-  constexpr int KS = M::KS, KL = M::KL, NSD = D / KS, NT = D / 32;
-  __shared__ Tile<T, D> Qs0, Qs1, Qs2, Gs0, Gs1, Gs2;
-  __shared__ __attribute__((aligned(16))) float st0[256], st1[256], st2[256];
+  constexpr int KS = M::KS, KL = M::KL, NSD = D / KS, NT = D / 32, ROWS = KvShape<T>::ROWS;
+  __shared__ Tile<T, D, ROWS> Qs0, Qs1, Qs2, Gs0, Gs1, Gs2;
+  __shared__ __attribute__((aligned(16))) float st0[8 * ROWS], st1[8 * ROWS], st2[8 * ROWS];
 
   KvState<T, D> S;
   const int w = threadIdx.x >> 6;
@@ -381,8 +422,8 @@ __global__ __launch_bounds__(256) void k_kv_bwd(const DenseParams p) {
   const int jlast = min(j0b + 128, p.Sk) - 1;
   const int ilo = max(0, (int)max((int64_t)j0b - p.hi_off, (int64_t)0));
   const int ihi = min(p.Sq - 1, (int)min((int64_t)jlast - p.lo_off, (int64_t)kBig));
-  const int c_first = ilo >> 5;
-  S.c_last = ihi >= ilo ? ihi >> 5 : c_first - 1;
+  const int c_first = ilo / ROWS;
+  S.c_last = ihi >= ilo ? ihi / ROWS : c_first - 1;
 
 #pragma unroll
   for (int t = 0; t < NT; ++t) S.dk[t] = S.dv[t] = f32x16{};

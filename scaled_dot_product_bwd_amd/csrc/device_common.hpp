@@ -112,7 +112,7 @@ __device__ __forceinline__ float creuse<float>(const float *v, int st) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS tile holding one 32-row chunk of a strided [S, D] matrix.
+// LDS tile holding one 32- or 64-row chunk of a strided [S, D] matrix.
 //
 // bf16: rows are laid out in groups of four, row r at byte offset
 // (r / 4) * G + (r % 4) * RS.  gfx950 LDS has 64 banks of 4 bytes; it serves a
@@ -130,12 +130,12 @@ __device__ __forceinline__ float creuse<float>(const float *v, int st) {
 //
 // fp32: rows of D + 1 floats; 32 lanes reading one column of 32 rows hit 32
 // different banks.
-template <typename T, int D> struct Tile;
+template <typename T, int D, int ROWS = 32> struct Tile;
 
-template <int D> struct Tile<bf16, D> {
+template <int D, int ROWS> struct Tile<bf16, D, ROWS> {
   static constexpr int RS = D == 128 ? 160 : (D == 64 ? 96 : 32);   // row stride in a group, elements
   static constexpr int G = D == 128 ? 616 : (D == 64 ? 360 : 136);  // group stride, elements
-  static constexpr int SLOTS = 8 * G / 8;                            // 16-byte slots of 8 groups
+  static constexpr int SLOTS = ROWS / 4 * G / 8;                     // 16-byte slots of all groups
   static constexpr int NSEG = ((SLOTS + 63) / 64 + 3) / 4 * 4;       // 1 KB load segments
   bf16 a[NSEG * 512];
   __device__ __forceinline__ static constexpr int row_off(int r) { return (r >> 2) * G + (r & 3) * RS; }
@@ -143,29 +143,30 @@ template <int D> struct Tile<bf16, D> {
   __device__ __forceinline__ bf16x8 frag(int r, int s, int half) const {
     return *reinterpret_cast<const bf16x8 *>(&a[row_off(r) + 16 * s + 8 * half]);
   }
-  // A operand of a C-reuse product: column n0 + (lane's n), rows kidx(st, half, e).
+  // A operand of a C-reuse product: column n0 + (lane's n), rows
+  // r0 + kidx(st, half, e) (r0 a multiple of 32).
   // ds_read_b64_tr_b16 hands lane i of each 16-lane group element i % 4 of the
   // 8 bytes addressed by lanes i / 4 + 4 e (e = 0..3); so lane i addresses row
   // rowbase + i / 4, columns colbase + 4 (i % 4) .. + 3, and receives rows
-  // rowbase .. rowbase + 3 of column colbase + i.  rowbase = 16 st + 4 half
-  // (+ 8) is a multiple of 4, so the row offset splits into a per-lane part and
-  // a compile-time group offset.
-  __device__ __forceinline__ bf16x8 tfrag(int n0, int st, int lane) const {
+  // rowbase .. rowbase + 3 of column colbase + i.  rowbase = r0 + 16 st +
+  // 4 half (+ 8) is a multiple of 4, so the row offset splits into a per-lane
+  // part and a compile-time group offset.
+  __device__ __forceinline__ bf16x8 tfrag(int n0, int st, int lane, int r0 = 0) const {
     const int i = lane & 15, g = lane >> 4, half = lane >> 5;
     const int base = half * G + (i >> 2) * RS + 16 * (g & 1) + 4 * (i & 3);
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_i16x4 *)(const_cast<bf16 *>(&a[base + 4 * st * G + n0])));
+        (lds_i16x4 *)(const_cast<bf16 *>(&a[base + (r0 / 4 + 4 * st) * G + n0])));
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_i16x4 *)(const_cast<bf16 *>(&a[base + (4 * st + 2) * G + n0])));
+        (lds_i16x4 *)(const_cast<bf16 *>(&a[base + (r0 / 4 + 4 * st + 2) * G + n0])));
     const bf16x4 l = __builtin_bit_cast(bf16x4, lo), h = __builtin_bit_cast(bf16x4, hi);
     return bf16x8{l[0], l[1], l[2], l[3], h[0], h[1], h[2], h[3]};
   }
 };
 
-template <int D> struct Tile<float, D> {
+template <int D, int ROWS> struct Tile<float, D, ROWS> {
   static constexpr int LD = D + 1;
-  float a[32 * LD];
+  float a[ROWS * LD];
   __device__ __forceinline__ void put(int r, int c, f32x4 x) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) a[r * LD + 4 * c + e] = x[e];
@@ -173,8 +174,8 @@ template <int D> struct Tile<float, D> {
   __device__ __forceinline__ float frag(int r, int s, int half) const {
     return a[r * LD + 2 * s + half];
   }
-  __device__ __forceinline__ float tfrag(int n0, int st, int lane) const {
-    return a[kr(st, lane >> 5) * LD + n0 + (lane & 31)];
+  __device__ __forceinline__ float tfrag(int n0, int st, int lane, int r0 = 0) const {
+    return a[(r0 + kr(st, lane >> 5)) * LD + n0 + (lane & 31)];
   }
 };
 
@@ -211,8 +212,8 @@ template <int N> __device__ __forceinline__ void wait_vmem_le() {
 }
 __device__ __forceinline__ void wait_vmem() { wait_vmem_le<0>(); }
 
-// Streams 32-row chunks of a strided [S, D] matrix into a Tile.  issue() starts
-// the transfer of rows [r0, r0 + 32) (rows past the end repeat the last row, so
+// Streams ROWS-row chunks of a strided [S, D] matrix into a Tile.  issue() starts
+// the transfer of rows [r0, r0 + ROWS) (rows past the end repeat the last row, so
 // every tile element is finite and no lane branches).  The data must have
 // landed, in every wave, before the barrier that hands the tile over: for bf16
 // that is a vmcnt wait (LOADS = the number of loads one issue() leaves in
@@ -224,10 +225,10 @@ __device__ __forceinline__ void wait_vmem() { wait_vmem_le<0>(); }
 // (pad slots and the slack past the last row fetch a harmless duplicate).
 // No registers or LDS write instructions are involved.
 // fp32: a register prefetch written to LDS by complete().
-template <typename T, int D> struct ChunkIO;
+template <typename T, int D, int ROWS = 32> struct ChunkIO;
 
-template <int D> struct ChunkIO<bf16, D> {
-  typedef Tile<bf16, D> TileT;
+template <int D, int ROWS> struct ChunkIO<bf16, D, ROWS> {
+  typedef Tile<bf16, D, ROWS> TileT;
   static constexpr int LOADS = TileT::NSEG / 4;
   static constexpr bool DIRECT = true;
   int rloc[LOADS], col[LOADS];
@@ -240,8 +241,8 @@ template <int D> struct ChunkIO<bf16, D> {
       const int slot = (wave + 4 * j) * 64 + lane;  // 16-byte slot of the tile
       const int grp = slot / (TileT::G / 8), o = slot % (TileT::G / 8);
       const int q = o / (TileT::RS / 8), c = o % (TileT::RS / 8);
-      const bool data = grp < 8 && q < 4 && c < D / 8;
-      rloc[j] = data ? 4 * grp + q : 31;
+      const bool data = grp < ROWS / 4 && q < 4 && c < D / 8;
+      rloc[j] = data ? 4 * grp + q : ROWS - 1;
       col[j] = data ? 8 * c : 0;
     }
   }
@@ -256,12 +257,12 @@ template <int D> struct ChunkIO<bf16, D> {
   __device__ __forceinline__ void complete(TileT &) {}
 };
 
-template <int D> struct ChunkIO<float, D> {
-  typedef Tile<float, D> TileT;
+template <int D, int ROWS> struct ChunkIO<float, D, ROWS> {
+  typedef Tile<float, D, ROWS> TileT;
   static constexpr int LOADS = 0;
   static constexpr bool DIRECT = false;
   static constexpr int CH = D / 4;  // 16-byte chunks per row
-  static constexpr int PER = (32 * CH + 255) / 256;
+  static constexpr int PER = (ROWS * CH + 255) / 256;
   f32x4 r[PER];
   __device__ __forceinline__ void init() {}
   __device__ __forceinline__ void issue(const float *base, int64_t stride, int r0, int nrows,
@@ -270,7 +271,7 @@ template <int D> struct ChunkIO<float, D> {
     for (int j = 0; j < PER; ++j) {
       const int id = threadIdx.x + 256 * j;
       const int row = min(r0 + id / CH, nrows - 1), c = id % CH;
-      r[j] = (32 * CH % 256 == 0 || id < 32 * CH)
+      r[j] = (ROWS * CH % 256 == 0 || id < ROWS * CH)
                  ? *reinterpret_cast<const f32x4 *>(base + (int64_t)row * stride + 4 * c)
                  : f32x4{};
     }
@@ -279,7 +280,7 @@ template <int D> struct ChunkIO<float, D> {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int id = threadIdx.x + 256 * j;
-      if (32 * CH % 256 == 0 || id < 32 * CH) t.put(id / CH, id % CH, r[j]);
+      if (ROWS * CH % 256 == 0 || id < ROWS * CH) t.put(id / CH, id % CH, r[j]);
     }
   }
 };
