@@ -120,6 +120,73 @@ int attn_bwd_row_stats(const attn_bwd_args *a, void *stream);
 int attn_bwd_kv(const attn_bwd_args *a, void *stream);
 int attn_bwd_dq(const attn_bwd_args *a, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Paged, grouped-query history backward (dK / dV only), ruDNN 0.1.43
+ * src/paged_attention/ordered_kernel.rs `history_backward`.
+ *
+ * Sequence s has seq_lens[s] tokens; its token t lives in pool slot
+ * block_table[s * max_pages_per_seq + t / page_size] * page_size + t % page_size.
+ * Query row r (0 <= r < nq, rows packed in any order) belongs to sequence
+ * query_seq[r] at position query_pos[r]; with `causal` it sees the tokens
+ * t <= query_pos[r] of its sequence, otherwise all of them.  Query head h
+ * reads KV head h / (heads / kv_heads).  For every (slot, KV head g) of every
+ * listed page (a page some sequence reaches below its length):
+ *   dK[slot, g] = sum over links (s, logical page) of the page, rows r of s
+ *                 that see the slot's token, heads h of group g, with
+ *                 denominator l > 0:  ds * q[r, h]
+ *   dV[slot, g] = ... same sum of p * dY[r, h]
+ *   p  = exp(scale * q[r,h] . k[slot,g] - m) / l,
+ *   ds = p * (dY[r,h] . v[slot,g] - delta) * scale,
+ * with (m, l, delta) = stats[r, h, 0..2] (supplied, as on the pages).  Tail
+ * slots of listed pages get +0; slots of unlisted pages are left untouched.
+ * K / V rows of slots no link reaches are never read (they may hold NaN).
+ * Each output element is written once, by one workgroup, in a fixed order.
+ *
+ * Host planning is split from the launch (the pages prepare their page and
+ * row tables on the host too): attn_bwd_paged_plan_words() bounds the plan
+ * size, attn_bwd_paged_plan_build() fills host int32 words, the caller copies
+ * them to device memory and passes both copies to attn_bwd_paged().  A plan
+ * may be reused for any call with the same tables and geometry. */
+
+/* Upper bound on the int32 words of a plan, or -1 (see attn_bwd_last_error)
+ * for inconsistent sizes.  seq_lens: host [nseq]. */
+int64_t attn_bwd_paged_plan_words(int32_t nseq, const int32_t *seq_lens, int32_t max_pages_per_seq,
+                                  int32_t nq, int32_t heads, int32_t kv_heads, int32_t page_size,
+                                  int32_t pool_pages);
+
+/* Builds the plan into plan_out (host, plan_words words).  All arrays are host
+ * memory: seq_lens [nseq], block_table [nseq, max_pages_per_seq] (only the
+ * first ceil(len / page_size) entries of a row are read; each in
+ * [0, pool_pages)), query_seq / query_pos [nq] (query_seq in [0, nseq),
+ * query_pos >= 0).  Word 1 of the result is the number of words used.
+ * ATTN_E_INVALID on any inconsistency; nothing is enqueued anywhere. */
+int attn_bwd_paged_plan_build(int32_t nseq, const int32_t *seq_lens, const int32_t *block_table,
+                              int32_t max_pages_per_seq, int32_t nq, const int32_t *query_seq,
+                              const int32_t *query_pos, int32_t heads, int32_t kv_heads,
+                              int32_t page_size, int32_t pool_pages, int32_t *plan_out,
+                              int64_t plan_words);
+
+typedef struct attn_bwd_paged_args {
+  int32_t dtype;      /* ATTN_F32 or ATTN_BF16: q, dy, pools and gradient pools */
+  int32_t need;       /* bit 0: dK, bit 1: dV (at least one) */
+  int32_t heads, kv_heads, head_dim, page_size, causal; /* head_dim in {32, 64, 128}; causal 0 / 1 */
+  int32_t nq, pool_pages;                /* must match the plan */
+  float scale;                           /* finite */
+  const void *q, *dy;                    /* device [nq, heads, head_dim], contiguous */
+  const void *k_pool, *v_pool;           /* device [pool_pages * page_size, kv_heads, head_dim] */
+  const float *stats;                    /* device [nq, heads, 3] = (max, denominator, delta) */
+  const int32_t *plan_host;              /* host plan words (read during the call) */
+  const int32_t *plan;                   /* device copy of the same words (read by the kernel) */
+  void *dk_pool, *dv_pool;               /* device, same shape as the pools; written only at
+                                            slots of listed pages; NULL allowed iff not in `need` */
+} attn_bwd_paged_args;
+
+/* Enqueues the paged backward.  Every device pointer must be 16-byte aligned;
+ * the gradient pools may not overlap any input or each other.  The device plan
+ * must be an unmodified copy of plan_host (it is trusted: its tables address
+ * the pools).  A plan with no item does nothing. */
+int attn_bwd_paged(const attn_bwd_paged_args *a, void *stream);
+
 /* Thread-local description of the last non-OK status returned on this thread. */
 const char *attn_bwd_last_error(void);
 

@@ -50,9 +50,9 @@ def _load():
     paged = [i32, _ip, _ip, i32, i32, _ip, _ip, i32, i32, i32, i32, i32, i32, dbl,
              _dp, _dp, _dp, _dp]
     lib.oracle_paged_row_stats.restype = ctypes.c_int
-    lib.oracle_paged_row_stats.argtypes = paged + [_dp]
+    lib.oracle_paged_row_stats.argtypes = paged + [_dp, ctypes.c_int]
     lib.oracle_paged_kv_bwd.restype = ctypes.c_int
-    lib.oracle_paged_kv_bwd.argtypes = paged + [_dp, _dp, _dp]
+    lib.oracle_paged_kv_bwd.argtypes = paged + [_dp, _dp, _dp, ctypes.c_int]
     _lib = lib
     return lib
 
@@ -131,7 +131,7 @@ def _paged_common(w):
 
 
 def paged_row_stats(w, q, dy, k_pool, v_pool, *, heads, kv_heads, page_size,
-                    causal=True, scale=None):
+                    causal=True, scale=None, nthreads=None):
     """(max, denominator, delta) per (row, head) for the paged layout, shape [nq, heads, 3]."""
     seq_lens, bt, nseq, max_pages, qs, qp = _paged_common(w)
     q, dy, kp, vp = _f64(q), _f64(dy), _f64(k_pool), _f64(v_pool)
@@ -143,14 +143,15 @@ def paged_row_stats(w, q, dy, k_pool, v_pool, *, heads, kv_heads, page_size,
     rc = _load().oracle_paged_row_stats(
         nseq, _ptr(seq_lens, _ip), _ptr(bt, _ip), max_pages, nq, _ptr(qs, _ip),
         _ptr(qp, _ip), heads, kv_heads, D, page_size, pool_pages, int(bool(causal)),
-        float(scale), _ptr(q), _ptr(dy), _ptr(kp), _ptr(vp), _ptr(stats))
+        float(scale), _ptr(q), _ptr(dy), _ptr(kp), _ptr(vp), _ptr(stats),
+        int(nthreads or default_threads()))
     if rc != 0:
         raise ValueError(f"oracle_paged_row_stats rejected its arguments (rc={rc})")
     return stats
 
 
 def paged_kv_bwd(w, q, dy, k_pool, v_pool, stats, dk_init, dv_init, *, heads,
-                 kv_heads, page_size, causal=True, scale=None):
+                 kv_heads, page_size, causal=True, scale=None, nthreads=None):
     """dK, dV pools: listed pages' slots overwritten, all other slots = the *_init contents."""
     seq_lens, bt, nseq, max_pages, qs, qp = _paged_common(w)
     q, dy, kp, vp, st = _f64(q), _f64(dy), _f64(k_pool), _f64(v_pool), _f64(stats)
@@ -162,7 +163,8 @@ def paged_kv_bwd(w, q, dy, k_pool, v_pool, stats, dk_init, dv_init, *, heads,
     rc = _load().oracle_paged_kv_bwd(
         nseq, _ptr(seq_lens, _ip), _ptr(bt, _ip), max_pages, nq, _ptr(qs, _ip),
         _ptr(qp, _ip), heads, kv_heads, D, page_size, pool_pages, int(bool(causal)),
-        float(scale), _ptr(q), _ptr(dy), _ptr(kp), _ptr(vp), _ptr(st), _ptr(dk), _ptr(dv))
+        float(scale), _ptr(q), _ptr(dy), _ptr(kp), _ptr(vp), _ptr(st), _ptr(dk), _ptr(dv),
+        int(nthreads or default_threads()))
     if rc != 0:
         raise ValueError(f"oracle_paged_kv_bwd rejected its arguments (rc={rc})")
     return dk, dv

@@ -292,45 +292,74 @@ static int paged_check(int nseq, const int32_t *seq_lens, const int32_t *block_t
   return 0;
 }
 
-/* Row statistics (max, denominator, delta) for the paged layout, from the
- * definition: the row's visible scores, their softmax, and delta = sum_t P dP.
- * [ruDNN] takes these as an input computed "once by the query kernel". */
-int oracle_paged_row_stats(int nseq, const int32_t *seq_lens, const int32_t *block_table,
-                           int max_pages, int nq, const int32_t *query_seq,
-                           const int32_t *query_pos, int heads, int kv_heads, int D,
-                           int page_size, int pool_pages, int causal, double scale,
-                           const double *q, const double *dy, const double *k_pool,
-                           const double *v_pool, double *stats) {
-  if (paged_check(nseq, seq_lens, block_table, max_pages, nq, query_seq, heads, kv_heads,
-                  page_size, pool_pages))
-    return -1;
-  const int group = heads / kv_heads;
+typedef struct {
+  int nseq, max_pages, nq, heads, kv_heads, D, page_size, pool_pages, causal;
+  const int32_t *seq_lens, *block_table, *query_seq, *query_pos;
+  double scale;
+  const double *q, *dy, *k_pool, *v_pool, *stats_in;
+  double *stats_out;  /* row statistics (paged_row_stats) */
+  double *gk, *gv;    /* gradient accumulators over the whole pool (paged_kv_bwd) */
+  int64_t next, count; /* work counter shared by threads */
+  pthread_mutex_t lock;
+} paged_job;
+
+static int64_t paged_take(paged_job *J) {
+  pthread_mutex_lock(&J->lock);
+  const int64_t i = J->next++;
+  pthread_mutex_unlock(&J->lock);
+  return i < J->count ? i : -1;
+}
+
+static int64_t paged_slot(const paged_job *J, int s, int t) {
+  return (int64_t)J->block_table[(int64_t)s * J->max_pages + t / J->page_size] * J->page_size +
+         t % J->page_size;
+}
+
+/* Runs `worker` on `nthreads` threads (the caller included). */
+static void paged_parallel(paged_job *J, void *(*worker)(void *), int nthreads) {
+  pthread_mutex_init(&J->lock, NULL);
+  J->next = 0;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > J->count) nthreads = J->count > 0 ? (int)J->count : 1;
+  pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * nthreads);
+  int started = 0;
+  for (int t = 1; t < nthreads; ++t)
+    if (th && pthread_create(&th[started], NULL, worker, J) == 0) ++started;
+  worker(J);
+  for (int t = 0; t < started; ++t) pthread_join(th[t], NULL);
+  free(th);
+  pthread_mutex_destroy(&J->lock);
+}
+
+/* One query row r, every head: its visible scores, their softmax, and
+ * delta = sum_t P dP, straight from the definition. */
+static void *paged_stats_worker(void *arg) {
+  paged_job *J = (paged_job *)arg;
+  const int D = J->D, group = J->heads / J->kv_heads;
   int maxlen = 1;
-  for (int s = 0; s < nseq; ++s)
-    if (seq_lens[s] > maxlen) maxlen = seq_lens[s];
+  for (int s = 0; s < J->nseq; ++s)
+    if (J->seq_lens[s] > maxlen) maxlen = J->seq_lens[s];
   double *sc = (double *)malloc(sizeof(double) * maxlen);
   double *dp = (double *)malloc(sizeof(double) * maxlen);
   unsigned char *vis = (unsigned char *)malloc(maxlen);
-  if (!sc || !dp || !vis) { free(sc); free(dp); free(vis); return -1; }
-  for (int r = 0; r < nq; ++r) {
-    const int s = query_seq[r];
-    const int len = seq_lens[s];
-    for (int h = 0; h < heads; ++h) {
+  for (int64_t r; sc && dp && vis && (r = paged_take(J)) >= 0;) {
+    const int s = J->query_seq[r];
+    const int len = J->seq_lens[s];
+    for (int h = 0; h < J->heads; ++h) {
       const int g = h / group;
-      const double *qr = q + ((int64_t)r * heads + h) * D;
-      const double *gr = dy + ((int64_t)r * heads + h) * D;
+      const double *qr = J->q + (r * J->heads + h) * D;
+      const double *gr = J->dy + (r * J->heads + h) * D;
       double mx = -INFINITY;
       int any = 0;
       for (int t = 0; t < len; ++t) {
-        const int64_t slot = (int64_t)block_table[(int64_t)s * max_pages + t / page_size] * page_size +
-                             t % page_size;
-        const double *kr = k_pool + (slot * kv_heads + g) * D;
-        const double *vr = v_pool + (slot * kv_heads + g) * D;
+        const int64_t slot = paged_slot(J, s, t);
+        const double *kr = J->k_pool + (slot * J->kv_heads + g) * D;
+        const double *vr = J->v_pool + (slot * J->kv_heads + g) * D;
         double a = 0.0, c = 0.0;
         for (int d = 0; d < D; ++d) { a += qr[d] * kr[d]; c += gr[d] * vr[d]; }
-        sc[t] = scale * a;
+        sc[t] = J->scale * a;
         dp[t] = c;
-        vis[t] = (unsigned char)(!causal || t <= query_pos[r]);
+        vis[t] = (unsigned char)(!J->causal || t <= J->query_pos[r]);
         if (vis[t]) { any = 1; if (sc[t] > mx) mx = sc[t]; }
       }
       double den = 0.0, delta = 0.0;
@@ -338,31 +367,90 @@ int oracle_paged_row_stats(int nseq, const int32_t *seq_lens, const int32_t *blo
         for (int t = 0; t < len; ++t) if (vis[t]) den += exp(sc[t] - mx);
         for (int t = 0; t < len; ++t) if (vis[t]) delta += exp(sc[t] - mx) / den * dp[t];
       }
-      double *st = stats + ((int64_t)r * heads + h) * 3;
+      double *st = J->stats_out + (r * J->heads + h) * 3;
       st[0] = any ? mx : -INFINITY;
       st[1] = den;
       st[2] = delta;
     }
   }
   free(sc); free(dp); free(vis);
+  return NULL;
+}
+
+/* Row statistics (max, denominator, delta) for the paged layout, from the
+ * definition: the row's visible scores, their softmax, and delta = sum_t P dP.
+ * [ruDNN] takes these as an input computed "once by the query kernel".
+ * Rows are independent; threads split them. */
+int oracle_paged_row_stats(int nseq, const int32_t *seq_lens, const int32_t *block_table,
+                           int max_pages, int nq, const int32_t *query_seq,
+                           const int32_t *query_pos, int heads, int kv_heads, int D,
+                           int page_size, int pool_pages, int causal, double scale,
+                           const double *q, const double *dy, const double *k_pool,
+                           const double *v_pool, double *stats, int nthreads) {
+  if (paged_check(nseq, seq_lens, block_table, max_pages, nq, query_seq, heads, kv_heads,
+                  page_size, pool_pages))
+    return -1;
+  paged_job J;
+  memset(&J, 0, sizeof J);
+  J.nseq = nseq; J.max_pages = max_pages; J.nq = nq; J.heads = heads; J.kv_heads = kv_heads;
+  J.D = D; J.page_size = page_size; J.pool_pages = pool_pages; J.causal = causal;
+  J.seq_lens = seq_lens; J.block_table = block_table; J.query_seq = query_seq;
+  J.query_pos = query_pos; J.scale = scale;
+  J.q = q; J.dy = dy; J.k_pool = k_pool; J.v_pool = v_pool; J.stats_out = stats;
+  J.count = nq;
+  paged_parallel(&J, paged_stats_worker, nthreads);
   return 0;
+}
+
+/* All contributions to the slots of one KV head g, in a fixed order:
+ * sequences, then tokens, then query rows, then the group's heads. */
+static void *paged_kv_worker(void *arg) {
+  paged_job *J = (paged_job *)arg;
+  const int D = J->D, group = J->heads / J->kv_heads;
+  for (int64_t g; (g = paged_take(J)) >= 0;) {
+    for (int s = 0; s < J->nseq; ++s) {
+      const int len = J->seq_lens[s];
+      for (int t = 0; t < len; ++t) {
+        const int64_t slot = paged_slot(J, s, t);
+        for (int r = 0; r < J->nq; ++r) {
+          if (J->query_seq[r] != s) continue;
+          if (J->causal && t > J->query_pos[r]) continue;
+          for (int h = (int)g * group; h < ((int)g + 1) * group; ++h) {
+            const double *st = J->stats_in + ((int64_t)r * J->heads + h) * 3;
+            if (st[1] == 0.0) continue;
+            const double *qr = J->q + ((int64_t)r * J->heads + h) * D;
+            const double *gr = J->dy + ((int64_t)r * J->heads + h) * D;
+            const double *kr = J->k_pool + (slot * J->kv_heads + g) * D;
+            const double *vr = J->v_pool + (slot * J->kv_heads + g) * D;
+            double a = 0.0, c = 0.0;
+            for (int d = 0; d < D; ++d) { a += qr[d] * kr[d]; c += gr[d] * vr[d]; }
+            const double p = exp(J->scale * a - st[0]) / st[1];
+            const double ds = p * (c - st[2]) * J->scale;
+            double *ak = J->gk + (slot * J->kv_heads + g) * D;
+            double *av = J->gv + (slot * J->kv_heads + g) * D;
+            for (int d = 0; d < D; ++d) { ak[d] += ds * qr[d]; av[d] += p * gr[d]; }
+          }
+        }
+      }
+    }
+  }
+  return NULL;
 }
 
 /* dK / dV into the page pools.  `dk_pool` / `dv_pool` hold the caller's pool
  * contents on entry (either may be NULL: not requested); on return every slot of
  * every listed page holds its gradient (zero where no row sees it) and every
- * other slot is unchanged. */
+ * other slot is unchanged.  KV heads have disjoint outputs; threads split them. */
 int oracle_paged_kv_bwd(int nseq, const int32_t *seq_lens, const int32_t *block_table,
                         int max_pages, int nq, const int32_t *query_seq,
                         const int32_t *query_pos, int heads, int kv_heads, int D,
                         int page_size, int pool_pages, int causal, double scale,
                         const double *q, const double *dy, const double *k_pool,
                         const double *v_pool, const double *stats, double *dk_pool,
-                        double *dv_pool) {
+                        double *dv_pool, int nthreads) {
   if (paged_check(nseq, seq_lens, block_table, max_pages, nq, query_seq, heads, kv_heads,
                   page_size, pool_pages))
     return -1;
-  const int group = heads / kv_heads;
   const int64_t nslot = (int64_t)pool_pages * page_size;
   double *gk = (double *)calloc((size_t)(nslot * kv_heads * D) + 1, sizeof(double));
   double *gv = (double *)calloc((size_t)(nslot * kv_heads * D) + 1, sizeof(double));
@@ -370,34 +458,20 @@ int oracle_paged_kv_bwd(int nseq, const int32_t *seq_lens, const int32_t *block_
   if (!gk || !gv || !listed) { free(gk); free(gv); free(listed); return -1; }
 
   for (int s = 0; s < nseq; ++s) {
-    const int len = seq_lens[s];
-    const int np = (len + page_size - 1) / page_size;
+    const int np = (seq_lens[s] + page_size - 1) / page_size;
     for (int p = 0; p < np; ++p) listed[block_table[(int64_t)s * max_pages + p]] = 1;
-    for (int t = 0; t < len; ++t) {
-      const int64_t slot = (int64_t)block_table[(int64_t)s * max_pages + t / page_size] * page_size +
-                           t % page_size;
-      for (int r = 0; r < nq; ++r) {
-        if (query_seq[r] != s) continue;
-        if (causal && t > query_pos[r]) continue;
-        for (int h = 0; h < heads; ++h) {
-          const int g = h / group;
-          const double *st = stats + ((int64_t)r * heads + h) * 3;
-          if (st[1] == 0.0) continue;
-          const double *qr = q + ((int64_t)r * heads + h) * D;
-          const double *gr = dy + ((int64_t)r * heads + h) * D;
-          const double *kr = k_pool + (slot * kv_heads + g) * D;
-          const double *vr = v_pool + (slot * kv_heads + g) * D;
-          double a = 0.0, c = 0.0;
-          for (int d = 0; d < D; ++d) { a += qr[d] * kr[d]; c += gr[d] * vr[d]; }
-          const double p = exp(scale * a - st[0]) / st[1];
-          const double ds = p * (c - st[2]) * scale;
-          double *ak = gk + (slot * kv_heads + g) * D;
-          double *av = gv + (slot * kv_heads + g) * D;
-          for (int d = 0; d < D; ++d) { ak[d] += ds * qr[d]; av[d] += p * gr[d]; }
-        }
-      }
-    }
   }
+  paged_job J;
+  memset(&J, 0, sizeof J);
+  J.nseq = nseq; J.max_pages = max_pages; J.nq = nq; J.heads = heads; J.kv_heads = kv_heads;
+  J.D = D; J.page_size = page_size; J.pool_pages = pool_pages; J.causal = causal;
+  J.seq_lens = seq_lens; J.block_table = block_table; J.query_seq = query_seq;
+  J.query_pos = query_pos; J.scale = scale;
+  J.q = q; J.dy = dy; J.k_pool = k_pool; J.v_pool = v_pool; J.stats_in = stats;
+  J.gk = gk; J.gv = gv;
+  J.count = kv_heads;
+  paged_parallel(&J, paged_kv_worker, nthreads);
+
   for (int pg = 0; pg < pool_pages; ++pg) {
     if (!listed[pg]) continue;
     const int64_t base = (int64_t)pg * page_size * kv_heads * D;

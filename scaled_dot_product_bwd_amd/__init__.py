@@ -7,11 +7,16 @@ There is no CPU fallback: without the built library every call raises.
 
     dq, dk, dv = attn_bwd(q, k, v, dy, mask_kind="causal")
 
+    plan = paged_plan(seq_lens, block_table, query_seq, query_pos, heads=32,
+                      kv_heads=8, page_size=16, pool_pages=N, device="cuda")
+    attn_bwd_paged(q, dy, k_pool, v_pool, stats, plan, dk_pool=dk, dv_pool=dv)
+
 Tensors are ``[B, S, H, D]`` (any strides with ``D`` contiguous; pass
 ``x.transpose(1, 2)`` for a ``[B, H, S, D]`` tensor), float32 or bfloat16, on the
 GPU.  The semantics are those of rlx-cpu 0.2.17 src/attention_bwd.rs
 (`attention_backward_all`) with the mask codes of rlx-wgpu 0.2.1
-attention_bwd.wgsl (`mask_score`).
+attention_bwd.wgsl (`mask_score`); the paged path is ruDNN 0.1.43
+src/paged_attention/ordered_kernel.rs (`history_backward`).
 """
 from __future__ import annotations
 
@@ -19,13 +24,15 @@ import ctypes
 import math
 import os
 
+from . import _abi
 from ._abi import (ATTN_BF16, ATTN_F32, ATTN_MASK_BIAS, ATTN_MASK_CAUSAL,
                    ATTN_MASK_FLAG_CAUSAL, ATTN_MASK_KEYPAD, ATTN_MASK_NONE, ATTN_MASK_WINDOW,
-                   ATTN_WRT_ALL, ATTN_WRT_K, ATTN_WRT_Q, ATTN_WRT_V, AttnBwdArgs, AttnError,
-                   load_library, library_path)
+                   ATTN_WRT_ALL, ATTN_WRT_K, ATTN_WRT_Q, ATTN_WRT_V, AttnBwdArgs,
+                   AttnBwdPagedArgs, AttnError, load_library, library_path)
 
 __all__ = ["attn_bwd", "attn_bwd_stage", "workspace_bytes", "make_args", "AttnError",
-           "load_library", "library_path", "MASKS", "WRT"]
+           "load_library", "library_path", "MASKS", "WRT", "PagedPlan", "paged_plan",
+           "attn_bwd_paged", "make_paged_args"]
 
 MASKS = {"none": ATTN_MASK_NONE, "causal": ATTN_MASK_CAUSAL, "keypad": ATTN_MASK_KEYPAD,
          "window": ATTN_MASK_WINDOW, "bias": ATTN_MASK_BIAS}
@@ -142,3 +149,128 @@ def row_stats_views(workspace, B, H, Sq):
     for i in range(3):
         out.append(f[i * plane: i * plane + B * H * Sq * 4].view(_torch().float32).view(B, H, Sq))
     return tuple(out)
+
+
+# ---------------------------------------------------------------------------
+# Paged history backward.
+
+class PagedPlan:
+    """Host plan words (numpy int32) and, once uploaded, their device copy."""
+
+    def __init__(self, words, *, heads, kv_heads, page_size, pool_pages, nq, device=None):
+        self.words = words
+        self.heads, self.kv_heads, self.page_size = heads, kv_heads, page_size
+        self.pool_pages, self.nq = pool_pages, nq
+        self.device_words = None
+        if device is not None:
+            self.to(device)
+
+    def to(self, device):
+        torch = _torch()
+        self.device_words = torch.from_numpy(self.words).to(device)
+        return self
+
+    def header(self, w):
+        return int(self.words[w])
+
+    @property
+    def items(self):
+        return self.header(_abi.W_ITEMS)
+
+    def _table(self, off_word, n):
+        off = self.header(off_word)
+        return self.words[off: off + n]
+
+    def listed_pages(self):
+        """Physical pages whose slots the backward writes, ascending."""
+        return self._table(_abi.W_OFF_LISTED, self.header(_abi.W_LISTED)).copy()
+
+    def item_slots(self):
+        """[items, 128] slot entries (slot * 2 + live, -1 = unused lane)."""
+        return self._table(_abi.W_OFF_ITEM_SLOTS,
+                           self.items * _abi.PLAN_ITEM_SLOTS).reshape(self.items, -1).copy()
+
+
+def _np_i32(x):
+    import numpy as np
+    if hasattr(x, "detach"):
+        x = x.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def paged_plan(seq_lens, block_table, query_seq, query_pos, *, heads, kv_heads, page_size,
+               pool_pages, device=None):
+    """Builds the host plan of the paged backward (attn_bwd_paged_plan_build) and,
+    with ``device``, uploads it.  seq_lens [nseq], block_table [nseq, max_pages],
+    query_seq / query_pos [nq]: integer arrays or tensors (any device)."""
+    import numpy as np
+    lib = load_library()
+    lens = _np_i32(seq_lens).reshape(-1)
+    bt = _np_i32(block_table)
+    nseq = int(lens.size)
+    bt = bt.reshape(nseq, -1) if bt.size else np.zeros((nseq, 0), np.int32)
+    qs = _np_i32(query_seq).reshape(-1)
+    qp = _np_i32(query_pos).reshape(-1)
+    nq = int(qs.size)
+    vp = ctypes.c_void_p
+    words = lib.attn_bwd_paged_plan_words(nseq, lens.ctypes.data_as(vp), bt.shape[1], nq, heads,
+                                          kv_heads, page_size, pool_pages)
+    if words < 0:
+        _check(_abi.ATTN_E_INVALID)
+    buf = np.zeros(max(int(words), 32), dtype=np.int32)
+    _check(lib.attn_bwd_paged_plan_build(
+        nseq, lens.ctypes.data_as(vp), bt.ctypes.data_as(vp), bt.shape[1], nq,
+        qs.ctypes.data_as(vp), qp.ctypes.data_as(vp), heads, kv_heads, page_size, pool_pages,
+        buf.ctypes.data_as(vp), buf.size))
+    used = int(buf[_abi.W_WORDS])
+    return PagedPlan(buf[:used].copy(), heads=heads, kv_heads=kv_heads, page_size=page_size,
+                     pool_pages=pool_pages, nq=nq, device=device)
+
+
+def make_paged_args(q, dy, k_pool, v_pool, stats, plan, dk_pool=None, dv_pool=None, *,
+                    causal=True, scale=None, need=3):
+    torch = _torch()
+    nq, heads, D = q.shape
+    a = AttnBwdPagedArgs()
+    a.dtype = ATTN_BF16 if q.dtype == torch.bfloat16 else ATTN_F32
+    a.need = int(need)
+    a.heads, a.kv_heads, a.head_dim = heads, k_pool.shape[1], D
+    a.page_size, a.causal = plan.page_size, int(bool(causal))
+    a.nq, a.pool_pages = nq, plan.pool_pages
+    a.scale = float(scale) if scale is not None else float(
+        torch.tensor(1.0 / math.sqrt(D), dtype=torch.float32))
+    a.q, a.dy = q.data_ptr(), dy.data_ptr()
+    a.k_pool, a.v_pool = k_pool.data_ptr(), v_pool.data_ptr()
+    a.stats = stats.data_ptr()
+    a.plan_host = plan.words.ctypes.data
+    a.plan = plan.device_words.data_ptr()
+    if dk_pool is not None:
+        a.dk_pool = dk_pool.data_ptr()
+    if dv_pool is not None:
+        a.dv_pool = dv_pool.data_ptr()
+    return a
+
+
+def attn_bwd_paged(q, dy, k_pool, v_pool, stats, plan, *, dk_pool=None, dv_pool=None,
+                   need="dkdv", causal=True, scale=None, stream=None):
+    """dK / dV of the paged grouped-query history backward, written into the
+    given gradient pools at the slots of listed pages (other slots untouched);
+    pools that are not given are allocated zero-filled.  q, dy: [nq, heads, D];
+    pools: [pool_pages * page_size, kv_heads, D] (contiguous, fp32 or bf16, on
+    the GPU); stats: float32 [nq, heads, 3] = (max, denominator, delta); plan:
+    a PagedPlan uploaded to the same device.  Returns (dk_pool, dv_pool)."""
+    torch = _torch()
+    n = {"dk": 1, "dv": 2, "dkdv": 3}[need] if isinstance(need, str) else int(need)
+    if plan.device_words is None:
+        plan.to(q.device)
+    for t in (q, dy, k_pool, v_pool, stats):
+        if not t.is_contiguous():
+            raise ValueError("attn_bwd_paged takes contiguous tensors")
+    if dk_pool is None and n & 1:
+        dk_pool = torch.zeros_like(k_pool)
+    if dv_pool is None and n & 2:
+        dv_pool = torch.zeros_like(v_pool)
+    args = make_paged_args(q, dy, k_pool, v_pool, stats, plan, dk_pool, dv_pool,
+                           causal=causal, scale=scale, need=n)
+    _check(load_library().attn_bwd_paged(ctypes.byref(args), _stream_handle(stream)))
+    return dk_pool, dv_pool

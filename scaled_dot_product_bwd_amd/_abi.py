@@ -22,7 +22,16 @@ STATUS_NAMES = {ATTN_E_INVALID: "ATTN_E_INVALID", ATTN_E_UNSUPPORTED: "ATTN_E_UN
 
 # Every symbol include/attn_bwd.h declares.
 EXPORTED = ["attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_row_stats", "attn_bwd_kv",
-            "attn_bwd_dq", "attn_bwd_last_error"]
+            "attn_bwd_dq", "attn_bwd_paged_plan_words", "attn_bwd_paged_plan_build",
+            "attn_bwd_paged", "attn_bwd_last_error"]
+
+# Plan header words (scaled_dot_product_bwd_amd/csrc/paged.hpp).
+PLAN_MAGIC = 0x31504241
+PLAN_ITEM_SLOTS = 128
+(W_MAGIC, W_WORDS, W_NSEQ, W_NQ, W_HEADS, W_KV_HEADS, W_PAGE_SIZE, W_POOL_PAGES, W_ITEMS,
+ W_LINKS, W_QH, W_LISTED, W_OFF_ITEM_LINKS, W_OFF_ITEM_SLOTS, W_OFF_LINK_SEQ, W_OFF_LINK_INFO,
+ W_OFF_LINK_TOK, W_OFF_SEQ_QH, W_OFF_QH_RH, W_OFF_QH_POS, W_OFF_SEQ_MAXPOS,
+ W_OFF_LISTED) = range(22)
 
 
 class AttnError(RuntimeError):
@@ -53,6 +62,21 @@ class AttnBwdArgs(ctypes.Structure):
     ]
 
 
+class AttnBwdPagedArgs(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("need", ctypes.c_int32),
+        ("heads", ctypes.c_int32), ("kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("causal", ctypes.c_int32),
+        ("nq", ctypes.c_int32), ("pool_pages", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("q", ctypes.c_void_p), ("dy", ctypes.c_void_p),
+        ("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
+        ("stats", ctypes.c_void_p),
+        ("plan_host", ctypes.c_void_p), ("plan", ctypes.c_void_p),
+        ("dk_pool", ctypes.c_void_p), ("dv_pool", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 
 
@@ -75,6 +99,14 @@ def load_library():
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [ctypes.POINTER(AttnBwdArgs), ctypes.c_void_p]
+    _i32, _p = ctypes.c_int32, ctypes.c_void_p
+    lib.attn_bwd_paged_plan_words.restype = ctypes.c_int64
+    lib.attn_bwd_paged_plan_words.argtypes = [_i32, _p, _i32, _i32, _i32, _i32, _i32, _i32]
+    lib.attn_bwd_paged_plan_build.restype = ctypes.c_int
+    lib.attn_bwd_paged_plan_build.argtypes = [_i32, _p, _p, _i32, _i32, _p, _p, _i32, _i32, _i32,
+                                              _i32, _p, ctypes.c_int64]
+    lib.attn_bwd_paged.restype = ctypes.c_int
+    lib.attn_bwd_paged.argtypes = [ctypes.POINTER(AttnBwdPagedArgs), ctypes.c_void_p]
     lib.attn_bwd_last_error.restype = ctypes.c_char_p
     lib.attn_bwd_last_error.argtypes = []
     _lib = lib

@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["abi.cpp", "dense_kernels.hip"]
+SOURCES = ["abi.cpp", "paged_plan.cpp", "dense_kernels.hip", "paged_kernels.hip"]
 
 
 def library_path() -> str:

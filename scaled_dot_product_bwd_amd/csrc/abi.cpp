@@ -1,5 +1,6 @@
 // abi.cpp -- the C ABI of libattn_bwd.so (declared in include/attn_bwd.h):
-// argument validation, workspace sizing and kernel dispatch for the dense path.
+// argument validation, workspace sizing and kernel dispatch for the dense path,
+// and validation + dispatch of the paged path (its planner is paged_plan.cpp).
 //
 // Every check happens on the host before anything is enqueued, so a rejected
 // call leaves the stream untouched.  The pages' own interfaces have no error
@@ -14,6 +15,7 @@
 
 #include "attn_bwd.h"
 #include "launch.hpp"
+#include "paged.hpp"
 
 namespace {
 
@@ -251,9 +253,119 @@ int run(const attn_bwd_args *a, void *stream, int first, int last) {
   return ATTN_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Paged history backward.
+
+int validate_paged(const attn_bwd_paged_args *a, attn::PagedParams &p, int &nblocks, bool &bf16) {
+  using namespace attn::plan;
+  if (!a) return fail(ATTN_E_INVALID, "args is NULL");
+  if (a->dtype != ATTN_F32 && a->dtype != ATTN_BF16)
+    return fail(ATTN_E_INVALID, "dtype %d is not ATTN_F32 or ATTN_BF16", a->dtype);
+  if (a->need < 1 || a->need > 3) return fail(ATTN_E_INVALID, "need %d is not 1, 2 or 3", a->need);
+  if (a->head_dim != 32 && a->head_dim != 64 && a->head_dim != 128)
+    return fail(ATTN_E_UNSUPPORTED, "head_dim %d is not 32, 64 or 128", a->head_dim);
+  if (!std::isfinite(a->scale)) return fail(ATTN_E_INVALID, "scale is not finite");
+  if (a->causal != 0 && a->causal != 1) return fail(ATTN_E_INVALID, "causal must be 0 or 1");
+  const int32_t *w = a->plan_host;
+  if (!w || !a->plan) return fail(ATTN_E_INVALID, "plan_host / plan is NULL");
+  if (w[W_MAGIC] != kMagic) return fail(ATTN_E_INVALID, "plan_host is not a plan (bad magic)");
+  const int64_t words = w[W_WORDS];
+  if (words < HEADER_WORDS) return fail(ATTN_E_INVALID, "plan header is inconsistent");
+  for (int k = W_OFF_ITEM_LINKS; k <= W_OFF_LISTED; ++k)
+    if (w[k] < HEADER_WORDS || w[k] > words) return fail(ATTN_E_INVALID, "plan offsets are inconsistent");
+  if (w[W_HEADS] != a->heads || w[W_KV_HEADS] != a->kv_heads || w[W_PAGE_SIZE] != a->page_size ||
+      w[W_NQ] != a->nq || w[W_POOL_PAGES] != a->pool_pages)
+    return fail(ATTN_E_INVALID,
+                "plan was built for heads %d, kv_heads %d, page_size %d, nq %d, pool_pages %d",
+                w[W_HEADS], w[W_KV_HEADS], w[W_PAGE_SIZE], w[W_NQ], w[W_POOL_PAGES]);
+  const int64_t items = w[W_ITEMS];
+  if (items < 0 || items * (int64_t)a->kv_heads > INT32_MAX)
+    return fail(ATTN_E_INVALID, "plan item count is inconsistent");
+  bf16 = a->dtype == ATTN_BF16;
+  nblocks = (int)(items * a->kv_heads);
+
+  const size_t es = bf16 ? 2 : 4;
+  const int64_t D = a->head_dim;
+  const int64_t qrows = (int64_t)a->nq * a->heads;
+  const int64_t pslots = (int64_t)a->pool_pages * a->page_size * a->kv_heads;
+  const bool work = nblocks > 0;
+  struct T {
+    const char *name;
+    const void *ptr;
+    int64_t bytes;
+    bool needed;
+  } ts[7] = {
+      {"q", a->q, qrows * D * (int64_t)es, work && qrows > 0},
+      {"dy", a->dy, qrows * D * (int64_t)es, work && qrows > 0},
+      {"stats", a->stats, qrows * 3 * (int64_t)sizeof(float), work && qrows > 0},
+      {"k_pool", a->k_pool, pslots * D * (int64_t)es, work},
+      {"v_pool", a->v_pool, pslots * D * (int64_t)es, work},
+      {"dk_pool", a->dk_pool, pslots * D * (int64_t)es, work && (a->need & 1)},
+      {"dv_pool", a->dv_pool, pslots * D * (int64_t)es, work && (a->need & 2)},
+  };
+  Range rng[7];
+  for (int i = 0; i < 7; ++i) {
+    if (!ts[i].needed) continue;
+    if (!ts[i].ptr) return fail(ATTN_E_INVALID, "%s is NULL", ts[i].name);
+    if ((uintptr_t)ts[i].ptr % 16) return fail(ATTN_E_UNSUPPORTED, "%s is not 16-byte aligned", ts[i].name);
+    rng[i].lo = (uintptr_t)ts[i].ptr;
+    rng[i].hi = rng[i].lo + (uintptr_t)ts[i].bytes;
+  }
+  for (int i = 5; i < 7; ++i) {
+    if (!ts[i].needed) continue;
+    for (int j = 0; j < 7; ++j)
+      if (j != i && ts[j].needed && overlap(rng[i], rng[j]))
+        return fail(ATTN_E_INVALID, "%s overlaps %s", ts[i].name, ts[j].name);
+  }
+
+  std::memset(&p, 0, sizeof p);
+  p.q = a->q; p.dy = a->dy; p.k_pool = a->k_pool; p.v_pool = a->v_pool;
+  p.dk_pool = a->dk_pool; p.dv_pool = a->dv_pool;
+  p.stats = a->stats;
+  p.plan = a->plan;
+  p.heads = a->heads;
+  p.kv_heads = a->kv_heads;
+  p.group = a->heads / a->kv_heads;
+  p.causal = a->causal;
+  p.need_dk = a->need & 1;
+  p.need_dv = (a->need >> 1) & 1;
+  p.scale = a->scale;
+  p.scale_log2 = a->scale * attn::kLog2e;
+  p.items = (int)items;
+  p.off_item_links = w[W_OFF_ITEM_LINKS];
+  p.off_item_slots = w[W_OFF_ITEM_SLOTS];
+  p.off_link_seq = w[W_OFF_LINK_SEQ];
+  p.off_link_info = w[W_OFF_LINK_INFO];
+  p.off_link_tok = w[W_OFF_LINK_TOK];
+  p.off_seq_qh = w[W_OFF_SEQ_QH];
+  p.off_qh_rh = w[W_OFF_QH_RH];
+  p.off_qh_pos = w[W_OFF_QH_POS];
+  p.off_seq_maxpos = w[W_OFF_SEQ_MAXPOS];
+  return ATTN_OK;
+}
+
 }  // namespace
 
+namespace attn {
+void set_last_error(const char *msg) {
+  snprintf(g_err, sizeof g_err, "%s", msg);
+}
+hipError_t launch_paged(bool bf16_in, int D, const PagedParams &p, int nblocks, hipStream_t stream);
+}  // namespace attn
+
 extern "C" {
+
+int attn_bwd_paged(const attn_bwd_paged_args *a, void *stream) {
+  attn::PagedParams p;
+  int nblocks = 0;
+  bool bf16 = false;
+  const int rc = validate_paged(a, p, nblocks, bf16);
+  if (rc != ATTN_OK) return rc;
+  if (nblocks == 0) return ATTN_OK;
+  const hipError_t e = attn::launch_paged(bf16, a->head_dim, p, nblocks, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(ATTN_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ATTN_OK;
+}
 
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq) {
   if (B < 0 || H < 0 || Sq < 0) return 0;

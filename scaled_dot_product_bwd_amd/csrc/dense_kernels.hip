@@ -5,8 +5,9 @@
 //                accumulated online (equal in exact arithmetic).  The
 //                statistics triple is the one ruDNN ordered_kernel.rs
 //                `history_backward` consumes (max, denominator, delta).
-//   k_kv_bwd     KV-block-major: per 128-key block, over its visible 32-query
-//                chunks in ascending order, recompute S and P, then
+//   k_kv_bwd     KV-block-major: per 128-key block, over its visible query
+//                chunks (64 rows bf16, 32 fp32) in ascending order,
+//                recompute S and P, then
 //                dV += P^T dY, dP = dY V^T, dS = P (dP - delta) scale,
 //                dK += dS^T Q.  dK / dV stay in registers; one store at the end.
 //   k_dq_bwd     query-block-major: per 128-query block, over its visible
@@ -24,6 +25,7 @@
 // global -> LDS loads), so each chunk costs one barrier and HBM / L2 latency
 // stays hidden behind two chunks of compute.
 #include "device_common.hpp"
+#include "kv_core.hpp"
 #include "launch.hpp"
 
 namespace attn {
@@ -224,12 +226,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 // ---------------------------------------------------------------------------
 // dK / dV, KV-block-major.  A step covers ROWS = 32 * NSUB queries as NSUB
-// independent 32-row sub-tiles (two for bf16): their chains of MFMA and VALU
-// work interleave within the wave, and the step's barrier is shared.
-template <typename T> struct KvShape {
-  static constexpr int NSUB = sizeof(T) == 2 ? 2 : 1;
-  static constexpr int ROWS = 32 * NSUB;
-};
+// independent 32-row sub-tiles (kv_core.hpp).
 
 // Statistics of the ROWS rows of chunk i0 into LDS, [lse2 x ROWS | delta x ROWS]
 // per wave copy: direct-to-LDS dword loads, each wave writing its own copy so
@@ -278,70 +275,19 @@ __device__ __forceinline__ void kv_step(const DenseParams &p, KvState<T, D> &S, 
                                         const float *st_c, int cn,
                                         Tile<T, D, KvShape<T>::ROWS> *Qn,
                                         Tile<T, D, KvShape<T>::ROWS> *Gn, float *st_n) {
-  typedef MT<T> M;
-  constexpr int NSD = D / M::KS, NT = D / 32, CS = M::CSTEPS;
-  constexpr int NSUB = KvShape<T>::NSUB, ROWS = KvShape<T>::ROWS;
+  constexpr int ROWS = KvShape<T>::ROWS;
   constexpr int PER_CHUNK = 2 * ChunkIO<T, D, ROWS>::LOADS + stat_loads<ROWS>();
   const int i0 = c * ROWS;
   const bool issued = cn <= S.c_last;
   if (issued) kv_issue<T, D, MODE>(p, S, cn, Qn, Gn, st_n);
-  const int kj = S.kj, half = S.half;
-
-  // S = Q K^T and dP = dY V^T per sub-tile: rows = queries (A from LDS),
-  // columns = this lane's key.
-  f32x16 sacc[NSUB], pacc[NSUB];
-#pragma unroll
-  for (int u = 0; u < NSUB; ++u) {
-    typename M::frag qa[NSD], ga[NSD];
-#pragma unroll
-    for (int s = 0; s < NSD; ++s) {
-      qa[s] = Qc->frag(32 * u + S.l32, s, S.half);
-      ga[s] = Gc->frag(32 * u + S.l32, s, S.half);
-    }
-    sacc[u] = f32x16{};
-    pacc[u] = f32x16{};
-#pragma unroll
-    for (int s = 0; s < NSD; ++s) {
-      sacc[u] = M::mma(qa[s], S.kf[s], sacc[u]);
-      pacc[u] = M::mma(ga[s], S.vf[s], pacc[u]);
-    }
-  }
-  // P and dS (the statistics of wave 0's copy).
-  typename M::frag pf[NSUB][CS], sf[NSUB][CS];
-#pragma unroll
-  for (int u = 0; u < NSUB; ++u) {
-    const bool check = MODE != MODE_INDEX || !tile_all_visible(p, i0 + 32 * u, S.jw);
-    float sc[16], pv[16], dsv[16];
-    scores16<MODE>(p, sacc[u], sc, S.b, S.h, check,
-                   [&](int r) { return i0 + 32 * u + kr(r, half); }, [&](int) { return kj; });
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const f32x4 lse4 = *reinterpret_cast<const f32x4 *>(&st_c[32 * u + 8 * g + 4 * half]);
-      const f32x4 del4 = *reinterpret_cast<const f32x4 *>(&st_c[ROWS + 32 * u + 8 * g + 4 * half]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * g + e;
-        const float pr = fast_exp2(sc[r] - lse4[e]);
-        pv[r] = pr;
-        dsv[r] = pr * (pacc[u][r] - del4[e]) * p.scale;
-      }
-    }
-#pragma unroll
-    for (int st = 0; st < CS; ++st) {
-      pf[u][st] = creuse<T>(pv, st);
-      sf[u][st] = creuse<T>(dsv, st);
-    }
-  }
-  // dV^T += dY^T P and dK^T += Q^T dS: A = rows read transposed from LDS, B = C reuse.
-#pragma unroll
-  for (int u = 0; u < NSUB; ++u)
-#pragma unroll
-    for (int st = 0; st < CS; ++st)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        S.dv[t] = M::mma(Gc->tfrag(32 * t, st, S.lane, 32 * u), pf[u][st], S.dv[t]);
-        S.dk[t] = M::mma(Qc->tfrag(32 * t, st, S.lane, 32 * u), sf[u][st], S.dk[t]);
-      }
+  const int kj = S.kj, half = S.half, jw = S.jw, b = S.b, h = S.h;
+  kv_chunk<T, D>(S.kf, S.vf, S.dk, S.dv, Qc, Gc, st_c, st_c + ROWS, p.scale, S.lane,
+                 [&](int u, const f32x16 &acc, float *sc) {
+                   const bool check = MODE != MODE_INDEX || !tile_all_visible(p, i0 + 32 * u, jw);
+                   scores16<MODE>(p, acc, sc, b, h, check,
+                                  [&](int r) { return i0 + 32 * u + kr(r, half); },
+                                  [&](int) { return kj; });
+                 });
   if (issued) {
     S.io_q.complete(*Qn);
     S.io_g.complete(*Gn);

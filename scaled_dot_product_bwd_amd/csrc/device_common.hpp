@@ -246,13 +246,14 @@ template <int D, int ROWS> struct ChunkIO<bf16, D, ROWS> {
       col[j] = data ? 8 * c : 0;
     }
   }
+  // Rows given by a functor: rowptr(r) is the start of chunk row r (0 <= r < ROWS).
+  template <typename F> __device__ __forceinline__ void issue_at(F rowptr, TileT &t) {
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) dma_lds16(&t.a[(wave + 4 * j) * 512], rowptr(rloc[j]) + col[j]);
+  }
   __device__ __forceinline__ void issue(const bf16 *base, int64_t stride, int r0, int nrows,
                                         TileT &t) {
-#pragma unroll
-    for (int j = 0; j < LOADS; ++j) {
-      const int row = min(r0 + rloc[j], nrows - 1);
-      dma_lds16(&t.a[(wave + 4 * j) * 512], base + (int64_t)row * stride + col[j]);
-    }
+    issue_at([&](int r) { return base + (int64_t)min(r0 + r, nrows - 1) * stride; }, t);
   }
   __device__ __forceinline__ void complete(TileT &) {}
 };
@@ -265,16 +266,18 @@ template <int D, int ROWS> struct ChunkIO<float, D, ROWS> {
   static constexpr int PER = (ROWS * CH + 255) / 256;
   f32x4 r[PER];
   __device__ __forceinline__ void init() {}
-  __device__ __forceinline__ void issue(const float *base, int64_t stride, int r0, int nrows,
-                                        TileT &) {
+  template <typename F> __device__ __forceinline__ void issue_at(F rowptr, TileT &) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int id = threadIdx.x + 256 * j;
-      const int row = min(r0 + id / CH, nrows - 1), c = id % CH;
       r[j] = (ROWS * CH % 256 == 0 || id < ROWS * CH)
-                 ? *reinterpret_cast<const f32x4 *>(base + (int64_t)row * stride + 4 * c)
+                 ? *reinterpret_cast<const f32x4 *>(rowptr(id / CH) + 4 * (id % CH))
                  : f32x4{};
     }
+  }
+  __device__ __forceinline__ void issue(const float *base, int64_t stride, int r0, int nrows,
+                                        TileT &t) {
+    issue_at([&](int r) { return base + (int64_t)min(r0 + r, nrows - 1) * stride; }, t);
   }
   __device__ __forceinline__ void complete(TileT &t) {
 #pragma unroll

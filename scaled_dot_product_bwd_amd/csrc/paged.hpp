@@ -1,0 +1,81 @@
+// paged.hpp -- the plan-word format of the paged history backward and the
+// kernel's parameter block, shared by the host planner (paged_plan.cpp), the
+// C ABI (abi.cpp) and the kernel (paged_kernels.hip).
+//
+// The method is ruDNN 0.1.43 src/paged_attention/ordered_kernel.rs
+// `history_backward`: every physical KV slot that a sequence lists receives
+// dK / dV summed over all (sequence, logical page) links of its page, all
+// query rows of each linked sequence that can see the slot's token and all
+// query heads of the slot's KV-head group, with one final store per element.
+// The pages derive, on the host, a list of history pages, a page -> link CSR
+// and a sequence -> row CSR.  The plan here carries the same information
+// regrouped for 128-slot MFMA tiles:
+//
+//   item     up to 128 slots of listed pages that share the same list of
+//            linked sequences (in practice: consecutive pages of one
+//            sequence, or the pages of a shared prefix); one workgroup per
+//            (item, KV head).  Slot entry = physical slot * 2 + live, -1 for
+//            an unused lane; live = some link's token at this slot lies
+//            inside its sequence (tail slots of a last page are not live:
+//            they store zero and their K / V rows are never read).
+//   link     one sequence linked to every page of an item: per lane the
+//            token position of the slot in that sequence (-1: past its
+//            length, or no slot), plus min / max token and whether all 128
+//            lanes hold a token.
+//   qh row   the query rows of each sequence in their original packed order,
+//            each expanded to its group of query heads (head index minor):
+//            rh = row * heads + head-in-group, and the row's position.
+#pragma once
+
+#include <stdint.h>
+
+namespace attn {
+namespace plan {
+
+constexpr int32_t kMagic = 0x31504241;  // "ABP1"
+constexpr int kItemSlots = 128;
+
+enum Word {
+  W_MAGIC = 0,
+  W_WORDS,       // words actually used by this plan
+  W_NSEQ,
+  W_NQ,
+  W_HEADS,
+  W_KV_HEADS,
+  W_PAGE_SIZE,
+  W_POOL_PAGES,
+  W_ITEMS,
+  W_LINKS,
+  W_QH,          // total query-head rows = nq * heads / kv_heads
+  W_LISTED,      // listed physical pages
+  W_OFF_ITEM_LINKS,  // [items + 1] CSR into links
+  W_OFF_ITEM_SLOTS,  // [items * 128] slot entries
+  W_OFF_LINK_SEQ,    // [links] sequence
+  W_OFF_LINK_INFO,   // [links * 4] (min token, max token, all lanes valid, 0)
+  W_OFF_LINK_TOK,    // [links * 128] token per lane, -1 = none
+  W_OFF_SEQ_QH,      // [nseq + 1] CSR into qh rows
+  W_OFF_QH_RH,       // [qh] row * heads + head-in-group
+  W_OFF_QH_POS,      // [qh] position of the row
+  W_OFF_SEQ_MAXPOS,  // [nseq] largest position of the sequence's rows, -1 if none
+  W_OFF_LISTED,      // [listed] listed physical pages, ascending
+  HEADER_WORDS = 32
+};
+
+enum { LI_MIN_TOK = 0, LI_MAX_TOK = 1, LI_ALL_VALID = 2, LINK_INFO_WORDS = 4 };
+
+}  // namespace plan
+
+struct PagedParams {
+  const void *q, *dy, *k_pool, *v_pool;
+  void *dk_pool, *dv_pool;
+  const float *stats;   // [nq, heads, 3] = (max, denominator, delta)
+  const int32_t *plan;  // device copy of the plan words
+  int heads, kv_heads, group;
+  int causal, need_dk, need_dv;
+  float scale, scale_log2;
+  int items;
+  int off_item_links, off_item_slots, off_link_seq, off_link_info, off_link_tok;
+  int off_seq_qh, off_qh_rh, off_qh_pos, off_seq_maxpos;
+};
+
+}  // namespace attn

@@ -1,0 +1,277 @@
+// paged_kernels.hip -- the gfx950 kernel of the paged, grouped-query history
+// backward (dK / dV only), ruDNN 0.1.43 src/paged_attention/ordered_kernel.rs
+// `history_backward`.
+//
+// The pages give one wavefront to each (physical token, KV head), which walks
+// the page's links, the linked sequence's query rows and the group's query
+// heads, forms each score with a cross-lane dot product and accumulates
+// dK += ds q, dV += p dY, then stores once.  The same contraction over a whole
+// item of 128 slots is dense enough for MFMA: one workgroup per (item, KV head
+// g), 4 waves of 32 slots each (slot = MFMA column, K / V rows in registers),
+// and the linked sequence's query rows times the group's query heads as the
+// streamed row dimension ("qh rows", 64 per chunk for bf16).  Per chunk the
+// body is the dense kernel's (kv_core.hpp); what differs is the addressing:
+//   * qh row -> (row, head) and the row's position come from the plan
+//     (rowinfo, fetched two chunks ahead of the Q / dY rows it addresses);
+//   * P uses the supplied statistics, lse2 = max * log2 e + log2(denominator)
+//     (a zero denominator gives P = 0, as the pages skip such rows);
+//   * slot t of the item is visible to row r iff its token in the linked
+//     sequence exists and, when causal, is <= the row's position.
+// Each (slot, KV head) element is stored exactly once after all links: the
+// gradient, or +0 for a slot no link reaches (tail slots, whose K / V rows are
+// never read).  Slots of pages no sequence lists are never touched.
+#include "device_common.hpp"
+#include "kv_core.hpp"
+#include "paged.hpp"
+
+namespace attn {
+
+// Per-wave LDS copies of the row metadata.  Stats buffer (one per chunk in
+// flight): m -> lse2, den, delta, position; 64 entries each (fp32 chunks use
+// the first 32).  Rowinfo buffer: rh of the chunk's qh rows.
+constexpr int kStatWave = 4 * 64;
+constexpr int kStatWords = 4 * kStatWave;
+constexpr int kRiWords = 4 * 64;
+
+template <typename T, int D> struct PagedState {
+  typedef MT<T> M;
+  static constexpr int NSD = D / M::KS, NT = D / 32, ROWS = KvShape<T>::ROWS;
+  typename M::frag kf[NSD], vf[NSD];
+  f32x16 dk[NT], dv[NT];
+  ChunkIO<T, D, ROWS> io_q, io_g;
+  const T *qbase, *gbase;  // Q / dY at head g * group
+  const float *sbase;      // statistics at head g * group
+  const int32_t *rh_tab, *pos_tab;  // the link's sequence: qh rows from 0
+  int nqh, c_last, tok, maxtok, wave, lane;
+  bool all_valid;
+};
+
+// Rowinfo of chunk c into this wave's copy: lane l <- rh of qh row c * ROWS + l
+// (clamped to the last row, so every lane reads inside the plan).
+template <typename T, int D>
+__device__ __forceinline__ void issue_rowinfo(PagedState<T, D> &S, int c, int *ri) {
+  const int qh = min(c * PagedState<T, D>::ROWS + S.lane, S.nqh - 1);
+  dma_lds4(ri + 64 * S.wave, S.rh_tab + qh);
+}
+
+// Statistics and Q / dY rows of chunk c; `ri` holds the chunk's rowinfo (landed).
+template <typename T, int D>
+__device__ __forceinline__ void issue_chunk(const PagedParams &p, PagedState<T, D> &S, int c,
+                                            const int *ri, float *st,
+                                            Tile<T, D, KvShape<T>::ROWS> *Q,
+                                            Tile<T, D, KvShape<T>::ROWS> *G) {
+  constexpr int ROWS = KvShape<T>::ROWS;
+  const int *myri = ri + 64 * S.wave;
+  float *myst = st + kStatWave * S.wave;
+  const int rh = myri[S.lane];
+  const float *srow = S.sbase + 3 * (int64_t)rh;
+  dma_lds4(myst, srow);
+  dma_lds4(myst + 64, srow + 1);
+  dma_lds4(myst + 128, srow + 2);
+  dma_lds4(myst + 192, S.pos_tab + min(c * ROWS + S.lane, S.nqh - 1));
+  S.io_q.issue_at([&](int r) { return S.qbase + (int64_t)myri[r] * D; }, *Q);
+  S.io_g.issue_at([&](int r) { return S.gbase + (int64_t)myri[r] * D; }, *G);
+}
+
+// Replace max by lse2 in this wave's statistics of chunk c (landed); returns the
+// smallest position over the chunk's real rows (INT_MAX if none).  Rows past the
+// sequence's last qh row get lse2 = +inf, so P = 0 for them with or without the
+// per-element test.
+template <typename T, int D>
+__device__ __forceinline__ int convert_stats(PagedState<T, D> &S, int c, float *st) {
+  constexpr int ROWS = KvShape<T>::ROWS;
+  float *myst = st + kStatWave * S.wave;
+  const int l = S.lane;
+  const bool real = l < ROWS && c * ROWS + l < S.nqh;
+  const float m = myst[l], den = myst[64 + l];
+  const int pos = __float_as_int(myst[192 + l]);
+  myst[l] = (real && den > 0.f) ? fmaf(m, kLog2e, log2f(den)) : INFINITY;
+  int mp = real ? pos : INT32_MAX;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mp = min(mp, __shfl_xor(mp, o));
+  return __builtin_amdgcn_readfirstlane(mp);
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void paged_step(const PagedParams &p, PagedState<T, D> &S, int c,
+                                           const Tile<T, D, KvShape<T>::ROWS> *Qc,
+                                           const Tile<T, D, KvShape<T>::ROWS> *Gc, float *stc,
+                                           Tile<T, D, KvShape<T>::ROWS> *Qn,
+                                           Tile<T, D, KvShape<T>::ROWS> *Gn, float *stn,
+                                           const int *rin, int *riw) {
+  constexpr int ROWS = KvShape<T>::ROWS;
+  constexpr int PER_CHUNK = 5 + 2 * ChunkIO<T, D, ROWS>::LOADS;
+  static_assert(PER_CHUNK < 16, "vmcnt budget");
+  const bool issued = c + 2 <= S.c_last;
+  if (issued) {
+    issue_rowinfo(S, c + 4, riw);  // always issued with the chunk: fixed count per step
+    issue_chunk(p, S, c + 2, rin, stn, Qn, Gn);
+  }
+  const int minpos = convert_stats(S, c, stc);
+  const bool check = !(S.all_valid && (!p.causal || minpos >= S.maxtok));
+  const float *myst = stc + kStatWave * S.wave;
+  const int *posv = reinterpret_cast<const int *>(myst + 192);
+  const int tok = S.tok, half = S.lane >> 5;
+  const bool causal = p.causal;
+  const float sl2 = p.scale_log2;
+  kv_chunk<T, D>(S.kf, S.vf, S.dk, S.dv, Qc, Gc, myst, myst + 128, p.scale, S.lane,
+                 [&](int u, const f32x16 &acc, float *sc) {
+#pragma unroll
+                   for (int r = 0; r < 16; ++r) sc[r] = acc[r] * sl2;
+                   if (check) {
+#pragma unroll
+                     for (int g = 0; g < 4; ++g) {
+                       const int4 p4 = *reinterpret_cast<const int4 *>(&posv[32 * u + 8 * g + 4 * half]);
+                       const int pp[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+                       for (int e = 0; e < 4; ++e) {
+                         const bool vis = tok >= 0 && (!causal || tok <= pp[e]);
+                         sc[4 * g + e] = vis ? sc[4 * g + e] : -INFINITY;
+                       }
+                     }
+                   }
+                 });
+  if (issued) {
+    S.io_q.complete(*Qn);
+    S.io_g.complete(*Gn);
+  }
+  if constexpr (ChunkIO<T, D, ROWS>::DIRECT) {
+    if (issued)
+      wait_vmem_le<PER_CHUNK>();
+    else
+      wait_vmem();
+  } else {
+    wait_vmem();
+  }
+  __syncthreads();
+}
+
+// One link: all chunks of the sequence's qh rows, triple-buffered as in the
+// dense kernels (chunk c in buffer c % 3; rowinfo of chunk k in buffer k % 3,
+// fetched at step k - 4 and read at step k - 2).
+template <typename T, int D>
+__device__ __forceinline__ void paged_run(
+    const PagedParams &p, PagedState<T, D> &S, Tile<T, D, KvShape<T>::ROWS> *__restrict__ Q0,
+    Tile<T, D, KvShape<T>::ROWS> *__restrict__ Q1, Tile<T, D, KvShape<T>::ROWS> *__restrict__ Q2,
+    Tile<T, D, KvShape<T>::ROWS> *__restrict__ G0, Tile<T, D, KvShape<T>::ROWS> *__restrict__ G1,
+    Tile<T, D, KvShape<T>::ROWS> *__restrict__ G2, float *__restrict__ s0,
+    float *__restrict__ s1, float *__restrict__ s2, int *__restrict__ r0, int *__restrict__ r1,
+    int *__restrict__ r2) {
+  const int c_last = S.c_last;
+  issue_rowinfo(S, 0, r0);
+  issue_rowinfo(S, 1, r1);
+  issue_rowinfo(S, 2, r2);
+  wait_vmem();
+  issue_chunk(p, S, 0, r0, s0, Q0, G0);
+  S.io_q.complete(*Q0);
+  S.io_g.complete(*G0);
+  if (c_last >= 1) {
+    issue_chunk(p, S, 1, r1, s1, Q1, G1);
+    S.io_q.complete(*Q1);
+    S.io_g.complete(*G1);
+  }
+  issue_rowinfo(S, 3, r0);
+  wait_vmem();
+  __syncthreads();
+  int c = 0;
+  for (; c + 2 <= c_last; c += 3) {
+    paged_step<T, D>(p, S, c, Q0, G0, s0, Q2, G2, s2, r2, r1);
+    paged_step<T, D>(p, S, c + 1, Q1, G1, s1, Q0, G0, s0, r0, r2);
+    paged_step<T, D>(p, S, c + 2, Q2, G2, s2, Q1, G1, s1, r1, r0);
+  }
+  if (c <= c_last) paged_step<T, D>(p, S, c, Q0, G0, s0, Q2, G2, s2, r2, r1);
+  if (c + 1 <= c_last) paged_step<T, D>(p, S, c + 1, Q1, G1, s1, Q0, G0, s0, r0, r2);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_paged_kv_bwd(const PagedParams p) {
+  typedef MT<T> M;
+  constexpr int KS = M::KS, KL = M::KL, NSD = D / KS, NT = D / 32, ROWS = KvShape<T>::ROWS;
+  __shared__ Tile<T, D, ROWS> Qs0, Qs1, Qs2, Gs0, Gs1, Gs2;
+  __shared__ __attribute__((aligned(16))) float st0[kStatWords], st1[kStatWords], st2[kStatWords];
+  __shared__ __attribute__((aligned(16))) int ri0[kRiWords], ri1[kRiWords], ri2[kRiWords];
+
+  PagedState<T, D> S;
+  S.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  S.lane = threadIdx.x & 63;
+  const int l32 = S.lane & 31, half = S.lane >> 5;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int g = L / p.items, item = L % p.items;  // consecutive ids: one KV head, adjacent items
+  const int32_t *plan = p.plan;
+
+  const int ent = plan[p.off_item_slots + item * plan::kItemSlots + 32 * S.wave + l32];
+  const bool live = ent >= 0 && (ent & 1);
+  const int64_t krow_idx = ((int64_t)(ent >= 0 ? ent >> 1 : 0) * p.kv_heads + g) * D;
+  const T *krow = (const T *)p.k_pool + krow_idx;
+  const T *vrow = (const T *)p.v_pool + krow_idx;
+#pragma unroll
+  for (int s = 0; s < NSD; ++s) {
+    S.kf[s] = load_frag<T>(krow, s * KS + half * KL, live);
+    S.vf[s] = load_frag<T>(vrow, s * KS + half * KL, live);
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) S.dk[t] = S.dv[t] = f32x16{};
+  S.io_q.init();
+  S.io_g.init();
+  const int hg = g * p.group;
+  S.qbase = (const T *)p.q + (int64_t)hg * D;
+  S.gbase = (const T *)p.dy + (int64_t)hg * D;
+  S.sbase = p.stats + 3 * (int64_t)hg;
+
+  const int lb = plan[p.off_item_links + item], le = plan[p.off_item_links + item + 1];
+  for (int li = lb; li < le; ++li) {
+    const int seq = plan[p.off_link_seq + li];
+    const int32_t *info = plan + p.off_link_info + plan::LINK_INFO_WORDS * li;
+    const int mintok = info[plan::LI_MIN_TOK];
+    if (p.causal && mintok > plan[p.off_seq_maxpos + seq]) continue;  // no row sees the item
+    const int qh0 = plan[p.off_seq_qh + seq];
+    S.nqh = plan[p.off_seq_qh + seq + 1] - qh0;
+    if (S.nqh <= 0) continue;
+    S.maxtok = info[plan::LI_MAX_TOK];
+    S.all_valid = info[plan::LI_ALL_VALID] != 0;
+    S.tok = plan[p.off_link_tok + li * plan::kItemSlots + 32 * S.wave + l32];
+    S.rh_tab = plan + p.off_qh_rh + qh0;
+    S.pos_tab = plan + p.off_qh_pos + qh0;
+    S.c_last = (S.nqh - 1) / ROWS;
+    paged_run<T, D>(p, S, &Qs0, &Qs1, &Qs2, &Gs0, &Gs1, &Gs2, st0, st1, st2, ri0, ri1, ri2);
+  }
+
+  if (ent < 0) return;
+  T *dkrow = (T *)p.dk_pool + krow_idx;
+  T *dvrow = (T *)p.dv_pool + krow_idx;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int d0 = 32 * t + 8 * q + 4 * half;
+      const f32x16 &a = S.dk[t], &b = S.dv[t];
+      if (p.need_dk)
+        store4<T>(dkrow + d0, live ? a[4 * q] : 0.f, live ? a[4 * q + 1] : 0.f,
+                  live ? a[4 * q + 2] : 0.f, live ? a[4 * q + 3] : 0.f);
+      if (p.need_dv)
+        store4<T>(dvrow + d0, live ? b[4 * q] : 0.f, live ? b[4 * q + 1] : 0.f,
+                  live ? b[4 * q + 2] : 0.f, live ? b[4 * q + 3] : 0.f);
+    }
+}
+
+template <typename T, int D>
+static hipError_t launch_t(const PagedParams &p, int nblocks, hipStream_t stream) {
+  hipLaunchKernelGGL((k_paged_kv_bwd<T, D>), dim3(nblocks), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_paged(bool bf16_in, int D, const PagedParams &p, int nblocks,
+                        hipStream_t stream) {
+  if (bf16_in) {
+    if (D == 32) return launch_t<bf16, 32>(p, nblocks, stream);
+    if (D == 64) return launch_t<bf16, 64>(p, nblocks, stream);
+    if (D == 128) return launch_t<bf16, 128>(p, nblocks, stream);
+  } else {
+    if (D == 32) return launch_t<float, 32>(p, nblocks, stream);
+    if (D == 64) return launch_t<float, 64>(p, nblocks, stream);
+    if (D == 128) return launch_t<float, 128>(p, nblocks, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace attn

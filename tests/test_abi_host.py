@@ -120,3 +120,92 @@ def test_unrequested_outputs_may_be_null():
     a = _args(wrt=_abi.ATTN_WRT_Q, dk=0, dv=0, q=0)
     rc, msg = _rc(a)
     assert rc == _abi.ATTN_E_INVALID and msg.startswith("q is NULL")
+
+
+# ---------------------------------------------------------------------------
+# attn_bwd_paged: validation happens on the host before any launch.
+
+def test_paged_args_struct_size():
+    # 9 int32 + float, then 9 pointers
+    assert ctypes.sizeof(_abi.AttnBwdPagedArgs) == 40 + 9 * 8
+
+
+def _paged_plan(heads=4, kv_heads=2):
+    import numpy as np
+    lens = np.array([20, 9], np.int32)
+    bt = np.array([[3, 0], [1, -1]], np.int32)
+    qs = np.array([0, 0, 1], np.int32)
+    qp = np.array([18, 19, 8], np.int32)
+    return sdb.paged_plan(lens, bt, qs, qp, heads=heads, kv_heads=kv_heads, page_size=16,
+                          pool_pages=4)
+
+
+def _paged_args(the_plan, **kw):
+    a = _abi.AttnBwdPagedArgs()
+    a.dtype, a.need, a.heads, a.kv_heads, a.head_dim = 1, 3, 4, 2, 64
+    a.page_size, a.causal, a.nq, a.pool_pages, a.scale = 16, 1, 3, 4, 0.125
+    base = 1 << 24  # fake, aligned, disjoint addresses: only validated, never touched
+    for i, name in enumerate(("q", "dy", "k_pool", "v_pool", "stats", "plan", "dk_pool",
+                              "dv_pool")):
+        setattr(a, name, base * (i + 1))
+    a.plan_host = the_plan.words.ctypes.data
+    for k_, v_ in kw.items():
+        setattr(a, k_, v_)
+    return a
+
+
+def _paged_rc(a):
+    lib = sdb.load_library()
+    rc = lib.attn_bwd_paged(ctypes.byref(a), None)
+    return rc, lib.attn_bwd_last_error().decode()
+
+
+@pytest.mark.parametrize("field,value,code,msg", [
+    ("dtype", 2, _abi.ATTN_E_INVALID, "dtype"),
+    ("need", 0, _abi.ATTN_E_INVALID, "need"),
+    ("need", 4, _abi.ATTN_E_INVALID, "need"),
+    ("head_dim", 48, _abi.ATTN_E_UNSUPPORTED, "head_dim"),
+    ("causal", 2, _abi.ATTN_E_INVALID, "causal"),
+    ("heads", 8, _abi.ATTN_E_INVALID, "plan was built"),
+    ("page_size", 8, _abi.ATTN_E_INVALID, "plan was built"),
+    ("nq", 4, _abi.ATTN_E_INVALID, "plan was built"),
+    ("pool_pages", 5, _abi.ATTN_E_INVALID, "plan was built"),
+    ("plan", 0, _abi.ATTN_E_INVALID, "plan"),
+    ("q", 0, _abi.ATTN_E_INVALID, "q is NULL"),
+    ("stats", (1 << 24) * 5 + 4, _abi.ATTN_E_UNSUPPORTED, "aligned"),
+    ("dk_pool", 0, _abi.ATTN_E_INVALID, "dk_pool is NULL"),
+    ("dv_pool", (1 << 24) * 3, _abi.ATTN_E_INVALID, "overlaps"),
+    ("scale", float("inf"), _abi.ATTN_E_INVALID, "scale"),
+])
+def test_paged_rejections(field, value, code, msg):
+    plan = _paged_plan()
+    rc, err = _paged_rc(_paged_args(plan, **{field: value}))
+    assert rc == code and msg in err, (rc, err)
+
+
+def test_paged_rejects_foreign_plan():
+    import numpy as np
+    plan = _paged_plan()
+    words = plan.words.copy()
+    words[0] = 12345
+    a = _paged_args(plan)
+    a.plan_host = words.ctypes.data
+    rc, err = _paged_rc(a)
+    assert rc == _abi.ATTN_E_INVALID and "magic" in err
+    words = plan.words.copy()
+    words[_abi.W_OFF_LINK_TOK] = 10 ** 8
+    a.plan_host = words.ctypes.data
+    rc, err = _paged_rc(a)
+    assert rc == _abi.ATTN_E_INVALID and "offsets" in err
+    assert np.array_equal(plan.words[:2], [_abi.PLAN_MAGIC, len(plan.words)])
+
+
+def test_paged_empty_plan_is_a_no_op():
+    import numpy as np
+    plan = sdb.paged_plan(np.zeros(1, np.int32), np.zeros((1, 1), np.int32), np.zeros(0, np.int32),
+                          np.zeros(0, np.int32), heads=4, kv_heads=2, page_size=16, pool_pages=4)
+    assert plan.items == 0
+    a = _paged_args(plan, nq=0)
+    for name in ("q", "dy", "k_pool", "v_pool", "stats", "dk_pool", "dv_pool"):
+        setattr(a, name, 0)
+    assert _paged_rc(a)[0] == _abi.ATTN_OK
