@@ -2,6 +2,7 @@
 """Benchmark of the dense attention backward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--mask causal|window]
+    python bench.py --workload paged [--steps K] [--warmup W]
 
 Workload: bf16 Q, K, V, dY of shape [B=4, S=2048, H=16, D=128] (N(0,1), seeded,
 already resident in HBM), fp32 accumulation, bf16 dQ, dK, dV, causal mask.  One
@@ -17,6 +18,15 @@ Prints one JSON line.  Besides the contract fields it carries
                rocprofv3 FETCH_SIZE / WRITE_SIZE measurement when it was taken
                on the current kernel source, else null;
   cpu_baseline the CPU oracle timed on a bounded sample of the same workload.
+
+--workload paged measures the paged grouped-query history backward instead
+(ruDNN `history_backward`): bf16, 32 query / 8 KV heads, D 128, page 16, 16
+sequences of UniformInt[256, 4096] tokens scattered through a pool with 25%
+unused pages, 64 queries per sequence at its last positions, causal, supplied
+fp32 row statistics; one step = one attn_bwd_paged call (plan built and
+uploaded beforehand).  Its roofline is HBM: algorithmic bytes (K / V history
+read once, dK / dV written over the listed pages, Q, dY and statistics read
+once) over the kernel time.
 """
 from __future__ import annotations
 
@@ -34,9 +44,15 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # MI355X dense MFMA peaks
 HBM_PEAK_GBS = 8000.0
 # Contractions each kernel issues per visible (query, key) pair, 2 D flops each.
 CONTRACTIONS = {"row_stats": 2, "kv": 4, "dq": 3}
-KERNEL_NAMES = {"row_stats": "k_row_stats", "kv": "k_kv_bwd", "dq": "k_dq_bwd"}
+KERNEL_NAMES = {"row_stats": "k_row_stats", "kv": "k_kv_bwd", "dq": "k_dq_bwd",
+                "paged": "k_paged_kv_bwd"}
 KERNEL_SOURCES = ["scaled_dot_product_bwd_amd/csrc/dense_kernels.hip",
-                  "scaled_dot_product_bwd_amd/csrc/device_common.hpp"]
+                  "scaled_dot_product_bwd_amd/csrc/device_common.hpp",
+                  "scaled_dot_product_bwd_amd/csrc/kv_core.hpp"]
+PAGED_SOURCES = ["scaled_dot_product_bwd_amd/csrc/paged_kernels.hip",
+                 "scaled_dot_product_bwd_amd/csrc/paged.hpp",
+                 "scaled_dot_product_bwd_amd/csrc/device_common.hpp",
+                 "scaled_dot_product_bwd_amd/csrc/kv_core.hpp"]
 
 
 def log(msg):
@@ -55,18 +71,18 @@ def visible_pairs(Sq, Sk, mask, window):
     return total
 
 
-def source_hash():
+def source_hash(sources=None):
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def stored_traffic(kernel):
-    """Per-launch HBM bytes from profiles/traffic_<kernel>_*.txt, if measured on
+def stored_traffic(kernel, tag="b4h16s2048d128_causal", sources=None):
+    """Per-launch HBM bytes from profiles/traffic_<kernel>_<tag>.txt, if measured on
     this kernel source (key: value lines)."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{KERNEL_NAMES[kernel]}_b4h16s2048d128_causal.txt")
+    path = os.path.join(ROOT, "profiles", f"traffic_{KERNEL_NAMES[kernel]}_{tag}.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -74,7 +90,7 @@ def stored_traffic(kernel):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha") != source_hash():
+    if kv.get("kernel_source_sha") != source_hash(sources):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -105,11 +121,156 @@ def counted_flops(B, H, Sq, Sk, D, mask, window):
     return 10.0 * D * B * H * visible_pairs(Sq, Sk, mask, window)
 
 
+def paged_stats_torch(w, dev, scale):
+    """Input synthesis for the paged workload: fp32 (max, denominator, delta) per
+    (row, head), with plain torch float32 ops on the device (the statistics are
+    an input of this backward, as on the pages)."""
+    import torch
+    heads, kv, ps = w["heads"], w["kv_heads"], w["page_size"]
+    group = heads // kv
+    q = w["q"].to(dev).float()
+    dy = w["dy"].to(dev).float()
+    kp = w["k_pool"].to(dev)
+    vp = w["v_pool"].to(dev)
+    stats = torch.zeros(q.shape[0], heads, 3, device=dev)
+    qs, qp = w["query_seq"].to(dev), w["query_pos"].to(dev)
+    for s, L in enumerate(w["seq_lens"].tolist()):
+        t = torch.arange(L, device=dev)
+        slots = w["block_table"][s].to(dev).long()[t // ps] * ps + t % ps
+        rows = torch.nonzero(qs == s).flatten()
+        K = kp[slots].float().repeat_interleave(group, dim=1).permute(1, 2, 0).contiguous()
+        V = vp[slots].float().repeat_interleave(group, dim=1).permute(1, 2, 0).contiguous()
+        Q = q[rows].permute(1, 0, 2).contiguous()           # [heads, r, D]
+        G = dy[rows].permute(1, 0, 2).contiguous()
+        sc = torch.bmm(Q, K) * scale                        # [heads, r, L]
+        vis = t[None, :] <= qp[rows][:, None]
+        sc = sc.masked_fill(~vis[None], float("-inf"))
+        m = sc.amax(-1)
+        e = torch.exp(sc - m[..., None])
+        den = e.sum(-1)
+        dp = torch.bmm(G, V)
+        delta = (e / den[..., None] * dp).sum(-1)
+        stats[rows] = torch.stack([m, den, delta], -1).permute(1, 0, 2)
+    return stats
+
+
+def paged_bytes(w, plan):
+    """Algorithmic HBM bytes of one paged backward: K / V history read once,
+    dK / dV written over every listed slot, Q, dY and the statistics read once."""
+    es = 2 if str(w["dtype"]).endswith("bfloat16") else 4
+    kvd = w["kv_heads"] * w["D"] * es
+    hist = int(w["seq_lens"].sum()) * kvd * 2
+    out = len(plan.listed_pages()) * w["page_size"] * kvd * 2
+    nq, heads, D = w["q"].shape
+    return hist + out + nq * heads * D * es * 2 + nq * heads * 3 * 4
+
+
+def paged_flops(w):
+    """Visible (row, head, token) triples x 8 D (four contractions)."""
+    total = 0
+    qs, qp = w["query_seq"].tolist(), w["query_pos"].tolist()
+    lens = w["seq_lens"].tolist()
+    for s, p in zip(qs, qp):
+        total += min(p + 1, lens[s])
+    return 8.0 * w["D"] * w["heads"] * total
+
+
+def cpu_baseline_paged(w, nseq):
+    import numpy as np
+    import oracle
+    sub = {k: v for k, v in w.items()}
+    keep = [s for s in range(nseq)]
+    sub["seq_lens"] = w["seq_lens"][keep]
+    sub["block_table"] = w["block_table"][keep]
+    rows = [r for r, s in enumerate(w["query_seq"].tolist()) if s in keep]
+    for n in ("query_seq", "query_pos", "q", "dy"):
+        sub[n] = w[n][rows]
+    threads = max(1, min(os.cpu_count() or 1, 16))
+    kw = dict(heads=w["heads"], kv_heads=w["kv_heads"], page_size=w["page_size"])
+    t0 = time.perf_counter()
+    st = oracle.paged_row_stats(sub, sub["q"], sub["dy"], w["k_pool"], w["v_pool"],
+                                nthreads=threads, **kw)
+    t1 = time.perf_counter()
+    oracle.paged_kv_bwd(sub, sub["q"], sub["dy"], w["k_pool"], w["v_pool"], st,
+                        np.zeros(w["k_pool"].shape), np.zeros(w["v_pool"].shape),
+                        nthreads=threads, **kw)
+    dt = time.perf_counter() - t1
+    flops = paged_flops(sub)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{nseq} of {len(w['seq_lens'])} sequences ({int(sub['seq_lens'].sum())} "
+                      f"tokens) of the same workload, float64 C oracle dK/dV "
+                      f"({t1 - t0:.2f} s of statistics not counted), {dt:.2f} s wall on "
+                      f"{threads} threads"}
+
+
+def main_paged(args, torch, sdb, dev):
+    import sdpa_inputs
+    log("bench: generating the paged workload")
+    w = sdpa_inputs.paged_workload(seed=1005)
+    D = w["D"]
+    scale = float(torch.tensor(1.0 / D ** 0.5, dtype=torch.float32))
+    plan = sdb.paged_plan(w["seq_lens"], w["block_table"], w["query_seq"], w["query_pos"],
+                          heads=w["heads"], kv_heads=w["kv_heads"], page_size=w["page_size"],
+                          pool_pages=w["pool_pages"], device=dev)
+    stats = paged_stats_torch(w, dev, scale)
+    q, dy, kp, vp = (w[n].to(dev) for n in ("q", "dy", "k_pool", "v_pool"))
+    dk, dv = torch.zeros_like(kp), torch.zeros_like(vp)
+    a = sdb.make_paged_args(q, dy, kp, vp, stats, plan, dk, dv, causal=True, scale=scale)
+    lib = sdb.load_library()
+    import ctypes
+
+    def step():
+        rc = lib.attn_bwd_paged(ctypes.byref(a), sdb._stream_handle(None))
+        if rc != 0:
+            raise RuntimeError(lib.attn_bwd_last_error().decode())
+
+    log(f"bench: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    if not all(torch.isfinite(x[w["live_slots"].to(dev)]).all().item() for x in (dk, dv)):
+        raise RuntimeError("non-finite gradients in the benchmark output")
+    nbytes = paged_bytes(w, plan)
+    flops = paged_flops(w)
+    gbs = nbytes / (ms / 1e3) / 1e9
+    tflops = flops / (ms / 1e3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: CPU oracle baseline on 2 sequences")
+        cpu = cpu_baseline_paged(w, 2)
+    wl = (f"paged_gqa_bwd nseq16 len[256,4096] heads32/8 D128 page16 q64/seq bf16 causal "
+          f"(tokens {int(w['seq_lens'].sum())}, pool pages {w['pool_pages']})")
+    line = {
+        "metric": "paged GQA history bwd (dK+dV) TFLOP/s & HBM GB/s",
+        "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl, "counted_flops": flops, "algorithmic_bytes": nbytes,
+                   "items": plan.items},
+        "pct_mfma_peak": round(100.0 * tflops / PEAK_TFLOPS["bf16"], 3),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": stored_traffic("paged", "paged_config5", PAGED_SOURCES),
+                     "kernel": KERNEL_NAMES["paged"], "kernel_ms": round(ms, 4),
+                     "bytes_per_launch": nbytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dense", choices=["dense", "paged"])
     ap.add_argument("--mask", default="causal", choices=["causal", "window"])
     ap.add_argument("--window", type=int, default=256)
     ap.add_argument("--cpu-heads", type=int, default=16,
@@ -141,6 +302,8 @@ def main():
         return
 
     sdb.load_library()
+    if args.workload == "paged":
+        return main_paged(args, torch, sdb, dev)
     log("bench: generating inputs")
     d = sdpa_inputs.dense_config_inputs(3)
     qc, kc, vc, gc = d["q"], d["k"], d["v"], d["dy"]

@@ -31,7 +31,7 @@ PLAN_ITEM_SLOTS = 128
 (W_MAGIC, W_WORDS, W_NSEQ, W_NQ, W_HEADS, W_KV_HEADS, W_PAGE_SIZE, W_POOL_PAGES, W_ITEMS,
  W_LINKS, W_QH, W_LISTED, W_OFF_ITEM_LINKS, W_OFF_ITEM_SLOTS, W_OFF_LINK_SEQ, W_OFF_LINK_INFO,
  W_OFF_LINK_TOK, W_OFF_SEQ_QH, W_OFF_QH_RH, W_OFF_QH_POS, W_OFF_SEQ_MAXPOS,
- W_OFF_LISTED) = range(22)
+ W_OFF_LISTED, W_OFF_SEQ_MINPOS) = range(23)
 
 
 class AttnError(RuntimeError):

@@ -93,7 +93,9 @@ int validate(const attn_bwd_args *a, Checked &c) {
   if (a->mask_kind == ATTN_MASK_KEYPAD && std::isnan(a->mask_threshold))
     return fail(ATTN_E_INVALID, "mask_threshold is NaN");
 
-  const int64_t nblk_q = (a->Sq + 127) / 128, nblk_k = (a->Sk + 127) / 128;
+  // Query-major kernels: 128 queries per workgroup; the KV-major kernel: 128 keys.
+  const int64_t qrows = 128;
+  const int64_t nblk_q = (a->Sq + qrows - 1) / qrows, nblk_k = (a->Sk + 127) / 128;
   const int64_t heads = a->B * a->H;
   if (a->H > 0 && a->B > INT32_MAX / a->H) return fail(ATTN_E_INVALID, "B * H too large");
   if (heads * (nblk_q > nblk_k ? nblk_q : nblk_k) > INT32_MAX)
@@ -136,6 +138,10 @@ int validate(const attn_bwd_args *a, Checked &c) {
     for (int j = 0; j < 3; ++j)
       if ((ts[i].st[j] * (int64_t)es) % 16)
         return fail(ATTN_E_UNSUPPORTED, "%s stride %d is not a multiple of 16 bytes", ts[i].name, j);
+    // Streamed chunks address their rows with 32-bit byte offsets.
+    if (i < 4 && ts[i].st[1] * 64 * (int64_t)es >= ((int64_t)1 << 31))
+      return fail(ATTN_E_UNSUPPORTED, "%s sequence stride %lld is too large (64 rows must span < 2 GiB)",
+                  ts[i].name, (long long)ts[i].st[1]);
     const int64_t n[4] = {a->B, ts[i].S, a->H, a->D};
     const int64_t st[4] = {ts[i].st[0], ts[i].st[1], ts[i].st[2], 1};
     rng[i] = extent(ts[i].ptr, n, st, es);
@@ -271,7 +277,7 @@ int validate_paged(const attn_bwd_paged_args *a, attn::PagedParams &p, int &nblo
   if (w[W_MAGIC] != kMagic) return fail(ATTN_E_INVALID, "plan_host is not a plan (bad magic)");
   const int64_t words = w[W_WORDS];
   if (words < HEADER_WORDS) return fail(ATTN_E_INVALID, "plan header is inconsistent");
-  for (int k = W_OFF_ITEM_LINKS; k <= W_OFF_LISTED; ++k)
+  for (int k = W_OFF_ITEM_LINKS; k <= W_OFF_SEQ_MINPOS; ++k)
     if (w[k] < HEADER_WORDS || w[k] > words) return fail(ATTN_E_INVALID, "plan offsets are inconsistent");
   if (w[W_HEADS] != a->heads || w[W_KV_HEADS] != a->kv_heads || w[W_PAGE_SIZE] != a->page_size ||
       w[W_NQ] != a->nq || w[W_POOL_PAGES] != a->pool_pages)
@@ -341,6 +347,7 @@ int validate_paged(const attn_bwd_paged_args *a, attn::PagedParams &p, int &nblo
   p.off_qh_rh = w[W_OFF_QH_RH];
   p.off_qh_pos = w[W_OFF_QH_POS];
   p.off_seq_maxpos = w[W_OFF_SEQ_MAXPOS];
+  p.off_seq_minpos = w[W_OFF_SEQ_MINPOS];
   return ATTN_OK;
 }
 

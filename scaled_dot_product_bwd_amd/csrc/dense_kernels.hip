@@ -26,6 +26,7 @@
 // stays hidden behind two chunks of compute.
 #include "device_common.hpp"
 #include "kv_core.hpp"
+#include "q_core.hpp"
 #include "launch.hpp"
 
 namespace attn {
@@ -51,176 +52,168 @@ __device__ __forceinline__ void end_step(bool issued) {
 }
 
 // ---------------------------------------------------------------------------
-// Row statistics.
-template <typename T, int D> struct RowStatsState {
+// Row statistics.  Per query row: the running max m (log2 domain), the
+// denominator l = sum 2^(s - m) and delta' = sum 2^(s - m) dP, rescaled
+// together whenever m grows; at the end delta = delta' / l = rowsum(P * dP)
+// (rlx-cpu `backward_dense_head_all`), with dP = dY V^T from phase A.
+template <typename T, int D> struct RsState {
   typedef MT<T> M;
-  static constexpr int NSD = D / M::KS, NT = D / 32;
-  typename M::frag qf[NSD];
-  f32x16 o[NT];
-  float m_run, l_run;
+  static constexpr int NSD = D / M::KS, NQB = QShape<T>::NQB;
+  typename M::frag qf[NQB][NSD], gf[NQB][NSD];
+  float m[NQB], l[NQB], dl[NQB];
+  int qi[NQB];
   ChunkIO<T, D> io_k, io_v;
   const T *kbase, *vbase;
-  int b, h, iw, qi, lane, l32, half, c_last;
+  int b, h, lane, half, c_last, buf;
 };
 
-template <typename T, int D, int MODE>
-__device__ __forceinline__ void row_stats_step(const DenseParams &p, RowStatsState<T, D> &S, int c,
-                                               const Tile<T, D> *Kc, const Tile<T, D> *Vc, int cn,
-                                               Tile<T, D> *Kn, Tile<T, D> *Vn) {
-  typedef MT<T> M;
-  constexpr int NSD = D / M::KS, NT = D / 32, CS = M::CSTEPS;
-  const int j0 = c * 32;
-  const bool issued = cn <= S.c_last;
-  if (issued) {
-    S.io_k.issue(S.kbase, p.ks[1], cn * 32, p.Sk, *Kn);
-    S.io_v.issue(S.vbase, p.vs[1], cn * 32, p.Sk, *Vn);
+// Per-element mask term of (query qi, key kj), log2 domain (query-major kernels).
+template <int MODE>
+__device__ __forceinline__ float q_adj(const DenseParams &p, int b, int h, int qi, int kj) {
+  if (!idx_visible(p, qi, kj)) return -INFINITY;
+  if constexpr (MODE == MODE_INDEX) {
+    return 0.f;
+  } else {
+    const float mv = p.mask[b * p.ms[0] + h * p.ms[1] + (int64_t)qi * p.ms[2] + (int64_t)kj * p.ms[3]];
+    if constexpr (MODE == MODE_KEYPAD)
+      return mv < p.thr ? -INFINITY : 0.f;
+    else
+      return mv * kLog2e;
   }
-  const bool check = MODE != MODE_INDEX || !tile_all_visible(p, S.iw, j0);
-  // S^T = K Q^T: rows = keys (A from LDS), columns = this lane's query.
-  typename M::frag ka[NSD];
-#pragma unroll
-  for (int s = 0; s < NSD; ++s) ka[s] = Kc->frag(S.l32, s, S.half);
-  f32x16 sacc = f32x16{};
-#pragma unroll
-  for (int s = 0; s < NSD; ++s) sacc = M::mma(ka[s], S.qf[s], sacc);
-
-  float sc[16];
-  const int qi = S.qi, half = S.half;
-  scores16<MODE>(p, sacc, sc, S.b, S.h, check, [&](int) { return qi; },
-                 [&](int r) { return j0 + kr(r, half); });
-  float mloc = sc[0];
-#pragma unroll
-  for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, sc[r]);
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-  const float m_new = fmaxf(S.m_run, mloc);
-  const float m_use = m_new == -INFINITY ? 0.f : m_new;
-  const float alpha = fast_exp2(S.m_run - m_use);
-  float psum = 0.f;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    sc[r] = fast_exp2(sc[r] - m_use);
-    psum += sc[r];
-  }
-  S.l_run = S.l_run * alpha + psum;
-  S.m_run = m_new;
-#pragma unroll
-  for (int t = 0; t < NT; ++t) S.o[t] *= alpha;
-
-  // O^T += V^T P^T: A = V read transposed from LDS, B = P straight from the S^T tile.
-#pragma unroll
-  for (int st = 0; st < CS; ++st) {
-    const typename M::frag pf = creuse<T>(sc, st);
-#pragma unroll
-    for (int t = 0; t < NT; ++t) S.o[t] = M::mma(Vc->tfrag(32 * t, st, S.lane), pf, S.o[t]);
-  }
-  if (issued) {
-    S.io_k.complete(*Kn);
-    S.io_v.complete(*Vn);
-  }
-  end_step<ChunkIO<T, D>::DIRECT, 2 * ChunkIO<T, D>::LOADS>(issued);
 }
 
 template <typename T, int D, int MODE>
-__device__ __forceinline__ void row_stats_run(const DenseParams &p, RowStatsState<T, D> &S,
-                                              int c_first, Tile<T, D> *__restrict__ K0,
-                                              Tile<T, D> *__restrict__ K1,
-                                              Tile<T, D> *__restrict__ K2,
-                                              Tile<T, D> *__restrict__ V0,
-                                              Tile<T, D> *__restrict__ V1,
-                                              Tile<T, D> *__restrict__ V2) {
-  const int c_last = S.c_last;
+__device__ __forceinline__ void rs_step(const DenseParams &p, RsState<T, D> &S, int c,
+                                        Tile<T, D> *Ks, Tile<T, D> *Vs, bool masked) {
+  constexpr int NQB = QShape<T>::NQB;
+  const int bc = S.buf, bn = bc == 0 ? 2 : bc - 1;
+  const bool issued = c + 2 <= S.c_last;
+  if (issued) {
+    S.io_k.issue(S.kbase, p.ks[1], (c + 2) * 32, p.Sk, Ks[bn]);
+    S.io_v.issue(S.vbase, p.vs[1], (c + 2) * 32, p.Sk, Vs[bn]);
+  }
+  f32x16 sacc[NQB], pacc[NQB];
+  q_phase_a<T, D, NQB>(&Ks[bc], &Vs[bc], S.qf, S.gf, sacc, pacc, S.lane);
+  const int j0 = c * 32, half = S.half;
+#pragma unroll
+  for (int q = 0; q < NQB; ++q) {
+    float s2[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s2[r] = sacc[q][r] * p.scale_log2;
+    if (MODE != MODE_INDEX || masked) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s2[r] += q_adj<MODE>(p, S.b, S.h, S.qi[q], j0 + kr(r, half));
+    }
+    float mx = s2[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s2[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(S.m[q], mx);
+    const float mu = mn == -INFINITY ? 0.f : mn;
+    const float al = fast_exp2(S.m[q] - mu);
+    float ls = 0.f, ds = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float pr = fast_exp2(s2[r] - mu);
+      ls += pr;
+      ds = fmaf(pr, pacc[q][r], ds);
+    }
+    S.l[q] = fmaf(S.l[q], al, ls);
+    S.dl[q] = fmaf(S.dl[q], al, ds);
+    S.m[q] = mn;
+  }
+  if (issued) {
+    S.io_k.complete(Ks[bn]);
+    S.io_v.complete(Vs[bn]);
+  }
+  end_step<ChunkIO<T, D>::DIRECT, 2 * ChunkIO<T, D>::LOADS>(issued);
+  S.buf = bc == 2 ? 0 : bc + 1;
+}
+
+// Prologue shared by the query-major kernels: chunks c_first and c_first + 1
+// into buffers 0 and 1.
+template <typename T, int D>
+__device__ __forceinline__ void q_prologue(const DenseParams &p, ChunkIO<T, D> &io_k,
+                                           ChunkIO<T, D> &io_v, const T *kbase, const T *vbase,
+                                           int c_first, int c_last, Tile<T, D> *Ks, Tile<T, D> *Vs) {
   if (c_first <= c_last) {
-    S.io_k.issue(S.kbase, p.ks[1], c_first * 32, p.Sk, *K0);
-    S.io_v.issue(S.vbase, p.vs[1], c_first * 32, p.Sk, *V0);
-    S.io_k.complete(*K0);
-    S.io_v.complete(*V0);
+    io_k.issue(kbase, p.ks[1], c_first * 32, p.Sk, Ks[0]);
+    io_v.issue(vbase, p.vs[1], c_first * 32, p.Sk, Vs[0]);
+    io_k.complete(Ks[0]);
+    io_v.complete(Vs[0]);
   }
   const bool second = c_first + 1 <= c_last;
   if (second) {
-    S.io_k.issue(S.kbase, p.ks[1], (c_first + 1) * 32, p.Sk, *K1);
-    S.io_v.issue(S.vbase, p.vs[1], (c_first + 1) * 32, p.Sk, *V1);
-    S.io_k.complete(*K1);
-    S.io_v.complete(*V1);
+    io_k.issue(kbase, p.ks[1], (c_first + 1) * 32, p.Sk, Ks[1]);
+    io_v.issue(vbase, p.vs[1], (c_first + 1) * 32, p.Sk, Vs[1]);
+    io_k.complete(Ks[1]);
+    io_v.complete(Vs[1]);
   }
   end_step<ChunkIO<T, D>::DIRECT, 2 * ChunkIO<T, D>::LOADS>(second);
-  int c = c_first;
-  for (; c + 2 <= c_last; c += 3) {
-    row_stats_step<T, D, MODE>(p, S, c, K0, V0, c + 2, K2, V2);
-    row_stats_step<T, D, MODE>(p, S, c + 1, K1, V1, c + 3, K0, V0);
-    row_stats_step<T, D, MODE>(p, S, c + 2, K2, V2, c + 4, K1, V1);
-  }
-  if (c <= c_last) row_stats_step<T, D, MODE>(p, S, c, K0, V0, c + 2, K2, V2);
-  if (c + 1 <= c_last) row_stats_step<T, D, MODE>(p, S, c + 1, K1, V1, c + 3, K0, V0);
 }
 
 template <typename T, int D, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_row_stats(const DenseParams p) {
   typedef MT<T> M;
-  constexpr int KS = M::KS, KL = M::KL, NSD = D / KS, NT = D / 32;
-  __shared__ Tile<T, D> Ks0, Ks1, Ks2, Vs0, Vs1, Vs2;
+  constexpr int KS = M::KS, KL = M::KL, NSD = D / KS, NQB = QShape<T>::NQB,
+                QROWS = QShape<T>::QROWS;
+  __shared__ Tile<T, D> Ks[3], Vs[3];
 
-  RowStatsState<T, D> S;
+  RsState<T, D> S;
   const int tid = threadIdx.x, w = tid >> 6;
   S.lane = tid & 63;
-  S.l32 = S.lane & 31;
   S.half = S.lane >> 5;
+  const int l32 = S.lane & 31, half = S.half;
   const int nb = p.nblk;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int blk = nb - 1 - (L % nb);  // the heaviest causal blocks first
   S.h = (L / nb) % p.H;
   S.b = L / (nb * p.H);
-  const int i0 = blk * 128;
-  S.iw = i0 + 32 * w;
-  S.qi = S.iw + S.l32;
-  const int b = S.b, h = S.h, qi = S.qi, half = S.half;
-  const bool qvalid = qi < p.Sq;
-
-  const T *qrow = (const T *)p.q + b * p.qs[0] + (int64_t)(qvalid ? qi : 0) * p.qs[1] + h * p.qs[2];
+  const int b = S.b, h = S.h;
+  const int i0 = blk * QROWS;
 #pragma unroll
-  for (int s = 0; s < NSD; ++s) S.qf[s] = load_frag<T>(qrow, s * KS + half * KL, qvalid);
-
+  for (int q = 0; q < NQB; ++q) {
+    const int qi = i0 + 32 * (NQB * w + q) + l32;
+    S.qi[q] = qi;
+    const bool qvalid = qi < p.Sq;
+    const T *qrow = (const T *)p.q + b * p.qs[0] + (int64_t)(qvalid ? qi : 0) * p.qs[1] + h * p.qs[2];
+    const T *grow = (const T *)p.dy + b * p.dys[0] + (int64_t)(qvalid ? qi : 0) * p.dys[1] + h * p.dys[2];
+#pragma unroll
+    for (int s = 0; s < NSD; ++s) {
+      S.qf[q][s] = load_frag<T>(qrow, s * KS + half * KL, qvalid);
+      S.gf[q][s] = load_frag<T>(grow, s * KS + half * KL, qvalid);
+    }
+    S.m[q] = -INFINITY;
+    S.l[q] = S.dl[q] = 0.f;
+  }
   S.kbase = (const T *)p.k + b * p.ks[0] + h * p.ks[2];
   S.vbase = (const T *)p.v + b * p.vs[0] + h * p.vs[2];
-  const int ilast = min(i0 + 128, p.Sq) - 1;
-  const int jlo = max(0, i0 + p.lo_off);
-  const int jhi = min(p.Sk - 1, (int)min((int64_t)ilast + p.hi_off, (int64_t)kBig));
-  const int c_first = jlo >> 5;
-  S.c_last = jhi >= jlo ? jhi >> 5 : c_first - 1;
-
-  S.m_run = -INFINITY;
-  S.l_run = 0.f;
-#pragma unroll
-  for (int t = 0; t < NT; ++t) S.o[t] = f32x16{};
-  S.io_k.init();
-  S.io_v.init();
+  const QRange R = q_range(p, i0, QROWS, MODE == MODE_INDEX);
+  S.c_last = R.c_last;
+  S.io_k.init(p.ks[1]);
+  S.io_v.init(p.vs[1]);
   // Let the fragment loads above land before the first chunk load is issued,
   // so the compiler knows they are complete inside the loop (otherwise it
   // would wait for them there, and with them for the chunk loads in flight).
   wait_vmem();
-  row_stats_run<T, D, MODE>(p, S, c_first, &Ks0, &Ks1, &Ks2, &Vs0, &Vs1, &Vs2);
+  q_prologue<T, D>(p, S.io_k, S.io_v, S.kbase, S.vbase, R.c_first, R.c_last, Ks, Vs);
+  S.buf = 0;
+  for (int c = R.c_first; c <= R.c_last; ++c)
+    rs_step<T, D, MODE>(p, S, c, Ks, Vs, c < R.cu0 || c > R.cu1);
 
-  // delta = dY . O / l  (O^T tile: lane holds its query, d = 32 t + kr(r, half)).
-  const float l_tot = S.l_run + __shfl_xor(S.l_run, 32);
-  const T *grow = (const T *)p.dy + b * p.dys[0] + (int64_t)(qvalid ? qi : 0) * p.dys[1] + h * p.dys[2];
-  float dsum = 0.f;
-  if (qvalid) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * t + 8 * g + 4 * half;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dsum += (float)grow[d0 + e] * S.o[t][4 * g + e];
-      }
-  }
-  dsum += __shfl_xor(dsum, 32);
-  if (qvalid && half == 0) {
-    const int64_t row = ((int64_t)b * p.H + h) * p.Sq + qi;
-    const bool empty = !(l_tot > 0.f);
-    p.st_m[row] = empty ? -INFINITY : S.m_run * kLn2;
-    p.st_l[row] = empty ? 0.f : l_tot;
-    p.st_delta[row] = empty ? 0.f : dsum / l_tot;
-    p.st_lse2[row] = empty ? INFINITY : S.m_run + __log2f(l_tot);
+  for (int q = 0; q < NQB; ++q) {
+    const float l_tot = S.l[q] + __shfl_xor(S.l[q], 32);
+    const float d_tot = S.dl[q] + __shfl_xor(S.dl[q], 32);
+    const int qi = S.qi[q];
+    if (qi < p.Sq && half == 0) {
+      const int64_t row = ((int64_t)b * p.H + h) * p.Sq + qi;
+      const bool empty = !(l_tot > 0.f);
+      p.st_m[row] = empty ? -INFINITY : S.m[q] * kLn2;
+      p.st_l[row] = empty ? 0.f : l_tot;
+      p.st_delta[row] = empty ? 0.f : d_tot / l_tot;
+      p.st_lse2[row] = empty ? -INFINITY : -(S.m[q] + __log2f(l_tot));  // -lse2
+    }
   }
 }
 
@@ -228,7 +221,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // dK / dV, KV-block-major.  A step covers ROWS = 32 * NSUB queries as NSUB
 // independent 32-row sub-tiles (kv_core.hpp).
 
-// Statistics of the ROWS rows of chunk i0 into LDS, [lse2 x ROWS | delta x ROWS]
+// Statistics of the ROWS rows of chunk i0 into LDS, [-lse2 x ROWS | delta x ROWS]
 // per wave copy: direct-to-LDS dword loads, each wave writing its own copy so
 // that every wave issues the same number of loads (STAT_LOADS).  Rows past Sq
 // repeat the last row; the index mask gives them P = 0.
@@ -255,7 +248,7 @@ template <typename T, int D> struct KvState {
   ChunkIO<T, D, ROWS> io_q, io_g;
   const T *qbase, *gbase;
   int64_t srow0;
-  int b, h, jw, kj, wave, lane, l32, half, c_last;
+  int b, h, jw, kj, wave, lane, l32, half, c_last, buf;
 };
 
 template <typename T, int D, int MODE>
@@ -268,74 +261,93 @@ __device__ __forceinline__ void kv_issue(const DenseParams &p, KvState<T, D> &S,
   issue_row_stats<ROWS>(p, S.srow0, c * ROWS, st, S.wave, S.lane);
 }
 
-template <typename T, int D, int MODE>
+// One chunk: request chunk c + 2, consume chunk c (MASKED: with the per-element
+// mask term), hand over.  Buffers rotate at run time: chunk c sits in buffer
+// S.buf, chunk c + 2 goes to the buffer chunk c - 1 used.
+template <typename T, int D, int MODE, bool MASKED>
 __device__ __forceinline__ void kv_step(const DenseParams &p, KvState<T, D> &S, int c,
-                                        const Tile<T, D, KvShape<T>::ROWS> *Qc,
-                                        const Tile<T, D, KvShape<T>::ROWS> *Gc,
-                                        const float *st_c, int cn,
-                                        Tile<T, D, KvShape<T>::ROWS> *Qn,
-                                        Tile<T, D, KvShape<T>::ROWS> *Gn, float *st_n) {
+                                        Tile<T, D, KvShape<T>::ROWS> *Qs,
+                                        Tile<T, D, KvShape<T>::ROWS> *Gs, float (*st)[8 * KvShape<T>::ROWS]) {
   constexpr int ROWS = KvShape<T>::ROWS;
   constexpr int PER_CHUNK = 2 * ChunkIO<T, D, ROWS>::LOADS + stat_loads<ROWS>();
+  const int bc = S.buf, bn = bc == 0 ? 2 : bc - 1;
   const int i0 = c * ROWS;
-  const bool issued = cn <= S.c_last;
-  if (issued) kv_issue<T, D, MODE>(p, S, cn, Qn, Gn, st_n);
-  const int kj = S.kj, half = S.half, jw = S.jw, b = S.b, h = S.h;
-  kv_chunk<T, D>(S.kf, S.vf, S.dk, S.dv, Qc, Gc, st_c, st_c + ROWS, p.scale, S.lane,
-                 [&](int u, const f32x16 &acc, float *sc) {
-                   const bool check = MODE != MODE_INDEX || !tile_all_visible(p, i0 + 32 * u, jw);
-                   scores16<MODE>(p, acc, sc, b, h, check,
-                                  [&](int r) { return i0 + 32 * u + kr(r, half); },
-                                  [&](int) { return kj; });
-                 });
+  const bool issued = c + 2 <= S.c_last;
+  if (issued) kv_issue<T, D, MODE>(p, S, c + 2, &Qs[bn], &Gs[bn], st[bn]);
+  const int kj = S.kj, half = S.half, b = S.b, h = S.h;
+  // Per-element mask term: the index rule, then padding or bias (log2 domain).
+  auto adj = [&](int u, int r) -> float {
+    const int i = i0 + 32 * u + kr(r, half);
+    if (!idx_visible(p, i, kj)) return -INFINITY;
+    if constexpr (MODE == MODE_INDEX) {
+      return 0.f;
+    } else {
+      const float mv = p.mask[b * p.ms[0] + h * p.ms[1] + (int64_t)i * p.ms[2] + (int64_t)kj * p.ms[3]];
+      if constexpr (MODE == MODE_KEYPAD)
+        return mv < p.thr ? -INFINITY : 0.f;
+      else
+        return mv * kLog2e;
+    }
+  };
+  const float *stc = st[bc];
+  kv_chunk<T, D, MASKED>(S.kf, S.vf, S.dk, S.dv, &Qs[bc], &Gs[bc], stc, stc + ROWS, p.scale_log2,
+                         S.lane, adj);
   if (issued) {
-    S.io_q.complete(*Qn);
-    S.io_g.complete(*Gn);
+    S.io_q.complete(Qs[bn]);
+    S.io_g.complete(Gs[bn]);
   }
   end_step<ChunkIO<T, D, ROWS>::DIRECT, PER_CHUNK>(issued);
+  S.buf = bc == 2 ? 0 : bc + 1;
 }
 
+// All visible chunks of the block, in ascending order.  Chunks every (query,
+// key) pair of which the index rule keeps (the causal or window band's
+// interior) run the unmasked body; the band's edges and padding / bias masks
+// the masked one.  Each variant has its own loop, so no loop body holds both.
 template <typename T, int D, int MODE>
 __device__ __forceinline__ void kv_run(const DenseParams &p, KvState<T, D> &S, int c_first,
-                                       Tile<T, D, KvShape<T>::ROWS> *__restrict__ Q0,
-                                       Tile<T, D, KvShape<T>::ROWS> *__restrict__ Q1,
-                                       Tile<T, D, KvShape<T>::ROWS> *__restrict__ Q2,
-                                       Tile<T, D, KvShape<T>::ROWS> *__restrict__ G0,
-                                       Tile<T, D, KvShape<T>::ROWS> *__restrict__ G1,
-                                       Tile<T, D, KvShape<T>::ROWS> *__restrict__ G2,
-                                       float *__restrict__ s0, float *__restrict__ s1,
-                                       float *__restrict__ s2) {
+                                       int j0b, Tile<T, D, KvShape<T>::ROWS> *Qs,
+                                       Tile<T, D, KvShape<T>::ROWS> *Gs,
+                                       float (*st)[8 * KvShape<T>::ROWS]) {
   constexpr int ROWS = KvShape<T>::ROWS;
   constexpr int PER_CHUNK = 2 * ChunkIO<T, D, ROWS>::LOADS + stat_loads<ROWS>();
   const int c_last = S.c_last;
   if (c_first <= c_last) {
-    kv_issue<T, D, MODE>(p, S, c_first, Q0, G0, s0);
-    S.io_q.complete(*Q0);
-    S.io_g.complete(*G0);
+    kv_issue<T, D, MODE>(p, S, c_first, &Qs[0], &Gs[0], st[0]);
+    S.io_q.complete(Qs[0]);
+    S.io_g.complete(Gs[0]);
   }
   const bool second = c_first + 1 <= c_last;
   if (second) {
-    kv_issue<T, D, MODE>(p, S, c_first + 1, Q1, G1, s1);
-    S.io_q.complete(*Q1);
-    S.io_g.complete(*G1);
+    kv_issue<T, D, MODE>(p, S, c_first + 1, &Qs[1], &Gs[1], st[1]);
+    S.io_q.complete(Qs[1]);
+    S.io_g.complete(Gs[1]);
   }
   end_step<ChunkIO<T, D, ROWS>::DIRECT, PER_CHUNK>(second);
-  int c = c_first;
-  for (; c + 2 <= c_last; c += 3) {
-    kv_step<T, D, MODE>(p, S, c, Q0, G0, s0, c + 2, Q2, G2, s2);
-    kv_step<T, D, MODE>(p, S, c + 1, Q1, G1, s1, c + 3, Q0, G0, s0);
-    kv_step<T, D, MODE>(p, S, c + 2, Q2, G2, s2, c + 4, Q1, G1, s1);
+  S.buf = 0;
+  // Unmasked chunks [cu0, cu1]: every row i of the chunk sees every key j of the
+  // block: j_last - i <= hi_off, j0 - i >= lo_off, i < Sq, j_last < Sk.
+  int cu0 = c_last + 1, cu1 = c_last;
+  if (MODE == MODE_INDEX && j0b + 128 <= p.Sk) {
+    const int64_t lo_i = max((int64_t)j0b + 127 - p.hi_off, (int64_t)0);
+    const int64_t hi_i = min((int64_t)j0b - p.lo_off, (int64_t)p.Sq - 1);
+    cu0 = (int)min((lo_i + ROWS - 1) / ROWS, (int64_t)c_last + 1);
+    cu1 = (int)min((hi_i + 1) / ROWS - 1, (int64_t)c_last);
+    if (cu0 < c_first) cu0 = c_first;
+    if (cu1 < cu0 - 1) cu1 = cu0 - 1;
   }
-  if (c <= c_last) kv_step<T, D, MODE>(p, S, c, Q0, G0, s0, c + 2, Q2, G2, s2);
-  if (c + 1 <= c_last) kv_step<T, D, MODE>(p, S, c + 1, Q1, G1, s1, c + 3, Q0, G0, s0);
+  int c = c_first;
+  for (; c < cu0; ++c) kv_step<T, D, MODE, true>(p, S, c, Qs, Gs, st);
+  for (; c <= cu1; ++c) kv_step<T, D, MODE, false>(p, S, c, Qs, Gs, st);
+  for (; c <= c_last; ++c) kv_step<T, D, MODE, true>(p, S, c, Qs, Gs, st);
 }
 
 template <typename T, int D, int MODE>
 __global__ __launch_bounds__(256) void k_kv_bwd(const DenseParams p) {
   typedef MT<T> M;
   constexpr int KS = M::KS, KL = M::KL, NSD = D / KS, NT = D / 32, ROWS = KvShape<T>::ROWS;
-  __shared__ Tile<T, D, ROWS> Qs0, Qs1, Qs2, Gs0, Gs1, Gs2;
-  __shared__ __attribute__((aligned(16))) float st0[8 * ROWS], st1[8 * ROWS], st2[8 * ROWS];
+  __shared__ Tile<T, D, ROWS> Qs[3], Gs[3];
+  __shared__ __attribute__((aligned(16))) float st[3][8 * ROWS];
 
   KvState<T, D> S;
   const int w = threadIdx.x >> 6;
@@ -373,10 +385,10 @@ __global__ __launch_bounds__(256) void k_kv_bwd(const DenseParams p) {
 
 #pragma unroll
   for (int t = 0; t < NT; ++t) S.dk[t] = S.dv[t] = f32x16{};
-  S.io_q.init();
-  S.io_g.init();
+  S.io_q.init(p.qs[1]);
+  S.io_g.init(p.dys[1]);
   wait_vmem();  // fragment loads complete before the loop (see k_row_stats)
-  kv_run<T, D, MODE>(p, S, c_first, &Qs0, &Qs1, &Qs2, &Gs0, &Gs1, &Gs2, st0, st1, st2);
+  kv_run<T, D, MODE>(p, S, c_first, j0b, Qs, Gs, st);
 
   if (!kvalid) return;
   T *dkrow = (T *)p.dk + b * p.dks[0] + (int64_t)kj * p.dks[1] + h * p.dks[2];
@@ -386,161 +398,141 @@ __global__ __launch_bounds__(256) void k_kv_bwd(const DenseParams p) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int d0 = 32 * t + 8 * g + 4 * half;
+      const float sc = p.scale;  // the factor of dS, applied once
       if (p.need_dk)
-        store4<T>(dkrow + d0, S.dk[t][4 * g], S.dk[t][4 * g + 1], S.dk[t][4 * g + 2], S.dk[t][4 * g + 3]);
+        store4<T>(dkrow + d0, sc * S.dk[t][4 * g], sc * S.dk[t][4 * g + 1], sc * S.dk[t][4 * g + 2],
+                  sc * S.dk[t][4 * g + 3]);
       if (p.need_dv)
         store4<T>(dvrow + d0, S.dv[t][4 * g], S.dv[t][4 * g + 1], S.dv[t][4 * g + 2], S.dv[t][4 * g + 3]);
     }
 }
 
 // ---------------------------------------------------------------------------
-// dQ, query-block-major.
+// dQ, query-block-major: per chunk P = 2^(s - lse2), dS' = P (dP - delta) and
+// dQ^T += K^T dS'^T (A = K read transposed from LDS, once per fragment for all
+// query blocks); the factor `scale` of dS is applied at the store.
 template <typename T, int D> struct DqState {
   typedef MT<T> M;
-  static constexpr int NSD = D / M::KS, NT = D / 32;
-  typename M::frag qf[NSD], gf[NSD];
-  f32x16 dq[NT];
+  static constexpr int NSD = D / M::KS, NT = D / 32, NQB = QShape<T>::NQB;
+  typename M::frag qf[NQB][NSD], gf[NQB][NSD];
+  f32x16 dq[NQB][NT];
+  float nlse[NQB], del[NQB];
+  int qi[NQB];
   ChunkIO<T, D> io_k, io_v;
   const T *kbase, *vbase;
-  float lse, del;
-  int b, h, iw, qi, lane, l32, half, c_last;
+  int b, h, lane, half, c_last, buf;
 };
 
 template <typename T, int D, int MODE>
 __device__ __forceinline__ void dq_step(const DenseParams &p, DqState<T, D> &S, int c,
-                                        const Tile<T, D> *Kc, const Tile<T, D> *Vc, int cn,
-                                        Tile<T, D> *Kn, Tile<T, D> *Vn) {
+                                        Tile<T, D> *Ks, Tile<T, D> *Vs, bool masked) {
   typedef MT<T> M;
-  constexpr int NSD = D / M::KS, NT = D / 32, CS = M::CSTEPS;
-  const int j0 = c * 32;
-  const bool issued = cn <= S.c_last;
+  constexpr int NT = D / 32, CS = M::CSTEPS, NQB = QShape<T>::NQB;
+  const int bc = S.buf, bn = bc == 0 ? 2 : bc - 1;
+  const bool issued = c + 2 <= S.c_last;
   if (issued) {
-    S.io_k.issue(S.kbase, p.ks[1], cn * 32, p.Sk, *Kn);
-    S.io_v.issue(S.vbase, p.vs[1], cn * 32, p.Sk, *Vn);
+    S.io_k.issue(S.kbase, p.ks[1], (c + 2) * 32, p.Sk, Ks[bn]);
+    S.io_v.issue(S.vbase, p.vs[1], (c + 2) * 32, p.Sk, Vs[bn]);
   }
-  const bool check = MODE != MODE_INDEX || !tile_all_visible(p, S.iw, j0);
-  // S^T = K Q^T and dP^T = V dY^T: rows = keys, columns = this lane's query.
-  typename M::frag ka[NSD], va[NSD];
+  f32x16 sacc[NQB], pacc[NQB];
+  q_phase_a<T, D, NQB>(&Ks[bc], &Vs[bc], S.qf, S.gf, sacc, pacc, S.lane);
+  const int j0 = c * 32, half = S.half;
+  float dsv[NQB][16];
 #pragma unroll
-  for (int s = 0; s < NSD; ++s) {
-    ka[s] = Kc->frag(S.l32, s, S.half);
-    va[s] = Vc->frag(S.l32, s, S.half);
-  }
-  f32x16 sacc = f32x16{}, pacc = f32x16{};
+  for (int q = 0; q < NQB; ++q) {
+    float t[16];
 #pragma unroll
-  for (int s = 0; s < NSD; ++s) {
-    sacc = M::mma(ka[s], S.qf[s], sacc);
-    pacc = M::mma(va[s], S.gf[s], pacc);
-  }
-  float sc[16], dsv[16];
-  const int qi = S.qi, half = S.half;
-  scores16<MODE>(p, sacc, sc, S.b, S.h, check, [&](int) { return qi; },
-                 [&](int r) { return j0 + kr(r, half); });
+    for (int r = 0; r < 16; ++r) t[r] = fmaf(sacc[q][r], p.scale_log2, S.nlse[q]);
+    if (MODE != MODE_INDEX || masked) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const float pr = fast_exp2(sc[r] - S.lse);
-    dsv[r] = pr * (pacc[r] - S.del) * p.scale;
+      for (int r = 0; r < 16; ++r) t[r] += q_adj<MODE>(p, S.b, S.h, S.qi[q], j0 + kr(r, half));
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dsv[q][r] = fast_exp2(t[r]) * (pacc[q][r] - S.del[q]);
   }
-  // dQ^T += K^T dS^T: A = K read transposed from LDS, B = dS straight from the tile.
+  const Tile<T, D> *Kc = &Ks[bc];
 #pragma unroll
   for (int st = 0; st < CS; ++st) {
-    const typename M::frag sf = creuse<T>(dsv, st);
+    typename M::frag sf[NQB];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) S.dq[t] = M::mma(Kc->tfrag(32 * t, st, S.lane), sf, S.dq[t]);
+    for (int q = 0; q < NQB; ++q) sf[q] = creuse<T>(dsv[q], st);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const typename M::frag kt = Kc->tfrag(32 * t, st, S.lane);
+#pragma unroll
+      for (int q = 0; q < NQB; ++q) S.dq[q][t] = M::mma(kt, sf[q], S.dq[q][t]);
+    }
   }
   if (issued) {
-    S.io_k.complete(*Kn);
-    S.io_v.complete(*Vn);
+    S.io_k.complete(Ks[bn]);
+    S.io_v.complete(Vs[bn]);
   }
   end_step<ChunkIO<T, D>::DIRECT, 2 * ChunkIO<T, D>::LOADS>(issued);
-}
-
-template <typename T, int D, int MODE>
-__device__ __forceinline__ void dq_run(const DenseParams &p, DqState<T, D> &S, int c_first,
-                                       Tile<T, D> *__restrict__ K0, Tile<T, D> *__restrict__ K1,
-                                       Tile<T, D> *__restrict__ K2, Tile<T, D> *__restrict__ V0,
-                                       Tile<T, D> *__restrict__ V1, Tile<T, D> *__restrict__ V2) {
-  const int c_last = S.c_last;
-  if (c_first <= c_last) {
-    S.io_k.issue(S.kbase, p.ks[1], c_first * 32, p.Sk, *K0);
-    S.io_v.issue(S.vbase, p.vs[1], c_first * 32, p.Sk, *V0);
-    S.io_k.complete(*K0);
-    S.io_v.complete(*V0);
-  }
-  const bool second = c_first + 1 <= c_last;
-  if (second) {
-    S.io_k.issue(S.kbase, p.ks[1], (c_first + 1) * 32, p.Sk, *K1);
-    S.io_v.issue(S.vbase, p.vs[1], (c_first + 1) * 32, p.Sk, *V1);
-    S.io_k.complete(*K1);
-    S.io_v.complete(*V1);
-  }
-  end_step<ChunkIO<T, D>::DIRECT, 2 * ChunkIO<T, D>::LOADS>(second);
-  int c = c_first;
-  for (; c + 2 <= c_last; c += 3) {
-    dq_step<T, D, MODE>(p, S, c, K0, V0, c + 2, K2, V2);
-    dq_step<T, D, MODE>(p, S, c + 1, K1, V1, c + 3, K0, V0);
-    dq_step<T, D, MODE>(p, S, c + 2, K2, V2, c + 4, K1, V1);
-  }
-  if (c <= c_last) dq_step<T, D, MODE>(p, S, c, K0, V0, c + 2, K2, V2);
-  if (c + 1 <= c_last) dq_step<T, D, MODE>(p, S, c + 1, K1, V1, c + 3, K0, V0);
+  S.buf = bc == 2 ? 0 : bc + 1;
 }
 
 template <typename T, int D, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_dq_bwd(const DenseParams p) {
   typedef MT<T> M;
-  constexpr int KS = M::KS, KL = M::KL, NSD = D / KS, NT = D / 32;
-  __shared__ Tile<T, D> Ks0, Ks1, Ks2, Vs0, Vs1, Vs2;
+  constexpr int KS = M::KS, KL = M::KL, NSD = D / KS, NT = D / 32, NQB = QShape<T>::NQB,
+                QROWS = QShape<T>::QROWS;
+  __shared__ Tile<T, D> Ks[3], Vs[3];
 
   DqState<T, D> S;
   const int tid = threadIdx.x, w = tid >> 6;
   S.lane = tid & 63;
-  S.l32 = S.lane & 31;
   S.half = S.lane >> 5;
+  const int l32 = S.lane & 31, half = S.half;
   const int nb = p.nblk;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int blk = nb - 1 - (L % nb);
   S.h = (L / nb) % p.H;
   S.b = L / (nb * p.H);
-  const int i0 = blk * 128;
-  S.iw = i0 + 32 * w;
-  S.qi = S.iw + S.l32;
-  const int b = S.b, h = S.h, qi = S.qi, half = S.half;
-  const bool qvalid = qi < p.Sq;
-
-  const T *qrow = (const T *)p.q + b * p.qs[0] + (int64_t)(qvalid ? qi : 0) * p.qs[1] + h * p.qs[2];
-  const T *grow = (const T *)p.dy + b * p.dys[0] + (int64_t)(qvalid ? qi : 0) * p.dys[1] + h * p.dys[2];
+  const int b = S.b, h = S.h;
+  const int i0 = blk * QROWS;
 #pragma unroll
-  for (int s = 0; s < NSD; ++s) {
-    S.qf[s] = load_frag<T>(qrow, s * KS + half * KL, qvalid);
-    S.gf[s] = load_frag<T>(grow, s * KS + half * KL, qvalid);
+  for (int q = 0; q < NQB; ++q) {
+    const int qi = i0 + 32 * (NQB * w + q) + l32;
+    S.qi[q] = qi;
+    const bool qvalid = qi < p.Sq;
+    const T *qrow = (const T *)p.q + b * p.qs[0] + (int64_t)(qvalid ? qi : 0) * p.qs[1] + h * p.qs[2];
+    const T *grow = (const T *)p.dy + b * p.dys[0] + (int64_t)(qvalid ? qi : 0) * p.dys[1] + h * p.dys[2];
+#pragma unroll
+    for (int s = 0; s < NSD; ++s) {
+      S.qf[q][s] = load_frag<T>(qrow, s * KS + half * KL, qvalid);
+      S.gf[q][s] = load_frag<T>(grow, s * KS + half * KL, qvalid);
+    }
+    const int64_t srow = ((int64_t)b * p.H + h) * p.Sq + (qvalid ? qi : 0);
+    S.nlse[q] = qvalid ? p.st_lse2[srow] : -INFINITY;
+    S.del[q] = qvalid ? p.st_delta[srow] : 0.f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) S.dq[q][t] = f32x16{};
   }
-  const int64_t srow = ((int64_t)b * p.H + h) * p.Sq + (qvalid ? qi : 0);
-  S.lse = qvalid ? p.st_lse2[srow] : INFINITY;
-  S.del = qvalid ? p.st_delta[srow] : 0.f;
-
   S.kbase = (const T *)p.k + b * p.ks[0] + h * p.ks[2];
   S.vbase = (const T *)p.v + b * p.vs[0] + h * p.vs[2];
-  const int ilast = min(i0 + 128, p.Sq) - 1;
-  const int jlo = max(0, i0 + p.lo_off);
-  const int jhi = min(p.Sk - 1, (int)min((int64_t)ilast + p.hi_off, (int64_t)kBig));
-  const int c_first = jlo >> 5;
-  S.c_last = jhi >= jlo ? jhi >> 5 : c_first - 1;
-
-#pragma unroll
-  for (int t = 0; t < NT; ++t) S.dq[t] = f32x16{};
-  S.io_k.init();
-  S.io_v.init();
+  const QRange R = q_range(p, i0, QROWS, MODE == MODE_INDEX);
+  S.c_last = R.c_last;
+  S.io_k.init(p.ks[1]);
+  S.io_v.init(p.vs[1]);
   wait_vmem();  // fragment and statistics loads complete before the loop (see k_row_stats)
-  dq_run<T, D, MODE>(p, S, c_first, &Ks0, &Ks1, &Ks2, &Vs0, &Vs1, &Vs2);
+  q_prologue<T, D>(p, S.io_k, S.io_v, S.kbase, S.vbase, R.c_first, R.c_last, Ks, Vs);
+  S.buf = 0;
+  for (int c = R.c_first; c <= R.c_last; ++c)
+    dq_step<T, D, MODE>(p, S, c, Ks, Vs, c < R.cu0 || c > R.cu1);
 
-  if (!qvalid) return;
-  T *dqrow = (T *)p.dq + b * p.dqs[0] + (int64_t)qi * p.dqs[1] + h * p.dqs[2];
+  const float sc = p.scale;  // the factor of dS, applied once
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
+  for (int q = 0; q < NQB; ++q) {
+    const int qi = S.qi[q];
+    if (qi >= p.Sq) continue;
+    T *dqrow = (T *)p.dq + b * p.dqs[0] + (int64_t)qi * p.dqs[1] + h * p.dqs[2];
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-      store4<T>(dqrow + 32 * t + 8 * g + 4 * half, S.dq[t][4 * g], S.dq[t][4 * g + 1],
-                S.dq[t][4 * g + 2], S.dq[t][4 * g + 3]);
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        store4<T>(dqrow + 32 * t + 8 * g + 4 * half, sc * S.dq[q][t][4 * g], sc * S.dq[q][t][4 * g + 1],
+                  sc * S.dq[q][t][4 * g + 2], sc * S.dq[q][t][4 * g + 3]);
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -56,7 +56,7 @@ struct DenseParams {
   int lo_off, hi_off;
   int need_dk, need_dv;
   int nblk;  // tiles along the blocked sequence axis
-  float *st_m, *st_l, *st_delta, *st_lse2;  // [B * H * Sq] each
+  float *st_m, *st_l, *st_delta, *st_lse2;  // [B * H * Sq] each; st_lse2 holds -lse2
 };
 
 __device__ __forceinline__ int kr(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
@@ -198,6 +198,14 @@ __device__ __forceinline__ void dma_lds16(void *lds, const void *g) {
                : "s"(lds_addr(lds)), "v"(g)
                : "memory");
 }
+// The same with a wave-uniform 64-bit base and a 32-bit per-lane byte offset
+// (saddr form: no per-lane 64-bit address arithmetic); m0 = LDS byte address.
+__device__ __forceinline__ void dma_lds16_at(unsigned m0, const void *sbase, unsigned voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(m0), "v"(voff), "s"(sbase)
+               : "memory");
+}
 __device__ __forceinline__ void dma_lds4(void *lds, const void *g) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
                :
@@ -231,29 +239,58 @@ template <int D, int ROWS> struct ChunkIO<bf16, D, ROWS> {
   typedef Tile<bf16, D, ROWS> TileT;
   static constexpr int LOADS = TileT::NSEG / 4;
   static constexpr bool DIRECT = true;
-  int rloc[LOADS], col[LOADS];
+  unsigned off[LOADS];  // byte offset of load j from the chunk's first row
   int wave;
-  __device__ __forceinline__ void init() {
-    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // Chunk row and column of this lane's load j (pad slots: row ROWS - 1, col 0).
+  __device__ __forceinline__ void slot_rc(int j, int &row, int &col) const {
     const int lane = threadIdx.x & 63;
+    const int slot = (wave + 4 * j) * 64 + lane;  // 16-byte slot of the tile
+    const int grp = slot / (TileT::G / 8), o = slot % (TileT::G / 8);
+    const int q = o / (TileT::RS / 8), c = o % (TileT::RS / 8);
+    const bool data = grp < ROWS / 4 && q < 4 && c < D / 8;
+    row = data ? 4 * grp + q : ROWS - 1;
+    col = data ? 8 * c : 0;
+  }
+  // stride: elements between consecutive rows of the streamed matrix.
+  __device__ __forceinline__ void init(int64_t stride) {
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
-      const int slot = (wave + 4 * j) * 64 + lane;  // 16-byte slot of the tile
-      const int grp = slot / (TileT::G / 8), o = slot % (TileT::G / 8);
-      const int q = o / (TileT::RS / 8), c = o % (TileT::RS / 8);
-      const bool data = grp < ROWS / 4 && q < 4 && c < D / 8;
-      rloc[j] = data ? 4 * grp + q : ROWS - 1;
-      col[j] = data ? 8 * c : 0;
+      int row, col;
+      slot_rc(j, row, col);
+      off[j] = (unsigned)((row * stride + col) * 2);
     }
+  }
+  // LDS byte address of load j's segment of tile t.
+  __device__ __forceinline__ unsigned seg(const TileT &t, int j) const {
+    return lds_addr(t.a) + ((wave + 4 * j) << 10);
   }
   // Rows given by a functor: rowptr(r) is the start of chunk row r (0 <= r < ROWS).
   template <typename F> __device__ __forceinline__ void issue_at(F rowptr, TileT &t) {
 #pragma unroll
-    for (int j = 0; j < LOADS; ++j) dma_lds16(&t.a[(wave + 4 * j) * 512], rowptr(rloc[j]) + col[j]);
+    for (int j = 0; j < LOADS; ++j) {
+      int row, col;
+      slot_rc(j, row, col);
+      dma_lds16(&t.a[(wave + 4 * j) * 512], rowptr(row) + col);
+    }
   }
+  // Rows [r0, r0 + ROWS) of a matrix with `stride` (the one given to init) and
+  // `nrows` rows; rows past the end repeat the last row.  r0 < nrows.
   __device__ __forceinline__ void issue(const bf16 *base, int64_t stride, int r0, int nrows,
                                         TileT &t) {
-    issue_at([&](int r) { return base + (int64_t)min(r0 + r, nrows - 1) * stride; }, t);
+    const bf16 *cb = base + (int64_t)r0 * stride;  // wave-uniform
+    if (r0 + ROWS <= nrows) {
+#pragma unroll
+      for (int j = 0; j < LOADS; ++j) dma_lds16_at(seg(t, j), cb, off[j]);
+    } else {
+      const int last = nrows - 1 - r0;
+#pragma unroll
+      for (int j = 0; j < LOADS; ++j) {
+        int row, col;
+        slot_rc(j, row, col);
+        dma_lds16_at(seg(t, j), cb, (unsigned)((min(row, last) * stride + col) * 2));
+      }
+    }
   }
   __device__ __forceinline__ void complete(TileT &) {}
 };
@@ -265,7 +302,7 @@ template <int D, int ROWS> struct ChunkIO<float, D, ROWS> {
   static constexpr int CH = D / 4;  // 16-byte chunks per row
   static constexpr int PER = (ROWS * CH + 255) / 256;
   f32x4 r[PER];
-  __device__ __forceinline__ void init() {}
+  __device__ __forceinline__ void init(int64_t) {}
   template <typename F> __device__ __forceinline__ void issue_at(F rowptr, TileT &) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
@@ -294,50 +331,7 @@ __device__ __forceinline__ bool idx_visible(const DenseParams &p, int i, int j) 
   return i < p.Sq && j < p.Sk && d >= p.lo_off && d <= p.hi_off;
 }
 
-// True iff every (i, j) of the tile [i0, i0 + 32) x [j0, j0 + 32) is visible by
-// the index rule (no per-element test needed in MODE_INDEX).
-__device__ __forceinline__ bool tile_all_visible(const DenseParams &p, int i0, int j0) {
-  return i0 + 32 <= p.Sq && j0 + 32 <= p.Sk && (j0 + 31) - i0 <= p.hi_off &&
-         j0 - (i0 + 31) >= p.lo_off;
-}
-
-// True iff no (i, j) of the tile is visible by the index rule.
-__device__ __forceinline__ bool tile_none_visible(const DenseParams &p, int i0, int j0) {
-  return i0 >= p.Sq || j0 >= p.Sk || j0 - (i0 + 31) > p.hi_off || (j0 + 31) - i0 < p.lo_off;
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Turn the 16 raw dot products of a C tile into masked log2-domain scores.
-// Element r sits at (query qi(r), key kj(r)) as given by the functors.  The
-// index rule is only evaluated on tiles that need it (`check`, wave-uniform),
-// and then without branches.
-template <int MODE, typename QI, typename KJ>
-__device__ __forceinline__ void scores16(const DenseParams &p, const f32x16 &acc, float *s2, int b,
-                                         int h, bool check, QI qi, KJ kj) {
-#pragma unroll
-  for (int r = 0; r < 16; ++r) s2[r] = acc[r] * p.scale_log2;
-  if constexpr (MODE == MODE_INDEX) {
-    if (check) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s2[r] = idx_visible(p, qi(r), kj(r)) ? s2[r] : -INFINITY;
-    }
-  } else {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = qi(r), j = kj(r);
-      if (idx_visible(p, i, j)) {
-        const float mv = p.mask[b * p.ms[0] + h * p.ms[1] + (int64_t)i * p.ms[2] + (int64_t)j * p.ms[3]];
-        if constexpr (MODE == MODE_KEYPAD)
-          s2[r] = mv < p.thr ? -INFINITY : s2[r];
-        else
-          s2[r] = fmaf(mv, kLog2e, s2[r]);
-      } else {
-        s2[r] = -INFINITY;
-      }
-    }
-  }
-}
 
 // Workgroup id -> logical tile id.  The hardware hands workgroup i to XCD i % 8;
 // this gives every XCD a contiguous range of logical ids, so the tiles of one

@@ -7,13 +7,23 @@
 // 32 * NSUB query rows staged in LDS (Q, dY tiles and the row statistics) as
 // NSUB independent 32-row sub-tiles, following rlx-cpu 0.2.17
 // src/attention_bwd.rs `backward_dense_head_all`:
-//   S = Q K^T, dP = dY V^T               rows = queries, A from LDS
-//   P = exp2(S * scale * log2 e - lse2)   lse2 = m log2 e + log2 l, per row
-//   dS = P (dP - delta) scale
-//   dV^T += dY^T P,  dK^T += Q^T dS       A read transposed from LDS, B = C reuse
-// The masking of the raw scores is the caller's (`scores`), so the same body
-// serves index / padding / bias masks (dense) and page-table token positions
-// (paged).
+//   A  S = Q K^T, dP = dY V^T              rows = queries, A operand from LDS
+//   B  P = exp2(S * scale * log2 e - lse2)  lse2 = m log2 e + log2 l, per row
+//      dS' = P (dP - delta)                 (the factor `scale` of dS is applied
+//                                            to dK once, by the caller)
+//   C  dV^T += dY^T P,  dK^T += Q^T dS'     A read transposed from LDS, B = C reuse
+//
+// Schedule.  With one wave per SIMD nothing hides latency but the wave's own
+// instruction order, so the body is written as an explicit software pipeline
+// and fenced with scheduling barriers that the compiler keeps:
+//   * every MFMA's LDS operand is read three MFMAs ahead (a ring of four
+//     fragment registers), so an MFMA never waits for the LDS;
+//   * phase B of sub-tile 0 is spread over phase A of sub-tile 1, and phase B
+//     of sub-tile 1 over phase C of sub-tile 0, so the softmax VALU work issues
+//     while the matrix core runs.
+// Masking is decided per chunk by the caller: the unmasked body has no
+// per-element test at all; the masked one adds the caller's log2-domain term
+// (0, a bias, or -inf) to every score, branch-free.
 #pragma once
 
 #include "device_common.hpp"
@@ -28,71 +38,116 @@ template <typename T> struct KvShape {
   static constexpr int ROWS = 32 * NSUB;
 };
 
-// scores(u, acc, sc): turn the raw Q.K dot products `acc` of sub-tile u into the
-// 16 masked log2-domain scores sc[] of this lane (element r = query row
-// 32 u + kr(r, half) of the chunk, key = this lane's column).
-// lse2 / delta: the chunk's per-row statistics in LDS (row i at [i]).
-template <typename T, int D, typename Scores>
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// adj(u, r): log2-domain term added to the score of element r of sub-tile u
+// (query row 32 u + kr(r, half) of the chunk, key = this lane's column); only
+// called when MASKED.  nlse2 / delta: the chunk's per-row -lse2 and delta in
+// LDS (row i at [i]).
+template <typename T, int D, bool MASKED, typename Adj>
 __device__ __forceinline__ void kv_chunk(const typename MT<T>::frag *kf,
                                          const typename MT<T>::frag *vf, f32x16 *dk, f32x16 *dv,
                                          const Tile<T, D, KvShape<T>::ROWS> *Qc,
                                          const Tile<T, D, KvShape<T>::ROWS> *Gc,
-                                         const float *lse2, const float *delta, float scale,
-                                         int lane, Scores scores) {
+                                         const float *nlse2, const float *delta, float scale_log2,
+                                         int lane, Adj adj) {
   typedef MT<T> M;
+  typedef typename M::frag F;
   constexpr int NSD = D / M::KS, NT = D / 32, CS = M::CSTEPS;
   constexpr int NSUB = KvShape<T>::NSUB;
+  constexpr int NA = NSUB * NSD;    // phase-A steps (two MFMAs each: S and dP)
+  constexpr int NC = NSUB * CS * NT;  // phase-C steps (two MFMAs each: dV and dK)
+  constexpr int RING = 4;
   const int l32 = lane & 31, half = lane >> 5;
 
   f32x16 sacc[NSUB], pacc[NSUB];
+  float pv[NSUB][16], dsv[NSUB][16];
+  f32x4 nl4, dl4;  // statistics of the 4 rows of the current element group
 #pragma unroll
-  for (int u = 0; u < NSUB; ++u) {
-    typename M::frag qa[NSD], ga[NSD];
+  for (int u = 0; u < NSUB; ++u) sacc[u] = pacc[u] = f32x16{};
+
+  // Phase B for elements [r0, r1) of sub-tile u (needs sacc[u] / pacc[u] done).
+  // Elements 4g .. 4g + 3 are rows 8g + 4 half + 0..3: one vector read each.
+  auto softmax = [&](int u, int r0, int r1) {
 #pragma unroll
-    for (int s = 0; s < NSD; ++s) {
-      qa[s] = Qc->frag(32 * u + l32, s, half);
-      ga[s] = Gc->frag(32 * u + l32, s, half);
+    for (int r = r0; r < r1; ++r) {
+      if (r % 4 == 0 || r == r0) {
+        const int rb = 32 * u + 8 * (r / 4) + 4 * half;
+        nl4 = *reinterpret_cast<const f32x4 *>(&nlse2[rb]);
+        dl4 = *reinterpret_cast<const f32x4 *>(&delta[rb]);
+      }
+      const float nl = nl4[r % 4], dl = dl4[r % 4];
+      float t;
+      if constexpr (MASKED)
+        t = fmaf(sacc[u][r], scale_log2, nl + adj(u, r));
+      else
+        t = fmaf(sacc[u][r], scale_log2, nl);
+      const float pr = fast_exp2(t);
+      pv[u][r] = pr;
+      dsv[u][r] = pr * (pacc[u][r] - dl);
     }
-    sacc[u] = f32x16{};
-    pacc[u] = f32x16{};
+  };
+
+  // Phase A: S and dP.  Step a = (u, s) reads Q / dY row fragments.
+  F qa[RING], ga[RING];
+  auto load_a = [&](int a) {
+    const int u = a / NSD, s = a % NSD;
+    qa[a % RING] = Qc->frag(32 * u + l32, s, half);
+    ga[a % RING] = Gc->frag(32 * u + l32, s, half);
+  };
 #pragma unroll
-    for (int s = 0; s < NSD; ++s) {
-      sacc[u] = M::mma(qa[s], kf[s], sacc[u]);
-      pacc[u] = M::mma(ga[s], vf[s], pacc[u]);
+  for (int a = 0; a < RING - 1 && a < NA; ++a) load_a(a);
+#pragma unroll
+  for (int a = 0; a < NA; ++a) {
+    const int u = a / NSD, s = a % NSD;
+    sched_fence();
+    if (a + RING - 1 < NA) load_a(a + RING - 1);
+    sacc[u] = M::mma(qa[a % RING], kf[s], sacc[u]);
+    pacc[u] = M::mma(ga[a % RING], vf[s], pacc[u]);
+    // Sub-tile u - 1 is complete: spread its softmax over this sub-tile's steps.
+    if (NSUB > 1 && u >= 1) {
+      constexpr int PER = (16 + NSD - 1) / NSD;
+      const int r0 = s * PER, r1 = r0 + PER < 16 ? r0 + PER : 16;
+      if (r0 < 16) softmax(u - 1, r0, r1);
     }
   }
-  typename M::frag pf[NSUB][CS], sf[NSUB][CS];
+  sched_fence();
+  if constexpr (NSUB == 1) softmax(0, 0, 16);
+
+  // Phase C: dV and dK.  Step c = (u, st, t) reads two transposed fragments;
+  // the packed P / dS' operands of a (u, st) are built one step before their
+  // first MFMA.
+  F ta[RING], tb[RING], pf[NSUB][CS], sf[NSUB][CS];
+  auto load_c = [&](int c) {
+    const int u = c / (CS * NT), st = (c / NT) % CS, t = c % NT;
+    ta[c % RING] = Gc->tfrag(32 * t, st, lane, 32 * u);
+    tb[c % RING] = Qc->tfrag(32 * t, st, lane, 32 * u);
+  };
+  auto pack = [&](int c) {
+    const int u = c / (CS * NT), st = (c / NT) % CS;
+    pf[u][st] = creuse<T>(pv[u], st);
+    sf[u][st] = creuse<T>(dsv[u], st);
+  };
 #pragma unroll
-  for (int u = 0; u < NSUB; ++u) {
-    float sc[16], pv[16], dsv[16];
-    scores(u, sacc[u], sc);
+  for (int c = 0; c < RING - 1 && c < NC; ++c) load_c(c);
+  pack(0);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const f32x4 lse4 = *reinterpret_cast<const f32x4 *>(&lse2[32 * u + 8 * g + 4 * half]);
-      const f32x4 del4 = *reinterpret_cast<const f32x4 *>(&delta[32 * u + 8 * g + 4 * half]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * g + e;
-        const float pr = fast_exp2(sc[r] - lse4[e]);
-        pv[r] = pr;
-        dsv[r] = pr * (pacc[u][r] - del4[e]) * scale;
-      }
+  for (int c = 0; c < NC; ++c) {
+    const int u = c / (CS * NT), st = (c / NT) % CS, t = c % NT;
+    sched_fence();
+    if (c + RING - 1 < NC) load_c(c + RING - 1);
+    // The last sub-tile's softmax runs under the first sub-tile's phase C.
+    if (NSUB > 1 && u == 0) {
+      constexpr int PER = (16 + CS * NT - 1) / (CS * NT);
+      const int i = c % (CS * NT);
+      const int r0 = i * PER, r1 = r0 + PER < 16 ? r0 + PER : 16;
+      if (r0 < 16) softmax(NSUB - 1, r0, r1);
     }
-#pragma unroll
-    for (int st = 0; st < CS; ++st) {
-      pf[u][st] = creuse<T>(pv, st);
-      sf[u][st] = creuse<T>(dsv, st);
-    }
+    if (c + 1 < NC && (c + 1) % NT == 0) pack(c + 1);
+    dv[t] = M::mma(ta[c % RING], pf[u][st], dv[t]);
+    dk[t] = M::mma(tb[c % RING], sf[u][st], dk[t]);
   }
-#pragma unroll
-  for (int u = 0; u < NSUB; ++u)
-#pragma unroll
-    for (int st = 0; st < CS; ++st)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        dv[t] = M::mma(Gc->tfrag(32 * t, st, lane, 32 * u), pf[u][st], dv[t]);
-        dk[t] = M::mma(Qc->tfrag(32 * t, st, lane, 32 * u), sf[u][st], dk[t]);
-      }
+  sched_fence();
 }
 
 }  // namespace attn

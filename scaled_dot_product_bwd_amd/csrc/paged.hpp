@@ -58,6 +58,7 @@ enum Word {
   W_OFF_QH_POS,      // [qh] position of the row
   W_OFF_SEQ_MAXPOS,  // [nseq] largest position of the sequence's rows, -1 if none
   W_OFF_LISTED,      // [listed] listed physical pages, ascending
+  W_OFF_SEQ_MINPOS,  // [nseq] smallest position of the sequence's rows, INT32_MAX if none
   HEADER_WORDS = 32
 };
 
@@ -75,7 +76,7 @@ struct PagedParams {
   float scale, scale_log2;
   int items;
   int off_item_links, off_item_slots, off_link_seq, off_link_info, off_link_tok;
-  int off_seq_qh, off_qh_rh, off_qh_pos, off_seq_maxpos;
+  int off_seq_qh, off_qh_rh, off_qh_pos, off_seq_maxpos, off_seq_minpos;
 };
 
 }  // namespace attn

@@ -42,8 +42,7 @@ template <typename T, int D> struct PagedState {
   const T *qbase, *gbase;  // Q / dY at head g * group
   const float *sbase;      // statistics at head g * group
   const int32_t *rh_tab, *pos_tab;  // the link's sequence: qh rows from 0
-  int nqh, c_last, tok, maxtok, wave, lane;
-  bool all_valid;
+  int nqh, c_last, tok, maxtok, wave, lane, buf;
 };
 
 // Rowinfo of chunk c into this wave's copy: lane l <- rh of qh row c * ROWS + l
@@ -73,67 +72,51 @@ __device__ __forceinline__ void issue_chunk(const PagedParams &p, PagedState<T, 
   S.io_g.issue_at([&](int r) { return S.gbase + (int64_t)myri[r] * D; }, *G);
 }
 
-// Replace max by lse2 in this wave's statistics of chunk c (landed); returns the
-// smallest position over the chunk's real rows (INT_MAX if none).  Rows past the
-// sequence's last qh row get lse2 = +inf, so P = 0 for them with or without the
-// per-element test.
+// Replace max by -lse2 in this wave's statistics of chunk c (landed).  Rows past
+// the sequence's last qh row get -lse2 = -inf, so P = 0 for them with or without
+// the per-element test.
 template <typename T, int D>
-__device__ __forceinline__ int convert_stats(PagedState<T, D> &S, int c, float *st) {
+__device__ __forceinline__ void convert_stats(PagedState<T, D> &S, int c, float *st) {
   constexpr int ROWS = KvShape<T>::ROWS;
   float *myst = st + kStatWave * S.wave;
   const int l = S.lane;
   const bool real = l < ROWS && c * ROWS + l < S.nqh;
   const float m = myst[l], den = myst[64 + l];
-  const int pos = __float_as_int(myst[192 + l]);
-  myst[l] = (real && den > 0.f) ? fmaf(m, kLog2e, log2f(den)) : INFINITY;
-  int mp = real ? pos : INT32_MAX;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) mp = min(mp, __shfl_xor(mp, o));
-  return __builtin_amdgcn_readfirstlane(mp);
+  myst[l] = (real && den > 0.f) ? -fmaf(m, kLog2e, log2f(den)) : -INFINITY;  // -lse2
 }
 
-template <typename T, int D>
+// One chunk: request rowinfo of chunk c + 4 and the data of chunk c + 2,
+// convert and consume chunk c (MASKED: per-element visibility), hand over.
+// Chunk k's tiles, statistics and rowinfo sit in buffer k % 3 (S.buf = c % 3).
+template <typename T, int D, bool MASKED>
 __device__ __forceinline__ void paged_step(const PagedParams &p, PagedState<T, D> &S, int c,
-                                           const Tile<T, D, KvShape<T>::ROWS> *Qc,
-                                           const Tile<T, D, KvShape<T>::ROWS> *Gc, float *stc,
-                                           Tile<T, D, KvShape<T>::ROWS> *Qn,
-                                           Tile<T, D, KvShape<T>::ROWS> *Gn, float *stn,
-                                           const int *rin, int *riw) {
+                                           Tile<T, D, KvShape<T>::ROWS> *Qs,
+                                           Tile<T, D, KvShape<T>::ROWS> *Gs,
+                                           float (*st)[kStatWords], int (*ri)[kRiWords]) {
   constexpr int ROWS = KvShape<T>::ROWS;
   constexpr int PER_CHUNK = 5 + 2 * ChunkIO<T, D, ROWS>::LOADS;
   static_assert(PER_CHUNK < 16, "vmcnt budget");
+  const int bc = S.buf, bn = bc == 0 ? 2 : bc - 1, bz = bc == 2 ? 0 : bc + 1;
   const bool issued = c + 2 <= S.c_last;
   if (issued) {
-    issue_rowinfo(S, c + 4, riw);  // always issued with the chunk: fixed count per step
-    issue_chunk(p, S, c + 2, rin, stn, Qn, Gn);
+    issue_rowinfo(S, c + 4, ri[bz]);  // always issued with the chunk: fixed count per step
+    issue_chunk(p, S, c + 2, ri[bn], st[bn], &Qs[bn], &Gs[bn]);
   }
-  const int minpos = convert_stats(S, c, stc);
-  const bool check = !(S.all_valid && (!p.causal || minpos >= S.maxtok));
-  const float *myst = stc + kStatWave * S.wave;
+  convert_stats(S, c, st[bc]);
+  const float *myst = st[bc] + kStatWave * S.wave;
   const int *posv = reinterpret_cast<const int *>(myst + 192);
   const int tok = S.tok, half = S.lane >> 5;
   const bool causal = p.causal;
-  const float sl2 = p.scale_log2;
-  kv_chunk<T, D>(S.kf, S.vf, S.dk, S.dv, Qc, Gc, myst, myst + 128, p.scale, S.lane,
-                 [&](int u, const f32x16 &acc, float *sc) {
-#pragma unroll
-                   for (int r = 0; r < 16; ++r) sc[r] = acc[r] * sl2;
-                   if (check) {
-#pragma unroll
-                     for (int g = 0; g < 4; ++g) {
-                       const int4 p4 = *reinterpret_cast<const int4 *>(&posv[32 * u + 8 * g + 4 * half]);
-                       const int pp[4] = {p4.x, p4.y, p4.z, p4.w};
-#pragma unroll
-                       for (int e = 0; e < 4; ++e) {
-                         const bool vis = tok >= 0 && (!causal || tok <= pp[e]);
-                         sc[4 * g + e] = vis ? sc[4 * g + e] : -INFINITY;
-                       }
-                     }
-                   }
-                 });
+  // Slot visible to the row: its token exists and, when causal, is <= the position.
+  auto adj = [&](int u, int r) -> float {
+    const bool vis = tok >= 0 && (!causal || tok <= posv[32 * u + kr(r, half)]);
+    return vis ? 0.f : -INFINITY;
+  };
+  kv_chunk<T, D, MASKED>(S.kf, S.vf, S.dk, S.dv, &Qs[bc], &Gs[bc], myst, myst + 128,
+                         p.scale_log2, S.lane, adj);
   if (issued) {
-    S.io_q.complete(*Qn);
-    S.io_g.complete(*Gn);
+    S.io_q.complete(Qs[bn]);
+    S.io_g.complete(Gs[bn]);
   }
   if constexpr (ChunkIO<T, D, ROWS>::DIRECT) {
     if (issued)
@@ -144,52 +127,49 @@ __device__ __forceinline__ void paged_step(const PagedParams &p, PagedState<T, D
     wait_vmem();
   }
   __syncthreads();
+  S.buf = bz;
 }
 
-// One link: all chunks of the sequence's qh rows, triple-buffered as in the
-// dense kernels (chunk c in buffer c % 3; rowinfo of chunk k in buffer k % 3,
-// fetched at step k - 4 and read at step k - 2).
+// One link: all chunks of the sequence's qh rows (rowinfo of chunk k fetched at
+// step k - 4, read at step k - 2).  The link runs the unmasked body when every
+// lane holds a token that every row of the sequence sees; otherwise the masked
+// one.  Each variant has its own loop.
 template <typename T, int D>
-__device__ __forceinline__ void paged_run(
-    const PagedParams &p, PagedState<T, D> &S, Tile<T, D, KvShape<T>::ROWS> *__restrict__ Q0,
-    Tile<T, D, KvShape<T>::ROWS> *__restrict__ Q1, Tile<T, D, KvShape<T>::ROWS> *__restrict__ Q2,
-    Tile<T, D, KvShape<T>::ROWS> *__restrict__ G0, Tile<T, D, KvShape<T>::ROWS> *__restrict__ G1,
-    Tile<T, D, KvShape<T>::ROWS> *__restrict__ G2, float *__restrict__ s0,
-    float *__restrict__ s1, float *__restrict__ s2, int *__restrict__ r0, int *__restrict__ r1,
-    int *__restrict__ r2) {
+__device__ __forceinline__ void paged_run(const PagedParams &p, PagedState<T, D> &S,
+                                          bool masked, Tile<T, D, KvShape<T>::ROWS> *Qs,
+                                          Tile<T, D, KvShape<T>::ROWS> *Gs,
+                                          float (*st)[kStatWords], int (*ri)[kRiWords]) {
   const int c_last = S.c_last;
-  issue_rowinfo(S, 0, r0);
-  issue_rowinfo(S, 1, r1);
-  issue_rowinfo(S, 2, r2);
+  issue_rowinfo(S, 0, ri[0]);
+  issue_rowinfo(S, 1, ri[1]);
+  issue_rowinfo(S, 2, ri[2]);
   wait_vmem();
-  issue_chunk(p, S, 0, r0, s0, Q0, G0);
-  S.io_q.complete(*Q0);
-  S.io_g.complete(*G0);
+  issue_chunk(p, S, 0, ri[0], st[0], &Qs[0], &Gs[0]);
+  S.io_q.complete(Qs[0]);
+  S.io_g.complete(Gs[0]);
   if (c_last >= 1) {
-    issue_chunk(p, S, 1, r1, s1, Q1, G1);
-    S.io_q.complete(*Q1);
-    S.io_g.complete(*G1);
+    issue_chunk(p, S, 1, ri[1], st[1], &Qs[1], &Gs[1]);
+    S.io_q.complete(Qs[1]);
+    S.io_g.complete(Gs[1]);
   }
-  issue_rowinfo(S, 3, r0);
+  issue_rowinfo(S, 3, ri[0]);
   wait_vmem();
   __syncthreads();
-  int c = 0;
-  for (; c + 2 <= c_last; c += 3) {
-    paged_step<T, D>(p, S, c, Q0, G0, s0, Q2, G2, s2, r2, r1);
-    paged_step<T, D>(p, S, c + 1, Q1, G1, s1, Q0, G0, s0, r0, r2);
-    paged_step<T, D>(p, S, c + 2, Q2, G2, s2, Q1, G1, s1, r1, r0);
+  S.buf = 0;
+  if (masked) {
+    for (int c = 0; c <= c_last; ++c) paged_step<T, D, true>(p, S, c, Qs, Gs, st, ri);
+  } else {
+    for (int c = 0; c <= c_last; ++c) paged_step<T, D, false>(p, S, c, Qs, Gs, st, ri);
   }
-  if (c <= c_last) paged_step<T, D>(p, S, c, Q0, G0, s0, Q2, G2, s2, r2, r1);
-  if (c + 1 <= c_last) paged_step<T, D>(p, S, c + 1, Q1, G1, s1, Q0, G0, s0, r0, r2);
 }
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_paged_kv_bwd(const PagedParams p) {
   typedef MT<T> M;
   constexpr int KS = M::KS, KL = M::KL, NSD = D / KS, NT = D / 32, ROWS = KvShape<T>::ROWS;
-  __shared__ Tile<T, D, ROWS> Qs0, Qs1, Qs2, Gs0, Gs1, Gs2;
-  __shared__ __attribute__((aligned(16))) float st0[kStatWords], st1[kStatWords], st2[kStatWords];
-  __shared__ __attribute__((aligned(16))) int ri0[kRiWords], ri1[kRiWords], ri2[kRiWords];
+  __shared__ Tile<T, D, ROWS> Qs[3], Gs[3];
+  __shared__ __attribute__((aligned(16))) float st[3][kStatWords];
+  __shared__ __attribute__((aligned(16))) int ri[3][kRiWords];
 
   PagedState<T, D> S;
   S.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -211,8 +191,8 @@ __global__ __launch_bounds__(256) void k_paged_kv_bwd(const PagedParams p) {
   }
 #pragma unroll
   for (int t = 0; t < NT; ++t) S.dk[t] = S.dv[t] = f32x16{};
-  S.io_q.init();
-  S.io_g.init();
+  S.io_q.init(D);
+  S.io_g.init(D);
   const int hg = g * p.group;
   S.qbase = (const T *)p.q + (int64_t)hg * D;
   S.gbase = (const T *)p.dy + (int64_t)hg * D;
@@ -228,12 +208,13 @@ __global__ __launch_bounds__(256) void k_paged_kv_bwd(const PagedParams p) {
     S.nqh = plan[p.off_seq_qh + seq + 1] - qh0;
     if (S.nqh <= 0) continue;
     S.maxtok = info[plan::LI_MAX_TOK];
-    S.all_valid = info[plan::LI_ALL_VALID] != 0;
     S.tok = plan[p.off_link_tok + li * plan::kItemSlots + 32 * S.wave + l32];
     S.rh_tab = plan + p.off_qh_rh + qh0;
     S.pos_tab = plan + p.off_qh_pos + qh0;
     S.c_last = (S.nqh - 1) / ROWS;
-    paged_run<T, D>(p, S, &Qs0, &Qs1, &Qs2, &Gs0, &Gs1, &Gs2, st0, st1, st2, ri0, ri1, ri2);
+    const bool masked = !(info[plan::LI_ALL_VALID] != 0 &&
+                          (!p.causal || plan[p.off_seq_minpos + seq] >= S.maxtok));
+    paged_run<T, D>(p, S, masked, Qs, Gs, st, ri);
   }
 
   if (ent < 0) return;
@@ -245,9 +226,9 @@ __global__ __launch_bounds__(256) void k_paged_kv_bwd(const PagedParams p) {
     for (int q = 0; q < 4; ++q) {
       const int d0 = 32 * t + 8 * q + 4 * half;
       const f32x16 &a = S.dk[t], &b = S.dv[t];
+      const float sc = live ? p.scale : 0.f;  // dS's factor, applied once; tails store +0
       if (p.need_dk)
-        store4<T>(dkrow + d0, live ? a[4 * q] : 0.f, live ? a[4 * q + 1] : 0.f,
-                  live ? a[4 * q + 2] : 0.f, live ? a[4 * q + 3] : 0.f);
+        store4<T>(dkrow + d0, sc * a[4 * q], sc * a[4 * q + 1], sc * a[4 * q + 2], sc * a[4 * q + 3]);
       if (p.need_dv)
         store4<T>(dvrow + d0, live ? b[4 * q] : 0.f, live ? b[4 * q + 1] : 0.f,
                   live ? b[4 * q + 2] : 0.f, live ? b[4 * q + 3] : 0.f);

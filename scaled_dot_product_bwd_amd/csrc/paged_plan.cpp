@@ -72,7 +72,7 @@ int64_t words_bound(int32_t nseq, const int32_t *seq_lens, int32_t nq, int32_t h
   const int64_t items = refs * pieces, links = refs * pieces;
   const int64_t qh = (int64_t)nq * (heads / kv_heads);
   return HEADER_WORDS + (items + 1) + items * kItemSlots + links * (1 + LINK_INFO_WORDS + kItemSlots) +
-         (nseq + 1) + 2 * qh + nseq + std::min<int64_t>(refs, pool_pages);
+         (nseq + 1) + 2 * qh + 2 * nseq + std::min<int64_t>(refs, pool_pages);
 }
 
 }  // namespace
@@ -211,6 +211,8 @@ extern "C" int attn_bwd_paged_plan_build(int32_t nseq, const int32_t *seq_lens,
   at += nseq;
   w[W_OFF_LISTED] = (int32_t)at;
   at += (int64_t)listed.size();
+  w[W_OFF_SEQ_MINPOS] = (int32_t)at;
+  at += nseq;
   if (at > plan_words) return perr(ATTN_E_INVALID, "paged plan: internal size error");
 
   int32_t *item_links = w + w[W_OFF_ITEM_LINKS], *item_slots = w + w[W_OFF_ITEM_SLOTS];
@@ -271,18 +273,21 @@ extern "C" int attn_bwd_paged_plan_build(int32_t nseq, const int32_t *seq_lens,
 
   int32_t *seq_qh = w + w[W_OFF_SEQ_QH], *qh_rh = w + w[W_OFF_QH_RH];
   int32_t *qh_pos = w + w[W_OFF_QH_POS], *seq_max = w + w[W_OFF_SEQ_MAXPOS];
+  int32_t *seq_min = w + w[W_OFF_SEQ_MINPOS];
   for (int32_t s = 0; s <= nseq; ++s) seq_qh[s] = (int32_t)(row_start[s] * group);
   for (int32_t s = 0; s < nseq; ++s) {
-    int32_t mx = -1;
+    int32_t mx = -1, mn = INT32_MAX;
     for (int64_t k = row_start[s]; k < row_start[s + 1]; ++k) {
       const int32_t r = seq_rows[k];
       mx = std::max(mx, query_pos[r]);
+      mn = std::min(mn, query_pos[r]);
       for (int32_t hh = 0; hh < group; ++hh) {
         qh_rh[k * group + hh] = r * heads + hh;
         qh_pos[k * group + hh] = query_pos[r];
       }
     }
     seq_max[s] = mx;
+    seq_min[s] = mn;
   }
   std::copy(listed.begin(), listed.end(), w + w[W_OFF_LISTED]);
 

@@ -46,6 +46,7 @@ def _tables(plan):
         qh_pos=W[h(_abi.W_OFF_QH_POS):][:qh],
         seq_maxpos=W[h(_abi.W_OFF_SEQ_MAXPOS):][:nseq],
         listed=W[h(_abi.W_OFF_LISTED):][:h(_abi.W_LISTED)],
+        seq_minpos=W[h(_abi.W_OFF_SEQ_MINPOS):][:nseq],
     )
     assert h(_abi.W_MAGIC) == _abi.PLAN_MAGIC and h(_abi.W_WORDS) == len(W)
     return t
@@ -160,6 +161,7 @@ def test_plan_rows_keep_packed_order():
         assert np.array_equal(rows, np.where(qs == s)[0])          # original packed order
         assert np.array_equal(rh.reshape(-1, G) % 8, np.tile(np.arange(G), (len(rows), 1)))
         assert t["seq_maxpos"][s] == w["query_pos"].numpy()[qs == s].max()
+        assert t["seq_minpos"][s] == w["query_pos"].numpy()[qs == s].min()
 
 
 def _plan_eval(w, plan, stats, causal=True, scale=None):
