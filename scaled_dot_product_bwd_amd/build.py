@@ -3,7 +3,7 @@
     python -m scaled_dot_product_bwd_amd.build
 
 Every HIP source is compiled with hipcc for gfx950 only, with packed-fp32
-instructions disabled (-packed-fp32-ops).  The sources compile in parallel and
+instructions disabled (-packed-fp32-ops) and MFMA results kept in VGPRs.  The sources compile in parallel and
 link into one shared library.
 """
 from __future__ import annotations
@@ -33,8 +33,11 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain (ROCm) is required to build")
 
 
+# -amdgpu-mfma-vgpr-form: MFMA results in VGPRs, so the softmax reads them
+# without accumulator-register moves.
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-I", INCLUDE, "-I", CSRC]
 
 

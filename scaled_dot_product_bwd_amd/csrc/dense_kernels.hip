@@ -82,15 +82,15 @@ __device__ __forceinline__ float q_adj(const DenseParams &p, int b, int h, int q
   }
 }
 
-template <typename T, int D, int MODE>
+template <typename T, int D, int MODE, int NBUF>
 __device__ __forceinline__ void rs_step(const DenseParams &p, RsState<T, D> &S, int c,
                                         Tile<T, D> *Ks, Tile<T, D> *Vs, bool masked) {
   constexpr int NQB = QShape<T>::NQB;
-  const int bc = S.buf, bn = bc == 0 ? 2 : bc - 1;
-  const bool issued = c + 2 <= S.c_last;
+  const int bc = S.buf, bn = (bc + NBUF - 1) % NBUF;  // chunk c + NBUF - 1 goes to bn
+  const bool issued = c + NBUF - 1 <= S.c_last;
   if (issued) {
-    S.io_k.issue(S.kbase, p.ks[1], (c + 2) * 32, p.Sk, Ks[bn]);
-    S.io_v.issue(S.vbase, p.vs[1], (c + 2) * 32, p.Sk, Vs[bn]);
+    S.io_k.issue(S.kbase, p.ks[1], (c + NBUF - 1) * 32, p.Sk, Ks[bn]);
+    S.io_v.issue(S.vbase, p.vs[1], (c + NBUF - 1) * 32, p.Sk, Vs[bn]);
   }
   f32x16 sacc[NQB], pacc[NQB];
   q_phase_a<T, D, NQB>(&Ks[bc], &Vs[bc], S.qf, S.gf, sacc, pacc, S.lane);
@@ -126,13 +126,14 @@ __device__ __forceinline__ void rs_step(const DenseParams &p, RsState<T, D> &S, 
     S.io_k.complete(Ks[bn]);
     S.io_v.complete(Vs[bn]);
   }
-  end_step<ChunkIO<T, D>::DIRECT, 2 * ChunkIO<T, D>::LOADS>(issued);
-  S.buf = bc == 2 ? 0 : bc + 1;
+  // With two buffers the chunk issued here is the next one: wait for all of it.
+  end_step<ChunkIO<T, D>::DIRECT, 2 * ChunkIO<T, D>::LOADS>(issued && NBUF == 3);
+  S.buf = bc == NBUF - 1 ? 0 : bc + 1;
 }
 
-// Prologue shared by the query-major kernels: chunks c_first and c_first + 1
-// into buffers 0 and 1.
-template <typename T, int D>
+// Prologue shared by the query-major kernels: chunks c_first (and, with three
+// buffers, c_first + 1) into buffers 0 (and 1).
+template <typename T, int D, int NBUF = 3>
 __device__ __forceinline__ void q_prologue(const DenseParams &p, ChunkIO<T, D> &io_k,
                                            ChunkIO<T, D> &io_v, const T *kbase, const T *vbase,
                                            int c_first, int c_last, Tile<T, D> *Ks, Tile<T, D> *Vs) {
@@ -142,7 +143,7 @@ __device__ __forceinline__ void q_prologue(const DenseParams &p, ChunkIO<T, D> &
     io_k.complete(Ks[0]);
     io_v.complete(Vs[0]);
   }
-  const bool second = c_first + 1 <= c_last;
+  const bool second = NBUF == 3 && c_first + 1 <= c_last;
   if (second) {
     io_k.issue(kbase, p.ks[1], (c_first + 1) * 32, p.Sk, Ks[1]);
     io_v.issue(vbase, p.vs[1], (c_first + 1) * 32, p.Sk, Vs[1]);
@@ -152,12 +153,17 @@ __device__ __forceinline__ void q_prologue(const DenseParams &p, ChunkIO<T, D> &
   end_step<ChunkIO<T, D>::DIRECT, 2 * ChunkIO<T, D>::LOADS>(second);
 }
 
+// Buffers of the row-statistics chunk stream.  Two (48 KB of LDS at D = 128)
+// let three workgroups share a CU, three waves per SIMD, which hides more
+// latency than a third buffer would.
+constexpr int kRsBuf = 2;
+
 template <typename T, int D, int MODE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_row_stats(const DenseParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_row_stats(const DenseParams p) {
   typedef MT<T> M;
   constexpr int KS = M::KS, KL = M::KL, NSD = D / KS, NQB = QShape<T>::NQB,
                 QROWS = QShape<T>::QROWS;
-  __shared__ Tile<T, D> Ks[3], Vs[3];
+  __shared__ Tile<T, D> Ks[kRsBuf], Vs[kRsBuf];
 
   RsState<T, D> S;
   const int tid = threadIdx.x, w = tid >> 6;
@@ -196,10 +202,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // so the compiler knows they are complete inside the loop (otherwise it
   // would wait for them there, and with them for the chunk loads in flight).
   wait_vmem();
-  q_prologue<T, D>(p, S.io_k, S.io_v, S.kbase, S.vbase, R.c_first, R.c_last, Ks, Vs);
+  q_prologue<T, D, kRsBuf>(p, S.io_k, S.io_v, S.kbase, S.vbase, R.c_first, R.c_last, Ks, Vs);
   S.buf = 0;
   for (int c = R.c_first; c <= R.c_last; ++c)
-    rs_step<T, D, MODE>(p, S, c, Ks, Vs, c < R.cu0 || c > R.cu1);
+    rs_step<T, D, MODE, kRsBuf>(p, S, c, Ks, Vs, c < R.cu0 || c > R.cu1);
 
 #pragma unroll
   for (int q = 0; q < NQB; ++q) {
