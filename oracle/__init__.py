@@ -53,6 +53,8 @@ def _load():
     lib.oracle_paged_row_stats.argtypes = paged + [_dp, ctypes.c_int]
     lib.oracle_paged_kv_bwd.restype = ctypes.c_int
     lib.oracle_paged_kv_bwd.argtypes = paged + [_dp, _dp, _dp, ctypes.c_int]
+    lib.oracle_paged_dq.restype = ctypes.c_int
+    lib.oracle_paged_dq.argtypes = paged + [_dp, _dp, ctypes.c_int]
     _lib = lib
     return lib
 
@@ -170,5 +172,25 @@ def paged_kv_bwd(w, q, dy, k_pool, v_pool, stats, dk_init, dv_init, *, heads,
     return dk, dv
 
 
-__all__ = ["attn_bwd", "paged_row_stats", "paged_kv_bwd", "MASK_NONE", "MASK_CAUSAL",
+def paged_dq(w, q, dy, k_pool, v_pool, stats, *, heads, kv_heads, page_size, causal=True,
+             scale=None, nthreads=None):
+    """dQ [nq, heads, D] of the paged layout from the given (max, denominator, delta)."""
+    seq_lens, bt, nseq, max_pages, qs, qp = _paged_common(w)
+    q, dy, kp, vp, st = _f64(q), _f64(dy), _f64(k_pool), _f64(v_pool), _f64(stats)
+    nq, _, D = q.shape
+    pool_pages = kp.shape[0] // page_size
+    if scale is None:
+        scale = float(np.float32(1.0) / np.sqrt(np.float32(D)))
+    dq = np.empty((nq, heads, D))
+    rc = _load().oracle_paged_dq(
+        nseq, _ptr(seq_lens, _ip), _ptr(bt, _ip), max_pages, nq, _ptr(qs, _ip),
+        _ptr(qp, _ip), heads, kv_heads, D, page_size, pool_pages, int(bool(causal)),
+        float(scale), _ptr(q), _ptr(dy), _ptr(kp), _ptr(vp), _ptr(st), _ptr(dq),
+        int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError(f"oracle_paged_dq rejected its arguments (rc={rc})")
+    return dq
+
+
+__all__ = ["attn_bwd", "paged_row_stats", "paged_kv_bwd", "paged_dq", "MASK_NONE", "MASK_CAUSAL",
            "MASK_KEYPAD", "MASK_WINDOW", "MASK_BIAS", "default_threads"]

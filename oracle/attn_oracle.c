@@ -402,6 +402,64 @@ int oracle_paged_row_stats(int nseq, const int32_t *seq_lens, const int32_t *blo
   return 0;
 }
 
+/* dQ of one query row r, every head, from the supplied statistics: the
+ * definition dQ_r = sum_t dS_rt K_t over the row's visible tokens, with
+ * dS = P (dP - delta) scale and P = exp(s - max) / den; a zero denominator
+ * gives a zero row (as [ruDNN] skips such rows). */
+static void *paged_dq_worker(void *arg) {
+  paged_job *J = (paged_job *)arg;
+  const int D = J->D, group = J->heads / J->kv_heads;
+  for (int64_t r; (r = paged_take(J)) >= 0;) {
+    const int s = J->query_seq[r];
+    const int len = J->seq_lens[s];
+    for (int h = 0; h < J->heads; ++h) {
+      const int g = h / group;
+      const double *st = J->stats_in + (r * J->heads + h) * 3;
+      const double *qr = J->q + (r * J->heads + h) * D;
+      const double *gr = J->dy + (r * J->heads + h) * D;
+      double *out = J->gk + (r * J->heads + h) * D;
+      for (int d = 0; d < D; ++d) out[d] = 0.0;
+      if (st[1] == 0.0) continue;
+      for (int t = 0; t < len; ++t) {
+        if (J->causal && t > J->query_pos[r]) continue;
+        const int64_t slot = paged_slot(J, s, t);
+        const double *kr = J->k_pool + (slot * J->kv_heads + g) * D;
+        const double *vr = J->v_pool + (slot * J->kv_heads + g) * D;
+        double a = 0.0, c = 0.0;
+        for (int d = 0; d < D; ++d) { a += qr[d] * kr[d]; c += gr[d] * vr[d]; }
+        const double p = exp(J->scale * a - st[0]) / st[1];
+        const double ds = p * (c - st[2]) * J->scale;
+        for (int d = 0; d < D; ++d) out[d] += ds * kr[d];
+      }
+    }
+  }
+  return NULL;
+}
+
+/* dQ [nq, heads, D] of the paged layout from supplied statistics (the query
+ * side of [ruDNN] `history_backward`'s data).  Rows are independent; threads
+ * split them. */
+int oracle_paged_dq(int nseq, const int32_t *seq_lens, const int32_t *block_table, int max_pages,
+                    int nq, const int32_t *query_seq, const int32_t *query_pos, int heads,
+                    int kv_heads, int D, int page_size, int pool_pages, int causal, double scale,
+                    const double *q, const double *dy, const double *k_pool, const double *v_pool,
+                    const double *stats, double *dq, int nthreads) {
+  if (paged_check(nseq, seq_lens, block_table, max_pages, nq, query_seq, heads, kv_heads,
+                  page_size, pool_pages))
+    return -1;
+  paged_job J;
+  memset(&J, 0, sizeof J);
+  J.nseq = nseq; J.max_pages = max_pages; J.nq = nq; J.heads = heads; J.kv_heads = kv_heads;
+  J.D = D; J.page_size = page_size; J.pool_pages = pool_pages; J.causal = causal;
+  J.seq_lens = seq_lens; J.block_table = block_table; J.query_seq = query_seq;
+  J.query_pos = query_pos; J.scale = scale;
+  J.q = q; J.dy = dy; J.k_pool = k_pool; J.v_pool = v_pool; J.stats_in = stats;
+  J.gk = dq;
+  J.count = nq;
+  paged_parallel(&J, paged_dq_worker, nthreads);
+  return 0;
+}
+
 /* All contributions to the slots of one KV head g, in a fixed order:
  * sequences, then tokens, then query rows, then the group's heads. */
 static void *paged_kv_worker(void *arg) {

@@ -24,6 +24,7 @@ def _dense_reference(w):
     nslot = kp.shape[0]
     dk = np.zeros((nslot, kv, D))
     dv = np.zeros((nslot, kv, D))
+    dq = np.zeros(q.shape)
     stats = np.zeros((q.shape[0], heads, 3))
     qs, qpos = w["query_seq"].numpy(), w["query_pos"].numpy()
     bt = w["block_table"].numpy()
@@ -44,6 +45,8 @@ def _dense_reference(w):
         stats[rows, :, 0] = r["m"][0].T
         stats[rows, :, 1] = r["l"][0].T
         stats[rows, :, 2] = r["delta"][0].T
+        dq[rows] = r["dq"][0]
+    _dense_reference.dq = dq
     return dk, dv, stats
 
 
@@ -132,3 +135,23 @@ def test_paged_rejects_bad_tables():
     with pytest.raises(ValueError):
         oracle.paged_row_stats(w, w["q"], w["dy"], w["k_pool"], w["v_pool"], heads=2,
                                kv_heads=1, page_size=2)
+
+
+@pytest.mark.parametrize("share,shuffle", [(0, False), (2, True)])
+def test_paged_dq_equals_dense_gather(share, shuffle):
+    """dQ of each packed row equals the dense oracle's dQ on its gathered
+    sequence (causal offset len - rows), with the oracle's own statistics."""
+    w = sdpa_inputs.paged_workload(seed=17, nseq=3, len_lo=9, len_hi=40, q_per_seq=6,
+                                   page_size=4, heads=4, kv_heads=2, D=8, dtype=torch.float64,
+                                   share_prefix_pages=share, shuffle_rows=shuffle)
+    kw = dict(heads=4, kv_heads=2, page_size=4)
+    stats = oracle.paged_row_stats(w, w["q"], w["dy"], w["k_pool"], w["v_pool"], **kw)
+    dq = oracle.paged_dq(w, w["q"], w["dy"], w["k_pool"], w["v_pool"], stats, **kw)
+    _dense_reference(w)
+    np.testing.assert_allclose(dq, _dense_reference.dq, rtol=1e-11, atol=1e-11)
+    # a row the pages skip (zero denominator) gets a zero dQ row
+    st0 = stats.copy()
+    st0[1, :, 1] = 0.0
+    dq0 = oracle.paged_dq(w, w["q"], w["dy"], w["k_pool"], w["v_pool"], st0, **kw)
+    assert np.all(dq0[1] == 0.0)
+    np.testing.assert_array_equal(dq0[0], dq[0])
