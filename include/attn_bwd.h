@@ -187,6 +187,26 @@ typedef struct attn_bwd_paged_args {
  * the pools).  A plan with no item does nothing. */
 int attn_bwd_paged(const attn_bwd_paged_args *a, void *stream);
 
+/* The query side of the paged backward, for callers without forward
+ * statistics (ruDNN computes them "once by the query kernel"): the same
+ * arguments and plan as attn_bwd_paged, `need` ignored.
+ *
+ * attn_bwd_paged_row_stats writes `stats` (device [nq, heads, 3] fp32, the
+ * argument struct's `stats` is ignored) = (max of the scaled visible scores,
+ * denominator sum exp(s - max), delta = sum_t P dP) per (row, head), with
+ * P = exp(s - max) / denominator and dP = dY . v; a row that sees no token
+ * gets (-inf, 0, 0).  Feed the result to attn_bwd_paged and attn_bwd_paged_dq.
+ *
+ * attn_bwd_paged_dq writes `dq` (device [nq, heads, head_dim], the element
+ * type of q) = sum over the row's visible tokens of dS k, with
+ * dS = P (dP - delta) scale from the argument struct's `stats`; a row with a
+ * zero denominator gets a zero dQ row.  Every row of `dq` is written.
+ *
+ * Both reject outputs that overlap an input; the plan, pointers and
+ * alignment follow attn_bwd_paged. */
+int attn_bwd_paged_row_stats(const attn_bwd_paged_args *a, float *stats, void *stream);
+int attn_bwd_paged_dq(const attn_bwd_paged_args *a, void *dq, void *stream);
+
 /* Thread-local description of the last non-OK status returned on this thread. */
 const char *attn_bwd_last_error(void);
 

@@ -9,7 +9,9 @@ There is no CPU fallback: without the built library every call raises.
 
     plan = paged_plan(seq_lens, block_table, query_seq, query_pos, heads=32,
                       kv_heads=8, page_size=16, pool_pages=N, device="cuda")
+    stats = paged_row_stats(q, dy, k_pool, v_pool, plan)
     attn_bwd_paged(q, dy, k_pool, v_pool, stats, plan, dk_pool=dk, dv_pool=dv)
+    dq = attn_bwd_paged_dq(q, dy, k_pool, v_pool, stats, plan)
 
 Tensors are ``[B, S, H, D]`` (any strides with ``D`` contiguous; pass
 ``x.transpose(1, 2)`` for a ``[B, H, S, D]`` tensor), float32 or bfloat16, on the
@@ -32,7 +34,7 @@ from ._abi import (ATTN_BF16, ATTN_F32, ATTN_MASK_BIAS, ATTN_MASK_CAUSAL,
 
 __all__ = ["attn_bwd", "attn_bwd_stage", "workspace_bytes", "make_args", "AttnError",
            "load_library", "library_path", "MASKS", "WRT", "PagedPlan", "paged_plan",
-           "attn_bwd_paged", "make_paged_args"]
+           "attn_bwd_paged", "make_paged_args", "paged_row_stats", "attn_bwd_paged_dq"]
 
 MASKS = {"none": ATTN_MASK_NONE, "causal": ATTN_MASK_CAUSAL, "keypad": ATTN_MASK_KEYPAD,
          "window": ATTN_MASK_WINDOW, "bias": ATTN_MASK_BIAS}
@@ -274,3 +276,34 @@ def attn_bwd_paged(q, dy, k_pool, v_pool, stats, plan, *, dk_pool=None, dv_pool=
                            causal=causal, scale=scale, need=n)
     _check(load_library().attn_bwd_paged(ctypes.byref(args), _stream_handle(stream)))
     return dk_pool, dv_pool
+
+
+def paged_row_stats(q, dy, k_pool, v_pool, plan, *, causal=True, scale=None, out=None,
+                    stream=None):
+    """(max, denominator, delta) per (row, head) of the paged layout, float32
+    [nq, heads, 3], computed on the GPU (attn_bwd_paged_row_stats)."""
+    torch = _torch()
+    nq, heads, _ = q.shape
+    if plan.device_words is None:
+        plan.to(q.device)
+    if out is None:
+        out = torch.empty(nq, heads, 3, dtype=torch.float32, device=q.device)
+    dummy = out  # the struct's input statistics are not read by this call
+    args = make_paged_args(q, dy, k_pool, v_pool, dummy, plan, causal=causal, scale=scale)
+    _check(load_library().attn_bwd_paged_row_stats(ctypes.byref(args), ctypes.c_void_p(out.data_ptr()),
+                                                   _stream_handle(stream)))
+    return out
+
+
+def attn_bwd_paged_dq(q, dy, k_pool, v_pool, stats, plan, *, causal=True, scale=None, out=None,
+                      stream=None):
+    """dQ [nq, heads, D] of the paged layout from the statistics (attn_bwd_paged_dq)."""
+    torch = _torch()
+    if plan.device_words is None:
+        plan.to(q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    args = make_paged_args(q, dy, k_pool, v_pool, stats, plan, causal=causal, scale=scale)
+    _check(load_library().attn_bwd_paged_dq(ctypes.byref(args), ctypes.c_void_p(out.data_ptr()),
+                                            _stream_handle(stream)))
+    return out

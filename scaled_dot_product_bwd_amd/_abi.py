@@ -23,7 +23,8 @@ STATUS_NAMES = {ATTN_E_INVALID: "ATTN_E_INVALID", ATTN_E_UNSUPPORTED: "ATTN_E_UN
 # Every symbol include/attn_bwd.h declares.
 EXPORTED = ["attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_row_stats", "attn_bwd_kv",
             "attn_bwd_dq", "attn_bwd_paged_plan_words", "attn_bwd_paged_plan_build",
-            "attn_bwd_paged", "attn_bwd_last_error"]
+            "attn_bwd_paged", "attn_bwd_paged_row_stats", "attn_bwd_paged_dq",
+            "attn_bwd_last_error"]
 
 # Plan header words (scaled_dot_product_bwd_amd/csrc/paged.hpp).
 PLAN_MAGIC = 0x31504241
@@ -31,7 +32,8 @@ PLAN_ITEM_SLOTS = 128
 (W_MAGIC, W_WORDS, W_NSEQ, W_NQ, W_HEADS, W_KV_HEADS, W_PAGE_SIZE, W_POOL_PAGES, W_ITEMS,
  W_LINKS, W_QH, W_LISTED, W_OFF_ITEM_LINKS, W_OFF_ITEM_SLOTS, W_OFF_LINK_SEQ, W_OFF_LINK_INFO,
  W_OFF_LINK_TOK, W_OFF_SEQ_QH, W_OFF_QH_RH, W_OFF_QH_POS, W_OFF_SEQ_MAXPOS,
- W_OFF_LISTED, W_OFF_SEQ_MINPOS) = range(23)
+ W_OFF_LISTED, W_OFF_SEQ_MINPOS, W_OFF_SEQ_TOK, W_OFF_TOK_SLOT, W_TOKENS, W_OFF_QBLK,
+ W_QBLK) = range(28)
 
 
 class AttnError(RuntimeError):
@@ -107,6 +109,10 @@ def load_library():
                                               _i32, _p, ctypes.c_int64]
     lib.attn_bwd_paged.restype = ctypes.c_int
     lib.attn_bwd_paged.argtypes = [ctypes.POINTER(AttnBwdPagedArgs), ctypes.c_void_p]
+    for name in ("attn_bwd_paged_row_stats", "attn_bwd_paged_dq"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.POINTER(AttnBwdPagedArgs), ctypes.c_void_p, ctypes.c_void_p]
     lib.attn_bwd_last_error.restype = ctypes.c_char_p
     lib.attn_bwd_last_error.argtypes = []
     _lib = lib

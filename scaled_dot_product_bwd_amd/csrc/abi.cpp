@@ -262,12 +262,18 @@ int run(const attn_bwd_args *a, void *stream, int first, int last) {
 // ---------------------------------------------------------------------------
 // Paged history backward.
 
-int validate_paged(const attn_bwd_paged_args *a, attn::PagedParams &p, int &nblocks, bool &bf16) {
+// What a paged call computes: dK / dV (attn_bwd_paged), the statistics or dQ
+// (the query side).
+enum PagedMode { PM_KV = 0, PM_STATS = 1, PM_DQ = 2 };
+
+int validate_paged(const attn_bwd_paged_args *a, int mode, void *out, attn::PagedParams &p,
+                   int &nblocks, bool &bf16) {
   using namespace attn::plan;
   if (!a) return fail(ATTN_E_INVALID, "args is NULL");
   if (a->dtype != ATTN_F32 && a->dtype != ATTN_BF16)
     return fail(ATTN_E_INVALID, "dtype %d is not ATTN_F32 or ATTN_BF16", a->dtype);
-  if (a->need < 1 || a->need > 3) return fail(ATTN_E_INVALID, "need %d is not 1, 2 or 3", a->need);
+  if (mode == PM_KV && (a->need < 1 || a->need > 3))
+    return fail(ATTN_E_INVALID, "need %d is not 1, 2 or 3", a->need);
   if (a->head_dim != 32 && a->head_dim != 64 && a->head_dim != 128)
     return fail(ATTN_E_UNSUPPORTED, "head_dim %d is not 32, 64 or 128", a->head_dim);
   if (!std::isfinite(a->scale)) return fail(ATTN_E_INVALID, "scale is not finite");
@@ -277,18 +283,21 @@ int validate_paged(const attn_bwd_paged_args *a, attn::PagedParams &p, int &nblo
   if (w[W_MAGIC] != kMagic) return fail(ATTN_E_INVALID, "plan_host is not a plan (bad magic)");
   const int64_t words = w[W_WORDS];
   if (words < HEADER_WORDS) return fail(ATTN_E_INVALID, "plan header is inconsistent");
-  for (int k = W_OFF_ITEM_LINKS; k <= W_OFF_SEQ_MINPOS; ++k)
+  for (int k = W_OFF_ITEM_LINKS; k <= W_OFF_QBLK; ++k) {
+    if (k == W_TOKENS) continue;
     if (w[k] < HEADER_WORDS || w[k] > words) return fail(ATTN_E_INVALID, "plan offsets are inconsistent");
+  }
   if (w[W_HEADS] != a->heads || w[W_KV_HEADS] != a->kv_heads || w[W_PAGE_SIZE] != a->page_size ||
       w[W_NQ] != a->nq || w[W_POOL_PAGES] != a->pool_pages)
     return fail(ATTN_E_INVALID,
                 "plan was built for heads %d, kv_heads %d, page_size %d, nq %d, pool_pages %d",
                 w[W_HEADS], w[W_KV_HEADS], w[W_PAGE_SIZE], w[W_NQ], w[W_POOL_PAGES]);
-  const int64_t items = w[W_ITEMS];
-  if (items < 0 || items * (int64_t)a->kv_heads > INT32_MAX)
+  const int64_t items = w[W_ITEMS], qblocks = w[W_QBLK];
+  if (items < 0 || items * (int64_t)a->kv_heads > INT32_MAX || qblocks < 0 ||
+      qblocks * (int64_t)a->kv_heads > INT32_MAX)
     return fail(ATTN_E_INVALID, "plan item count is inconsistent");
   bf16 = a->dtype == ATTN_BF16;
-  nblocks = (int)(items * a->kv_heads);
+  nblocks = (int)((mode == PM_KV ? items : qblocks) * a->kv_heads);
 
   const size_t es = bf16 ? 2 : 4;
   const int64_t D = a->head_dim;
@@ -300,26 +309,29 @@ int validate_paged(const attn_bwd_paged_args *a, attn::PagedParams &p, int &nblo
     const void *ptr;
     int64_t bytes;
     bool needed;
-  } ts[7] = {
+  } ts[8] = {
       {"q", a->q, qrows * D * (int64_t)es, work && qrows > 0},
       {"dy", a->dy, qrows * D * (int64_t)es, work && qrows > 0},
-      {"stats", a->stats, qrows * 3 * (int64_t)sizeof(float), work && qrows > 0},
+      {"stats", a->stats, qrows * 3 * (int64_t)sizeof(float), work && qrows > 0 && mode != PM_STATS},
       {"k_pool", a->k_pool, pslots * D * (int64_t)es, work},
       {"v_pool", a->v_pool, pslots * D * (int64_t)es, work},
-      {"dk_pool", a->dk_pool, pslots * D * (int64_t)es, work && (a->need & 1)},
-      {"dv_pool", a->dv_pool, pslots * D * (int64_t)es, work && (a->need & 2)},
+      {"dk_pool", a->dk_pool, pslots * D * (int64_t)es, work && mode == PM_KV && (a->need & 1)},
+      {"dv_pool", a->dv_pool, pslots * D * (int64_t)es, work && mode == PM_KV && (a->need & 2)},
+      {mode == PM_STATS ? "stats_out" : "dq", out,
+       qrows * (mode == PM_STATS ? 3 * (int64_t)sizeof(float) : D * (int64_t)es),
+       work && mode != PM_KV},
   };
-  Range rng[7];
-  for (int i = 0; i < 7; ++i) {
+  Range rng[8];
+  for (int i = 0; i < 8; ++i) {
     if (!ts[i].needed) continue;
     if (!ts[i].ptr) return fail(ATTN_E_INVALID, "%s is NULL", ts[i].name);
     if ((uintptr_t)ts[i].ptr % 16) return fail(ATTN_E_UNSUPPORTED, "%s is not 16-byte aligned", ts[i].name);
     rng[i].lo = (uintptr_t)ts[i].ptr;
     rng[i].hi = rng[i].lo + (uintptr_t)ts[i].bytes;
   }
-  for (int i = 5; i < 7; ++i) {
+  for (int i = 5; i < 8; ++i) {  // outputs
     if (!ts[i].needed) continue;
-    for (int j = 0; j < 7; ++j)
+    for (int j = 0; j < 8; ++j)
       if (j != i && ts[j].needed && overlap(rng[i], rng[j]))
         return fail(ATTN_E_INVALID, "%s overlaps %s", ts[i].name, ts[j].name);
   }
@@ -327,6 +339,8 @@ int validate_paged(const attn_bwd_paged_args *a, attn::PagedParams &p, int &nblo
   std::memset(&p, 0, sizeof p);
   p.q = a->q; p.dy = a->dy; p.k_pool = a->k_pool; p.v_pool = a->v_pool;
   p.dk_pool = a->dk_pool; p.dv_pool = a->dv_pool;
+  if (mode == PM_STATS) p.stats_out = (float *)out;
+  if (mode == PM_DQ) p.dq = out;
   p.stats = a->stats;
   p.plan = a->plan;
   p.heads = a->heads;
@@ -348,6 +362,10 @@ int validate_paged(const attn_bwd_paged_args *a, attn::PagedParams &p, int &nblo
   p.off_qh_pos = w[W_OFF_QH_POS];
   p.off_seq_maxpos = w[W_OFF_SEQ_MAXPOS];
   p.off_seq_minpos = w[W_OFF_SEQ_MINPOS];
+  p.off_seq_tok = w[W_OFF_SEQ_TOK];
+  p.off_tok_slot = w[W_OFF_TOK_SLOT];
+  p.off_qblk = w[W_OFF_QBLK];
+  p.qblocks = w[W_QBLK];
   return ATTN_OK;
 }
 
@@ -358,20 +376,39 @@ void set_last_error(const char *msg) {
   snprintf(g_err, sizeof g_err, "%s", msg);
 }
 hipError_t launch_paged(bool bf16_in, int D, const PagedParams &p, int nblocks, hipStream_t stream);
+hipError_t launch_paged_q(int stage, bool bf16_in, int D, const PagedParams &p, int nblocks,
+                          hipStream_t stream);
 }  // namespace attn
+
+namespace {
+int run_paged(const attn_bwd_paged_args *a, int mode, void *out, void *stream) {
+  attn::PagedParams p;
+  int nblocks = 0;
+  bool bf16 = false;
+  const int rc = validate_paged(a, mode, out, p, nblocks, bf16);
+  if (rc != ATTN_OK) return rc;
+  if (nblocks == 0) return ATTN_OK;
+  const hipError_t e =
+      mode == PM_KV ? attn::launch_paged(bf16, a->head_dim, p, nblocks, (hipStream_t)stream)
+                    : attn::launch_paged_q(mode == PM_STATS ? 0 : 1, bf16, a->head_dim, p, nblocks,
+                                           (hipStream_t)stream);
+  if (e != hipSuccess) return fail(ATTN_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ATTN_OK;
+}
+}  // namespace
 
 extern "C" {
 
 int attn_bwd_paged(const attn_bwd_paged_args *a, void *stream) {
-  attn::PagedParams p;
-  int nblocks = 0;
-  bool bf16 = false;
-  const int rc = validate_paged(a, p, nblocks, bf16);
-  if (rc != ATTN_OK) return rc;
-  if (nblocks == 0) return ATTN_OK;
-  const hipError_t e = attn::launch_paged(bf16, a->head_dim, p, nblocks, (hipStream_t)stream);
-  if (e != hipSuccess) return fail(ATTN_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-  return ATTN_OK;
+  return run_paged(a, PM_KV, nullptr, stream);
+}
+
+int attn_bwd_paged_row_stats(const attn_bwd_paged_args *a, float *stats, void *stream) {
+  return run_paged(a, PM_STATS, stats, stream);
+}
+
+int attn_bwd_paged_dq(const attn_bwd_paged_args *a, void *dq, void *stream) {
+  return run_paged(a, PM_DQ, dq, stream);
 }
 
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq) {

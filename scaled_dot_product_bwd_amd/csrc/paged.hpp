@@ -25,6 +25,10 @@
 //   qh row   the query rows of each sequence in their original packed order,
 //            each expanded to its group of query heads (head index minor):
 //            rh = row * heads + head-in-group, and the row's position.
+//   token    each sequence's tokens in order, as pool slots (the query-side
+//            kernels stream a sequence's keys through this table).
+//   qblock   a sequence's qh rows cut into blocks of 128, one query-side
+//            workgroup per (block, KV head).
 #pragma once
 
 #include <stdint.h>
@@ -59,6 +63,12 @@ enum Word {
   W_OFF_SEQ_MAXPOS,  // [nseq] largest position of the sequence's rows, -1 if none
   W_OFF_LISTED,      // [listed] listed physical pages, ascending
   W_OFF_SEQ_MINPOS,  // [nseq] smallest position of the sequence's rows, INT32_MAX if none
+  W_OFF_SEQ_TOK,     // [nseq + 1] CSR into the token -> slot table
+  W_OFF_TOK_SLOT,    // [sum of lengths] pool slot of each token of each sequence
+  W_TOKENS,          // sum of lengths
+  W_OFF_QBLK,        // [qblocks * 2] (sequence, first qh row) of each 128-qh-row block,
+                     // sequences with more visible tokens first
+  W_QBLK,            // number of query blocks
   HEADER_WORDS = 32
 };
 
@@ -66,9 +76,13 @@ enum { LI_MIN_TOK = 0, LI_MAX_TOK = 1, LI_ALL_VALID = 2, LINK_INFO_WORDS = 4 };
 
 }  // namespace plan
 
+constexpr int kQBlockRows = 128;
+
 struct PagedParams {
   const void *q, *dy, *k_pool, *v_pool;
   void *dk_pool, *dv_pool;
+  float *stats_out;  // query side: statistics written here
+  void *dq;          // query side: dQ [nq, heads, D]
   const float *stats;   // [nq, heads, 3] = (max, denominator, delta)
   const int32_t *plan;  // device copy of the plan words
   int heads, kv_heads, group;
@@ -77,6 +91,7 @@ struct PagedParams {
   int items;
   int off_item_links, off_item_slots, off_link_seq, off_link_info, off_link_tok;
   int off_seq_qh, off_qh_rh, off_qh_pos, off_seq_maxpos, off_seq_minpos;
+  int off_seq_tok, off_tok_slot, off_qblk, qblocks;
 };
 
 }  // namespace attn

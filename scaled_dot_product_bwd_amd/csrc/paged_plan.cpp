@@ -27,6 +27,7 @@ void set_last_error(const char *msg);
 namespace {
 
 using namespace attn::plan;
+using attn::kQBlockRows;
 
 int perr(int code, const char *fmt, ...) {
   char buf[512];
@@ -66,13 +67,18 @@ int check_dims(int32_t nseq, const int32_t *seq_lens, int32_t max_pages, int32_t
 // fits an item by itself).
 int64_t words_bound(int32_t nseq, const int32_t *seq_lens, int32_t nq, int32_t heads,
                     int32_t kv_heads, int32_t page_size, int32_t pool_pages) {
-  int64_t refs = 0;
-  for (int32_t s = 0; s < nseq; ++s) refs += npages_of(seq_lens[s], page_size);
+  int64_t refs = 0, tokens = 0;
+  for (int32_t s = 0; s < nseq; ++s) {
+    refs += npages_of(seq_lens[s], page_size);
+    tokens += seq_lens[s];
+  }
   const int64_t pieces = npages_of(page_size, kItemSlots);
   const int64_t items = refs * pieces, links = refs * pieces;
   const int64_t qh = (int64_t)nq * (heads / kv_heads);
+  using attn::kQBlockRows;
   return HEADER_WORDS + (items + 1) + items * kItemSlots + links * (1 + LINK_INFO_WORDS + kItemSlots) +
-         (nseq + 1) + 2 * qh + 2 * nseq + std::min<int64_t>(refs, pool_pages);
+         (nseq + 1) + 2 * qh + 2 * nseq + std::min<int64_t>(refs, pool_pages) + (nseq + 1) +
+         tokens + 2 * ((qh + kQBlockRows - 1) / kQBlockRows + nseq);
 }
 
 }  // namespace
@@ -213,6 +219,29 @@ extern "C" int attn_bwd_paged_plan_build(int32_t nseq, const int32_t *seq_lens,
   at += (int64_t)listed.size();
   w[W_OFF_SEQ_MINPOS] = (int32_t)at;
   at += nseq;
+  int64_t tokens = 0;
+  for (int32_t s = 0; s < nseq; ++s) tokens += seq_lens[s];
+  w[W_OFF_SEQ_TOK] = (int32_t)at;
+  at += nseq + 1;
+  w[W_OFF_TOK_SLOT] = (int32_t)at;
+  at += tokens;
+  // Query blocks: 128 qh rows of one sequence each, the sequences whose rows
+  // see the most tokens first (the heaviest workgroups start first).
+  std::vector<std::pair<int64_t, int32_t>> order;  // (-visible tokens, sequence)
+  for (int32_t s = 0; s < nseq; ++s) {
+    if (rows_cnt[s + 1] == 0) continue;
+    int32_t mx = -1;
+    for (int64_t k = row_start[s]; k < row_start[s + 1]; ++k) mx = std::max(mx, query_pos[seq_rows[k]]);
+    order.push_back({-std::min<int64_t>(seq_lens[s], (int64_t)mx + 1), s});
+  }
+  std::stable_sort(order.begin(), order.end(),
+                   [](const std::pair<int64_t, int32_t> &a, const std::pair<int64_t, int32_t> &b) {
+                     return a.first < b.first;
+                   });
+  int64_t n_qblk = 0;
+  for (auto &o : order) n_qblk += (rows_cnt[o.second + 1] * (int64_t)group + kQBlockRows - 1) / kQBlockRows;
+  w[W_OFF_QBLK] = (int32_t)at;
+  at += 2 * n_qblk;
   if (at > plan_words) return perr(ATTN_E_INVALID, "paged plan: internal size error");
 
   int32_t *item_links = w + w[W_OFF_ITEM_LINKS], *item_slots = w + w[W_OFF_ITEM_SLOTS];
@@ -290,7 +319,30 @@ extern "C" int attn_bwd_paged_plan_build(int32_t nseq, const int32_t *seq_lens,
     seq_min[s] = mn;
   }
   std::copy(listed.begin(), listed.end(), w + w[W_OFF_LISTED]);
+  int32_t *seq_tok = w + w[W_OFF_SEQ_TOK], *tok_slot = w + w[W_OFF_TOK_SLOT];
+  {
+    int64_t k = 0;
+    for (int32_t s = 0; s < nseq; ++s) {
+      seq_tok[s] = (int32_t)k;
+      for (int64_t t = 0; t < seq_lens[s]; ++t)
+        tok_slot[k++] = (int32_t)((int64_t)block_table[s * mp + t / ps] * ps + t % ps);
+    }
+    seq_tok[nseq] = (int32_t)k;
+  }
 
+  {
+    int32_t *qb = w + w[W_OFF_QBLK];
+    int64_t k = 0;
+    for (auto &o : order) {
+      const int64_t nqh = rows_cnt[o.second + 1] * (int64_t)group;
+      for (int64_t b = 0; b < nqh; b += kQBlockRows) {
+        qb[2 * k] = o.second;
+        qb[2 * k + 1] = (int32_t)b;
+        ++k;
+      }
+    }
+  }
+  w[W_QBLK] = (int32_t)n_qblk;
   w[W_MAGIC] = kMagic;
   w[W_WORDS] = (int32_t)at;
   w[W_NSEQ] = nseq;
@@ -303,5 +355,6 @@ extern "C" int attn_bwd_paged_plan_build(int32_t nseq, const int32_t *seq_lens,
   w[W_LINKS] = (int32_t)n_links;
   w[W_QH] = (int32_t)n_qh;
   w[W_LISTED] = (int32_t)listed.size();
+  w[W_TOKENS] = (int32_t)tokens;
   return ATTN_OK;
 }

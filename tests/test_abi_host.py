@@ -209,3 +209,20 @@ def test_paged_empty_plan_is_a_no_op():
     for name in ("q", "dy", "k_pool", "v_pool", "stats", "dk_pool", "dv_pool"):
         setattr(a, name, 0)
     assert _paged_rc(a)[0] == _abi.ATTN_OK
+
+
+def test_paged_query_side_rejections():
+    plan = _paged_plan()
+    lib = sdb.load_library()
+    a = _paged_args(plan)
+    for fn in (lib.attn_bwd_paged_row_stats, lib.attn_bwd_paged_dq):
+        assert fn(ctypes.byref(a), None, None) == _abi.ATTN_E_INVALID      # no output
+        assert "NULL" in lib.attn_bwd_last_error().decode()
+        assert fn(ctypes.byref(a), ctypes.c_void_p(a.q), None) == _abi.ATTN_E_INVALID  # aliases q
+        assert "overlaps" in lib.attn_bwd_last_error().decode()
+    a.stats = 0   # the statistics kernel does not read the input statistics
+    a.need = 0    # nor `need`
+    assert lib.attn_bwd_paged_row_stats(ctypes.byref(a), None, None) == _abi.ATTN_E_INVALID
+    assert "stats_out is NULL" in lib.attn_bwd_last_error().decode()
+    assert lib.attn_bwd_paged_dq(ctypes.byref(a), ctypes.c_void_p(1 << 30), None) == _abi.ATTN_E_INVALID
+    assert "stats is NULL" in lib.attn_bwd_last_error().decode()

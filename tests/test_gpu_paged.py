@@ -39,7 +39,10 @@ def _bits(t):
     return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).numpy()
 
 
-def run_case(w, *, causal=True, need="dkdv", stats=None, check=True, label=""):
+def run_case(w, *, causal=True, need="dkdv", stats=None, check=True, label="", gpu_stats=None):
+    """stats: the oracle's statistics (computed here when None), used by the
+    reference and, rounded to fp32, by the GPU unless `gpu_stats` (a device
+    tensor computed on the GPU) is given for the GPU call."""
     heads, kv, ps = w["heads"], w["kv_heads"], w["page_size"]
     kw = dict(heads=heads, kv_heads=kv, page_size=ps)
     if stats is None:
@@ -51,7 +54,7 @@ def run_case(w, *, causal=True, need="dkdv", stats=None, check=True, label=""):
           f"pool={w['pool_pages']} items={plan.items} {w['dtype']} causal={causal} need={need}",
           flush=True)
     dev = torch.device("cuda:0")
-    st32 = torch.from_numpy(stats.astype(np.float32)).to(dev)
+    st32 = gpu_stats if gpu_stats is not None else torch.from_numpy(stats.astype(np.float32)).to(dev)
     q, dy, kp, vp = (w[n].to(dev) for n in ("q", "dy", "k_pool", "v_pool"))
     dk0, dv0 = _sentinel_pool(w["k_pool"]), _sentinel_pool(w["v_pool"])
     dk = dk0.to(dev) if need in ("dk", "dkdv") else None
@@ -188,3 +191,70 @@ def test_paged_rejections():
                           dk_pool=dk, need="dk")
     torch.cuda.synchronize()
     assert torch.count_nonzero(dk) == 0                   # nothing ran
+
+
+# ---------------------------------------------------------------------------
+# Query side: statistics and dQ (attn_bwd_paged_row_stats, attn_bwd_paged_dq).
+
+def _stats_err(got, ref):
+    """Per component (max, denominator, delta) over the rows that see a token."""
+    fin = ref[..., 1] > 0
+    errs = []
+    for k in range(3):
+        errs.append(rel_err(got[..., k][fin], ref[..., k][fin]))
+    empty = ~fin
+    assert np.all(np.isneginf(got[..., 0][empty])) and np.all(got[..., 1:][empty] == 0)
+    return errs
+
+
+def run_query_side(w, *, causal=True, label=""):
+    heads, kv, ps = w["heads"], w["kv_heads"], w["page_size"]
+    kw = dict(heads=heads, kv_heads=kv, page_size=ps)
+    plan = sb.paged_plan(w["seq_lens"], w["block_table"], w["query_seq"], w["query_pos"],
+                         pool_pages=w["pool_pages"], device="cuda:0", **kw)
+    print(f"[paged-q] {label} nq={w['q'].shape[0]} heads={heads}/{kv} D={w['D']} ps={ps} "
+          f"{w['dtype']} causal={causal} qblocks={plan.header(sb._abi.W_QBLK)}", flush=True)
+    dev = torch.device("cuda:0")
+    q, dy, kp, vp = (w[n].to(dev) for n in ("q", "dy", "k_pool", "v_pool"))
+    st_gpu = sb.paged_row_stats(q, dy, kp, vp, plan, causal=causal)
+    st_ref = oracle.paged_row_stats(w, w["q"], w["dy"], w["k_pool"], w["v_pool"], causal=causal, **kw)
+    # dQ from the oracle's statistics (rounded to fp32), against the oracle's dQ
+    st32 = torch.from_numpy(st_ref.astype(np.float32)).to(dev)
+    dq_gpu = sb.attn_bwd_paged_dq(q, dy, kp, vp, st32, plan, causal=causal)
+    torch.cuda.synchronize()
+    dq_ref = oracle.paged_dq(w, w["q"], w["dy"], w["k_pool"], w["v_pool"], st_ref, causal=causal, **kw)
+    tol = TOL[w["dtype"]]
+    errs = _stats_err(st_gpu.cpu().double().numpy(), st_ref)
+    for name, e in zip(("max", "denominator", "delta"), errs):
+        assert e <= tol, f"{label} stats {name}: rel err {e:.3e} > {tol:g}"
+    g = dq_gpu.double().cpu().numpy()
+    assert not np.isnan(g).any()
+    e = rel_err(g, dq_ref)
+    assert e <= tol, f"{label} dq: rel err {e:.3e} > {tol:g}"
+    return dict(plan=plan, stats=st_gpu, dq=dq_gpu, stats_err=errs, dq_err=e)
+
+
+Q_CASES = [CASES[0], CASES[1], CASES[3], CASES[4], CASES[5]]
+
+
+@pytest.mark.parametrize("case", Q_CASES, ids=lambda c: f"seed{c['seed']}")
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+def test_paged_query_side_parity(case, causal):
+    w = sdpa_inputs.paged_workload(**case)
+    if case["seed"] == 106:
+        qp = w["query_pos"].clone()
+        for s in range(len(w["seq_lens"])):
+            m = w["query_seq"] == s
+            qp[m] = qp[m] - int(w["seq_lens"][s]) // 2
+        w["query_pos"] = qp
+    run_query_side(w, causal=causal, label=f"seed{case['seed']}")
+
+
+def test_paged_config5_gpu_chain():
+    """Config 5 with no precomputed statistics: GPU statistics -> GPU dK / dV and
+    GPU dQ, against the oracle run end to end in float64."""
+    w = sdpa_inputs.paged_workload(seed=1005)
+    out = run_query_side(w, label="config5")
+    print(f"[paged-q] config5 stats err {out['stats_err']} dq err {out['dq_err']:.3e}", flush=True)
+    kv = run_case(w, gpu_stats=out["stats"], label="config5 gpu-stats")
+    print(f"[paged-q] config5 chain dk {kv['dk_err']:.3e} dv {kv['dv_err']:.3e}", flush=True)

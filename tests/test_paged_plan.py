@@ -47,6 +47,8 @@ def _tables(plan):
         seq_maxpos=W[h(_abi.W_OFF_SEQ_MAXPOS):][:nseq],
         listed=W[h(_abi.W_OFF_LISTED):][:h(_abi.W_LISTED)],
         seq_minpos=W[h(_abi.W_OFF_SEQ_MINPOS):][:nseq],
+        seq_tok=W[h(_abi.W_OFF_SEQ_TOK):][:nseq + 1],
+        tok_slot=W[h(_abi.W_OFF_TOK_SLOT):][:h(_abi.W_TOKENS)],
     )
     assert h(_abi.W_MAGIC) == _abi.PLAN_MAGIC and h(_abi.W_WORDS) == len(W)
     return t
@@ -250,3 +252,15 @@ def test_empty_plan():
     plan = sb.paged_plan(np.zeros(0, np.int32), np.zeros((0, 1), np.int32), np.zeros(0, np.int32),
                          np.zeros(0, np.int32), heads=4, kv_heads=2, page_size=16, pool_pages=3)
     assert plan.items == 0 and len(plan.listed_pages()) == 0
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"seed{c['seed']}")
+def test_plan_token_slots(case):
+    """Token t of sequence s sits at block_table[s][t / page_size] * page_size + t % page_size."""
+    w = sdpa_inputs.paged_workload(D=8, dtype=torch.float32, **case)
+    t = _tables(_plan(w))
+    ps, bt = w["page_size"], w["block_table"].numpy()
+    for s, L in enumerate(w["seq_lens"].tolist()):
+        got = t["tok_slot"][t["seq_tok"][s]:t["seq_tok"][s + 1]]
+        want = [bt[s, k // ps] * ps + k % ps for k in range(L)]
+        assert got.tolist() == want
