@@ -124,6 +124,24 @@ def attn_bwd(q, k, v, dy, *, mask_kind=MASK_NONE, causal_flag=False, window=0,
     return res
 
 
+def attn_bwd_gqa(q, k, v, dy, **kw):
+    """Grouped-query backward: K, V ``[B, Sk, Hkv, D]`` serve ``H / Hkv`` query
+    heads each (query head h reads KV head h // (H / Hkv)).  By definition the
+    forward equals the dense one with each KV head repeated over its group, so
+    dQ is that problem's dQ and dK, dV are its dK, dV summed over each group.
+    Same keywords and result keys as `attn_bwd` (dk, dv with Hkv heads)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    H, Hkv = q.shape[2], k.shape[2]
+    if H % Hkv:
+        raise ValueError("H must be a multiple of Hkv")
+    g = H // Hkv
+    res = attn_bwd(q, np.repeat(k, g, axis=2), np.repeat(v, g, axis=2), dy, **kw)
+    B, Sk, _, D = k.shape
+    res["dk"] = res["dk"].reshape(B, Sk, Hkv, g, D).sum(axis=3)
+    res["dv"] = res["dv"].reshape(B, Sk, Hkv, g, D).sum(axis=3)
+    return res
+
+
 def _paged_common(w):
     seq_lens = _i32(w["seq_lens"])
     bt = _i32(w["block_table"])
@@ -192,5 +210,5 @@ def paged_dq(w, q, dy, k_pool, v_pool, stats, *, heads, kv_heads, page_size, cau
     return dq
 
 
-__all__ = ["attn_bwd", "paged_row_stats", "paged_kv_bwd", "paged_dq", "MASK_NONE", "MASK_CAUSAL",
+__all__ = ["attn_bwd", "attn_bwd_gqa", "paged_row_stats", "paged_kv_bwd", "paged_dq", "MASK_NONE", "MASK_CAUSAL",
            "MASK_KEYPAD", "MASK_WINDOW", "MASK_BIAS", "default_threads"]
