@@ -95,6 +95,9 @@ typedef struct attn_bwd_args {
   float scale;             /* finite; callers usually pass (float)(1/sqrt(D)) */
   void *workspace;         /* device, >= attn_bwd_workspace_bytes(B, H, Sq) bytes, 256-byte aligned */
   size_t workspace_bytes;
+  int64_t Hkv;             /* K / V heads (grouped-query attention); 0 means H.  H must be a
+                              multiple of Hkv; query head h reads K / V head h / (H / Hkv);
+                              k, v, dk, dv are [B, Sk, Hkv, D] and dk, dv sum over each group */
 } attn_bwd_args;
 
 /* Bytes of device workspace attn_bwd needs: four fp32 planes of B*H*Sq row

@@ -66,6 +66,7 @@ def make_args(q, k, v, dy, dq=None, dk=None, dv=None, *, wrt="all", mask_kind="n
     a.dtype = ATTN_BF16 if q.dtype == torch.bfloat16 else ATTN_F32
     a.wrt = WRT[wrt] if isinstance(wrt, str) else int(wrt)
     a.B, a.H, a.Sq, a.Sk, a.D = B, H, Sq, Sk, D
+    a.Hkv = k.shape[2]  # grouped-query attention when k has fewer heads than q
     a.q, a.k, a.v, a.dy = q.data_ptr(), k.data_ptr(), v.data_ptr(), dy.data_ptr()
     a.q_stride[:], a.k_stride[:] = _strides3(q), _strides3(k)
     a.v_stride[:], a.dy_stride[:] = _strides3(v), _strides3(dy)
@@ -113,7 +114,9 @@ def attn_bwd_stage(stage: str, args: AttnBwdArgs, stream=None):
 def attn_bwd(q, k, v, dy, *, wrt="all", mask_kind="none", causal=False, window=0, mask=None,
              threshold=0.5, scale=None, out=None, workspace=None, stream=None,
              return_workspace=False):
-    """Gradients of scaled dot-product attention.
+    """Gradients of scaled dot-product attention.  k and v may have fewer heads
+    than q (grouped-query attention: H a multiple of Hkv, query head h reads
+    K / V head h // (H // Hkv)); dk and dv then have Hkv heads.
 
     mask_kind: "none", "causal", "keypad" (mask = key validity, hidden iff
     < threshold), "window" (keeps [a - window, a] for query position a) or

@@ -61,6 +61,7 @@ class AttnBwdArgs(ctypes.Structure):
         ("mask", ctypes.c_void_p), ("mask_stride", _i64x4),
         ("mask_threshold", ctypes.c_float), ("scale", ctypes.c_float),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("Hkv", ctypes.c_int64),
     ]
 
 

@@ -96,6 +96,10 @@ int validate(const attn_bwd_args *a, Checked &c) {
   // Query-major kernels: 128 queries per workgroup; the KV-major kernel: 128 keys.
   const int64_t qrows = 128;
   const int64_t nblk_q = (a->Sq + qrows - 1) / qrows, nblk_k = (a->Sk + 127) / 128;
+  const int64_t Hkv = a->Hkv == 0 ? a->H : a->Hkv;
+  if (Hkv < 0 || (a->H > 0 && (Hkv == 0 || a->H % Hkv != 0)) || (a->H == 0 && Hkv != 0))
+    return fail(ATTN_E_INVALID, "H (%lld) must be a positive multiple of Hkv (%lld)",
+                (long long)a->H, (long long)a->Hkv);
   const int64_t heads = a->B * a->H;
   if (a->H > 0 && a->B > INT32_MAX / a->H) return fail(ATTN_E_INVALID, "B * H too large");
   if (heads * (nblk_q > nblk_k ? nblk_q : nblk_k) > INT32_MAX)
@@ -115,17 +119,17 @@ int validate(const attn_bwd_args *a, Checked &c) {
     const char *name;
     const void *ptr;
     const int64_t *st;
-    int64_t S;
+    int64_t S, nh;  // sequence length, heads
     bool needed;
     bool output;
   } ts[7] = {
-      {"q", a->q, a->q_stride, a->Sq, has_q, false},
-      {"k", a->k, a->k_stride, a->Sk, has_k, false},
-      {"v", a->v, a->v_stride, a->Sk, has_k, false},
-      {"dy", a->dy, a->dy_stride, a->Sq, has_q, false},
-      {"dq", a->dq, a->dq_stride, a->Sq, has_q && c.want_q, true},
-      {"dk", a->dk, a->dk_stride, a->Sk, has_k && c.want_k, true},
-      {"dv", a->dv, a->dv_stride, a->Sk, has_k && c.want_v, true},
+      {"q", a->q, a->q_stride, a->Sq, a->H, has_q, false},
+      {"k", a->k, a->k_stride, a->Sk, Hkv, has_k, false},
+      {"v", a->v, a->v_stride, a->Sk, Hkv, has_k, false},
+      {"dy", a->dy, a->dy_stride, a->Sq, a->H, has_q, false},
+      {"dq", a->dq, a->dq_stride, a->Sq, a->H, has_q && c.want_q, true},
+      {"dk", a->dk, a->dk_stride, a->Sk, Hkv, has_k && c.want_k, true},
+      {"dv", a->dv, a->dv_stride, a->Sk, Hkv, has_k && c.want_v, true},
   };
   Range rng[7];
   for (int i = 0; i < 7; ++i) {
@@ -142,7 +146,7 @@ int validate(const attn_bwd_args *a, Checked &c) {
     if (i < 4 && ts[i].st[1] * 64 * (int64_t)es >= ((int64_t)1 << 31))
       return fail(ATTN_E_UNSUPPORTED, "%s sequence stride %lld is too large (64 rows must span < 2 GiB)",
                   ts[i].name, (long long)ts[i].st[1]);
-    const int64_t n[4] = {a->B, ts[i].S, a->H, a->D};
+    const int64_t n[4] = {a->B, ts[i].S, ts[i].nh, a->D};
     const int64_t st[4] = {ts[i].st[0], ts[i].st[1], ts[i].st[2], 1};
     rng[i] = extent(ts[i].ptr, n, st, es);
   }
@@ -199,6 +203,8 @@ int validate(const attn_bwd_args *a, Checked &c) {
   p.scale = a->scale;
   p.scale_log2 = a->scale * attn::kLog2e;
   p.B = (int)a->B; p.H = (int)a->H; p.Sq = (int)a->Sq; p.Sk = (int)a->Sk;
+  p.Hkv = (int)Hkv;
+  p.G = Hkv > 0 ? (int)(a->H / Hkv) : 1;
   // Query i sits at absolute position max(Sk - Sq, 0) + i (rlx-cpu
   // `apply_synthetic_mask`, saturating_sub).
   const int64_t q_off = a->Sk > a->Sq ? a->Sk - a->Sq : 0;
@@ -236,7 +242,7 @@ int run_stage(int stage, Checked &c, hipStream_t stream) {
   } else if (stage == attn::STAGE_KV) {
     if (!(c.want_k || c.want_v) || p.Sk == 0) return ATTN_OK;
     p.nblk = c.nblk_k;
-    nblocks = heads * c.nblk_k;
+    nblocks = p.B * p.Hkv * c.nblk_k;  // one key block of one K / V head each
   } else {
     if (!c.want_q || p.Sq == 0) return ATTN_OK;
     p.nblk = c.nblk_q;

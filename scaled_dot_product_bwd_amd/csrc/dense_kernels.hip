@@ -192,8 +192,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     S.m[q] = -INFINITY;
     S.l[q] = S.dl[q] = 0.f;
   }
-  S.kbase = (const T *)p.k + b * p.ks[0] + h * p.ks[2];
-  S.vbase = (const T *)p.v + b * p.vs[0] + h * p.vs[2];
+  S.kbase = (const T *)p.k + b * p.ks[0] + (h / p.G) * p.ks[2];  // the head's K / V head
+  S.vbase = (const T *)p.v + b * p.vs[0] + (h / p.G) * p.vs[2];
   const QRange R = q_range(p, i0, QROWS, MODE == MODE_INDEX);
   S.c_last = R.c_last;
   S.io_k.init(p.ks[1]);
@@ -252,35 +252,38 @@ template <typename T, int D> struct KvState {
   typename M::frag kf[NSD], vf[NSD];
   f32x16 dk[NT], dv[NT];
   ChunkIO<T, D, ROWS> io_q, io_g;
-  const T *qbase, *gbase;
-  int64_t srow0;
-  int b, h, jw, kj, wave, lane, l32, half, c_last, buf;
+  const T *qbase, *gbase;  // Q, dY of the group's first query head
+  int64_t srow0;           // statistics row of (b, first query head, 0)
+  int b, h0, jw, kj, wave, lane, l32, half, c_first, nch, total, buf;
 };
 
+// Chunks are numbered over the whole group: v = head * nch + (c - c_first) for
+// the group's query heads in order, so the stream runs on across heads.
 template <typename T, int D, int MODE>
-__device__ __forceinline__ void kv_issue(const DenseParams &p, KvState<T, D> &S, int c,
+__device__ __forceinline__ void kv_issue(const DenseParams &p, KvState<T, D> &S, int v,
                                          Tile<T, D, KvShape<T>::ROWS> *Q,
                                          Tile<T, D, KvShape<T>::ROWS> *G, float *st) {
   constexpr int ROWS = KvShape<T>::ROWS;
-  S.io_q.issue(S.qbase, p.qs[1], c * ROWS, p.Sq, *Q);
-  S.io_g.issue(S.gbase, p.dys[1], c * ROWS, p.Sq, *G);
-  issue_row_stats<ROWS>(p, S.srow0, c * ROWS, st, S.wave, S.lane);
+  const int hi = v / S.nch, c = S.c_first + (v - hi * S.nch);
+  S.io_q.issue(S.qbase + hi * p.qs[2], p.qs[1], c * ROWS, p.Sq, *Q);
+  S.io_g.issue(S.gbase + hi * p.dys[2], p.dys[1], c * ROWS, p.Sq, *G);
+  issue_row_stats<ROWS>(p, S.srow0 + (int64_t)hi * p.Sq, c * ROWS, st, S.wave, S.lane);
 }
 
 // One chunk: request chunk c + 2, consume chunk c (MASKED: with the per-element
 // mask term), hand over.  Buffers rotate at run time: chunk c sits in buffer
 // S.buf, chunk c + 2 goes to the buffer chunk c - 1 used.
 template <typename T, int D, int MODE, bool MASKED>
-__device__ __forceinline__ void kv_step(const DenseParams &p, KvState<T, D> &S, int c,
+__device__ __forceinline__ void kv_step(const DenseParams &p, KvState<T, D> &S, int v, int c, int h,
                                         Tile<T, D, KvShape<T>::ROWS> *Qs,
                                         Tile<T, D, KvShape<T>::ROWS> *Gs, float (*st)[8 * KvShape<T>::ROWS]) {
   constexpr int ROWS = KvShape<T>::ROWS;
   constexpr int PER_CHUNK = 2 * ChunkIO<T, D, ROWS>::LOADS + stat_loads<ROWS>();
   const int bc = S.buf, bn = bc == 0 ? 2 : bc - 1;
   const int i0 = c * ROWS;
-  const bool issued = c + 2 <= S.c_last;
-  if (issued) kv_issue<T, D, MODE>(p, S, c + 2, &Qs[bn], &Gs[bn], st[bn]);
-  const int kj = S.kj, half = S.half, b = S.b, h = S.h;
+  const bool issued = v + 2 < S.total;
+  if (issued) kv_issue<T, D, MODE>(p, S, v + 2, &Qs[bn], &Gs[bn], st[bn]);
+  const int kj = S.kj, half = S.half, b = S.b;
   // Per-element mask term: the index rule, then padding or bias (log2 domain).
   auto adj = [&](int u, int r) -> float {
     const int i = i0 + 32 * u + kr(r, half);
@@ -306,26 +309,26 @@ __device__ __forceinline__ void kv_step(const DenseParams &p, KvState<T, D> &S, 
   S.buf = bc == 2 ? 0 : bc + 1;
 }
 
-// All visible chunks of the block, in ascending order.  Chunks every (query,
-// key) pair of which the index rule keeps (the causal or window band's
-// interior) run the unmasked body; the band's edges and padding / bias masks
-// the masked one.  Each variant has its own loop, so no loop body holds both.
+// All visible chunks of the block, in ascending order, for each query head of
+// the group in turn.  Chunks every (query, key) pair of which the index rule
+// keeps (the causal or window band's interior) run the unmasked body; the
+// band's edges and padding / bias masks the masked one.  Each variant has its
+// own loop, so no loop body holds both.
 template <typename T, int D, int MODE>
-__device__ __forceinline__ void kv_run(const DenseParams &p, KvState<T, D> &S, int c_first,
+__device__ __forceinline__ void kv_run(const DenseParams &p, KvState<T, D> &S, int c_last,
                                        int j0b, Tile<T, D, KvShape<T>::ROWS> *Qs,
                                        Tile<T, D, KvShape<T>::ROWS> *Gs,
                                        float (*st)[8 * KvShape<T>::ROWS]) {
   constexpr int ROWS = KvShape<T>::ROWS;
   constexpr int PER_CHUNK = 2 * ChunkIO<T, D, ROWS>::LOADS + stat_loads<ROWS>();
-  const int c_last = S.c_last;
-  if (c_first <= c_last) {
-    kv_issue<T, D, MODE>(p, S, c_first, &Qs[0], &Gs[0], st[0]);
-    S.io_q.complete(Qs[0]);
-    S.io_g.complete(Gs[0]);
-  }
-  const bool second = c_first + 1 <= c_last;
+  const int c_first = S.c_first;
+  if (S.total <= 0) return;
+  kv_issue<T, D, MODE>(p, S, 0, &Qs[0], &Gs[0], st[0]);
+  S.io_q.complete(Qs[0]);
+  S.io_g.complete(Gs[0]);
+  const bool second = S.total > 1;
   if (second) {
-    kv_issue<T, D, MODE>(p, S, c_first + 1, &Qs[1], &Gs[1], st[1]);
+    kv_issue<T, D, MODE>(p, S, 1, &Qs[1], &Gs[1], st[1]);
     S.io_q.complete(Qs[1]);
     S.io_g.complete(Gs[1]);
   }
@@ -342,10 +345,13 @@ __device__ __forceinline__ void kv_run(const DenseParams &p, KvState<T, D> &S, i
     if (cu0 < c_first) cu0 = c_first;
     if (cu1 < cu0 - 1) cu1 = cu0 - 1;
   }
-  int c = c_first;
-  for (; c < cu0; ++c) kv_step<T, D, MODE, true>(p, S, c, Qs, Gs, st);
-  for (; c <= cu1; ++c) kv_step<T, D, MODE, false>(p, S, c, Qs, Gs, st);
-  for (; c <= c_last; ++c) kv_step<T, D, MODE, true>(p, S, c, Qs, Gs, st);
+  for (int hi = 0; hi < p.G; ++hi) {
+    const int h = S.h0 + hi, v0 = hi * S.nch - c_first;
+    int c = c_first;
+    for (; c < cu0; ++c) kv_step<T, D, MODE, true>(p, S, v0 + c, c, h, Qs, Gs, st);
+    for (; c <= cu1; ++c) kv_step<T, D, MODE, false>(p, S, v0 + c, c, h, Qs, Gs, st);
+    for (; c <= c_last; ++c) kv_step<T, D, MODE, true>(p, S, v0 + c, c, h, Qs, Gs, st);
+  }
 }
 
 template <typename T, int D, int MODE>
@@ -364,41 +370,44 @@ __global__ __launch_bounds__(256) void k_kv_bwd(const DenseParams p) {
   const int nb = p.nblk;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int blk = L % nb;  // key block 0 sees the most queries under a causal mask
-  S.h = (L / nb) % p.H;
-  S.b = L / (nb * p.H);
+  const int g = (L / nb) % p.Hkv;  // the K / V head; its query heads are g * G ... g * G + G - 1
+  S.b = L / (nb * p.Hkv);
+  S.h0 = g * p.G;
   const int j0b = blk * 128;
   S.jw = j0b + 32 * w;
   S.kj = S.jw + S.l32;
-  const int b = S.b, h = S.h, kj = S.kj, half = S.half;
+  const int b = S.b, kj = S.kj, half = S.half;
   const bool kvalid = kj < p.Sk;
 
-  const T *krow = (const T *)p.k + b * p.ks[0] + (int64_t)(kvalid ? kj : 0) * p.ks[1] + h * p.ks[2];
-  const T *vrow = (const T *)p.v + b * p.vs[0] + (int64_t)(kvalid ? kj : 0) * p.vs[1] + h * p.vs[2];
+  const T *krow = (const T *)p.k + b * p.ks[0] + (int64_t)(kvalid ? kj : 0) * p.ks[1] + g * p.ks[2];
+  const T *vrow = (const T *)p.v + b * p.vs[0] + (int64_t)(kvalid ? kj : 0) * p.vs[1] + g * p.vs[2];
 #pragma unroll
   for (int s = 0; s < NSD; ++s) {
     S.kf[s] = load_frag<T>(krow, s * KS + half * KL, kvalid);
     S.vf[s] = load_frag<T>(vrow, s * KS + half * KL, kvalid);
   }
 
-  S.qbase = (const T *)p.q + b * p.qs[0] + h * p.qs[2];
-  S.gbase = (const T *)p.dy + b * p.dys[0] + h * p.dys[2];
-  S.srow0 = ((int64_t)b * p.H + h) * p.Sq;
+  S.qbase = (const T *)p.q + b * p.qs[0] + S.h0 * p.qs[2];
+  S.gbase = (const T *)p.dy + b * p.dys[0] + S.h0 * p.dys[2];
+  S.srow0 = ((int64_t)b * p.H + S.h0) * p.Sq;
   const int jlast = min(j0b + 128, p.Sk) - 1;
   const int ilo = max(0, (int)max((int64_t)j0b - p.hi_off, (int64_t)0));
   const int ihi = min(p.Sq - 1, (int)min((int64_t)jlast - p.lo_off, (int64_t)kBig));
-  const int c_first = ilo / ROWS;
-  S.c_last = ihi >= ilo ? ihi / ROWS : c_first - 1;
+  S.c_first = ilo / ROWS;
+  const int c_last = ihi >= ilo ? ihi / ROWS : S.c_first - 1;
+  S.nch = c_last - S.c_first + 1;
+  S.total = S.nch > 0 ? S.nch * p.G : 0;
 
 #pragma unroll
   for (int t = 0; t < NT; ++t) S.dk[t] = S.dv[t] = f32x16{};
   S.io_q.init(p.qs[1]);
   S.io_g.init(p.dys[1]);
   wait_vmem();  // fragment loads complete before the loop (see k_row_stats)
-  kv_run<T, D, MODE>(p, S, c_first, j0b, Qs, Gs, st);
+  kv_run<T, D, MODE>(p, S, c_last, j0b, Qs, Gs, st);
 
   if (!kvalid) return;
-  T *dkrow = (T *)p.dk + b * p.dks[0] + (int64_t)kj * p.dks[1] + h * p.dks[2];
-  T *dvrow = (T *)p.dv + b * p.dvs[0] + (int64_t)kj * p.dvs[1] + h * p.dvs[2];
+  T *dkrow = (T *)p.dk + b * p.dks[0] + (int64_t)kj * p.dks[1] + g * p.dks[2];
+  T *dvrow = (T *)p.dv + b * p.dvs[0] + (int64_t)kj * p.dvs[1] + g * p.dvs[2];
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -514,8 +523,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int t = 0; t < NT; ++t) S.dq[q][t] = f32x16{};
   }
-  S.kbase = (const T *)p.k + b * p.ks[0] + h * p.ks[2];
-  S.vbase = (const T *)p.v + b * p.vs[0] + h * p.vs[2];
+  S.kbase = (const T *)p.k + b * p.ks[0] + (h / p.G) * p.ks[2];  // the head's K / V head
+  S.vbase = (const T *)p.v + b * p.vs[0] + (h / p.G) * p.vs[2];
   const QRange R = q_range(p, i0, QROWS, MODE == MODE_INDEX);
   S.c_last = R.c_last;
   S.io_k.init(p.ks[1]);

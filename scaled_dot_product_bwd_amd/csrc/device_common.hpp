@@ -50,6 +50,7 @@ struct DenseParams {
   float scale;       // natural scale, multiplies dS
   float scale_log2;  // scale * log2(e), turns Q.K into a log2-domain score
   int B, H, Sq, Sk;
+  int Hkv, G;  // K / V heads and the query heads per K / V head (H = Hkv * G)
   // Index rule: key j is visible to query i iff lo_off <= j - i <= hi_off
   // (and i < Sq, j < Sk).  Causal: hi_off = max(Sk - Sq, 0); window:
   // lo_off = hi_off - w; otherwise +-kBig.

@@ -39,8 +39,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_args_struct_size_matches_header_layout():
     # 2 int32 + 5 int64 + 7 pointers + 21 int64 strides + 2 int32 + int64 window
-    # + pointer + 4 int64 + 2 float + pointer + size_t
-    assert ctypes.sizeof(_abi.AttnBwdArgs) == 8 + 40 + 56 + 168 + 8 + 8 + 8 + 32 + 8 + 8 + 8
+    # + pointer + 4 int64 + 2 float + pointer + size_t + int64 Hkv
+    assert ctypes.sizeof(_abi.AttnBwdArgs) == 8 + 40 + 56 + 168 + 8 + 8 + 8 + 32 + 8 + 8 + 8 + 8
 
 
 def test_workspace_bytes():
@@ -75,6 +75,8 @@ def _rc(a):
     ("wrt", 4, _abi.ATTN_E_INVALID),
     ("mask_kind", 9, _abi.ATTN_E_INVALID),
     ("D", 96, _abi.ATTN_E_UNSUPPORTED),
+    ("Hkv", 3, _abi.ATTN_E_INVALID),   # H = 2 is not a multiple of 3
+    ("Hkv", -1, _abi.ATTN_E_INVALID),
     ("D", 256, _abi.ATTN_E_UNSUPPORTED),
     ("Sq", -1, _abi.ATTN_E_INVALID),
     ("q", 0, _abi.ATTN_E_INVALID),
