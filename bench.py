@@ -48,13 +48,18 @@ HBM_PEAK_GBS = 8000.0
 CONTRACTIONS = {"row_stats": 2, "kv": 4, "dq": 3}
 KERNEL_NAMES = {"row_stats": "k_row_stats", "kv": "k_kv_bwd", "dq": "k_dq_bwd",
                 "paged": "k_paged_kv_bwd"}
+# Files whose content decides a kernel's code (a stored traffic measurement is
+# used only while their hash is unchanged).
 KERNEL_SOURCES = ["scaled_dot_product_bwd_amd/csrc/dense_kernels.hip",
                   "scaled_dot_product_bwd_amd/csrc/device_common.hpp",
-                  "scaled_dot_product_bwd_amd/csrc/kv_core.hpp"]
+                  "scaled_dot_product_bwd_amd/csrc/kv_core.hpp",
+                  "scaled_dot_product_bwd_amd/csrc/q_core.hpp",
+                  "scaled_dot_product_bwd_amd/build.py"]
 PAGED_SOURCES = ["scaled_dot_product_bwd_amd/csrc/paged_kernels.hip",
                  "scaled_dot_product_bwd_amd/csrc/paged.hpp",
                  "scaled_dot_product_bwd_amd/csrc/device_common.hpp",
-                 "scaled_dot_product_bwd_amd/csrc/kv_core.hpp"]
+                 "scaled_dot_product_bwd_amd/csrc/kv_core.hpp",
+                 "scaled_dot_product_bwd_amd/build.py"]
 
 
 def log(msg):
