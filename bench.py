@@ -17,7 +17,9 @@ Prints one JSON line.  Besides the contract fields it carries
                the MI355X dense bf16 MFMA peak; `traffic` comes from a stored
                rocprofv3 FETCH_SIZE / WRITE_SIZE measurement when it was taken
                on the current kernel source, else null;
-  cpu_baseline the CPU oracle timed on a bounded sample of the same workload.
+  cpu_baseline the CPU oracle timed on a bounded sample of the same workload;
+  from_forward the same step when a forward's log-sum-exp and output replace
+               the row statistics pass (attn_bwd_from_forward).
 
 --workload paged measures the paged grouped-query history backward instead
 (ruDNN `history_backward`): bf16, 32 query / 8 KV heads, D 128, page 16, 16
@@ -372,6 +374,35 @@ def main():
     if not all(torch.isfinite(t).all().item() for t in (dq, dk, dv)):
         raise RuntimeError("non-finite gradients in the benchmark output")
 
+    # The same backward from a forward's saved statistics (attn_bwd_from_forward:
+    # log-sum-exp and O replace the row statistics pass).  Timing only: lse comes
+    # from this run's statistics and O is a stand-in tensor of the right shape
+    # (the kernels' cost does not depend on the values).
+    import ctypes
+    m_ws, l_ws, _ = sdb.row_stats_views(ws, B, H, S)
+    lse = (m_ws + torch.log(l_ws)).contiguous()
+    o_stand = dy.clone()
+    ost = (ctypes.c_int64 * 3)(*o_stand.stride()[:3])
+    lib = sdb.load_library()
+    dq2, dk2, dv2 = (torch.empty_like(x) for x in (q, k, v))
+    a2 = sdb.make_args(q, k, v, dy, dq2, dk2, dv2, mask_kind=args.mask, window=window, workspace=ws)
+
+    def fstep():
+        rc = lib.attn_bwd_from_forward(ctypes.byref(a2), ctypes.c_void_p(lse.data_ptr()),
+                                       ctypes.c_void_p(o_stand.data_ptr()), ost,
+                                       sdb._stream_handle(None))
+        if rc != 0:
+            raise RuntimeError(lib.attn_bwd_last_error().decode())
+    for _ in range(args.warmup):
+        fstep()
+    torch.cuda.synchronize()
+    t_start.record()
+    for _ in range(args.steps):
+        fstep()
+    t_end.record()
+    torch.cuda.synchronize()
+    ff_ms = t_start.elapsed_time(t_end) / args.steps
+
     flops = counted_flops(B, H, S, S, D, args.mask, window)
     value = flops / (ms_step / 1e3) / 1e12
     pairs_step = flops / (10.0 * D)  # visible pairs as counted
@@ -402,6 +433,8 @@ def main():
                    "counted_flops": flops},
         "pct_mfma_peak": round(100.0 * value / PEAK_TFLOPS["bf16"], 3),
         "kernels_ms": {k_: round(v_, 4) for k_, v_ in per_kernel.items()},
+        "from_forward": {"ms_per_step": round(ff_ms, 5),
+                         "tflops": round(flops / (ff_ms / 1e3) / 1e12, 3)},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

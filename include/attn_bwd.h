@@ -210,6 +210,18 @@ int attn_bwd_paged(const attn_bwd_paged_args *a, void *stream);
 int attn_bwd_paged_row_stats(const attn_bwd_paged_args *a, float *stats, void *stream);
 int attn_bwd_paged_dq(const attn_bwd_paged_args *a, void *dq, void *stream);
 
+/* The dense backward from what a forward pass saved, instead of recomputing
+ * the row statistics: `lse` (device fp32 [B, H, Sq], contiguous) holds, per
+ * row, the natural log-sum-exp of its scaled, masked scores (-inf for a row
+ * that sees no key), and `out` (device, the element type of q, [B, Sq, H, D]
+ * with element strides out_stride[0..2] for (b, s, h)) the forward output O.
+ * Then delta = rowsum(dY * O) (= rowsum(P * dP)) and P = exp(s - lse); the
+ * dK / dV and dQ stages run as in attn_bwd.  Workspace planes 2 (delta) and 3
+ * are written, planes 0 and 1 are not.  Same arguments and rules as attn_bwd
+ * otherwise; lse and out must not overlap the workspace. */
+int attn_bwd_from_forward(const attn_bwd_args *a, const float *lse, const void *out,
+                          const int64_t *out_stride, void *stream);
+
 /* Thread-local description of the last non-OK status returned on this thread. */
 const char *attn_bwd_last_error(void);
 

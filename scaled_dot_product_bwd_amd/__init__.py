@@ -113,7 +113,7 @@ def attn_bwd_stage(stage: str, args: AttnBwdArgs, stream=None):
 
 def attn_bwd(q, k, v, dy, *, wrt="all", mask_kind="none", causal=False, window=0, mask=None,
              threshold=0.5, scale=None, out=None, workspace=None, stream=None,
-             return_workspace=False):
+             return_workspace=False, fwd_lse=None, fwd_out=None):
     """Gradients of scaled dot-product attention.  k and v may have fewer heads
     than q (grouped-query attention: H a multiple of Hkv, query head h reads
     K / V head h // (H // Hkv)); dk and dv then have Hkv heads.
@@ -123,6 +123,9 @@ def attn_bwd(q, k, v, dy, *, wrt="all", mask_kind="none", causal=False, window=0
     "bias" (mask added to the scaled scores); ``causal=True`` adds the causal
     rule to "keypad" / "bias".  ``mask`` is float32 and broadcasts to
     [B, H, Sq, Sk] ([B, 1, 1, Sk] for per-batch padding).
+    With ``fwd_lse`` (float32 [B, H, Sq]: the forward's natural log-sum-exp
+    per row) and ``fwd_out`` (the forward output O, like q), the row
+    statistics come from them (attn_bwd_from_forward) instead of a recompute.
     Returns (dq, dk, dv); entries that ``wrt`` does not ask for are None.
     """
     torch = _torch()
@@ -140,7 +143,16 @@ def attn_bwd(q, k, v, dy, *, wrt="all", mask_kind="none", causal=False, window=0
     args = make_args(q, k, v, dy, dq, dk, dv, wrt=w, mask_kind=mask_kind, causal=causal,
                      window=window, mask=mask, threshold=threshold, scale=scale,
                      workspace=workspace)
-    attn_bwd_stage("all", args, stream)
+    if fwd_lse is not None or fwd_out is not None:
+        if fwd_lse is None or fwd_out is None:
+            raise ValueError("fwd_lse and fwd_out go together")
+        lse = fwd_lse.contiguous()
+        ost = (ctypes.c_int64 * 3)(*_strides3(fwd_out))
+        _check(load_library().attn_bwd_from_forward(
+            ctypes.byref(args), ctypes.c_void_p(lse.data_ptr()), ctypes.c_void_p(fwd_out.data_ptr()),
+            ost, _stream_handle(stream)))
+    else:
+        attn_bwd_stage("all", args, stream)
     if return_workspace:
         return (dq, dk, dv), workspace
     return dq, dk, dv

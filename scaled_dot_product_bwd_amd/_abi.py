@@ -24,6 +24,7 @@ STATUS_NAMES = {ATTN_E_INVALID: "ATTN_E_INVALID", ATTN_E_UNSUPPORTED: "ATTN_E_UN
 EXPORTED = ["attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_row_stats", "attn_bwd_kv",
             "attn_bwd_dq", "attn_bwd_paged_plan_words", "attn_bwd_paged_plan_build",
             "attn_bwd_paged", "attn_bwd_paged_row_stats", "attn_bwd_paged_dq",
+            "attn_bwd_from_forward",
             "attn_bwd_last_error"]
 
 # Plan header words (scaled_dot_product_bwd_amd/csrc/paged.hpp).
@@ -110,6 +111,10 @@ def load_library():
                                               _i32, _p, ctypes.c_int64]
     lib.attn_bwd_paged.restype = ctypes.c_int
     lib.attn_bwd_paged.argtypes = [ctypes.POINTER(AttnBwdPagedArgs), ctypes.c_void_p]
+    lib.attn_bwd_from_forward.restype = ctypes.c_int
+    lib.attn_bwd_from_forward.argtypes = [ctypes.POINTER(AttnBwdArgs), ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
+                                          ctypes.c_void_p]
     for name in ("attn_bwd_paged_row_stats", "attn_bwd_paged_dq"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int

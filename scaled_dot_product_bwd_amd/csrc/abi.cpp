@@ -265,6 +265,47 @@ int run(const attn_bwd_args *a, void *stream, int first, int last) {
   return ATTN_OK;
 }
 
+// Dense backward from a forward's saved statistics: lse and O replace the row
+// statistics pass.
+int run_from_forward(const attn_bwd_args *a, const float *lse, const void *out,
+                     const int64_t *out_stride, void *stream) {
+  Checked c;
+  int rc = validate(a, c);
+  if (rc != ATTN_OK) return rc;
+  const int64_t rows = a->B * a->H * a->Sq;
+  const bool any = rows > 0 && a->Sk > 0 && (c.want_q || c.want_k || c.want_v);
+  if (any) {
+    if (!lse || !out || !out_stride) return fail(ATTN_E_INVALID, "lse / out / out_stride is NULL");
+    const size_t es = c.bf16 ? 2 : 4;
+    if ((uintptr_t)lse % 4) return fail(ATTN_E_INVALID, "lse is not 4-byte aligned");
+    if ((uintptr_t)out % 16) return fail(ATTN_E_UNSUPPORTED, "out is not 16-byte aligned");
+    for (int j = 0; j < 3; ++j) {
+      if (out_stride[j] < 0) return fail(ATTN_E_INVALID, "out has a negative stride");
+      if ((out_stride[j] * (int64_t)es) % 16)
+        return fail(ATTN_E_UNSUPPORTED, "out stride %d is not a multiple of 16 bytes", j);
+    }
+    // The workspace planes written here must not alias the inputs read.
+    Range ws, lr, orng;
+    ws.lo = (uintptr_t)a->workspace;
+    ws.hi = ws.lo + attn_bwd_workspace_bytes(a->B, a->H, a->Sq);
+    lr.lo = (uintptr_t)lse;
+    lr.hi = lr.lo + (uintptr_t)(rows * 4);
+    const int64_t n[4] = {a->B, a->Sq, a->H, a->D};
+    const int64_t st[4] = {out_stride[0], out_stride[1], out_stride[2], 1};
+    orng = extent(out, n, st, es);
+    if (overlap(ws, lr) || overlap(ws, orng))
+      return fail(ATTN_E_INVALID, "lse / out overlap the workspace");
+    const hipError_t e = attn::launch_fwd_stats(c.bf16, c.D, c.p, lse, out, out_stride,
+                                                (hipStream_t)stream);
+    if (e != hipSuccess) return fail(ATTN_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  }
+  for (int s = attn::STAGE_KV; s <= attn::STAGE_DQ; ++s) {
+    rc = run_stage(s, c, (hipStream_t)stream);
+    if (rc != ATTN_OK) return rc;
+  }
+  return ATTN_OK;
+}
+
 // ---------------------------------------------------------------------------
 // Paged history backward.
 
@@ -432,6 +473,11 @@ int attn_bwd_row_stats(const attn_bwd_args *a, void *stream) {
 
 int attn_bwd_kv(const attn_bwd_args *a, void *stream) {
   return run(a, stream, attn::STAGE_KV, attn::STAGE_KV);
+}
+
+int attn_bwd_from_forward(const attn_bwd_args *a, const float *lse, const void *out,
+                          const int64_t *out_stride, void *stream) {
+  return run_from_forward(a, lse, out, out_stride, stream);
 }
 
 int attn_bwd_dq(const attn_bwd_args *a, void *stream) {

@@ -228,3 +228,18 @@ def test_paged_query_side_rejections():
     assert "stats_out is NULL" in lib.attn_bwd_last_error().decode()
     assert lib.attn_bwd_paged_dq(ctypes.byref(a), ctypes.c_void_p(1 << 30), None) == _abi.ATTN_E_INVALID
     assert "stats is NULL" in lib.attn_bwd_last_error().decode()
+
+
+def test_from_forward_rejections():
+    lib = sdb.load_library()
+    a = _args()
+    ost = (ctypes.c_int64 * 3)(64 * 2 * 64, 2 * 64, 64)
+    rc = lib.attn_bwd_from_forward(ctypes.byref(a), None, ctypes.c_void_p(1 << 28), ost, None)
+    assert rc == _abi.ATTN_E_INVALID and "NULL" in lib.attn_bwd_last_error().decode()
+    rc = lib.attn_bwd_from_forward(ctypes.byref(a), ctypes.c_void_p(1 << 29), ctypes.c_void_p((1 << 28) + 2),
+                                   ost, None)
+    assert rc == _abi.ATTN_E_UNSUPPORTED and "aligned" in lib.attn_bwd_last_error().decode()
+    # lse inside the workspace
+    rc = lib.attn_bwd_from_forward(ctypes.byref(a), ctypes.c_void_p(a.workspace), ctypes.c_void_p(1 << 28),
+                                   ost, None)
+    assert rc == _abi.ATTN_E_INVALID and "workspace" in lib.attn_bwd_last_error().decode()
