@@ -55,6 +55,12 @@ def _load():
     lib.oracle_paged_kv_bwd.argtypes = paged + [_dp, _dp, _dp, ctypes.c_int]
     lib.oracle_paged_dq.restype = ctypes.c_int
     lib.oracle_paged_dq.argtypes = paged + [_dp, _dp, ctypes.c_int]
+    mla = [i32, _ip, _ip, i32, i32, _ip, _ip, i32, i32, i32, i32, i32, i32, i32, dbl,
+           _dp, _dp, _dp, _dp, _dp]
+    lib.oracle_paged_mla_row_stats.restype = ctypes.c_int
+    lib.oracle_paged_mla_row_stats.argtypes = mla + [_dp, ctypes.c_int]
+    lib.oracle_paged_mla_kv_bwd.restype = ctypes.c_int
+    lib.oracle_paged_mla_kv_bwd.argtypes = mla + [_dp, _dp, _dp, ctypes.c_int]
     _lib = lib
     return lib
 
@@ -210,5 +216,58 @@ def paged_dq(w, q, dy, k_pool, v_pool, stats, *, heads, kv_heads, page_size, cau
     return dq
 
 
-__all__ = ["attn_bwd", "attn_bwd_gqa", "paged_row_stats", "paged_kv_bwd", "paged_dq", "MASK_NONE", "MASK_CAUSAL",
+def _mla_scale(D, P, scale):
+    # the score contracts over the latent and the position parts together
+    if scale is None:
+        scale = float(np.float32(1.0) / np.sqrt(np.float32(D + P)))
+    return float(scale)
+
+
+def paged_mla_row_stats(w, q, qp, dy, latent_pool, kp_pool, *, heads, kv_heads, page_size,
+                        causal=True, scale=None, nthreads=None):
+    """Latent variant: (max, denominator, delta) per (row, head), shape [nq, heads, 3].
+
+    q, dy: [nq, heads, D] (latent width); qp: [nq, heads, P]; latent_pool:
+    [slots, kv_heads, D] (both key and value); kp_pool: [slots, kv_heads, P].
+    The default scale is 1/sqrt(D + P) (the score's contraction width)."""
+    seq_lens, bt, nseq, max_pages, qs, qpos = _paged_common(w)
+    q, qp, dy = _f64(q), _f64(qp), _f64(dy)
+    lat, kp = _f64(latent_pool), _f64(kp_pool)
+    nq, _, D = q.shape
+    P = qp.shape[2]
+    pool_pages = lat.shape[0] // page_size
+    stats = np.empty((nq, heads, 3))
+    rc = _load().oracle_paged_mla_row_stats(
+        nseq, _ptr(seq_lens, _ip), _ptr(bt, _ip), max_pages, nq, _ptr(qs, _ip),
+        _ptr(qpos, _ip), heads, kv_heads, D, P, page_size, pool_pages, int(bool(causal)),
+        _mla_scale(D, P, scale), _ptr(q), _ptr(qp), _ptr(dy), _ptr(lat), _ptr(kp), _ptr(stats),
+        int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError(f"oracle_paged_mla_row_stats rejected its arguments (rc={rc})")
+    return stats
+
+
+def paged_mla_kv_bwd(w, q, qp, dy, latent_pool, kp_pool, stats, dlat_init, dkp_init, *,
+                     heads, kv_heads, page_size, causal=True, scale=None, nthreads=None):
+    """Latent variant: (d latent, d position key) pools; listed pages' slots
+    overwritten, all other slots = the *_init contents."""
+    seq_lens, bt, nseq, max_pages, qs, qpos = _paged_common(w)
+    q, qp, dy, st = _f64(q), _f64(qp), _f64(dy), _f64(stats)
+    lat, kp = _f64(latent_pool), _f64(kp_pool)
+    dlat, dkp = _f64(dlat_init).copy(), _f64(dkp_init).copy()
+    nq, _, D = q.shape
+    P = qp.shape[2]
+    pool_pages = lat.shape[0] // page_size
+    rc = _load().oracle_paged_mla_kv_bwd(
+        nseq, _ptr(seq_lens, _ip), _ptr(bt, _ip), max_pages, nq, _ptr(qs, _ip),
+        _ptr(qpos, _ip), heads, kv_heads, D, P, page_size, pool_pages, int(bool(causal)),
+        _mla_scale(D, P, scale), _ptr(q), _ptr(qp), _ptr(dy), _ptr(lat), _ptr(kp), _ptr(st),
+        _ptr(dlat), _ptr(dkp), int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError(f"oracle_paged_mla_kv_bwd rejected its arguments (rc={rc})")
+    return dlat, dkp
+
+
+__all__ = ["attn_bwd", "attn_bwd_gqa", "paged_row_stats", "paged_kv_bwd", "paged_dq",
+           "paged_mla_row_stats", "paged_mla_kv_bwd", "MASK_NONE", "MASK_CAUSAL",
            "MASK_KEYPAD", "MASK_WINDOW", "MASK_BIAS", "default_threads"]

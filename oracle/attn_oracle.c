@@ -299,6 +299,11 @@ typedef struct {
   const double *q, *dy, *k_pool, *v_pool, *stats_in;
   double *stats_out;  /* row statistics (paged_row_stats) */
   double *gk, *gv;    /* gradient accumulators over the whole pool (paged_kv_bwd) */
+  /* latent variant: position width, position parts of queries and keys, and the
+   * position-key gradient accumulator */
+  int P;
+  const double *qp, *kp_pool;
+  double *gkp;
   int64_t next, count; /* work counter shared by threads */
   pthread_mutex_t lock;
 } paged_job;
@@ -538,5 +543,178 @@ int oracle_paged_kv_bwd(int nseq, const int32_t *seq_lens, const int32_t *block_
     if (dv_pool) memcpy(dv_pool + base, gv + base, sizeof(double) * n);
   }
   free(gk); free(gv); free(listed);
+  return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Latent (MLA) variant of the paged history backward ([ruDNN]
+ * `history_backward` with its `mla` switch on).  Every pool slot holds one
+ * latent row c (width D) that is BOTH the key and the value, plus a position
+ * key kp (width P).  A query row carries q (width D, in the latent space) and
+ * qp (width P); dY has the latent width D.  Per visible (row, head, token):
+ *   s  = scale (q . c + qp . kp)          the score uses both parts
+ *   dP = dY . c                           the value is the latent itself
+ *   p  = exp(s - max) / den,  ds = p (dP - delta) scale
+ *   dc  += ds q + p dY                    the latent's key and value derivatives
+ *   dkp += ds qp
+ * There is no separate value gradient.  Reading: the value width equals the
+ * latent width (dY rows are indexed with it while the latent's derivative runs
+ * over the key width), and the value is the latent row. */
+
+/* One query row r, every head: visible latent-variant scores, their softmax and
+ * delta = sum_t P dP, from the definition. */
+static void *paged_mla_stats_worker(void *arg) {
+  paged_job *J = (paged_job *)arg;
+  const int D = J->D, P = J->P, group = J->heads / J->kv_heads;
+  int maxlen = 1;
+  for (int s = 0; s < J->nseq; ++s)
+    if (J->seq_lens[s] > maxlen) maxlen = J->seq_lens[s];
+  double *sc = (double *)malloc(sizeof(double) * maxlen);
+  double *dp = (double *)malloc(sizeof(double) * maxlen);
+  unsigned char *vis = (unsigned char *)malloc(maxlen);
+  for (int64_t r; sc && dp && vis && (r = paged_take(J)) >= 0;) {
+    const int s = J->query_seq[r];
+    const int len = J->seq_lens[s];
+    for (int h = 0; h < J->heads; ++h) {
+      const int g = h / group;
+      const double *qr = J->q + (r * J->heads + h) * D;
+      const double *qpr = J->qp + (r * J->heads + h) * P;
+      const double *gr = J->dy + (r * J->heads + h) * D;
+      double mx = -INFINITY;
+      int any = 0;
+      for (int t = 0; t < len; ++t) {
+        const int64_t slot = paged_slot(J, s, t);
+        const double *cr = J->k_pool + (slot * J->kv_heads + g) * D;
+        const double *pr = J->kp_pool + (slot * J->kv_heads + g) * P;
+        double a = 0.0, c = 0.0;
+        for (int d = 0; d < D; ++d) { a += qr[d] * cr[d]; c += gr[d] * cr[d]; }
+        for (int d = 0; d < P; ++d) a += qpr[d] * pr[d];
+        sc[t] = J->scale * a;
+        dp[t] = c;
+        vis[t] = (unsigned char)(!J->causal || t <= J->query_pos[r]);
+        if (vis[t]) { any = 1; if (sc[t] > mx) mx = sc[t]; }
+      }
+      double den = 0.0, delta = 0.0;
+      if (any) {
+        for (int t = 0; t < len; ++t) if (vis[t]) den += exp(sc[t] - mx);
+        for (int t = 0; t < len; ++t) if (vis[t]) delta += exp(sc[t] - mx) / den * dp[t];
+      }
+      double *st = J->stats_out + (r * J->heads + h) * 3;
+      st[0] = any ? mx : -INFINITY;
+      st[1] = den;
+      st[2] = delta;
+    }
+  }
+  free(sc); free(dp); free(vis);
+  return NULL;
+}
+
+/* (max, denominator, delta) per (row, head) of the latent variant. */
+int oracle_paged_mla_row_stats(int nseq, const int32_t *seq_lens, const int32_t *block_table,
+                               int max_pages, int nq, const int32_t *query_seq,
+                               const int32_t *query_pos, int heads, int kv_heads, int D, int P,
+                               int page_size, int pool_pages, int causal, double scale,
+                               const double *q, const double *qp, const double *dy,
+                               const double *latent_pool, const double *kp_pool, double *stats,
+                               int nthreads) {
+  if (P < 0 || paged_check(nseq, seq_lens, block_table, max_pages, nq, query_seq, heads,
+                           kv_heads, page_size, pool_pages))
+    return -1;
+  paged_job J;
+  memset(&J, 0, sizeof J);
+  J.nseq = nseq; J.max_pages = max_pages; J.nq = nq; J.heads = heads; J.kv_heads = kv_heads;
+  J.D = D; J.P = P; J.page_size = page_size; J.pool_pages = pool_pages; J.causal = causal;
+  J.seq_lens = seq_lens; J.block_table = block_table; J.query_seq = query_seq;
+  J.query_pos = query_pos; J.scale = scale;
+  J.q = q; J.qp = qp; J.dy = dy; J.k_pool = latent_pool; J.kp_pool = kp_pool;
+  J.stats_out = stats;
+  J.count = nq;
+  paged_parallel(&J, paged_mla_stats_worker, nthreads);
+  return 0;
+}
+
+/* All latent-variant contributions to the slots of one KV head g, in a fixed
+ * order: sequences, tokens, query rows, the group's heads. */
+static void *paged_mla_kv_worker(void *arg) {
+  paged_job *J = (paged_job *)arg;
+  const int D = J->D, P = J->P, group = J->heads / J->kv_heads;
+  for (int64_t g; (g = paged_take(J)) >= 0;) {
+    for (int s = 0; s < J->nseq; ++s) {
+      const int len = J->seq_lens[s];
+      for (int t = 0; t < len; ++t) {
+        const int64_t slot = paged_slot(J, s, t);
+        const double *cr = J->k_pool + (slot * J->kv_heads + g) * D;
+        const double *pr = J->kp_pool + (slot * J->kv_heads + g) * P;
+        double *ac = J->gk + (slot * J->kv_heads + g) * D;
+        double *ap = J->gkp + (slot * J->kv_heads + g) * P;
+        for (int r = 0; r < J->nq; ++r) {
+          if (J->query_seq[r] != s) continue;
+          if (J->causal && t > J->query_pos[r]) continue;
+          for (int h = (int)g * group; h < ((int)g + 1) * group; ++h) {
+            const double *st = J->stats_in + ((int64_t)r * J->heads + h) * 3;
+            if (st[1] == 0.0) continue;
+            const double *qr = J->q + ((int64_t)r * J->heads + h) * D;
+            const double *qpr = J->qp + ((int64_t)r * J->heads + h) * P;
+            const double *gr = J->dy + ((int64_t)r * J->heads + h) * D;
+            double a = 0.0, c = 0.0;
+            for (int d = 0; d < D; ++d) { a += qr[d] * cr[d]; c += gr[d] * cr[d]; }
+            for (int d = 0; d < P; ++d) a += qpr[d] * pr[d];
+            const double p = exp(J->scale * a - st[0]) / st[1];
+            const double ds = p * (c - st[2]) * J->scale;
+            for (int d = 0; d < D; ++d) ac[d] += ds * qr[d] + p * gr[d];
+            for (int d = 0; d < P; ++d) ap[d] += ds * qpr[d];
+          }
+        }
+      }
+    }
+  }
+  return NULL;
+}
+
+/* Latent and position-key gradients into their pools.  `dlat_pool` [slots,
+ * kv_heads, D] and `dkp_pool` [slots, kv_heads, P] hold the caller's contents on
+ * entry (either may be NULL: not requested); on return every slot of every
+ * listed page holds its gradient (zero where no row sees it) and every other
+ * slot is unchanged.  KV heads have disjoint outputs; threads split them. */
+int oracle_paged_mla_kv_bwd(int nseq, const int32_t *seq_lens, const int32_t *block_table,
+                            int max_pages, int nq, const int32_t *query_seq,
+                            const int32_t *query_pos, int heads, int kv_heads, int D, int P,
+                            int page_size, int pool_pages, int causal, double scale,
+                            const double *q, const double *qp, const double *dy,
+                            const double *latent_pool, const double *kp_pool,
+                            const double *stats, double *dlat_pool, double *dkp_pool,
+                            int nthreads) {
+  if (P < 0 || paged_check(nseq, seq_lens, block_table, max_pages, nq, query_seq, heads,
+                           kv_heads, page_size, pool_pages))
+    return -1;
+  const int64_t nslot = (int64_t)pool_pages * page_size;
+  double *gc = (double *)calloc((size_t)(nslot * kv_heads * D) + 1, sizeof(double));
+  double *gp = (double *)calloc((size_t)(nslot * kv_heads * P) + 1, sizeof(double));
+  unsigned char *listed = (unsigned char *)calloc((size_t)pool_pages + 1, 1);
+  if (!gc || !gp || !listed) { free(gc); free(gp); free(listed); return -1; }
+
+  for (int s = 0; s < nseq; ++s) {
+    const int np = (seq_lens[s] + page_size - 1) / page_size;
+    for (int p = 0; p < np; ++p) listed[block_table[(int64_t)s * max_pages + p]] = 1;
+  }
+  paged_job J;
+  memset(&J, 0, sizeof J);
+  J.nseq = nseq; J.max_pages = max_pages; J.nq = nq; J.heads = heads; J.kv_heads = kv_heads;
+  J.D = D; J.P = P; J.page_size = page_size; J.pool_pages = pool_pages; J.causal = causal;
+  J.seq_lens = seq_lens; J.block_table = block_table; J.query_seq = query_seq;
+  J.query_pos = query_pos; J.scale = scale;
+  J.q = q; J.qp = qp; J.dy = dy; J.k_pool = latent_pool; J.kp_pool = kp_pool;
+  J.stats_in = stats;
+  J.gk = gc; J.gkp = gp;
+  J.count = kv_heads;
+  paged_parallel(&J, paged_mla_kv_worker, nthreads);
+
+  for (int pg = 0; pg < pool_pages; ++pg) {
+    if (!listed[pg]) continue;
+    const int64_t nc = (int64_t)page_size * kv_heads * D, npp = (int64_t)page_size * kv_heads * P;
+    if (dlat_pool) memcpy(dlat_pool + pg * nc, gc + pg * nc, sizeof(double) * nc);
+    if (dkp_pool) memcpy(dkp_pool + pg * npp, gp + pg * npp, sizeof(double) * npp);
+  }
+  free(gc); free(gp); free(listed);
   return 0;
 }

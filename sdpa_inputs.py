@@ -104,7 +104,7 @@ def hash_inputs(n, seed):
 def paged_workload(*, seed, nseq=16, len_lo=256, len_hi=4096, q_per_seq=64, page_size=16,
                    unused_frac=0.25, heads=32, kv_heads=8, D=128, dtype=torch.bfloat16,
                    share_prefix_pages=0, shuffle_rows=False, nan_unused=True,
-                   lengths=None):
+                   lengths=None, position_dim=0):
     """A paged KV pool and packed query rows.
 
     Draw order: lengths, page permutation, (row shuffle), Q, dY, K pool, V pool.
@@ -116,6 +116,9 @@ def paged_workload(*, seed, nseq=16, len_lo=256, len_hi=4096, q_per_seq=64, page
     (a shared prefix), so those pages have several (sequence, logical page) links.
     Row r of sequence s sits at position len_s - q_per_seq + i.  Tail slots and
     unused pages of the K/V pools hold NaN when ``nan_unused``.
+    With ``position_dim`` = P > 0 (the latent variant, where the K pool holds
+    the latents) the draw continues with qp [nq, heads, P] and the position-key
+    pool kp_pool [slots, kv_heads, P], NaN at the same slots.
     """
     g = _gen(seed)
     if lengths is None:
@@ -163,7 +166,15 @@ def paged_workload(*, seed, nseq=16, len_lo=256, len_hi=4096, q_per_seq=64, page
     if nan_unused:
         k_pool[~live] = float("nan")
         v_pool[~live] = float("nan")
-    return dict(seq_lens=lens.to(torch.int32), block_table=bt, query_seq=query_seq,
-                query_pos=query_pos, q=q, dy=dy, k_pool=k_pool, v_pool=v_pool,
-                live_slots=live, pool_pages=pool_pages, page_size=page_size,
-                heads=heads, kv_heads=kv_heads, D=D, dtype=dtype)
+    out = dict(seq_lens=lens.to(torch.int32), block_table=bt, query_seq=query_seq,
+               query_pos=query_pos, q=q, dy=dy, k_pool=k_pool, v_pool=v_pool,
+               live_slots=live, pool_pages=pool_pages, page_size=page_size,
+               heads=heads, kv_heads=kv_heads, D=D, dtype=dtype)
+    if position_dim > 0:
+        out["qp"] = _randn(g, (nq, heads, position_dim), dtype)
+        kp_pool = _randn(g, (pool_pages * page_size, kv_heads, position_dim), dtype)
+        if nan_unused:
+            kp_pool[~live] = float("nan")
+        out["kp_pool"] = kp_pool
+        out["P"] = position_dim
+    return out
