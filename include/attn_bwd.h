@@ -171,7 +171,7 @@ int attn_bwd_paged_plan_build(int32_t nseq, const int32_t *seq_lens, const int32
 
 typedef struct attn_bwd_paged_args {
   int32_t dtype;      /* ATTN_F32 or ATTN_BF16: q, dy, pools and gradient pools */
-  int32_t need;       /* bit 0: dK, bit 1: dV (at least one) */
+  int32_t need;       /* bit 0: dK, bit 1: dV (at least one); latent variant: see below */
   int32_t heads, kv_heads, head_dim, page_size, causal; /* head_dim in {32, 64, 128}; causal 0 / 1 */
   int32_t nq, pool_pages;                /* must match the plan */
   float scale;                           /* finite */
@@ -182,6 +182,23 @@ typedef struct attn_bwd_paged_args {
   const int32_t *plan;                   /* device copy of the same words (read by the kernel) */
   void *dk_pool, *dv_pool;               /* device, same shape as the pools; written only at
                                             slots of listed pages; NULL allowed iff not in `need` */
+  /* Latent (MLA) variant, ruDNN history_backward with its `mla` switch: set
+   * mla = 1.  Then k_pool holds each slot's latent row c (width head_dim, which
+   * is both key and value; v_pool and dv_pool are not used), kp_pool the
+   * position keys [pool_pages * page_size, kv_heads, position_dim], qp the
+   * queries' position parts [nq, heads, position_dim]; q and dy keep width
+   * head_dim.  Per visible (row, head, token):
+   *   s  = scale * (q . c + qp . kp),  p = exp(s - m) / l,
+   *   ds = p * (dY . c - delta) * scale,
+   *   dk_pool[slot, g]  (the latent's gradient) += ds * q + p * dY,
+   *   dkp_pool[slot, g] += ds * qp.
+   * need: bit 0 the latent's gradient, bit 2 the position keys' (bit 1 is
+   * invalid).  head_dim in {64, 128}, position_dim in {0, 32, 64}.  The query
+   * side (row statistics, dQ) does not take the latent variant.  mla = 0: the
+   * fields below are ignored. */
+  int32_t mla, position_dim;
+  const void *qp, *kp_pool;              /* device, 16-byte aligned, contiguous */
+  void *dkp_pool;                        /* device [pool_pages * page_size, kv_heads, position_dim] */
 } attn_bwd_paged_args;
 
 /* Enqueues the paged backward.  Every device pointer must be 16-byte aligned;

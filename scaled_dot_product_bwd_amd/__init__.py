@@ -34,7 +34,8 @@ from ._abi import (ATTN_BF16, ATTN_F32, ATTN_MASK_BIAS, ATTN_MASK_CAUSAL,
 
 __all__ = ["attn_bwd", "attn_bwd_stage", "workspace_bytes", "make_args", "AttnError",
            "load_library", "library_path", "MASKS", "WRT", "PagedPlan", "paged_plan",
-           "attn_bwd_paged", "make_paged_args", "paged_row_stats", "attn_bwd_paged_dq"]
+           "attn_bwd_paged", "attn_bwd_paged_mla", "make_paged_args", "paged_row_stats",
+           "attn_bwd_paged_dq"]
 
 MASKS = {"none": ATTN_MASK_NONE, "causal": ATTN_MASK_CAUSAL, "keypad": ATTN_MASK_KEYPAD,
          "window": ATTN_MASK_WINDOW, "bias": ATTN_MASK_BIAS}
@@ -291,6 +292,44 @@ def attn_bwd_paged(q, dy, k_pool, v_pool, stats, plan, *, dk_pool=None, dv_pool=
                            causal=causal, scale=scale, need=n)
     _check(load_library().attn_bwd_paged(ctypes.byref(args), _stream_handle(stream)))
     return dk_pool, dv_pool
+
+
+def attn_bwd_paged_mla(q, qp, dy, latent_pool, kp_pool, stats, plan, *, dlat_pool=None,
+                       dkp_pool=None, need="both", causal=True, scale=None, stream=None):
+    """Latent (MLA) variant of attn_bwd_paged: each slot's latent row is both its
+    key and its value, and a position key adds qp . kp to the score.
+    q, dy: [nq, heads, D]; qp: [nq, heads, P]; latent_pool: [slots, kv_heads, D];
+    kp_pool: [slots, kv_heads, P] (D in {64, 128}, P in {0, 32, 64}).  Writes the
+    latent's gradient (ds q + p dY, summed) into dlat_pool and the position
+    keys' (ds qp) into dkp_pool at the slots of listed pages; pools that are not
+    given are allocated zero-filled.  The default scale is 1/sqrt(D + P).
+    need: "dlat", "dkp" or "both".  Returns (dlat_pool, dkp_pool)."""
+    torch = _torch()
+    n = {"dlat": 1, "dkp": 4, "both": 5}[need] if isinstance(need, str) else int(need)
+    D, P = q.shape[2], qp.shape[2]
+    if P == 0:
+        n &= 1
+    if plan.device_words is None:
+        plan.to(q.device)
+    for t in (q, qp, dy, latent_pool, kp_pool, stats):
+        if not t.is_contiguous():
+            raise ValueError("attn_bwd_paged_mla takes contiguous tensors")
+    if dlat_pool is None and n & 1:
+        dlat_pool = torch.zeros_like(latent_pool)
+    if dkp_pool is None and n & 4:
+        dkp_pool = torch.zeros_like(kp_pool)
+    if scale is None:
+        scale = float(torch.tensor(1.0 / math.sqrt(D + P), dtype=torch.float32))
+    args = make_paged_args(q, dy, latent_pool, latent_pool, stats, plan, dlat_pool, None,
+                           causal=causal, scale=scale, need=n)
+    args.v_pool = None
+    args.mla, args.position_dim = 1, P
+    args.qp = qp.data_ptr() if qp.numel() else None
+    args.kp_pool = kp_pool.data_ptr() if kp_pool.numel() else None
+    if dkp_pool is not None:
+        args.dkp_pool = dkp_pool.data_ptr()
+    _check(load_library().attn_bwd_paged(ctypes.byref(args), _stream_handle(stream)))
+    return dlat_pool, dkp_pool
 
 
 def paged_row_stats(q, dy, k_pool, v_pool, plan, *, causal=True, scale=None, out=None,

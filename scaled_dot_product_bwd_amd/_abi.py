@@ -78,6 +78,9 @@ class AttnBwdPagedArgs(ctypes.Structure):
         ("stats", ctypes.c_void_p),
         ("plan_host", ctypes.c_void_p), ("plan", ctypes.c_void_p),
         ("dk_pool", ctypes.c_void_p), ("dv_pool", ctypes.c_void_p),
+        ("mla", ctypes.c_int32), ("position_dim", ctypes.c_int32),
+        ("qp", ctypes.c_void_p), ("kp_pool", ctypes.c_void_p),
+        ("dkp_pool", ctypes.c_void_p),
     ]
 
 

@@ -319,10 +319,24 @@ int validate_paged(const attn_bwd_paged_args *a, int mode, void *out, attn::Page
   if (!a) return fail(ATTN_E_INVALID, "args is NULL");
   if (a->dtype != ATTN_F32 && a->dtype != ATTN_BF16)
     return fail(ATTN_E_INVALID, "dtype %d is not ATTN_F32 or ATTN_BF16", a->dtype);
-  if (mode == PM_KV && (a->need < 1 || a->need > 3))
+  if (a->mla != 0 && a->mla != 1) return fail(ATTN_E_INVALID, "mla must be 0 or 1");
+  const bool mla = a->mla == 1;
+  if (mla && mode != PM_KV)
+    return fail(ATTN_E_UNSUPPORTED, "the query side does not take the latent variant");
+  if (mode == PM_KV && !mla && (a->need < 1 || a->need > 3))
     return fail(ATTN_E_INVALID, "need %d is not 1, 2 or 3", a->need);
-  if (a->head_dim != 32 && a->head_dim != 64 && a->head_dim != 128)
+  if (mode == PM_KV && mla && (a->need < 1 || a->need > 5 || (a->need & 2)))
+    return fail(ATTN_E_INVALID, "latent variant: need %d is not 1, 4 or 5", a->need);
+  if (mla) {
+    if (a->head_dim != 64 && a->head_dim != 128)
+      return fail(ATTN_E_UNSUPPORTED, "latent width %d is not 64 or 128", a->head_dim);
+    if (a->position_dim != 0 && a->position_dim != 32 && a->position_dim != 64)
+      return fail(ATTN_E_UNSUPPORTED, "position_dim %d is not 0, 32 or 64", a->position_dim);
+    if ((a->need & 4) && a->position_dim == 0)
+      return fail(ATTN_E_INVALID, "need asks for position-key gradients but position_dim is 0");
+  } else if (a->head_dim != 32 && a->head_dim != 64 && a->head_dim != 128) {
     return fail(ATTN_E_UNSUPPORTED, "head_dim %d is not 32, 64 or 128", a->head_dim);
+  }
   if (!std::isfinite(a->scale)) return fail(ATTN_E_INVALID, "scale is not finite");
   if (a->causal != 0 && a->causal != 1) return fail(ATTN_E_INVALID, "causal must be 0 or 1");
   const int32_t *w = a->plan_host;
@@ -347,38 +361,45 @@ int validate_paged(const attn_bwd_paged_args *a, int mode, void *out, attn::Page
   nblocks = (int)((mode == PM_KV ? items : qblocks) * a->kv_heads);
 
   const size_t es = bf16 ? 2 : 4;
-  const int64_t D = a->head_dim;
+  const int64_t D = a->head_dim, P = mla ? a->position_dim : 0;
   const int64_t qrows = (int64_t)a->nq * a->heads;
   const int64_t pslots = (int64_t)a->pool_pages * a->page_size * a->kv_heads;
-  const bool work = nblocks > 0;
+  const bool work = nblocks > 0, kv = mode == PM_KV;
+  constexpr int NT = 11, FIRST_OUT = 8;
   struct T {
     const char *name;
     const void *ptr;
     int64_t bytes;
     bool needed;
-  } ts[8] = {
+  } ts[NT] = {
       {"q", a->q, qrows * D * (int64_t)es, work && qrows > 0},
       {"dy", a->dy, qrows * D * (int64_t)es, work && qrows > 0},
       {"stats", a->stats, qrows * 3 * (int64_t)sizeof(float), work && qrows > 0 && mode != PM_STATS},
       {"k_pool", a->k_pool, pslots * D * (int64_t)es, work},
-      {"v_pool", a->v_pool, pslots * D * (int64_t)es, work},
-      {"dk_pool", a->dk_pool, pslots * D * (int64_t)es, work && mode == PM_KV && (a->need & 1)},
-      {"dv_pool", a->dv_pool, pslots * D * (int64_t)es, work && mode == PM_KV && (a->need & 2)},
-      {mode == PM_STATS ? "stats_out" : "dq", out,
-       qrows * (mode == PM_STATS ? 3 * (int64_t)sizeof(float) : D * (int64_t)es),
-       work && mode != PM_KV},
+      {"v_pool", a->v_pool, pslots * D * (int64_t)es, work && !mla},
+      {"qp", a->qp, qrows * P * (int64_t)es, work && qrows > 0 && P > 0},
+      {"kp_pool", a->kp_pool, pslots * P * (int64_t)es, work && P > 0},
+      {"plan", a->plan, (int64_t)words * 4, work},
+      {"dk_pool", a->dk_pool, pslots * D * (int64_t)es, work && kv && (a->need & 1)},
+      {"dv_pool", a->dv_pool, pslots * D * (int64_t)es, work && kv && !mla && (a->need & 2)},
+      {kv ? "dkp_pool" : (mode == PM_STATS ? "stats_out" : "dq"), kv ? a->dkp_pool : out,
+       kv ? pslots * P * (int64_t)es
+          : qrows * (mode == PM_STATS ? 3 * (int64_t)sizeof(float) : D * (int64_t)es),
+       work && (kv ? mla && (a->need & 4) : true)},
   };
-  Range rng[8];
-  for (int i = 0; i < 8; ++i) {
+  Range rng[NT];
+  for (int i = 0; i < NT; ++i) {
     if (!ts[i].needed) continue;
     if (!ts[i].ptr) return fail(ATTN_E_INVALID, "%s is NULL", ts[i].name);
-    if ((uintptr_t)ts[i].ptr % 16) return fail(ATTN_E_UNSUPPORTED, "%s is not 16-byte aligned", ts[i].name);
+    const unsigned align = i == 7 ? 4 : 16;  // the plan is read as int32 words
+    if ((uintptr_t)ts[i].ptr % align)
+      return fail(ATTN_E_UNSUPPORTED, "%s is not %u-byte aligned", ts[i].name, align);
     rng[i].lo = (uintptr_t)ts[i].ptr;
     rng[i].hi = rng[i].lo + (uintptr_t)ts[i].bytes;
   }
-  for (int i = 5; i < 8; ++i) {  // outputs
+  for (int i = FIRST_OUT; i < NT; ++i) {  // outputs
     if (!ts[i].needed) continue;
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < NT; ++j)
       if (j != i && ts[j].needed && overlap(rng[i], rng[j]))
         return fail(ATTN_E_INVALID, "%s overlaps %s", ts[i].name, ts[j].name);
   }
@@ -386,6 +407,14 @@ int validate_paged(const attn_bwd_paged_args *a, int mode, void *out, attn::Page
   std::memset(&p, 0, sizeof p);
   p.q = a->q; p.dy = a->dy; p.k_pool = a->k_pool; p.v_pool = a->v_pool;
   p.dk_pool = a->dk_pool; p.dv_pool = a->dv_pool;
+  if (mla) {
+    p.mla = 1;
+    p.P = (int)P;
+    p.qp = a->qp;
+    p.kp_pool = a->kp_pool;
+    p.dkp_pool = a->dkp_pool;
+    p.need_dkp = (a->need >> 2) & 1;
+  }
   if (mode == PM_STATS) p.stats_out = (float *)out;
   if (mode == PM_DQ) p.dq = out;
   p.stats = a->stats;
@@ -395,7 +424,7 @@ int validate_paged(const attn_bwd_paged_args *a, int mode, void *out, attn::Page
   p.group = a->heads / a->kv_heads;
   p.causal = a->causal;
   p.need_dk = a->need & 1;
-  p.need_dv = (a->need >> 1) & 1;
+  p.need_dv = mla ? 0 : (a->need >> 1) & 1;
   p.scale = a->scale;
   p.scale_log2 = a->scale * attn::kLog2e;
   p.items = (int)items;

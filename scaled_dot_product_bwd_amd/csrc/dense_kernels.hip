@@ -299,7 +299,7 @@ __device__ __forceinline__ void kv_step(const DenseParams &p, KvState<T, D> &S, 
     }
   };
   const float *stc = st[bc];
-  kv_chunk<T, D, MASKED>(S.kf, S.vf, S.dk, S.dv, &Qs[bc], &Gs[bc], stc, stc + ROWS, p.scale_log2,
+  kv_chunk<T, D, D, MASKED>(S.kf, S.vf, S.dk, S.dv, &Qs[bc], &Gs[bc], stc, stc + ROWS, p.scale_log2,
                          S.lane, adj);
   if (issued) {
     S.io_q.complete(Qs[bn]);

@@ -133,9 +133,18 @@ __device__ __forceinline__ float creuse<float>(const float *v, int st) {
 // different banks.
 template <typename T, int D, int ROWS = 32> struct Tile;
 
+// Row stride in 16-byte slots: the smallest >= D / 8 that is 4 or 12 mod 16
+// (a group's 4 rows then fall in 4 different quarters); group stride: the
+// smallest odd slot count that holds the group (odd: successive groups shift by
+// one 16-byte slot mod 4).  D = 32 / 64 / 128 give 32 / 96 / 160 and
+// 136 / 360 / 616 elements.
+constexpr int tile_rs_slots(int d8) { return (d8 % 16 == 4 || d8 % 16 == 12) ? d8 : tile_rs_slots(d8 + 1); }
+constexpr int tile_g_slots(int need) { return need % 2 ? need : need + 1; }
+
 template <int D, int ROWS> struct Tile<bf16, D, ROWS> {
-  static constexpr int RS = D == 128 ? 160 : (D == 64 ? 96 : 32);   // row stride in a group, elements
-  static constexpr int G = D == 128 ? 616 : (D == 64 ? 360 : 136);  // group stride, elements
+  static_assert(D % 32 == 0, "tile width");
+  static constexpr int RS = 8 * tile_rs_slots(D / 8);               // row stride in a group, elements
+  static constexpr int G = 8 * tile_g_slots((3 * RS + D) / 8);      // group stride, elements
   static constexpr int SLOTS = ROWS / 4 * G / 8;                     // 16-byte slots of all groups
   static constexpr int NSEG = ((SLOTS + 63) / 64 + 3) / 4 * 4;       // 1 KB load segments
   bf16 a[NSEG * 512];
@@ -214,10 +223,11 @@ __device__ __forceinline__ void dma_lds4(void *lds, const void *g) {
                : "memory");
 }
 
-// s_waitcnt vmcnt(n), other counters unconstrained (n < 16).
+// s_waitcnt vmcnt(n), other counters unconstrained (n < 64: the count's low
+// four bits sit in bits 3:0 of the immediate, its high two in bits 15:14).
 template <int N> __device__ __forceinline__ void wait_vmem_le() {
-  static_assert(N >= 0 && N < 16, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 __device__ __forceinline__ void wait_vmem() { wait_vmem_le<0>(); }
 
@@ -268,11 +278,16 @@ template <int D, int ROWS> struct ChunkIO<bf16, D, ROWS> {
   }
   // Rows given by a functor: rowptr(r) is the start of chunk row r (0 <= r < ROWS).
   template <typename F> __device__ __forceinline__ void issue_at(F rowptr, TileT &t) {
+    issue_elem([&](int r, int c) { return rowptr(r) + c; }, t);
+  }
+  // Elements given by a functor: elem(r, c) addresses columns c .. c + 7 of chunk
+  // row r (c a multiple of 8), so a row may be assembled from several sources.
+  template <typename F> __device__ __forceinline__ void issue_elem(F elem, TileT &t) {
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
       int row, col;
       slot_rc(j, row, col);
-      dma_lds16(&t.a[(wave + 4 * j) * 512], rowptr(row) + col);
+      dma_lds16(&t.a[(wave + 4 * j) * 512], elem(row, col));
     }
   }
   // Rows [r0, r0 + ROWS) of a matrix with `stride` (the one given to init) and
@@ -304,12 +319,16 @@ template <int D, int ROWS> struct ChunkIO<float, D, ROWS> {
   static constexpr int PER = (ROWS * CH + 255) / 256;
   f32x4 r[PER];
   __device__ __forceinline__ void init(int64_t) {}
-  template <typename F> __device__ __forceinline__ void issue_at(F rowptr, TileT &) {
+  template <typename F> __device__ __forceinline__ void issue_at(F rowptr, TileT &t) {
+    issue_elem([&](int row, int c) { return rowptr(row) + c; }, t);
+  }
+  // elem(r, c): columns c .. c + 3 of chunk row r (c a multiple of 4).
+  template <typename F> __device__ __forceinline__ void issue_elem(F elem, TileT &) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       const int id = threadIdx.x + 256 * j;
       r[j] = (ROWS * CH % 256 == 0 || id < ROWS * CH)
-                 ? *reinterpret_cast<const f32x4 *>(rowptr(id / CH) + 4 * (id % CH))
+                 ? *reinterpret_cast<const f32x4 *>(elem(id / CH, 4 * (id % CH)))
                  : f32x4{};
     }
   }

@@ -44,19 +44,33 @@ __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0
 // (query row 32 u + kr(r, half) of the chunk, key = this lane's column); only
 // called when MASKED.  nlse2 / delta: the chunk's per-row -lse2 and delta in
 // LDS (row i at [i]).
-template <typename T, int D, bool MASKED, typename Adj>
+//
+// DK is the width of the score's contraction (Q and K rows, dK), DV that of the
+// value side (dY and V rows, dV); DV <= DK.  They differ for a latent key: the
+// score runs over [latent | position key] while the value is the latent alone,
+// so the last (DK - DV) / KS score steps have no dP partner and the last
+// (DK - DV) / 32 dK tiles no dV partner.
+//
+// MERGE (a latent that is both key and value): dS is scaled by ds_scale before
+// it is packed, and P^T dY accumulates into the same tiles as dS^T Q, so dk
+// holds the latent's whole gradient (tiles below DV / 32) and the position
+// key's (the rest); dv is not used.  Phase C then issues all P^T dY products of
+// a 32-row step before its dS^T Q products, so two MFMAs into one tile are
+// never adjacent.
+template <typename T, int DK, int DV, bool MASKED, bool MERGE = false, typename Adj>
 __device__ __forceinline__ void kv_chunk(const typename MT<T>::frag *kf,
                                          const typename MT<T>::frag *vf, f32x16 *dk, f32x16 *dv,
-                                         const Tile<T, D, KvShape<T>::ROWS> *Qc,
-                                         const Tile<T, D, KvShape<T>::ROWS> *Gc,
+                                         const Tile<T, DK, KvShape<T>::ROWS> *Qc,
+                                         const Tile<T, DV, KvShape<T>::ROWS> *Gc,
                                          const float *nlse2, const float *delta, float scale_log2,
-                                         int lane, Adj adj) {
+                                         int lane, Adj adj, float ds_scale = 1.f) {
   typedef MT<T> M;
   typedef typename M::frag F;
-  constexpr int NSD = D / M::KS, NT = D / 32, CS = M::CSTEPS;
+  static_assert(DV <= DK && DV % 32 == 0 && DK % 32 == 0, "widths");
+  constexpr int NSD = DK / M::KS, NSV = DV / M::KS, NT = DK / 32, NTV = DV / 32, CS = M::CSTEPS;
   constexpr int NSUB = KvShape<T>::NSUB;
-  constexpr int NA = NSUB * NSD;    // phase-A steps (two MFMAs each: S and dP)
-  constexpr int NC = NSUB * CS * NT;  // phase-C steps (two MFMAs each: dV and dK)
+  constexpr int NA = NSUB * NSD;    // phase-A steps (S, and dP while s < NSV)
+  constexpr int NC = NSUB * CS * NT;  // phase-C steps (dK, and dV while t < NTV)
   constexpr int RING = 4;
   const int l32 = lane & 31, half = lane >> 5;
 
@@ -84,7 +98,10 @@ __device__ __forceinline__ void kv_chunk(const typename MT<T>::frag *kf,
         t = fmaf(sacc[u][r], scale_log2, nl);
       const float pr = fast_exp2(t);
       pv[u][r] = pr;
-      dsv[u][r] = pr * (pacc[u][r] - dl);
+      if constexpr (MERGE)
+        dsv[u][r] = (pr * ds_scale) * (pacc[u][r] - dl);
+      else
+        dsv[u][r] = pr * (pacc[u][r] - dl);
     }
   };
 
@@ -93,7 +110,7 @@ __device__ __forceinline__ void kv_chunk(const typename MT<T>::frag *kf,
   auto load_a = [&](int a) {
     const int u = a / NSD, s = a % NSD;
     qa[a % RING] = Qc->frag(32 * u + l32, s, half);
-    ga[a % RING] = Gc->frag(32 * u + l32, s, half);
+    if (s < NSV) ga[a % RING] = Gc->frag(32 * u + l32, s, half);
   };
 #pragma unroll
   for (int a = 0; a < RING - 1 && a < NA; ++a) load_a(a);
@@ -103,7 +120,7 @@ __device__ __forceinline__ void kv_chunk(const typename MT<T>::frag *kf,
     sched_fence();
     if (a + RING - 1 < NA) load_a(a + RING - 1);
     sacc[u] = M::mma(qa[a % RING], kf[s], sacc[u]);
-    pacc[u] = M::mma(ga[a % RING], vf[s], pacc[u]);
+    if (s < NSV) pacc[u] = M::mma(ga[a % RING], vf[s], pacc[u]);
     // Sub-tile u - 1 is complete: spread its softmax over this sub-tile's steps.
     if (NSUB > 1 && u >= 1) {
       constexpr int PER = (16 + NSD - 1) / NSD;
@@ -114,13 +131,52 @@ __device__ __forceinline__ void kv_chunk(const typename MT<T>::frag *kf,
   sched_fence();
   if constexpr (NSUB == 1) softmax(0, 0, 16);
 
+  if constexpr (MERGE) {
+    // Phase C, merged: op i of a (u, st) group is P^T dY into tile i for
+    // i < NTV, then dS^T [Q] into tile i - NTV; one transposed fragment each.
+    constexpr int NOP = NTV + NT, NCM = NSUB * CS * NOP;
+    F tf[RING], pf[NSUB][CS], sf[NSUB][CS];
+    auto load_m = [&](int c) {
+      const int u = c / (CS * NOP), st = (c / NOP) % CS, i = c % NOP;
+      tf[c % RING] = i < NTV ? Gc->tfrag(32 * i, st, lane, 32 * u)
+                             : Qc->tfrag(32 * (i - NTV), st, lane, 32 * u);
+    };
+    auto pack_m = [&](int c) {
+      const int u = c / (CS * NOP), st = (c / NOP) % CS;
+      pf[u][st] = creuse<T>(pv[u], st);
+      sf[u][st] = creuse<T>(dsv[u], st);
+    };
+#pragma unroll
+    for (int c = 0; c < RING - 1 && c < NCM; ++c) load_m(c);
+    pack_m(0);
+#pragma unroll
+    for (int c = 0; c < NCM; ++c) {
+      const int u = c / (CS * NOP), st = (c / NOP) % CS, i = c % NOP;
+      sched_fence();
+      if (c + RING - 1 < NCM) load_m(c + RING - 1);
+      if (NSUB > 1 && u == 0) {
+        constexpr int PER = (16 + CS * NOP - 1) / (CS * NOP);
+        const int k = c % (CS * NOP);
+        const int r0 = k * PER, r1 = r0 + PER < 16 ? r0 + PER : 16;
+        if (r0 < 16) softmax(NSUB - 1, r0, r1);
+      }
+      if (c + 1 < NCM && (c + 1) % NOP == 0) pack_m(c + 1);
+      if (i < NTV)
+        dk[i] = M::mma(tf[c % RING], pf[u][st], dk[i]);
+      else
+        dk[i - NTV] = M::mma(tf[c % RING], sf[u][st], dk[i - NTV]);
+    }
+    sched_fence();
+    return;
+  }
+
   // Phase C: dV and dK.  Step c = (u, st, t) reads two transposed fragments;
   // the packed P / dS' operands of a (u, st) are built one step before their
   // first MFMA.
   F ta[RING], tb[RING], pf[NSUB][CS], sf[NSUB][CS];
   auto load_c = [&](int c) {
     const int u = c / (CS * NT), st = (c / NT) % CS, t = c % NT;
-    ta[c % RING] = Gc->tfrag(32 * t, st, lane, 32 * u);
+    if (t < NTV) ta[c % RING] = Gc->tfrag(32 * t, st, lane, 32 * u);
     tb[c % RING] = Qc->tfrag(32 * t, st, lane, 32 * u);
   };
   auto pack = [&](int c) {
@@ -144,7 +200,7 @@ __device__ __forceinline__ void kv_chunk(const typename MT<T>::frag *kf,
       if (r0 < 16) softmax(NSUB - 1, r0, r1);
     }
     if (c + 1 < NC && (c + 1) % NT == 0) pack(c + 1);
-    dv[t] = M::mma(ta[c % RING], pf[u][st], dv[t]);
+    if (t < NTV) dv[t] = M::mma(ta[c % RING], pf[u][st], dv[t]);
     dk[t] = M::mma(tb[c % RING], sf[u][st], dk[t]);
   }
   sched_fence();

@@ -81,6 +81,12 @@ constexpr int kQBlockRows = 128;
 struct PagedParams {
   const void *q, *dy, *k_pool, *v_pool;
   void *dk_pool, *dv_pool;
+  // latent variant: q's position part [nq, heads, P], the position keys
+  // [slots, kv_heads, P] and their gradient; k_pool is the latent, dk_pool its
+  // gradient, v_pool / dv_pool unused
+  const void *qp, *kp_pool;
+  void *dkp_pool;
+  int mla, P, need_dkp;
   float *stats_out;  // query side: statistics written here
   void *dq;          // query side: dQ [nq, heads, D]
   const float *stats;   // [nq, heads, 3] = (max, denominator, delta)

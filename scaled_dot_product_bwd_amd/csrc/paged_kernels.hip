@@ -20,6 +20,16 @@
 // Each (slot, KV head) element is stored exactly once after all links: the
 // gradient, or +0 for a slot no link reaches (tail slots, whose K / V rows are
 // never read).  Slots of pages no sequence lists are never touched.
+//
+// Latent variant (the pages' `mla` switch): a slot holds one latent row c of
+// width D that is both key and value, plus a position key of width P; a query
+// row holds q (width D) and qp (width P).  The score contracts [q | qp] with
+// [c | kp] (width D + P), dP contracts dY with c, and the latent receives both
+// derivatives, d c = scale dS^T q + P^T dY, while the position key gets
+// scale dS^T qp.  The body is the same with key width D + P and value width D:
+// the V fragments are the first D / KS key fragments, dK's last P / 32 tiles
+// are the position-key gradient, and the latent's two parts are summed at the
+// store.
 #include "device_common.hpp"
 #include "kv_core.hpp"
 #include "paged.hpp"
@@ -33,33 +43,40 @@ constexpr int kStatWave = 4 * 64;
 constexpr int kStatWords = 4 * kStatWave;
 constexpr int kRiWords = 4 * 64;
 
-template <typename T, int D> struct PagedState {
+// D: value / latent width; P: position-key width (latent variant only, else 0).
+template <typename T_, int D_, int P_, bool MLA_> struct PagedState {
+  typedef T_ T;
   typedef MT<T> M;
-  static constexpr int NSD = D / M::KS, NT = D / 32, ROWS = KvShape<T>::ROWS;
-  typename M::frag kf[NSD], vf[NSD];
-  f32x16 dk[NT], dv[NT];
-  ChunkIO<T, D, ROWS> io_q, io_g;
-  const T *qbase, *gbase;  // Q / dY at head g * group
-  const float *sbase;      // statistics at head g * group
+  static constexpr int D = D_, P = P_, DK = D_ + P_;
+  static constexpr bool MLA = MLA_;
+  static constexpr int NSD = DK / M::KS, NSV = D / M::KS, NT = DK / 32, NTV = D / 32;
+  static constexpr int ROWS = KvShape<T>::ROWS;
+  typedef Tile<T, DK, ROWS> QTile;  // Q rows (latent variant: [q | qp])
+  typedef Tile<T, D, ROWS> GTile;   // dY rows
+  typename M::frag kf[NSD], vf[MLA ? 1 : NSV];
+  f32x16 dk[NT], dv[MLA ? 1 : NTV];  // latent variant: dk holds both derivatives
+  ChunkIO<T, DK, ROWS> io_q;
+  ChunkIO<T, D, ROWS> io_g;
+  const T *qbase, *qpbase, *gbase;  // Q / qp / dY at head g * group
+  const float *sbase;               // statistics at head g * group
   const int32_t *rh_tab, *pos_tab;  // the link's sequence: qh rows from 0
   int nqh, c_last, tok, maxtok, wave, lane, buf;
 };
 
 // Rowinfo of chunk c into this wave's copy: lane l <- rh of qh row c * ROWS + l
 // (clamped to the last row, so every lane reads inside the plan).
-template <typename T, int D>
-__device__ __forceinline__ void issue_rowinfo(PagedState<T, D> &S, int c, int *ri) {
-  const int qh = min(c * PagedState<T, D>::ROWS + S.lane, S.nqh - 1);
+template <typename St>
+__device__ __forceinline__ void issue_rowinfo(St &S, int c, int *ri) {
+  const int qh = min(c * St::ROWS + S.lane, S.nqh - 1);
   dma_lds4(ri + 64 * S.wave, S.rh_tab + qh);
 }
 
 // Statistics and Q / dY rows of chunk c; `ri` holds the chunk's rowinfo (landed).
-template <typename T, int D>
-__device__ __forceinline__ void issue_chunk(const PagedParams &p, PagedState<T, D> &S, int c,
-                                            const int *ri, float *st,
-                                            Tile<T, D, KvShape<T>::ROWS> *Q,
-                                            Tile<T, D, KvShape<T>::ROWS> *G) {
-  constexpr int ROWS = KvShape<T>::ROWS;
+template <typename St>
+__device__ __forceinline__ void issue_chunk(const PagedParams &p, St &S, int c, const int *ri,
+                                            float *st, typename St::QTile *Q,
+                                            typename St::GTile *G) {
+  constexpr int D = St::D, P = St::P;
   const int *myri = ri + 64 * S.wave;
   float *myst = st + kStatWave * S.wave;
   const int rh = myri[S.lane];
@@ -67,20 +84,29 @@ __device__ __forceinline__ void issue_chunk(const PagedParams &p, PagedState<T, 
   dma_lds4(myst, srow);
   dma_lds4(myst + 64, srow + 1);
   dma_lds4(myst + 128, srow + 2);
-  dma_lds4(myst + 192, S.pos_tab + min(c * ROWS + S.lane, S.nqh - 1));
-  S.io_q.issue_at([&](int r) { return S.qbase + (int64_t)myri[r] * D; }, *Q);
+  dma_lds4(myst + 192, S.pos_tab + min(c * St::ROWS + S.lane, S.nqh - 1));
+  if constexpr (P > 0) {
+    // a row of the tile is [q | qp]: columns below D from q, the rest from qp
+    S.io_q.issue_elem(
+        [&](int r, int col) {
+          return col < D ? S.qbase + (int64_t)myri[r] * D + col
+                         : S.qpbase + (int64_t)myri[r] * P + (col - D);
+        },
+        *Q);
+  } else {
+    S.io_q.issue_at([&](int r) { return S.qbase + (int64_t)myri[r] * D; }, *Q);
+  }
   S.io_g.issue_at([&](int r) { return S.gbase + (int64_t)myri[r] * D; }, *G);
 }
 
 // Replace max by -lse2 in this wave's statistics of chunk c (landed).  Rows past
 // the sequence's last qh row get -lse2 = -inf, so P = 0 for them with or without
 // the per-element test.
-template <typename T, int D>
-__device__ __forceinline__ void convert_stats(PagedState<T, D> &S, int c, float *st) {
-  constexpr int ROWS = KvShape<T>::ROWS;
+template <typename St>
+__device__ __forceinline__ void convert_stats(St &S, int c, float *st) {
   float *myst = st + kStatWave * S.wave;
   const int l = S.lane;
-  const bool real = l < ROWS && c * ROWS + l < S.nqh;
+  const bool real = l < St::ROWS && c * St::ROWS + l < S.nqh;
   const float m = myst[l], den = myst[64 + l];
   myst[l] = (real && den > 0.f) ? -fmaf(m, kLog2e, log2f(den)) : -INFINITY;  // -lse2
 }
@@ -88,14 +114,14 @@ __device__ __forceinline__ void convert_stats(PagedState<T, D> &S, int c, float 
 // One chunk: request rowinfo of chunk c + 4 and the data of chunk c + 2,
 // convert and consume chunk c (MASKED: per-element visibility), hand over.
 // Chunk k's tiles, statistics and rowinfo sit in buffer k % 3 (S.buf = c % 3).
-template <typename T, int D, bool MASKED>
-__device__ __forceinline__ void paged_step(const PagedParams &p, PagedState<T, D> &S, int c,
-                                           Tile<T, D, KvShape<T>::ROWS> *Qs,
-                                           Tile<T, D, KvShape<T>::ROWS> *Gs,
+template <bool MASKED, typename St>
+__device__ __forceinline__ void paged_step(const PagedParams &p, St &S, int c,
+                                           typename St::QTile *Qs, typename St::GTile *Gs,
                                            float (*st)[kStatWords], int (*ri)[kRiWords]) {
-  constexpr int ROWS = KvShape<T>::ROWS;
-  constexpr int PER_CHUNK = 5 + 2 * ChunkIO<T, D, ROWS>::LOADS;
-  static_assert(PER_CHUNK < 16, "vmcnt budget");
+  typedef typename St::T T;
+  constexpr int PER_CHUNK =
+      5 + ChunkIO<T, St::DK, St::ROWS>::LOADS + ChunkIO<T, St::D, St::ROWS>::LOADS;
+  static_assert(PER_CHUNK < 64, "vmcnt budget");
   const int bc = S.buf, bn = bc == 0 ? 2 : bc - 1, bz = bc == 2 ? 0 : bc + 1;
   const bool issued = c + 2 <= S.c_last;
   if (issued) {
@@ -112,13 +138,14 @@ __device__ __forceinline__ void paged_step(const PagedParams &p, PagedState<T, D
     const bool vis = tok >= 0 && (!causal || tok <= posv[32 * u + kr(r, half)]);
     return vis ? 0.f : -INFINITY;
   };
-  kv_chunk<T, D, MASKED>(S.kf, S.vf, S.dk, S.dv, &Qs[bc], &Gs[bc], myst, myst + 128,
-                         p.scale_log2, S.lane, adj);
+  kv_chunk<T, St::DK, St::D, MASKED, St::MLA>(S.kf, St::MLA ? S.kf : S.vf, S.dk, S.dv, &Qs[bc],
+                                              &Gs[bc], myst, myst + 128, p.scale_log2, S.lane,
+                                              adj, p.scale);
   if (issued) {
     S.io_q.complete(Qs[bn]);
     S.io_g.complete(Gs[bn]);
   }
-  if constexpr (ChunkIO<T, D, ROWS>::DIRECT) {
+  if constexpr (ChunkIO<T, St::D, St::ROWS>::DIRECT) {
     if (issued)
       wait_vmem_le<PER_CHUNK>();
     else
@@ -134,10 +161,9 @@ __device__ __forceinline__ void paged_step(const PagedParams &p, PagedState<T, D
 // step k - 4, read at step k - 2).  The link runs the unmasked body when every
 // lane holds a token that every row of the sequence sees; otherwise the masked
 // one.  Each variant has its own loop.
-template <typename T, int D>
-__device__ __forceinline__ void paged_run(const PagedParams &p, PagedState<T, D> &S,
-                                          bool masked, Tile<T, D, KvShape<T>::ROWS> *Qs,
-                                          Tile<T, D, KvShape<T>::ROWS> *Gs,
+template <typename St>
+__device__ __forceinline__ void paged_run(const PagedParams &p, St &S, bool masked,
+                                          typename St::QTile *Qs, typename St::GTile *Gs,
                                           float (*st)[kStatWords], int (*ri)[kRiWords]) {
   const int c_last = S.c_last;
   issue_rowinfo(S, 0, ri[0]);
@@ -157,21 +183,23 @@ __device__ __forceinline__ void paged_run(const PagedParams &p, PagedState<T, D>
   __syncthreads();
   S.buf = 0;
   if (masked) {
-    for (int c = 0; c <= c_last; ++c) paged_step<T, D, true>(p, S, c, Qs, Gs, st, ri);
+    for (int c = 0; c <= c_last; ++c) paged_step<true>(p, S, c, Qs, Gs, st, ri);
   } else {
-    for (int c = 0; c <= c_last; ++c) paged_step<T, D, false>(p, S, c, Qs, Gs, st, ri);
+    for (int c = 0; c <= c_last; ++c) paged_step<false>(p, S, c, Qs, Gs, st, ri);
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, int P, bool MLA>
 __global__ __launch_bounds__(256) void k_paged_kv_bwd(const PagedParams p) {
+  typedef PagedState<T, D, P, MLA> St;
   typedef MT<T> M;
-  constexpr int KS = M::KS, KL = M::KL, NSD = D / KS, NT = D / 32, ROWS = KvShape<T>::ROWS;
-  __shared__ Tile<T, D, ROWS> Qs[3], Gs[3];
+  constexpr int KS = M::KS, KL = M::KL, NSD = St::NSD, NT = St::NT, NTV = St::NTV;
+  __shared__ typename St::QTile Qs[3];
+  __shared__ typename St::GTile Gs[3];
   __shared__ __attribute__((aligned(16))) float st[3][kStatWords];
   __shared__ __attribute__((aligned(16))) int ri[3][kRiWords];
 
-  PagedState<T, D> S;
+  St S;
   S.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   S.lane = threadIdx.x & 63;
   const int l32 = S.lane & 31, half = S.lane >> 5;
@@ -181,20 +209,28 @@ __global__ __launch_bounds__(256) void k_paged_kv_bwd(const PagedParams p) {
 
   const int ent = plan[p.off_item_slots + item * plan::kItemSlots + 32 * S.wave + l32];
   const bool live = ent >= 0 && (ent & 1);
-  const int64_t krow_idx = ((int64_t)(ent >= 0 ? ent >> 1 : 0) * p.kv_heads + g) * D;
-  const T *krow = (const T *)p.k_pool + krow_idx;
-  const T *vrow = (const T *)p.v_pool + krow_idx;
+  const int64_t srow = (int64_t)(ent >= 0 ? ent >> 1 : 0) * p.kv_heads + g;  // pool row
+  const T *krow = (const T *)p.k_pool + srow * D;
+  const T *kprow = (const T *)p.kp_pool + srow * P;
 #pragma unroll
   for (int s = 0; s < NSD; ++s) {
-    S.kf[s] = load_frag<T>(krow, s * KS + half * KL, live);
-    S.vf[s] = load_frag<T>(vrow, s * KS + half * KL, live);
+    const int d0 = s * KS + half * KL;
+    S.kf[s] = d0 < D ? load_frag<T>(krow, d0, live) : load_frag<T>(kprow, d0 - D, live);
+  }
+  if constexpr (!MLA) {
+    const T *vrow = (const T *)p.v_pool + srow * D;
+#pragma unroll
+    for (int s = 0; s < St::NSV; ++s) S.vf[s] = load_frag<T>(vrow, s * KS + half * KL, live);
   }
 #pragma unroll
-  for (int t = 0; t < NT; ++t) S.dk[t] = S.dv[t] = f32x16{};
-  S.io_q.init(D);
+  for (int t = 0; t < NT; ++t) S.dk[t] = f32x16{};
+#pragma unroll
+  for (int t = 0; t < (MLA ? 1 : NTV); ++t) S.dv[t] = f32x16{};
+  S.io_q.init(St::DK);
   S.io_g.init(D);
   const int hg = g * p.group;
   S.qbase = (const T *)p.q + (int64_t)hg * D;
+  S.qpbase = (const T *)p.qp + (int64_t)hg * P;
   S.gbase = (const T *)p.dy + (int64_t)hg * D;
   S.sbase = p.stats + 3 * (int64_t)hg;
 
@@ -211,48 +247,76 @@ __global__ __launch_bounds__(256) void k_paged_kv_bwd(const PagedParams p) {
     S.tok = plan[p.off_link_tok + li * plan::kItemSlots + 32 * S.wave + l32];
     S.rh_tab = plan + p.off_qh_rh + qh0;
     S.pos_tab = plan + p.off_qh_pos + qh0;
-    S.c_last = (S.nqh - 1) / ROWS;
+    S.c_last = (S.nqh - 1) / St::ROWS;
     const bool masked = !(info[plan::LI_ALL_VALID] != 0 &&
                           (!p.causal || plan[p.off_seq_minpos + seq] >= S.maxtok));
-    paged_run<T, D>(p, S, masked, Qs, Gs, st, ri);
+    paged_run(p, S, masked, Qs, Gs, st, ri);
   }
 
   if (ent < 0) return;
-  T *dkrow = (T *)p.dk_pool + krow_idx;
-  T *dvrow = (T *)p.dv_pool + krow_idx;
+  const float sc = live ? p.scale : 0.f;  // dS's factor, applied once; tails store +0
+  if constexpr (MLA) {
+    // dS was scaled before its products: dk holds the latent's gradient (both
+    // derivatives) and then the position key's; tails store +0
+    T *dcrow = (T *)p.dk_pool + srow * D;
+    T *dprow = (T *)p.dkp_pool + srow * P;
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int d0 = 32 * t + 8 * q + 4 * half;
-      const f32x16 &a = S.dk[t], &b = S.dv[t];
-      const float sc = live ? p.scale : 0.f;  // dS's factor, applied once; tails store +0
-      if (p.need_dk)
-        store4<T>(dkrow + d0, sc * a[4 * q], sc * a[4 * q + 1], sc * a[4 * q + 2], sc * a[4 * q + 3]);
-      if (p.need_dv)
-        store4<T>(dvrow + d0, live ? b[4 * q] : 0.f, live ? b[4 * q + 1] : 0.f,
-                  live ? b[4 * q + 2] : 0.f, live ? b[4 * q + 3] : 0.f);
-    }
+      for (int q = 0; q < 4; ++q) {
+        const int d0 = 32 * t + 8 * q + 4 * half;
+        const f32x16 &a = S.dk[t];
+        T *dst = t < NTV ? (p.need_dk ? dcrow + d0 : nullptr) : (p.need_dkp ? dprow + (d0 - D) : nullptr);
+        if (dst)
+          store4<T>(dst, live ? a[4 * q] : 0.f, live ? a[4 * q + 1] : 0.f,
+                    live ? a[4 * q + 2] : 0.f, live ? a[4 * q + 3] : 0.f);
+      }
+  } else {
+    T *dkrow = (T *)p.dk_pool + srow * D;
+    T *dvrow = (T *)p.dv_pool + srow * D;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int d0 = 32 * t + 8 * q + 4 * half;
+        const f32x16 &a = S.dk[t], &b = S.dv[t];
+        if (p.need_dk)
+          store4<T>(dkrow + d0, sc * a[4 * q], sc * a[4 * q + 1], sc * a[4 * q + 2], sc * a[4 * q + 3]);
+        if (p.need_dv)
+          store4<T>(dvrow + d0, live ? b[4 * q] : 0.f, live ? b[4 * q + 1] : 0.f,
+                    live ? b[4 * q + 2] : 0.f, live ? b[4 * q + 3] : 0.f);
+      }
+  }
 }
 
-template <typename T, int D>
+template <typename T, int D, int P, bool MLA>
 static hipError_t launch_t(const PagedParams &p, int nblocks, hipStream_t stream) {
-  hipLaunchKernelGGL((k_paged_kv_bwd<T, D>), dim3(nblocks), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((k_paged_kv_bwd<T, D, P, MLA>), dim3(nblocks), dim3(256), 0, stream, p);
   return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_dtype(int D, const PagedParams &p, int nblocks, hipStream_t stream) {
+  if (!p.mla) {
+    if (D == 32) return launch_t<T, 32, 0, false>(p, nblocks, stream);
+    if (D == 64) return launch_t<T, 64, 0, false>(p, nblocks, stream);
+    if (D == 128) return launch_t<T, 128, 0, false>(p, nblocks, stream);
+    return hipErrorInvalidValue;
+  }
+  // latent variant: latent width 64 or 128, position-key width 0, 32 or 64
+  if (D == 64 && p.P == 0) return launch_t<T, 64, 0, true>(p, nblocks, stream);
+  if (D == 64 && p.P == 32) return launch_t<T, 64, 32, true>(p, nblocks, stream);
+  if (D == 64 && p.P == 64) return launch_t<T, 64, 64, true>(p, nblocks, stream);
+  if (D == 128 && p.P == 0) return launch_t<T, 128, 0, true>(p, nblocks, stream);
+  if (D == 128 && p.P == 32) return launch_t<T, 128, 32, true>(p, nblocks, stream);
+  if (D == 128 && p.P == 64) return launch_t<T, 128, 64, true>(p, nblocks, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_paged(bool bf16_in, int D, const PagedParams &p, int nblocks,
                         hipStream_t stream) {
-  if (bf16_in) {
-    if (D == 32) return launch_t<bf16, 32>(p, nblocks, stream);
-    if (D == 64) return launch_t<bf16, 64>(p, nblocks, stream);
-    if (D == 128) return launch_t<bf16, 128>(p, nblocks, stream);
-  } else {
-    if (D == 32) return launch_t<float, 32>(p, nblocks, stream);
-    if (D == 64) return launch_t<float, 64>(p, nblocks, stream);
-    if (D == 128) return launch_t<float, 128>(p, nblocks, stream);
-  }
-  return hipErrorInvalidValue;
+  return bf16_in ? launch_dtype<bf16>(D, p, nblocks, stream)
+                 : launch_dtype<float>(D, p, nblocks, stream);
 }
 
 }  // namespace attn

@@ -128,8 +128,8 @@ def test_unrequested_outputs_may_be_null():
 # attn_bwd_paged: validation happens on the host before any launch.
 
 def test_paged_args_struct_size():
-    # 9 int32 + float, then 9 pointers
-    assert ctypes.sizeof(_abi.AttnBwdPagedArgs) == 40 + 9 * 8
+    # 9 int32 + float, then 9 pointers, then the latent variant's 2 int32 + 3 pointers
+    assert ctypes.sizeof(_abi.AttnBwdPagedArgs) == 40 + 9 * 8 + 8 + 3 * 8
 
 
 def _paged_plan(heads=4, kv_heads=2):
@@ -183,6 +183,41 @@ def test_paged_rejections(field, value, code, msg):
     plan = _paged_plan()
     rc, err = _paged_rc(_paged_args(plan, **{field: value}))
     assert rc == code and msg in err, (rc, err)
+
+
+_MLA = dict(mla=1, need=5, position_dim=32, v_pool=0, dv_pool=0, qp=(1 << 24) * 9,
+            kp_pool=(1 << 24) * 10, dkp_pool=(1 << 24) * 11)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(mla=2), _abi.ATTN_E_INVALID, "mla"),
+    (dict(_MLA, need=2), _abi.ATTN_E_INVALID, "need"),
+    (dict(_MLA, need=3), _abi.ATTN_E_INVALID, "need"),
+    (dict(_MLA, need=8), _abi.ATTN_E_INVALID, "need"),
+    (dict(_MLA, head_dim=32), _abi.ATTN_E_UNSUPPORTED, "latent width"),
+    (dict(_MLA, position_dim=16), _abi.ATTN_E_UNSUPPORTED, "position_dim"),
+    (dict(_MLA, position_dim=0), _abi.ATTN_E_INVALID, "position_dim is 0"),
+    (dict(_MLA, qp=0), _abi.ATTN_E_INVALID, "qp is NULL"),
+    (dict(_MLA, kp_pool=0), _abi.ATTN_E_INVALID, "kp_pool is NULL"),
+    (dict(_MLA, dkp_pool=0), _abi.ATTN_E_INVALID, "dkp_pool is NULL"),
+    (dict(_MLA, dkp_pool=(1 << 24) * 10), _abi.ATTN_E_INVALID, "overlaps"),
+    (dict(_MLA, dk_pool=(1 << 24) * 9), _abi.ATTN_E_INVALID, "overlaps"),
+    (dict(_MLA, dkp_pool=(1 << 24) * 6), _abi.ATTN_E_INVALID, "overlaps"),  # the plan
+    (dict(_MLA, kp_pool=(1 << 24) * 10 + 8), _abi.ATTN_E_UNSUPPORTED, "aligned"),
+])
+def test_paged_latent_rejections(kw, code, msg):
+    plan = _paged_plan()
+    rc, err = _paged_rc(_paged_args(plan, **kw))
+    assert rc == code and msg in err, (rc, err)
+
+
+def test_paged_query_side_rejects_latent_variant():
+    plan = _paged_plan()
+    lib = sdb.load_library()
+    a = _paged_args(plan, **_MLA)
+    for fn in (lib.attn_bwd_paged_row_stats, lib.attn_bwd_paged_dq):
+        assert fn(ctypes.byref(a), ctypes.c_void_p(1 << 30), None) == _abi.ATTN_E_UNSUPPORTED
+        assert "latent" in lib.attn_bwd_last_error().decode()
 
 
 def test_paged_rejects_foreign_plan():
