@@ -2,7 +2,7 @@
 """Benchmark of the dense attention backward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--mask causal|window]
-    python bench.py --workload paged [--steps K] [--warmup W]
+    python bench.py --workload paged|paged_mla [--steps K] [--warmup W]
 
 Workload: bf16 Q, K, V, dY of shape [B=4, S=2048, H=16, D=128] (N(0,1), seeded,
 already resident in HBM), fp32 accumulation, bf16 dQ, dK, dV, causal mask.  One
@@ -31,6 +31,12 @@ read once, dK / dV written over the listed pages, Q, dY and statistics read
 once) over the kernel time.  The line also times the query side (statistics
 and dQ on the GPU) and gives the whole chain's rate counted like the dense
 metric (10 D flops per visible triple).
+
+--workload paged_mla measures the latent variant of the same kernel on the same
+page tables (16 query heads on one latent KV head of width 128 plus a position
+key of width 64): TFLOP/s over the visible triples (4 (D + P) + 4 D flops each)
+against the MFMA peak, since at 16 query heads per latent row the kernel sits
+far above the HBM ridge.
 """
 from __future__ import annotations
 
@@ -296,12 +302,149 @@ def main_paged(args, torch, sdb, dev):
     print(json.dumps(line), flush=True)
 
 
+def paged_mla_stats_torch(w, dev, scale):
+    """Input synthesis for the latent workload: fp32 (max, denominator, delta)
+    per (row, head) with plain torch float32 ops on the device; the score is
+    scale (q . c + qp . kp) and dP = dY . c (the latent c is key and value)."""
+    import torch
+    heads, kv, ps = w["heads"], w["kv_heads"], w["page_size"]
+    group = heads // kv
+    q, qp, dy = (w[n].to(dev).float() for n in ("q", "qp", "dy"))
+    lat, kpp = w["k_pool"].to(dev), w["kp_pool"].to(dev)
+    stats = torch.zeros(q.shape[0], heads, 3, device=dev)
+    qs, qpos = w["query_seq"].to(dev), w["query_pos"].to(dev)
+    for s, L in enumerate(w["seq_lens"].tolist()):
+        t = torch.arange(L, device=dev)
+        slots = w["block_table"][s].to(dev).long()[t // ps] * ps + t % ps
+        rows = torch.nonzero(qs == s).flatten()
+        C = lat[slots].float().repeat_interleave(group, dim=1).permute(1, 2, 0).contiguous()
+        KP = kpp[slots].float().repeat_interleave(group, dim=1).permute(1, 2, 0).contiguous()
+        sc = (torch.bmm(q[rows].permute(1, 0, 2).contiguous(), C)
+              + torch.bmm(qp[rows].permute(1, 0, 2).contiguous(), KP)) * scale
+        vis = t[None, :] <= qpos[rows][:, None]
+        sc = sc.masked_fill(~vis[None], float("-inf"))
+        m = sc.amax(-1)
+        e = torch.exp(sc - m[..., None])
+        den = e.sum(-1)
+        dp = torch.bmm(dy[rows].permute(1, 0, 2).contiguous(), C)
+        delta = (e / den[..., None] * dp).sum(-1)
+        stats[rows] = torch.stack([m, den, delta], -1).permute(1, 0, 2)
+    return stats
+
+
+def paged_mla_counts(w, plan):
+    """Latent workload: flops per visible (row, head, token) = 2 (D + P) for the
+    score, 2 D for dP, 2 D for P^T dY and 2 (D + P) for dS^T [q | qp]; bytes =
+    latent and position-key history read once, both gradients written over the
+    listed slots, q, qp, dY and the statistics read once."""
+    D, P = w["D"], w["P"]
+    total = 0
+    lens = w["seq_lens"].tolist()
+    for s, p in zip(w["query_seq"].tolist(), w["query_pos"].tolist()):
+        total += min(p + 1, lens[s])
+    flops = (4.0 * (D + P) + 4.0 * D) * w["heads"] * total
+    es = 2
+    row = w["kv_heads"] * (D + P) * es
+    nq, heads = w["q"].shape[:2]
+    nbytes = (int(w["seq_lens"].sum()) * row + len(plan.listed_pages()) * w["page_size"] * row
+              + nq * heads * (2 * D + P) * es + nq * heads * 3 * 4)
+    return flops, nbytes
+
+
+def main_paged_mla(args, torch, sdb, dev):
+    import ctypes
+    import numpy as np
+    import sdpa_inputs
+    log("bench: generating the latent paged workload")
+    w = sdpa_inputs.paged_workload(seed=1005, heads=16, kv_heads=1, D=128, position_dim=64)
+    D, P = w["D"], w["P"]
+    scale = float(torch.tensor(1.0 / (D + P) ** 0.5, dtype=torch.float32))
+    plan = sdb.paged_plan(w["seq_lens"], w["block_table"], w["query_seq"], w["query_pos"],
+                          heads=w["heads"], kv_heads=w["kv_heads"], page_size=w["page_size"],
+                          pool_pages=w["pool_pages"], device=dev)
+    stats = paged_mla_stats_torch(w, dev, scale)
+    q, qp, dy, lat, kpp = (w[n].to(dev) for n in ("q", "qp", "dy", "k_pool", "kp_pool"))
+    dl, dp = torch.zeros_like(lat), torch.zeros_like(kpp)
+    a = sdb.make_paged_args(q, dy, lat, lat, stats, plan, dl, None, causal=True, scale=scale,
+                            need=5)
+    a.v_pool = None
+    a.mla, a.position_dim = 1, P
+    a.qp, a.kp_pool, a.dkp_pool = qp.data_ptr(), kpp.data_ptr(), dp.data_ptr()
+    lib = sdb.load_library()
+
+    def step():
+        rc = lib.attn_bwd_paged(ctypes.byref(a), sdb._stream_handle(None))
+        if rc != 0:
+            raise RuntimeError(lib.attn_bwd_last_error().decode())
+
+    log(f"bench: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    live = w["live_slots"].to(dev)
+    if not all(torch.isfinite(x[live]).all().item() for x in (dl, dp)):
+        raise RuntimeError("non-finite gradients in the benchmark output")
+    flops, nbytes = paged_mla_counts(w, plan)
+    tflops = flops / (ms / 1e3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        log("bench: CPU oracle baseline on 2 sequences")
+        keep = [0, 1]
+        sub = dict(w)
+        sub["seq_lens"], sub["block_table"] = w["seq_lens"][keep], w["block_table"][keep]
+        rows = [r for r, s_ in enumerate(w["query_seq"].tolist()) if s_ in keep]
+        for n in ("query_seq", "query_pos", "q", "qp", "dy"):
+            sub[n] = w[n][rows]
+        kw = dict(heads=w["heads"], kv_heads=w["kv_heads"], page_size=w["page_size"])
+        threads = max(1, min(os.cpu_count() or 1, 16))
+        st = oracle.paged_mla_row_stats(sub, sub["q"], sub["qp"], sub["dy"], w["k_pool"],
+                                        w["kp_pool"], scale=scale, nthreads=threads, **kw)
+        c0 = time.perf_counter()
+        oracle.paged_mla_kv_bwd(sub, sub["q"], sub["qp"], sub["dy"], w["k_pool"], w["kp_pool"],
+                                st, np.zeros(w["k_pool"].shape), np.zeros(w["kp_pool"].shape),
+                                scale=scale, nthreads=threads, **kw)
+        dt = time.perf_counter() - c0
+        sf, _ = paged_mla_counts(sub, plan)
+        cpu = {"value": sf / dt / 1e12, "unit": "TFLOP/s", "cores": min(threads, w["kv_heads"]),
+               "kind": "oracle",
+               "sample": f"2 of {len(w['seq_lens'])} sequences ({int(sub['seq_lens'].sum())} "
+                         f"tokens) of the same workload, float64 C oracle latent/position-key "
+                         f"gradients, {dt:.2f} s wall (the oracle splits work by KV head: one "
+                         f"thread here)"}
+    wl = (f"paged_mla_bwd nseq16 len[256,4096] heads16/1 latent{D}+pos{P} page16 q64/seq bf16 "
+          f"causal (tokens {int(w['seq_lens'].sum())}, pool pages {w['pool_pages']})")
+    line = {
+        "metric": "paged latent (MLA) history bwd (d latent + d pos-key) TFLOP/s",
+        "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl, "counted_flops": flops, "algorithmic_bytes": nbytes,
+                   "items": plan.items},
+        "pct_mfma_peak": round(100.0 * tflops / PEAK_TFLOPS["bf16"], 3),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_TFLOPS["bf16"],
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_TFLOPS["bf16"], 4),
+                     "traffic": stored_traffic("paged", "paged_mla", PAGED_SOURCES),
+                     "kernel": KERNEL_NAMES["paged"], "kernel_ms": round(ms, 4),
+                     "flops_per_launch": flops, "hbm_gbs": round(nbytes / (ms / 1e3) / 1e9, 1)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="dense", choices=["dense", "paged"])
+    ap.add_argument("--workload", default="dense", choices=["dense", "paged", "paged_mla"])
     ap.add_argument("--mask", default="causal", choices=["causal", "window"])
     ap.add_argument("--window", type=int, default=256)
     ap.add_argument("--cpu-heads", type=int, default=16,
@@ -335,6 +478,8 @@ def main():
     sdb.load_library()
     if args.workload == "paged":
         return main_paged(args, torch, sdb, dev)
+    if args.workload == "paged_mla":
+        return main_paged_mla(args, torch, sdb, dev)
     log("bench: generating inputs")
     d = sdpa_inputs.dense_config_inputs(3)
     qc, kc, vc, gc = d["q"], d["k"], d["v"], d["dy"]

@@ -92,7 +92,8 @@ typedef struct attn_bwd_args {
   const float *mask;       /* device fp32, KEYPAD validity or BIAS values; else ignored */
   int64_t mask_stride[4];  /* (b, h, i, j) element strides, 0 = broadcast ([B,Sk] padding: {Sk,0,0,1}) */
   float mask_threshold;    /* KEYPAD: key hidden iff value < threshold */
-  float scale;             /* finite; callers usually pass (float)(1/sqrt(D)) */
+  float scale;             /* finite, |scale| >= 2^-64 (else ATTN_E_UNSUPPORTED); callers
+                              usually pass (float)(1/sqrt(D)) */
   void *workspace;         /* device, >= attn_bwd_workspace_bytes(B, H, Sq) bytes, 256-byte aligned */
   size_t workspace_bytes;
   int64_t Hkv;             /* K / V heads (grouped-query attention); 0 means H.  H must be a
@@ -174,7 +175,7 @@ typedef struct attn_bwd_paged_args {
   int32_t need;       /* bit 0: dK, bit 1: dV (at least one); latent variant: see below */
   int32_t heads, kv_heads, head_dim, page_size, causal; /* head_dim in {32, 64, 128}; causal 0 / 1 */
   int32_t nq, pool_pages;                /* must match the plan */
-  float scale;                           /* finite */
+  float scale;                           /* finite, |scale| >= 2^-64 */
   const void *q, *dy;                    /* device [nq, heads, head_dim], contiguous */
   const void *k_pool, *v_pool;           /* device [pool_pages * page_size, kv_heads, head_dim] */
   const float *stats;                    /* device [nq, heads, 3] = (max, denominator, delta) */

@@ -17,6 +17,10 @@
 #include "launch.hpp"
 #include "paged.hpp"
 
+// The dK / dV kernels start the score accumulators at -lse2 / (scale log2 e),
+// so the scale must have an invertible, normal-range magnitude.
+constexpr float kMinScale = 5.421010862427522e-20f;  // 2^-64
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -88,6 +92,8 @@ int validate(const attn_bwd_args *a, Checked &c) {
   if (a->D != 32 && a->D != 64 && a->D != 128)
     return fail(ATTN_E_UNSUPPORTED, "head_dim %lld is not 32, 64 or 128", (long long)a->D);
   if (!std::isfinite(a->scale)) return fail(ATTN_E_INVALID, "scale is not finite");
+  if (std::fabs(a->scale) < kMinScale)
+    return fail(ATTN_E_UNSUPPORTED, "|scale| below 2^-64 (including 0) is not supported");
   if (a->mask_kind == ATTN_MASK_WINDOW && a->window < 0)
     return fail(ATTN_E_INVALID, "window %lld is negative", (long long)a->window);
   if (a->mask_kind == ATTN_MASK_KEYPAD && std::isnan(a->mask_threshold))
@@ -338,6 +344,8 @@ int validate_paged(const attn_bwd_paged_args *a, int mode, void *out, attn::Page
     return fail(ATTN_E_UNSUPPORTED, "head_dim %d is not 32, 64 or 128", a->head_dim);
   }
   if (!std::isfinite(a->scale)) return fail(ATTN_E_INVALID, "scale is not finite");
+  if (std::fabs(a->scale) < kMinScale)
+    return fail(ATTN_E_UNSUPPORTED, "|scale| below 2^-64 (including 0) is not supported");
   if (a->causal != 0 && a->causal != 1) return fail(ATTN_E_INVALID, "causal must be 0 or 1");
   const int32_t *w = a->plan_host;
   if (!w || !a->plan) return fail(ATTN_E_INVALID, "plan_host / plan is NULL");

@@ -10,7 +10,8 @@
 //   A  S = Q K^T, dP = dY V^T              rows = queries, A operand from LDS
 //   B  P = exp2(S * scale * log2 e - lse2)  lse2 = m log2 e + log2 l, per row
 //      dS' = P (dP - delta)                 (the factor `scale` of dS is applied
-//                                            to dK once, by the caller)
+//                                            to dK once, by the caller; -lse2 and
+//                                            -delta are the accumulators' start)
 //   C  dV^T += dY^T P,  dK^T += Q^T dS'     A read transposed from LDS, B = C reuse
 //
 // Schedule.  With one wave per SIMD nothing hides latency but the wave's own
@@ -76,32 +77,43 @@ __device__ __forceinline__ void kv_chunk(const typename MT<T>::frag *kf,
 
   f32x16 sacc[NSUB], pacc[NSUB];
   float pv[NSUB][16], dsv[NSUB][16];
-  f32x4 nl4, dl4;  // statistics of the 4 rows of the current element group
+
+  // The row statistics enter through the accumulators' initial values: S
+  // starts at -lse2 / (scale log2 e) and dP at -delta, so after phase A
+  // sacc * scale_log2 is the log2-domain exponent and pacc is dP - delta.
+  // Elements 4g .. 4g + 3 of a lane are rows 8g + 4 half + 0..3: one vector
+  // read per group and statistic, once per sub-tile and before its first MFMA
+  // (no LDS read, hence no wait on the operand prefetch, inside phase B).
+  const float inv_sl2 = 1.f / scale_log2;
+  auto init_acc = [&](int u) {
 #pragma unroll
-  for (int u = 0; u < NSUB; ++u) sacc[u] = pacc[u] = f32x16{};
+    for (int g = 0; g < 4; ++g) {
+      const int rb = 32 * u + 8 * g + 4 * half;
+      const f32x4 nl4 = *reinterpret_cast<const f32x4 *>(&nlse2[rb]);
+      const f32x4 dl4 = *reinterpret_cast<const f32x4 *>(&delta[rb]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sacc[u][4 * g + i] = nl4[i] * inv_sl2;
+        pacc[u][4 * g + i] = -dl4[i];
+      }
+    }
+  };
 
   // Phase B for elements [r0, r1) of sub-tile u (needs sacc[u] / pacc[u] done).
-  // Elements 4g .. 4g + 3 are rows 8g + 4 half + 0..3: one vector read each.
   auto softmax = [&](int u, int r0, int r1) {
 #pragma unroll
     for (int r = r0; r < r1; ++r) {
-      if (r % 4 == 0 || r == r0) {
-        const int rb = 32 * u + 8 * (r / 4) + 4 * half;
-        nl4 = *reinterpret_cast<const f32x4 *>(&nlse2[rb]);
-        dl4 = *reinterpret_cast<const f32x4 *>(&delta[rb]);
-      }
-      const float nl = nl4[r % 4], dl = dl4[r % 4];
       float t;
       if constexpr (MASKED)
-        t = fmaf(sacc[u][r], scale_log2, nl + adj(u, r));
+        t = fmaf(sacc[u][r], scale_log2, adj(u, r));
       else
-        t = fmaf(sacc[u][r], scale_log2, nl);
+        t = sacc[u][r] * scale_log2;
       const float pr = fast_exp2(t);
       pv[u][r] = pr;
       if constexpr (MERGE)
-        dsv[u][r] = (pr * ds_scale) * (pacc[u][r] - dl);
+        dsv[u][r] = (pr * ds_scale) * pacc[u][r];
       else
-        dsv[u][r] = pr * (pacc[u][r] - dl);
+        dsv[u][r] = pr * pacc[u][r];
     }
   };
 
@@ -112,6 +124,7 @@ __device__ __forceinline__ void kv_chunk(const typename MT<T>::frag *kf,
     qa[a % RING] = Qc->frag(32 * u + l32, s, half);
     if (s < NSV) ga[a % RING] = Gc->frag(32 * u + l32, s, half);
   };
+  init_acc(0);
 #pragma unroll
   for (int a = 0; a < RING - 1 && a < NA; ++a) load_a(a);
 #pragma unroll
@@ -119,6 +132,8 @@ __device__ __forceinline__ void kv_chunk(const typename MT<T>::frag *kf,
     const int u = a / NSD, s = a % NSD;
     sched_fence();
     if (a + RING - 1 < NA) load_a(a + RING - 1);
+    // the next sub-tile's statistics, two steps before its first MFMA
+    if (u + 1 < NSUB && s == NSD - 2) init_acc(u + 1);
     sacc[u] = M::mma(qa[a % RING], kf[s], sacc[u]);
     if (s < NSV) pacc[u] = M::mma(ga[a % RING], vf[s], pacc[u]);
     // Sub-tile u - 1 is complete: spread its softmax over this sub-tile's steps.

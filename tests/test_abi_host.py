@@ -85,6 +85,8 @@ def _rc(a):
     ("workspace", 0, _abi.ATTN_E_WORKSPACE),
     ("workspace_bytes", 100, _abi.ATTN_E_WORKSPACE),
     ("scale", float("inf"), _abi.ATTN_E_INVALID),
+    ("scale", 0.0, _abi.ATTN_E_UNSUPPORTED),
+    ("scale", -1e-30, _abi.ATTN_E_UNSUPPORTED),
     ("mask_flags", 1, _abi.ATTN_E_INVALID),   # the causal flag needs KEYPAD or BIAS
 ])
 def test_validation_rejects(field, value, code):
@@ -178,6 +180,7 @@ def _paged_rc(a):
     ("dk_pool", 0, _abi.ATTN_E_INVALID, "dk_pool is NULL"),
     ("dv_pool", (1 << 24) * 3, _abi.ATTN_E_INVALID, "overlaps"),
     ("scale", float("inf"), _abi.ATTN_E_INVALID, "scale"),
+    ("scale", 0.0, _abi.ATTN_E_UNSUPPORTED, "scale"),
 ])
 def test_paged_rejections(field, value, code, msg):
     plan = _paged_plan()
