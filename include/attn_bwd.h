@@ -104,7 +104,7 @@ typedef struct attn_bwd_args {
 /* Bytes of device workspace attn_bwd needs: four fp32 planes of B*H*Sq row
  * statistics, each padded to 256 bytes.  Plane 0 = row max m of the scaled
  * scores, plane 1 = denominator l = sum exp(s - m), plane 2 = delta =
- * rowsum(P * dP), plane 3 = internal (negated log2-domain log-sum-exp).  Row (b, h, i)
+ * rowsum(P * dP), plane 3 = internal (-lse / scale, lse = m + ln l).  Row (b, h, i)
  * sits at index (b * H + h) * Sq + i.  An empty row holds m = -inf, l = 0,
  * delta = 0.  Returns 0 for negative sizes. */
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq);

@@ -208,6 +208,7 @@ int validate(const attn_bwd_args *a, Checked &c) {
   p.thr = a->mask_threshold;
   p.scale = a->scale;
   p.scale_log2 = a->scale * attn::kLog2e;
+  p.inv_scale_log2 = 1.f / p.scale_log2;
   p.B = (int)a->B; p.H = (int)a->H; p.Sq = (int)a->Sq; p.Sk = (int)a->Sk;
   p.Hkv = (int)Hkv;
   p.G = Hkv > 0 ? (int)(a->H / Hkv) : 1;
@@ -230,7 +231,7 @@ int validate(const attn_bwd_args *a, Checked &c) {
   p.st_m = (float *)ws;
   p.st_l = (float *)(ws ? ws + pb : nullptr);
   p.st_delta = (float *)(ws ? ws + 2 * pb : nullptr);
-  p.st_lse2 = (float *)(ws ? ws + 3 * pb : nullptr);
+  p.st_nls = (float *)(ws ? ws + 3 * pb : nullptr);
   c.mode = a->mask_kind == ATTN_MASK_KEYPAD ? attn::MODE_KEYPAD
            : a->mask_kind == ATTN_MASK_BIAS ? attn::MODE_BIAS
                                             : attn::MODE_INDEX;
@@ -435,6 +436,7 @@ int validate_paged(const attn_bwd_paged_args *a, int mode, void *out, attn::Page
   p.need_dv = mla ? 0 : (a->need >> 1) & 1;
   p.scale = a->scale;
   p.scale_log2 = a->scale * attn::kLog2e;
+  p.inv_scale_log2 = 1.f / p.scale_log2;
   p.items = (int)items;
   p.off_item_links = w[W_OFF_ITEM_LINKS];
   p.off_item_slots = w[W_OFF_ITEM_SLOTS];

@@ -218,7 +218,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
       p.st_m[row] = empty ? -INFINITY : S.m[q] * kLn2;
       p.st_l[row] = empty ? 0.f : l_tot;
       p.st_delta[row] = empty ? 0.f : d_tot / l_tot;
-      p.st_lse2[row] = empty ? -INFINITY : -(S.m[q] + __log2f(l_tot));  // -lse2
+      p.st_nls[row] = (empty ? -INFINITY : -(S.m[q] + __log2f(l_tot))) * p.inv_scale_log2;
     }
   }
 }
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 // dK / dV, KV-block-major.  A step covers ROWS = 32 * NSUB queries as NSUB
 // independent 32-row sub-tiles (kv_core.hpp).
 
-// Statistics of the ROWS rows of chunk i0 into LDS, [-lse2 x ROWS | delta x ROWS]
+// Statistics of the ROWS rows of chunk i0 into LDS, [-lse2 / scale_log2 x ROWS | delta x ROWS]
 // per wave copy: direct-to-LDS dword loads, each wave writing its own copy so
 // that every wave issues the same number of loads (STAT_LOADS).  Rows past Sq
 // repeat the last row; the index mask gives them P = 0.
@@ -237,10 +237,10 @@ __device__ __forceinline__ void issue_row_stats(const DenseParams &p, int64_t sr
   float *dst = st + 2 * ROWS * wave;
   if constexpr (ROWS == 32) {
     const int row = min(i0 + (lane & 31), p.Sq - 1);
-    dma_lds4(dst, (lane < 32 ? p.st_lse2 : p.st_delta) + srow0 + row);
+    dma_lds4(dst, (lane < 32 ? p.st_nls : p.st_delta) + srow0 + row);
   } else {
     const int row = min(i0 + lane, p.Sq - 1);
-    dma_lds4(dst, p.st_lse2 + srow0 + row);
+    dma_lds4(dst, p.st_nls + srow0 + row);
     dma_lds4(dst + 64, p.st_delta + srow0 + row);
   }
 }
@@ -299,7 +299,7 @@ __device__ __forceinline__ void kv_step(const DenseParams &p, KvState<T, D> &S, 
     }
   };
   const float *stc = st[bc];
-  kv_chunk<T, D, D, MASKED>(S.kf, S.vf, S.dk, S.dv, &Qs[bc], &Gs[bc], stc, stc + ROWS, p.scale_log2,
+  kv_chunk<T, D, D, MASKED, false, true>(S.kf, S.vf, S.dk, S.dv, &Qs[bc], &Gs[bc], stc, stc + ROWS, p.scale_log2,
                          S.lane, adj);
   if (issued) {
     S.io_q.complete(Qs[bn]);
@@ -384,7 +384,7 @@ __global__ __launch_bounds__(256) void k_kv_bwd(const DenseParams p) {
 #pragma unroll
   for (int s = 0; s < NSD; ++s) {
     S.kf[s] = load_frag<T>(krow, s * KS + half * KL, kvalid);
-    S.vf[s] = load_frag<T>(vrow, s * KS + half * KL, kvalid);
+    S.vf[s] = neg_frag<T>(load_frag<T>(vrow, s * KS + half * KL, kvalid));  // -V
   }
 
   S.qbase = (const T *)p.q + b * p.qs[0] + S.h0 * p.qs[2];
@@ -518,7 +518,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       S.gf[q][s] = load_frag<T>(grow, s * KS + half * KL, qvalid);
     }
     const int64_t srow = ((int64_t)b * p.H + h) * p.Sq + (qvalid ? qi : 0);
-    S.nlse[q] = qvalid ? p.st_lse2[srow] : -INFINITY;
+    S.nlse[q] = qvalid ? p.st_nls[srow] * p.scale_log2 : -INFINITY;  // -lse2
     S.del[q] = qvalid ? p.st_delta[srow] : 0.f;
 #pragma unroll
     for (int t = 0; t < NT; ++t) S.dq[q][t] = f32x16{};

@@ -49,6 +49,7 @@ struct DenseParams {
   float thr;
   float scale;       // natural scale, multiplies dS
   float scale_log2;  // scale * log2(e), turns Q.K into a log2-domain score
+  float inv_scale_log2;  // 1 / scale_log2
   int B, H, Sq, Sk;
   int Hkv, G;  // K / V heads and the query heads per K / V head (H = Hkv * G)
   // Index rule: key j is visible to query i iff lo_off <= j - i <= hi_off
@@ -57,7 +58,10 @@ struct DenseParams {
   int lo_off, hi_off;
   int need_dk, need_dv;
   int nblk;  // tiles along the blocked sequence axis
-  float *st_m, *st_l, *st_delta, *st_lse2;  // [B * H * Sq] each; st_lse2 holds -lse2
+  // [B * H * Sq] each.  st_nls = -lse2 / scale_log2 = -(m + ln l) / scale
+  // (-inf / scale for a row that sees nothing), so that st_nls * scale_log2 is
+  // the log2-domain offset of the row's probabilities.
+  float *st_m, *st_l, *st_delta, *st_nls;
 };
 
 __device__ __forceinline__ int kr(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
@@ -96,6 +100,14 @@ template <>
 __device__ __forceinline__ float load_frag<float>(const float *row, int d0, bool valid) {
   return valid ? row[d0] : 0.f;
 }
+
+// -f (a sign flip per element).
+template <typename T> __device__ __forceinline__ typename MT<T>::frag neg_frag(typename MT<T>::frag f);
+template <> __device__ __forceinline__ bf16x8 neg_frag<bf16>(bf16x8 f) {
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  return __builtin_bit_cast(bf16x8, __builtin_bit_cast(s16x8, f) ^ (short)0x8000);
+}
+template <> __device__ __forceinline__ float neg_frag<float>(float f) { return -f; }
 
 // Pack C-tile values as a C-reuse B operand for step `st` (see header).
 template <typename T>

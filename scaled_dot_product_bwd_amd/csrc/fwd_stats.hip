@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256) void k_fwd_stats(const DenseParams p, const fl
     const float L = lse[r];
     const bool empty = !(L > -INFINITY);  // a row that sees no key: P = 0, delta = 0
     p.st_delta[r] = empty ? 0.f : s;
-    p.st_lse2[r] = empty ? -INFINITY : -L * kLog2e;
+    p.st_nls[r] = (empty ? -INFINITY : -L * kLog2e) * p.inv_scale_log2;
   }
 }
 

@@ -43,8 +43,9 @@ __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0
 
 // adj(u, r): log2-domain term added to the score of element r of sub-tile u
 // (query row 32 u + kr(r, half) of the chunk, key = this lane's column); only
-// called when MASKED.  nlse2 / delta: the chunk's per-row -lse2 and delta in
-// LDS (row i at [i]).
+// called when MASKED.  nls / dst: the chunk's per-row statistics in LDS (row i
+// at [i]): nls = -lse2 / scale_log2, and dst = delta when the caller's V
+// fragments are negated (NEGV), else -delta.
 //
 // DK is the width of the score's contraction (Q and K rows, dK), DV that of the
 // value side (dY and V rows, dV); DV <= DK.  They differ for a latent key: the
@@ -58,12 +59,12 @@ __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0
 // key's (the rest); dv is not used.  Phase C then issues all P^T dY products of
 // a 32-row step before its dS^T Q products, so two MFMAs into one tile are
 // never adjacent.
-template <typename T, int DK, int DV, bool MASKED, bool MERGE = false, typename Adj>
+template <typename T, int DK, int DV, bool MASKED, bool MERGE, bool NEGV, typename Adj>
 __device__ __forceinline__ void kv_chunk(const typename MT<T>::frag *kf,
                                          const typename MT<T>::frag *vf, f32x16 *dk, f32x16 *dv,
                                          const Tile<T, DK, KvShape<T>::ROWS> *Qc,
                                          const Tile<T, DV, KvShape<T>::ROWS> *Gc,
-                                         const float *nlse2, const float *delta, float scale_log2,
+                                         const float *nls, const float *dst, float scale_log2,
                                          int lane, Adj adj, float ds_scale = 1.f) {
   typedef MT<T> M;
   typedef typename M::frag F;
@@ -79,22 +80,23 @@ __device__ __forceinline__ void kv_chunk(const typename MT<T>::frag *kf,
   float pv[NSUB][16], dsv[NSUB][16];
 
   // The row statistics enter through the accumulators' initial values: S
-  // starts at -lse2 / (scale log2 e) and dP at -delta, so after phase A
-  // sacc * scale_log2 is the log2-domain exponent and pacc is dP - delta.
-  // Elements 4g .. 4g + 3 of a lane are rows 8g + 4 half + 0..3: one vector
-  // read per group and statistic, once per sub-tile and before its first MFMA
-  // (no LDS read, hence no wait on the operand prefetch, inside phase B).
-  const float inv_sl2 = 1.f / scale_log2;
+  // starts at -lse2 / scale_log2 and dP at -delta (or, with negated V
+  // fragments, the accumulator runs delta - dP), so after phase A
+  // sacc * scale_log2 is the log2-domain exponent and pacc is +-(dP - delta).
+  // Elements 4g .. 4g + 3 of a lane are rows 8g + 4 half + 0..3: plain vector
+  // loads into the accumulators, once per sub-tile and a few steps before its
+  // first MFMA (no LDS read, hence no wait on the operand prefetch, inside
+  // phase B).
   auto init_acc = [&](int u) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int rb = 32 * u + 8 * g + 4 * half;
-      const f32x4 nl4 = *reinterpret_cast<const f32x4 *>(&nlse2[rb]);
-      const f32x4 dl4 = *reinterpret_cast<const f32x4 *>(&delta[rb]);
+      const f32x4 nl4 = *reinterpret_cast<const f32x4 *>(&nls[rb]);
+      const f32x4 dl4 = *reinterpret_cast<const f32x4 *>(&dst[rb]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sacc[u][4 * g + i] = nl4[i] * inv_sl2;
-        pacc[u][4 * g + i] = -dl4[i];
+        sacc[u][4 * g + i] = nl4[i];
+        pacc[u][4 * g + i] = dl4[i];
       }
     }
   };
@@ -110,10 +112,11 @@ __device__ __forceinline__ void kv_chunk(const typename MT<T>::frag *kf,
         t = sacc[u][r] * scale_log2;
       const float pr = fast_exp2(t);
       pv[u][r] = pr;
+      const float pd = NEGV ? -pacc[u][r] : pacc[u][r];  // dP - delta
       if constexpr (MERGE)
-        dsv[u][r] = (pr * ds_scale) * pacc[u][r];
+        dsv[u][r] = (pr * ds_scale) * pd;
       else
-        dsv[u][r] = pr * pacc[u][r];
+        dsv[u][r] = pr * pd;
     }
   };
 

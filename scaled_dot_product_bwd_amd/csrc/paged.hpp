@@ -93,7 +93,7 @@ struct PagedParams {
   const int32_t *plan;  // device copy of the plan words
   int heads, kv_heads, group;
   int causal, need_dk, need_dv;
-  float scale, scale_log2;
+  float scale, scale_log2, inv_scale_log2;
   int items;
   int off_item_links, off_item_slots, off_link_seq, off_link_info, off_link_tok;
   int off_seq_qh, off_qh_rh, off_qh_pos, off_seq_maxpos, off_seq_minpos;

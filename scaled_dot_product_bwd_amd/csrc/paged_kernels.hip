@@ -99,16 +99,18 @@ __device__ __forceinline__ void issue_chunk(const PagedParams &p, St &S, int c, 
   S.io_g.issue_at([&](int r) { return S.gbase + (int64_t)myri[r] * D; }, *G);
 }
 
-// Replace max by -lse2 in this wave's statistics of chunk c (landed).  Rows past
-// the sequence's last qh row get -lse2 = -inf, so P = 0 for them with or without
-// the per-element test.
+// Replace max by -lse2 / scale_log2 in this wave's statistics of chunk c
+// (landed): the kv body's starting score.  Rows past the sequence's last qh
+// row get -inf, so P = 0 for them with or without the per-element test.  The
+// latent variant, whose V fragments are not negated, also negates delta.
 template <typename St>
-__device__ __forceinline__ void convert_stats(St &S, int c, float *st) {
+__device__ __forceinline__ void convert_stats(const PagedParams &p, St &S, int c, float *st) {
   float *myst = st + kStatWave * S.wave;
   const int l = S.lane;
   const bool real = l < St::ROWS && c * St::ROWS + l < S.nqh;
   const float m = myst[l], den = myst[64 + l];
-  myst[l] = (real && den > 0.f) ? -fmaf(m, kLog2e, log2f(den)) : -INFINITY;  // -lse2
+  myst[l] = ((real && den > 0.f) ? -fmaf(m, kLog2e, log2f(den)) : -INFINITY) * p.inv_scale_log2;
+  if constexpr (St::MLA) myst[128 + l] = -myst[128 + l];
 }
 
 // One chunk: request rowinfo of chunk c + 4 and the data of chunk c + 2,
@@ -128,7 +130,7 @@ __device__ __forceinline__ void paged_step(const PagedParams &p, St &S, int c,
     issue_rowinfo(S, c + 4, ri[bz]);  // always issued with the chunk: fixed count per step
     issue_chunk(p, S, c + 2, ri[bn], st[bn], &Qs[bn], &Gs[bn]);
   }
-  convert_stats(S, c, st[bc]);
+  convert_stats(p, S, c, st[bc]);
   const float *myst = st[bc] + kStatWave * S.wave;
   const int *posv = reinterpret_cast<const int *>(myst + 192);
   const int tok = S.tok, half = S.lane >> 5;
@@ -138,7 +140,7 @@ __device__ __forceinline__ void paged_step(const PagedParams &p, St &S, int c,
     const bool vis = tok >= 0 && (!causal || tok <= posv[32 * u + kr(r, half)]);
     return vis ? 0.f : -INFINITY;
   };
-  kv_chunk<T, St::DK, St::D, MASKED, St::MLA>(S.kf, St::MLA ? S.kf : S.vf, S.dk, S.dv, &Qs[bc],
+  kv_chunk<T, St::DK, St::D, MASKED, St::MLA, !St::MLA>(S.kf, St::MLA ? S.kf : S.vf, S.dk, S.dv, &Qs[bc],
                                               &Gs[bc], myst, myst + 128, p.scale_log2, S.lane,
                                               adj, p.scale);
   if (issued) {
@@ -220,7 +222,8 @@ __global__ __launch_bounds__(256) void k_paged_kv_bwd(const PagedParams p) {
   if constexpr (!MLA) {
     const T *vrow = (const T *)p.v_pool + srow * D;
 #pragma unroll
-    for (int s = 0; s < St::NSV; ++s) S.vf[s] = load_frag<T>(vrow, s * KS + half * KL, live);
+    for (int s = 0; s < St::NSV; ++s)
+      S.vf[s] = neg_frag<T>(load_frag<T>(vrow, s * KS + half * KL, live));  // -V
   }
 #pragma unroll
   for (int t = 0; t < NT; ++t) S.dk[t] = f32x16{};
