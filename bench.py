@@ -130,6 +130,23 @@ def cpu_baseline(q, k, v, dy, mask, window, nheads):
                       f"oracle, {dt:.2f} s wall on {threads} threads"}
 
 
+def preheat(step, torch, seconds):
+    """Untimed steps for a fixed wall time before the warmup steps.  Measured on
+    this part: the first ~60 back-to-back steps of the dense workload run up to
+    ~40% slower while the clocks ramp (652 us for steps 0-19, 470 us from step
+    ~60 on, flat over 600 steps), so a few warmup steps alone time the ramp.
+    Returns (steps run, seconds) for the JSON line."""
+    import time as _t
+    t0 = _t.perf_counter()
+    n = 0
+    while _t.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            step()
+        n += 10
+        torch.cuda.synchronize()
+    return n, _t.perf_counter() - t0
+
+
 def counted_flops(B, H, Sq, Sk, D, mask, window):
     if mask == "causal":
         return 10.0 * B * H * Sq * Sk * D / 2
@@ -239,7 +256,8 @@ def main_paged(args, torch, sdb, dev):
         if rc != 0:
             raise RuntimeError(lib.attn_bwd_last_error().decode())
 
-    log(f"bench: warmup {args.warmup}")
+    ph_steps, ph_s = preheat(step, torch, args.preheat)
+    log(f"bench: preheat {ph_steps} steps ({ph_s:.3f} s), warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -285,7 +303,7 @@ def main_paged(args, torch, sdb, dev):
     line = {
         "metric": "paged GQA history bwd (dK+dV) TFLOP/s & HBM GB/s",
         "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "warmup": args.warmup, "preheat": {"steps": ph_steps, "s": round(ph_s, 3)}, "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl, "counted_flops": flops, "algorithmic_bytes": nbytes,
                    "items": plan.items},
@@ -377,7 +395,8 @@ def main_paged_mla(args, torch, sdb, dev):
         if rc != 0:
             raise RuntimeError(lib.attn_bwd_last_error().decode())
 
-    log(f"bench: warmup {args.warmup}")
+    ph_steps, ph_s = preheat(step, torch, args.preheat)
+    log(f"bench: preheat {ph_steps} steps ({ph_s:.3f} s), warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -424,7 +443,7 @@ def main_paged_mla(args, torch, sdb, dev):
     line = {
         "metric": "paged latent (MLA) history bwd (d latent + d pos-key) TFLOP/s",
         "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "warmup": args.warmup, "preheat": {"steps": ph_steps, "s": round(ph_s, 3)}, "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl, "counted_flops": flops, "algorithmic_bytes": nbytes,
                    "items": plan.items},
@@ -450,6 +469,8 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=16,
                     help="(b,h) heads the CPU oracle baseline processes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--preheat", type=float, default=0.1,
+                    help="seconds of untimed steps before the warmup steps (clock ramp)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB (for HBM counter scaling)")
     args = ap.parse_args()
@@ -499,7 +520,8 @@ def main():
         if ev is not None:
             ev[len(stages)].record()
 
-    log(f"bench: warmup {args.warmup}")
+    ph_steps, ph_s = preheat(step, torch, args.preheat)
+    log(f"bench: preheat {ph_steps} steps ({ph_s:.3f} s), warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -571,7 +593,7 @@ def main():
     line = {
         "metric": "attn-bwd TFLOP/s (dQ+dK+dV) & % MFMA peak, B4 H16 S2048 D128 bf16 causal",
         "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "warmup": args.warmup, "preheat": {"steps": ph_steps, "s": round(ph_s, 3)}, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl, "B": B, "H": H, "Sq": S, "Sk": S, "D": D, "mask": args.mask,
                    "window": window if args.mask == "window" else None, "layout": "BSHD",

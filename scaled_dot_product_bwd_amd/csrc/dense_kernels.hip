@@ -171,10 +171,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   S.half = S.lane >> 5;
   const int l32 = S.lane & 31, half = S.half;
   const int nb = p.nblk;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int blk = nb - 1 - (L % nb);  // the heaviest causal blocks first
-  S.h = (L / nb) % p.H;
-  S.b = L / (nb * p.H);
+  int bh, rank;
+  tile_order(blockIdx.x, gridDim.x, nb, bh, rank);
+  const int blk = nb - 1 - rank;  // the heaviest causal blocks first
+  S.h = bh % p.H;
+  S.b = bh / p.H;
   const int b = S.b, h = S.h;
   const int i0 = blk * QROWS;
 #pragma unroll
@@ -368,10 +369,10 @@ __global__ __launch_bounds__(256) void k_kv_bwd(const DenseParams p) {
   S.l32 = S.lane & 31;
   S.half = S.lane >> 5;
   const int nb = p.nblk;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int blk = L % nb;  // key block 0 sees the most queries under a causal mask
-  const int g = (L / nb) % p.Hkv;  // the K / V head; its query heads are g * G ... g * G + G - 1
-  S.b = L / (nb * p.Hkv);
+  int bg, blk;  // key block 0 sees the most queries under a causal mask: rank = block
+  tile_order(blockIdx.x, gridDim.x, nb, bg, blk);
+  const int g = bg % p.Hkv;  // the K / V head; its query heads are g * G ... g * G + G - 1
+  S.b = bg / p.Hkv;
   S.h0 = g * p.G;
   const int j0b = blk * 128;
   S.jw = j0b + 32 * w;
@@ -499,10 +500,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   S.half = S.lane >> 5;
   const int l32 = S.lane & 31, half = S.half;
   const int nb = p.nblk;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int blk = nb - 1 - (L % nb);
-  S.h = (L / nb) % p.H;
-  S.b = L / (nb * p.H);
+  int bh, rank;
+  tile_order(blockIdx.x, gridDim.x, nb, bh, rank);
+  const int blk = nb - 1 - rank;
+  S.h = bh % p.H;
+  S.b = bh / p.H;
   const int b = S.b, h = S.h;
   const int i0 = blk * QROWS;
 #pragma unroll

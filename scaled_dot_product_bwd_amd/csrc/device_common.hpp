@@ -374,6 +374,26 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   return x * per + (x < rem ? x : rem) + idx;
 }
 
+// Workgroup id -> (head, rank) for a grid of n = heads * nb tiles, nb per head.
+// Every XCD gets a contiguous range of heads (their tiles share its L2), and
+// when the heads split evenly over the 8 XCDs an XCD runs its tiles rank by
+// rank: rank 0 (the caller's heaviest tile) of all its heads, then rank 1, ...
+// Workgroups start in id order on each XCD, so the longest tiles start first
+// and the short ones fill in at the end (greedy longest-first).  Otherwise the
+// order is head by head.
+__device__ __forceinline__ void tile_order(int bid, int n, int nb, int &head, int &rank) {
+  const int L = xcd_remap(bid, n);
+  if (n % (8 * nb) == 0) {
+    const int hp = n / (8 * nb);  // heads per XCD
+    const int x = L / (hp * nb), idx = L % (hp * nb);
+    rank = idx / hp;
+    head = x * hp + idx % hp;
+  } else {
+    head = L / nb;
+    rank = L % nb;
+  }
+}
+
 // Store 4 consecutive fp32 values as T.
 template <typename T> __device__ __forceinline__ void store4(T *dst, float a, float b, float c, float d);
 template <> __device__ __forceinline__ void store4<bf16>(bf16 *dst, float a, float b, float c, float d) {
