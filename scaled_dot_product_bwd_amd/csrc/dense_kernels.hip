@@ -31,6 +31,12 @@
 
 namespace attn {
 
+// Heads whose tiles an XCD interleaves (tile_order): enough for longest-first
+// balance of the causal block sizes, few enough to keep their operands in L2.
+// Measured: dK / dV and dQ run as fast with 2 and 4 as with all of an XCD's
+// heads; the row statistics (three workgroups per CU) are faster with all.
+constexpr int kKvGroup = 2, kDqGroup = 4, kRsGroup = 8;
+
 // Each kernel's chunk loop runs in a force-inlined `*_run` function unrolled by
 // three, so every step has its LDS buffers fixed at compile time.  Steps are
 // unconditional (a conditional step would make the accumulators merge across
@@ -172,7 +178,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   const int l32 = S.lane & 31, half = S.half;
   const int nb = p.nblk;
   int bh, rank;
-  tile_order(blockIdx.x, gridDim.x, nb, bh, rank);
+  tile_order<kRsGroup>(blockIdx.x, gridDim.x, nb, bh, rank);
   const int blk = nb - 1 - rank;  // the heaviest causal blocks first
   S.h = bh % p.H;
   S.b = bh / p.H;
@@ -370,7 +376,7 @@ __global__ __launch_bounds__(256) void k_kv_bwd(const DenseParams p) {
   S.half = S.lane >> 5;
   const int nb = p.nblk;
   int bg, blk;  // key block 0 sees the most queries under a causal mask: rank = block
-  tile_order(blockIdx.x, gridDim.x, nb, bg, blk);
+  tile_order<kKvGroup>(blockIdx.x, gridDim.x, nb, bg, blk);
   const int g = bg % p.Hkv;  // the K / V head; its query heads are g * G ... g * G + G - 1
   S.b = bg / p.Hkv;
   S.h0 = g * p.G;
@@ -501,7 +507,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int l32 = S.lane & 31, half = S.half;
   const int nb = p.nblk;
   int bh, rank;
-  tile_order(blockIdx.x, gridDim.x, nb, bh, rank);
+  tile_order<kDqGroup>(blockIdx.x, gridDim.x, nb, bh, rank);
   const int blk = nb - 1 - rank;
   S.h = bh % p.H;
   S.b = bh / p.H;

@@ -375,19 +375,24 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
 }
 
 // Workgroup id -> (head, rank) for a grid of n = heads * nb tiles, nb per head.
-// Every XCD gets a contiguous range of heads (their tiles share its L2), and
-// when the heads split evenly over the 8 XCDs an XCD runs its tiles rank by
-// rank: rank 0 (the caller's heaviest tile) of all its heads, then rank 1, ...
-// Workgroups start in id order on each XCD, so the longest tiles start first
-// and the short ones fill in at the end (greedy longest-first).  Otherwise the
-// order is head by head.
+// Every XCD gets a contiguous range of heads (their tiles share its L2).  When
+// the heads split evenly over the 8 XCDs, an XCD takes its heads GS at a time
+// (all of them if GS does not divide their count) and runs each group's tiles
+// rank by rank: rank 0 (the caller's heaviest tile) of the group's heads, then
+// rank 1, ...  Workgroups start in id order on each XCD, so long tiles start
+// early and short ones fill in at the end (close to greedy longest-first),
+// while only about GS heads' operands are in flight in the XCD's L2 at a time.
+// Otherwise the order is head by head.
+template <int GS>
 __device__ __forceinline__ void tile_order(int bid, int n, int nb, int &head, int &rank) {
   const int L = xcd_remap(bid, n);
   if (n % (8 * nb) == 0) {
     const int hp = n / (8 * nb);  // heads per XCD
+    const int gs = hp % GS == 0 ? GS : hp;
     const int x = L / (hp * nb), idx = L % (hp * nb);
-    rank = idx / hp;
-    head = x * hp + idx % hp;
+    const int grp = idx / (gs * nb), w = idx % (gs * nb);
+    rank = w / gs;
+    head = x * hp + grp * gs + w % gs;
   } else {
     head = L / nb;
     rank = L % nb;
