@@ -29,8 +29,9 @@ fp32 row statistics; one step = one attn_bwd_paged call (plan built and
 uploaded beforehand).  Its roofline is HBM: algorithmic bytes (K / V history
 read once, dK / dV written over the listed pages, Q, dY and statistics read
 once) over the kernel time.  The line also times the query side (statistics
-and dQ on the GPU) and gives the whole chain's rate counted like the dense
-metric (10 D flops per visible triple).
+and dQ on the GPU; split form, and the direct form beside it) and gives the
+whole chain's rate counted like the dense metric (10 D flops per visible
+triple).
 
 --workload paged_mla measures the latent variant of the same kernel on the same
 page tables (16 query heads on one latent KV head of width 128 plus a position
@@ -272,24 +273,30 @@ def main_paged(args, torch, sdb, dev):
         raise RuntimeError("non-finite gradients in the benchmark output")
     # The query side (statistics and dQ on the GPU, attn_bwd_paged_row_stats /
     # attn_bwd_paged_dq), timed the same way; reported beside the dK / dV line.
+    # Split form (each block's tokens in pieces of <= 1024, merged; the default)
+    # and the direct form (one workgroup per block).
     st_gpu = torch.empty_like(stats)
     dq = torch.empty_like(q)
-    q_ms = {}
-    for name, fn, outp in (("row_stats", lib.attn_bwd_paged_row_stats, st_gpu),
-                           ("dq", lib.attn_bwd_paged_dq, dq)):
-        def qstep():
-            rc = fn(ctypes.byref(a), ctypes.c_void_p(outp.data_ptr()), sdb._stream_handle(None))
-            if rc != 0:
-                raise RuntimeError(lib.attn_bwd_last_error().decode())
-        for _ in range(args.warmup):
-            qstep()
-        torch.cuda.synchronize()
-        t0.record()
-        for _ in range(args.steps):
-            qstep()
-        t1.record()
-        torch.cuda.synchronize()
-        q_ms[name] = round(t0.elapsed_time(t1) / args.steps, 4)
+    qws = sdb.paged_q_workspace(plan, D, dev)
+    q_ms, q_direct_ms = {}, {}
+    for split, dst in ((True, q_ms), (False, q_direct_ms)):
+        a.q_workspace = qws.data_ptr() if split else None
+        a.q_workspace_bytes = qws.numel() if split else 0
+        for name, fn, outp in (("row_stats", lib.attn_bwd_paged_row_stats, st_gpu),
+                               ("dq", lib.attn_bwd_paged_dq, dq)):
+            def qstep():
+                rc = fn(ctypes.byref(a), ctypes.c_void_p(outp.data_ptr()), sdb._stream_handle(None))
+                if rc != 0:
+                    raise RuntimeError(lib.attn_bwd_last_error().decode())
+            for _ in range(args.warmup):
+                qstep()
+            torch.cuda.synchronize()
+            t0.record()
+            for _ in range(args.steps):
+                qstep()
+            t1.record()
+            torch.cuda.synchronize()
+            dst[name] = round(t0.elapsed_time(t1) / args.steps, 4)
     nbytes = paged_bytes(w, plan)
     flops = paged_flops(w)
     gbs = nbytes / (ms / 1e3) / 1e9
@@ -314,6 +321,7 @@ def main_paged(args, torch, sdb, dev):
                      "kernel": KERNEL_NAMES["paged"], "kernel_ms": round(ms, 4),
                      "bytes_per_launch": nbytes},
         "query_side_ms": q_ms,
+        "query_side_direct_ms": q_direct_ms,
         "full_chain_tflops": round(flops * 10.0 / 8.0 / ((ms + sum(q_ms.values())) / 1e3) / 1e12, 3),
         "cpu_baseline": cpu,
     }

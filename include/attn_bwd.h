@@ -200,6 +200,15 @@ typedef struct attn_bwd_paged_args {
   int32_t mla, position_dim;
   const void *qp, *kp_pool;              /* device, 16-byte aligned, contiguous */
   void *dkp_pool;                        /* device [pool_pages * page_size, kv_heads, position_dim] */
+  /* Query side only (attn_bwd_paged_row_stats / attn_bwd_paged_dq): NULL, or a
+   * device workspace of q_workspace_bytes >= attn_bwd_paged_q_workspace_bytes()
+   * (16-byte aligned, overlapping nothing else).  With it the call runs in split
+   * form: each query block's tokens are cut into pieces of at most 1024, one
+   * workgroup per piece, and a merge pass combines the pieces in token order,
+   * so a long sequence no longer sets the time.  Results equal the direct form
+   * up to rounding order; both are bit-identical from run to run. */
+  void *q_workspace;
+  size_t q_workspace_bytes;
 } attn_bwd_paged_args;
 
 /* Enqueues the paged backward.  Every device pointer must be 16-byte aligned;
@@ -226,6 +235,12 @@ int attn_bwd_paged(const attn_bwd_paged_args *a, void *stream);
  * Both reject outputs that overlap an input; the plan, pointers and
  * alignment follow attn_bwd_paged. */
 int attn_bwd_paged_row_stats(const attn_bwd_paged_args *a, float *stats, void *stream);
+
+/* Bytes of q_workspace the split form of the query side needs for a plan
+ * (host words) and head_dim: pieces * kv_heads * 128 rows * head_dim fp32
+ * (the statistics use 4 of the head_dim floats per row).  0 for a buffer that
+ * is not a plan. */
+size_t attn_bwd_paged_q_workspace_bytes(const int32_t *plan_host, int32_t head_dim);
 int attn_bwd_paged_dq(const attn_bwd_paged_args *a, void *dq, void *stream);
 
 /* The dense backward from what a forward pass saved, instead of recomputing

@@ -35,6 +35,7 @@ from ._abi import (ATTN_BF16, ATTN_F32, ATTN_MASK_BIAS, ATTN_MASK_CAUSAL,
 __all__ = ["attn_bwd", "attn_bwd_stage", "workspace_bytes", "make_args", "AttnError",
            "load_library", "library_path", "MASKS", "WRT", "PagedPlan", "paged_plan",
            "attn_bwd_paged", "attn_bwd_paged_mla", "make_paged_args", "paged_row_stats",
+           "paged_q_workspace",
            "attn_bwd_paged_dq"]
 
 MASKS = {"none": ATTN_MASK_NONE, "causal": ATTN_MASK_CAUSAL, "keypad": ATTN_MASK_KEYPAD,
@@ -332,32 +333,52 @@ def attn_bwd_paged_mla(q, qp, dy, latent_pool, kp_pool, stats, plan, *, dlat_poo
     return dlat_pool, dkp_pool
 
 
-def paged_row_stats(q, dy, k_pool, v_pool, plan, *, causal=True, scale=None, out=None,
-                    stream=None):
-    """(max, denominator, delta) per (row, head) of the paged layout, float32
-    [nq, heads, 3], computed on the GPU (attn_bwd_paged_row_stats)."""
+def paged_q_workspace(plan, head_dim, device):
+    """A device workspace for the split form of the query side (torch-allocated)."""
     torch = _torch()
-    nq, heads, _ = q.shape
+    n = load_library().attn_bwd_paged_q_workspace_bytes(plan.words.ctypes.data, int(head_dim))
+    return torch.empty(max(int(n), 16), dtype=torch.uint8, device=device)
+
+
+def _set_q_workspace(args, ws):
+    if ws is not None:
+        args.q_workspace = ws.data_ptr()
+        args.q_workspace_bytes = ws.numel() * ws.element_size()
+
+
+def paged_row_stats(q, dy, k_pool, v_pool, plan, *, causal=True, scale=None, out=None,
+                    stream=None, split=True, workspace=None):
+    """(max, denominator, delta) per (row, head) of the paged layout, float32
+    [nq, heads, 3], computed on the GPU (attn_bwd_paged_row_stats).  split: use
+    the split form (each block's tokens in pieces; a workspace is allocated
+    unless one is given)."""
+    torch = _torch()
+    nq, heads, D = q.shape
     if plan.device_words is None:
         plan.to(q.device)
     if out is None:
         out = torch.empty(nq, heads, 3, dtype=torch.float32, device=q.device)
     dummy = out  # the struct's input statistics are not read by this call
     args = make_paged_args(q, dy, k_pool, v_pool, dummy, plan, causal=causal, scale=scale)
+    if split:
+        _set_q_workspace(args, workspace if workspace is not None else paged_q_workspace(plan, D, q.device))
     _check(load_library().attn_bwd_paged_row_stats(ctypes.byref(args), ctypes.c_void_p(out.data_ptr()),
                                                    _stream_handle(stream)))
     return out
 
 
 def attn_bwd_paged_dq(q, dy, k_pool, v_pool, stats, plan, *, causal=True, scale=None, out=None,
-                      stream=None):
-    """dQ [nq, heads, D] of the paged layout from the statistics (attn_bwd_paged_dq)."""
+                      stream=None, split=True, workspace=None):
+    """dQ [nq, heads, D] of the paged layout from the statistics (attn_bwd_paged_dq).
+    split: as for paged_row_stats."""
     torch = _torch()
     if plan.device_words is None:
         plan.to(q.device)
     if out is None:
         out = torch.empty_like(q)
     args = make_paged_args(q, dy, k_pool, v_pool, stats, plan, causal=causal, scale=scale)
+    if split:
+        _set_q_workspace(args, workspace if workspace is not None else paged_q_workspace(plan, q.shape[2], q.device))
     _check(load_library().attn_bwd_paged_dq(ctypes.byref(args), ctypes.c_void_p(out.data_ptr()),
                                             _stream_handle(stream)))
     return out

@@ -24,7 +24,7 @@ STATUS_NAMES = {ATTN_E_INVALID: "ATTN_E_INVALID", ATTN_E_UNSUPPORTED: "ATTN_E_UN
 EXPORTED = ["attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_row_stats", "attn_bwd_kv",
             "attn_bwd_dq", "attn_bwd_paged_plan_words", "attn_bwd_paged_plan_build",
             "attn_bwd_paged", "attn_bwd_paged_row_stats", "attn_bwd_paged_dq",
-            "attn_bwd_from_forward",
+            "attn_bwd_from_forward", "attn_bwd_paged_q_workspace_bytes",
             "attn_bwd_last_error"]
 
 # Plan header words (scaled_dot_product_bwd_amd/csrc/paged.hpp).
@@ -34,7 +34,8 @@ PLAN_ITEM_SLOTS = 128
  W_LINKS, W_QH, W_LISTED, W_OFF_ITEM_LINKS, W_OFF_ITEM_SLOTS, W_OFF_LINK_SEQ, W_OFF_LINK_INFO,
  W_OFF_LINK_TOK, W_OFF_SEQ_QH, W_OFF_QH_RH, W_OFF_QH_POS, W_OFF_SEQ_MAXPOS,
  W_OFF_LISTED, W_OFF_SEQ_MINPOS, W_OFF_SEQ_TOK, W_OFF_TOK_SLOT, W_TOKENS, W_OFF_QBLK,
- W_QBLK) = range(28)
+ W_QBLK, W_OFF_QPIECE, W_OFF_QBLK_PIECE, W_OFF_QPIECE_ORDER, W_QPIECES) = range(32)
+PLAN_QPIECE_TOKENS = 1024
 
 
 class AttnError(RuntimeError):
@@ -81,6 +82,7 @@ class AttnBwdPagedArgs(ctypes.Structure):
         ("mla", ctypes.c_int32), ("position_dim", ctypes.c_int32),
         ("qp", ctypes.c_void_p), ("kp_pool", ctypes.c_void_p),
         ("dkp_pool", ctypes.c_void_p),
+        ("q_workspace", ctypes.c_void_p), ("q_workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -122,6 +124,8 @@ def load_library():
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [ctypes.POINTER(AttnBwdPagedArgs), ctypes.c_void_p, ctypes.c_void_p]
+    lib.attn_bwd_paged_q_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_bwd_paged_q_workspace_bytes.argtypes = [_p, _i32]
     lib.attn_bwd_last_error.restype = ctypes.c_char_p
     lib.attn_bwd_last_error.argtypes = []
     _lib = lib

@@ -353,8 +353,8 @@ int validate_paged(const attn_bwd_paged_args *a, int mode, void *out, attn::Page
   if (w[W_MAGIC] != kMagic) return fail(ATTN_E_INVALID, "plan_host is not a plan (bad magic)");
   const int64_t words = w[W_WORDS];
   if (words < HEADER_WORDS) return fail(ATTN_E_INVALID, "plan header is inconsistent");
-  for (int k = W_OFF_ITEM_LINKS; k <= W_OFF_QBLK; ++k) {
-    if (k == W_TOKENS) continue;
+  for (int k = W_OFF_ITEM_LINKS; k <= W_OFF_QPIECE_ORDER; ++k) {
+    if (k == W_TOKENS || k == W_QBLK) continue;
     if (w[k] < HEADER_WORDS || w[k] > words) return fail(ATTN_E_INVALID, "plan offsets are inconsistent");
   }
   if (w[W_HEADS] != a->heads || w[W_KV_HEADS] != a->kv_heads || w[W_PAGE_SIZE] != a->page_size ||
@@ -362,9 +362,11 @@ int validate_paged(const attn_bwd_paged_args *a, int mode, void *out, attn::Page
     return fail(ATTN_E_INVALID,
                 "plan was built for heads %d, kv_heads %d, page_size %d, nq %d, pool_pages %d",
                 w[W_HEADS], w[W_KV_HEADS], w[W_PAGE_SIZE], w[W_NQ], w[W_POOL_PAGES]);
-  const int64_t items = w[W_ITEMS], qblocks = w[W_QBLK];
+  const int64_t items = w[W_ITEMS], qblocks = w[W_QBLK], qpieces = w[W_QPIECES];
   if (items < 0 || items * (int64_t)a->kv_heads > INT32_MAX || qblocks < 0 ||
-      qblocks * (int64_t)a->kv_heads > INT32_MAX)
+      qblocks * (int64_t)a->kv_heads > INT32_MAX || qpieces < 0 ||
+      qpieces * (int64_t)a->kv_heads > INT32_MAX ||
+      qblocks * (int64_t)a->kv_heads * attn::kQBlockRows * 32 > INT32_MAX * (int64_t)256)
     return fail(ATTN_E_INVALID, "plan item count is inconsistent");
   bf16 = a->dtype == ATTN_BF16;
   nblocks = (int)((mode == PM_KV ? items : qblocks) * a->kv_heads);
@@ -413,7 +415,31 @@ int validate_paged(const attn_bwd_paged_args *a, int mode, void *out, attn::Page
         return fail(ATTN_E_INVALID, "%s overlaps %s", ts[i].name, ts[j].name);
   }
 
+  // Query side, split form: the partial results' workspace.
+  float *qws = nullptr;
+  if (mode != PM_KV && a->q_workspace && work) {
+    const int64_t need = qpieces * a->kv_heads * attn::kQBlockRows *
+                         (mode == PM_STATS ? 4 : D) * (int64_t)sizeof(float);
+    if ((int64_t)a->q_workspace_bytes < need)
+      return fail(ATTN_E_WORKSPACE, "q_workspace_bytes %zu < %lld needed", a->q_workspace_bytes,
+                  (long long)need);
+    if ((uintptr_t)a->q_workspace % 16)
+      return fail(ATTN_E_UNSUPPORTED, "q_workspace is not 16-byte aligned");
+    Range wr;
+    wr.lo = (uintptr_t)a->q_workspace;
+    wr.hi = wr.lo + (uintptr_t)need;
+    for (int j = 0; j < NT; ++j)
+      if (ts[j].needed && overlap(wr, rng[j]))
+        return fail(ATTN_E_INVALID, "q_workspace overlaps %s", ts[j].name);
+    qws = (float *)a->q_workspace;
+  }
+
   std::memset(&p, 0, sizeof p);
+  p.qws = qws;
+  p.off_qpiece = w[W_OFF_QPIECE];
+  p.off_qblk_piece = w[W_OFF_QBLK_PIECE];
+  p.off_qpiece_order = w[W_OFF_QPIECE_ORDER];
+  p.qpieces = (int)qpieces;
   p.q = a->q; p.dy = a->dy; p.k_pool = a->k_pool; p.v_pool = a->v_pool;
   p.dk_pool = a->dk_pool; p.dv_pool = a->dv_pool;
   if (mla) {
@@ -495,6 +521,17 @@ int attn_bwd_paged_row_stats(const attn_bwd_paged_args *a, float *stats, void *s
 
 int attn_bwd_paged_dq(const attn_bwd_paged_args *a, void *dq, void *stream) {
   return run_paged(a, PM_DQ, dq, stream);
+}
+
+size_t attn_bwd_paged_q_workspace_bytes(const int32_t *plan_host, int32_t head_dim) {
+  using namespace attn::plan;
+  if (!plan_host || plan_host[W_MAGIC] != kMagic || head_dim <= 0 || plan_host[W_QPIECES] < 0 ||
+      plan_host[W_KV_HEADS] <= 0) {
+    fail(ATTN_E_INVALID, "not a plan, or head_dim <= 0");
+    return 0;
+  }
+  return (size_t)plan_host[W_QPIECES] * (size_t)plan_host[W_KV_HEADS] * attn::kQBlockRows *
+         (size_t)(head_dim > 4 ? head_dim : 4) * sizeof(float);
 }
 
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq) {

@@ -138,7 +138,9 @@ __device__ __forceinline__ void rs_step(const DenseParams &p, RsState<T, D> &S, 
 }
 
 // Prologue shared by the query-major kernels: chunks c_first (and, with three
-// buffers, c_first + 1) into buffers 0 (and 1).
+// buffers, c_first + 1) into buffers 0 (and 1).  It ends with a full drain, which
+// also covers the register fragment loads issued before it: their latency and
+// the first chunks' overlap, and the compiler knows them complete in the loop.
 template <typename T, int D, int NBUF = 3>
 __device__ __forceinline__ void q_prologue(const DenseParams &p, ChunkIO<T, D> &io_k,
                                            ChunkIO<T, D> &io_v, const T *kbase, const T *vbase,
@@ -156,7 +158,8 @@ __device__ __forceinline__ void q_prologue(const DenseParams &p, ChunkIO<T, D> &
     io_k.complete(Ks[1]);
     io_v.complete(Vs[1]);
   }
-  end_step<ChunkIO<T, D>::DIRECT, 2 * ChunkIO<T, D>::LOADS>(second);
+  wait_vmem();
+  __syncthreads();
 }
 
 // Buffers of the row-statistics chunk stream.  Two (48 KB of LDS at D = 128)
@@ -205,10 +208,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   S.c_last = R.c_last;
   S.io_k.init(p.ks[1]);
   S.io_v.init(p.vs[1]);
-  // Let the fragment loads above land before the first chunk load is issued,
-  // so the compiler knows they are complete inside the loop (otherwise it
-  // would wait for them there, and with them for the chunk loads in flight).
-  wait_vmem();
   q_prologue<T, D, kRsBuf>(p, S.io_k, S.io_v, S.kbase, S.vbase, R.c_first, R.c_last, Ks, Vs);
   S.buf = 0;
   for (int c = R.c_first; c <= R.c_last; ++c)
@@ -327,7 +326,6 @@ __device__ __forceinline__ void kv_run(const DenseParams &p, KvState<T, D> &S, i
                                        Tile<T, D, KvShape<T>::ROWS> *Gs,
                                        float (*st)[8 * KvShape<T>::ROWS]) {
   constexpr int ROWS = KvShape<T>::ROWS;
-  constexpr int PER_CHUNK = 2 * ChunkIO<T, D, ROWS>::LOADS + stat_loads<ROWS>();
   const int c_first = S.c_first;
   if (S.total <= 0) return;
   kv_issue<T, D, MODE>(p, S, 0, &Qs[0], &Gs[0], st[0]);
@@ -339,7 +337,10 @@ __device__ __forceinline__ void kv_run(const DenseParams &p, KvState<T, D> &S, i
     S.io_q.complete(Qs[1]);
     S.io_g.complete(Gs[1]);
   }
-  end_step<ChunkIO<T, D, ROWS>::DIRECT, PER_CHUNK>(second);
+  // A full drain: also the K / V fragment loads issued before (their latency
+  // overlaps the first chunks'; the compiler then knows them complete).
+  wait_vmem();
+  __syncthreads();
   S.buf = 0;
   // Unmasked chunks [cu0, cu1]: every row i of the chunk sees every key j of the
   // block: j_last - i <= hi_off, j0 - i >= lo_off, i < Sq, j_last < Sk.
@@ -409,7 +410,6 @@ __global__ __launch_bounds__(256) void k_kv_bwd(const DenseParams p) {
   for (int t = 0; t < NT; ++t) S.dk[t] = S.dv[t] = f32x16{};
   S.io_q.init(p.qs[1]);
   S.io_g.init(p.dys[1]);
-  wait_vmem();  // fragment loads complete before the loop (see k_row_stats)
   kv_run<T, D, MODE>(p, S, c_last, j0b, Qs, Gs, st);
 
   if (!kvalid) return;
@@ -537,7 +537,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   S.c_last = R.c_last;
   S.io_k.init(p.ks[1]);
   S.io_v.init(p.vs[1]);
-  wait_vmem();  // fragment and statistics loads complete before the loop (see k_row_stats)
   q_prologue<T, D>(p, S.io_k, S.io_v, S.kbase, S.vbase, R.c_first, R.c_last, Ks, Vs);
   S.buf = 0;
   for (int c = R.c_first; c <= R.c_last; ++c)

@@ -29,6 +29,10 @@
 //            kernels stream a sequence's keys through this table).
 //   qblock   a sequence's qh rows cut into blocks of 128, one query-side
 //            workgroup per (block, KV head).
+//   qpiece   a query block's token range cut into pieces of at most
+//            kQPieceTokens tokens, for the query side's split form: one
+//            workgroup per (piece, KV head) writes partial results that a
+//            merge pass combines in piece order.
 #pragma once
 
 #include <stdint.h>
@@ -69,6 +73,11 @@ enum Word {
   W_OFF_QBLK,        // [qblocks * 2] (sequence, first qh row) of each 128-qh-row block,
                      // sequences with more visible tokens first
   W_QBLK,            // number of query blocks
+  W_OFF_QPIECE,      // [qpieces * 3] (query block, first token, end token), block-major,
+                     // token order within a block
+  W_OFF_QBLK_PIECE,  // [qblocks + 1] CSR: the pieces of query block b
+  W_OFF_QPIECE_ORDER,  // [qpieces] piece ids, longest first (the split grid's order)
+  W_QPIECES,         // number of pieces
   HEADER_WORDS = 32
 };
 
@@ -77,6 +86,7 @@ enum { LI_MIN_TOK = 0, LI_MAX_TOK = 1, LI_ALL_VALID = 2, LINK_INFO_WORDS = 4 };
 }  // namespace plan
 
 constexpr int kQBlockRows = 128;
+constexpr int kQPieceTokens = 1024;  // a multiple of the 32-token chunk
 
 struct PagedParams {
   const void *q, *dy, *k_pool, *v_pool;
@@ -98,6 +108,10 @@ struct PagedParams {
   int off_item_links, off_item_slots, off_link_seq, off_link_info, off_link_tok;
   int off_seq_qh, off_qh_rh, off_qh_pos, off_seq_maxpos, off_seq_minpos;
   int off_seq_tok, off_tok_slot, off_qblk, qblocks;
+  // query side, split form: pieces and the partial results' workspace
+  // (per (piece, KV head, row of the block): 4 floats of statistics or D of dQ)
+  int off_qpiece, off_qblk_piece, off_qpiece_order, qpieces;
+  float *qws;
 };
 
 }  // namespace attn

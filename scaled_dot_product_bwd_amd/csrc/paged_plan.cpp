@@ -67,18 +67,22 @@ int check_dims(int32_t nseq, const int32_t *seq_lens, int32_t max_pages, int32_t
 // fits an item by itself).
 int64_t words_bound(int32_t nseq, const int32_t *seq_lens, int32_t nq, int32_t heads,
                     int32_t kv_heads, int32_t page_size, int32_t pool_pages) {
-  int64_t refs = 0, tokens = 0;
+  int64_t refs = 0, tokens = 0, maxlen = 0;
   for (int32_t s = 0; s < nseq; ++s) {
     refs += npages_of(seq_lens[s], page_size);
     tokens += seq_lens[s];
+    maxlen = std::max<int64_t>(maxlen, seq_lens[s]);
   }
   const int64_t pieces = npages_of(page_size, kItemSlots);
   const int64_t items = refs * pieces, links = refs * pieces;
   const int64_t qh = (int64_t)nq * (heads / kv_heads);
   using attn::kQBlockRows;
+  using attn::kQPieceTokens;
+  const int64_t qblk = (qh + kQBlockRows - 1) / kQBlockRows + nseq;
+  const int64_t qpieces = qblk * std::max<int64_t>(1, (maxlen + kQPieceTokens - 1) / kQPieceTokens);
   return HEADER_WORDS + (items + 1) + items * kItemSlots + links * (1 + LINK_INFO_WORDS + kItemSlots) +
          (nseq + 1) + 2 * qh + 2 * nseq + std::min<int64_t>(refs, pool_pages) + (nseq + 1) +
-         tokens + 2 * ((qh + kQBlockRows - 1) / kQBlockRows + nseq);
+         tokens + 2 * qblk + 4 * qpieces + qblk + 1;
 }
 
 }  // namespace
@@ -242,6 +246,20 @@ extern "C" int attn_bwd_paged_plan_build(int32_t nseq, const int32_t *seq_lens,
   for (auto &o : order) n_qblk += (rows_cnt[o.second + 1] * (int64_t)group + kQBlockRows - 1) / kQBlockRows;
   w[W_OFF_QBLK] = (int32_t)at;
   at += 2 * n_qblk;
+  // Query pieces: each block's token range [0, len) in pieces of at most
+  // kQPieceTokens (an empty sequence still gets one, empty, piece).
+  using attn::kQPieceTokens;
+  int64_t n_qpiece = 0;
+  for (auto &o : order) {
+    const int64_t nb = (rows_cnt[o.second + 1] * (int64_t)group + kQBlockRows - 1) / kQBlockRows;
+    n_qpiece += nb * std::max<int64_t>(1, (seq_lens[o.second] + kQPieceTokens - 1) / kQPieceTokens);
+  }
+  w[W_OFF_QPIECE] = (int32_t)at;
+  at += 3 * n_qpiece;
+  w[W_OFF_QBLK_PIECE] = (int32_t)at;
+  at += n_qblk + 1;
+  w[W_OFF_QPIECE_ORDER] = (int32_t)at;
+  at += n_qpiece;
   if (at > plan_words) return perr(ATTN_E_INVALID, "paged plan: internal size error");
 
   int32_t *item_links = w + w[W_OFF_ITEM_LINKS], *item_slots = w + w[W_OFF_ITEM_SLOTS];
@@ -343,6 +361,34 @@ extern "C" int attn_bwd_paged_plan_build(int32_t nseq, const int32_t *seq_lens,
     }
   }
   w[W_QBLK] = (int32_t)n_qblk;
+  {
+    const int32_t *qb = w + w[W_OFF_QBLK];
+    int32_t *qp = w + w[W_OFF_QPIECE], *qbp = w + w[W_OFF_QBLK_PIECE];
+    int32_t *qord = w + w[W_OFF_QPIECE_ORDER];
+    int64_t k = 0;
+    for (int64_t b = 0; b < n_qblk; ++b) {
+      qbp[b] = (int32_t)k;
+      const int32_t len = seq_lens[qb[2 * b]];
+      int32_t t = 0;
+      do {
+        const int32_t e = (int32_t)std::min<int64_t>(len, (int64_t)t + kQPieceTokens);
+        qp[3 * k] = (int32_t)b;
+        qp[3 * k + 1] = t;
+        qp[3 * k + 2] = e;
+        ++k;
+        t = e;
+      } while (t < len);
+    }
+    qbp[n_qblk] = (int32_t)k;
+    // Split grid order: the longest pieces first (ties in piece order).
+    std::vector<int32_t> ids(k);
+    for (int64_t i = 0; i < k; ++i) ids[i] = (int32_t)i;
+    std::stable_sort(ids.begin(), ids.end(), [&](int32_t a, int32_t b2) {
+      return qp[3 * a + 2] - qp[3 * a + 1] > qp[3 * b2 + 2] - qp[3 * b2 + 1];
+    });
+    std::copy(ids.begin(), ids.end(), qord);
+    w[W_QPIECES] = (int32_t)k;
+  }
   w[W_MAGIC] = kMagic;
   w[W_WORDS] = (int32_t)at;
   w[W_NSEQ] = nseq;

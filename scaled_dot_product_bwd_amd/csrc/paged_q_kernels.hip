@@ -17,6 +17,14 @@
 // A token is visible to a row iff it lies inside the sequence and, when
 // causal, at or before the row's position.  Rows with no visible token get
 // (-inf, 0, 0) and a zero dQ row (a zero denominator, which the pages skip).
+//
+// Split form: the time of the one-workgroup-per-block form is set by the
+// longest sequence.  The split form runs one workgroup per (piece of at most
+// kQPieceTokens tokens of a block, KV head), longest pieces first, each writing
+// its partial statistics (log2-domain max, l, delta') or unscaled partial dQ to
+// a workspace; a merge kernel then combines a block's pieces in token order
+// (the statistics by rescaling to the common max, dQ by summing) and writes
+// the same outputs.
 #include "device_common.hpp"
 #include "paged.hpp"
 #include "q_core.hpp"
@@ -128,7 +136,7 @@ __device__ __forceinline__ void pq_step(const PagedParams &p, PqState<T, D, STAG
   S.buf = bz;
 }
 
-template <typename T, int D, int STAGE>
+template <typename T, int D, int STAGE, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_paged_q(const PagedParams p) {
   typedef MT<T> M;
   constexpr int KS = M::KS, KL = M::KL, NSD = D / KS, NT = D / 32;
@@ -140,10 +148,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   S.lane = threadIdx.x & 63;
   const int l32 = S.lane & 31, half = S.lane >> 5;
   const int32_t *plan = p.plan;
-  // Workgroup -> (query block, KV head): consecutive ids share a block, so the
-  // group's KV heads of one sequence run side by side.
+  // Workgroup -> (query block or piece, KV head): consecutive ids share a
+  // block, so the group's KV heads of one sequence run side by side.
   const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int blk = L / p.kv_heads, g = L % p.kv_heads;
+  const int g = L % p.kv_heads;
+  int blk = L / p.kv_heads, piece = 0, tb0 = 0, te0 = INT32_MAX;
+  if constexpr (SPLIT) {
+    piece = plan[p.off_qpiece_order + blk];
+    blk = plan[p.off_qpiece + 3 * piece];
+    tb0 = plan[p.off_qpiece + 3 * piece + 1];
+    te0 = plan[p.off_qpiece + 3 * piece + 2];
+  }
   const int seq = plan[p.off_qblk + 2 * blk], qh_begin = plan[p.off_qblk + 2 * blk + 1];
   const int qs0 = plan[p.off_seq_qh + seq], nqh = plan[p.off_seq_qh + seq + 1] - qs0;
   const int tb = plan[p.off_seq_tok + seq];
@@ -180,33 +195,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // Tokens any row of the sequence can see: [0, min(len, maxpos + 1)) when
   // causal; chunks all of whose tokens every row sees need no per-element test.
+  // The split form's piece covers tokens [tb0, te0) (tb0 a multiple of 32).
   const int maxpos = plan[p.off_seq_maxpos + seq], minpos = plan[p.off_seq_minpos + seq];
-  const int tend = p.causal ? min(S.len, maxpos + 1) : S.len;
-  S.c_last = tend > 0 ? (tend - 1) / 32 : -1;
+  const int tend = min(p.causal ? min(S.len, maxpos + 1) : S.len, te0);
+  const int c0 = tb0 / 32;
+  S.c_last = tend > tb0 ? (tend - 1) / 32 : c0 - 1;
   const int tfull = p.causal ? min(S.len, minpos + 1) : S.len;  // tokens [0, tfull) seen by all
   wait_vmem();
-  if (S.c_last >= 0) {
-    pq_rowinfo(S, 0, ri[0]);
-    pq_rowinfo(S, 1, ri[1]);
-    pq_rowinfo(S, 2, ri[2]);
+  if (S.c_last >= c0) {
+    pq_rowinfo(S, c0, ri[0]);
+    pq_rowinfo(S, c0 + 1, ri[1]);
+    pq_rowinfo(S, c0 + 2, ri[2]);
     wait_vmem();
     pq_chunk(p, S, ri[0], &Ks[0], &Vs[0]);
     S.io_k.complete(Ks[0]);
     S.io_v.complete(Vs[0]);
-    if (S.c_last >= 1) {
+    if (S.c_last >= c0 + 1) {
       pq_chunk(p, S, ri[1], &Ks[1], &Vs[1]);
       S.io_k.complete(Ks[1]);
       S.io_v.complete(Vs[1]);
     }
-    pq_rowinfo(S, 3, ri[0]);
+    pq_rowinfo(S, c0 + 3, ri[0]);
     wait_vmem();
     __syncthreads();
     S.buf = 0;
-    for (int c = 0; c <= S.c_last; ++c)
+    for (int c = c0; c <= S.c_last; ++c)
       pq_step<T, D, STAGE>(p, S, c, Ks, Vs, ri, c * 32 + 32 > tfull);
   }
 
   if (!S.valid) return;
+  if constexpr (SPLIT) {
+    // partial results of this piece: row 32 wave + l32 of the block
+    const int64_t prow = ((int64_t)piece * p.kv_heads + g) * kQBlockRows + 32 * S.wave + l32;
+    if constexpr (STAGE == PQ_STATS) {
+      const float l_tot = S.l + __shfl_xor(S.l, 32);
+      const float d_tot = S.dl + __shfl_xor(S.dl, 32);
+      if (half == 0) store4<float>(p.qws + 4 * prow, S.m, l_tot, d_tot, 0.f);
+    } else {
+      float *w = p.qws + prow * D;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          store4<float>(w + 32 * t + 8 * q + 4 * half, S.dq[t][4 * q], S.dq[t][4 * q + 1],
+                        S.dq[t][4 * q + 2], S.dq[t][4 * q + 3]);
+    }
+    return;
+  }
   if constexpr (STAGE == PQ_STATS) {
     const float l_tot = S.l + __shfl_xor(S.l, 32);
     const float d_tot = S.dl + __shfl_xor(S.dl, 32);
@@ -229,12 +264,73 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
+// Merge of the split form: one thread per (block, KV head, row of the block)
+// for the statistics, per 4 columns of such a row for dQ.  A block's pieces
+// are combined in token order.
+template <typename T, int D, int STAGE>
+__global__ __launch_bounds__(256) void k_paged_q_merge(const PagedParams p) {
+  constexpr int PER = STAGE == PQ_STATS ? 1 : D / 4;  // threads per row
+  const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (tid >= (int64_t)p.qblocks * p.kv_heads * kQBlockRows * PER) return;
+  const int dc = (int)(tid % PER);
+  int64_t r = tid / PER;
+  const int j = (int)(r % kQBlockRows);
+  r /= kQBlockRows;
+  const int g = (int)(r % p.kv_heads), b = (int)(r / p.kv_heads);
+  const int32_t *plan = p.plan;
+  const int seq = plan[p.off_qblk + 2 * b], qh = plan[p.off_qblk + 2 * b + 1] + j;
+  const int qs0 = plan[p.off_seq_qh + seq];
+  if (qh >= plan[p.off_seq_qh + seq + 1] - qs0) return;
+  const int64_t rh = (int64_t)plan[p.off_qh_rh + qs0 + qh] + (int64_t)g * p.group;
+  const int p0 = plan[p.off_qblk_piece + b], p1 = plan[p.off_qblk_piece + b + 1];
+  if constexpr (STAGE == PQ_STATS) {
+    float m = -INFINITY, l = 0.f, d = 0.f;
+    for (int pc = p0; pc < p1; ++pc) {
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(
+          p.qws + 4 * (((int64_t)pc * p.kv_heads + g) * kQBlockRows + j));
+      const float mn = fmaxf(m, v[0]);
+      if (mn == -INFINITY) continue;  // nothing seen yet
+      const float a = fast_exp2(m - mn), c = fast_exp2(v[0] - mn);
+      l = fmaf(l, a, v[1] * c);
+      d = fmaf(d, a, v[2] * c);
+      m = mn;
+    }
+    const bool empty = !(l > 0.f);
+    float *st = p.stats_out + 3 * rh;
+    st[0] = empty ? -INFINITY : m * kLn2;
+    st[1] = empty ? 0.f : l;
+    st[2] = empty ? 0.f : d / l;
+  } else {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int pc = p0; pc < p1; ++pc)
+      acc += *reinterpret_cast<const f32x4 *>(
+          p.qws + (((int64_t)pc * p.kv_heads + g) * kQBlockRows + j) * D + 4 * dc);
+    const float sc = p.scale;
+    store4<T>((T *)p.dq + rh * D + 4 * dc, sc * acc[0], sc * acc[1], sc * acc[2], sc * acc[3]);
+  }
+}
+
 template <typename T, int D>
 static hipError_t launch_t(int stage, const PagedParams &p, int nblocks, hipStream_t stream) {
-  if (stage == PQ_STATS)
-    hipLaunchKernelGGL((k_paged_q<T, D, PQ_STATS>), dim3(nblocks), dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL((k_paged_q<T, D, PQ_DQ>), dim3(nblocks), dim3(256), 0, stream, p);
+  if (!p.qws) {
+    if (stage == PQ_STATS)
+      hipLaunchKernelGGL((k_paged_q<T, D, PQ_STATS, false>), dim3(nblocks), dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((k_paged_q<T, D, PQ_DQ, false>), dim3(nblocks), dim3(256), 0, stream, p);
+    return hipGetLastError();
+  }
+  // split form: the pieces, then the merge
+  const int npiece = p.qpieces * p.kv_heads;
+  const int64_t mthreads =
+      (int64_t)p.qblocks * p.kv_heads * kQBlockRows * (stage == PQ_STATS ? 1 : D / 4);
+  const int mblocks = (int)((mthreads + 255) / 256);
+  if (stage == PQ_STATS) {
+    hipLaunchKernelGGL((k_paged_q<T, D, PQ_STATS, true>), dim3(npiece), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((k_paged_q_merge<T, D, PQ_STATS>), dim3(mblocks), dim3(256), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((k_paged_q<T, D, PQ_DQ, true>), dim3(npiece), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((k_paged_q_merge<T, D, PQ_DQ>), dim3(mblocks), dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

@@ -130,8 +130,9 @@ def test_unrequested_outputs_may_be_null():
 # attn_bwd_paged: validation happens on the host before any launch.
 
 def test_paged_args_struct_size():
-    # 9 int32 + float, then 9 pointers, then the latent variant's 2 int32 + 3 pointers
-    assert ctypes.sizeof(_abi.AttnBwdPagedArgs) == 40 + 9 * 8 + 8 + 3 * 8
+    # 9 int32 + float, then 9 pointers, the latent variant's 2 int32 + 3 pointers,
+    # the query side's workspace pointer and size
+    assert ctypes.sizeof(_abi.AttnBwdPagedArgs) == 40 + 9 * 8 + 8 + 3 * 8 + 16
 
 
 def _paged_plan(heads=4, kv_heads=2):
@@ -212,6 +213,25 @@ def test_paged_latent_rejections(kw, code, msg):
     plan = _paged_plan()
     rc, err = _paged_rc(_paged_args(plan, **kw))
     assert rc == code and msg in err, (rc, err)
+
+
+def test_paged_query_workspace_rules():
+    plan = _paged_plan()
+    lib = sdb.load_library()
+    W = plan.words
+    need_dq = int(W[_abi.W_QPIECES]) * 2 * 128 * 64 * 4  # pieces * kv_heads * rows * D * 4
+    assert lib.attn_bwd_paged_q_workspace_bytes(W.ctypes.data, 64) == need_dq
+    bad = W.copy()
+    bad[0] = 7
+    assert lib.attn_bwd_paged_q_workspace_bytes(bad.ctypes.data, 64) == 0
+    out = ctypes.c_void_p(1 << 30)
+    a = _paged_args(plan, q_workspace=(1 << 24) * 12, q_workspace_bytes=need_dq - 4)
+    assert lib.attn_bwd_paged_dq(ctypes.byref(a), out, None) == _abi.ATTN_E_WORKSPACE
+    a = _paged_args(plan, q_workspace=(1 << 24) * 12 + 8, q_workspace_bytes=need_dq)
+    assert lib.attn_bwd_paged_dq(ctypes.byref(a), out, None) == _abi.ATTN_E_UNSUPPORTED
+    a = _paged_args(plan, q_workspace=(1 << 24) * 1, q_workspace_bytes=need_dq)  # over q
+    assert lib.attn_bwd_paged_dq(ctypes.byref(a), out, None) == _abi.ATTN_E_INVALID
+    assert "q_workspace overlaps" in lib.attn_bwd_last_error().decode()
 
 
 def test_paged_query_side_rejects_latent_variant():

@@ -207,20 +207,21 @@ def _stats_err(got, ref):
     return errs
 
 
-def run_query_side(w, *, causal=True, label=""):
+def run_query_side(w, *, causal=True, label="", split=True):
     heads, kv, ps = w["heads"], w["kv_heads"], w["page_size"]
     kw = dict(heads=heads, kv_heads=kv, page_size=ps)
     plan = sb.paged_plan(w["seq_lens"], w["block_table"], w["query_seq"], w["query_pos"],
                          pool_pages=w["pool_pages"], device="cuda:0", **kw)
     print(f"[paged-q] {label} nq={w['q'].shape[0]} heads={heads}/{kv} D={w['D']} ps={ps} "
-          f"{w['dtype']} causal={causal} qblocks={plan.header(sb._abi.W_QBLK)}", flush=True)
+          f"{w['dtype']} causal={causal} qblocks={plan.header(sb._abi.W_QBLK)} "
+          f"pieces={plan.header(sb._abi.W_QPIECES)} split={split}", flush=True)
     dev = torch.device("cuda:0")
     q, dy, kp, vp = (w[n].to(dev) for n in ("q", "dy", "k_pool", "v_pool"))
-    st_gpu = sb.paged_row_stats(q, dy, kp, vp, plan, causal=causal)
+    st_gpu = sb.paged_row_stats(q, dy, kp, vp, plan, causal=causal, split=split)
     st_ref = oracle.paged_row_stats(w, w["q"], w["dy"], w["k_pool"], w["v_pool"], causal=causal, **kw)
     # dQ from the oracle's statistics (rounded to fp32), against the oracle's dQ
     st32 = torch.from_numpy(st_ref.astype(np.float32)).to(dev)
-    dq_gpu = sb.attn_bwd_paged_dq(q, dy, kp, vp, st32, plan, causal=causal)
+    dq_gpu = sb.attn_bwd_paged_dq(q, dy, kp, vp, st32, plan, causal=causal, split=split)
     torch.cuda.synchronize()
     dq_ref = oracle.paged_dq(w, w["q"], w["dy"], w["k_pool"], w["v_pool"], st_ref, causal=causal, **kw)
     tol = TOL[w["dtype"]]
@@ -231,23 +232,50 @@ def run_query_side(w, *, causal=True, label=""):
     assert not np.isnan(g).any()
     e = rel_err(g, dq_ref)
     assert e <= tol, f"{label} dq: rel err {e:.3e} > {tol:g}"
-    return dict(plan=plan, stats=st_gpu, dq=dq_gpu, stats_err=errs, dq_err=e)
+    return dict(plan=plan, stats=st_gpu, dq=dq_gpu, stats_err=errs, dq_err=e, st32=st32)
 
 
-Q_CASES = [CASES[0], CASES[1], CASES[3], CASES[4], CASES[5]]
+# Sequences longer than a 1024-token piece, so the split form merges several
+# pieces per query block (seed 110: queries in the middle, so under the causal
+# mask the pieces past them see nothing).
+LONG_CASES = [
+    dict(seed=109, nseq=3, len_lo=1100, len_hi=2700, q_per_seq=20, page_size=16, heads=8,
+         kv_heads=2, D=64, dtype=torch.bfloat16, shuffle_rows=True),
+    dict(seed=110, nseq=2, len_lo=2100, len_hi=3300, q_per_seq=36, page_size=32, heads=4,
+         kv_heads=1, D=128, dtype=torch.float32),
+]
+Q_CASES = [CASES[0], CASES[1], CASES[3], CASES[4], CASES[5]] + LONG_CASES
+
+
+def _middle_rows(w):
+    qp = w["query_pos"].clone()
+    for s in range(len(w["seq_lens"])):
+        m = w["query_seq"] == s
+        qp[m] = qp[m] - int(w["seq_lens"][s]) // 2
+    w["query_pos"] = qp
 
 
 @pytest.mark.parametrize("case", Q_CASES, ids=lambda c: f"seed{c['seed']}")
 @pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
-def test_paged_query_side_parity(case, causal):
+@pytest.mark.parametrize("split", [True, False], ids=["split", "direct"])
+def test_paged_query_side_parity(case, causal, split):
     w = sdpa_inputs.paged_workload(**case)
-    if case["seed"] == 106:
-        qp = w["query_pos"].clone()
-        for s in range(len(w["seq_lens"])):
-            m = w["query_seq"] == s
-            qp[m] = qp[m] - int(w["seq_lens"][s]) // 2
-        w["query_pos"] = qp
-    run_query_side(w, causal=causal, label=f"seed{case['seed']}")
+    if case["seed"] in (106, 110):
+        _middle_rows(w)
+    run_query_side(w, causal=causal, label=f"seed{case['seed']}", split=split)
+
+
+def test_paged_query_split_rerun_bitwise():
+    """The split form's merge runs in a fixed piece order: reruns are bit-identical."""
+    w = sdpa_inputs.paged_workload(**LONG_CASES[0])
+    out = run_query_side(w, label="rerun")
+    dev = torch.device("cuda:0")
+    q, dy, kp, vp = (w[n].to(dev) for n in ("q", "dy", "k_pool", "v_pool"))
+    st2 = sb.paged_row_stats(q, dy, kp, vp, out["plan"])
+    dq2 = sb.attn_bwd_paged_dq(q, dy, kp, vp, out["st32"], out["plan"])
+    torch.cuda.synchronize()
+    assert torch.equal(st2.view(torch.int32), out["stats"].view(torch.int32))
+    assert torch.equal(dq2.view(torch.int16), out["dq"].view(torch.int16))
 
 
 def test_paged_config5_gpu_chain():

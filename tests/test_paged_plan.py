@@ -264,3 +264,42 @@ def test_plan_token_slots(case):
         got = t["tok_slot"][t["seq_tok"][s]:t["seq_tok"][s + 1]]
         want = [bt[s, k // ps] * ps + k % ps for k in range(L)]
         assert got.tolist() == want
+
+
+@pytest.mark.parametrize("lengths", [[5000, 1, 1024, 2048, 3000], [100, 0, 4096], [1025]])
+def test_plan_query_pieces(lengths):
+    """Split form of the query side: each query block's tokens [0, len) are cut,
+    in order, into pieces of at most 1024 tokens starting at multiples of 1024
+    (one empty piece for an empty sequence); the grid order lists every piece
+    once, longest first, ties in piece order."""
+    w = sdpa_inputs.paged_workload(seed=41, lengths=lengths, q_per_seq=0, page_size=16,
+                                   heads=8, kv_heads=2, D=8, dtype=torch.float32)
+    # rows: 70 per sequence (two query blocks of 128 qh rows with group 4 -> 280 qh rows)
+    qs, qp = [], []
+    for s, L in enumerate(lengths):
+        for i in range(70):
+            qs.append(s)
+            qp.append(max(L - 70, 0) + i)
+    w["query_seq"] = torch.tensor(qs, dtype=torch.int32)
+    w["query_pos"] = torch.tensor(qp, dtype=torch.int32)
+    plan = _plan(w)
+    W = plan.words
+    nblk, npc = int(W[_abi.W_QBLK]), int(W[_abi.W_QPIECES])
+    qb = W[W[_abi.W_OFF_QBLK]:W[_abi.W_OFF_QBLK] + 2 * nblk].reshape(nblk, 2)
+    pcs = W[W[_abi.W_OFF_QPIECE]:W[_abi.W_OFF_QPIECE] + 3 * npc].reshape(npc, 3)
+    csr = W[W[_abi.W_OFF_QBLK_PIECE]:W[_abi.W_OFF_QBLK_PIECE] + nblk + 1]
+    order = W[W[_abi.W_OFF_QPIECE_ORDER]:W[_abi.W_OFF_QPIECE_ORDER] + npc]
+    T = _abi.PLAN_QPIECE_TOKENS
+    assert csr[0] == 0 and csr[-1] == npc
+    for b in range(nblk):
+        L = lengths[qb[b, 0]]
+        mine = pcs[csr[b]:csr[b + 1]]
+        assert (mine[:, 0] == b).all()
+        want = [(t, min(L, t + T)) for t in range(0, L, T)] or [(0, 0)]
+        assert [tuple(x) for x in mine[:, 1:]] == want
+    assert sorted(order.tolist()) == list(range(npc))
+    ln = pcs[order, 2] - pcs[order, 1]
+    assert (np.diff(ln) <= 0).all()
+    for i in range(1, npc):  # stable: equal lengths keep piece order
+        if ln[i] == ln[i - 1]:
+            assert order[i] > order[i - 1]
