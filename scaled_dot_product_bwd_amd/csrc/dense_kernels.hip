@@ -57,6 +57,30 @@ __device__ __forceinline__ void end_step(bool issued) {
   __syncthreads();
 }
 
+// The query-major kernels' loads of a later K / V chunk cn, as a per-step hook
+// for q_phase_a (direct loads only): load k < LOADS of K, then of V.  Past the
+// last chunk the caller passes cn = c_last again (loaded into the free buffer,
+// never read); the kernel drains the loads before it ends.
+template <typename T, int D>
+__device__ __forceinline__ auto q_next_chunk_dma(const DenseParams &p, ChunkIO<T, D> &io_k,
+                                                 ChunkIO<T, D> &io_v, const T *kbase,
+                                                 const T *vbase, int cn, Tile<T, D> &K,
+                                                 Tile<T, D> &V) {
+  constexpr int L = ChunkIO<T, D>::LOADS;
+  const T *kc = kbase + (int64_t)cn * 32 * p.ks[1];
+  const T *vc = vbase + (int64_t)cn * 32 * p.vs[1];
+  const int last = p.Sk - 1 - cn * 32;
+  const unsigned ksb = (unsigned)(p.ks[1] * sizeof(T)), vsb = (unsigned)(p.vs[1] * sizeof(T));
+  return [=, &io_k, &io_v, &K, &V](int k) {
+    if constexpr (ChunkIO<T, D>::DIRECT) {
+      if (k < L)
+        io_k.issue_one(k, kc, last, ksb, K);
+      else
+        io_v.issue_one(k - L, vc, last, vsb, V);
+    }
+  };
+}
+
 // ---------------------------------------------------------------------------
 // Row statistics.  Per query row: the running max m (log2 domain), the
 // denominator l = sum 2^(s - m) and delta' = sum 2^(s - m) dP, rescaled
@@ -94,12 +118,16 @@ __device__ __forceinline__ void rs_step(const DenseParams &p, RsState<T, D> &S, 
   constexpr int NQB = QShape<T>::NQB;
   const int bc = S.buf, bn = (bc + NBUF - 1) % NBUF;  // chunk c + NBUF - 1 goes to bn
   const bool issued = c + NBUF - 1 <= S.c_last;
-  if (issued) {
+  constexpr bool SPREAD = ChunkIO<T, D>::DIRECT;
+  auto dma = q_next_chunk_dma<T, D>(p, S.io_k, S.io_v, S.kbase, S.vbase,
+                                    min(c + NBUF - 1, S.c_last), Ks[bn], Vs[bn]);
+  if (!SPREAD && issued) {
     S.io_k.issue(S.kbase, p.ks[1], (c + NBUF - 1) * 32, p.Sk, Ks[bn]);
     S.io_v.issue(S.vbase, p.vs[1], (c + NBUF - 1) * 32, p.Sk, Vs[bn]);
   }
   f32x16 sacc[NQB], pacc[NQB];
-  q_phase_a<T, D, NQB>(&Ks[bc], &Vs[bc], S.qf, S.gf, sacc, pacc, S.lane);
+  q_phase_a<T, D, NQB, SPREAD ? 2 * ChunkIO<T, D>::LOADS : 0>(&Ks[bc], &Vs[bc], S.qf, S.gf, sacc,
+                                                              pacc, S.lane, dma);
   const int j0 = c * 32, half = S.half;
 #pragma unroll
   for (int q = 0; q < NQB; ++q) {
@@ -133,7 +161,7 @@ __device__ __forceinline__ void rs_step(const DenseParams &p, RsState<T, D> &S, 
     S.io_v.complete(Vs[bn]);
   }
   // With two buffers the chunk issued here is the next one: wait for all of it.
-  end_step<ChunkIO<T, D>::DIRECT, 2 * ChunkIO<T, D>::LOADS>(issued && NBUF == 3);
+  end_step<ChunkIO<T, D>::DIRECT, 2 * ChunkIO<T, D>::LOADS>((SPREAD || issued) && NBUF == 3);
   S.buf = bc == NBUF - 1 ? 0 : bc + 1;
 }
 
@@ -212,6 +240,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   S.buf = 0;
   for (int c = R.c_first; c <= R.c_last; ++c)
     rs_step<T, D, MODE, kRsBuf>(p, S, c, Ks, Vs, c < R.cu0 || c > R.cu1);
+  wait_vmem();  // the repeated loads of the last step land before the workgroup ends
 
 #pragma unroll
   for (int q = 0; q < NQB; ++q) {
@@ -288,7 +317,29 @@ __device__ __forceinline__ void kv_step(const DenseParams &p, KvState<T, D> &S, 
   const int bc = S.buf, bn = bc == 0 ? 2 : bc - 1;
   const int i0 = c * ROWS;
   const bool issued = v + 2 < S.total;
-  if (issued) kv_issue<T, D, MODE>(p, S, v + 2, &Qs[bn], &Gs[bn], st[bn]);
+  // Chunk v + 2: with direct loads, one load per step of this chunk (the
+  // kv_chunk dma hook), branch-free: past the end of the stream the last chunk
+  // is loaded again into the free buffer (never read; drained by kv_run), so
+  // every step issues the same loads.  With register loads (fp32) all of them
+  // are issued here.
+  constexpr bool SPREAD = ChunkIO<T, D, ROWS>::DIRECT;
+  constexpr int LQ = ChunkIO<T, D, ROWS>::LOADS;
+  const int vn = min(v + 2, S.total - 1), hn = vn / S.nch, cn = S.c_first + (vn - hn * S.nch);
+  const T *qn = S.qbase + hn * p.qs[2] + (int64_t)cn * ROWS * p.qs[1];
+  const T *gn = S.gbase + hn * p.dys[2] + (int64_t)cn * ROWS * p.dys[1];
+  const int64_t srn = S.srow0 + (int64_t)hn * p.Sq;
+  const int lastn = p.Sq - 1 - cn * ROWS;
+  auto dma = [&](int k) {
+    if constexpr (SPREAD) {
+      if (k < LQ)
+        S.io_q.issue_one(k, qn, lastn, (unsigned)(p.qs[1] * 2), Qs[bn]);
+      else if (k < 2 * LQ)
+        S.io_g.issue_one(k - LQ, gn, lastn, (unsigned)(p.dys[1] * 2), Gs[bn]);
+      else if (k == 2 * LQ)
+        issue_row_stats<ROWS>(p, srn, cn * ROWS, st[bn], S.wave, S.lane);
+    }
+  };
+  if (!SPREAD && issued) kv_issue<T, D, MODE>(p, S, v + 2, &Qs[bn], &Gs[bn], st[bn]);
   const int kj = S.kj, half = S.half, b = S.b;
   // Per-element mask term: the index rule, then padding or bias (log2 domain).
   auto adj = [&](int u, int r) -> float {
@@ -305,13 +356,14 @@ __device__ __forceinline__ void kv_step(const DenseParams &p, KvState<T, D> &S, 
     }
   };
   const float *stc = st[bc];
-  kv_chunk<T, D, D, MASKED, false, true>(S.kf, S.vf, S.dk, S.dv, &Qs[bc], &Gs[bc], stc, stc + ROWS, p.scale_log2,
-                         S.lane, adj);
+  kv_chunk<T, D, D, MASKED, false, true, SPREAD ? 2 * LQ + 1 : 0>(
+      S.kf, S.vf, S.dk, S.dv, &Qs[bc], &Gs[bc], stc, stc + ROWS, p.scale_log2, S.lane, adj, 1.f,
+      dma);
   if (issued) {
     S.io_q.complete(Qs[bn]);
     S.io_g.complete(Gs[bn]);
   }
-  end_step<ChunkIO<T, D, ROWS>::DIRECT, PER_CHUNK>(issued);
+  end_step<ChunkIO<T, D, ROWS>::DIRECT, PER_CHUNK>(SPREAD || issued);
   S.buf = bc == 2 ? 0 : bc + 1;
 }
 
@@ -360,6 +412,7 @@ __device__ __forceinline__ void kv_run(const DenseParams &p, KvState<T, D> &S, i
     for (; c <= cu1; ++c) kv_step<T, D, MODE, false>(p, S, v0 + c, c, h, Qs, Gs, st);
     for (; c <= c_last; ++c) kv_step<T, D, MODE, true>(p, S, v0 + c, c, h, Qs, Gs, st);
   }
+  wait_vmem();  // the repeated loads of the last steps land before the workgroup ends
 }
 
 template <typename T, int D, int MODE>
@@ -452,12 +505,16 @@ __device__ __forceinline__ void dq_step(const DenseParams &p, DqState<T, D> &S, 
   constexpr int NT = D / 32, CS = M::CSTEPS, NQB = QShape<T>::NQB;
   const int bc = S.buf, bn = bc == 0 ? 2 : bc - 1;
   const bool issued = c + 2 <= S.c_last;
-  if (issued) {
+  constexpr bool SPREAD = ChunkIO<T, D>::DIRECT;
+  auto dma = q_next_chunk_dma<T, D>(p, S.io_k, S.io_v, S.kbase, S.vbase, min(c + 2, S.c_last),
+                                    Ks[bn], Vs[bn]);
+  if (!SPREAD && issued) {
     S.io_k.issue(S.kbase, p.ks[1], (c + 2) * 32, p.Sk, Ks[bn]);
     S.io_v.issue(S.vbase, p.vs[1], (c + 2) * 32, p.Sk, Vs[bn]);
   }
   f32x16 sacc[NQB], pacc[NQB];
-  q_phase_a<T, D, NQB>(&Ks[bc], &Vs[bc], S.qf, S.gf, sacc, pacc, S.lane);
+  q_phase_a<T, D, NQB, SPREAD ? 2 * ChunkIO<T, D>::LOADS : 0>(&Ks[bc], &Vs[bc], S.qf, S.gf, sacc,
+                                                              pacc, S.lane, dma);
   const int j0 = c * 32, half = S.half;
   float dsv[NQB][16];
 #pragma unroll
@@ -489,7 +546,7 @@ __device__ __forceinline__ void dq_step(const DenseParams &p, DqState<T, D> &S, 
     S.io_k.complete(Ks[bn]);
     S.io_v.complete(Vs[bn]);
   }
-  end_step<ChunkIO<T, D>::DIRECT, 2 * ChunkIO<T, D>::LOADS>(issued);
+  end_step<ChunkIO<T, D>::DIRECT, 2 * ChunkIO<T, D>::LOADS>(SPREAD || issued);
   S.buf = bc == 2 ? 0 : bc + 1;
 }
 
@@ -541,6 +598,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   S.buf = 0;
   for (int c = R.c_first; c <= R.c_last; ++c)
     dq_step<T, D, MODE>(p, S, c, Ks, Vs, c < R.cu0 || c > R.cu1);
+  wait_vmem();  // the repeated loads of the last steps land before the workgroup ends
 
   const float sc = p.scale;  // the factor of dS, applied once
 #pragma unroll

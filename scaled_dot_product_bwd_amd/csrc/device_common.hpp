@@ -302,6 +302,17 @@ template <int D, int ROWS> struct ChunkIO<bf16, D, ROWS> {
       dma_lds16(&t.a[(wave + 4 * j) * 512], elem(row, col));
     }
   }
+  // Load j alone of issue() below, branch-free (the loads of one chunk may be
+  // spread over the previous chunk's compute; see the dK / dV kernel): cb is
+  // the chunk's first row, last = nrows - 1 - r0, rstride = bytes per row.
+  // A lane whose row is past `last` is moved back to it arithmetically.
+  __device__ __forceinline__ void issue_one(int j, const bf16 *cb, int last, unsigned rstride,
+                                            TileT &t) {
+    int row, col;
+    slot_rc(j, row, col);
+    const int dr = max(row - last, 0);
+    dma_lds16_at(seg(t, j), cb, off[j] - (unsigned)dr * rstride);
+  }
   // Rows [r0, r0 + ROWS) of a matrix with `stride` (the one given to init) and
   // `nrows` rows; rows past the end repeat the last row.  r0 < nrows.
   __device__ __forceinline__ void issue(const bf16 *base, int64_t stride, int r0, int nrows,

@@ -59,13 +59,22 @@ __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0
 // key's (the rest); dv is not used.  Phase C then issues all P^T dY products of
 // a 32-row step before its dS^T Q products, so two MFMAs into one tile are
 // never adjacent.
-template <typename T, int DK, int DV, bool MASKED, bool MERGE, bool NEGV, typename Adj>
+// dma(k), k < NDMA: the caller's k-th direct-to-LDS load for a later chunk,
+// issued at step k (phase-A steps, then phase-C steps).  A wave stalls on a vector-memory issue while the
+// CU's memory pipe is busy with the other waves' loads; spread one per step,
+// the stalls fall under the running MFMAs instead of in front of them.
+struct NoDma {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+
+template <typename T, int DK, int DV, bool MASKED, bool MERGE, bool NEGV, int NDMA = 0,
+          typename Adj, typename Dma = NoDma>
 __device__ __forceinline__ void kv_chunk(const typename MT<T>::frag *kf,
                                          const typename MT<T>::frag *vf, f32x16 *dk, f32x16 *dv,
                                          const Tile<T, DK, KvShape<T>::ROWS> *Qc,
                                          const Tile<T, DV, KvShape<T>::ROWS> *Gc,
                                          const float *nls, const float *dst, float scale_log2,
-                                         int lane, Adj adj, float ds_scale = 1.f) {
+                                         int lane, Adj adj, float ds_scale = 1.f, Dma dma = Dma()) {
   typedef MT<T> M;
   typedef typename M::frag F;
   static_assert(DV <= DK && DV % 32 == 0 && DK % 32 == 0, "widths");
@@ -74,6 +83,7 @@ __device__ __forceinline__ void kv_chunk(const typename MT<T>::frag *kf,
   constexpr int NA = NSUB * NSD;    // phase-A steps (S, and dP while s < NSV)
   constexpr int NC = NSUB * CS * NT;  // phase-C steps (dK, and dV while t < NTV)
   constexpr int RING = 4;
+  static_assert(NDMA <= NA + NC, "one load per step");
   const int l32 = lane & 31, half = lane >> 5;
 
   f32x16 sacc[NSUB], pacc[NSUB];
@@ -135,6 +145,7 @@ __device__ __forceinline__ void kv_chunk(const typename MT<T>::frag *kf,
     const int u = a / NSD, s = a % NSD;
     sched_fence();
     if (a + RING - 1 < NA) load_a(a + RING - 1);
+    if (a < NDMA) dma(a);
     // the next sub-tile's statistics, two steps before its first MFMA
     if (u + 1 < NSUB && s == NSD - 2) init_acc(u + 1);
     sacc[u] = M::mma(qa[a % RING], kf[s], sacc[u]);
@@ -210,6 +221,7 @@ __device__ __forceinline__ void kv_chunk(const typename MT<T>::frag *kf,
     const int u = c / (CS * NT), st = (c / NT) % CS, t = c % NT;
     sched_fence();
     if (c + RING - 1 < NC) load_c(c + RING - 1);
+    if (NA + c < NDMA) dma(NA + c);
     // The last sub-tile's softmax runs under the first sub-tile's phase C.
     if (NSUB > 1 && u == 0) {
       constexpr int PER = (16 + CS * NT - 1) / (CS * NT);

@@ -21,11 +21,14 @@ template <typename T> struct QShape {
 
 // Phase A for every query block.  The K / V fragments of k-step s are read
 // three steps ahead (a ring of four) and feed the MFMAs of all query blocks.
-template <typename T, int D, int NQB>
+// dma(s), s < NDMA: the caller's s-th direct-to-LDS load for a later chunk,
+// one per step, so a wave's stall on a busy vector-memory pipe falls under
+// its running MFMAs (as in the dK / dV body).
+template <typename T, int D, int NQB, int NDMA = 0, typename Dma = NoDma>
 __device__ __forceinline__ void q_phase_a(const Tile<T, D> *Kc, const Tile<T, D> *Vc,
                                           const typename MT<T>::frag (*qf)[D / MT<T>::KS],
                                           const typename MT<T>::frag (*gf)[D / MT<T>::KS],
-                                          f32x16 *sacc, f32x16 *pacc, int lane) {
+                                          f32x16 *sacc, f32x16 *pacc, int lane, Dma dma = Dma()) {
   typedef MT<T> M;
   constexpr int NSD = D / M::KS, RING = 4;
   const int l32 = lane & 31, half = lane >> 5;
@@ -38,9 +41,11 @@ __device__ __forceinline__ void q_phase_a(const Tile<T, D> *Kc, const Tile<T, D>
   for (int s = 0; s < RING - 1 && s < NSD; ++s) load(s);
 #pragma unroll
   for (int q = 0; q < NQB; ++q) sacc[q] = pacc[q] = f32x16{};
+  static_assert(NDMA <= NSD, "one load per step");
 #pragma unroll
   for (int s = 0; s < NSD; ++s) {
     if (s + RING - 1 < NSD) load(s + RING - 1);
+    if (s < NDMA) dma(s);
 #pragma unroll
     for (int q = 0; q < NQB; ++q) {
       sacc[q] = M::mma(ka[s % RING], qf[q][s], sacc[q]);
