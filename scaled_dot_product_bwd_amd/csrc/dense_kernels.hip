@@ -465,21 +465,38 @@ __global__ __launch_bounds__(256) void k_kv_bwd(const DenseParams p) {
   S.io_g.init(p.dys[1]);
   kv_run<T, D, MODE>(p, S, c_last, j0b, Qs, Gs, st);
 
-  if (!kvalid) return;
-  T *dkrow = (T *)p.dk + b * p.dks[0] + (int64_t)kj * p.dks[1] + g * p.dks[2];
-  T *dvrow = (T *)p.dv + b * p.dvs[0] + (int64_t)kj * p.dvs[1] + g * p.dvs[2];
+  // dK (times the factor of dS, applied once) and dV of the wave's 32 keys.
+  typedef RowStore<T, D> RS;
+  if constexpr (4 * RS::BYTES <= sizeof(Qs) && 4 * RS::BYTES <= sizeof(Gs)) {
+    // whole rows through LDS (the chunk tiles are free once every wave is done)
+    __syncthreads();
+    char *lk = reinterpret_cast<char *>(Qs) + w * RS::BYTES;
+    char *lv = reinterpret_cast<char *>(Gs) + w * RS::BYTES;
+    if (p.need_dk) RS::write_tiles(S.dk, p.scale, lk, S.lane);
+    if (p.need_dv) RS::write_tiles(S.dv, 1.f, lv, S.lane);
+    const int nvalid = max(0, min(32, p.Sk - S.jw));
+    T *dk0 = (T *)p.dk + b * p.dks[0] + (int64_t)S.jw * p.dks[1] + g * p.dks[2];
+    T *dv0 = (T *)p.dv + b * p.dvs[0] + (int64_t)S.jw * p.dvs[1] + g * p.dvs[2];
+    if (p.need_dk) RS::store_rows(lk, nvalid, [&](int n) { return dk0 + (int64_t)n * p.dks[1]; }, S.lane);
+    if (p.need_dv) RS::store_rows(lv, nvalid, [&](int n) { return dv0 + (int64_t)n * p.dvs[1]; }, S.lane);
+  } else {
+    if (!kvalid) return;
+    T *dkrow = (T *)p.dk + b * p.dks[0] + (int64_t)kj * p.dks[1] + g * p.dks[2];
+    T *dvrow = (T *)p.dv + b * p.dvs[0] + (int64_t)kj * p.dvs[1] + g * p.dvs[2];
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d0 = 32 * t + 8 * g + 4 * half;
-      const float sc = p.scale;  // the factor of dS, applied once
-      if (p.need_dk)
-        store4<T>(dkrow + d0, sc * S.dk[t][4 * g], sc * S.dk[t][4 * g + 1], sc * S.dk[t][4 * g + 2],
-                  sc * S.dk[t][4 * g + 3]);
-      if (p.need_dv)
-        store4<T>(dvrow + d0, S.dv[t][4 * g], S.dv[t][4 * g + 1], S.dv[t][4 * g + 2], S.dv[t][4 * g + 3]);
-    }
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * t + 8 * g + 4 * half;
+        const float sc = p.scale;
+        if (p.need_dk)
+          store4<T>(dkrow + d0, sc * S.dk[t][4 * g], sc * S.dk[t][4 * g + 1], sc * S.dk[t][4 * g + 2],
+                    sc * S.dk[t][4 * g + 3]);
+        if (p.need_dv)
+          store4<T>(dvrow + d0, S.dv[t][4 * g], S.dv[t][4 * g + 1], S.dv[t][4 * g + 2],
+                    S.dv[t][4 * g + 3]);
+      }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -601,17 +618,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   wait_vmem();  // the repeated loads of the last steps land before the workgroup ends
 
   const float sc = p.scale;  // the factor of dS, applied once
+  typedef RowStore<T, D> RS;
+  if constexpr (NQB == 1 && 4 * RS::BYTES <= sizeof(Ks)) {
+    // whole rows through LDS (the chunk tiles are free once every wave is done)
+    __syncthreads();
+    char *lq = reinterpret_cast<char *>(Ks) + w * RS::BYTES;
+    RS::write_tiles(S.dq[0], sc, lq, S.lane);
+    const int q0 = i0 + 32 * w;
+    T *dq0 = (T *)p.dq + b * p.dqs[0] + (int64_t)q0 * p.dqs[1] + h * p.dqs[2];
+    RS::store_rows(lq, max(0, min(32, p.Sq - q0)), [&](int n) { return dq0 + (int64_t)n * p.dqs[1]; },
+                   S.lane);
+  } else {
 #pragma unroll
-  for (int q = 0; q < NQB; ++q) {
-    const int qi = S.qi[q];
-    if (qi >= p.Sq) continue;
-    T *dqrow = (T *)p.dq + b * p.dqs[0] + (int64_t)qi * p.dqs[1] + h * p.dqs[2];
+    for (int q = 0; q < NQB; ++q) {
+      const int qi = S.qi[q];
+      if (qi >= p.Sq) continue;
+      T *dqrow = (T *)p.dq + b * p.dqs[0] + (int64_t)qi * p.dqs[1] + h * p.dqs[2];
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        store4<T>(dqrow + 32 * t + 8 * g + 4 * half, sc * S.dq[q][t][4 * g], sc * S.dq[q][t][4 * g + 1],
-                  sc * S.dq[q][t][4 * g + 2], sc * S.dq[q][t][4 * g + 3]);
+        for (int g = 0; g < 4; ++g)
+          store4<T>(dqrow + 32 * t + 8 * g + 4 * half, sc * S.dq[q][t][4 * g],
+                    sc * S.dq[q][t][4 * g + 1], sc * S.dq[q][t][4 * g + 2],
+                    sc * S.dq[q][t][4 * g + 3]);
+    }
   }
 }
 

@@ -419,4 +419,40 @@ template <> __device__ __forceinline__ void store4<float>(float *dst, float a, f
   *reinterpret_cast<f32x4 *>(dst) = f32x4{a, b, c, d};
 }
 
+// Stores a wave's accumulator tiles acc[D / 32] -- lane column n = l32 is row n
+// of the output, tile t's element r is column 32 t + kr(r, half) -- times
+// `scale` as rows 0 .. nvalid - 1 of a [32, D] matrix of T whose row n starts
+// at rowptr(n).  Straight from the C layout each store instruction would
+// scatter 64 small pieces over 32 rows; instead the wave writes the tiles to
+// `lds` (its own 32 * (D * sizeof(T) + 16) bytes, 16-byte aligned, free) and
+// reads them back row-major, so every lane stores 16 contiguous bytes and
+// consecutive lanes fill whole rows.  The caller synchronises the wave's LDS
+// (a barrier) between writes and reads: write_tiles(), barrier, store_rows().
+template <typename T, int D> struct RowStore {
+  static constexpr int ES = sizeof(T), RB = D * ES + 16;  // padded row bytes
+  static constexpr int BYTES = 32 * RB;
+  static constexpr int LPR = D * ES / 16, RPI = 64 / LPR;  // lanes per row, rows per instruction
+  __device__ __forceinline__ static void write_tiles(const f32x16 *acc, float scale, char *lds,
+                                                     int lane) {
+    const int l32 = lane & 31, half = lane >> 5;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        store4<T>(reinterpret_cast<T *>(lds + l32 * RB) + 32 * t + 8 * g + 4 * half,
+                  scale * acc[t][4 * g], scale * acc[t][4 * g + 1], scale * acc[t][4 * g + 2],
+                  scale * acc[t][4 * g + 3]);
+  }
+  template <typename F>
+  __device__ __forceinline__ static void store_rows(const char *lds, int nvalid, F rowptr, int lane) {
+    const int c = lane % LPR;
+#pragma unroll
+    for (int it = 0; it < 32 / RPI; ++it) {
+      const int n = it * RPI + lane / LPR;
+      const f32x4 x = *reinterpret_cast<const f32x4 *>(lds + n * RB + 16 * c);
+      if (n < nvalid) *reinterpret_cast<f32x4 *>(reinterpret_cast<char *>(rowptr(n)) + 16 * c) = x;
+    }
+  }
+};
+
 }  // namespace attn
