@@ -426,7 +426,7 @@ template <> __device__ __forceinline__ void store4<float>(float *dst, float a, f
 // scatter 64 small pieces over 32 rows; instead the wave writes the tiles to
 // `lds` (its own 32 * (D * sizeof(T) + 16) bytes, 16-byte aligned, free) and
 // reads them back row-major, so every lane stores 16 contiguous bytes and
-// consecutive lanes fill whole rows.  The caller synchronises the wave's LDS
+// consecutive lanes fill whole rows.  `scale` may differ per lane (row).  The caller synchronises the wave's LDS
 // (a barrier) between writes and reads: write_tiles(), barrier, store_rows().
 template <typename T, int D> struct RowStore {
   static constexpr int ES = sizeof(T), RB = D * ES + 16;  // padded row bytes
@@ -450,7 +450,8 @@ template <typename T, int D> struct RowStore {
     for (int it = 0; it < 32 / RPI; ++it) {
       const int n = it * RPI + lane / LPR;
       const f32x4 x = *reinterpret_cast<const f32x4 *>(lds + n * RB + 16 * c);
-      if (n < nvalid) *reinterpret_cast<f32x4 *>(reinterpret_cast<char *>(rowptr(n)) + 16 * c) = x;
+      T *dst = n < nvalid ? rowptr(n) : nullptr;  // rowptr may return nullptr: no such row
+      if (dst) *reinterpret_cast<f32x4 *>(reinterpret_cast<char *>(dst) + 16 * c) = x;
     }
   }
 };

@@ -256,8 +256,55 @@ __global__ __launch_bounds__(256) void k_paged_kv_bwd(const PagedParams p) {
     paged_run(p, S, masked, Qs, Gs, st, ri);
   }
 
-  if (ent < 0) return;
+  // One store per (slot, KV head) element: the gradient, +0 for a tail slot;
+  // unused lanes (no slot) store nothing.  Whole rows through LDS when the
+  // staging fits the chunk tiles (free once every wave is done).
   const float sc = live ? p.scale : 0.f;  // dS's factor, applied once; tails store +0
+  typedef RowStore<T, D> RSd;
+  typedef RowStore<T, (P > 0 ? P : 32)> RSp;
+  if constexpr (4 * (RSd::BYTES + (MLA && P > 0 ? RSp::BYTES : 0)) <= sizeof(Qs) &&
+                4 * RSd::BYTES <= sizeof(Gs)) {
+    __syncthreads();
+    char *l0 = reinterpret_cast<char *>(Qs) + S.wave * RSd::BYTES;
+    char *lp = reinterpret_cast<char *>(Qs) + 4 * RSd::BYTES + S.wave * RSp::BYTES;
+    char *l1 = reinterpret_cast<char *>(Gs) + S.wave * RSd::BYTES;
+    const int32_t *slot_ent = plan + p.off_item_slots + item * plan::kItemSlots + 32 * S.wave;
+    auto row_of = [&](int n) -> int64_t {  // pool row of the wave's lane n, -1 for no slot
+      const int e = slot_ent[n];
+      return e < 0 ? -1 : (int64_t)(e >> 1) * p.kv_heads + g;
+    };
+    if constexpr (MLA) {
+      // dk holds both derivatives already scaled: the latent's tiles, then the position key's
+      if (p.need_dk) RSd::write_tiles(S.dk, live ? 1.f : 0.f, l0, S.lane);
+      if (P > 0 && p.need_dkp)
+        RSp::write_tiles(S.dk + D / 32, live ? 1.f : 0.f, lp, S.lane);
+      if (p.need_dk)
+        RSd::store_rows(l0, 32, [&](int n) -> T * {
+          const int64_t r = row_of(n);
+          return r < 0 ? nullptr : (T *)p.dk_pool + r * D;
+        }, S.lane);
+      if (P > 0 && p.need_dkp)
+        RSp::store_rows(lp, 32, [&](int n) -> T * {
+          const int64_t r = row_of(n);
+          return r < 0 ? nullptr : (T *)p.dkp_pool + r * P;
+        }, S.lane);
+    } else {
+      if (p.need_dk) RSd::write_tiles(S.dk, sc, l0, S.lane);
+      if (p.need_dv) RSd::write_tiles(S.dv, live ? 1.f : 0.f, l1, S.lane);
+      if (p.need_dk)
+        RSd::store_rows(l0, 32, [&](int n) -> T * {
+          const int64_t r = row_of(n);
+          return r < 0 ? nullptr : (T *)p.dk_pool + r * D;
+        }, S.lane);
+      if (p.need_dv)
+        RSd::store_rows(l1, 32, [&](int n) -> T * {
+          const int64_t r = row_of(n);
+          return r < 0 ? nullptr : (T *)p.dv_pool + r * D;
+        }, S.lane);
+    }
+    return;
+  }
+  if (ent < 0) return;
   if constexpr (MLA) {
     // dS was scaled before its products: dk holds the latent's gradient (both
     // derivatives) and then the position key's; tails store +0
