@@ -54,9 +54,9 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # MI355X dense MFMA peaks
 HBM_PEAK_GBS = 8000.0
 # Contractions each kernel issues per visible (query, key) pair, 2 D flops each.
-CONTRACTIONS = {"row_stats": 2, "kv": 4, "dq": 3}
+CONTRACTIONS = {"row_stats": 2, "kv": 4, "dq": 3, "stats_dq": 4}
 KERNEL_NAMES = {"row_stats": "k_row_stats", "kv": "k_kv_bwd", "dq": "k_dq_bwd",
-                "paged": "k_paged_kv_bwd"}
+                "stats_dq": "k_stats_dq", "paged": "k_paged_kv_bwd"}
 # Files whose content decides a kernel's code (a stored traffic measurement is
 # used only while their hash is unchanged).
 KERNEL_SOURCES = ["scaled_dot_product_bwd_amd/csrc/dense_kernels.hip",
@@ -518,7 +518,8 @@ def main():
     dq, dk, dv = (torch.empty_like(x) for x in (q, k, v))
     ws = torch.empty(sdb.workspace_bytes(B, H, S), dtype=torch.uint8, device=dev)
     a = sdb.make_args(q, k, v, dy, dq, dk, dv, mask_kind=args.mask, window=window, workspace=ws)
-    stages = ["row_stats", "kv", "dq"]
+    # attn_bwd's bf16 sequence: statistics and dQ in one pass, then dK / dV.
+    stages = ["stats_dq", "kv"]
 
     def step(ev=None):
         for i, st in enumerate(stages):

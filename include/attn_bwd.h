@@ -109,8 +109,10 @@ typedef struct attn_bwd_args {
  * delta = 0.  Returns 0 for negative sizes. */
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq);
 
-/* The whole dense backward: row statistics, then dK / dV, then dQ, as `wrt`
- * asks.  Every element of every requested output is written (no pre-zeroing
+/* The whole dense backward, as `wrt` asks.  bf16: one query-major pass
+ * computes the row statistics and dQ together (attn_bwd_stats_dq), then the
+ * KV-major pass writes dK / dV.  fp32: row statistics, dK / dV, dQ (the three
+ * stages below).  Every element of every requested output is written (no pre-zeroing
  * needed, as rlx-cpu `attention_backward_all`); no output may overlap any
  * input, another output or the workspace.  B, H, Sq or Sk = 0 is valid: the
  * requested outputs that have elements are then written with zeros. */
@@ -123,6 +125,16 @@ int attn_bwd(const attn_bwd_args *a, void *stream);
 int attn_bwd_row_stats(const attn_bwd_args *a, void *stream);
 int attn_bwd_kv(const attn_bwd_args *a, void *stream);
 int attn_bwd_dq(const attn_bwd_args *a, void *stream);
+
+/* Row statistics and dQ in one query-major pass (rlx-cpu
+ * `backward_dense_head_all`: dS = P (dP - rowsum(P dP)) scale, dQ = dS K,
+ * with rowsum(P dP) found in the same pass: dQ_i = scale (A_i - delta_i B_i)
+ * / l_i, A_i = sum_j p~_ij dP_ij K_j, B_i = sum_j p~_ij K_j).  Same arguments
+ * and validation as attn_bwd.  It fills the workspace statistics exactly as
+ * attn_bwd_row_stats does (bit for bit) and writes dQ if `wrt` asks for it;
+ * attn_bwd_kv may follow on the same stream.  bf16 runs one kernel; fp32 runs
+ * attn_bwd_row_stats then attn_bwd_dq. */
+int attn_bwd_stats_dq(const attn_bwd_args *a, void *stream);
 
 /* ------------------------------------------------------------------------
  * Paged, grouped-query history backward (dK / dV only), ruDNN 0.1.43

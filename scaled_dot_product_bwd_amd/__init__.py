@@ -105,11 +105,11 @@ def _stream_handle(stream):
 
 
 def attn_bwd_stage(stage: str, args: AttnBwdArgs, stream=None):
-    """Runs one stage ("all", "row_stats", "kv" or "dq") of the backward on the
-    given (default: current) torch stream."""
+    """Runs one stage ("all", "row_stats", "kv", "dq" or "stats_dq") of the
+    backward on the given (default: current) torch stream."""
     lib = load_library()
     fn = {"all": lib.attn_bwd, "row_stats": lib.attn_bwd_row_stats, "kv": lib.attn_bwd_kv,
-          "dq": lib.attn_bwd_dq}[stage]
+          "dq": lib.attn_bwd_dq, "stats_dq": lib.attn_bwd_stats_dq}[stage]
     _check(fn(ctypes.byref(args), _stream_handle(stream)))
 
 

@@ -22,7 +22,7 @@ STATUS_NAMES = {ATTN_E_INVALID: "ATTN_E_INVALID", ATTN_E_UNSUPPORTED: "ATTN_E_UN
 
 # Every symbol include/attn_bwd.h declares.
 EXPORTED = ["attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_row_stats", "attn_bwd_kv",
-            "attn_bwd_dq", "attn_bwd_paged_plan_words", "attn_bwd_paged_plan_build",
+            "attn_bwd_dq", "attn_bwd_stats_dq", "attn_bwd_paged_plan_words", "attn_bwd_paged_plan_build",
             "attn_bwd_paged", "attn_bwd_paged_row_stats", "attn_bwd_paged_dq",
             "attn_bwd_from_forward", "attn_bwd_paged_q_workspace_bytes",
             "attn_bwd_last_error"]
@@ -104,7 +104,8 @@ def load_library():
     lib = ctypes.CDLL(path)
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_bwd_workspace_bytes.argtypes = [ctypes.c_int64] * 3
-    for name in ("attn_bwd", "attn_bwd_row_stats", "attn_bwd_kv", "attn_bwd_dq"):
+    for name in ("attn_bwd", "attn_bwd_row_stats", "attn_bwd_kv", "attn_bwd_dq",
+                 "attn_bwd_stats_dq"):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [ctypes.POINTER(AttnBwdArgs), ctypes.c_void_p]

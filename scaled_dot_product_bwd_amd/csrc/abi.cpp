@@ -250,8 +250,13 @@ int run_stage(int stage, Checked &c, hipStream_t stream) {
     if (!(c.want_k || c.want_v) || p.Sk == 0) return ATTN_OK;
     p.nblk = c.nblk_k;
     nblocks = p.B * p.Hkv * c.nblk_k;  // one key block of one K / V head each
-  } else {
+  } else if (stage == attn::STAGE_DQ) {
     if (!c.want_q || p.Sq == 0) return ATTN_OK;
+    p.nblk = c.nblk_q;
+    nblocks = heads * c.nblk_q;
+  } else {  // STAGE_STATS_DQ (bf16): statistics always, dQ if asked
+    if (p.Sq == 0 || !(c.want_q || c.want_k || c.want_v)) return ATTN_OK;
+    if (!c.want_q) p.dq = nullptr;
     p.nblk = c.nblk_q;
     nblocks = heads * c.nblk_q;
   }
@@ -539,8 +544,32 @@ size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq) {
   return 4 * plane_bytes(B, H, Sq);
 }
 
-int attn_bwd(const attn_bwd_args *a, void *stream) {
-  return run(a, stream, attn::STAGE_ROW_STATS, attn::STAGE_DQ);
+// bf16: one query-major pass for the statistics and dQ, then dK / dV.
+// fp32: statistics, dK / dV, dQ (three passes; dQ from the exact delta).
+static int run_all(const attn_bwd_args *a, void *stream) {
+  Checked c;
+  const int rc = validate(a, c);
+  if (rc != ATTN_OK) return rc;
+  static const int bf16_order[] = {attn::STAGE_STATS_DQ, attn::STAGE_KV};
+  static const int f32_order[] = {attn::STAGE_ROW_STATS, attn::STAGE_KV, attn::STAGE_DQ};
+  const int *order = c.bf16 ? bf16_order : f32_order;
+  const int n = c.bf16 ? 2 : 3;
+  for (int i = 0; i < n; ++i) {
+    const int r = run_stage(order[i], c, (hipStream_t)stream);
+    if (r != ATTN_OK) return r;
+  }
+  return ATTN_OK;
+}
+
+int attn_bwd(const attn_bwd_args *a, void *stream) { return run_all(a, stream); }
+
+int attn_bwd_stats_dq(const attn_bwd_args *a, void *stream) {
+  Checked c;
+  const int rc = validate(a, c);
+  if (rc != ATTN_OK) return rc;
+  if (c.bf16) return run_stage(attn::STAGE_STATS_DQ, c, (hipStream_t)stream);
+  const int r = run_stage(attn::STAGE_ROW_STATS, c, (hipStream_t)stream);
+  return r != ATTN_OK ? r : run_stage(attn::STAGE_DQ, c, (hipStream_t)stream);
 }
 
 int attn_bwd_row_stats(const attn_bwd_args *a, void *stream) {

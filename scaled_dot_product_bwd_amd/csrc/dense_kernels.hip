@@ -81,16 +81,23 @@ __device__ __forceinline__ auto q_next_chunk_dma(const DenseParams &p, ChunkIO<T
   };
 }
 
+__device__ __forceinline__ void store_row_stat(const DenseParams &p, int64_t row, const RowStatOut &o) {
+  p.st_m[row] = o.m;
+  p.st_l[row] = o.l;
+  p.st_delta[row] = o.delta;
+  p.st_nls[row] = o.nls;
+}
+
 // ---------------------------------------------------------------------------
-// Row statistics.  Per query row: the running max m (log2 domain), the
-// denominator l = sum 2^(s - m) and delta' = sum 2^(s - m) dP, rescaled
-// together whenever m grows; at the end delta = delta' / l = rowsum(P * dP)
-// (rlx-cpu `backward_dense_head_all`), with dP = dY V^T from phase A.
+// Row statistics.  Per query row: the denominator l = sum 2^(s - mref) and
+// delta' = sum 2^(s - mref) dP against a lazily moved reference max (RowStat);
+// at the end delta = delta' / l = rowsum(P * dP) (rlx-cpu
+// `backward_dense_head_all`), with dP = dY V^T from phase A.
 template <typename T, int D> struct RsState {
   typedef MT<T> M;
   static constexpr int NSD = D / M::KS, NQB = QShape<T>::NQB;
   typename M::frag qf[NQB][NSD], gf[NQB][NSD];
-  float m[NQB], l[NQB], dl[NQB];
+  RowStat st[NQB];
   int qi[NQB];
   ChunkIO<T, D> io_k, io_v;
   const T *kbase, *vbase;
@@ -138,23 +145,9 @@ __device__ __forceinline__ void rs_step(const DenseParams &p, RsState<T, D> &S, 
 #pragma unroll
       for (int r = 0; r < 16; ++r) s2[r] += q_adj<MODE>(p, S.b, S.h, S.qi[q], j0 + kr(r, half));
     }
-    float mx = s2[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s2[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mn = fmaxf(S.m[q], mx);
-    const float mu = mn == -INFINITY ? 0.f : mn;
-    const float al = fast_exp2(S.m[q] - mu);
-    float ls = 0.f, ds = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float pr = fast_exp2(s2[r] - mu);
-      ls += pr;
-      ds = fmaf(pr, pacc[q][r], ds);
-    }
-    S.l[q] = fmaf(S.l[q], al, ls);
-    S.dl[q] = fmaf(S.dl[q], al, ds);
-    S.m[q] = mn;
+    float pr[16];
+    bool moved;
+    row_stat_chunk(S.st[q], s2, pacc[q], pr, moved);
   }
   if (issued) {
     S.io_k.complete(Ks[bn]);
@@ -227,8 +220,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
       S.qf[q][s] = load_frag<T>(qrow, s * KS + half * KL, qvalid);
       S.gf[q][s] = load_frag<T>(grow, s * KS + half * KL, qvalid);
     }
-    S.m[q] = -INFINITY;
-    S.l[q] = S.dl[q] = 0.f;
+    S.st[q].init();
   }
   S.kbase = (const T *)p.k + b * p.ks[0] + (h / p.G) * p.ks[2];  // the head's K / V head
   S.vbase = (const T *)p.v + b * p.vs[0] + (h / p.G) * p.vs[2];
@@ -244,17 +236,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 
 #pragma unroll
   for (int q = 0; q < NQB; ++q) {
-    const float l_tot = S.l[q] + __shfl_xor(S.l[q], 32);
-    const float d_tot = S.dl[q] + __shfl_xor(S.dl[q], 32);
+    const RowStatOut o = row_stat_final(S.st[q], p.inv_scale_log2);
     const int qi = S.qi[q];
-    if (qi < p.Sq && half == 0) {
-      const int64_t row = ((int64_t)b * p.H + h) * p.Sq + qi;
-      const bool empty = !(l_tot > 0.f);
-      p.st_m[row] = empty ? -INFINITY : S.m[q] * kLn2;
-      p.st_l[row] = empty ? 0.f : l_tot;
-      p.st_delta[row] = empty ? 0.f : d_tot / l_tot;
-      p.st_nls[row] = (empty ? -INFINITY : -(S.m[q] + __log2f(l_tot))) * p.inv_scale_log2;
-    }
+    if (qi < p.Sq && half == 0) store_row_stat(p, ((int64_t)b * p.H + h) * p.Sq + qi, o);
   }
 }
 
@@ -646,6 +630,183 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ---------------------------------------------------------------------------
+// Row statistics and dQ in one query-major pass (bf16).  Per 32-key chunk,
+// after S^T and dP^T (phase A) and the online statistics (RowStat, reference
+// mref):
+//   A^T += K^T (P~ * (dP - dh))^T,   B^T += K^T P~^T,   P~ = 2^(s - mref),
+// both products reading the same transposed K fragment.  In exact arithmetic
+//   dQ_i = scale sum_j P_ij (dP_ij - delta_i) K_j = scale (A_i - delta_i B_i) / l_i
+// with delta_i = dl_i / l_i (rlx-cpu `backward_dense_head_all`: dS = P (dP -
+// rowsum(P dP)) scale, dQ = dS K), so the statistics need no pass of their
+// own: four contractions per visible pair instead of the statistics pass's
+// two plus the dQ pass's three, and K / V stream through LDS once.  When a
+// row's mref moves, its A and B are rescaled with l.
+// Rounding: A - delta B cancels where one key dominates a row (dP ~ delta), and
+// the bf16 rounding of P~ dP would then dominate dQ.  So A carries
+// A' = sum P~ (dP - dh) K with dh the running estimate of delta (this chunk
+// included): each chunk first moves A' to the new estimate (A' += (dh_old -
+// dh) B, fp32), then adds P~ (dP - dh) K, the difference formed in fp32 before
+// the bf16 rounding as in the dQ pass.  After the last chunk dh is delta.  The statistics are
+// stored exactly as the row-statistics kernel stores them (same arithmetic,
+// same chunk order), so the dK / dV pass sees the same bits either way.
+constexpr int kSdRing = 4;  // phase-A fragment ring of the fused pass
+
+template <typename T, int D> struct SdState {
+  typedef MT<T> M;
+  static constexpr int NSD = D / M::KS, NT = D / 32;
+  typename M::frag qf[1][NSD], gf[1][NSD];
+  f32x16 acc_a[NT], acc_b[NT];
+  RowStat st;
+  float dh;  // the estimate of delta that acc_a currently subtracts
+  int qi;
+  ChunkIO<T, D> io_k, io_v;
+  const T *kbase, *vbase;
+  int b, h, lane, half, c_last, buf;
+};
+
+template <typename T, int D, int MODE>
+__device__ __forceinline__ void sd_step(const DenseParams &p, SdState<T, D> &S, int c,
+                                        Tile<T, D> *Ks, Tile<T, D> *Vs, bool masked) {
+  typedef MT<T> M;
+  constexpr int NT = D / 32, CS = M::CSTEPS;
+  const int bc = S.buf, bn = bc == 0 ? 2 : bc - 1;
+  const bool issued = c + 2 <= S.c_last;
+  constexpr bool SPREAD = ChunkIO<T, D>::DIRECT;
+  auto dma = q_next_chunk_dma<T, D>(p, S.io_k, S.io_v, S.kbase, S.vbase, min(c + 2, S.c_last),
+                                    Ks[bn], Vs[bn]);
+  if (!SPREAD && issued) {
+    S.io_k.issue(S.kbase, p.ks[1], (c + 2) * 32, p.Sk, Ks[bn]);
+    S.io_v.issue(S.vbase, p.vs[1], (c + 2) * 32, p.Sk, Vs[bn]);
+  }
+  f32x16 sacc[1], pacc[1];
+  constexpr int NDMA = SPREAD ? 2 * ChunkIO<T, D>::LOADS : 0;
+  q_phase_a<T, D, 1, NDMA, decltype(dma), kSdRing>(&Ks[bc], &Vs[bc], S.qf, S.gf, sacc, pacc,
+                                                   S.lane, dma);
+  const int j0 = c * 32, half = S.half;
+  float s2[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s2[r] = sacc[0][r] * p.scale_log2;
+  if (MODE != MODE_INDEX || masked) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s2[r] += q_adj<MODE>(p, S.b, S.h, S.qi, j0 + kr(r, half));
+  }
+  float pr[16];
+  bool moved;
+  const float al = row_stat_chunk(S.st, s2, pacc[0], pr, moved);
+  if (__any(moved)) {  // rare after the first visible chunk: wave-uniform branch
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      S.acc_a[t] *= al;
+      S.acc_b[t] *= al;
+    }
+  }
+  // delta's running estimate, this chunk included (the expression
+  // row_stat_final uses, so after the last chunk it is delta itself)
+  const float l_tot = S.st.l + __shfl_xor(S.st.l, 32);
+  const float dl_tot = S.st.dl + __shfl_xor(S.st.dl, 32);
+  const float dh = l_tot > 0.f ? dl_tot / l_tot : 0.f;
+  const float shift = S.dh - dh;
+  S.dh = dh;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S.acc_a[t][r] = fmaf(shift, S.acc_b[t][r], S.acc_a[t][r]);
+  typename M::frag uf[CS], pf[CS];
+#pragma unroll
+  for (int st = 0; st < CS; ++st) {
+    float pd[16 / CS];
+#pragma unroll
+    for (int e = 0; e < 16 / CS; ++e)
+      pd[e] = pr[st * (16 / CS) + e] * (pacc[0][st * (16 / CS) + e] - dh);
+    uf[st] = creuse<T>(pd, 0);
+    pf[st] = creuse<T>(pr, st);
+  }
+  const Tile<T, D> *Kc = &Ks[bc];
+#pragma unroll
+  for (int st = 0; st < CS; ++st) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const typename M::frag kt = Kc->tfrag(32 * t, st, S.lane);
+      S.acc_a[t] = M::mma(kt, uf[st], S.acc_a[t]);
+      S.acc_b[t] = M::mma(kt, pf[st], S.acc_b[t]);
+    }
+  }
+  if (issued) {
+    S.io_k.complete(Ks[bn]);
+    S.io_v.complete(Vs[bn]);
+  }
+  end_step<ChunkIO<T, D>::DIRECT, 2 * ChunkIO<T, D>::LOADS>(SPREAD || issued);
+  S.buf = bc == 2 ? 0 : bc + 1;
+}
+
+template <typename T, int D, int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_stats_dq(const DenseParams p) {
+  typedef MT<T> M;
+  constexpr int KS = M::KS, KL = M::KL, NSD = D / KS, NT = D / 32, QROWS = 128;
+  static_assert(QShape<T>::QROWS == QROWS, "one 32-query block per wave");
+  __shared__ Tile<T, D> Ks[3], Vs[3];
+
+  SdState<T, D> S;
+  const int tid = threadIdx.x, w = tid >> 6;
+  S.lane = tid & 63;
+  S.half = S.lane >> 5;
+  const int l32 = S.lane & 31, half = S.half;
+  const int nb = p.nblk;
+  int bh, rank;
+  tile_order<kDqGroup>(blockIdx.x, gridDim.x, nb, bh, rank);
+  const int blk = nb - 1 - rank;  // the heaviest causal blocks first
+  S.h = bh % p.H;
+  S.b = bh / p.H;
+  const int b = S.b, h = S.h;
+  const int i0 = blk * QROWS;
+  {
+    const int qi = i0 + 32 * w + l32;
+    S.qi = qi;
+    const bool qvalid = qi < p.Sq;
+    const T *qrow = (const T *)p.q + b * p.qs[0] + (int64_t)(qvalid ? qi : 0) * p.qs[1] + h * p.qs[2];
+    const T *grow = (const T *)p.dy + b * p.dys[0] + (int64_t)(qvalid ? qi : 0) * p.dys[1] + h * p.dys[2];
+#pragma unroll
+    for (int s = 0; s < NSD; ++s) {
+      S.qf[0][s] = load_frag<T>(qrow, s * KS + half * KL, qvalid);
+      S.gf[0][s] = load_frag<T>(grow, s * KS + half * KL, qvalid);
+    }
+    S.st.init();
+    S.dh = 0.f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) S.acc_a[t] = S.acc_b[t] = f32x16{};
+  }
+  S.kbase = (const T *)p.k + b * p.ks[0] + (h / p.G) * p.ks[2];  // the head's K / V head
+  S.vbase = (const T *)p.v + b * p.vs[0] + (h / p.G) * p.vs[2];
+  const QRange R = q_range(p, i0, QROWS, MODE == MODE_INDEX);
+  S.c_last = R.c_last;
+  S.io_k.init(p.ks[1]);
+  S.io_v.init(p.vs[1]);
+  q_prologue<T, D>(p, S.io_k, S.io_v, S.kbase, S.vbase, R.c_first, R.c_last, Ks, Vs);
+  S.buf = 0;
+  for (int c = R.c_first; c <= R.c_last; ++c)
+    sd_step<T, D, MODE>(p, S, c, Ks, Vs, c < R.cu0 || c > R.cu1);
+  wait_vmem();  // the repeated loads of the last steps land before the workgroup ends
+
+  const RowStatOut o = row_stat_final(S.st, p.inv_scale_log2);
+  if (S.qi < p.Sq && half == 0) store_row_stat(p, ((int64_t)b * p.H + h) * p.Sq + S.qi, o);
+  if (p.dq == nullptr) return;  // statistics only (dQ not requested)
+
+  // dQ^T = A'^T * scale / l per lane column (row): after the last chunk the
+  // estimate is delta itself (o.delta, bit for bit), so A' = A - delta B.
+  // Whole rows stored through LDS (the chunk tiles are free once every wave
+  // is done).
+  typedef RowStore<T, D> RS;
+  static_assert(4 * RS::BYTES <= sizeof(Ks), "row staging fits the chunk tiles");
+  __syncthreads();
+  char *lq = reinterpret_cast<char *>(Ks) + w * RS::BYTES;
+  RS::write_tiles(S.acc_a, p.scale * o.inv_l, lq, S.lane);
+  const int q0 = i0 + 32 * w;
+  T *dq0 = (T *)p.dq + b * p.dqs[0] + (int64_t)q0 * p.dqs[1] + h * p.dqs[2];
+  RS::store_rows(lq, max(0, min(32, p.Sq - q0)), [&](int n) { return dq0 + (int64_t)n * p.dqs[1]; },
+                 S.lane);
+}
+
+// ---------------------------------------------------------------------------
 // Launchers: one instantiation per (element type, head dim, mask mode).
 
 template <typename T, int D, int MODE>
@@ -654,8 +815,12 @@ static hipError_t launch_t(int stage, const DenseParams &p, int nblocks, hipStre
     hipLaunchKernelGGL((k_row_stats<T, D, MODE>), dim3(nblocks), dim3(256), 0, stream, p);
   else if (stage == STAGE_KV)
     hipLaunchKernelGGL((k_kv_bwd<T, D, MODE>), dim3(nblocks), dim3(256), 0, stream, p);
-  else
+  else if (stage == STAGE_DQ)
     hipLaunchKernelGGL((k_dq_bwd<T, D, MODE>), dim3(nblocks), dim3(256), 0, stream, p);
+  else if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL((k_stats_dq<T, D, MODE>), dim3(nblocks), dim3(256), 0, stream, p);
+  else
+    return hipErrorInvalidValue;  // the fused pass is built for bf16 only
   return hipGetLastError();
 }
 

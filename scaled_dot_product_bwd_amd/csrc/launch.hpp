@@ -7,7 +7,8 @@
 
 namespace attn {
 
-enum { STAGE_ROW_STATS = 0, STAGE_KV = 1, STAGE_DQ = 2 };
+// STAGE_STATS_DQ: row statistics and dQ in one pass (bf16 only).
+enum { STAGE_ROW_STATS = 0, STAGE_KV = 1, STAGE_DQ = 2, STAGE_STATS_DQ = 3 };
 
 // Launches one dense stage over `nblocks` workgroups of 256 threads.
 hipError_t launch_dense_stage(int stage, bool bf16_in, int D, int mode, const DenseParams &p,

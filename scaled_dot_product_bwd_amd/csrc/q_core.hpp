@@ -24,13 +24,14 @@ template <typename T> struct QShape {
 // dma(s), s < NDMA: the caller's s-th direct-to-LDS load for a later chunk,
 // one per step, so a wave's stall on a busy vector-memory pipe falls under
 // its running MFMAs (as in the dK / dV body).
-template <typename T, int D, int NQB, int NDMA = 0, typename Dma = NoDma>
+// RING: fragment registers per operand (reads run RING - 1 steps ahead).
+template <typename T, int D, int NQB, int NDMA = 0, typename Dma = NoDma, int RING = 4>
 __device__ __forceinline__ void q_phase_a(const Tile<T, D> *Kc, const Tile<T, D> *Vc,
                                           const typename MT<T>::frag (*qf)[D / MT<T>::KS],
                                           const typename MT<T>::frag (*gf)[D / MT<T>::KS],
                                           f32x16 *sacc, f32x16 *pacc, int lane, Dma dma = Dma()) {
   typedef MT<T> M;
-  constexpr int NSD = D / M::KS, RING = 4;
+  constexpr int NSD = D / M::KS;
   const int l32 = lane & 31, half = lane >> 5;
   typename M::frag ka[RING], va[RING];
   auto load = [&](int s) {
@@ -81,6 +82,76 @@ __device__ __forceinline__ QRange q_range(const DenseParams &p, int i0, int qrow
     }
   }
   return r;
+}
+
+}  // namespace attn
+
+namespace attn {
+
+// Online row statistics, log2 domain, with a lazily moved reference.
+// Per query row (a lane column; the wave's two halves hold different keys of
+// the same row): l = sum 2^(s - mref) and dl = sum 2^(s - mref) dP over the
+// keys seen so far, where the reference mref moves to a chunk's max only when
+// that max exceeds it by more than kRefSlack.  The terms 2^(s - mref) then
+// stay <= 2^kRefSlack, and after the first visible chunk almost no chunk
+// rescales anything (a caller that carries accumulators in the same scale
+// multiplies them only then).  mtrue is the running max itself.  The row
+// statistics kernel and the fused statistics + dQ kernel both use this
+// arithmetic, in the same chunk order, so their statistics agree bit for bit.
+constexpr float kRefSlack = 8.f;
+
+struct RowStat {
+  float mref, mtrue, l, dl;
+  __device__ __forceinline__ void init() {
+    mref = mtrue = -INFINITY;
+    l = dl = 0.f;
+  }
+};
+
+// One 32-key chunk: s2[r] is the log2-domain score (masked: -inf) of the
+// lane's key r, pacc[r] its dP.  Writes pr[r] = 2^(s2[r] - mref) and returns
+// the factor by which earlier terms were rescaled (1 if mref did not move).
+// `moved` tells whether it did, for this lane's row.
+__device__ __forceinline__ float row_stat_chunk(RowStat &st, const float *s2, const f32x16 &pacc,
+                                                float *pr, bool &moved) {
+  float mx = s2[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s2[r]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  st.mtrue = fmaxf(st.mtrue, mx);
+  moved = mx > st.mref + kRefSlack;  // false while every key so far is hidden
+  const float al = moved ? fast_exp2(st.mref - mx) : 1.f;  // 0 from mref = -inf
+  if (moved) st.mref = mx;
+  const float mu = st.mref == -INFINITY ? 0.f : st.mref;
+  float ls = 0.f, ds = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    pr[r] = fast_exp2(s2[r] - mu);
+    ls += pr[r];
+    ds = fmaf(pr[r], pacc[r], ds);
+  }
+  st.l = fmaf(st.l, al, ls);
+  st.dl = fmaf(st.dl, al, ds);
+  return al;
+}
+
+// Final statistics of a row into the workspace planes (both halves call it;
+// the caller lets one store).  l_tot / dl_tot: the two halves' sums combined.
+struct RowStatOut {
+  float m, l, delta, nls, inv_l;
+  bool empty;
+};
+__device__ __forceinline__ RowStatOut row_stat_final(const RowStat &st, float inv_scale_log2) {
+  RowStatOut o;
+  const float l_tot = st.l + __shfl_xor(st.l, 32);
+  const float d_tot = st.dl + __shfl_xor(st.dl, 32);
+  o.empty = !(l_tot > 0.f);
+  o.m = o.empty ? -INFINITY : st.mtrue * kLn2;
+  o.l = o.empty ? 0.f : l_tot * fast_exp2(st.mref - st.mtrue);
+  o.delta = o.empty ? 0.f : d_tot / l_tot;
+  o.nls = (o.empty ? -INFINITY : -(st.mref + __log2f(l_tot))) * inv_scale_log2;
+  o.inv_l = o.empty ? 0.f : 1.f / l_tot;
+  return o;
 }
 
 }  // namespace attn

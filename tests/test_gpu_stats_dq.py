@@ -1,0 +1,101 @@
+"""GPU tests of the fused query-major pass (row statistics and dQ together,
+attn_bwd_stats_dq; bf16), which attn_bwd uses for bf16 inputs.
+
+dQ comes out as scale (A - delta B) / l with A = sum p~ dP K and B = sum p~ K
+accumulated against a lazily moved reference max; these tests check it
+against the oracle where that reference moves at every chunk (scores rising
+steeply with the key index), on rows dominated by one key (where A - delta B
+cancels), under every mask kind, and that its statistics equal the
+row-statistics kernel's bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import sdpa_inputs
+import scaled_dot_product_bwd_amd as sdb
+from gpu_helpers import assert_parity, gpu_run, oracle_run
+
+pytestmark = pytest.mark.gpu
+
+BF = torch.bfloat16
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_reference_max_moves_every_chunk(causal):
+    """A bias rising 0.4 per key lifts a row's max by ~18 log2 units per 32-key
+    chunk, so the reference moves (and A, B, l are rescaled) at every chunk."""
+    B, H, S, D = 1, 2, 320, 64
+    q, k, v, dy, _ = sdpa_inputs.dense_inputs(B, S, S, H, D, seed=11, dtype=BF)
+    bias = (0.4 * torch.arange(S, dtype=torch.float32)).expand(B, H, S, S).contiguous()
+    res = gpu_run(q, k, v, dy, mask_kind="bias", mask=bias, causal=causal)
+    ref = oracle_run(q, k, v, dy, mask_kind="bias", mask=bias, causal=causal)
+    print(causal, assert_parity(res, ref, BF, label=f"rising bias causal={causal}"))
+
+
+@pytest.mark.parametrize("qscale", [4.0, 8.0])
+def test_peaked_rows(qscale):
+    """Large |q|: most rows are dominated by one key (dP ~ delta there), where
+    A - delta B cancels; dQ must stay as accurate as the three-pass path."""
+    B, H, S, D = 1, 2, 320, 64
+    q, k, v, dy, _ = sdpa_inputs.dense_inputs(B, S, S, H, D, seed=5, dtype=torch.float64)
+    q, k, v, dy = ((qscale * q).to(BF), k.to(BF), v.to(BF), dy.to(BF))
+    for mask in ("none", "causal"):
+        res = gpu_run(q, k, v, dy, mask_kind=mask)
+        ref = oracle_run(q, k, v, dy, mask_kind=mask)
+        print(qscale, mask, assert_parity(res, ref, BF, label=f"peaked x{qscale} {mask}"))
+
+
+@pytest.mark.parametrize("mask,window", [("window", 40), ("keypad", 0), ("bias", 0)])
+def test_masks_bf16(mask, window):
+    B, H, Sq, Sk, D = 2, 2, 150, 290, 128
+    q, k, v, dy, _ = sdpa_inputs.dense_inputs(B, Sq, Sk, H, D, seed=123, dtype=BF)
+    m = None
+    if mask == "keypad":
+        m = torch.ones(B, 1, 1, Sk)
+        m[0, ..., 200:] = 0.0
+        m[1, ..., :17] = 0.0
+    elif mask == "bias":
+        g = torch.Generator().manual_seed(9)
+        m = torch.randn(B, H, Sq, Sk, generator=g, dtype=torch.float64).float()
+    res = gpu_run(q, k, v, dy, mask_kind=mask, window=window, mask=m, causal=mask != "window")
+    ref = oracle_run(q, k, v, dy, mask_kind=mask, window=window, mask=m, causal=mask != "window")
+    print(mask, assert_parity(res, ref, BF, label=mask))
+
+
+@pytest.mark.parametrize("D", [32, 64, 128])
+def test_statistics_match_row_stats_kernel_bitwise(D):
+    """attn_bwd_stats_dq and attn_bwd_row_stats fill the workspace with the same
+    bits, so dK / dV do not depend on which of them ran."""
+    B, S, H = 2, 333, 3
+    q, k, v, dy, _ = sdpa_inputs.dense_inputs(B, S, S, H, D, seed=40 + D, dtype=BF)
+    dev = torch.device("cuda:0")
+    qd, kd, vd, gd = (x.to(dev) for x in (q, k, v, dy))
+    outs = [torch.empty_like(x) for x in (qd, kd, vd)]
+    ws = []
+    for stage in ("stats_dq", "row_stats"):
+        w = torch.full((sdb.workspace_bytes(B, H, S),), 0xFF, dtype=torch.uint8, device=dev)
+        a = sdb.make_args(qd, kd, vd, gd, *outs, mask_kind="causal", workspace=w)
+        sdb.attn_bwd_stage(stage, a)
+        ws.append(w)
+    torch.cuda.synchronize()
+    assert torch.equal(ws[0], ws[1])
+
+
+def test_dq_only_and_stats_only_calls():
+    """wrt=K runs the fused pass without its dQ store: dQ memory is untouched."""
+    B, S, H, D = 1, 200, 2, 64
+    q, k, v, dy, _ = sdpa_inputs.dense_inputs(B, S, S, H, D, seed=3, dtype=BF)
+    dev = torch.device("cuda:0")
+    qd, kd, vd, gd = (x.to(dev) for x in (q, k, v, dy))
+    dq = torch.full_like(qd, 7.0)
+    dk, dv = torch.empty_like(kd), torch.empty_like(vd)
+    w = torch.empty(sdb.workspace_bytes(B, H, S), dtype=torch.uint8, device=dev)
+    a = sdb.make_args(qd, kd, vd, gd, dq, dk, dv, mask_kind="causal", workspace=w, wrt="k")
+    sdb.attn_bwd_stage("all", a)
+    torch.cuda.synchronize()
+    assert torch.all(dq == 7.0)
+    ref = oracle_run(q, k, v, dy, mask_kind="causal")
+    full = gpu_run(q, k, v, dy, mask_kind="causal")
+    assert np.array_equal(dk.float().cpu().double().numpy(), full["dk"])
+    assert_parity(full, ref, BF)
