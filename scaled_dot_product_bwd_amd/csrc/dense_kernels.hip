@@ -136,18 +136,14 @@ __device__ __forceinline__ void rs_step(const DenseParams &p, RsState<T, D> &S, 
   q_phase_a<T, D, NQB, SPREAD ? 2 * ChunkIO<T, D>::LOADS : 0>(&Ks[bc], &Vs[bc], S.qf, S.gf, sacc,
                                                               pacc, S.lane, dma);
   const int j0 = c * 32, half = S.half;
+  const bool plain = MODE == MODE_INDEX && !masked && p.scale_log2 > 0.f;
 #pragma unroll
   for (int q = 0; q < NQB; ++q) {
-    float s2[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s2[r] = sacc[q][r] * p.scale_log2;
-    if (MODE != MODE_INDEX || masked) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s2[r] += q_adj<MODE>(p, S.b, S.h, S.qi[q], j0 + kr(r, half));
-    }
     float pr[16];
     bool moved;
-    row_stat_chunk(S.st[q], s2, pacc[q], pr, moved);
+    row_stat_chunk(S.st[q], sacc[q], pacc[q], p.scale_log2, plain,
+                   [&](int r) { return q_adj<MODE>(p, S.b, S.h, S.qi[q], j0 + kr(r, half)); },
+                   pr, moved);
   }
   if (issued) {
     S.io_k.complete(Ks[bn]);
@@ -664,12 +660,15 @@ template <typename T, int D> struct SdState {
   int b, h, lane, half, c_last, buf;
 };
 
-template <typename T, int D, int MODE>
+// Chunk c, whose tiles are in buffer BC (chunk c + 2 goes to the buffer chunk
+// c - 1 used); the caller unrolls the chunk loop by three, so every LDS
+// address is a base plus a compile-time offset.
+template <typename T, int D, int MODE, int BC>
 __device__ __forceinline__ void sd_step(const DenseParams &p, SdState<T, D> &S, int c,
                                         Tile<T, D> *Ks, Tile<T, D> *Vs, bool masked) {
   typedef MT<T> M;
   constexpr int NT = D / 32, CS = M::CSTEPS;
-  const int bc = S.buf, bn = bc == 0 ? 2 : bc - 1;
+  constexpr int bc = BC, bn = (BC + 2) % 3;
   const bool issued = c + 2 <= S.c_last;
   constexpr bool SPREAD = ChunkIO<T, D>::DIRECT;
   auto dma = q_next_chunk_dma<T, D>(p, S.io_k, S.io_v, S.kbase, S.vbase, min(c + 2, S.c_last),
@@ -683,16 +682,12 @@ __device__ __forceinline__ void sd_step(const DenseParams &p, SdState<T, D> &S, 
   q_phase_a<T, D, 1, NDMA, decltype(dma), kSdRing>(&Ks[bc], &Vs[bc], S.qf, S.gf, sacc, pacc,
                                                    S.lane, dma);
   const int j0 = c * 32, half = S.half;
-  float s2[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) s2[r] = sacc[0][r] * p.scale_log2;
-  if (MODE != MODE_INDEX || masked) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s2[r] += q_adj<MODE>(p, S.b, S.h, S.qi, j0 + kr(r, half));
-  }
+  const bool plain = MODE == MODE_INDEX && !masked && p.scale_log2 > 0.f;
   float pr[16];
   bool moved;
-  const float al = row_stat_chunk(S.st, s2, pacc[0], pr, moved);
+  const float al = row_stat_chunk(
+      S.st, sacc[0], pacc[0], p.scale_log2, plain,
+      [&](int r) { return q_adj<MODE>(p, S.b, S.h, S.qi, j0 + kr(r, half)); }, pr, moved);
   if (__any(moved)) {  // rare after the first visible chunk: wave-uniform branch
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -736,7 +731,6 @@ __device__ __forceinline__ void sd_step(const DenseParams &p, SdState<T, D> &S, 
     S.io_v.complete(Vs[bn]);
   }
   end_step<ChunkIO<T, D>::DIRECT, 2 * ChunkIO<T, D>::LOADS>(SPREAD || issued);
-  S.buf = bc == 2 ? 0 : bc + 1;
 }
 
 template <typename T, int D, int MODE>
@@ -782,9 +776,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   S.io_k.init(p.ks[1]);
   S.io_v.init(p.vs[1]);
   q_prologue<T, D>(p, S.io_k, S.io_v, S.kbase, S.vbase, R.c_first, R.c_last, Ks, Vs);
-  S.buf = 0;
-  for (int c = R.c_first; c <= R.c_last; ++c)
-    sd_step<T, D, MODE>(p, S, c, Ks, Vs, c < R.cu0 || c > R.cu1);
+  auto masked = [&](int c) { return c < R.cu0 || c > R.cu1; };
+  int c = R.c_first;
+  for (; c + 2 <= R.c_last; c += 3) {
+    sd_step<T, D, MODE, 0>(p, S, c, Ks, Vs, masked(c));
+    sd_step<T, D, MODE, 1>(p, S, c + 1, Ks, Vs, masked(c + 1));
+    sd_step<T, D, MODE, 2>(p, S, c + 2, Ks, Vs, masked(c + 2));
+  }
+  if (c <= R.c_last) sd_step<T, D, MODE, 0>(p, S, c, Ks, Vs, masked(c));
+  if (c + 1 <= R.c_last) sd_step<T, D, MODE, 1>(p, S, c + 1, Ks, Vs, masked(c + 1));
   wait_vmem();  // the repeated loads of the last steps land before the workgroup ends
 
   const RowStatOut o = row_stat_final(S.st, p.inv_scale_log2);

@@ -108,30 +108,64 @@ struct RowStat {
   }
 };
 
-// One 32-key chunk: s2[r] is the log2-domain score (masked: -inf) of the
-// lane's key r, pacc[r] its dP.  Writes pr[r] = 2^(s2[r] - mref) and returns
-// the factor by which earlier terms were rescaled (1 if mref did not move).
-// `moved` tells whether it did, for this lane's row.
-__device__ __forceinline__ float row_stat_chunk(RowStat &st, const float *s2, const f32x16 &pacc,
-                                                float *pr, bool &moved) {
-  float mx = s2[0];
-#pragma unroll
-  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s2[r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+// The reference update for a chunk whose (both halves') max score is mx.
+__device__ __forceinline__ float row_stat_ref(RowStat &st, float mx, bool &moved, float &mu) {
   st.mtrue = fmaxf(st.mtrue, mx);
   moved = mx > st.mref + kRefSlack;  // false while every key so far is hidden
   const float al = moved ? fast_exp2(st.mref - mx) : 1.f;  // 0 from mref = -inf
   if (moved) st.mref = mx;
-  const float mu = st.mref == -INFINITY ? 0.f : st.mref;
+  mu = st.mref == -INFINITY ? 0.f : st.mref;
+  return al;
+}
+
+// The sums: l = l al + sum pr, dl = dl al + sum pr dP.
+__device__ __forceinline__ void row_stat_sum(RowStat &st, const float *pr, const f32x16 &pacc,
+                                             float al) {
   float ls = 0.f, ds = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    pr[r] = fast_exp2(s2[r] - mu);
     ls += pr[r];
     ds = fmaf(pr[r], pacc[r], ds);
   }
   st.l = fmaf(st.l, al, ls);
   st.dl = fmaf(st.dl, al, ds);
+}
+
+// One 32-key chunk into the statistics.  sacc[r]: the raw score accumulator
+// (Q . K) of the lane's key r, pacc[r] its dP, c = scale log2 e.  Writes
+// pr[r] = 2^(s2[r] - mref), s2 = sacc c + adj(r) the log2-domain score, and
+// returns the factor by which earlier terms were rescaled (1 if mref did not
+// move); `moved` tells whether it did, for this lane's row.  `plain` (a chunk
+// every key of which is visible, no bias, c > 0) skips the mask term, takes
+// the max on the raw accumulators (max(x) c == max(x c) exactly for c > 0)
+// and folds c into the exponent's FMA.  The row-statistics kernel and the
+// fused statistics + dQ kernel call this with the same arguments per chunk.
+template <typename Adj>
+__device__ __forceinline__ float row_stat_chunk(RowStat &st, const f32x16 &sacc,
+                                                const f32x16 &pacc, float c, bool plain, Adj adj,
+                                                float *pr, bool &moved) {
+  float mu, al;
+  if (plain) {
+    float mx = sacc[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+    al = row_stat_ref(st, mx, moved, mu);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pr[r] = fast_exp2(fmaf(sacc[r], c, -mu));
+  } else {
+    float s2[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s2[r] = fmaf(sacc[r], c, adj(r));
+    float mx = s2[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s2[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    al = row_stat_ref(st, mx, moved, mu);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pr[r] = fast_exp2(s2[r] - mu);
+  }
+  row_stat_sum(st, pr, pacc, al);
   return al;
 }
 
