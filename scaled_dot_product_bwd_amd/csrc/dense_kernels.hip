@@ -677,17 +677,78 @@ __device__ __forceinline__ void sd_step(const DenseParams &p, SdState<T, D> &S, 
     S.io_k.issue(S.kbase, p.ks[1], (c + 2) * 32, p.Sk, Ks[bn]);
     S.io_v.issue(S.vbase, p.vs[1], (c + 2) * 32, p.Sk, Vs[bn]);
   }
-  f32x16 sacc[1], pacc[1];
-  constexpr int NDMA = SPREAD ? 2 * ChunkIO<T, D>::LOADS : 0;
-  q_phase_a<T, D, 1, NDMA, decltype(dma), kSdRing>(&Ks[bc], &Vs[bc], S.qf, S.gf, sacc, pacc,
-                                                   S.lane, dma);
-  const int j0 = c * 32, half = S.half;
+  typedef typename M::frag F;
+  constexpr int NSD = D / M::KS, RING = kSdRing, NDMA = SPREAD ? 2 * ChunkIO<T, D>::LOADS : 0;
+  static_assert(NDMA <= 2 * NSD, "one load per phase-A step");
+  const Tile<T, D> *Kc = &Ks[bc], *Vc = &Vs[bc];
+  const int l32 = S.lane & 31, half = S.half, j0 = c * 32;
   const bool plain = MODE == MODE_INDEX && !masked && p.scale_log2 > 0.f;
-  float pr[16];
-  bool moved;
-  const float al = row_stat_chunk(
-      S.st, sacc[0], pacc[0], p.scale_log2, plain,
-      [&](int r) { return q_adj<MODE>(p, S.b, S.h, S.qi, j0 + kr(r, half)); }, pr, moved);
+  const float cl = p.scale_log2;
+
+  // Phase A: the S^T chain (K fragments), then the dP^T chain (V fragments)
+  // with the statistics' max and exponentials of S in its steps (row_stat_chunk's
+  // arithmetic, stage by stage).  One fragment ring over both operands, read
+  // RING - 1 steps ahead; the next chunk's loads one per step.
+  F fr[RING];
+  auto load = [&](int i) {
+    fr[i % RING] = i < NSD ? Kc->frag(l32, i, half) : Vc->frag(l32, i - NSD, half);
+  };
+#pragma unroll
+  for (int i = 0; i < RING - 1 && i < 2 * NSD; ++i) load(i);
+  f32x16 sacc{}, pacc{};
+  float s2[16], pr[16], mx = 0.f, mu = 0.f, al = 1.f, ls = 0.f;
+  bool moved = false;
+  auto stat_part = [&](int k) {  // k = 0..7
+    if (k == 0 || k == 1) {
+      const int r0 = 8 * k;
+      if (plain) {
+        if (k == 0) mx = sacc[0];
+#pragma unroll
+        for (int r = r0 + (k == 0); r < r0 + 8; ++r) mx = fmaxf(mx, sacc[r]);
+      } else {
+#pragma unroll
+        for (int r = r0; r < r0 + 8; ++r)
+          s2[r] = fmaf(sacc[r], cl, q_adj<MODE>(p, S.b, S.h, S.qi, j0 + kr(r, half)));
+        if (k == 0) mx = s2[0];
+#pragma unroll
+        for (int r = r0 + (k == 0); r < r0 + 8; ++r) mx = fmaxf(mx, s2[r]);
+      }
+    } else if (k == 2) {
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      if (plain) mx *= cl;
+      al = row_stat_ref(S.st, mx, moved, mu);
+    } else if (k < 7) {
+      const int r0 = 4 * (k - 3);
+#pragma unroll
+      for (int r = r0; r < r0 + 4; ++r)
+        pr[r] = fast_exp2(plain ? fmaf(sacc[r], cl, -mu) : s2[r] - mu);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ls += pr[r];
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < 2 * NSD; ++i) {
+    sched_fence();
+    if (i + RING - 1 < 2 * NSD) load(i + RING - 1);
+    if (i < NDMA) dma(i);
+    if (i < NSD) {
+      sacc = M::mma(fr[i % RING], S.qf[0][i], sacc);
+    } else {
+      pacc = M::mma(fr[i % RING], S.gf[0][i - NSD], pacc);
+      const int s = i - NSD;
+#pragma unroll
+      for (int k = s * 8 / NSD; k < (s + 1) * 8 / NSD; ++k) stat_part(k);
+    }
+  }
+  sched_fence();
+  {  // the sums (row_stat_sum's ls was formed above in the same order)
+    float ds = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ds = fmaf(pr[r], pacc[r], ds);
+    S.st.l = fmaf(S.st.l, al, ls);
+    S.st.dl = fmaf(S.st.dl, al, ds);
+  }
   if (__any(moved)) {  // rare after the first visible chunk: wave-uniform branch
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -702,30 +763,38 @@ __device__ __forceinline__ void sd_step(const DenseParams &p, SdState<T, D> &S, 
   const float dh = l_tot > 0.f ? dl_tot / l_tot : 0.f;
   const float shift = S.dh - dh;
   S.dh = dh;
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) S.acc_a[t][r] = fmaf(shift, S.acc_b[t][r], S.acc_a[t][r]);
-  typename M::frag uf[CS], pf[CS];
+  F uf[CS], pf[CS];
 #pragma unroll
   for (int st = 0; st < CS; ++st) {
     float pd[16 / CS];
 #pragma unroll
     for (int e = 0; e < 16 / CS; ++e)
-      pd[e] = pr[st * (16 / CS) + e] * (pacc[0][st * (16 / CS) + e] - dh);
+      pd[e] = pr[st * (16 / CS) + e] * (pacc[st * (16 / CS) + e] - dh);
     uf[st] = creuse<T>(pd, 0);
     pf[st] = creuse<T>(pr, st);
   }
-  const Tile<T, D> *Kc = &Ks[bc];
+
+  // Phase C: per tile t, A' moves to the new estimate (A' += shift B, B before
+  // this chunk) just before its first product of the chunk, so each tile's
+  // shift overlaps the previous tile's MFMAs; then B and A' accumulate.
+  constexpr int NC = CS * NT;
+  F kt[RING];
+  auto loadc = [&](int k) { kt[k % RING] = Kc->tfrag(32 * (k % NT), k / NT, S.lane); };
 #pragma unroll
-  for (int st = 0; st < CS; ++st) {
+  for (int k = 0; k < RING - 1 && k < NC; ++k) loadc(k);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const typename M::frag kt = Kc->tfrag(32 * t, st, S.lane);
-      S.acc_a[t] = M::mma(kt, uf[st], S.acc_a[t]);
-      S.acc_b[t] = M::mma(kt, pf[st], S.acc_b[t]);
+  for (int k = 0; k < NC; ++k) {
+    const int st = k / NT, t = k % NT;
+    sched_fence();
+    if (k + RING - 1 < NC) loadc(k + RING - 1);
+    if (st == 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S.acc_a[t][r] = fmaf(shift, S.acc_b[t][r], S.acc_a[t][r]);
     }
+    S.acc_b[t] = M::mma(kt[k % RING], pf[st], S.acc_b[t]);
+    S.acc_a[t] = M::mma(kt[k % RING], uf[st], S.acc_a[t]);
   }
+  sched_fence();
   if (issued) {
     S.io_k.complete(Ks[bn]);
     S.io_v.complete(Vs[bn]);
