@@ -118,6 +118,20 @@ def test_validation_rejects_aliasing():
     assert _rc(a)[0] == _abi.ATTN_E_INVALID
 
 
+@pytest.mark.parametrize("entry", ["attn_bwd_row_stats", "attn_bwd_kv", "attn_bwd_dq",
+                                   "attn_bwd_stats_dq"])
+def test_stage_entries_validate_like_attn_bwd(entry):
+    """The stage entry points take attn_bwd's validation before any launch."""
+    lib = sdb.load_library()
+    for field, value, code in (("D", 96, _abi.ATTN_E_UNSUPPORTED), ("q", 0, _abi.ATTN_E_INVALID),
+                               ("workspace", 0, _abi.ATTN_E_WORKSPACE)):
+        a = _args(**{field: value})
+        assert getattr(lib, entry)(ctypes.byref(a), None) == code, (entry, field)
+    a = _args()
+    a.dq = a.k  # output over an input
+    assert getattr(lib, entry)(ctypes.byref(a), None) == _abi.ATTN_E_INVALID
+
+
 def test_unrequested_outputs_may_be_null():
     # wrt = Q with dk = dv = NULL passes validation up to the first check that
     # needs a real device; give it a NULL q to stop there instead.
