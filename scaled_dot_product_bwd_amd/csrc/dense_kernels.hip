@@ -37,11 +37,14 @@ namespace attn {
 // heads; the row statistics (three workgroups per CU) are faster with all.
 constexpr int kKvGroup = 2, kDqGroup = 4, kRsGroup = 8;
 
-// Each kernel's chunk loop runs in a force-inlined `*_run` function unrolled by
-// three, so every step has its LDS buffers fixed at compile time.  Steps are
-// unconditional (a conditional step would make the accumulators merge across
-// paths, which the compiler pays for with register copies); chunks no row of
-// a wave sees are computed like any other and contribute P = 0.
+// The query-major kernels' chunk loops (dQ, and statistics + dQ) are unrolled
+// by three, so every step has its LDS buffers fixed at compile time (no
+// per-read address arithmetic); the row statistics and dK / dV rotate their
+// buffers at run time (unrolled, the former spills at three waves per SIMD;
+// the latter's body addresses with immediate offsets from one base anyway).
+// Steps are unconditional (a conditional step would make the accumulators merge
+// across paths, which the compiler pays for with register copies); chunks no
+// row of a wave sees are computed like any other and contribute P = 0.
 
 // After the compute of a step: make this wave's loads of the next chunk land
 // (leaving the `issued` loads of the chunk after it in flight), then hand the
@@ -226,6 +229,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   S.io_v.init(p.vs[1]);
   q_prologue<T, D, kRsBuf>(p, S.io_k, S.io_v, S.kbase, S.vbase, R.c_first, R.c_last, Ks, Vs);
   S.buf = 0;
+  // Buffers rotate at run time here: unrolled by two (compile-time offsets)
+  // the kernel spills at three waves per SIMD.
   for (int c = R.c_first; c <= R.c_last; ++c)
     rs_step<T, D, MODE, kRsBuf>(p, S, c, Ks, Vs, c < R.cu0 || c > R.cu1);
   wait_vmem();  // the repeated loads of the last step land before the workgroup ends
@@ -495,12 +500,12 @@ template <typename T, int D> struct DqState {
   int b, h, lane, half, c_last, buf;
 };
 
-template <typename T, int D, int MODE>
+template <typename T, int D, int MODE, int BC>
 __device__ __forceinline__ void dq_step(const DenseParams &p, DqState<T, D> &S, int c,
                                         Tile<T, D> *Ks, Tile<T, D> *Vs, bool masked) {
   typedef MT<T> M;
   constexpr int NT = D / 32, CS = M::CSTEPS, NQB = QShape<T>::NQB;
-  const int bc = S.buf, bn = bc == 0 ? 2 : bc - 1;
+  constexpr int bc = BC, bn = (BC + 2) % 3;
   const bool issued = c + 2 <= S.c_last;
   constexpr bool SPREAD = ChunkIO<T, D>::DIRECT;
   auto dma = q_next_chunk_dma<T, D>(p, S.io_k, S.io_v, S.kbase, S.vbase, min(c + 2, S.c_last),
@@ -544,7 +549,6 @@ __device__ __forceinline__ void dq_step(const DenseParams &p, DqState<T, D> &S, 
     S.io_v.complete(Vs[bn]);
   }
   end_step<ChunkIO<T, D>::DIRECT, 2 * ChunkIO<T, D>::LOADS>(SPREAD || issued);
-  S.buf = bc == 2 ? 0 : bc + 1;
 }
 
 template <typename T, int D, int MODE>
@@ -592,9 +596,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   S.io_k.init(p.ks[1]);
   S.io_v.init(p.vs[1]);
   q_prologue<T, D>(p, S.io_k, S.io_v, S.kbase, S.vbase, R.c_first, R.c_last, Ks, Vs);
-  S.buf = 0;
-  for (int c = R.c_first; c <= R.c_last; ++c)
-    dq_step<T, D, MODE>(p, S, c, Ks, Vs, c < R.cu0 || c > R.cu1);
+  auto masked = [&](int c) { return c < R.cu0 || c > R.cu1; };
+  int c = R.c_first;
+  for (; c + 2 <= R.c_last; c += 3) {  // unrolled by three: compile-time LDS offsets
+    dq_step<T, D, MODE, 0>(p, S, c, Ks, Vs, masked(c));
+    dq_step<T, D, MODE, 1>(p, S, c + 1, Ks, Vs, masked(c + 1));
+    dq_step<T, D, MODE, 2>(p, S, c + 2, Ks, Vs, masked(c + 2));
+  }
+  if (c <= R.c_last) dq_step<T, D, MODE, 0>(p, S, c, Ks, Vs, masked(c));
+  if (c + 1 <= R.c_last) dq_step<T, D, MODE, 1>(p, S, c + 1, Ks, Vs, masked(c + 1));
   wait_vmem();  // the repeated loads of the last steps land before the workgroup ends
 
   const float sc = p.scale;  // the factor of dS, applied once
