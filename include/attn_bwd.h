@@ -130,10 +130,11 @@ int attn_bwd_dq(const attn_bwd_args *a, void *stream);
  * `backward_dense_head_all`: dS = P (dP - rowsum(P dP)) scale, dQ = dS K,
  * with rowsum(P dP) found in the same pass: dQ_i = scale (A_i - delta_i B_i)
  * / l_i, A_i = sum_j p~_ij dP_ij K_j, B_i = sum_j p~_ij K_j).  Same arguments
- * and validation as attn_bwd.  It fills the workspace statistics exactly as
- * attn_bwd_row_stats does (bit for bit) and writes dQ if `wrt` asks for it;
- * attn_bwd_kv may follow on the same stream.  bf16 runs one kernel; fp32 runs
- * attn_bwd_row_stats then attn_bwd_dq. */
+ * and validation as attn_bwd.  It fills the workspace statistics (as
+ * attn_bwd_row_stats does, up to rounding: it takes keys 64 at a time, the
+ * row-statistics pass 32) and writes dQ if `wrt` asks for it; attn_bwd_kv may
+ * follow on the same stream, which is what attn_bwd does for bf16 (same bits).
+ * bf16 runs one kernel; fp32 runs attn_bwd_row_stats then attn_bwd_dq. */
 int attn_bwd_stats_dq(const attn_bwd_args *a, void *stream);
 
 /* ------------------------------------------------------------------------

@@ -36,9 +36,12 @@ def hipcc() -> str:
 
 # -amdgpu-mfma-vgpr-form: MFMA results in VGPRs, so the softmax reads them
 # without accumulator-register moves.
+# -pragma-unroll-threshold: the fused statistics + dQ step is large; below this
+# the compiler leaves some of its `#pragma unroll` loops rolled and indexes the
+# fragment and score arrays in scratch memory.
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-mllvm", "-amdgpu-mfma-vgpr-form",
+          "-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-pragma-unroll-threshold=1000000",
           "-I", INCLUDE, "-I", CSRC]
 
 

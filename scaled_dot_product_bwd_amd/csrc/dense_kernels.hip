@@ -636,7 +636,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // ---------------------------------------------------------------------------
-// Row statistics and dQ in one query-major pass (bf16).  Per 32-key chunk,
+// Row statistics and dQ in one query-major pass (bf16).  Per 64-key chunk,
 // after S^T and dP^T (phase A) and the online statistics (RowStat, reference
 // mref):
 //   A^T += K^T (P~ * (dP - dh))^T,   B^T += K^T P~^T,   P~ = 2^(s - mref),
@@ -652,110 +652,136 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // A' = sum P~ (dP - dh) K with dh the running estimate of delta (this chunk
 // included): each chunk first moves A' to the new estimate (A' += (dh_old -
 // dh) B, fp32), then adds P~ (dP - dh) K, the difference formed in fp32 before
-// the bf16 rounding as in the dQ pass.  After the last chunk dh is delta.  The statistics are
-// stored exactly as the row-statistics kernel stores them (same arithmetic,
-// same chunk order), so the dK / dV pass sees the same bits either way.
-constexpr int kSdRing = 4;  // phase-A fragment ring of the fused pass
+// the bf16 rounding as in the dQ pass.  After the last chunk dh is delta.  The
+// statistics use the row-statistics kernel's arithmetic over 64 keys at a time
+// (one reference update, one dh move and one barrier per 64 keys); they equal
+// that kernel's (32 keys at a time) up to rounding.
+constexpr int kSdRing = 4;  // fragment ring of the fused pass (reads RING - 1 steps ahead)
+constexpr int kSdKeys = 64;  // keys per chunk: two 32-key sub-tiles per statistics update
 
 template <typename T, int D> struct SdState {
   typedef MT<T> M;
   static constexpr int NSD = D / M::KS, NT = D / 32;
-  typename M::frag qf[1][NSD], gf[1][NSD];
+  typename M::frag qf[NSD], gf[NSD];
   f32x16 acc_a[NT], acc_b[NT];
   RowStat st;
   float dh;  // the estimate of delta that acc_a currently subtracts
   int qi;
-  ChunkIO<T, D> io_k, io_v;
+  ChunkIO<T, D, kSdKeys> io_k, io_v;
   const T *kbase, *vbase;
-  int b, h, lane, half, c_last, buf;
+  int b, h, lane, half, c_last;
 };
 
-// Chunk c, whose tiles are in buffer BC (chunk c + 2 goes to the buffer chunk
-// c - 1 used); the caller unrolls the chunk loop by three, so every LDS
-// address is a base plus a compile-time offset.
+// Chunk c (keys 64 c .. 64 c + 63, two 32-key sub-tiles u), whose tiles are in
+// buffer BC; chunk c + 2 goes to the buffer chunk c - 1 used.  The caller
+// unrolls the chunk loop by three, so every LDS address is a base plus a
+// compile-time offset.
+//   Phase A: the S^T chains of both sub-tiles, then their dP^T chains with the
+//     statistics' max and exponentials of S in the steps (one reference update
+//     per 64 keys, the row-statistics arithmetic over 32 scores per lane).
+//   Then: the sums, the rescale (rare, wave-uniform), delta's new estimate dh,
+//     the packed operands p~ (dP - dh) and p~.
+//   Phase C: per tile t, A' += (dh_old - dh) B just before its first product
+//     (so each tile's shift overlaps the previous tile's MFMAs); then B and A'
+//     accumulate over the chunk's four 16-key steps, one transposed K fragment
+//     per pair of products.
 template <typename T, int D, int MODE, int BC>
 __device__ __forceinline__ void sd_step(const DenseParams &p, SdState<T, D> &S, int c,
-                                        Tile<T, D> *Ks, Tile<T, D> *Vs, bool masked) {
+                                        Tile<T, D, kSdKeys> *Ks, Tile<T, D, kSdKeys> *Vs,
+                                        bool masked) {
   typedef MT<T> M;
-  constexpr int NT = D / 32, CS = M::CSTEPS;
-  constexpr int bc = BC, bn = (BC + 2) % 3;
-  const bool issued = c + 2 <= S.c_last;
-  constexpr bool SPREAD = ChunkIO<T, D>::DIRECT;
-  auto dma = q_next_chunk_dma<T, D>(p, S.io_k, S.io_v, S.kbase, S.vbase, min(c + 2, S.c_last),
-                                    Ks[bn], Vs[bn]);
-  if (!SPREAD && issued) {
-    S.io_k.issue(S.kbase, p.ks[1], (c + 2) * 32, p.Sk, Ks[bn]);
-    S.io_v.issue(S.vbase, p.vs[1], (c + 2) * 32, p.Sk, Vs[bn]);
-  }
   typedef typename M::frag F;
-  constexpr int NSD = D / M::KS, RING = kSdRing, NDMA = SPREAD ? 2 * ChunkIO<T, D>::LOADS : 0;
-  static_assert(NDMA <= 2 * NSD, "one load per phase-A step");
-  const Tile<T, D> *Kc = &Ks[bc], *Vc = &Vs[bc];
-  const int l32 = S.lane & 31, half = S.half, j0 = c * 32;
+  constexpr int NT = D / 32, CS = M::CSTEPS, NSD = D / M::KS, RING = kSdRing;
+  constexpr int KC = kSdKeys, NU = KC / 32, L = ChunkIO<T, D, KC>::LOADS;
+  constexpr int NA = 2 * NU * NSD;  // phase-A steps (S, then dP)
+  static_assert(2 * L <= NA, "one load per phase-A step");
+  constexpr int bc = BC, bn = (BC + 2) % 3;
+  const Tile<T, D, KC> *Kc = &Ks[bc], *Vc = &Vs[bc];
+  const int l32 = S.lane & 31, half = S.half, j0 = c * KC;
   const bool plain = MODE == MODE_INDEX && !masked && p.scale_log2 > 0.f;
   const float cl = p.scale_log2;
 
-  // Phase A: the S^T chain (K fragments), then the dP^T chain (V fragments)
-  // with the statistics' max and exponentials of S in its steps (row_stat_chunk's
-  // arithmetic, stage by stage).  One fragment ring over both operands, read
-  // RING - 1 steps ahead; the next chunk's loads one per step.
+  // Chunk min(c + 2, c_last) into buffer bn, one load per phase-A step; past
+  // the end the last chunk is loaded again (never read, drained at the end).
+  const int cn = min(c + 2, S.c_last);
+  const T *kn = S.kbase + (int64_t)cn * KC * p.ks[1];
+  const T *vn = S.vbase + (int64_t)cn * KC * p.vs[1];
+  const int lastn = p.Sk - 1 - cn * KC;
+  const unsigned ksb = (unsigned)(p.ks[1] * sizeof(T)), vsb = (unsigned)(p.vs[1] * sizeof(T));
+  auto dma = [&](int k) {
+    if (k < L)
+      S.io_k.issue_one(k, kn, lastn, ksb, Ks[bn]);
+    else
+      S.io_v.issue_one(k - L, vn, lastn, vsb, Vs[bn]);
+  };
+
   F fr[RING];
-  auto load = [&](int i) {
-    fr[i % RING] = i < NSD ? Kc->frag(l32, i, half) : Vc->frag(l32, i - NSD, half);
+  auto load = [&](int i) {  // step i < NA / 2: K of sub-tile i % NU, else V
+    const int half_a = NA / 2, ii = i < half_a ? i : i - half_a;
+    const int u = ii % NU, s = ii / NU;
+    fr[i % RING] = i < half_a ? Kc->frag(32 * u + l32, s, half) : Vc->frag(32 * u + l32, s, half);
   };
 #pragma unroll
-  for (int i = 0; i < RING - 1 && i < 2 * NSD; ++i) load(i);
-  f32x16 sacc{}, pacc{};
-  float s2[16], pr[16], mx = 0.f, mu = 0.f, al = 1.f, ls = 0.f;
-  bool moved = false;
-  auto stat_part = [&](int k) {  // k = 0..7
-    if (k == 0 || k == 1) {
-      const int r0 = 8 * k;
-      if (plain) {
-        if (k == 0) mx = sacc[0];
+  for (int i = 0; i < RING - 1; ++i) load(i);
+  f32x16 sacc[NU], pacc[NU];
 #pragma unroll
-        for (int r = r0 + (k == 0); r < r0 + 8; ++r) mx = fmaxf(mx, sacc[r]);
+  for (int u = 0; u < NU; ++u) sacc[u] = pacc[u] = f32x16{};
+  float s2[NU][16], pr[NU][16], mx = 0.f, mu = 0.f, al = 1.f, ls = 0.f;
+  bool moved = false;
+  constexpr int NPART = 3 + 4 * NU + 1;
+  auto stat_part = [&](int k) {
+    if (k < NU) {  // sub-tile k's scores and running max
+      const int u = k;
+      if (plain) {
+        if (u == 0) mx = sacc[0][0];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[u][r]);
       } else {
 #pragma unroll
-        for (int r = r0; r < r0 + 8; ++r)
-          s2[r] = fmaf(sacc[r], cl, q_adj<MODE>(p, S.b, S.h, S.qi, j0 + kr(r, half)));
-        if (k == 0) mx = s2[0];
+        for (int r = 0; r < 16; ++r)
+          s2[u][r] = fmaf(sacc[u][r], cl, q_adj<MODE>(p, S.b, S.h, S.qi, j0 + 32 * u + kr(r, half)));
+        if (u == 0) mx = s2[0][0];
 #pragma unroll
-        for (int r = r0 + (k == 0); r < r0 + 8; ++r) mx = fmaxf(mx, s2[r]);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s2[u][r]);
       }
-    } else if (k == 2) {
+    } else if (k == NU) {
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       if (plain) mx *= cl;
       al = row_stat_ref(S.st, mx, moved, mu);
-    } else if (k < 7) {
-      const int r0 = 4 * (k - 3);
+    } else if (k < NU + 1 + 4 * NU) {  // exponentials, four at a time
+      const int q = k - NU - 1, u = q / 4, r0 = 4 * (q % 4);
 #pragma unroll
       for (int r = r0; r < r0 + 4; ++r)
-        pr[r] = fast_exp2(plain ? fmaf(sacc[r], cl, -mu) : s2[r] - mu);
+        pr[u][r] = fast_exp2(plain ? fmaf(sacc[u][r], cl, -mu) : s2[u][r] - mu);
     } else {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) ls += pr[r];
+      for (int u = 0; u < NU; ++u)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ls += pr[u][r];
     }
   };
 #pragma unroll
-  for (int i = 0; i < 2 * NSD; ++i) {
+  for (int i = 0; i < NA; ++i) {
     sched_fence();
-    if (i + RING - 1 < 2 * NSD) load(i + RING - 1);
-    if (i < NDMA) dma(i);
-    if (i < NSD) {
-      sacc = M::mma(fr[i % RING], S.qf[0][i], sacc);
+    if (i + RING - 1 < NA) load(i + RING - 1);
+    if (i < 2 * L) dma(i);
+    if (i < NA / 2) {
+      const int u = i % NU, s = i / NU;
+      sacc[u] = M::mma(fr[i % RING], S.qf[s], sacc[u]);
     } else {
-      pacc = M::mma(fr[i % RING], S.gf[0][i - NSD], pacc);
-      const int s = i - NSD;
+      const int ii = i - NA / 2, u = ii % NU, s = ii / NU;
+      pacc[u] = M::mma(fr[i % RING], S.gf[s], pacc[u]);
 #pragma unroll
-      for (int k = s * 8 / NSD; k < (s + 1) * 8 / NSD; ++k) stat_part(k);
+      for (int k = ii * NPART / (NA / 2); k < (ii + 1) * NPART / (NA / 2); ++k) stat_part(k);
     }
   }
   sched_fence();
-  {  // the sums (row_stat_sum's ls was formed above in the same order)
+  {
     float ds = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) ds = fmaf(pr[r], pacc[r], ds);
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ds = fmaf(pr[u][r], pacc[u][r], ds);
     S.st.l = fmaf(S.st.l, al, ls);
     S.st.dl = fmaf(S.st.dl, al, ds);
   }
@@ -773,51 +799,51 @@ __device__ __forceinline__ void sd_step(const DenseParams &p, SdState<T, D> &S, 
   const float dh = l_tot > 0.f ? dl_tot / l_tot : 0.f;
   const float shift = S.dh - dh;
   S.dh = dh;
-  F uf[CS], pf[CS];
+  F uf[NU][CS], pf[NU][CS];
 #pragma unroll
-  for (int st = 0; st < CS; ++st) {
-    float pd[16 / CS];
+  for (int u = 0; u < NU; ++u)
 #pragma unroll
-    for (int e = 0; e < 16 / CS; ++e)
-      pd[e] = pr[st * (16 / CS) + e] * (pacc[st * (16 / CS) + e] - dh);
-    uf[st] = creuse<T>(pd, 0);
-    pf[st] = creuse<T>(pr, st);
-  }
+    for (int st = 0; st < CS; ++st) {
+      float pd[16 / CS];
+#pragma unroll
+      for (int e = 0; e < 16 / CS; ++e)
+        pd[e] = pr[u][st * (16 / CS) + e] * (pacc[u][st * (16 / CS) + e] - dh);
+      uf[u][st] = creuse<T>(pd, 0);
+      pf[u][st] = creuse<T>(pr[u], st);
+    }
 
-  // Phase C: per tile t, A' moves to the new estimate (A' += shift B, B before
-  // this chunk) just before its first product of the chunk, so each tile's
-  // shift overlaps the previous tile's MFMAs; then B and A' accumulate.
-  constexpr int NC = CS * NT;
+  constexpr int NC = NU * CS * NT;
   F kt[RING];
-  auto loadc = [&](int k) { kt[k % RING] = Kc->tfrag(32 * (k % NT), k / NT, S.lane); };
+  auto loadc = [&](int k) {
+    const int t = k % NT, st = (k / NT) % CS, u = k / (NT * CS);
+    kt[k % RING] = Kc->tfrag(32 * t, st, S.lane, 32 * u);
+  };
 #pragma unroll
   for (int k = 0; k < RING - 1 && k < NC; ++k) loadc(k);
 #pragma unroll
   for (int k = 0; k < NC; ++k) {
-    const int st = k / NT, t = k % NT;
+    const int t = k % NT, st = (k / NT) % CS, u = k / (NT * CS);
     sched_fence();
     if (k + RING - 1 < NC) loadc(k + RING - 1);
-    if (st == 0) {
+    if (k < NT) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) S.acc_a[t][r] = fmaf(shift, S.acc_b[t][r], S.acc_a[t][r]);
     }
-    S.acc_b[t] = M::mma(kt[k % RING], pf[st], S.acc_b[t]);
-    S.acc_a[t] = M::mma(kt[k % RING], uf[st], S.acc_a[t]);
+    S.acc_b[t] = M::mma(kt[k % RING], pf[u][st], S.acc_b[t]);
+    S.acc_a[t] = M::mma(kt[k % RING], uf[u][st], S.acc_a[t]);
   }
   sched_fence();
-  if (issued) {
-    S.io_k.complete(Ks[bn]);
-    S.io_v.complete(Vs[bn]);
-  }
-  end_step<ChunkIO<T, D>::DIRECT, 2 * ChunkIO<T, D>::LOADS>(SPREAD || issued);
+  wait_vmem_le<2 * L>();  // chunk c + 1 (requested a step ago) has landed
+  __syncthreads();
 }
 
 template <typename T, int D, int MODE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_stats_dq(const DenseParams p) {
   typedef MT<T> M;
-  constexpr int KS = M::KS, KL = M::KL, NSD = D / KS, NT = D / 32, QROWS = 128;
+  constexpr int KS = M::KS, KL = M::KL, NSD = D / KS, NT = D / 32, QROWS = 128, KC = kSdKeys;
+  static_assert(sizeof(T) == 2, "bf16 only (direct-to-LDS chunk loads)");
   static_assert(QShape<T>::QROWS == QROWS, "one 32-query block per wave");
-  __shared__ Tile<T, D> Ks[3], Vs[3];
+  __shared__ Tile<T, D, KC> Ks[3], Vs[3];
 
   SdState<T, D> S;
   const int tid = threadIdx.x, w = tid >> 6;
@@ -840,8 +866,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const T *grow = (const T *)p.dy + b * p.dys[0] + (int64_t)(qvalid ? qi : 0) * p.dys[1] + h * p.dys[2];
 #pragma unroll
     for (int s = 0; s < NSD; ++s) {
-      S.qf[0][s] = load_frag<T>(qrow, s * KS + half * KL, qvalid);
-      S.gf[0][s] = load_frag<T>(grow, s * KS + half * KL, qvalid);
+      S.qf[s] = load_frag<T>(qrow, s * KS + half * KL, qvalid);
+      S.gf[s] = load_frag<T>(grow, s * KS + half * KL, qvalid);
     }
     S.st.init();
     S.dh = 0.f;
@@ -850,11 +876,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
   S.kbase = (const T *)p.k + b * p.ks[0] + (h / p.G) * p.ks[2];  // the head's K / V head
   S.vbase = (const T *)p.v + b * p.vs[0] + (h / p.G) * p.vs[2];
-  const QRange R = q_range(p, i0, QROWS, MODE == MODE_INDEX);
+  const QRange R = q_range<KC>(p, i0, QROWS, MODE == MODE_INDEX);
   S.c_last = R.c_last;
   S.io_k.init(p.ks[1]);
   S.io_v.init(p.vs[1]);
-  q_prologue<T, D>(p, S.io_k, S.io_v, S.kbase, S.vbase, R.c_first, R.c_last, Ks, Vs);
+  if (R.c_first <= R.c_last) {  // chunks c_first and c_first + 1 into buffers 0 and 1
+    S.io_k.issue(S.kbase, p.ks[1], R.c_first * KC, p.Sk, Ks[0]);
+    S.io_v.issue(S.vbase, p.vs[1], R.c_first * KC, p.Sk, Vs[0]);
+    const int c1 = min(R.c_first + 1, R.c_last);
+    S.io_k.issue(S.kbase, p.ks[1], c1 * KC, p.Sk, Ks[1]);
+    S.io_v.issue(S.vbase, p.vs[1], c1 * KC, p.Sk, Vs[1]);
+  }
+  wait_vmem();  // also the fragment loads above
+  __syncthreads();
   auto masked = [&](int c) { return c < R.cu0 || c > R.cu1; };
   int c = R.c_first;
   for (; c + 2 <= R.c_last; c += 3) {
@@ -872,11 +906,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   // dQ^T = A'^T * scale / l per lane column (row): after the last chunk the
   // estimate is delta itself (o.delta, bit for bit), so A' = A - delta B.
-  // Whole rows stored through LDS (the chunk tiles are free once every wave
-  // is done).
+  // Whole rows stored through LDS (the chunk tiles are free: the last step
+  // ended with a barrier).
   typedef RowStore<T, D> RS;
   static_assert(4 * RS::BYTES <= sizeof(Ks), "row staging fits the chunk tiles");
-  __syncthreads();
   char *lq = reinterpret_cast<char *>(Ks) + w * RS::BYTES;
   RS::write_tiles(S.acc_a, p.scale * o.inv_l, lq, S.lane);
   const int q0 = i0 + 32 * w;

@@ -55,26 +55,30 @@ __device__ __forceinline__ void q_phase_a(const Tile<T, D> *Kc, const Tile<T, D>
   }
 }
 
-// Query-major chunk ranges of a workgroup holding queries [i0, i0 + QROWS):
-// the visible chunks [c_first, c_last] and, inside them, the chunks [cu0, cu1]
-// whose every (query, key) pair the index rule keeps (no per-element test).
+// Query-major chunk ranges of a workgroup holding queries [i0, i0 + QROWS),
+// in chunks of KC keys: the visible chunks [c_first, c_last] and, inside them,
+// the chunks [cu0, cu1] whose every (query, key) pair the index rule keeps (no
+// per-element test).
 struct QRange {
   int c_first, c_last, cu0, cu1;
 };
+template <int KC = 32>
 __device__ __forceinline__ QRange q_range(const DenseParams &p, int i0, int qrows, bool index_only) {
+  static_assert(KC == 32 || KC == 64, "chunk size");
+  constexpr int SH = KC == 32 ? 5 : 6;
   QRange r;
   const int ilast = min(i0 + qrows, p.Sq) - 1;
   const int jlo = max(0, (int)max((int64_t)i0 + p.lo_off, (int64_t)0));
   const int jhi = min(p.Sk - 1, (int)min((int64_t)ilast + p.hi_off, (int64_t)kBig));
-  r.c_first = jlo >> 5;
-  r.c_last = jhi >= jlo ? jhi >> 5 : r.c_first - 1;
+  r.c_first = jlo >> SH;
+  r.c_last = jhi >= jlo ? jhi >> SH : r.c_first - 1;
   r.cu0 = r.c_last + 1;
   r.cu1 = r.c_last;
   if (index_only && i0 + qrows <= p.Sq) {
-    // key j of chunk c: j0 + 31 - i0 <= hi_off, j0 - (i0 + qrows - 1) >= lo_off, j0 + 32 <= Sk
-    const int64_t c_hi = min(((int64_t)i0 + p.hi_off - 31) >> 5, (int64_t)(p.Sk >> 5) - 1);
+    // key j of chunk c: j0 + KC - 1 - i0 <= hi_off, j0 - (i0 + qrows - 1) >= lo_off, j0 + KC <= Sk
+    const int64_t c_hi = min(((int64_t)i0 + p.hi_off - (KC - 1)) >> SH, (int64_t)(p.Sk >> SH) - 1);
     const int64_t lo_j = (int64_t)i0 + qrows - 1 + p.lo_off;
-    const int64_t c_lo = lo_j <= 0 ? 0 : (lo_j + 31) >> 5;
+    const int64_t c_lo = lo_j <= 0 ? 0 : (lo_j + KC - 1) >> SH;
     int64_t a = max(c_lo, (int64_t)r.c_first), b = min(c_hi, (int64_t)r.c_last);
     if (a <= b) {
       r.cu0 = (int)a;
@@ -96,8 +100,8 @@ namespace attn {
 // stay <= 2^kRefSlack, and after the first visible chunk almost no chunk
 // rescales anything (a caller that carries accumulators in the same scale
 // multiplies them only then).  mtrue is the running max itself.  The row
-// statistics kernel and the fused statistics + dQ kernel both use this
-// arithmetic, in the same chunk order, so their statistics agree bit for bit.
+// statistics kernel (32-key chunks) and the fused statistics + dQ kernel
+// (64-key chunks, the same stages) both use this arithmetic.
 constexpr float kRefSlack = 8.f;
 
 struct RowStat {
@@ -138,8 +142,7 @@ __device__ __forceinline__ void row_stat_sum(RowStat &st, const float *pr, const
 // move); `moved` tells whether it did, for this lane's row.  `plain` (a chunk
 // every key of which is visible, no bias, c > 0) skips the mask term, takes
 // the max on the raw accumulators (max(x) c == max(x c) exactly for c > 0)
-// and folds c into the exponent's FMA.  The row-statistics kernel and the
-// fused statistics + dQ kernel call this with the same arguments per chunk.
+// and folds c into the exponent's FMA.
 template <typename Adj>
 __device__ __forceinline__ float row_stat_chunk(RowStat &st, const f32x16 &sacc,
                                                 const f32x16 &pacc, float c, bool plain, Adj adj,
