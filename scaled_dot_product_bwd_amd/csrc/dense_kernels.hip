@@ -880,15 +880,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   S.c_last = R.c_last;
   S.io_k.init(p.ks[1]);
   S.io_v.init(p.vs[1]);
-  if (R.c_first <= R.c_last) {  // chunks c_first and c_first + 1 into buffers 0 and 1
+  // Chunk c_first into buffer 0 and landed (with the fragment loads above);
+  // chunk c_first + 1 into buffer 1 stays in flight under chunk c_first's
+  // compute (the first step waits for it at its end, as for every chunk).
+  if (R.c_first <= R.c_last) {
     S.io_k.issue(S.kbase, p.ks[1], R.c_first * KC, p.Sk, Ks[0]);
     S.io_v.issue(S.vbase, p.vs[1], R.c_first * KC, p.Sk, Vs[0]);
+  }
+  wait_vmem();
+  __syncthreads();
+  if (R.c_first <= R.c_last) {
     const int c1 = min(R.c_first + 1, R.c_last);
     S.io_k.issue(S.kbase, p.ks[1], c1 * KC, p.Sk, Ks[1]);
     S.io_v.issue(S.vbase, p.vs[1], c1 * KC, p.Sk, Vs[1]);
   }
-  wait_vmem();  // also the fragment loads above
-  __syncthreads();
   auto masked = [&](int c) { return c < R.cu0 || c > R.cu1; };
   int c = R.c_first;
   for (; c + 2 <= R.c_last; c += 3) {
