@@ -1,10 +1,14 @@
-// dense_kernels.hip -- the three gfx950 kernels of the dense attention backward.
+// dense_kernels.hip -- the gfx950 kernels of the dense attention backward.
+// bf16 runs k_stats_dq then k_kv_bwd; fp32 runs k_row_stats, k_kv_bwd,
+// k_dq_bwd.
 //
 //   k_row_stats  query-block-major, once per row: m, l = sum exp(s - m) and
-//                delta = rowsum(P * dP), the latter as dY . O with O = P V
-//                accumulated online (equal in exact arithmetic).  The
-//                statistics triple is the one ruDNN ordered_kernel.rs
+//                delta = rowsum(P * dP), accumulated online with dP = dY V^T.
+//                The statistics triple is the one ruDNN ordered_kernel.rs
 //                `history_backward` consumes (max, denominator, delta).
+//   k_stats_dq   query-block-major (bf16): the row statistics and dQ in one
+//                pass, dQ = scale (A - delta B) / l with A, B accumulated
+//                against the running statistics (see its section).
 //   k_kv_bwd     KV-block-major: per 128-key block, over its visible query
 //                chunks (64 rows bf16, 32 fp32) in ascending order,
 //                recompute S and P, then
@@ -18,7 +22,7 @@
 // its `apply_synthetic_mask` and Custom / Bias branches.
 //
 // Every workgroup has 4 waves; wave w owns 32 consecutive rows of the block.
-// All five contractions run on 32x32 MFMA tiles (device_common.hpp).  The
+// Every contraction runs on 32x32 MFMA tiles (device_common.hpp).  The
 // streamed operand (Q / dY chunks, or K / V chunks) is triple-buffered in LDS:
 // while chunk c is consumed from one buffer, chunk c + 1 is landing in the
 // second and chunk c + 2 is being requested into the third (bf16: direct

@@ -1,8 +1,9 @@
-// q_core.hpp -- pieces shared by the query-major kernels (row statistics, dQ).
+// q_core.hpp -- pieces shared by the query-major kernels (row statistics, dQ,
+// statistics + dQ).
 //
 // A wave owns NQB blocks of 32 queries (one query per lane column l32 in each
 // block); their Q and dY rows sit in registers as MFMA B operands.  Keys stream
-// through LDS in chunks of 32.  Phase A of a chunk forms, per query block,
+// through LDS in chunks of 32 (64 in the fused statistics + dQ pass).  Phase A of a chunk forms, per query block,
 //   S^T = K Q^T and dP^T = V dY^T     (rows = the chunk's keys, A from LDS)
 // as C tiles whose element r of a lane is key kr(r, half) of the chunk for the
 // lane's query.  Every K / V fragment is read from LDS once and used for all
