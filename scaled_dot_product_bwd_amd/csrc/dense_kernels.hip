@@ -95,6 +95,20 @@ __device__ __forceinline__ void store_row_stat(const DenseParams &p, int64_t row
   p.st_nls[row] = o.nls;
 }
 
+// The keys a query row sees by the index rule, [lo, lo + w]: key j is visible
+// iff (unsigned)(j - lo) <= w, one compare per element (the same set as
+// idx_visible).  A row past Sq, or one that sees no key, gets lo = INT_MAX,
+// which no key index reaches.  No sum overflows: |row|, |key| < 2^30 and the
+// offsets lie in [-2^30, 2^30].
+struct KeySpan {
+  int lo;
+  unsigned w;
+};
+__device__ __forceinline__ KeySpan key_span(const DenseParams &p, int qi) {
+  const int lo = max(qi + p.lo_off, 0), hi = min(qi + p.hi_off, p.Sk - 1);
+  return (qi < p.Sq && hi >= lo) ? KeySpan{lo, (unsigned)(hi - lo)} : KeySpan{INT_MAX, 0u};
+}
+
 // ---------------------------------------------------------------------------
 // Row statistics.  Per query row: the denominator l = sum 2^(s - mref) and
 // delta' = sum 2^(s - mref) dP against a lazily moved reference max (RowStat);
@@ -106,15 +120,18 @@ template <typename T, int D> struct RsState {
   typename M::frag qf[NQB][NSD], gf[NQB][NSD];
   RowStat st[NQB];
   int qi[NQB];
+  KeySpan ks[NQB];  // the keys each row sees by the index rule
   ChunkIO<T, D> io_k, io_v;
   const T *kbase, *vbase;
   int b, h, lane, half, c_last, buf;
 };
 
-// Per-element mask term of (query qi, key kj), log2 domain (query-major kernels).
+// Per-element mask term of (query qi, key kj), log2 domain (query-major
+// kernels); ks = key_span(p, qi).
 template <int MODE>
-__device__ __forceinline__ float q_adj(const DenseParams &p, int b, int h, int qi, int kj) {
-  if (!idx_visible(p, qi, kj)) return -INFINITY;
+__device__ __forceinline__ float q_adj(const DenseParams &p, int b, int h, int qi, int kj,
+                                       const KeySpan &ks) {
+  if ((unsigned)(kj - ks.lo) > ks.w) return -INFINITY;
   if constexpr (MODE == MODE_INDEX) {
     return 0.f;
   } else {
@@ -149,7 +166,7 @@ __device__ __forceinline__ void rs_step(const DenseParams &p, RsState<T, D> &S, 
     float pr[16];
     bool moved;
     row_stat_chunk(S.st[q], sacc[q], pacc[q], p.scale_log2, plain,
-                   [&](int r) { return q_adj<MODE>(p, S.b, S.h, S.qi[q], j0 + kr(r, half)); },
+                   [&](int r) { return q_adj<MODE>(p, S.b, S.h, S.qi[q], j0 + kr(r, half), S.ks[q]); },
                    pr, moved);
   }
   if (issued) {
@@ -215,6 +232,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   for (int q = 0; q < NQB; ++q) {
     const int qi = i0 + 32 * (NQB * w + q) + l32;
     S.qi[q] = qi;
+    S.ks[q] = key_span(p, qi);
     const bool qvalid = qi < p.Sq;
     const T *qrow = (const T *)p.q + b * p.qs[0] + (int64_t)(qvalid ? qi : 0) * p.qs[1] + h * p.qs[2];
     const T *grow = (const T *)p.dy + b * p.dys[0] + (int64_t)(qvalid ? qi : 0) * p.dys[1] + h * p.dys[2];
@@ -499,6 +517,7 @@ template <typename T, int D> struct DqState {
   f32x16 dq[NQB][NT];
   float nlse[NQB], del[NQB];
   int qi[NQB];
+  KeySpan ks[NQB];  // the keys each row sees by the index rule
   ChunkIO<T, D> io_k, io_v;
   const T *kbase, *vbase;
   int b, h, lane, half, c_last, buf;
@@ -530,7 +549,7 @@ __device__ __forceinline__ void dq_step(const DenseParams &p, DqState<T, D> &S, 
     for (int r = 0; r < 16; ++r) t[r] = fmaf(sacc[q][r], p.scale_log2, S.nlse[q]);
     if (MODE != MODE_INDEX || masked) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) t[r] += q_adj<MODE>(p, S.b, S.h, S.qi[q], j0 + kr(r, half));
+      for (int r = 0; r < 16; ++r) t[r] += q_adj<MODE>(p, S.b, S.h, S.qi[q], j0 + kr(r, half), S.ks[q]);
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) dsv[q][r] = fast_exp2(t[r]) * (pacc[q][r] - S.del[q]);
@@ -579,6 +598,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int q = 0; q < NQB; ++q) {
     const int qi = i0 + 32 * (NQB * w + q) + l32;
     S.qi[q] = qi;
+    S.ks[q] = key_span(p, qi);
     const bool qvalid = qi < p.Sq;
     const T *qrow = (const T *)p.q + b * p.qs[0] + (int64_t)(qvalid ? qi : 0) * p.qs[1] + h * p.qs[2];
     const T *grow = (const T *)p.dy + b * p.dys[0] + (int64_t)(qvalid ? qi : 0) * p.dys[1] + h * p.dys[2];
@@ -671,6 +691,7 @@ template <typename T, int D> struct SdState {
   RowStat st;
   float dh;  // the estimate of delta that acc_a currently subtracts
   int qi;
+  KeySpan ks;  // the keys the row sees by the index rule
   ChunkIO<T, D, kSdKeys> io_k, io_v;
   const T *kbase, *vbase;
   int b, h, lane, half, c_last;
@@ -743,7 +764,8 @@ __device__ __forceinline__ void sd_step(const DenseParams &p, SdState<T, D> &S, 
       } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          s2[u][r] = fmaf(sacc[u][r], cl, q_adj<MODE>(p, S.b, S.h, S.qi, j0 + 32 * u + kr(r, half)));
+          s2[u][r] = fmaf(sacc[u][r], cl,
+                          q_adj<MODE>(p, S.b, S.h, S.qi, j0 + 32 * u + kr(r, half), S.ks));
         if (u == 0) mx = s2[0][0];
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s2[u][r]);
@@ -865,6 +887,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   {
     const int qi = i0 + 32 * w + l32;
     S.qi = qi;
+    S.ks = key_span(p, qi);
     const bool qvalid = qi < p.Sq;
     const T *qrow = (const T *)p.q + b * p.qs[0] + (int64_t)(qvalid ? qi : 0) * p.qs[1] + h * p.qs[2];
     const T *grow = (const T *)p.dy + b * p.dys[0] + (int64_t)(qvalid ? qi : 0) * p.dys[1] + h * p.dys[2];
