@@ -98,15 +98,17 @@ __device__ __forceinline__ void store_row_stat(const DenseParams &p, int64_t row
 // The keys a query row sees by the index rule, [lo, lo + w]: key j is visible
 // iff (unsigned)(j - lo) <= w, one compare per element (the same set as
 // idx_visible).  A row past Sq, or one that sees no key, gets lo = INT_MAX,
-// which no key index reaches.  No sum overflows: |row|, |key| < 2^30 and the
-// offsets lie in [-2^30, 2^30].
+// which no key index reaches (indices stay below 2^30 + 128, so j - lo does
+// not overflow).  The bounds are formed in 64 bits: a padding row past Sq
+// plus an offset of 2^30 would not fit in 32.
 struct KeySpan {
   int lo;
   unsigned w;
 };
 __device__ __forceinline__ KeySpan key_span(const DenseParams &p, int qi) {
-  const int lo = max(qi + p.lo_off, 0), hi = min(qi + p.hi_off, p.Sk - 1);
-  return (qi < p.Sq && hi >= lo) ? KeySpan{lo, (unsigned)(hi - lo)} : KeySpan{INT_MAX, 0u};
+  const int64_t lo = max((int64_t)qi + p.lo_off, (int64_t)0);
+  const int64_t hi = min((int64_t)qi + p.hi_off, (int64_t)p.Sk - 1);
+  return (qi < p.Sq && hi >= lo) ? KeySpan{(int)lo, (unsigned)(hi - lo)} : KeySpan{INT_MAX, 0u};
 }
 
 // ---------------------------------------------------------------------------
@@ -297,6 +299,7 @@ template <typename T, int D> struct KvState {
   const T *qbase, *gbase;  // Q, dY of the group's first query head
   int64_t srow0;           // statistics row of (b, first query head, 0)
   int b, h0, jw, kj, wave, lane, l32, half, c_first, nch, total, buf;
+  KeySpan rows;  // the query rows that see key kj by the index rule (as a span)
 };
 
 // Chunks are numbered over the whole group: v = head * nch + (c - c_first) for
@@ -351,7 +354,7 @@ __device__ __forceinline__ void kv_step(const DenseParams &p, KvState<T, D> &S, 
   // Per-element mask term: the index rule, then padding or bias (log2 domain).
   auto adj = [&](int u, int r) -> float {
     const int i = i0 + 32 * u + kr(r, half);
-    if (!idx_visible(p, i, kj)) return -INFINITY;
+    if ((unsigned)(i - S.rows.lo) > S.rows.w) return -INFINITY;
     if constexpr (MODE == MODE_INDEX) {
       return 0.f;
     } else {
@@ -444,6 +447,12 @@ __global__ __launch_bounds__(256) void k_kv_bwd(const DenseParams p) {
   const int j0b = blk * 128;
   S.jw = j0b + 32 * w;
   S.kj = S.jw + S.l32;
+  {  // rows i with lo_off <= kj - i <= hi_off, i < Sq, for kj < Sk (64-bit bounds)
+    const int64_t lo = max((int64_t)S.kj - p.hi_off, (int64_t)0);
+    const int64_t hi = min((int64_t)S.kj - p.lo_off, (int64_t)p.Sq - 1);
+    S.rows = (S.kj < p.Sk && hi >= lo) ? KeySpan{(int)lo, (unsigned)(hi - lo)}
+                                       : KeySpan{INT_MAX, 0u};
+  }
   const int b = S.b, kj = S.kj, half = S.half;
   const bool kvalid = kj < p.Sk;
 
