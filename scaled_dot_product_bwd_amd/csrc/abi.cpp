@@ -307,6 +307,17 @@ int run_from_forward(const attn_bwd_args *a, const float *lse, const void *out,
     orng = extent(out, n, st, es);
     if (overlap(ws, lr) || overlap(ws, orng))
       return fail(ATTN_E_INVALID, "lse / out overlap the workspace");
+    if (c.want_q) {
+      // The dQ kernel forms the statistics from lse and O and publishes them;
+      // the dK / dV kernel follows it on the stream.
+      Checked cq = c;
+      cq.p.fo = out;
+      cq.p.flse = lse;
+      for (int j = 0; j < 3; ++j) cq.p.fos[j] = out_stride[j];
+      rc = run_stage(attn::STAGE_DQ, cq, (hipStream_t)stream);
+      if (rc != ATTN_OK) return rc;
+      return run_stage(attn::STAGE_KV, c, (hipStream_t)stream);
+    }
     const hipError_t e = attn::launch_fwd_stats(c.bf16, c.D, c.p, lse, out, out_stride,
                                                 (hipStream_t)stream);
     if (e != hipSuccess) return fail(ATTN_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));

@@ -617,8 +617,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       S.gf[q][s] = load_frag<T>(grow, s * KS + half * KL, qvalid);
     }
     const int64_t srow = ((int64_t)b * p.H + h) * p.Sq + (qvalid ? qi : 0);
-    S.nlse[q] = qvalid ? p.st_nls[srow] * p.scale_log2 : -INFINITY;  // -lse2
-    S.del[q] = qvalid ? p.st_delta[srow] : 0.f;
+    if (p.fo != nullptr) {
+      // From a forward's saved statistics: delta = dY . O (equal to rowsum(P *
+      // dP) as O = P V), -lse2 = -L log2 e; both halves of the wave hold half
+      // of the row's columns.  Published for the dK / dV pass, which follows.
+      const T *orow = (const T *)p.fo + b * p.fos[0] + (int64_t)(qvalid ? qi : 0) * p.fos[1] +
+                      h * p.fos[2];
+      float dsum = 0.f;
+#pragma unroll
+      for (int s = 0; s < NSD; ++s) {
+        const typename M::frag of = load_frag<T>(orow, s * KS + half * KL, qvalid);
+        dsum += frag_dot<T>(S.gf[q][s], of);
+      }
+      dsum += __shfl_xor(dsum, 32);
+      const float L = qvalid ? p.flse[srow] : -INFINITY;
+      const bool empty = !(L > -INFINITY);  // a row that sees no key: P = 0, delta = 0
+      const float nls = (empty ? -INFINITY : -L * kLog2e) * p.inv_scale_log2;
+      S.nlse[q] = nls * p.scale_log2;
+      S.del[q] = empty ? 0.f : dsum;
+      if (qvalid && half == 0) {
+        p.st_delta[srow] = S.del[q];
+        p.st_nls[srow] = nls;
+      }
+    } else {
+      S.nlse[q] = qvalid ? p.st_nls[srow] * p.scale_log2 : -INFINITY;  // -lse2
+      S.del[q] = qvalid ? p.st_delta[srow] : 0.f;
+    }
 #pragma unroll
     for (int t = 0; t < NT; ++t) S.dq[q][t] = f32x16{};
   }

@@ -62,6 +62,13 @@ struct DenseParams {
   // (-inf / scale for a row that sees nothing), so that st_nls * scale_log2 is
   // the log2-domain offset of the row's probabilities.
   float *st_m, *st_l, *st_delta, *st_nls;
+  // A forward's saved statistics (dQ kernel only; fo == nullptr otherwise):
+  // its natural log-sum-exp [B * H * Sq] and output O (strided like dY).  The
+  // dQ kernel then forms delta and -lse2 itself and writes them to st_delta /
+  // st_nls for the dK / dV kernel that follows.
+  const void *fo;
+  const float *flse;
+  int64_t fos[3];
 };
 
 __device__ __forceinline__ int kr(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }
@@ -100,6 +107,17 @@ template <>
 __device__ __forceinline__ float load_frag<float>(const float *row, int d0, bool valid) {
   return valid ? row[d0] : 0.f;
 }
+
+// Dot product of two fragments (a lane's KL elements), fp32.
+template <typename T>
+__device__ __forceinline__ float frag_dot(typename MT<T>::frag a, typename MT<T>::frag b);
+template <> __device__ __forceinline__ float frag_dot<bf16>(bf16x8 a, bf16x8 b) {
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s = fmaf((float)a[e], (float)b[e], s);
+  return s;
+}
+template <> __device__ __forceinline__ float frag_dot<float>(float a, float b) { return a * b; }
 
 // -f (a sign flip per element).
 template <typename T> __device__ __forceinline__ typename MT<T>::frag neg_frag(typename MT<T>::frag f);
