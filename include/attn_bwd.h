@@ -261,10 +261,11 @@ int attn_bwd_paged_dq(const attn_bwd_paged_args *a, void *dq, void *stream);
  * row, the natural log-sum-exp of its scaled, masked scores (-inf for a row
  * that sees no key), and `out` (device, the element type of q, [B, Sq, H, D]
  * with element strides out_stride[0..2] for (b, s, h)) the forward output O.
- * Then delta = rowsum(dY * O) (= rowsum(P * dP)) and P = exp(s - lse).  When
- * dQ is asked for, the dQ kernel forms delta and the row offsets itself and
- * the dK / dV kernel follows it; otherwise a small statistics kernel runs
- * first.  Workspace planes 2 (delta) and 3 are written, planes 0 and 1 are not.  Same arguments and rules as attn_bwd
+ * Then delta = rowsum(dY * O) (= rowsum(P * dP)) and P = exp(s - lse): the
+ * dQ kernel forms delta and the row offsets in its prologue (and stops there
+ * when dQ is not asked for), then the dK / dV kernel runs, so every `wrt`
+ * gives the same bits.  Workspace planes 2 (delta) and 3 are written, planes
+ * 0 and 1 are not.  Same arguments and rules as attn_bwd
  * otherwise; lse and out must not overlap the workspace. */
 int attn_bwd_from_forward(const attn_bwd_args *a, const float *lse, const void *out,
                           const int64_t *out_stride, void *stream);

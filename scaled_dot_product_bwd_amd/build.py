@@ -19,8 +19,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["abi.cpp", "paged_plan.cpp", "dense_kernels.hip", "fwd_stats.hip",
-           "paged_kernels.hip", "paged_q_kernels.hip"]
+SOURCES = ["abi.cpp", "paged_plan.cpp", "dense_kernels.hip", "paged_kernels.hip",
+           "paged_q_kernels.hip"]
 
 
 def library_path() -> str:

@@ -307,21 +307,22 @@ int run_from_forward(const attn_bwd_args *a, const float *lse, const void *out,
     orng = extent(out, n, st, es);
     if (overlap(ws, lr) || overlap(ws, orng))
       return fail(ATTN_E_INVALID, "lse / out overlap the workspace");
-    if (c.want_q) {
-      // The dQ kernel forms the statistics from lse and O and publishes them;
-      // the dK / dV kernel follows it on the stream.
-      Checked cq = c;
-      cq.p.fo = out;
-      cq.p.flse = lse;
-      for (int j = 0; j < 3; ++j) cq.p.fos[j] = out_stride[j];
-      rc = run_stage(attn::STAGE_DQ, cq, (hipStream_t)stream);
-      if (rc != ATTN_OK) return rc;
-      return run_stage(attn::STAGE_KV, c, (hipStream_t)stream);
+    // The dQ kernel forms delta and -lse2 from lse and O in its prologue and
+    // publishes them (without dQ asked for it stops there); the dK / dV kernel
+    // follows it on the stream.  Every `wrt` takes the same statistics.
+    Checked cq = c;
+    cq.p.fo = out;
+    cq.p.flse = lse;
+    for (int j = 0; j < 3; ++j) cq.p.fos[j] = out_stride[j];
+    if (!c.want_q) {
+      cq.want_q = true;
+      cq.p.dq = nullptr;
     }
-    const hipError_t e = attn::launch_fwd_stats(c.bf16, c.D, c.p, lse, out, out_stride,
-                                                (hipStream_t)stream);
-    if (e != hipSuccess) return fail(ATTN_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    rc = run_stage(attn::STAGE_DQ, cq, (hipStream_t)stream);
+    if (rc != ATTN_OK) return rc;
+    return run_stage(attn::STAGE_KV, c, (hipStream_t)stream);
   }
+  // Nothing to read (no rows or no keys): the stages write their zeros.
   for (int s = attn::STAGE_KV; s <= attn::STAGE_DQ; ++s) {
     rc = run_stage(s, c, (hipStream_t)stream);
     if (rc != ATTN_OK) return rc;

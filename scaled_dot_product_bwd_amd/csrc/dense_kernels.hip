@@ -646,6 +646,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int t = 0; t < NT; ++t) S.dq[q][t] = f32x16{};
   }
+  if (p.dq == nullptr) return;  // statistics only (a forward's, published above)
+
   S.kbase = (const T *)p.k + b * p.ks[0] + (h / p.G) * p.ks[2];  // the head's K / V head
   S.vbase = (const T *)p.v + b * p.vs[0] + (h / p.G) * p.vs[2];
   const QRange R = q_range(p, i0, QROWS, MODE == MODE_INDEX);

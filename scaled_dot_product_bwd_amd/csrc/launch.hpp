@@ -14,9 +14,4 @@ enum { STAGE_ROW_STATS = 0, STAGE_KV = 1, STAGE_DQ = 2, STAGE_STATS_DQ = 3 };
 hipError_t launch_dense_stage(int stage, bool bf16_in, int D, int mode, const DenseParams &p,
                               int nblocks, hipStream_t stream);
 
-// delta and -lse2 planes of the workspace from a forward's log-sum-exp [B, H, Sq]
-// (contiguous fp32) and output O (strided like dY).
-hipError_t launch_fwd_stats(bool bf16_in, int D, const DenseParams &p, const float *lse,
-                            const void *out, const int64_t *ostride, hipStream_t stream);
-
 }  // namespace attn
