@@ -299,6 +299,7 @@ template <typename T, int D> struct KvState {
   const T *qbase, *gbase;  // Q, dY of the group's first query head
   int64_t srow0;           // statistics row of (b, first query head, 0)
   int b, h0, jw, kj, wave, lane, l32, half, c_first, nch, total, buf;
+  int nh, nc;  // query head (in the group) and chunk of stream chunk min(v + 2, total - 1)
   KeySpan rows;  // the query rows that see key kj by the index rule (as a span)
 };
 
@@ -334,7 +335,7 @@ __device__ __forceinline__ void kv_step(const DenseParams &p, KvState<T, D> &S, 
   // are issued here.
   constexpr bool SPREAD = ChunkIO<T, D, ROWS>::DIRECT;
   constexpr int LQ = ChunkIO<T, D, ROWS>::LOADS;
-  const int vn = min(v + 2, S.total - 1), hn = vn / S.nch, cn = S.c_first + (vn - hn * S.nch);
+  const int hn = S.nh, cn = S.nc;  // stream chunk min(v + 2, total - 1)
   const T *qn = S.qbase + hn * p.qs[2] + (int64_t)cn * ROWS * p.qs[1];
   const T *gn = S.gbase + hn * p.dys[2] + (int64_t)cn * ROWS * p.dys[1];
   const int64_t srn = S.srow0 + (int64_t)hn * p.Sq;
@@ -375,6 +376,11 @@ __device__ __forceinline__ void kv_step(const DenseParams &p, KvState<T, D> &S, 
   }
   end_step<ChunkIO<T, D, ROWS>::DIRECT, PER_CHUNK>(SPREAD || issued);
   S.buf = bc == 2 ? 0 : bc + 1;
+  // Step v + 1 loads stream chunk min(v + 3, total - 1): the next chunk of the
+  // head, or the next head's first.
+  const bool adv = v + 3 < S.total, wrap = S.nc == S.c_first + S.nch - 1;
+  S.nc = adv ? (wrap ? S.c_first : S.nc + 1) : S.nc;
+  S.nh = adv && wrap ? S.nh + 1 : S.nh;
 }
 
 // All visible chunks of the block, in ascending order, for each query head of
@@ -404,6 +410,11 @@ __device__ __forceinline__ void kv_run(const DenseParams &p, KvState<T, D> &S, i
   wait_vmem();
   __syncthreads();
   S.buf = 0;
+  {
+    const int vn = min(2, S.total - 1);
+    S.nh = vn / S.nch;
+    S.nc = c_first + (vn - S.nh * S.nch);
+  }
   // Unmasked chunks [cu0, cu1]: every row i of the chunk sees every key j of the
   // block: j_last - i <= hi_off, j0 - i >= lo_off, i < Sq, j_last < Sk.
   int cu0 = c_last + 1, cu1 = c_last;

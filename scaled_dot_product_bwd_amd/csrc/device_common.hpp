@@ -322,14 +322,16 @@ template <int D, int ROWS> struct ChunkIO<bf16, D, ROWS> {
   }
   // Load j alone of issue() below, branch-free (the loads of one chunk may be
   // spread over the previous chunk's compute; see the dK / dV kernel): cb is
-  // the chunk's first row, last = nrows - 1 - r0, rstride = bytes per row.
-  // A lane whose row is past `last` is moved back to it arithmetically.
+  // the chunk's first row, last = nrows - 1 - r0 >= 0, rstride = bytes per row.
+  // The offset is capped at that of row `last`'s final 16-byte segment: a lane
+  // of a row <= last keeps its own (for any row stride, row * rstride + 2 col
+  // stays at or below that bound), a lane past the end reads that segment
+  // (finite data of the matrix, which the mask keeps out of every result).
+  // One unsigned min per load; the bound is wave-uniform.
   __device__ __forceinline__ void issue_one(int j, const bf16 *cb, int last, unsigned rstride,
                                             TileT &t) {
-    int row, col;
-    slot_rc(j, row, col);
-    const int dr = max(row - last, 0);
-    dma_lds16_at(seg(t, j), cb, off[j] - (unsigned)dr * rstride);
+    const unsigned cap = (unsigned)min(last, ROWS - 1) * rstride + 2u * (D - 8);
+    dma_lds16_at(seg(t, j), cb, min(off[j], cap));
   }
   // Rows [r0, r0 + ROWS) of a matrix with `stride` (the one given to init) and
   // `nrows` rows; rows past the end repeat the last row.  r0 < nrows.
