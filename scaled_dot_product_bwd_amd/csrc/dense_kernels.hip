@@ -288,6 +288,20 @@ __device__ __forceinline__ void issue_row_stats(const DenseParams &p, int64_t sr
     dma_lds4(dst + 64, p.st_delta + srow0 + row);
   }
 }
+// The same into the copy at LDS byte address st_lds (of wave 0's copy).
+template <int ROWS>
+__device__ __forceinline__ void issue_row_stats_at(const DenseParams &p, int64_t srow0, int i0,
+                                                   unsigned st_lds, int wave, int lane) {
+  const unsigned dst = st_lds + 4u * 2 * ROWS * wave;
+  if constexpr (ROWS == 32) {
+    const int row = min(i0 + (lane & 31), p.Sq - 1);
+    dma_lds4_at(dst, (lane < 32 ? p.st_nls : p.st_delta) + srow0 + row);
+  } else {
+    const int row = min(i0 + lane, p.Sq - 1);
+    dma_lds4_at(dst, p.st_nls + srow0 + row);
+    dma_lds4_at(dst + 4u * 64, p.st_delta + srow0 + row);
+  }
+}
 template <int ROWS> constexpr int stat_loads() { return ROWS == 32 ? 1 : 2; }
 
 template <typename T, int D> struct KvState {
@@ -299,7 +313,12 @@ template <typename T, int D> struct KvState {
   const T *qbase, *gbase;  // Q, dY of the group's first query head
   int64_t srow0;           // statistics row of (b, first query head, 0)
   int b, h0, jw, kj, wave, lane, l32, half, c_first, nch, total, buf;
-  int nh, nc;  // query head (in the group) and chunk of stream chunk min(v + 2, total - 1)
+  // Stream chunk min(v + 2, total - 1) while step v runs: its chunk index, its
+  // Q / dY chunk start and its head's statistics row; advanced by one chunk per
+  // step (dq_c, dg_c elements), or to the next head's first chunk (dq_w, dg_w).
+  int nc;
+  const T *qn, *gn;
+  int64_t srn, dq_c, dq_w, dg_c, dg_w;
   KeySpan rows;  // the query rows that see key kj by the index rule (as a span)
 };
 
@@ -335,19 +354,20 @@ __device__ __forceinline__ void kv_step(const DenseParams &p, KvState<T, D> &S, 
   // are issued here.
   constexpr bool SPREAD = ChunkIO<T, D, ROWS>::DIRECT;
   constexpr int LQ = ChunkIO<T, D, ROWS>::LOADS;
-  const int hn = S.nh, cn = S.nc;  // stream chunk min(v + 2, total - 1)
-  const T *qn = S.qbase + hn * p.qs[2] + (int64_t)cn * ROWS * p.qs[1];
-  const T *gn = S.gbase + hn * p.dys[2] + (int64_t)cn * ROWS * p.dys[1];
-  const int64_t srn = S.srow0 + (int64_t)hn * p.Sq;
+  const int cn = S.nc;  // stream chunk min(v + 2, total - 1)
   const int lastn = p.Sq - 1 - cn * ROWS;
+  // LDS byte addresses of buffer bn as integers (bn is known only at run time)
+  constexpr unsigned TB = sizeof(Tile<T, D, ROWS>), SB = sizeof(st[0]);
+  const unsigned qlds = lds_addr(Qs) + bn * TB, glds = lds_addr(Gs) + bn * TB;
+  const unsigned slds = lds_addr(st) + bn * SB;
   auto dma = [&](int k) {
     if constexpr (SPREAD) {
       if (k < LQ)
-        S.io_q.issue_one(k, qn, lastn, (unsigned)(p.qs[1] * 2), Qs[bn]);
+        S.io_q.issue_one_at(k, S.qn, lastn, (unsigned)(p.qs[1] * 2), qlds);
       else if (k < 2 * LQ)
-        S.io_g.issue_one(k - LQ, gn, lastn, (unsigned)(p.dys[1] * 2), Gs[bn]);
+        S.io_g.issue_one_at(k - LQ, S.gn, lastn, (unsigned)(p.dys[1] * 2), glds);
       else if (k == 2 * LQ)
-        issue_row_stats<ROWS>(p, srn, cn * ROWS, st[bn], S.wave, S.lane);
+        issue_row_stats_at<ROWS>(p, S.srn, cn * ROWS, slds, S.wave, S.lane);
     }
   };
   if (!SPREAD && issued) kv_issue<T, D, MODE>(p, S, v + 2, &Qs[bn], &Gs[bn], st[bn]);
@@ -379,8 +399,12 @@ __device__ __forceinline__ void kv_step(const DenseParams &p, KvState<T, D> &S, 
   // Step v + 1 loads stream chunk min(v + 3, total - 1): the next chunk of the
   // head, or the next head's first.
   const bool adv = v + 3 < S.total, wrap = S.nc == S.c_first + S.nch - 1;
-  S.nc = adv ? (wrap ? S.c_first : S.nc + 1) : S.nc;
-  S.nh = adv && wrap ? S.nh + 1 : S.nh;
+  if (adv) {  // wave-uniform
+    S.nc = wrap ? S.c_first : S.nc + 1;
+    S.qn += wrap ? S.dq_w : S.dq_c;
+    S.gn += wrap ? S.dg_w : S.dg_c;
+    S.srn += wrap ? (int64_t)p.Sq : 0;
+  }
 }
 
 // All visible chunks of the block, in ascending order, for each query head of
@@ -411,9 +435,15 @@ __device__ __forceinline__ void kv_run(const DenseParams &p, KvState<T, D> &S, i
   __syncthreads();
   S.buf = 0;
   {
-    const int vn = min(2, S.total - 1);
-    S.nh = vn / S.nch;
-    S.nc = c_first + (vn - S.nh * S.nch);
+    const int vn = min(2, S.total - 1), hn = vn / S.nch;
+    S.nc = c_first + (vn - hn * S.nch);
+    S.dq_c = (int64_t)ROWS * p.qs[1];
+    S.dg_c = (int64_t)ROWS * p.dys[1];
+    S.dq_w = p.qs[2] - (int64_t)(S.nch - 1) * S.dq_c;
+    S.dg_w = p.dys[2] - (int64_t)(S.nch - 1) * S.dg_c;
+    S.qn = S.qbase + hn * p.qs[2] + S.nc * S.dq_c;
+    S.gn = S.gbase + hn * p.dys[2] + S.nc * S.dg_c;
+    S.srn = S.srow0 + (int64_t)hn * p.Sq;
   }
   // Unmasked chunks [cu0, cu1]: every row i of the chunk sees every key j of the
   // block: j_last - i <= hi_off, j0 - i >= lo_off, i < Sq, j_last < Sk.

@@ -246,12 +246,13 @@ __device__ __forceinline__ void dma_lds16_at(unsigned m0, const void *sbase, uns
                : "s"(m0), "v"(voff), "s"(sbase)
                : "memory");
 }
-__device__ __forceinline__ void dma_lds4(void *lds, const void *g) {
+__device__ __forceinline__ void dma_lds4_at(unsigned m0, const void *g) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
                :
-               : "s"(lds_addr(lds)), "v"(g)
+               : "s"(m0), "v"(g)
                : "memory");
 }
+__device__ __forceinline__ void dma_lds4(void *lds, const void *g) { dma_lds4_at(lds_addr(lds), g); }
 
 // s_waitcnt vmcnt(n), other counters unconstrained (n < 64: the count's low
 // four bits sit in bits 3:0 of the immediate, its high two in bits 15:14).
@@ -330,8 +331,15 @@ template <int D, int ROWS> struct ChunkIO<bf16, D, ROWS> {
   // One unsigned min per load; the bound is wave-uniform.
   __device__ __forceinline__ void issue_one(int j, const bf16 *cb, int last, unsigned rstride,
                                             TileT &t) {
+    issue_one_at(j, cb, last, rstride, lds_addr(t.a));
+  }
+  // The same with the tile given by its LDS byte address (a wave-uniform
+  // integer: a tile picked at run time then costs no generic-pointer
+  // arithmetic).
+  __device__ __forceinline__ void issue_one_at(int j, const bf16 *cb, int last, unsigned rstride,
+                                               unsigned tile_lds) {
     const unsigned cap = (unsigned)min(last, ROWS - 1) * rstride + 2u * (D - 8);
-    dma_lds16_at(seg(t, j), cb, min(off[j], cap));
+    dma_lds16_at(tile_lds + ((wave + 4 * j) << 10), cb, min(off[j], cap));
   }
   // Rows [r0, r0 + ROWS) of a matrix with `stride` (the one given to init) and
   // `nrows` rows; rows past the end repeat the last row.  r0 < nrows.
