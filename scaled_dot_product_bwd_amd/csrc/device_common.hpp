@@ -232,12 +232,15 @@ __device__ __forceinline__ unsigned lds_addr(const void *p) {
   return __builtin_amdgcn_readfirstlane(
       (unsigned)(size_t)(__attribute__((address_space(3))) const void *)p);
 }
-__device__ __forceinline__ void dma_lds16(void *lds, const void *g) {
+// m0 = LDS byte address (wave-uniform, in an SGPR), g = this lane's global
+// address.
+__device__ __forceinline__ void dma_lds16_m0(unsigned m0, const void *g) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                :
-               : "s"(lds_addr(lds)), "v"(g)
+               : "s"(m0), "v"(g)
                : "memory");
 }
+__device__ __forceinline__ void dma_lds16(void *lds, const void *g) { dma_lds16_m0(lds_addr(lds), g); }
 // The same with a wave-uniform 64-bit base and a 32-bit per-lane byte offset
 // (saddr form: no per-lane 64-bit address arithmetic); m0 = LDS byte address.
 __device__ __forceinline__ void dma_lds16_at(unsigned m0, const void *sbase, unsigned voff) {
@@ -314,11 +317,15 @@ template <int D, int ROWS> struct ChunkIO<bf16, D, ROWS> {
   // Elements given by a functor: elem(r, c) addresses columns c .. c + 7 of chunk
   // row r (c a multiple of 8), so a row may be assembled from several sources.
   template <typename F> __device__ __forceinline__ void issue_elem(F elem, TileT &t) {
+    issue_elem_at(elem, lds_addr(t.a));
+  }
+  // The same into the tile at LDS byte address tile_lds (see issue_one_at).
+  template <typename F> __device__ __forceinline__ void issue_elem_at(F elem, unsigned tile_lds) {
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
       int row, col;
       slot_rc(j, row, col);
-      dma_lds16(&t.a[(wave + 4 * j) * 512], elem(row, col));
+      dma_lds16_m0(tile_lds + ((wave + 4 * j) << 10), elem(row, col));
     }
   }
   // Load j alone of issue() below, branch-free (the loads of one chunk may be

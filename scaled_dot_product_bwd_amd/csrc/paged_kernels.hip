@@ -67,36 +67,56 @@ template <typename T_, int D_, int P_, bool MLA_> struct PagedState {
 // (clamped to the last row, so every lane reads inside the plan).
 template <typename St>
 __device__ __forceinline__ void issue_rowinfo(St &S, int c, int *ri) {
+  issue_rowinfo_at(S, c, lds_addr(ri));
+}
+// The same into the buffer at LDS byte address ri_lds (an integer, so a buffer
+// picked at run time costs no generic-pointer arithmetic).
+template <typename St>
+__device__ __forceinline__ void issue_rowinfo_at(St &S, int c, unsigned ri_lds) {
   const int qh = min(c * St::ROWS + S.lane, S.nqh - 1);
-  dma_lds4(ri + 64 * S.wave, S.rh_tab + qh);
+  dma_lds4_at(__builtin_amdgcn_readfirstlane(ri_lds + 4u * 64 * S.wave), S.rh_tab + qh);
 }
 
 // Statistics and Q / dY rows of chunk c; `ri` holds the chunk's rowinfo (landed).
+// With direct-to-LDS loads the buffers are addressed by their LDS byte
+// addresses (integers: st_lds, q_lds, g_lds); register-staged loads (fp32) go
+// through the tile pointers.
+template <typename St>
+__device__ __forceinline__ void issue_chunk(const PagedParams &p, St &S, int c, const int *ri,
+                                            unsigned st_lds, typename St::QTile *Q,
+                                            typename St::GTile *G, unsigned q_lds,
+                                            unsigned g_lds) {
+  typedef typename St::T T;
+  constexpr int D = St::D, P = St::P;
+  const int *myri = ri + 64 * S.wave;
+  const unsigned myst = __builtin_amdgcn_readfirstlane(st_lds + 4u * kStatWave * S.wave);
+  const int rh = myri[S.lane];
+  const float *srow = S.sbase + 3 * (int64_t)rh;
+  dma_lds4_at(myst, srow);
+  dma_lds4_at(myst + 4u * 64, srow + 1);
+  dma_lds4_at(myst + 4u * 128, srow + 2);
+  dma_lds4_at(myst + 4u * 192, S.pos_tab + min(c * St::ROWS + S.lane, S.nqh - 1));
+  auto qelem = [&](int r, int col) {
+    if constexpr (P > 0)  // a row of the tile is [q | qp]: columns below D from q, the rest from qp
+      return col < D ? S.qbase + (int64_t)myri[r] * D + col
+                     : S.qpbase + (int64_t)myri[r] * P + (col - D);
+    else
+      return S.qbase + (int64_t)myri[r] * D + col;
+  };
+  auto gelem = [&](int r, int col) { return S.gbase + (int64_t)myri[r] * D + col; };
+  if constexpr (ChunkIO<T, St::DK, St::ROWS>::DIRECT) {
+    S.io_q.issue_elem_at(qelem, q_lds);
+    S.io_g.issue_elem_at(gelem, g_lds);
+  } else {
+    S.io_q.issue_elem(qelem, *Q);
+    S.io_g.issue_elem(gelem, *G);
+  }
+}
 template <typename St>
 __device__ __forceinline__ void issue_chunk(const PagedParams &p, St &S, int c, const int *ri,
                                             float *st, typename St::QTile *Q,
                                             typename St::GTile *G) {
-  constexpr int D = St::D, P = St::P;
-  const int *myri = ri + 64 * S.wave;
-  float *myst = st + kStatWave * S.wave;
-  const int rh = myri[S.lane];
-  const float *srow = S.sbase + 3 * (int64_t)rh;
-  dma_lds4(myst, srow);
-  dma_lds4(myst + 64, srow + 1);
-  dma_lds4(myst + 128, srow + 2);
-  dma_lds4(myst + 192, S.pos_tab + min(c * St::ROWS + S.lane, S.nqh - 1));
-  if constexpr (P > 0) {
-    // a row of the tile is [q | qp]: columns below D from q, the rest from qp
-    S.io_q.issue_elem(
-        [&](int r, int col) {
-          return col < D ? S.qbase + (int64_t)myri[r] * D + col
-                         : S.qpbase + (int64_t)myri[r] * P + (col - D);
-        },
-        *Q);
-  } else {
-    S.io_q.issue_at([&](int r) { return S.qbase + (int64_t)myri[r] * D; }, *Q);
-  }
-  S.io_g.issue_at([&](int r) { return S.gbase + (int64_t)myri[r] * D; }, *G);
+  issue_chunk(p, S, c, ri, lds_addr(st), Q, G, lds_addr(Q), lds_addr(G));
 }
 
 // Replace max by -lse2 / scale_log2 in this wave's statistics of chunk c
@@ -127,8 +147,13 @@ __device__ __forceinline__ void paged_step(const PagedParams &p, St &S, int c,
   const int bc = S.buf, bn = bc == 0 ? 2 : bc - 1, bz = bc == 2 ? 0 : bc + 1;
   const bool issued = c + 2 <= S.c_last;
   if (issued) {
-    issue_rowinfo(S, c + 4, ri[bz]);  // always issued with the chunk: fixed count per step
-    issue_chunk(p, S, c + 2, ri[bn], st[bn], &Qs[bn], &Gs[bn]);
+    // LDS byte addresses of the run-time-picked buffers, as wave-uniform integers
+    constexpr unsigned QB = sizeof(Qs[0]), GB = sizeof(Gs[0]), SB = sizeof(st[0]),
+                       RB = sizeof(ri[0]);
+    auto uni = [](unsigned x) { return (unsigned)__builtin_amdgcn_readfirstlane(x); };
+    issue_rowinfo_at(S, c + 4, uni(lds_addr(ri) + bz * RB));  // always issued with the chunk
+    issue_chunk(p, S, c + 2, ri[bn], uni(lds_addr(st) + bn * SB), &Qs[bn], &Gs[bn],
+                uni(lds_addr(Qs) + bn * QB), uni(lds_addr(Gs) + bn * GB));
   }
   convert_stats(p, S, c, st[bc]);
   const float *myst = st[bc] + kStatWave * S.wave;
