@@ -122,8 +122,9 @@ template <> __device__ __forceinline__ float frag_dot<float>(float a, float b) {
 // -f (a sign flip per element).
 template <typename T> __device__ __forceinline__ typename MT<T>::frag neg_frag(typename MT<T>::frag f);
 template <> __device__ __forceinline__ bf16x8 neg_frag<bf16>(bf16x8 f) {
-  typedef short s16x8 __attribute__((ext_vector_type(8)));
-  return __builtin_bit_cast(bf16x8, __builtin_bit_cast(s16x8, f) ^ (short)0x8000);
+  // both sign bits of each packed pair in one 32-bit xor
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, f) ^ 0x80008000u);
 }
 template <> __device__ __forceinline__ float neg_frag<float>(float f) { return -f; }
 
