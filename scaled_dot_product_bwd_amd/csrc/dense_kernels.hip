@@ -894,11 +894,12 @@ __device__ __forceinline__ void sd_step(const DenseParams &p, SdState<T, D> &S, 
       S.acc_b[t] *= al;
     }
   }
-  // delta's running estimate, this chunk included (the expression
-  // row_stat_final uses, so after the last chunk it is delta itself)
+  // delta's running estimate, this chunk included, through the hardware
+  // reciprocal (l_tot >= 1 once a key is visible: the row's max term is
+  // 2^(mtrue - mref) >= 1).  The epilogue moves A' to delta itself.
   const float l_tot = S.st.l + __shfl_xor(S.st.l, 32);
   const float dl_tot = S.st.dl + __shfl_xor(S.st.dl, 32);
-  const float dh = l_tot > 0.f ? dl_tot / l_tot : 0.f;
+  const float dh = l_tot > 0.f ? dl_tot * __builtin_amdgcn_rcpf(l_tot) : 0.f;
   const float shift = S.dh - dh;
   S.dh = dh;
   F uf[NU][CS], pf[NU][CS];
@@ -1012,10 +1013,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   if (S.qi < p.Sq && half == 0) store_row_stat(p, ((int64_t)b * p.H + h) * p.Sq + S.qi, o);
   if (p.dq == nullptr) return;  // statistics only (dQ not requested)
 
-  // dQ^T = A'^T * scale / l per lane column (row): after the last chunk the
-  // estimate is delta itself (o.delta, bit for bit), so A' = A - delta B.
-  // Whole rows stored through LDS (the chunk tiles are free: the last step
-  // ended with a barrier).
+  // dQ^T = A'^T * scale / l per lane column (row), once A' = A - dh B is moved
+  // to A - delta B with delta = o.delta, the stored statistic.  Whole rows
+  // stored through LDS (the chunk tiles are free: the last step ended with a
+  // barrier).
+  {
+    const float shift = S.dh - o.delta;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S.acc_a[t][r] = fmaf(shift, S.acc_b[t][r], S.acc_a[t][r]);
+  }
   typedef RowStore<T, D> RS;
   static_assert(4 * RS::BYTES <= sizeof(Ks), "row staging fits the chunk tiles");
   char *lq = reinterpret_cast<char *>(Ks) + w * RS::BYTES;
