@@ -17,8 +17,10 @@
 // Schedule.  With one wave per SIMD nothing hides latency but the wave's own
 // instruction order, so the body is written as an explicit software pipeline
 // and fenced with scheduling barriers that the compiler keeps:
-//   * every MFMA's LDS operand is read three MFMAs ahead (a ring of four
-//     fragment registers), so an MFMA never waits for the LDS;
+//   * a step's LDS operands (one per MFMA, two MFMAs a step) are read two
+//     steps ahead (a ring of three fragment registers per operand), so an
+//     MFMA rarely waits for the LDS; a deeper ring costs registers (AGPR
+//     copies) and measured slower;
 //   * phase B of sub-tile 0 is spread over phase A of sub-tile 1, and phase B
 //     of sub-tile 1 over phase C of sub-tile 0, so the softmax VALU work issues
 //     while the matrix core runs.
@@ -82,7 +84,7 @@ __device__ __forceinline__ void kv_chunk(const typename MT<T>::frag *kf,
   constexpr int NSUB = KvShape<T>::NSUB;
   constexpr int NA = NSUB * NSD;    // phase-A steps (S, and dP while s < NSV)
   constexpr int NC = NSUB * CS * NT;  // phase-C steps (dK, and dV while t < NTV)
-  constexpr int RING = 4;
+  constexpr int RING = 3;
   static_assert(NDMA <= NA + NC, "one load per step");
   const int l32 = lane & 31, half = lane >> 5;
 
