@@ -39,7 +39,7 @@ namespace attn {
 // balance of the causal block sizes, few enough to keep their operands in L2.
 // Measured: dK / dV and dQ run as fast with 2 and 4 as with all of an XCD's
 // heads; the row statistics (three workgroups per CU) are faster with all.
-constexpr int kKvGroup = 2, kDqGroup = 4, kRsGroup = 8;
+constexpr int kKvGroup = 8, kDqGroup = 4, kRsGroup = 8;
 
 // The query-major kernels' chunk loops (dQ, and statistics + dQ) are unrolled
 // by three, so every step has its LDS buffers fixed at compile time (no
