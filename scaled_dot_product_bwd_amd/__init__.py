@@ -57,11 +57,168 @@ def _strides3(t):
     return (s[0], s[1], s[2])
 
 
+# ---------------------------------------------------------------------------
+# Argument checks on the torch side.  The C ABI takes raw pointers and cannot
+# tell a host address from a device one, nor see a tensor's dtype: a CPU tensor
+# or a mismatched dtype would reach a kernel as a wild pointer or a buffer read
+# past its end.  So every tensor is checked here, before its pointer is taken:
+# dtype and shape first, then the device (all on q's GPU).
+
+def _fail(msg):
+    raise ValueError(msg)
+
+
+def _check_float(name, t, dtype):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        _fail(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        _fail(f"{name} is {t.dtype}, expected {dtype}")
+
+
+def _check_rows(name, t, shape):
+    """t has exactly `shape` and a contiguous last axis (the kernels read D
+    contiguous elements per row and are given only the outer strides)."""
+    if tuple(t.shape) != tuple(shape):
+        _fail(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dim() and t.shape[-1] > 1 and t.stride(-1) != 1:
+        _fail(f"{name} must have a contiguous last axis (stride {t.stride(-1)})")
+
+
+def _check_devices(ref_device, named):
+    if ref_device.type != "cuda":
+        _fail(f"tensors must be on a CUDA (HIP) device, got {ref_device}")
+    for name, t in named:
+        if t is not None and t.device != ref_device:
+            _fail(f"{name} is on {t.device}, expected {ref_device} (the device of q)")
+
+
+def _io_dtype(q):
+    torch = _torch()
+    if not isinstance(q, torch.Tensor):
+        _fail(f"q must be a torch.Tensor, got {type(q).__name__}")
+    if q.dtype not in (torch.float32, torch.bfloat16):
+        _fail(f"q is {q.dtype}: the kernels take float32 or bfloat16")
+    return q.dtype
+
+
+def check_dense_tensors(q, k, v, dy, dq=None, dk=None, dv=None, mask=None, workspace=None,
+                        fwd_lse=None, fwd_out=None):
+    """Raises ValueError unless the tensors fit one dense call: q, dy
+    [B, Sq, H, D]; k, v [B, Sk, Hkv, D] (H a multiple of Hkv); outputs shaped
+    like their inputs; all of q's dtype (float32 or bfloat16) with a contiguous
+    last axis; mask float32 broadcastable to [B, H, Sq, Sk]; fwd_lse float32
+    [B, H, Sq]; fwd_out like q; everything on q's GPU."""
+    torch = _torch()
+    dt = _io_dtype(q)
+    if q.dim() != 4:
+        _fail(f"q must be [B, S, H, D], got {q.dim()} dims")
+    B, Sq, H, D = q.shape
+    if not isinstance(k, torch.Tensor) or k.dim() != 4:
+        _fail("k must be a [B, S, H, D] tensor")
+    Sk, Hkv = k.shape[1], k.shape[2]
+    named = [("q", q), ("k", k), ("v", v), ("dy", dy), ("dq", dq), ("dk", dk), ("dv", dv)]
+    shapes = {"q": (B, Sq, H, D), "dy": (B, Sq, H, D), "dq": (B, Sq, H, D),
+              "k": (B, Sk, Hkv, D), "v": (B, Sk, Hkv, D), "dk": (B, Sk, Hkv, D),
+              "dv": (B, Sk, Hkv, D)}
+    for name, t in named:
+        if t is None and name in ("q", "k", "v", "dy"):
+            _fail(f"{name} is required")
+        if t is not None:
+            _check_float(name, t, dt)
+            _check_rows(name, t, shapes[name])
+    if mask is not None:
+        _check_float("mask", mask, torch.float32)
+        try:
+            torch.broadcast_shapes(tuple(mask.shape), (B, H, Sq, Sk))
+        except RuntimeError:
+            _fail(f"mask of shape {tuple(mask.shape)} does not broadcast to {(B, H, Sq, Sk)}")
+    if fwd_lse is not None:
+        _check_float("fwd_lse", fwd_lse, torch.float32)
+        if tuple(fwd_lse.shape) != (B, H, Sq):
+            _fail(f"fwd_lse has shape {tuple(fwd_lse.shape)}, expected {(B, H, Sq)}")
+    if fwd_out is not None:
+        _check_float("fwd_out", fwd_out, dt)
+        _check_rows("fwd_out", fwd_out, (B, Sq, H, D))
+    if workspace is not None and not isinstance(workspace, torch.Tensor):
+        _fail("workspace must be a torch.Tensor")
+    _check_devices(q.device, named + [("mask", mask), ("workspace", workspace),
+                                      ("fwd_lse", fwd_lse), ("fwd_out", fwd_out)])
+
+
+def check_paged_tensors(q, dy, k_pool, v_pool, stats, plan, dk_pool=None, dv_pool=None, *,
+                        qp=None, kp_pool=None, dkp_pool=None, outs=()):
+    """Raises ValueError unless the tensors fit one paged call: q, dy
+    [nq, heads, D]; pools [slots, kv_heads, D] (gradient pools shaped like
+    them); stats float32 [nq, heads, 3]; latent position parts qp
+    [nq, heads, P], kp_pool / dkp_pool [slots, kv_heads, P]; all contiguous, of
+    q's dtype (float32 or bfloat16) except stats, on q's GPU, where the plan's
+    device copy must live too.  outs: extra (name, tensor, shape, dtype)
+    outputs (the query side's statistics or dQ)."""
+    torch = _torch()
+    dt = _io_dtype(q)
+    if q.dim() != 3:
+        _fail(f"q must be [nq, heads, D], got {q.dim()} dims")
+    nq, heads, D = q.shape
+    if not isinstance(k_pool, torch.Tensor) or k_pool.dim() != 3:
+        _fail("k_pool must be a [slots, kv_heads, D] tensor")
+    slots, kvh = k_pool.shape[0], k_pool.shape[1]
+    named = [("q", q, (nq, heads, D), dt), ("dy", dy, (nq, heads, D), dt),
+             ("k_pool", k_pool, (slots, kvh, D), dt), ("v_pool", v_pool, (slots, kvh, D), dt),
+             ("stats", stats, (nq, heads, 3), torch.float32),
+             ("dk_pool", dk_pool, (slots, kvh, D), dt), ("dv_pool", dv_pool, (slots, kvh, D), dt)]
+    if qp is not None:
+        P = qp.shape[-1] if qp.dim() == 3 else -1
+        named += [("qp", qp, (nq, heads, P), dt), ("kp_pool", kp_pool, (slots, kvh, P), dt),
+                  ("dkp_pool", dkp_pool, (slots, kvh, P), dt)]
+    named += list(outs)
+    for name, t, shape, want in named:
+        if t is None:
+            if name in ("q", "dy", "k_pool", "stats"):
+                _fail(f"{name} is required")
+            continue
+        _check_float(name, t, want)
+        _check_rows(name, t, shape)
+        if not t.is_contiguous():
+            _fail(f"{name} must be contiguous")
+    if plan.device_words is not None and plan.device_words.device != q.device:
+        _fail(f"the plan was uploaded to {plan.device_words.device}, expected {q.device}")
+    _check_devices(q.device, [(n, t) for n, t, _, _ in named])
+
+
+# ---------------------------------------------------------------------------
+# Streams.  Work is enqueued on the caller's stream (default: the current one).
+# When that is another stream, it first waits for the current stream (where the
+# binding allocated, filled, copied or uploaded what the call reads), and every
+# tensor the binding created for the call is recorded on it, so torch's caching
+# allocator does not hand that memory to later work on the current stream while
+# the kernels may still run.
+
+def _launch_stream(stream, device):
+    """(void* handle, side) -- side is the caller's stream when it is not the
+    current one, else None."""
+    torch = _torch()
+    cur = torch.cuda.current_stream(device)
+    if stream is None or stream == cur:
+        return ctypes.c_void_p(cur.cuda_stream), None
+    stream.wait_stream(cur)
+    return ctypes.c_void_p(stream.cuda_stream), stream
+
+
+def _record(side, *tensors):
+    if side is not None:
+        for t in tensors:
+            if t is not None:
+                t.record_stream(side)
+
+
 def make_args(q, k, v, dy, dq=None, dk=None, dv=None, *, wrt="all", mask_kind="none",
               causal=False, window=0, mask=None, threshold=0.5, scale=None, workspace=None):
-    """Builds the attn_bwd_args struct for already-allocated tensors (no checks:
-    the library validates)."""
+    """Builds the attn_bwd_args struct for already-allocated tensors.  The
+    tensors are checked here (check_dense_tensors: dtype, shape, device); sizes,
+    strides, alignment and aliasing are validated by the library."""
     torch = _torch()
+    check_dense_tensors(q, k, v, dy, dq, dk, dv, mask=mask, workspace=workspace)
     B, Sq, H, D = q.shape
     Sk = k.shape[1]
     a = AttnBwdArgs()
@@ -106,7 +263,9 @@ def _stream_handle(stream):
 
 def attn_bwd_stage(stage: str, args: AttnBwdArgs, stream=None):
     """Runs one stage ("all", "row_stats", "kv", "dq" or "stats_dq") of the
-    backward on the given (default: current) torch stream."""
+    backward on the given (default: current) torch stream.  The tensors behind
+    `args` belong to the caller, who keeps them alive (and, on a side stream,
+    ordered) until the stream has passed this call."""
     lib = load_library()
     fn = {"all": lib.attn_bwd, "row_stats": lib.attn_bwd_row_stats, "kv": lib.attn_bwd_kv,
           "dq": lib.attn_bwd_dq, "stats_dq": lib.attn_bwd_stats_dq}[stage]
@@ -131,6 +290,11 @@ def attn_bwd(q, k, v, dy, *, wrt="all", mask_kind="none", causal=False, window=0
     Returns (dq, dk, dv); entries that ``wrt`` does not ask for are None.
     """
     torch = _torch()
+    if fwd_lse is not None or fwd_out is not None:
+        if fwd_lse is None or fwd_out is None:
+            raise ValueError("fwd_lse and fwd_out go together")
+    check_dense_tensors(q, k, v, dy, *(out if out is not None else (None, None, None)),
+                        mask=mask, workspace=workspace, fwd_lse=fwd_lse, fwd_out=fwd_out)
     B, Sq, H, D = q.shape
     w = WRT[wrt] if isinstance(wrt, str) else int(wrt)
     if out is None:
@@ -145,16 +309,16 @@ def attn_bwd(q, k, v, dy, *, wrt="all", mask_kind="none", causal=False, window=0
     args = make_args(q, k, v, dy, dq, dk, dv, wrt=w, mask_kind=mask_kind, causal=causal,
                      window=window, mask=mask, threshold=threshold, scale=scale,
                      workspace=workspace)
-    if fwd_lse is not None or fwd_out is not None:
-        if fwd_lse is None or fwd_out is None:
-            raise ValueError("fwd_lse and fwd_out go together")
-        lse = fwd_lse.contiguous()
+    lse = fwd_lse.contiguous() if fwd_lse is not None else None
+    handle, side = _launch_stream(stream, q.device)
+    if fwd_lse is not None:
         ost = (ctypes.c_int64 * 3)(*_strides3(fwd_out))
         _check(load_library().attn_bwd_from_forward(
             ctypes.byref(args), ctypes.c_void_p(lse.data_ptr()), ctypes.c_void_p(fwd_out.data_ptr()),
-            ost, _stream_handle(stream)))
+            ost, handle))
     else:
-        attn_bwd_stage("all", args, stream)
+        _check(load_library().attn_bwd(ctypes.byref(args), handle))
+    _record(side, dq, dk, dv, workspace, lse)
     if return_workspace:
         return (dq, dk, dv), workspace
     return dq, dk, dv
@@ -247,8 +411,13 @@ def paged_plan(seq_lens, block_table, query_seq, query_pos, *, heads, kv_heads, 
 
 
 def make_paged_args(q, dy, k_pool, v_pool, stats, plan, dk_pool=None, dv_pool=None, *,
-                    causal=True, scale=None, need=3):
+                    causal=True, scale=None, need=3, outs=()):
+    """Builds the attn_bwd_paged_args struct; the tensors are checked first
+    (check_paged_tensors), the plan must already be on q's device."""
     torch = _torch()
+    if plan.device_words is None:
+        raise ValueError("the plan has no device copy: call plan.to(device) first")
+    check_paged_tensors(q, dy, k_pool, v_pool, stats, plan, dk_pool, dv_pool, outs=outs)
     nq, heads, D = q.shape
     a = AttnBwdPagedArgs()
     a.dtype = ATTN_BF16 if q.dtype == torch.bfloat16 else ATTN_F32
@@ -280,18 +449,18 @@ def attn_bwd_paged(q, dy, k_pool, v_pool, stats, plan, *, dk_pool=None, dv_pool=
     a PagedPlan uploaded to the same device.  Returns (dk_pool, dv_pool)."""
     torch = _torch()
     n = {"dk": 1, "dv": 2, "dkdv": 3}[need] if isinstance(need, str) else int(need)
+    check_paged_tensors(q, dy, k_pool, v_pool, stats, plan, dk_pool, dv_pool)
     if plan.device_words is None:
         plan.to(q.device)
-    for t in (q, dy, k_pool, v_pool, stats):
-        if not t.is_contiguous():
-            raise ValueError("attn_bwd_paged takes contiguous tensors")
     if dk_pool is None and n & 1:
         dk_pool = torch.zeros_like(k_pool)
     if dv_pool is None and n & 2:
         dv_pool = torch.zeros_like(v_pool)
     args = make_paged_args(q, dy, k_pool, v_pool, stats, plan, dk_pool, dv_pool,
                            causal=causal, scale=scale, need=n)
-    _check(load_library().attn_bwd_paged(ctypes.byref(args), _stream_handle(stream)))
+    handle, side = _launch_stream(stream, q.device)
+    _check(load_library().attn_bwd_paged(ctypes.byref(args), handle))
+    _record(side, dk_pool, dv_pool, plan.device_words)
     return dk_pool, dv_pool
 
 
@@ -307,14 +476,13 @@ def attn_bwd_paged_mla(q, qp, dy, latent_pool, kp_pool, stats, plan, *, dlat_poo
     need: "dlat", "dkp" or "both".  Returns (dlat_pool, dkp_pool)."""
     torch = _torch()
     n = {"dlat": 1, "dkp": 4, "both": 5}[need] if isinstance(need, str) else int(need)
+    check_paged_tensors(q, dy, latent_pool, latent_pool, stats, plan, dlat_pool, None, qp=qp,
+                        kp_pool=kp_pool, dkp_pool=dkp_pool)
     D, P = q.shape[2], qp.shape[2]
     if P == 0:
         n &= 1
     if plan.device_words is None:
         plan.to(q.device)
-    for t in (q, qp, dy, latent_pool, kp_pool, stats):
-        if not t.is_contiguous():
-            raise ValueError("attn_bwd_paged_mla takes contiguous tensors")
     if dlat_pool is None and n & 1:
         dlat_pool = torch.zeros_like(latent_pool)
     if dkp_pool is None and n & 4:
@@ -329,7 +497,9 @@ def attn_bwd_paged_mla(q, qp, dy, latent_pool, kp_pool, stats, plan, *, dlat_poo
     args.kp_pool = kp_pool.data_ptr() if kp_pool.numel() else None
     if dkp_pool is not None:
         args.dkp_pool = dkp_pool.data_ptr()
-    _check(load_library().attn_bwd_paged(ctypes.byref(args), _stream_handle(stream)))
+    handle, side = _launch_stream(stream, q.device)
+    _check(load_library().attn_bwd_paged(ctypes.byref(args), handle))
+    _record(side, dlat_pool, dkp_pool, plan.device_words)
     return dlat_pool, dkp_pool
 
 
@@ -353,17 +523,25 @@ def paged_row_stats(q, dy, k_pool, v_pool, plan, *, causal=True, scale=None, out
     the split form (each block's tokens in pieces; a workspace is allocated
     unless one is given)."""
     torch = _torch()
+    _io_dtype(q)
     nq, heads, D = q.shape
+    if out is not None:  # checked as the call's input statistics below
+        _check_float("out", out, torch.float32)
     if plan.device_words is None:
         plan.to(q.device)
     if out is None:
         out = torch.empty(nq, heads, 3, dtype=torch.float32, device=q.device)
     dummy = out  # the struct's input statistics are not read by this call
     args = make_paged_args(q, dy, k_pool, v_pool, dummy, plan, causal=causal, scale=scale)
+    ws = None
     if split:
-        _set_q_workspace(args, workspace if workspace is not None else paged_q_workspace(plan, D, q.device))
+        ws = workspace if workspace is not None else paged_q_workspace(plan, D, q.device)
+        _check_devices(q.device, [("workspace", ws)])
+        _set_q_workspace(args, ws)
+    handle, side = _launch_stream(stream, q.device)
     _check(load_library().attn_bwd_paged_row_stats(ctypes.byref(args), ctypes.c_void_p(out.data_ptr()),
-                                                   _stream_handle(stream)))
+                                                   handle))
+    _record(side, out, ws, plan.device_words)
     return out
 
 
@@ -372,13 +550,20 @@ def attn_bwd_paged_dq(q, dy, k_pool, v_pool, stats, plan, *, causal=True, scale=
     """dQ [nq, heads, D] of the paged layout from the statistics (attn_bwd_paged_dq).
     split: as for paged_row_stats."""
     torch = _torch()
+    dt = _io_dtype(q)
     if plan.device_words is None:
         plan.to(q.device)
     if out is None:
-        out = torch.empty_like(q)
-    args = make_paged_args(q, dy, k_pool, v_pool, stats, plan, causal=causal, scale=scale)
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    args = make_paged_args(q, dy, k_pool, v_pool, stats, plan, causal=causal, scale=scale,
+                           outs=[("dq", out, tuple(q.shape), dt)])
+    ws = None
     if split:
-        _set_q_workspace(args, workspace if workspace is not None else paged_q_workspace(plan, q.shape[2], q.device))
+        ws = workspace if workspace is not None else paged_q_workspace(plan, q.shape[2], q.device)
+        _check_devices(q.device, [("workspace", ws)])
+        _set_q_workspace(args, ws)
+    handle, side = _launch_stream(stream, q.device)
     _check(load_library().attn_bwd_paged_dq(ctypes.byref(args), ctypes.c_void_p(out.data_ptr()),
-                                            _stream_handle(stream)))
+                                            handle))
+    _record(side, out, ws, plan.device_words)
     return out
