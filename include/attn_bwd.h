@@ -92,8 +92,8 @@ typedef struct attn_bwd_args {
   const float *mask;       /* device fp32, KEYPAD validity or BIAS values; else ignored */
   int64_t mask_stride[4];  /* (b, h, i, j) element strides, 0 = broadcast ([B,Sk] padding: {Sk,0,0,1}) */
   float mask_threshold;    /* KEYPAD: key hidden iff value < threshold */
-  float scale;             /* finite, |scale| >= 2^-64 (else ATTN_E_UNSUPPORTED); callers
-                              usually pass (float)(1/sqrt(D)) */
+  float scale;             /* 2^-64 <= |scale| <= 2^64 (else ATTN_E_UNSUPPORTED; NaN or inf:
+                              ATTN_E_INVALID); callers usually pass (float)(1/sqrt(D)) */
   void *workspace;         /* device, >= attn_bwd_workspace_bytes(B, H, Sq) bytes, 256-byte aligned */
   size_t workspace_bytes;
   int64_t Hkv;             /* K / V heads (grouped-query attention); 0 means H.  H must be a
@@ -106,7 +106,8 @@ typedef struct attn_bwd_args {
  * scores, plane 1 = denominator l = sum exp(s - m), plane 2 = delta =
  * rowsum(P * dP), plane 3 = internal (-lse / scale, lse = m + ln l).  Row (b, h, i)
  * sits at index (b * H + h) * Sq + i.  An empty row holds m = -inf, l = 0,
- * delta = 0.  Returns 0 for negative sizes. */
+ * delta = 0.  Returns 0 for negative sizes, and SIZE_MAX when the planes would
+ * exceed 2^60 bytes (sizes attn_bwd rejects). */
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq);
 
 /* The whole dense backward, as `wrt` asks.  bf16: one query-major pass
@@ -188,7 +189,7 @@ typedef struct attn_bwd_paged_args {
   int32_t need;       /* bit 0: dK, bit 1: dV (at least one); latent variant: see below */
   int32_t heads, kv_heads, head_dim, page_size, causal; /* head_dim in {32, 64, 128}; causal 0 / 1 */
   int32_t nq, pool_pages;                /* must match the plan */
-  float scale;                           /* finite, |scale| >= 2^-64 */
+  float scale;                           /* 2^-64 <= |scale| <= 2^64 */
   const void *q, *dy;                    /* device [nq, heads, head_dim], contiguous */
   const void *k_pool, *v_pool;           /* device [pool_pages * page_size, kv_heads, head_dim] */
   const float *stats;                    /* device [nq, heads, 3] = (max, denominator, delta) */
@@ -226,12 +227,17 @@ typedef struct attn_bwd_paged_args {
 
 /* Enqueues the paged backward.  Every device pointer must be 16-byte aligned;
  * the gradient pools may not overlap any input or each other.  The device plan
- * must be an unmodified copy of plan_host (it is trusted: its tables address
- * the pools).  A plan with no item does nothing. */
+ * must be an unmodified copy of plan_host.  Trust boundary: the library checks
+ * the host copy (magic, header offsets inside the plan, geometry equal to the
+ * arguments) but never reads the device copy on the host; the kernels trust
+ * its tables, which address the pools.  Every plan attn_bwd_paged_plan_build
+ * writes keeps each table inside the plan, each slot inside the pool and each
+ * query row inside [0, nq * heads).  A plan with no item does nothing. */
 int attn_bwd_paged(const attn_bwd_paged_args *a, void *stream);
 
 /* The query side of the paged backward, for callers without forward
- * statistics (ruDNN computes them "once by the query kernel"): the same
+ * statistics (in ruDNN history_backward a separate query-side kernel produces
+ * them, one triple per row): the same
  * arguments and plan as attn_bwd_paged, `need` ignored.
  *
  * attn_bwd_paged_row_stats writes `stats` (device [nq, heads, 3] fp32, the

@@ -18,8 +18,10 @@
 #include "paged.hpp"
 
 // The dK / dV kernels start the score accumulators at -lse2 / (scale log2 e),
-// so the scale must have an invertible, normal-range magnitude.
+// so the scale must have an invertible, normal-range magnitude, and scale log2 e
+// must stay finite: 2^-64 <= |scale| <= 2^64.
 constexpr float kMinScale = 5.421010862427522e-20f;  // 2^-64
+constexpr float kMaxScale = 1.8446744073709552e19f;  // 2^64
 
 namespace {
 
@@ -35,27 +37,50 @@ int fail(int code, const char *fmt, ...) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Largest byte extent a tensor may have: keeps every offset sum below 2^63.
+constexpr int64_t kMaxBytes = (int64_t)1 << 60;
+
+// Bytes of B * H * Sq fp32 values (sizes >= 0), or -1 beyond kMaxBytes.
+int64_t stat_bytes(int64_t B, int64_t H, int64_t Sq) {
+  int64_t n;
+  if (__builtin_mul_overflow(B, H, &n) || __builtin_mul_overflow(n, Sq, &n) ||
+      __builtin_mul_overflow(n, (int64_t)sizeof(float), &n) || n > kMaxBytes)
+    return -1;
+  return n;
+}
+
+// One statistics plane, 256-byte aligned; 0 beyond kMaxBytes (validate()
+// rejects such sizes before it asks).
 size_t plane_bytes(int64_t B, int64_t H, int64_t Sq) {
-  return align256((size_t)B * (size_t)H * (size_t)Sq * sizeof(float));
+  const int64_t n = stat_bytes(B, H, Sq);
+  return n < 0 ? 0 : align256((size_t)n);
 }
 
 // Byte range [lo, hi) covered by a [n0, n1, n2, n3] tensor with element strides
-// st[0..3] (last one for the innermost axis); empty if any extent is 0.
+// st[0..3] (last one for the innermost axis, all >= 0); empty if any extent is
+// 0.  `ok` turns false when the range exceeds kMaxBytes or the address space
+// (the arithmetic is exact: 128-bit).
 struct Range {
   uintptr_t lo = 0, hi = 0;
   bool empty() const { return hi <= lo; }
 };
 
-Range extent(const void *p, const int64_t n[4], const int64_t st[4], size_t esize) {
+Range extent(const void *p, const int64_t n[4], const int64_t st[4], size_t esize, bool &ok) {
   Range r;
+  ok = true;
   if (!p) return r;
-  int64_t last = 0;
+  __int128 last = 0;
   for (int i = 0; i < 4; ++i) {
     if (n[i] <= 0) return r;
-    last += (n[i] - 1) * st[i];
+    last += (__int128)(n[i] - 1) * st[i];
+  }
+  const __int128 bytes = (last + 1) * (__int128)esize;
+  if (bytes > kMaxBytes || (__int128)(uintptr_t)p + bytes > (__int128)UINTPTR_MAX) {
+    ok = false;
+    return r;
   }
   r.lo = (uintptr_t)p;
-  r.hi = r.lo + (uintptr_t)((last + 1) * (int64_t)esize);
+  r.hi = r.lo + (uintptr_t)bytes;
   return r;
 }
 
@@ -92,8 +117,8 @@ int validate(const attn_bwd_args *a, Checked &c) {
   if (a->D != 32 && a->D != 64 && a->D != 128)
     return fail(ATTN_E_UNSUPPORTED, "head_dim %lld is not 32, 64 or 128", (long long)a->D);
   if (!std::isfinite(a->scale)) return fail(ATTN_E_INVALID, "scale is not finite");
-  if (std::fabs(a->scale) < kMinScale)
-    return fail(ATTN_E_UNSUPPORTED, "|scale| below 2^-64 (including 0) is not supported");
+  if (std::fabs(a->scale) < kMinScale || std::fabs(a->scale) > kMaxScale)
+    return fail(ATTN_E_UNSUPPORTED, "|scale| outside [2^-64, 2^64] (including 0) is not supported");
   if (a->mask_kind == ATTN_MASK_WINDOW && a->window < 0)
     return fail(ATTN_E_INVALID, "window %lld is negative", (long long)a->window);
   if (a->mask_kind == ATTN_MASK_KEYPAD && std::isnan(a->mask_threshold))
@@ -106,8 +131,8 @@ int validate(const attn_bwd_args *a, Checked &c) {
   if (Hkv < 0 || (a->H > 0 && (Hkv == 0 || a->H % Hkv != 0)) || (a->H == 0 && Hkv != 0))
     return fail(ATTN_E_INVALID, "H (%lld) must be a positive multiple of Hkv (%lld)",
                 (long long)a->H, (long long)a->Hkv);
-  const int64_t heads = a->B * a->H;
   if (a->H > 0 && a->B > INT32_MAX / a->H) return fail(ATTN_E_INVALID, "B * H too large");
+  const int64_t heads = a->B * a->H;
   if (heads * (nblk_q > nblk_k ? nblk_q : nblk_k) > INT32_MAX)
     return fail(ATTN_E_INVALID, "problem too large for one launch");
 
@@ -145,16 +170,21 @@ int validate(const attn_bwd_args *a, Checked &c) {
       if (ts[i].st[j] < 0) return fail(ATTN_E_INVALID, "%s has a negative stride", ts[i].name);
     if ((uintptr_t)ts[i].ptr % 16)
       return fail(ATTN_E_UNSUPPORTED, "%s is not 16-byte aligned", ts[i].name);
-    for (int j = 0; j < 3; ++j)
+    for (int j = 0; j < 3; ++j) {
+      if (ts[i].st[j] > kMaxBytes)
+        return fail(ATTN_E_INVALID, "%s stride %d is larger than 2^60", ts[i].name, j);
       if ((ts[i].st[j] * (int64_t)es) % 16)
         return fail(ATTN_E_UNSUPPORTED, "%s stride %d is not a multiple of 16 bytes", ts[i].name, j);
+    }
     // Streamed chunks address their rows with 32-bit byte offsets.
     if (i < 4 && ts[i].st[1] * 64 * (int64_t)es >= ((int64_t)1 << 31))
       return fail(ATTN_E_UNSUPPORTED, "%s sequence stride %lld is too large (64 rows must span < 2 GiB)",
                   ts[i].name, (long long)ts[i].st[1]);
     const int64_t n[4] = {a->B, ts[i].S, ts[i].nh, a->D};
     const int64_t st[4] = {ts[i].st[0], ts[i].st[1], ts[i].st[2], 1};
-    rng[i] = extent(ts[i].ptr, n, st, es);
+    bool ok;
+    rng[i] = extent(ts[i].ptr, n, st, es, ok);
+    if (!ok) return fail(ATTN_E_INVALID, "%s spans more than 2^60 bytes", ts[i].name);
   }
 
   const bool masked = a->mask_kind == ATTN_MASK_KEYPAD || a->mask_kind == ATTN_MASK_BIAS;
@@ -165,7 +195,9 @@ int validate(const attn_bwd_args *a, Checked &c) {
     for (int j = 0; j < 4; ++j)
       if (a->mask_stride[j] < 0) return fail(ATTN_E_INVALID, "mask has a negative stride");
     const int64_t n[4] = {a->B, a->H, a->Sq, a->Sk};
-    mrng = extent(a->mask, n, a->mask_stride, sizeof(float));
+    bool ok;
+    mrng = extent(a->mask, n, a->mask_stride, sizeof(float), ok);
+    if (!ok) return fail(ATTN_E_INVALID, "mask spans more than 2^60 bytes");
   }
 
   const size_t ws_need = attn_bwd_workspace_bytes(a->B, a->H, a->Sq);
@@ -293,6 +325,7 @@ int run_from_forward(const attn_bwd_args *a, const float *lse, const void *out,
     if ((uintptr_t)out % 16) return fail(ATTN_E_UNSUPPORTED, "out is not 16-byte aligned");
     for (int j = 0; j < 3; ++j) {
       if (out_stride[j] < 0) return fail(ATTN_E_INVALID, "out has a negative stride");
+      if (out_stride[j] > kMaxBytes) return fail(ATTN_E_INVALID, "out stride %d is larger than 2^60", j);
       if ((out_stride[j] * (int64_t)es) % 16)
         return fail(ATTN_E_UNSUPPORTED, "out stride %d is not a multiple of 16 bytes", j);
     }
@@ -304,7 +337,9 @@ int run_from_forward(const attn_bwd_args *a, const float *lse, const void *out,
     lr.hi = lr.lo + (uintptr_t)(rows * 4);
     const int64_t n[4] = {a->B, a->Sq, a->H, a->D};
     const int64_t st[4] = {out_stride[0], out_stride[1], out_stride[2], 1};
-    orng = extent(out, n, st, es);
+    bool ok;
+    orng = extent(out, n, st, es, ok);
+    if (!ok) return fail(ATTN_E_INVALID, "out spans more than 2^60 bytes");
     if (overlap(ws, lr) || overlap(ws, orng))
       return fail(ATTN_E_INVALID, "lse / out overlap the workspace");
     // The dQ kernel forms delta and -lse2 from lse and O in its prologue and
@@ -362,8 +397,8 @@ int validate_paged(const attn_bwd_paged_args *a, int mode, void *out, attn::Page
     return fail(ATTN_E_UNSUPPORTED, "head_dim %d is not 32, 64 or 128", a->head_dim);
   }
   if (!std::isfinite(a->scale)) return fail(ATTN_E_INVALID, "scale is not finite");
-  if (std::fabs(a->scale) < kMinScale)
-    return fail(ATTN_E_UNSUPPORTED, "|scale| below 2^-64 (including 0) is not supported");
+  if (std::fabs(a->scale) < kMinScale || std::fabs(a->scale) > kMaxScale)
+    return fail(ATTN_E_UNSUPPORTED, "|scale| outside [2^-64, 2^64] (including 0) is not supported");
   if (a->causal != 0 && a->causal != 1) return fail(ATTN_E_INVALID, "causal must be 0 or 1");
   const int32_t *w = a->plan_host;
   if (!w || !a->plan) return fail(ATTN_E_INVALID, "plan_host / plan is NULL");
@@ -553,6 +588,7 @@ size_t attn_bwd_paged_q_workspace_bytes(const int32_t *plan_host, int32_t head_d
 
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq) {
   if (B < 0 || H < 0 || Sq < 0) return 0;
+  if (stat_bytes(B, H, Sq) < 0) return SIZE_MAX;  // never satisfiable
   return 4 * plane_bytes(B, H, Sq);
 }
 

@@ -87,6 +87,7 @@ def _rc(a):
     ("scale", float("inf"), _abi.ATTN_E_INVALID),
     ("scale", 0.0, _abi.ATTN_E_UNSUPPORTED),
     ("scale", -1e-30, _abi.ATTN_E_UNSUPPORTED),
+    ("scale", 3e38, _abi.ATTN_E_UNSUPPORTED),  # scale * log2(e) would overflow to inf
     ("mask_flags", 1, _abi.ATTN_E_INVALID),   # the causal flag needs KEYPAD or BIAS
 ])
 def test_validation_rejects(field, value, code):
@@ -315,3 +316,17 @@ def test_from_forward_rejections():
     rc = lib.attn_bwd_from_forward(ctypes.byref(a), ctypes.c_void_p(a.workspace), ctypes.c_void_p(1 << 28),
                                    ost, None)
     assert rc == _abi.ATTN_E_INVALID and "workspace" in lib.attn_bwd_last_error().decode()
+
+
+def test_validation_survives_huge_strides_and_sizes():
+    """Byte extents are computed exactly: a stride or size whose extent passes
+    2^60 bytes is refused instead of wrapping into a wrong overlap decision."""
+    for field, j, value in (("k_stride", 0, 2 ** 63 - 1), ("dq_stride", 1, 2 ** 61),
+                            ("q_stride", 2, 2 ** 62)):
+        a = _args()
+        getattr(a, field)[j] = value
+        rc, msg = _rc(a)
+        assert rc in (_abi.ATTN_E_INVALID, _abi.ATTN_E_UNSUPPORTED), (field, rc, msg)
+    rc, msg = _rc(_args(B=2 ** 40, H=2 ** 40))
+    assert rc == _abi.ATTN_E_INVALID and "too large" in msg
+    assert sdb.workspace_bytes(2 ** 40, 2 ** 20, 2 ** 20) == 2 ** 64 - 1  # never satisfiable
