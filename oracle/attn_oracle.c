@@ -384,7 +384,7 @@ static void *paged_stats_worker(void *arg) {
 
 /* Row statistics (max, denominator, delta) for the paged layout, from the
  * definition: the row's visible scores, their softmax, and delta = sum_t P dP.
- * [ruDNN] takes these as an input computed "once by the query kernel".
+ * [ruDNN] takes these as an input that a query-side kernel produces per row.
  * Rows are independent; threads split them. */
 int oracle_paged_row_stats(int nseq, const int32_t *seq_lens, const int32_t *block_table,
                            int max_pages, int nq, const int32_t *query_seq,

@@ -35,10 +35,12 @@
 
 namespace attn {
 
-// Heads whose tiles an XCD interleaves (tile_order): enough for longest-first
-// balance of the causal block sizes, few enough to keep their operands in L2.
-// Measured: dK / dV and dQ run as fast with 2 and 4 as with all of an XCD's
-// heads; the row statistics (three workgroups per CU) are faster with all.
+// Heads whose tiles an XCD interleaves (tile_order).  dQ: 4, which balances the
+// causal block sizes as well as all of an XCD's heads and keeps the group's
+// operands in L2.  dK / dV: all 8 of an XCD's heads, whose longest-first order
+// balances best (149.7 us against 153.9 us with 2 and 152.9 us with 4, on the
+// bf16 [4, 2048, 16, 128] causal workload) although it reads Q / dY about 1.5x
+// from HBM.  The row statistics (three workgroups per CU) are fastest with all.
 constexpr int kKvGroup = 8, kDqGroup = 4, kRsGroup = 8;
 
 // The query-major kernels' chunk loops (dQ, and statistics + dQ) are unrolled

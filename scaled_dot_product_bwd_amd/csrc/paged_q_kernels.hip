@@ -1,7 +1,7 @@
 // paged_q_kernels.hip -- the query side of the paged, grouped-query backward:
 // per (query row, head) the statistics (max, denominator, delta) that ruDNN
 // 0.1.43 src/paged_attention/ordered_kernel.rs `history_backward` takes as an
-// input ("computed once by the query kernel"), and dQ.
+// input (a query-side kernel there produces them per row), and dQ.
 //
 // One workgroup per (block of 128 qh rows of one sequence, KV head g); a qh row
 // is a (query row, head of g's group) pair, as in the paged dK / dV kernel.
