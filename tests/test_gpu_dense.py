@@ -1,9 +1,11 @@
 """GPU parity of the dense path (C ABI -> HIP kernels) against the CPU oracle.
 
-Workloads follow the five configurations of the build (see sdpa_inputs.py);
-sizes the oracle finishes in seconds are compared element by element, the full
-bf16 [4, 2048, 16, 128] case is compared on sampled (batch, head) heads, every
-one of whose outputs the oracle computes.
+Workloads follow the five configurations of the build (see sdpa_inputs.py).
+Every output element of every named workload is compared with the oracle,
+including all 64 (batch, head) heads of the full bf16 [4, 2048, 16, 128] one
+(window 256 and plain causal; the oracle runs them on 16 host threads), and
+every named workload is run twice: the second run must reproduce the first
+bit for bit (no atomics, fixed reduction orders).
 """
 import numpy as np
 import pytest
@@ -11,6 +13,17 @@ import torch
 
 import sdpa_inputs
 from gpu_helpers import (TOL, assert_parity, gpu_run, oracle_run, rel_err, sample_heads)
+
+ORACLE_THREADS = 16  # the host share of one GPU on the test machines
+
+
+def _rerun_bitwise(first, *args, **kw):
+    """Runs the same call again and requires identical bits in every output and
+    statistic (NaN-free outputs: the first run's parity check rejects NaN)."""
+    again = gpu_run(*args, **kw)
+    for n in ("dq", "dk", "dv", "m", "l", "delta"):
+        if first.get(n) is not None:
+            assert np.array_equal(first[n], again[n]), f"{n}: rerun differs"
 
 pytestmark = pytest.mark.gpu
 
@@ -25,6 +38,7 @@ def test_config1_fp32_no_mask():
     res = gpu_run(q, k, v, dy)
     ref = oracle_run(q, k, v, dy)
     print("config1", assert_parity(res, ref, torch.float32, label="config1"))
+    _rerun_bitwise(res, q, k, v, dy)
 
 
 def test_config2_fp32_causal():
@@ -32,6 +46,7 @@ def test_config2_fp32_causal():
     res = gpu_run(q, k, v, dy, mask_kind="causal")
     ref = oracle_run(q, k, v, dy, mask_kind="causal")
     print("config2", assert_parity(res, ref, torch.float32, label="config2"))
+    _rerun_bitwise(res, q, k, v, dy, mask_kind="causal")
 
 
 @pytest.mark.parametrize("case", ["keypad", "keypad_causal", "bias", "bias_causal"])
@@ -47,36 +62,38 @@ def test_config4_fp32_padding_and_bias(case):
     res = gpu_run(q, k, v, dy, mask_kind=kind, causal=causal, mask=mask)
     ref = oracle_run(q, k, v, dy, mask_kind=kind, causal=causal, mask=mask)
     print("config4", case, assert_parity(res, ref, torch.float32, label=case))
+    _rerun_bitwise(res, q, k, v, dy, mask_kind=kind, causal=causal, mask=mask)
 
 
-def _full_size_sampled(mask_kind, window, pairs):
+def _full_size_all_heads(mask_kind, window):
+    """The full bf16 [4, 2048, 16, 128] workload: every element of dQ, dK, dV and
+    of the statistics against the oracle over all 64 (batch, head) heads, the
+    tolerance applied per head as well as over the whole tensor; then a rerun
+    that must give the same bits."""
     d, q, k, v, dy = _cfg_inputs(3)
     res = gpu_run(q, k, v, dy, mask_kind=mask_kind, window=window, prefill_nan=True)
-    for n in ("dq", "dk", "dv"):
-        assert not np.isnan(res[n]).any(), f"{n}: NaN left"
-    qs, ks, vs, gs = (sample_heads(x, pairs) for x in (q, k, v, dy))
-    ref = oracle_run(qs, ks, vs, gs, mask_kind=mask_kind, window=window)
-    out = {}
-    for n in ("dq", "dk", "dv"):
-        g = np.stack([res[n][b, :, h, :] for b, h in pairs], axis=1)[None]
-        out[n] = rel_err(g, ref[n])
-        assert out[n] <= TOL[torch.bfloat16], (n, out[n])
-    for n, t in (("m", 1e-5), ("l", 1e-4), ("delta", 2e-2)):
-        g = np.stack([res[n][b, h] for b, h in pairs])[None]
-        out[n] = rel_err(g, ref[n])
-        assert out[n] <= t, (n, out[n])
+    ref = oracle_run(q, k, v, dy, mask_kind=mask_kind, window=window, nthreads=ORACLE_THREADS)
+    out = assert_parity(res, ref, torch.bfloat16, label=f"config3 {mask_kind}")
+    B, _, H, _ = q.shape
+    worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            for n in ("dq", "dk", "dv"):
+                e = rel_err(res[n][b, :, h, :], ref[n][b, :, h, :])
+                worst = max(worst, e)
+                assert e <= TOL[torch.bfloat16], (n, b, h, e)
+    out["worst_head"] = worst
+    _rerun_bitwise(res, q, k, v, dy, mask_kind=mask_kind, window=window)
     return out
 
 
-def test_config3_bf16_window_full_size_sampled_heads():
-    pairs = [(0, 0), (1, 7), (2, 13), (3, 15)]
-    print("config3 window", _full_size_sampled("window", 256, pairs))
+def test_config3_bf16_window_full_size_all_heads():
+    print("config3 window", _full_size_all_heads("window", 256))
 
 
-def test_config3_bf16_causal_full_size_sampled_heads():
+def test_config3_bf16_causal_full_size_all_heads():
     """The benchmark's workload: same tensors, plain causal mask."""
-    pairs = [(0, 3), (3, 9)]
-    print("config3 causal", _full_size_sampled("causal", 0, pairs))
+    print("config3 causal", _full_size_all_heads("causal", 0))
 
 
 EDGE = [
@@ -194,3 +211,43 @@ def test_validation_errors_on_device_tensors():
     with pytest.raises(sdb.AttnError, match="ATTN_E_UNSUPPORTED"):
         x = torch.randn(1, 64, 2, 48, device=dev)
         sdb.attn_bwd(x, x, x, x)
+
+
+def test_side_stream_call_with_allocations_on_the_current_stream():
+    """A call on a side stream while the current stream allocates and overwrites
+    memory right after it returns.  The binding's own temporaries (the
+    statistics workspace, the outputs, the contiguous copy of a strided
+    log-sum-exp) are recorded on the side stream, so torch's allocator does not
+    hand them out again before the kernels are done, and the side stream waits
+    for what the current stream prepared.  Outputs must equal, bit for bit,
+    the same call on the current stream."""
+    import scaled_dot_product_bwd_amd as sdb
+    dev = torch.device("cuda:0")
+    B, S, H, D = 4, 1024, 8, 128
+    q, k, v, dy, _ = sdpa_inputs.dense_inputs(B, S, S, H, D, seed=21, dtype=torch.bfloat16)
+    qd, kd, vd, gd = (x.to(dev) for x in (q, k, v, dy))
+    (ref, ws) = sdb.attn_bwd(qd, kd, vd, gd, mask_kind="causal", return_workspace=True)
+    ref = [t.clone() for t in ref]
+    m, l, _ = sdb.row_stats_views(ws, B, H, S)
+    lse_t = (m + torch.log(l)).transpose(1, 2).contiguous().transpose(1, 2)  # strided [B, H, Sq]
+    o_stand = gd.clone()
+    ref_ff = [t.clone() for t in sdb.attn_bwd(qd, kd, vd, gd, mask_kind="causal", fwd_lse=lse_t,
+                                              fwd_out=o_stand)]
+    torch.cuda.synchronize()
+    nbytes = sdb.workspace_bytes(B, H, S)
+    side = torch.cuda.Stream()
+    for it in range(4):
+        ff = it % 2 == 1
+        kw = dict(fwd_lse=lse_t, fwd_out=o_stand) if ff else {}
+        got = sdb.attn_bwd(qd, kd, vd, gd, mask_kind="causal", stream=side, **kw)
+        # Same-size allocations on the current stream, written at once: they would
+        # take the freed workspace / lse copy / outputs if those were not recorded.
+        junk = [torch.full((nbytes // 4,), float("nan"), device=dev) for _ in range(4)]
+        junk += [torch.full((B, S, H, D), float("nan"), dtype=torch.bfloat16, device=dev)
+                 for _ in range(3)]
+        junk.append(torch.full((B, H, S), float("nan"), device=dev))
+        torch.cuda.synchronize()
+        want = ref_ff if ff else ref
+        for a_, b_ in zip(got, want):
+            assert torch.equal(a_, b_), ("from_forward" if ff else "attn_bwd", it)
+        del junk

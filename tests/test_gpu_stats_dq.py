@@ -21,29 +21,36 @@ pytestmark = pytest.mark.gpu
 BF = torch.bfloat16
 
 
+# (S, D): a short case over ragged chunks, and the benchmark's sequence length
+# and head width, where a row's statistics move over 32 chunks of 64 keys.
+SIZES = [(320, 64), (2048, 128)]
+
+
+@pytest.mark.parametrize("S,D", SIZES)
 @pytest.mark.parametrize("causal", [False, True])
-def test_reference_max_moves_every_chunk(causal):
+def test_reference_max_moves_every_chunk(causal, S, D):
     """A bias rising 0.4 per key lifts a row's max by ~18 log2 units per 32-key
     chunk, so the reference moves (and A, B, l are rescaled) at every chunk."""
-    B, H, S, D = 1, 2, 320, 64
+    B, H = 1, 2
     q, k, v, dy, _ = sdpa_inputs.dense_inputs(B, S, S, H, D, seed=11, dtype=BF)
     bias = (0.4 * torch.arange(S, dtype=torch.float32)).expand(B, H, S, S).contiguous()
     res = gpu_run(q, k, v, dy, mask_kind="bias", mask=bias, causal=causal)
-    ref = oracle_run(q, k, v, dy, mask_kind="bias", mask=bias, causal=causal)
-    print(causal, assert_parity(res, ref, BF, label=f"rising bias causal={causal}"))
+    ref = oracle_run(q, k, v, dy, mask_kind="bias", mask=bias, causal=causal, nthreads=2)
+    print(causal, S, assert_parity(res, ref, BF, label=f"rising bias causal={causal} S={S}"))
 
 
+@pytest.mark.parametrize("S,D", SIZES)
 @pytest.mark.parametrize("qscale", [4.0, 8.0])
-def test_peaked_rows(qscale):
+def test_peaked_rows(qscale, S, D):
     """Large |q|: most rows are dominated by one key (dP ~ delta there), where
     A - delta B cancels; dQ must stay as accurate as the three-pass path."""
-    B, H, S, D = 1, 2, 320, 64
+    B, H = 1, 2
     q, k, v, dy, _ = sdpa_inputs.dense_inputs(B, S, S, H, D, seed=5, dtype=torch.float64)
     q, k, v, dy = ((qscale * q).to(BF), k.to(BF), v.to(BF), dy.to(BF))
     for mask in ("none", "causal"):
         res = gpu_run(q, k, v, dy, mask_kind=mask)
-        ref = oracle_run(q, k, v, dy, mask_kind=mask)
-        print(qscale, mask, assert_parity(res, ref, BF, label=f"peaked x{qscale} {mask}"))
+        ref = oracle_run(q, k, v, dy, mask_kind=mask, nthreads=2)
+        print(qscale, S, mask, assert_parity(res, ref, BF, label=f"peaked x{qscale} {mask} S={S}"))
 
 
 @pytest.mark.parametrize("mask,window", [("window", 40), ("keypad", 0), ("bias", 0)])
