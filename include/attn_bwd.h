@@ -119,6 +119,19 @@ size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq);
  * requested outputs that have elements are then written with zeros. */
 int attn_bwd(const attn_bwd_args *a, void *stream);
 
+/* attn_bwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments and results, but `workspace` / `workspace_bytes` are ignored and
+ * the row statistics live in a static device array the library holds on each
+ * GPU (16 MiB, from the first use of the library's code on that GPU until the
+ * process ends).  B * H * Sq must be at most 2^20 rows, else ATTN_E_WORKSPACE
+ * (before any HIP call).  The array's device address is looked up once per
+ * device, on the device current on the calling thread, which must be the
+ * stream's device.  The call allocates and frees nothing.  All calls on one
+ * GPU share the array: calls that may overlap on one GPU (other streams, other
+ * threads) race and must be ordered by the caller. */
+int attn_bwd_noalloc(const attn_bwd_args *a, void *stream);
+
 /* The three stages of attn_bwd, for callers that time or schedule them one by
  * one.  They take the same arguments and validation.  Run them in this order
  * on one stream: row_stats fills the workspace statistics; kv writes dK / dV

@@ -32,7 +32,7 @@ from ._abi import (ATTN_BF16, ATTN_F32, ATTN_MASK_BIAS, ATTN_MASK_CAUSAL,
                    ATTN_WRT_ALL, ATTN_WRT_K, ATTN_WRT_Q, ATTN_WRT_V, AttnBwdArgs,
                    AttnBwdPagedArgs, AttnError, load_library, library_path)
 
-__all__ = ["attn_bwd", "attn_bwd_stage", "workspace_bytes", "make_args", "AttnError",
+__all__ = ["attn_bwd", "attn_bwd_noalloc", "attn_bwd_stage", "workspace_bytes", "make_args", "AttnError",
            "load_library", "library_path", "MASKS", "WRT", "PagedPlan", "paged_plan",
            "attn_bwd_paged", "attn_bwd_paged_mla", "make_paged_args", "paged_row_stats",
            "paged_q_workspace",
@@ -321,6 +321,21 @@ def attn_bwd(q, k, v, dy, *, wrt="all", mask_kind="none", causal=False, window=0
     _record(side, dq, dk, dv, workspace, lse)
     if return_workspace:
         return (dq, dk, dv), workspace
+    return dq, dk, dv
+
+
+def attn_bwd_noalloc(q, k, v, dy, *, out, wrt="all", mask_kind="none", causal=False, window=0,
+                     mask=None, threshold=0.5, scale=None, stream=None):
+    """attn_bwd without any device allocation (attn_bwd_noalloc): the caller
+    passes the outputs ``out = (dq, dk, dv)`` (None where ``wrt`` does not ask
+    for one) and the row statistics live in the library's static per-GPU
+    scratch (B * H * Sq at most 2^20 rows).  Calls that overlap on one GPU
+    race on that scratch.  Returns ``out``."""
+    dq, dk, dv = out
+    args = make_args(q, k, v, dy, dq, dk, dv, wrt=wrt, mask_kind=mask_kind, causal=causal,
+                     window=window, mask=mask, threshold=threshold, scale=scale)
+    handle, _ = _launch_stream(stream, q.device)
+    _check(load_library().attn_bwd_noalloc(ctypes.byref(args), handle))
     return dq, dk, dv
 
 

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 
 SOURCES = ["abi.cpp", "paged_plan.cpp", "dense_kernels.hip", "paged_kernels.hip",
-           "paged_q_kernels.hip"]
+           "paged_q_kernels.hip", "noalloc.hip"]
 
 
 def library_path() -> str:

@@ -592,9 +592,12 @@ size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq) {
   return 4 * plane_bytes(B, H, Sq);
 }
 
+}  // extern "C"
+
 // bf16: one query-major pass for the statistics and dQ, then dK / dV.
 // fp32: statistics, dK / dV, dQ (three passes; dQ from the exact delta).
-static int run_all(const attn_bwd_args *a, void *stream) {
+// Also the body of attn_bwd_noalloc (noalloc.hip), with its workspace filled in.
+int attn::run_dense_all(const attn_bwd_args *a, void *stream) {
   Checked c;
   const int rc = validate(a, c);
   if (rc != ATTN_OK) return rc;
@@ -609,7 +612,11 @@ static int run_all(const attn_bwd_args *a, void *stream) {
   return ATTN_OK;
 }
 
-int attn_bwd(const attn_bwd_args *a, void *stream) { return run_all(a, stream); }
+extern "C" {
+
+int attn_bwd(const attn_bwd_args *a, void *stream) { return attn::run_dense_all(a, stream); }
+
+
 
 int attn_bwd_stats_dq(const attn_bwd_args *a, void *stream) {
   Checked c;
