@@ -6,22 +6,41 @@
 
 Workload: bf16 Q, K, V, dY of shape [B=4, S=2048, H=16, D=128] (N(0,1), seeded,
 already resident in HBM), fp32 accumulation, bf16 dQ, dK, dV, causal mask.  One
-step is the whole backward: row statistics, the KV-block-major dK / dV kernel and
-the query-block-major dQ kernel, each launched through the C ABI on the current
-stream.  Throughput counts 10 * B * H * Sq * Sk * D flops (five contractions),
-halved for the causal mask; the window variant counts its visible pairs.
+step is one attn_bwd call through the C ABI on the current stream (for bf16:
+the fused statistics + dQ pass, then the KV-block-major dK / dV pass).  The K
+timed steps run back to back between two synchronisations; throughput counts
+10 * B * H * Sq * Sk * D flops (the method's five contractions, 2 D flops each
+per visible pair), halved for the causal mask; the window variant counts its
+visible pairs.
 
 Prints one JSON line.  Besides the contract fields it carries
-  roofline     for the dominant kernel: algorithmic flops per launch over its
-               average launch time (HIP events on the launch stream), against
-               the MI355X dense bf16 MFMA peak; `traffic` comes from a stored
-               rocprofv3 FETCH_SIZE / WRITE_SIZE measurement when it was taken
-               on the current kernel source, else null;
-  cpu_baseline the CPU oracle timed on a bounded sample of the same workload;
+  per_step     the same call timed one step at a time (HIP events around each
+               call) over max(100, K) steps: median, min, p90; and again with a
+               512 MiB device write between steps (no operand left in L2 or the
+               256 MB Infinity Cache), median and min;
+  kernels_ms   each kernel's average, from the stage entry points timed with
+               events between the launches (they give attn_bwd's bits);
+  roofline     the step against the bf16 MFMA peak: achieved = the method's
+               counted flops over the sum of the kernels' times, so `frac` is
+               the fraction of the peak the method's work reaches; `traffic` is
+               the step's HBM bytes from stored rocprofv3 FETCH_SIZE /
+               WRITE_SIZE measurements taken on the current kernel source, else
+               null;
+  issued_mfma  per kernel: the contractions it issues per visible pair (the
+               dK / dV pass and the fused pass both recompute S and dP), its
+               issued rate against the peak, and the SQ_VALU_MFMA_BUSY share
+               measured on the current source (stored counters), else null;
+  cpu_baseline the float64 CPU oracle on a bounded sample of the same workload:
+               one thread on one (b, h) head, and 16 threads (one GPU's share of
+               the host) on 16 heads; the host's core count and CPU model;
   from_forward the same step when a forward's log-sum-exp and output replace
-               the row statistics pass (attn_bwd_from_forward).
+               the statistics (attn_bwd_from_forward);
+  window256    the same tensors under the sliding window w = 256 (the parity
+               workload of this shape), counted over its visible pairs;
+  paged        the paged grouped-query history backward (below), its dK / dV
+               call against the HBM roofline and its query side.
 
---workload paged measures the paged grouped-query history backward instead
+--workload paged measures the paged grouped-query history backward alone
 (ruDNN `history_backward`): bf16, 32 query / 8 KV heads, D 128, page 16, 16
 sequences of UniformInt[256, 4096] tokens scattered through a pool with 25%
 unused pages, 64 queries per sequence at its last positions, causal, supplied
@@ -38,6 +57,9 @@ page tables (16 query heads on one latent KV head of width 128 plus a position
 key of width 64): TFLOP/s over the visible triples (4 (D + P) + 4 D flops each)
 against the MFMA peak, since at 16 query heads per latent row the kernel sits
 far above the HBM ridge.
+
+--no-extras keeps only the headline measurement (for profiler runs, whose
+per-kernel averages then cover the headline's launches alone).
 """
 from __future__ import annotations
 
@@ -114,21 +136,102 @@ def stored_traffic(kernel, tag="b4h16s2048d128_causal", sources=None):
         return None
 
 
-def cpu_baseline(q, k, v, dy, mask, window, nheads):
+HOST_SHARE = 16  # host threads one GPU's jobs may use on the test machines
+
+
+def cpu_model():
+    """The host CPU's model name (lscpu, else /proc/cpuinfo), or None."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(q, k, v, dy, mask, window):
+    """The float64 C oracle (untuned: the full S x S definition per head, plain
+    loops) on a bounded sample of the workload: 1 thread on 1 (b, h) head, then
+    min(16, nproc) threads on as many heads (one thread per head).  `value` is
+    the multi-thread rate in the metric's counted TFLOP/s."""
     import oracle
-    B, S, H, D = q.shape
-    pairs = [(b, h) for b in range(B) for h in range(H)][:nheads]
     import torch
-    sub = [torch.stack([x[b, :, h, :] for b, h in pairs], dim=1).unsqueeze(0) for x in (q, k, v, dy)]
-    threads = max(1, min(len(pairs), os.cpu_count() or 1, 16))
+    B, S, H, D = q.shape
+    nproc = os.cpu_count() or 1
+    threads = max(1, min(HOST_SHARE, nproc, B * H))
     code = 1 if mask == "causal" else 3
-    t0 = time.perf_counter()
-    oracle.attn_bwd(*sub, mask_kind=code, window=window, nthreads=threads)
-    dt = time.perf_counter() - t0
-    flops = counted_flops(1, len(pairs), S, S, D, mask, window)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(pairs)} of {B * H} (b,h) heads of the same workload, float64 C "
-                      f"oracle, {dt:.2f} s wall on {threads} threads"}
+    pairs = [(b, h) for b in range(B) for h in range(H)]
+
+    def run(nheads, nthreads):
+        sub = [torch.stack([x[b, :, h, :] for b, h in pairs[:nheads]], dim=1).unsqueeze(0)
+               for x in (q, k, v, dy)]
+        t0 = time.perf_counter()
+        oracle.attn_bwd(*sub, mask_kind=code, window=window, nthreads=nthreads)
+        dt = time.perf_counter() - t0
+        return counted_flops(1, nheads, S, S, D, mask, window) / dt / 1e12, dt
+
+    v1, dt1 = run(1, 1)
+    vn, dtn = run(threads, threads)
+    return {"value": vn, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{threads} of {B * H} (b,h) heads of the same workload on {threads} threads "
+                      f"(one head each), {dtn:.2f} s wall; untuned float64 C oracle (full S x S "
+                      f"definition per head)",
+            "single_thread": {"value": v1, "unit": "TFLOP/s", "cores": 1,
+                              "sample": f"1 (b,h) head, {dt1:.2f} s wall"},
+            "nproc": nproc, "host_share_threads": HOST_SHARE, "cpu_model": cpu_model()}
+
+
+def time_calls(fn, n, torch, between=None):
+    """n calls of fn, each bracketed by its own pair of HIP events on the current
+    stream; `between` (untimed) runs before each call.  Returns the times in ms."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        if between is not None:
+            between()
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def dist(ms):
+    xs = sorted(ms)
+    n = len(xs)
+    return {"n": n, "median_ms": round(xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2]), 5),
+            "min_ms": round(xs[0], 5), "p90_ms": round(xs[min(n - 1, int(0.9 * n))], 5)}
+
+
+def stored_mfma_busy(kernel, tag="b4h16s2048d128_causal"):
+    """SQ_VALU_MFMA_BUSY share of `kernel` from profiles/counters_dense_kernels_<tag>.txt
+    when measured on the current kernel source, else None."""
+    import re
+    path = os.path.join(ROOT, "profiles", f"counters_dense_kernels_{tag}.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel_source_sha: (\w+)", text)
+    if not m or m.group(1) != source_hash():
+        return None
+    m = re.search(rf"^{re.escape(KERNEL_NAMES[kernel])} \| MFMA busy per SIMD ([0-9.]+)%", text, re.M)
+    return float(m.group(1)) / 100.0 if m else None
+
+
+def dense_bytes(B, H, Sq, Sk, D, es):
+    """Algorithmic HBM bytes of one dense step: Q, dY read, K, V read, dQ, dK, dV
+    written once each, the four statistics planes written once and read once."""
+    return es * D * H * B * (3 * Sq + 4 * Sk) + 2 * 4 * 4 * B * H * Sq
 
 
 def preheat(step, torch, seconds):
@@ -236,7 +339,10 @@ def cpu_baseline_paged(w, nseq):
                       f"{threads} threads"}
 
 
-def main_paged(args, torch, sdb, dev):
+def paged_measure(args, torch, sdb, dev, cpu=True):
+    """The paged dK / dV call on the config-5 workload (and its query side),
+    timed with HIP events; returns the measurements as a dict."""
+    import ctypes
     import sdpa_inputs
     log("bench: generating the paged workload")
     w = sdpa_inputs.paged_workload(seed=1005)
@@ -250,15 +356,15 @@ def main_paged(args, torch, sdb, dev):
     dk, dv = torch.zeros_like(kp), torch.zeros_like(vp)
     a = sdb.make_paged_args(q, dy, kp, vp, stats, plan, dk, dv, causal=True, scale=scale)
     lib = sdb.load_library()
-    import ctypes
+    handle = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
     def step():
-        rc = lib.attn_bwd_paged(ctypes.byref(a), sdb._stream_handle(None))
+        rc = lib.attn_bwd_paged(ctypes.byref(a), handle)
         if rc != 0:
             raise RuntimeError(lib.attn_bwd_last_error().decode())
 
     ph_steps, ph_s = preheat(step, torch, args.preheat)
-    log(f"bench: preheat {ph_steps} steps ({ph_s:.3f} s), warmup {args.warmup}")
+    log(f"bench: paged preheat {ph_steps} steps ({ph_s:.3f} s), warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -269,6 +375,7 @@ def main_paged(args, torch, sdb, dev):
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
+    per = dist(time_calls(step, max(100, args.steps), torch))
     if not all(torch.isfinite(x[w["live_slots"].to(dev)]).all().item() for x in (dk, dv)):
         raise RuntimeError("non-finite gradients in the benchmark output")
     # The query side (statistics and dQ on the GPU, attn_bwd_paged_row_stats /
@@ -285,7 +392,7 @@ def main_paged(args, torch, sdb, dev):
         for name, fn, outp in (("row_stats", lib.attn_bwd_paged_row_stats, st_gpu),
                                ("dq", lib.attn_bwd_paged_dq, dq)):
             def qstep():
-                rc = fn(ctypes.byref(a), ctypes.c_void_p(outp.data_ptr()), sdb._stream_handle(None))
+                rc = fn(ctypes.byref(a), ctypes.c_void_p(outp.data_ptr()), handle)
                 if rc != 0:
                     raise RuntimeError(lib.attn_bwd_last_error().decode())
             for _ in range(args.warmup):
@@ -301,17 +408,17 @@ def main_paged(args, torch, sdb, dev):
     flops = paged_flops(w)
     gbs = nbytes / (ms / 1e3) / 1e9
     tflops = flops / (ms / 1e3) / 1e12
-    cpu = None
-    if not args.no_cpu_baseline:
+    cpu_line = None
+    if cpu and not args.no_cpu_baseline:
         log("bench: CPU oracle baseline on 2 sequences")
-        cpu = cpu_baseline_paged(w, 2)
+        cpu_line = cpu_baseline_paged(w, 2)
     wl = (f"paged_gqa_bwd nseq16 len[256,4096] heads32/8 D128 page16 q64/seq bf16 causal "
           f"(tokens {int(w['seq_lens'].sum())}, pool pages {w['pool_pages']})")
-    line = {
+    return {
         "metric": "paged GQA history bwd (dK+dV) TFLOP/s & HBM GB/s",
-        "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "preheat": {"steps": ph_steps, "s": round(ph_s, 3)}, "ms_per_step": round(ms, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "value": round(tflops, 3), "unit": "TFLOP/s", "steps": args.steps,
+        "warmup": args.warmup, "preheat": {"steps": ph_steps, "s": round(ph_s, 3)},
+        "ms_per_step": round(ms, 5), "per_step": per,
         "config": {"workload": wl, "counted_flops": flops, "algorithmic_bytes": nbytes,
                    "items": plan.items},
         "pct_mfma_peak": round(100.0 * tflops / PEAK_TFLOPS["bf16"], 3),
@@ -322,9 +429,19 @@ def main_paged(args, torch, sdb, dev):
                      "bytes_per_launch": nbytes},
         "query_side_ms": q_ms,
         "query_side_direct_ms": q_direct_ms,
+        "full_chain_ms": round(ms + sum(q_ms.values()), 4),
         "full_chain_tflops": round(flops * 10.0 / 8.0 / ((ms + sum(q_ms.values())) / 1e3) / 1e12, 3),
-        "cpu_baseline": cpu,
+        "cpu_baseline": cpu_line,
     }
+
+
+def main_paged(args, torch, sdb, dev):
+    m = paged_measure(args, torch, sdb, dev)
+    line = {"metric": m.pop("metric"), "value": m.pop("value"), "unit": m.pop("unit"),
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": m.pop("ms_per_step"), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+    line.update(m)
     print(json.dumps(line), flush=True)
 
 
@@ -474,8 +591,9 @@ def main():
     ap.add_argument("--workload", default="dense", choices=["dense", "paged", "paged_mla"])
     ap.add_argument("--mask", default="causal", choices=["causal", "window"])
     ap.add_argument("--window", type=int, default=256)
-    ap.add_argument("--cpu-heads", type=int, default=16,
-                    help="(b,h) heads the CPU oracle baseline processes")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the headline measurement (no scrubbed, from_forward, window or "
+                         "paged parts): for profiler runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--preheat", type=float, default=0.1,
                     help="seconds of untimed steps before the warmup steps (clock ramp)")
@@ -484,8 +602,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the (b, h) heads are independent; see the design notes on sharding). "
+        print("bench.py measures one GPU only: this build has no multi-GPU path (the (b, h) "
+              "heads are independent and would split across GPUs with no exchange). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
@@ -515,107 +633,184 @@ def main():
     B, S, H, D = qc.shape
     window = args.window if args.mask == "window" else 0
     q, k, v, dy = (x.to(dev) for x in (qc, kc, vc, gc))
-    dq, dk, dv = (torch.empty_like(x) for x in (q, k, v))
-    ws = torch.empty(sdb.workspace_bytes(B, H, S), dtype=torch.uint8, device=dev)
-    a = sdb.make_args(q, k, v, dy, dq, dk, dv, mask_kind=args.mask, window=window, workspace=ws)
-    # attn_bwd's bf16 sequence: statistics and dQ in one pass, then dK / dV.
-    stages = ["stats_dq", "kv"]
-
-    def step(ev=None):
-        for i, st in enumerate(stages):
-            if ev is not None:
-                ev[i].record()
-            sdb.attn_bwd_stage(st, a)
-        if ev is not None:
-            ev[len(stages)].record()
-
-    ph_steps, ph_s = preheat(step, torch, args.preheat)
-    log(f"bench: preheat {ph_steps} steps ({ph_s:.3f} s), warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
-           for _ in range(args.steps)]
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
-    for s in range(args.steps):
-        step(evs[s])
-    t_end.record()
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_step = total_ms / args.steps
-    per_kernel = {st: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
-                  for i, st in enumerate(stages)}
-    if not all(torch.isfinite(t).all().item() for t in (dq, dk, dv)):
-        raise RuntimeError("non-finite gradients in the benchmark output")
-
-    # The same backward from a forward's saved statistics (attn_bwd_from_forward:
-    # log-sum-exp and O replace the row statistics pass).  Timing only: lse comes
-    # from this run's statistics and O is a stand-in tensor of the right shape
-    # (the kernels' cost does not depend on the values).
-    import ctypes
-    m_ws, l_ws, _ = sdb.row_stats_views(ws, B, H, S)
-    lse = (m_ws + torch.log(l_ws)).contiguous()
-    o_stand = dy.clone()
-    ost = (ctypes.c_int64 * 3)(*o_stand.stride()[:3])
-    lib = sdb.load_library()
-    dq2, dk2, dv2 = (torch.empty_like(x) for x in (q, k, v))
-    a2 = sdb.make_args(q, k, v, dy, dq2, dk2, dv2, mask_kind=args.mask, window=window, workspace=ws)
-
-    def fstep():
-        rc = lib.attn_bwd_from_forward(ctypes.byref(a2), ctypes.c_void_p(lse.data_ptr()),
-                                       ctypes.c_void_p(o_stand.data_ptr()), ost,
-                                       sdb._stream_handle(None))
-        if rc != 0:
-            raise RuntimeError(lib.attn_bwd_last_error().decode())
-    preheat(fstep, torch, args.preheat)  # the clocks drop while the host prepares this segment
-    for _ in range(args.warmup):
-        fstep()
-    torch.cuda.synchronize()
-    t_start.record()
-    for _ in range(args.steps):
-        fstep()
-    t_end.record()
-    torch.cuda.synchronize()
-    ff_ms = t_start.elapsed_time(t_end) / args.steps
-
-    flops = counted_flops(B, H, S, S, D, args.mask, window)
-    value = flops / (ms_step / 1e3) / 1e12
-    pairs_step = flops / (10.0 * D)  # visible pairs as counted
-    dom = max(per_kernel, key=per_kernel.get)
-    dom_flops = 2.0 * D * CONTRACTIONS[dom] * pairs_step
-    achieved = dom_flops / (per_kernel[dom] / 1e3) / 1e12
-    traffic = stored_traffic(dom) if args.mask == "causal" else None
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"],
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
-                "traffic": traffic, "kernel": KERNEL_NAMES[dom],
-                "kernel_ms": round(per_kernel[dom], 4),
-                "flops_per_launch": dom_flops}
+    head = dense_measure(args, torch, sdb, dev, (q, k, v, dy), args.mask, window, full=True)
 
     cpu = None
     if not args.no_cpu_baseline:
-        log(f"bench: CPU oracle baseline on {args.cpu_heads} heads")
-        cpu = cpu_baseline(qc, kc, vc, gc, args.mask, window, args.cpu_heads)
+        log("bench: CPU oracle baseline (1 thread on 1 head, then the host share)")
+        cpu = cpu_baseline(qc, kc, vc, gc, args.mask, window)
 
     wl = f"sdpa_bwd B{B} H{H} S{S} D{D} bf16 " + (args.mask if args.mask == "causal"
                                                    else f"window{window}")
     line = {
         "metric": "attn-bwd TFLOP/s (dQ+dK+dV) & % MFMA peak, B4 H16 S2048 D128 bf16 causal",
-        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "preheat": {"steps": ph_steps, "s": round(ph_s, 3)}, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "value": head["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "preheat": head["preheat"], "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
         "config": {"workload": wl, "B": B, "H": H, "Sq": S, "Sk": S, "D": D, "mask": args.mask,
                    "window": window if args.mask == "window" else None, "layout": "BSHD",
-                   "counted_flops": flops},
-        "pct_mfma_peak": round(100.0 * value / PEAK_TFLOPS["bf16"], 3),
-        "kernels_ms": {k_: round(v_, 4) for k_, v_ in per_kernel.items()},
-        "from_forward": {"ms_per_step": round(ff_ms, 5),
-                         "tflops": round(flops / (ff_ms / 1e3) / 1e12, 3)},
-        "roofline": roofline,
+                   "entry": "attn_bwd", "counted_flops": head["counted_flops"]},
+        "pct_mfma_peak": round(100.0 * head["tflops"] / PEAK_TFLOPS["bf16"], 3),
+        "per_step": head["per_step"],
+        "per_step_scrubbed": head["per_step_scrubbed"],
+        "kernels_ms": head["kernels_ms"],
+        "roofline": head["roofline"],
+        "issued_mfma": head["issued_mfma"],
+        "from_forward": head["from_forward"],
         "cpu_baseline": cpu,
     }
+    if not args.no_extras and args.mask == "causal":
+        log("bench: window-256 variant of the same tensors")
+        wv = dense_measure(args, torch, sdb, dev, (q, k, v, dy), "window", args.window, full=False)
+        line["window256"] = {k_: wv[k_] for k_ in ("ms_per_step", "tflops", "counted_flops",
+                                                   "per_step", "kernels_ms", "roofline")}
+        line["window256"]["pct_mfma_peak"] = round(100.0 * wv["tflops"] / PEAK_TFLOPS["bf16"], 3)
+        del q, k, v, dy
+        torch.cuda.empty_cache()
+        pm = paged_measure(args, torch, sdb, dev, cpu=False)
+        line["paged"] = {k_: pm[k_] for k_ in ("ms_per_step", "value", "unit", "per_step",
+                                               "pct_mfma_peak", "roofline", "query_side_ms",
+                                               "full_chain_ms", "full_chain_tflops", "config")}
     print(json.dumps(line), flush=True)
+
+
+def dense_measure(args, torch, sdb, dev, tensors, mask, window, full):
+    """One dense workload: the K-step timed region through attn_bwd, per-step
+    times, per-kernel times from the stage entry points, the roofline and the
+    issued-MFMA figures; with `full`, also the cache-scrubbed per-step times and
+    the supplied-statistics (from_forward) step."""
+    import ctypes
+    q, k, v, dy = tensors
+    B, S, H, D = q.shape
+    dq, dk, dv = (torch.empty_like(x) for x in (q, k, v))
+    ws = torch.empty(sdb.workspace_bytes(B, H, S), dtype=torch.uint8, device=dev)
+    a = sdb.make_args(q, k, v, dy, dq, dk, dv, mask_kind=mask, window=window, workspace=ws)
+    lib = sdb.load_library()
+    handle = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def step():
+        rc = lib.attn_bwd(ctypes.byref(a), handle)
+        if rc != 0:
+            raise RuntimeError(lib.attn_bwd_last_error().decode())
+
+    ph_steps, ph_s = preheat(step, torch, args.preheat)
+    log(f"bench: {mask} preheat {ph_steps} steps ({ph_s:.3f} s), warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    # The timed region: K back-to-back attn_bwd calls between two synchronisations.
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    if not all(torch.isfinite(t).all().item() for t in (dq, dk, dv)):
+        raise RuntimeError("non-finite gradients in the benchmark output")
+    out = {"preheat": {"steps": ph_steps, "s": round(ph_s, 3)}, "ms_per_step": round(ms_step, 5)}
+    out["per_step"] = dist(time_calls(step, max(100, args.steps), torch))
+    if full and not args.no_extras:
+        scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        fill = [0]
+
+        def between():  # a 512 MiB write: no operand stays in L2 or the Infinity Cache
+            fill[0] ^= 1
+            scrub.fill_(fill[0])
+        out["per_step_scrubbed"] = dist(time_calls(step, max(100, args.steps), torch, between))
+        out["per_step_scrubbed"]["scrub_bytes"] = 512 << 20
+        del scrub
+    else:
+        out["per_step_scrubbed"] = None
+
+    # Per-kernel times: the bf16 sequence of attn_bwd through the stage entry
+    # points (same kernels, same bits), events between the launches.
+    stages = ["stats_dq", "kv"]
+    n_k = max(30, args.steps)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(n_k)]
+    torch.cuda.synchronize()
+    for e in evs:
+        for i, st in enumerate(stages):
+            e[i].record()
+            sdb.attn_bwd_stage(st, a)
+        e[len(stages)].record()
+    torch.cuda.synchronize()
+    per_kernel = {st: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / n_k
+                  for i, st in enumerate(stages)}
+    out["kernels_ms"] = {k_: round(v_, 4) for k_, v_ in per_kernel.items()}
+
+    flops = counted_flops(B, H, S, S, D, mask, window)
+    out["counted_flops"] = flops
+    out["tflops"] = round(flops / (ms_step / 1e3) / 1e12, 3)
+    kern_ms = sum(per_kernel.values())
+    achieved = flops / (kern_ms / 1e3) / 1e12
+    nbytes = dense_bytes(B, H, S, S, D, 2)
+    ridge = PEAK_TFLOPS["bf16"] * 1e12 / (HBM_PEAK_GBS * 1e9)
+    tag = "b4h16s2048d128_causal"
+    traffic = None
+    if mask == "causal":
+        tr = [stored_traffic(st, tag) for st in stages]
+        traffic = sum(tr) if all(t is not None for t in tr) else None
+    # The bound follows the work's intensity against the ridge: MFMA-bound
+    # workloads are measured in TFLOP/s, HBM-bound ones (the window band) in GB/s.
+    if flops / nbytes > ridge:
+        bound, ach, peak, unit = "mfma", achieved, PEAK_TFLOPS["bf16"], "TFLOP/s"
+    else:
+        bound, ach, peak, unit = "hbm", nbytes / (kern_ms / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s"
+    out["roofline"] = {
+        "bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
+        "frac": round(ach / peak, 4), "traffic": traffic,
+        "mfma_frac": round(achieved / PEAK_TFLOPS["bf16"], 4),
+        "kernel": "attn_bwd step: " + " + ".join(KERNEL_NAMES[st] for st in stages),
+        "kernel_ms": round(kern_ms, 4), "flops_per_launch": flops,
+        "work": "10 D flops per visible (query, key) pair: the method's five contractions, "
+                "each counted once per step",
+        "algorithmic_bytes": nbytes, "intensity_flop_per_byte": round(flops / nbytes, 1),
+        "ridge_flop_per_byte": round(ridge, 1)}
+    pairs = flops / (10.0 * D)
+    issued = {}
+    for st in stages:
+        f_ = 2.0 * D * CONTRACTIONS[st] * pairs
+        t_ = f_ / (per_kernel[st] / 1e3) / 1e12
+        issued[KERNEL_NAMES[st]] = {
+            "ms": round(per_kernel[st], 4), "contractions_per_pair": CONTRACTIONS[st],
+            "issued_tflops": round(t_, 2), "frac_of_peak": round(t_ / PEAK_TFLOPS["bf16"], 4),
+            "counter_mfma_busy": stored_mfma_busy(st, tag) if mask == "causal" else None}
+    out["issued_mfma"] = issued
+
+    out["from_forward"] = None
+    if full and not args.no_extras:
+        # The same backward from a forward's saved statistics (attn_bwd_from_forward:
+        # log-sum-exp and O replace the statistics pass).  Timing only: lse comes
+        # from this run's statistics and O is a stand-in tensor of the right shape
+        # (the kernels' cost does not depend on the values).
+        m_ws, l_ws, _ = sdb.row_stats_views(ws, B, H, S)
+        lse = (m_ws + torch.log(l_ws)).contiguous()
+        o_stand = dy.clone()
+        ost = (ctypes.c_int64 * 3)(*o_stand.stride()[:3])
+        dq2, dk2, dv2 = (torch.empty_like(x) for x in (q, k, v))
+        ws2 = torch.empty_like(ws)
+        a2 = sdb.make_args(q, k, v, dy, dq2, dk2, dv2, mask_kind=mask, window=window, workspace=ws2)
+
+        def fstep():
+            rc = lib.attn_bwd_from_forward(ctypes.byref(a2), ctypes.c_void_p(lse.data_ptr()),
+                                           ctypes.c_void_p(o_stand.data_ptr()), ost, handle)
+            if rc != 0:
+                raise RuntimeError(lib.attn_bwd_last_error().decode())
+        preheat(fstep, torch, args.preheat)  # the clocks drop while the host prepares this segment
+        for _ in range(args.warmup):
+            fstep()
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(args.steps):
+            fstep()
+        t1.record()
+        torch.cuda.synchronize()
+        ff_ms = t0.elapsed_time(t1) / args.steps
+        out["from_forward"] = {"ms_per_step": round(ff_ms, 5),
+                               "tflops": round(flops / (ff_ms / 1e3) / 1e12, 3)}
+    return out
 
 
 if __name__ == "__main__":
