@@ -236,6 +236,14 @@ typedef struct attn_bwd_paged_args {
    * up to rounding order; both are bit-identical from run to run. */
   void *q_workspace;
   size_t q_workspace_bytes;
+  /* Form of the dK / dV pass of attn_bwd_paged (bf16, not latent; ignored
+   * otherwise).  0: chosen by the library, the persistent form (one workgroup
+   * per compute unit, each walking a fixed list of (item, KV head) units)
+   * when the units outnumber the compute units, else one workgroup per unit;
+   * n > 0: the persistent form with n workgroups (rounded down to a multiple
+   * of 8, at least 8, at most the units rounded up to 8); -1: one workgroup
+   * per unit.  Every form gives identical bits.  Below -1: ATTN_E_INVALID. */
+  int32_t kv_workgroups;
 } attn_bwd_paged_args;
 
 /* Enqueues the paged backward.  Every device pointer must be 16-byte aligned;

@@ -426,9 +426,12 @@ def paged_plan(seq_lens, block_table, query_seq, query_pos, *, heads, kv_heads, 
 
 
 def make_paged_args(q, dy, k_pool, v_pool, stats, plan, dk_pool=None, dv_pool=None, *,
-                    causal=True, scale=None, need=3, outs=()):
+                    causal=True, scale=None, need=3, outs=(), kv_workgroups=0):
     """Builds the attn_bwd_paged_args struct; the tensors are checked first
-    (check_paged_tensors), the plan must already be on q's device."""
+    (check_paged_tensors), the plan must already be on q's device.
+    kv_workgroups: 0 lets the library pick the dK / dV kernel form; n > 0
+    forces the persistent form with n workgroups, -1 one workgroup per
+    (item, KV head) unit (bf16, not latent; every form gives identical bits)."""
     torch = _torch()
     if plan.device_words is None:
         raise ValueError("the plan has no device copy: call plan.to(device) first")
@@ -451,17 +454,19 @@ def make_paged_args(q, dy, k_pool, v_pool, stats, plan, dk_pool=None, dv_pool=No
         a.dk_pool = dk_pool.data_ptr()
     if dv_pool is not None:
         a.dv_pool = dv_pool.data_ptr()
+    a.kv_workgroups = int(kv_workgroups)
     return a
 
 
 def attn_bwd_paged(q, dy, k_pool, v_pool, stats, plan, *, dk_pool=None, dv_pool=None,
-                   need="dkdv", causal=True, scale=None, stream=None):
+                   need="dkdv", causal=True, scale=None, stream=None, kv_workgroups=0):
     """dK / dV of the paged grouped-query history backward, written into the
     given gradient pools at the slots of listed pages (other slots untouched);
     pools that are not given are allocated zero-filled.  q, dy: [nq, heads, D];
     pools: [pool_pages * page_size, kv_heads, D] (contiguous, fp32 or bf16, on
     the GPU); stats: float32 [nq, heads, 3] = (max, denominator, delta); plan:
-    a PagedPlan uploaded to the same device.  Returns (dk_pool, dv_pool)."""
+    a PagedPlan uploaded to the same device.  kv_workgroups: see
+    make_paged_args.  Returns (dk_pool, dv_pool)."""
     torch = _torch()
     n = {"dk": 1, "dv": 2, "dkdv": 3}[need] if isinstance(need, str) else int(need)
     check_paged_tensors(q, dy, k_pool, v_pool, stats, plan, dk_pool, dv_pool)
@@ -472,7 +477,7 @@ def attn_bwd_paged(q, dy, k_pool, v_pool, stats, plan, *, dk_pool=None, dv_pool=
     if dv_pool is None and n & 2:
         dv_pool = torch.zeros_like(v_pool)
     args = make_paged_args(q, dy, k_pool, v_pool, stats, plan, dk_pool, dv_pool,
-                           causal=causal, scale=scale, need=n)
+                           causal=causal, scale=scale, need=n, kv_workgroups=kv_workgroups)
     handle, side = _launch_stream(stream, q.device)
     _check(load_library().attn_bwd_paged(ctypes.byref(args), handle))
     _record(side, dk_pool, dv_pool, plan.device_words)

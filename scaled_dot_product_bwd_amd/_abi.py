@@ -28,8 +28,11 @@ EXPORTED = ["attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_row_stats", "attn_
             "attn_bwd_last_error", "attn_bwd_noalloc"]
 
 # Plan header words (scaled_dot_product_bwd_amd/csrc/paged.hpp).
-PLAN_MAGIC = 0x31504241
+PLAN_MAGIC = 0x32504241
 PLAN_ITEM_SLOTS = 128
+# Link record words (LI_* in paged.hpp).
+(LI_MIN_TOK, LI_MAX_TOK, LI_ALL_VALID, LI_QH0, LI_NQH, LI_MINPOS, LI_MAXPOS, LI_SEQ) = range(8)
+LINK_INFO_WORDS = 8
 (W_MAGIC, W_WORDS, W_NSEQ, W_NQ, W_HEADS, W_KV_HEADS, W_PAGE_SIZE, W_POOL_PAGES, W_ITEMS,
  W_LINKS, W_QH, W_LISTED, W_OFF_ITEM_LINKS, W_OFF_ITEM_SLOTS, W_OFF_LINK_SEQ, W_OFF_LINK_INFO,
  W_OFF_LINK_TOK, W_OFF_SEQ_QH, W_OFF_QH_RH, W_OFF_QH_POS, W_OFF_SEQ_MAXPOS,
@@ -83,6 +86,7 @@ class AttnBwdPagedArgs(ctypes.Structure):
         ("qp", ctypes.c_void_p), ("kp_pool", ctypes.c_void_p),
         ("dkp_pool", ctypes.c_void_p),
         ("q_workspace", ctypes.c_void_p), ("q_workspace_bytes", ctypes.c_size_t),
+        ("kv_workgroups", ctypes.c_int32),
     ]
 
 

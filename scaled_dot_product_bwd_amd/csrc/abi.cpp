@@ -400,6 +400,7 @@ int validate_paged(const attn_bwd_paged_args *a, int mode, void *out, attn::Page
   if (std::fabs(a->scale) < kMinScale || std::fabs(a->scale) > kMaxScale)
     return fail(ATTN_E_UNSUPPORTED, "|scale| outside [2^-64, 2^64] (including 0) is not supported");
   if (a->causal != 0 && a->causal != 1) return fail(ATTN_E_INVALID, "causal must be 0 or 1");
+  if (a->kv_workgroups < -1) return fail(ATTN_E_INVALID, "kv_workgroups is below -1");
   const int32_t *w = a->plan_host;
   if (!w || !a->plan) return fail(ATTN_E_INVALID, "plan_host / plan is NULL");
   if (w[W_MAGIC] != kMagic) return fail(ATTN_E_INVALID, "plan_host is not a plan (bad magic)");
@@ -539,7 +540,8 @@ namespace attn {
 void set_last_error(const char *msg) {
   snprintf(g_err, sizeof g_err, "%s", msg);
 }
-hipError_t launch_paged(bool bf16_in, int D, const PagedParams &p, int nblocks, hipStream_t stream);
+hipError_t launch_paged(bool bf16_in, int D, const PagedParams &p, int nblocks, int workgroups,
+                        hipStream_t stream);
 hipError_t launch_paged_q(int stage, bool bf16_in, int D, const PagedParams &p, int nblocks,
                           hipStream_t stream);
 }  // namespace attn
@@ -553,7 +555,8 @@ int run_paged(const attn_bwd_paged_args *a, int mode, void *out, void *stream) {
   if (rc != ATTN_OK) return rc;
   if (nblocks == 0) return ATTN_OK;
   const hipError_t e =
-      mode == PM_KV ? attn::launch_paged(bf16, a->head_dim, p, nblocks, (hipStream_t)stream)
+      mode == PM_KV ? attn::launch_paged(bf16, a->head_dim, p, nblocks, a->kv_workgroups,
+                                         (hipStream_t)stream)
                     : attn::launch_paged_q(mode == PM_STATS ? 0 : 1, bf16, a->head_dim, p, nblocks,
                                            (hipStream_t)stream);
   if (e != hipSuccess) return fail(ATTN_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));

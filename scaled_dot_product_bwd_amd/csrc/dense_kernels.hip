@@ -389,7 +389,7 @@ __device__ __forceinline__ void kv_step(const DenseParams &p, KvState<T, D> &S, 
     }
   };
   const float *stc = st[bc];
-  kv_chunk<T, D, D, MASKED, false, true, SPREAD ? 2 * LQ + 1 : 0>(
+  kv_chunk<T, D, D, MASKED, false, SPREAD ? 2 * LQ + 1 : 0>(
       S.kf, S.vf, S.dk, S.dv, &Qs[bc], &Gs[bc], stc, stc + ROWS, p.scale_log2, S.lane, adj, 1.f,
       dma);
   if (issued) {
@@ -504,7 +504,7 @@ __global__ __launch_bounds__(256) void k_kv_bwd(const DenseParams p) {
 #pragma unroll
   for (int s = 0; s < NSD; ++s) {
     S.kf[s] = load_frag<T>(krow, s * KS + half * KL, kvalid);
-    S.vf[s] = neg_frag<T>(load_frag<T>(vrow, s * KS + half * KL, kvalid));  // -V
+    S.vf[s] = load_frag<T>(vrow, s * KS + half * KL, kvalid);
   }
 
   S.qbase = (const T *)p.q + b * p.qs[0] + S.h0 * p.qs[2];

@@ -119,15 +119,6 @@ template <> __device__ __forceinline__ float frag_dot<bf16>(bf16x8 a, bf16x8 b) 
 }
 template <> __device__ __forceinline__ float frag_dot<float>(float a, float b) { return a * b; }
 
-// -f (a sign flip per element).
-template <typename T> __device__ __forceinline__ typename MT<T>::frag neg_frag(typename MT<T>::frag f);
-template <> __device__ __forceinline__ bf16x8 neg_frag<bf16>(bf16x8 f) {
-  // both sign bits of each packed pair in one 32-bit xor
-  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-  return __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, f) ^ 0x80008000u);
-}
-template <> __device__ __forceinline__ float neg_frag<float>(float f) { return -f; }
-
 // Pack C-tile values as a C-reuse B operand for step `st` (see header).
 template <typename T>
 __device__ __forceinline__ typename MT<T>::frag creuse(const float *v, int st);
@@ -411,6 +402,15 @@ __device__ __forceinline__ bool idx_visible(const DenseParams &p, int i, int j) 
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// x, made opaque to the optimiser: what is derived from it is computed where it
+// is used instead of being hoisted out of a loop and kept live across it (in a
+// register the loop body needs, or in scratch memory).
+__device__ __forceinline__ int fresh(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 
 // Workgroup id -> logical tile id.  The hardware hands workgroup i to XCD i % 8;
 // this gives every XCD a contiguous range of logical ids, so the tiles of one

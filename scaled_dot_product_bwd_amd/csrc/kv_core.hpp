@@ -12,6 +12,9 @@
 //      dS' = P (dP - delta)                 (the factor `scale` of dS is applied
 //                                            to dK once, by the caller; -lse2 and
 //                                            -delta are the accumulators' start)
+// K and V sit in registers as loaded: nothing is computed from them before
+// their first MFMA, so their loads go straight into the operand registers and
+// all of a tile's loads are in flight at once.
 //   C  dV^T += dY^T P,  dK^T += Q^T dS'     A read transposed from LDS, B = C reuse
 //
 // Schedule.  With one wave per SIMD nothing hides latency but the wave's own
@@ -46,8 +49,7 @@ __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0
 // adj(u, r): log2-domain term added to the score of element r of sub-tile u
 // (query row 32 u + kr(r, half) of the chunk, key = this lane's column); only
 // called when MASKED.  nls / dst: the chunk's per-row statistics in LDS (row i
-// at [i]): nls = -lse2 / scale_log2, and dst = delta when the caller's V
-// fragments are negated (NEGV), else -delta.
+// at [i]): nls = -lse2 / scale_log2 and dst = delta.
 //
 // DK is the width of the score's contraction (Q and K rows, dK), DV that of the
 // value side (dY and V rows, dV); DV <= DK.  They differ for a latent key: the
@@ -69,7 +71,7 @@ struct NoDma {
   __device__ __forceinline__ void operator()(int) const {}
 };
 
-template <typename T, int DK, int DV, bool MASKED, bool MERGE, bool NEGV, int NDMA = 0,
+template <typename T, int DK, int DV, bool MASKED, bool MERGE, int NDMA = 0,
           typename Adj, typename Dma = NoDma>
 __device__ __forceinline__ void kv_chunk(const typename MT<T>::frag *kf,
                                          const typename MT<T>::frag *vf, f32x16 *dk, f32x16 *dv,
@@ -92,9 +94,8 @@ __device__ __forceinline__ void kv_chunk(const typename MT<T>::frag *kf,
   float pv[NSUB][16], dsv[NSUB][16];
 
   // The row statistics enter through the accumulators' initial values: S
-  // starts at -lse2 / scale_log2 and dP at -delta (or, with negated V
-  // fragments, the accumulator runs delta - dP), so after phase A
-  // sacc * scale_log2 is the log2-domain exponent and pacc is +-(dP - delta).
+  // starts at -lse2 / scale_log2 and dP at -delta, so after phase A
+  // sacc * scale_log2 is the log2-domain exponent and pacc is dP - delta.
   // Elements 4g .. 4g + 3 of a lane are rows 8g + 4 half + 0..3: plain vector
   // loads into the accumulators, once per sub-tile and a few steps before its
   // first MFMA (no LDS read, hence no wait on the operand prefetch, inside
@@ -108,7 +109,7 @@ __device__ __forceinline__ void kv_chunk(const typename MT<T>::frag *kf,
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         sacc[u][4 * g + i] = nl4[i];
-        pacc[u][4 * g + i] = dl4[i];
+        pacc[u][4 * g + i] = -dl4[i];
       }
     }
   };
@@ -124,7 +125,7 @@ __device__ __forceinline__ void kv_chunk(const typename MT<T>::frag *kf,
         t = sacc[u][r] * scale_log2;
       const float pr = fast_exp2(t);
       pv[u][r] = pr;
-      const float pd = NEGV ? -pacc[u][r] : pacc[u][r];  // dP - delta
+      const float pd = pacc[u][r];  // dP - delta
       if constexpr (MERGE)
         dsv[u][r] = (pr * ds_scale) * pd;
       else

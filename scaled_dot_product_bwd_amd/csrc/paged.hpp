@@ -20,8 +20,11 @@
 //            they store zero and their K / V rows are never read).
 //   link     one sequence linked to every page of an item: per lane the
 //            token position of the slot in that sequence (-1: past its
-//            length, or no slot), plus min / max token and whether all 128
-//            lanes hold a token.
+//            length, or no slot), plus an 8-word record: min / max token,
+//            whether all 128 lanes hold a token, and the linked sequence's
+//            own facts (its qh rows, smallest and largest row position, the
+//            sequence), so that a workgroup learns everything about a link
+//            from one record.
 //   qh row   the query rows of each sequence in their original packed order,
 //            each expanded to its group of query heads (head index minor):
 //            rh = row * heads + head-in-group, and the row's position.
@@ -40,7 +43,7 @@
 namespace attn {
 namespace plan {
 
-constexpr int32_t kMagic = 0x31504241;  // "ABP1"
+constexpr int32_t kMagic = 0x32504241;  // "ABP2"
 constexpr int kItemSlots = 128;
 
 enum Word {
@@ -59,7 +62,7 @@ enum Word {
   W_OFF_ITEM_LINKS,  // [items + 1] CSR into links
   W_OFF_ITEM_SLOTS,  // [items * 128] slot entries
   W_OFF_LINK_SEQ,    // [links] sequence
-  W_OFF_LINK_INFO,   // [links * 4] (min token, max token, all lanes valid, 0)
+  W_OFF_LINK_INFO,   // [links * LINK_INFO_WORDS] link records (LI_* below)
   W_OFF_LINK_TOK,    // [links * 128] token per lane, -1 = none
   W_OFF_SEQ_QH,      // [nseq + 1] CSR into qh rows
   W_OFF_QH_RH,       // [qh] row * heads + head-in-group
@@ -81,7 +84,21 @@ enum Word {
   HEADER_WORDS = 32
 };
 
-enum { LI_MIN_TOK = 0, LI_MAX_TOK = 1, LI_ALL_VALID = 2, LINK_INFO_WORDS = 4 };
+// Link record: the item's smallest / largest token in the sequence, 1 if all
+// 128 lanes hold a token; the sequence's first qh row and qh row count, its
+// rows' smallest and largest position (INT32_MAX / -1 without rows), the
+// sequence.
+enum {
+  LI_MIN_TOK = 0,
+  LI_MAX_TOK,
+  LI_ALL_VALID,
+  LI_QH0,
+  LI_NQH,
+  LI_MINPOS,
+  LI_MAXPOS,
+  LI_SEQ,
+  LINK_INFO_WORDS = 8
+};
 
 }  // namespace plan
 

@@ -192,6 +192,14 @@ extern "C" int attn_bwd_paged_plan_build(int32_t nseq, const int32_t *seq_lens,
     for (int32_t r = 0; r < nq; ++r) seq_rows[fill[query_seq[r]]++] = r;  // ascending r
   }
 
+  // Smallest / largest query position of each sequence (INT32_MAX / -1 without rows).
+  std::vector<int32_t> seq_minpos((size_t)nseq, INT32_MAX), seq_maxpos((size_t)nseq, -1);
+  for (int32_t r = 0; r < nq; ++r) {
+    const int32_t s = query_seq[r];
+    seq_minpos[s] = std::min(seq_minpos[s], query_pos[r]);
+    seq_maxpos[s] = std::max(seq_maxpos[s], query_pos[r]);
+  }
+
   // Emit.
   int32_t *w = plan_out;
   std::fill(w, w + HEADER_WORDS, 0);
@@ -309,7 +317,11 @@ extern "C" int attn_bwd_paged_plan_build(int32_t nseq, const int32_t *seq_lens,
       info[LI_MIN_TOK] = tmin;
       info[LI_MAX_TOK] = tmax;
       info[LI_ALL_VALID] = all;
-      info[3] = 0;
+      info[LI_QH0] = (int32_t)(row_start[s] * group);
+      info[LI_NQH] = (int32_t)(rows_cnt[s + 1] * (int64_t)group);
+      info[LI_MINPOS] = seq_minpos[s];
+      info[LI_MAXPOS] = seq_maxpos[s];
+      info[LI_SEQ] = s;
       ++n_links;
     }
     for (int i = 0; i < kItemSlots; ++i)
@@ -323,18 +335,15 @@ extern "C" int attn_bwd_paged_plan_build(int32_t nseq, const int32_t *seq_lens,
   int32_t *seq_min = w + w[W_OFF_SEQ_MINPOS];
   for (int32_t s = 0; s <= nseq; ++s) seq_qh[s] = (int32_t)(row_start[s] * group);
   for (int32_t s = 0; s < nseq; ++s) {
-    int32_t mx = -1, mn = INT32_MAX;
     for (int64_t k = row_start[s]; k < row_start[s + 1]; ++k) {
       const int32_t r = seq_rows[k];
-      mx = std::max(mx, query_pos[r]);
-      mn = std::min(mn, query_pos[r]);
       for (int32_t hh = 0; hh < group; ++hh) {
         qh_rh[k * group + hh] = r * heads + hh;
         qh_pos[k * group + hh] = query_pos[r];
       }
     }
-    seq_max[s] = mx;
-    seq_min[s] = mn;
+    seq_max[s] = seq_maxpos[s];
+    seq_min[s] = seq_minpos[s];
   }
   std::copy(listed.begin(), listed.end(), w + w[W_OFF_LISTED]);
   int32_t *seq_tok = w + w[W_OFF_SEQ_TOK], *tok_slot = w + w[W_OFF_TOK_SLOT];

@@ -88,8 +88,10 @@ hipError_t launch_dense_stage(int stage, bool, int D, int mode, const DenseParam
   return hipSuccess;
 }
 
-hipError_t launch_paged(bool, int D, const PagedParams &p, int nblocks, hipStream_t) {
+hipError_t launch_paged(bool, int D, const PagedParams &p, int nblocks, int workgroups,
+                        hipStream_t) {
   ++n_launch;
+  if (workgroups < -1) die("paged kv_workgroups below -1 reached the launcher");
   if (nblocks <= 0 || (int64_t)nblocks != (int64_t)p.items * p.kv_heads) die("paged grid");
   if (p.mla ? (D != 64 && D != 128) : (D != 32 && D != 64 && D != 128)) die("paged head_dim");
   if (p.group < 1 || p.group * p.kv_heads != p.heads) die("paged group");
@@ -296,6 +298,13 @@ void check_plan(const std::vector<int32_t> &w, int32_t nseq, int32_t nq, int32_t
   const int32_t *sq = &w[w[W_OFF_SEQ_QH]];
   for (int32_t s = 0; s < nseq; ++s)
     if (sq[s] < 0 || sq[s] > sq[s + 1] || sq[s + 1] > qh) die("sequence -> row CSR");
+  for (int64_t l = 0; l < links; ++l) {  // the record's copy of its sequence's facts
+    const int32_t *li = &w[w[W_OFF_LINK_INFO] + l * LINK_INFO_WORDS];
+    const int32_t s = w[w[W_OFF_LINK_SEQ] + l];
+    if (li[LI_SEQ] != s || li[LI_QH0] != sq[s] || li[LI_NQH] != sq[s + 1] - sq[s] ||
+        li[LI_MINPOS] != w[w[W_OFF_SEQ_MINPOS] + s] || li[LI_MAXPOS] != w[w[W_OFF_SEQ_MAXPOS] + s])
+      die("link record");
+  }
   for (int64_t r = 0; r < qh; ++r) {
     const int32_t rh = w[w[W_OFF_QH_RH] + r];
     if (rh < 0 || (int64_t)rh >= (int64_t)nq * heads) die("qh row outside [0, nq * heads)");
@@ -328,6 +337,7 @@ void call_paged(const std::vector<int32_t> &plan, int32_t nq, int32_t heads, int
   a.head_dim = (int32_t)pick({32, 64, 128, 128, 96});
   a.page_size = page_size;
   a.causal = (int32_t)pick({0, 1, 1, 2});
+  a.kv_workgroups = (int32_t)(chance(90) ? pick({0, 0, 8, 256, -1}) : pick({-2, INT32_MIN}));
   a.nq = chance(95) ? nq : nq + 1;
   a.pool_pages = pool_pages;
   a.scale = chance(90) ? 0.088f : std::nanf("");

@@ -146,8 +146,8 @@ def test_unrequested_outputs_may_be_null():
 
 def test_paged_args_struct_size():
     # 9 int32 + float, then 9 pointers, the latent variant's 2 int32 + 3 pointers,
-    # the query side's workspace pointer and size
-    assert ctypes.sizeof(_abi.AttnBwdPagedArgs) == 40 + 9 * 8 + 8 + 3 * 8 + 16
+    # the query side's workspace pointer and size, kv_workgroups (+ tail padding)
+    assert ctypes.sizeof(_abi.AttnBwdPagedArgs) == 40 + 9 * 8 + 8 + 3 * 8 + 16 + 8
 
 
 def _paged_plan(heads=4, kv_heads=2):
@@ -191,6 +191,7 @@ def _paged_rc(a):
     ("nq", 4, _abi.ATTN_E_INVALID, "plan was built"),
     ("pool_pages", 5, _abi.ATTN_E_INVALID, "plan was built"),
     ("plan", 0, _abi.ATTN_E_INVALID, "plan"),
+    ("kv_workgroups", -2, _abi.ATTN_E_INVALID, "kv_workgroups"),
     ("q", 0, _abi.ATTN_E_INVALID, "q is NULL"),
     ("stats", (1 << 24) * 5 + 4, _abi.ATTN_E_UNSUPPORTED, "aligned"),
     ("dk_pool", 0, _abi.ATTN_E_INVALID, "dk_pool is NULL"),

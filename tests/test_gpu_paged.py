@@ -39,10 +39,13 @@ def _bits(t):
     return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).numpy()
 
 
-def run_case(w, *, causal=True, need="dkdv", stats=None, check=True, label="", gpu_stats=None):
+def run_case(w, *, causal=True, need="dkdv", stats=None, check=True, label="", gpu_stats=None,
+             kv_workgroups=0):
     """stats: the oracle's statistics (computed here when None), used by the
     reference and, rounded to fp32, by the GPU unless `gpu_stats` (a device
-    tensor computed on the GPU) is given for the GPU call."""
+    tensor computed on the GPU) is given for the GPU call.  kv_workgroups:
+    the dK / dV kernel form (0 automatic, n > 0 persistent with n workgroups,
+    -1 one workgroup per unit)."""
     heads, kv, ps = w["heads"], w["kv_heads"], w["page_size"]
     kw = dict(heads=heads, kv_heads=kv, page_size=ps)
     if stats is None:
@@ -51,15 +54,16 @@ def run_case(w, *, causal=True, need="dkdv", stats=None, check=True, label="", g
     plan = sb.paged_plan(w["seq_lens"], w["block_table"], w["query_seq"], w["query_pos"],
                          pool_pages=w["pool_pages"], device="cuda:0", **kw)
     print(f"[paged] {label} nq={w['q'].shape[0]} heads={heads}/{kv} D={w['D']} ps={ps} "
-          f"pool={w['pool_pages']} items={plan.items} {w['dtype']} causal={causal} need={need}",
-          flush=True)
+          f"pool={w['pool_pages']} items={plan.items} {w['dtype']} causal={causal} need={need} "
+          f"kv_workgroups={kv_workgroups}", flush=True)
     dev = torch.device("cuda:0")
     st32 = gpu_stats if gpu_stats is not None else torch.from_numpy(stats.astype(np.float32)).to(dev)
     q, dy, kp, vp = (w[n].to(dev) for n in ("q", "dy", "k_pool", "v_pool"))
     dk0, dv0 = _sentinel_pool(w["k_pool"]), _sentinel_pool(w["v_pool"])
     dk = dk0.to(dev) if need in ("dk", "dkdv") else None
     dv = dv0.to(dev) if need in ("dv", "dkdv") else None
-    sb.attn_bwd_paged(q, dy, kp, vp, st32, plan, dk_pool=dk, dv_pool=dv, need=need, causal=causal)
+    sb.attn_bwd_paged(q, dy, kp, vp, st32, plan, dk_pool=dk, dv_pool=dv, need=need, causal=causal,
+                      kv_workgroups=kv_workgroups)
     torch.cuda.synchronize()
     out = {"dk": None if dk is None else dk.cpu(), "dv": None if dv is None else dv.cpu(),
            "plan": plan, "stats": stats}
@@ -149,13 +153,74 @@ def test_paged_edge_sequences():
 def test_paged_config5_full():
     """16 sequences of UniformInt[256, 4096] tokens, 32 / 8 heads, D 128, page 16,
     64 queries per sequence at its last positions, 25% unused pool pages, bf16,
-    every listed slot against the oracle; then two more runs, bit-identical."""
+    every listed slot against the oracle (the form the library picks: the
+    persistent one on a GPU with fewer compute units than the 2648 units);
+    then a rerun of that form and a run of the one-workgroup-per-unit form,
+    all bit-identical."""
     w = sdpa_inputs.paged_workload(seed=1005)
     out = run_case(w, label="config5")
     print(f"[paged] config5 rel err dk {out['dk_err']:.3e} dv {out['dv_err']:.3e}", flush=True)
     again = run_case(w, stats=out["stats"], check=False, label="config5 rerun")
     assert torch.equal(_bits_t(out["dk"]), _bits_t(again["dk"]))
     assert torch.equal(_bits_t(out["dv"]), _bits_t(again["dv"]))
+    classic = run_case(w, stats=out["stats"], check=False, label="config5 per-unit form",
+                       kv_workgroups=-1)
+    assert torch.equal(_bits_t(out["dk"]), _bits_t(classic["dk"]))
+    assert torch.equal(_bits_t(out["dv"]), _bits_t(classic["dv"]))
+
+
+FORM_CASES = [c for c in CASES if c["dtype"] == torch.bfloat16] + [
+    # many items per workgroup, 16 queries per sequence (one-chunk links), GQA 4
+    dict(seed=110, nseq=6, len_lo=64, len_hi=900, q_per_seq=4, page_size=16, heads=8,
+         kv_heads=2, D=64, dtype=torch.bfloat16),
+    # many items per workgroup with two- and three-chunk links (unit switches
+    # while the next link's first two chunks are in flight), D 128
+    dict(seed=112, nseq=3, len_lo=300, len_hi=900, q_per_seq=32, page_size=16, heads=8,
+         kv_heads=2, D=128, dtype=torch.bfloat16),
+    dict(seed=113, nseq=3, len_lo=300, len_hi=900, q_per_seq=48, page_size=16, heads=8,
+         kv_heads=2, D=128, dtype=torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("case", FORM_CASES, ids=lambda c: f"seed{c['seed']}")
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+@pytest.mark.parametrize("wgs", [8, 16])
+def test_paged_persistent_form(case, causal, wgs):
+    """The persistent form with few workgroups (so each walks many units, links
+    and unit switches) against the oracle, and bit-identical to the
+    one-workgroup-per-unit form, on the full pools (unlisted slots untouched,
+    tail slots +0)."""
+    w = sdpa_inputs.paged_workload(**case)
+    if case["seed"] == 106:
+        qp = w["query_pos"].clone()
+        for s in range(len(w["seq_lens"])):
+            m = w["query_seq"] == s
+            qp[m] = qp[m] - int(w["seq_lens"][s]) // 2
+        w["query_pos"] = qp
+    label = f"seed{case['seed']} wgs={wgs}"
+    out = run_case(w, causal=causal, label=label, kv_workgroups=wgs)
+    ref = run_case(w, causal=causal, stats=out["stats"], check=False, label=label + " per-unit",
+                   kv_workgroups=-1)
+    for name in ("dk", "dv"):
+        assert torch.equal(_bits_t(out[name]), _bits_t(ref[name])), f"{label} {name}"
+
+
+@pytest.mark.parametrize("need", ["dk", "dv"])
+def test_paged_persistent_single_output_and_empty_units(need):
+    """One gradient only, a sequence without query rows (its units store
+    zeros from the persistent form's scan) and a zero-denominator row."""
+    w = sdpa_inputs.paged_workload(seed=111, nseq=4, len_lo=40, len_hi=400, q_per_seq=10,
+                                   page_size=16, heads=4, kv_heads=2, D=128, dtype=torch.bfloat16)
+    keep = w["query_seq"] != 2
+    for n in ("query_seq", "query_pos", "q", "dy"):
+        w[n] = w[n][keep].contiguous()
+    kw = dict(heads=4, kv_heads=2, page_size=16)
+    stats = oracle.paged_row_stats(w, w["q"], w["dy"], w["k_pool"], w["v_pool"], **kw)
+    stats[0, :, 1] = 0.0
+    stats[0, :, 0] = -np.inf
+    out = run_case(w, stats=stats, need=need, label=f"persistent need={need}", kv_workgroups=8)
+    ref = run_case(w, stats=stats, need=need, check=False, label="per-unit", kv_workgroups=-1)
+    assert torch.equal(_bits_t(out[need]), _bits_t(ref[need]))
 
 
 def _bits_t(t):
@@ -178,6 +243,8 @@ def test_paged_rejections():
         sb.attn_bwd_paged(q[..., :48].contiguous(), dy[..., :48].contiguous(),
                           kp[..., :48].contiguous(), vp[..., :48].contiguous(), st, plan,
                           dk_pool=dk[..., :48].contiguous(), need="dk")
+    with pytest.raises(sb.AttnError, match="kv_workgroups"):
+        sb.attn_bwd_paged(q, dy, kp, vp, st, plan, dk_pool=dk, need="dk", kv_workgroups=-2)
     bad = sb.PagedPlan(plan.words.copy(), heads=4, kv_heads=2, page_size=16,
                        pool_pages=w["pool_pages"], nq=plan.nq, device=dev)
     bad.words[0] ^= 1

@@ -39,7 +39,8 @@ def _tables(plan):
         item_links=W[h(_abi.W_OFF_ITEM_LINKS):][:items + 1],
         item_slots=W[h(_abi.W_OFF_ITEM_SLOTS):][:items * S].reshape(items, S),
         link_seq=W[h(_abi.W_OFF_LINK_SEQ):][:links],
-        link_info=W[h(_abi.W_OFF_LINK_INFO):][:links * 4].reshape(links, 4),
+        link_info=W[h(_abi.W_OFF_LINK_INFO):][:links * _abi.LINK_INFO_WORDS].reshape(
+            links, _abi.LINK_INFO_WORDS),
         link_tok=W[h(_abi.W_OFF_LINK_TOK):][:links * S].reshape(links, S),
         seq_qh=W[h(_abi.W_OFF_SEQ_QH):][:nseq + 1],
         qh_rh=W[h(_abi.W_OFF_QH_RH):][:qh],
@@ -100,11 +101,14 @@ def _from_plan(w, plan, causal=True):
         for li in range(t["item_links"][it], t["item_links"][it + 1]):
             s = int(t["link_seq"][li])
             toks = t["link_tok"][li]
-            mn, mx, allv, _ = t["link_info"][li]
+            mn, mx, allv, rq0, rnqh, rminp, rmaxp, rseq = t["link_info"][li]
             valid = toks[toks >= 0]
             assert mn == valid.min() and mx == valid.max()
             assert allv == int((toks >= 0).all())
             q0, q1 = t["seq_qh"][s], t["seq_qh"][s + 1]
+            # the record repeats the linked sequence's own facts
+            assert (rseq, rq0, rnqh) == (s, q0, q1 - q0)
+            assert (rminp, rmaxp) == (t["seq_minpos"][s], t["seq_maxpos"][s])
             for lane in range(_abi.PLAN_ITEM_SLOTS):
                 tok = int(toks[lane])
                 if tok < 0:
