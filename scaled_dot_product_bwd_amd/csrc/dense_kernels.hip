@@ -43,11 +43,12 @@ namespace attn {
 // from HBM.  The row statistics (three workgroups per CU) are fastest with all.
 constexpr int kKvGroup = 8, kDqGroup = 4, kRsGroup = 8;
 
-// The query-major kernels' chunk loops (dQ, and statistics + dQ) are unrolled
-// by three, so every step has its LDS buffers fixed at compile time (no
-// per-read address arithmetic); the row statistics and dK / dV rotate their
-// buffers at run time (unrolled, the former spills at three waves per SIMD;
-// the latter's body addresses with immediate offsets from one base anyway).
+// The dQ kernel's chunk loop is unrolled by three, so every step has its LDS
+// buffers fixed at compile time (no per-read address arithmetic); the row
+// statistics, statistics + dQ and dK / dV rotate their buffers at run time
+// (unrolled, the row statistics spill at three waves per SIMD; the others
+// address their bodies with immediate offsets from one base anyway, and the
+// fused pass keeps separate masked and unmasked loops).
 // Steps are unconditional (a conditional step would make the accumulators merge
 // across paths, which the compiler pays for with register copies); chunks no
 // row of a wave sees are computed like any other and contribute P = 0.
@@ -672,7 +673,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const typename M::frag of = load_frag<T>(orow, s * KS + half * KL, qvalid);
         dsum += frag_dot<T>(S.gf[q][s], of);
       }
-      dsum += __shfl_xor(dsum, 32);
+      dsum = halves_sum(dsum);
       const float L = qvalid ? p.flse[srow] : -INFINITY;
       const bool empty = !(L > -INFINITY);  // a row that sees no key: P = 0, delta = 0
       const float nls = (empty ? -INFINITY : -L * kLog2e) * p.inv_scale_log2;
@@ -776,9 +777,11 @@ template <typename T, int D> struct SdState {
 };
 
 // Chunk c (keys 64 c .. 64 c + 63, two 32-key sub-tiles u), whose tiles are in
-// buffer BC; chunk c + 2 goes to the buffer chunk c - 1 used.  The caller
-// unrolls the chunk loop by three, so every LDS address is a base plus a
-// compile-time offset.
+// buffer bc; chunk c + 2 goes to the buffer chunk c - 1 used.  MASKED is fixed
+// per loop by the caller (no branch inside the step: a branch would split the
+// step into blocks and let the compiler move the exponentials out of the
+// phase-A steps that hide them); the unmasked step is for chunks whose every
+// (query, key) pair the index rule keeps, with scale > 0.
 //   Phase A: the S^T chains of both sub-tiles, then their dP^T chains with the
 //     statistics' max and exponentials of S in the steps (one reference update
 //     per 64 keys, the row-statistics arithmetic over 32 scores per lane).
@@ -788,20 +791,19 @@ template <typename T, int D> struct SdState {
 //     (so each tile's shift overlaps the previous tile's MFMAs); then B and A'
 //     accumulate over the chunk's four 16-key steps, one transposed K fragment
 //     per pair of products.
-template <typename T, int D, int MODE, int BC>
-__device__ __forceinline__ void sd_step(const DenseParams &p, SdState<T, D> &S, int c,
-                                        Tile<T, D, kSdKeys> *Ks, Tile<T, D, kSdKeys> *Vs,
-                                        bool masked) {
+template <typename T, int D, int MODE, bool MASKED>
+__device__ __forceinline__ void sd_step(const DenseParams &p, SdState<T, D> &S, int c, int bc,
+                                        Tile<T, D, kSdKeys> *Ks, Tile<T, D, kSdKeys> *Vs) {
   typedef MT<T> M;
   typedef typename M::frag F;
   constexpr int NT = D / 32, CS = M::CSTEPS, NSD = D / M::KS, RING = kSdRing;
   constexpr int KC = kSdKeys, NU = KC / 32, L = ChunkIO<T, D, KC>::LOADS;
   constexpr int NA = 2 * NU * NSD;  // phase-A steps (S, then dP)
   static_assert(2 * L <= NA, "one load per phase-A step");
-  constexpr int bc = BC, bn = (BC + 2) % 3;
+  constexpr bool plain = !MASKED;
+  const int bn = bc == 0 ? 2 : bc - 1;
   const Tile<T, D, KC> *Kc = &Ks[bc], *Vc = &Vs[bc];
   const int l32 = S.lane & 31, half = S.half, j0 = c * KC;
-  const bool plain = MODE == MODE_INDEX && !masked && p.scale_log2 > 0.f;
   const float cl = p.scale_log2;
 
   // Chunk min(c + 2, c_last) into buffer bn, one load per phase-A step; past
@@ -811,11 +813,13 @@ __device__ __forceinline__ void sd_step(const DenseParams &p, SdState<T, D> &S, 
   const T *vn = S.vbase + (int64_t)cn * KC * p.vs[1];
   const int lastn = p.Sk - 1 - cn * KC;
   const unsigned ksb = (unsigned)(p.ks[1] * sizeof(T)), vsb = (unsigned)(p.vs[1] * sizeof(T));
+  constexpr unsigned TB = sizeof(Tile<T, D, KC>);
+  const unsigned klds = lds_addr(Ks) + bn * TB, vlds = lds_addr(Vs) + bn * TB;
   auto dma = [&](int k) {
     if (k < L)
-      S.io_k.issue_one(k, kn, lastn, ksb, Ks[bn]);
+      S.io_k.issue_one_at(k, kn, lastn, ksb, klds);
     else
-      S.io_v.issue_one(k - L, vn, lastn, vsb, Vs[bn]);
+      S.io_v.issue_one_at(k - L, vn, lastn, vsb, vlds);
   };
 
   F fr[RING];
@@ -835,7 +839,7 @@ __device__ __forceinline__ void sd_step(const DenseParams &p, SdState<T, D> &S, 
   auto stat_part = [&](int k) {
     if (k < NU) {  // sub-tile k's scores and running max
       const int u = k;
-      if (plain) {
+      if constexpr (plain) {
         if (u == 0) mx = sacc[0][0];
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[u][r]);
@@ -849,19 +853,25 @@ __device__ __forceinline__ void sd_step(const DenseParams &p, SdState<T, D> &S, 
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s2[u][r]);
       }
     } else if (k == NU) {
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      if (plain) mx *= cl;
+      mx = halves_max(mx);
+      if constexpr (plain) mx *= cl;
       al = row_stat_ref(S.st, mx, moved, mu);
     } else if (k < NU + 1 + 4 * NU) {  // exponentials, four at a time
       const int q = k - NU - 1, u = q / 4, r0 = 4 * (q % 4);
 #pragma unroll
-      for (int r = r0; r < r0 + 4; ++r)
-        pr[u][r] = fast_exp2(plain ? fmaf(sacc[u][r], cl, -mu) : s2[u][r] - mu);
+      for (int r = r0; r < r0 + 4; ++r) {
+        if constexpr (plain)
+          pr[u][r] = fast_exp2(fmaf(sacc[u][r], cl, -mu));
+        else
+          pr[u][r] = fast_exp2(s2[u][r] - mu);
+        pin(pr[u][r]);
+      }
     } else {
 #pragma unroll
       for (int u = 0; u < NU; ++u)
 #pragma unroll
         for (int r = 0; r < 16; ++r) ls += pr[u][r];
+      pin(ls);
     }
   };
 #pragma unroll
@@ -899,8 +909,8 @@ __device__ __forceinline__ void sd_step(const DenseParams &p, SdState<T, D> &S, 
   // delta's running estimate, this chunk included, through the hardware
   // reciprocal (l_tot >= 1 once a key is visible: the row's max term is
   // 2^(mtrue - mref) >= 1).  The epilogue moves A' to delta itself.
-  const float l_tot = S.st.l + __shfl_xor(S.st.l, 32);
-  const float dl_tot = S.st.dl + __shfl_xor(S.st.dl, 32);
+  const float l_tot = halves_sum(S.st.l);
+  const float dl_tot = halves_sum(S.st.dl);
   const float dh = l_tot > 0.f ? dl_tot * __builtin_amdgcn_rcpf(l_tot) : 0.f;
   const float shift = S.dh - dh;
   S.dh = dh;
@@ -1000,15 +1010,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     S.io_k.issue(S.kbase, p.ks[1], c1 * KC, p.Sk, Ks[1]);
     S.io_v.issue(S.vbase, p.vs[1], c1 * KC, p.Sk, Vs[1]);
   }
-  auto masked = [&](int c) { return c < R.cu0 || c > R.cu1; };
-  int c = R.c_first;
-  for (; c + 2 <= R.c_last; c += 3) {
-    sd_step<T, D, MODE, 0>(p, S, c, Ks, Vs, masked(c));
-    sd_step<T, D, MODE, 1>(p, S, c + 1, Ks, Vs, masked(c + 1));
-    sd_step<T, D, MODE, 2>(p, S, c + 2, Ks, Vs, masked(c + 2));
+  // Masked chunks before cu0 and after cu1, unmasked ones between (only for
+  // the index rule with scale > 0: the unmasked step takes the max of the raw
+  // scores); the buffers rotate at run time.
+  int cu0 = R.cu0, cu1 = R.cu1;
+  if (!(p.scale_log2 > 0.f)) {
+    cu0 = R.c_last + 1;
+    cu1 = R.c_last;
   }
-  if (c <= R.c_last) sd_step<T, D, MODE, 0>(p, S, c, Ks, Vs, masked(c));
-  if (c + 1 <= R.c_last) sd_step<T, D, MODE, 1>(p, S, c + 1, Ks, Vs, masked(c + 1));
+  int c = R.c_first, bc = 0;
+  auto next = [&]() {
+    ++c;
+    bc = bc == 2 ? 0 : bc + 1;
+  };
+  for (; c < cu0 && c <= R.c_last; next()) sd_step<T, D, MODE, true>(p, S, c, bc, Ks, Vs);
+  if constexpr (MODE == MODE_INDEX)
+    for (; c <= cu1; next()) sd_step<T, D, MODE, false>(p, S, c, bc, Ks, Vs);
+  for (; c <= R.c_last; next()) sd_step<T, D, MODE, true>(p, S, c, bc, Ks, Vs);
   wait_vmem();  // the repeated loads of the last steps land before the workgroup ends
 
   const RowStatOut o = row_stat_final(S.st, p.inv_scale_log2);

@@ -403,6 +403,20 @@ __device__ __forceinline__ bool idx_visible(const DenseParams &p, int i, int j) 
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Sum / max of x over lanes i and i ^ 32 (the two halves of the wave), through
+// v_permlane32_swap: a VALU exchange, no LDS round trip.  The swap returns
+// (lanes 0-31 of x in both halves, lanes 32-63 of x in both halves); both
+// operations are commutative, so every lane gets the bits of
+// op(x, x of lane ^ 32).
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // x, made opaque to the optimiser: what is derived from it is computed where it
 // is used instead of being hoisted out of a loop and kept live across it (in a
 // register the loop body needs, or in scratch memory).
@@ -410,6 +424,11 @@ __device__ __forceinline__ int fresh(int x) {
   asm volatile("" : "+v"(x));
   return x;
 }
+
+// Computes x here: an empty asm that reads and rewrites it, so the value is
+// formed before this point and the optimiser cannot sink its computation into
+// a later block (past a branch that follows it), where nothing would hide it.
+__device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
 
 
 // Workgroup id -> logical tile id.  The hardware hands workgroup i to XCD i % 8;
@@ -421,7 +440,8 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
   return x * per + (x < rem ? x : rem) + idx;
 }
 
-// Workgroup id -> (head, rank) for a grid of n = heads * nb tiles, nb per head.
+// Workgroup id -> (head, rank) for a grid of n = heads * nb tiles, nb per head
+// (tile_of_logical: the same for the logical id L = xcd_remap(id, n)).
 // Every XCD gets a contiguous range of heads (their tiles share its L2).  When
 // the heads split evenly over the 8 XCDs, an XCD takes its heads GS at a time
 // (all of them if GS does not divide their count) and runs each group's tiles
@@ -431,8 +451,7 @@ __device__ __forceinline__ int xcd_remap(int bid, int n) {
 // while only about GS heads' operands are in flight in the XCD's L2 at a time.
 // Otherwise the order is head by head.
 template <int GS>
-__device__ __forceinline__ void tile_order(int bid, int n, int nb, int &head, int &rank) {
-  const int L = xcd_remap(bid, n);
+__device__ __forceinline__ void tile_of_logical(int L, int n, int nb, int &head, int &rank) {
   if (n % (8 * nb) == 0) {
     const int hp = n / (8 * nb);  // heads per XCD
     const int gs = hp % GS == 0 ? GS : hp;
@@ -444,6 +463,10 @@ __device__ __forceinline__ void tile_order(int bid, int n, int nb, int &head, in
     head = L / nb;
     rank = L % nb;
   }
+}
+template <int GS>
+__device__ __forceinline__ void tile_order(int bid, int n, int nb, int &head, int &rank) {
+  tile_of_logical<GS>(xcd_remap(bid, n), n, nb, head, rank);
 }
 
 // Store 4 consecutive fp32 values as T.

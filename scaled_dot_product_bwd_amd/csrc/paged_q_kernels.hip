@@ -98,7 +98,7 @@ __device__ __forceinline__ void pq_step(const PagedParams &p, PqState<T, D, STAG
     float mx = s2[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s2[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = halves_max(mx);
     const float mn = fmaxf(S.m, mx);
     const float mu = mn == -INFINITY ? 0.f : mn;
     const float al = fast_exp2(S.m - mu);
@@ -228,8 +228,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // partial results of this piece: row 32 wave + l32 of the block
     const int64_t prow = ((int64_t)piece * p.kv_heads + g) * kQBlockRows + 32 * S.wave + l32;
     if constexpr (STAGE == PQ_STATS) {
-      const float l_tot = S.l + __shfl_xor(S.l, 32);
-      const float d_tot = S.dl + __shfl_xor(S.dl, 32);
+      const float l_tot = halves_sum(S.l);
+      const float d_tot = halves_sum(S.dl);
       if (half == 0) store4<float>(p.qws + 4 * prow, S.m, l_tot, d_tot, 0.f);
     } else {
       float *w = p.qws + prow * D;
@@ -243,8 +243,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     return;
   }
   if constexpr (STAGE == PQ_STATS) {
-    const float l_tot = S.l + __shfl_xor(S.l, 32);
-    const float d_tot = S.dl + __shfl_xor(S.dl, 32);
+    const float l_tot = halves_sum(S.l);
+    const float d_tot = halves_sum(S.dl);
     if (half == 0) {
       const bool empty = !(l_tot > 0.f);
       float *st = p.stats_out + 3 * rh;

@@ -153,7 +153,7 @@ __device__ __forceinline__ float row_stat_chunk(RowStat &st, const f32x16 &sacc,
     float mx = sacc[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+    mx = halves_max(mx) * c;
     al = row_stat_ref(st, mx, moved, mu);
 #pragma unroll
     for (int r = 0; r < 16; ++r) pr[r] = fast_exp2(fmaf(sacc[r], c, -mu));
@@ -164,7 +164,7 @@ __device__ __forceinline__ float row_stat_chunk(RowStat &st, const f32x16 &sacc,
     float mx = s2[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s2[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = halves_max(mx);
     al = row_stat_ref(st, mx, moved, mu);
 #pragma unroll
     for (int r = 0; r < 16; ++r) pr[r] = fast_exp2(s2[r] - mu);
@@ -181,8 +181,8 @@ struct RowStatOut {
 };
 __device__ __forceinline__ RowStatOut row_stat_final(const RowStat &st, float inv_scale_log2) {
   RowStatOut o;
-  const float l_tot = st.l + __shfl_xor(st.l, 32);
-  const float d_tot = st.dl + __shfl_xor(st.dl, 32);
+  const float l_tot = halves_sum(st.l);
+  const float d_tot = halves_sum(st.dl);
   o.empty = !(l_tot > 0.f);
   o.m = o.empty ? -INFINITY : st.mtrue * kLn2;
   o.l = o.empty ? 0.f : l_tot * fast_exp2(st.mref - st.mtrue);
