@@ -390,7 +390,7 @@ __device__ __forceinline__ void kv_step(const DenseParams &p, KvState<T, D> &S, 
     }
   };
   const float *stc = st[bc];
-  kv_chunk<T, D, D, MASKED, false, SPREAD ? 2 * LQ + 1 : 0>(
+  kv_chunk<T, D, D, MASKED, false, SPREAD ? 2 * LQ + 1 : 0, decltype(adj), decltype(dma), true>(
       S.kf, S.vf, S.dk, S.dv, &Qs[bc], &Gs[bc], stc, stc + ROWS, p.scale_log2, S.lane, adj, 1.f,
       dma);
   if (issued) {
@@ -433,9 +433,12 @@ __device__ __forceinline__ void kv_run(const DenseParams &p, KvState<T, D> &S, i
     S.io_g.complete(Gs[1]);
   }
   // A full drain: also the K / V fragment loads issued before (their latency
-  // overlaps the first chunks'; the compiler then knows them complete).
+  // overlaps the first chunks'; the compiler then knows them complete).  V is
+  // negated now, once per tile, with every load landed (the body's NEGV form).
   wait_vmem();
   __syncthreads();
+#pragma unroll
+  for (int s = 0; s < KvState<T, D>::NSD; ++s) S.vf[s] = neg_frag<T>(S.vf[s]);
   S.buf = 0;
   {
     const int vn = min(2, S.total - 1), hn = vn / S.nch;
@@ -532,7 +535,7 @@ __global__ __launch_bounds__(256) void k_kv_bwd(const DenseParams p) {
     __syncthreads();
     char *lk = reinterpret_cast<char *>(Qs) + w * RS::BYTES;
     char *lv = reinterpret_cast<char *>(Gs) + w * RS::BYTES;
-    if (p.need_dk) RS::write_tiles(S.dk, p.scale, lk, S.lane);
+    if (p.need_dk) RS::write_tiles(S.dk, -p.scale, lk, S.lane);  // dK was accumulated negated
     if (p.need_dv) RS::write_tiles(S.dv, 1.f, lv, S.lane);
     const int nvalid = max(0, min(32, p.Sk - S.jw));
     T *dk0 = (T *)p.dk + b * p.dks[0] + (int64_t)S.jw * p.dks[1] + g * p.dks[2];
@@ -548,7 +551,7 @@ __global__ __launch_bounds__(256) void k_kv_bwd(const DenseParams p) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * t + 8 * g + 4 * half;
-        const float sc = p.scale;
+        const float sc = -p.scale;  // dK was accumulated negated
         if (p.need_dk)
           store4<T>(dkrow + d0, sc * S.dk[t][4 * g], sc * S.dk[t][4 * g + 1], sc * S.dk[t][4 * g + 2],
                     sc * S.dk[t][4 * g + 3]);

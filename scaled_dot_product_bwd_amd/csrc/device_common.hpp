@@ -108,6 +108,16 @@ __device__ __forceinline__ float load_frag<float>(const float *row, int d0, bool
   return valid ? row[d0] : 0.f;
 }
 
+// A fragment with every element negated: the sign bits flipped, one 32-bit
+// xor per register (exact).
+template <typename T>
+__device__ __forceinline__ typename MT<T>::frag neg_frag(typename MT<T>::frag f);
+template <> __device__ __forceinline__ bf16x8 neg_frag<bf16>(bf16x8 f) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, f) ^ 0x80008000u);
+}
+template <> __device__ __forceinline__ float neg_frag<float>(float f) { return -f; }
+
 // Dot product of two fragments (a lane's KL elements), fp32.
 template <typename T>
 __device__ __forceinline__ float frag_dot(typename MT<T>::frag a, typename MT<T>::frag b);

@@ -14,7 +14,12 @@
 //                                            -delta are the accumulators' start)
 // K and V sit in registers as loaded: nothing is computed from them before
 // their first MFMA, so their loads go straight into the operand registers and
-// all of a tile's loads are in flight at once.
+// all of a tile's loads are in flight at once.  NEGV: the caller has negated V
+// once its loads landed (dP starts at +delta, the chain forms delta - dP, and
+// dS' and so dK^T come out negated, which the caller's store undoes) -- this
+// saves the negation of delta in every chunk.  The matrix core's internal sum
+// is not exactly sign-symmetric, so dK may differ from the plain form in the
+// last bits (same arithmetic otherwise; dV is unchanged).
 //   C  dV^T += dY^T P,  dK^T += Q^T dS'     A read transposed from LDS, B = C reuse
 //
 // Schedule.  With one wave per SIMD nothing hides latency but the wave's own
@@ -72,7 +77,7 @@ struct NoDma {
 };
 
 template <typename T, int DK, int DV, bool MASKED, bool MERGE, int NDMA = 0,
-          typename Adj, typename Dma = NoDma>
+          typename Adj, typename Dma = NoDma, bool NEGV = false>
 __device__ __forceinline__ void kv_chunk(const typename MT<T>::frag *kf,
                                          const typename MT<T>::frag *vf, f32x16 *dk, f32x16 *dv,
                                          const Tile<T, DK, KvShape<T>::ROWS> *Qc,
@@ -109,7 +114,7 @@ __device__ __forceinline__ void kv_chunk(const typename MT<T>::frag *kf,
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         sacc[u][4 * g + i] = nl4[i];
-        pacc[u][4 * g + i] = -dl4[i];
+        pacc[u][4 * g + i] = NEGV ? dl4[i] : -dl4[i];
       }
     }
   };
