@@ -785,11 +785,13 @@ template <typename T, int D> struct SdState {
 // step into blocks and let the compiler move the exponentials out of the
 // phase-A steps that hide them); the unmasked step is for chunks whose every
 // (query, key) pair the index rule keeps, with scale > 0.
-//   Phase A: the S^T chains of both sub-tiles, then their dP^T chains with the
-//     statistics' max and exponentials of S in the steps (one reference update
-//     per 64 keys, the row-statistics arithmetic over 32 scores per lane).
-//   Then: the sums, the rescale (rare, wave-uniform), delta's new estimate dh,
-//     the packed operands p~ (dP - dh) and p~.
+//   Phase A: the S^T chains of both sub-tiles, then their dP^T chains (sub-tile
+//     0's, then sub-tile 1's) with the statistics in the steps: the max and
+//     the exponentials of S (one reference update per 64 keys, the
+//     row-statistics arithmetic over 32 scores per lane), their sum, the
+//     packed p~, and sub-tile 0's part of sum p~ dP.
+//   Then: the rest of the sums, the rescale (rare, wave-uniform), delta's new
+//     estimate dh, the packed operand p~ (dP - dh).
 //   Phase C: per tile t, A' += (dh_old - dh) B just before its first product
 //     (so each tile's shift overlaps the previous tile's MFMAs); then B and A'
 //     accumulate over the chunk's four 16-key steps, one transposed K fragment
@@ -825,10 +827,12 @@ __device__ __forceinline__ void sd_step(const DenseParams &p, SdState<T, D> &S, 
       S.io_v.issue_one_at(k - L, vn, lastn, vsb, vlds);
   };
 
+  // Phase A: the S chains of both sub-tiles interleaved (u = i % NU), then the
+  // dP chains one sub-tile after the other (sub-tile 0's completes halfway).
   F fr[RING];
   auto load = [&](int i) {  // step i < NA / 2: K of sub-tile i % NU, else V
     const int half_a = NA / 2, ii = i < half_a ? i : i - half_a;
-    const int u = ii % NU, s = ii / NU;
+    const int u = i < half_a ? ii % NU : ii / NSD, s = i < half_a ? ii / NU : ii % NSD;
     fr[i % RING] = i < half_a ? Kc->frag(32 * u + l32, s, half) : Vc->frag(32 * u + l32, s, half);
   };
 #pragma unroll
@@ -836,9 +840,20 @@ __device__ __forceinline__ void sd_step(const DenseParams &p, SdState<T, D> &S, 
   f32x16 sacc[NU], pacc[NU];
 #pragma unroll
   for (int u = 0; u < NU; ++u) sacc[u] = pacc[u] = f32x16{};
-  float s2[NU][16], pr[NU][16], mx = 0.f, mu = 0.f, al = 1.f, ls = 0.f;
+  float s2[NU][16], pr[NU][16], mx = 0.f, mu = 0.f, al = 1.f, ls = 0.f, ds = 0.f;
   bool moved = false;
-  constexpr int NPART = 3 + 4 * NU + 1;
+  F uf[NU][CS], pf[NU][CS];
+  // The statistics spread over the dP steps, part k:
+  //   k < NU: sub-tile k's scores and running max;  k = NU: the reference;
+  //   then the exponentials four at a time (their sum l as they come);
+  //   then each sub-tile's p~ packed for phase C;
+  //   then sum p~ dP over sub-tile 0 (its dP chain is done by then), in
+  //   three pieces.  Every sum runs in the order of the plain loop.
+  constexpr int KX = NU + 1, KP = KX + 4 * NU, KD = KP + NU, NPART = KD + 3;
+  // the mask term (log2 domain) of element r of sub-tile u
+  auto adj_of = [&](int u, int r) {
+    return q_adj<MODE>(p, S.b, S.h, S.qi, j0 + 32 * u + kr(r, half), S.ks);
+  };
   auto stat_part = [&](int k) {
     if (k < NU) {  // sub-tile k's scores and running max
       const int u = k;
@@ -848,9 +863,7 @@ __device__ __forceinline__ void sd_step(const DenseParams &p, SdState<T, D> &S, 
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[u][r]);
       } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          s2[u][r] = fmaf(sacc[u][r], cl,
-                          q_adj<MODE>(p, S.b, S.h, S.qi, j0 + 32 * u + kr(r, half), S.ks));
+        for (int r = 0; r < 16; ++r) s2[u][r] = fmaf(sacc[u][r], cl, adj_of(u, r));
         if (u == 0) mx = s2[0][0];
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s2[u][r]);
@@ -859,22 +872,26 @@ __device__ __forceinline__ void sd_step(const DenseParams &p, SdState<T, D> &S, 
       mx = halves_max(mx);
       if constexpr (plain) mx *= cl;
       al = row_stat_ref(S.st, mx, moved, mu);
-    } else if (k < NU + 1 + 4 * NU) {  // exponentials, four at a time
-      const int q = k - NU - 1, u = q / 4, r0 = 4 * (q % 4);
+    } else if (k < KP) {  // exponentials, four at a time, and their sum
+      const int q = k - KX, u = q / 4, r0 = 4 * (q % 4);
 #pragma unroll
       for (int r = r0; r < r0 + 4; ++r) {
         if constexpr (plain)
           pr[u][r] = fast_exp2(fmaf(sacc[u][r], cl, -mu));
         else
           pr[u][r] = fast_exp2(s2[u][r] - mu);
-        pin(pr[u][r]);
+        ls += pr[u][r];
       }
-    } else {
-#pragma unroll
-      for (int u = 0; u < NU; ++u)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) ls += pr[u][r];
       pin(ls);
+    } else if (k < KD) {  // sub-tile k - KP's p~ for phase C
+      const int u = k - KP;
+#pragma unroll
+      for (int st = 0; st < CS; ++st) pf[u][st] = creuse<T>(pr[u], st);
+    } else {  // sum p~ dP, sub-tile 0, piece k - KD
+      const int r0 = (k - KD) * 16 / 3, r1 = (k - KD + 1) * 16 / 3;
+#pragma unroll
+      for (int r = r0; r < r1; ++r) ds = fmaf(pr[0][r], pacc[0][r], ds);
+      pin(ds);
     }
   };
 #pragma unroll
@@ -886,7 +903,7 @@ __device__ __forceinline__ void sd_step(const DenseParams &p, SdState<T, D> &S, 
       const int u = i % NU, s = i / NU;
       sacc[u] = M::mma(fr[i % RING], S.qf[s], sacc[u]);
     } else {
-      const int ii = i - NA / 2, u = ii % NU, s = ii / NU;
+      const int ii = i - NA / 2, u = ii / NSD, s = ii % NSD;
       pacc[u] = M::mma(fr[i % RING], S.gf[s], pacc[u]);
 #pragma unroll
       for (int k = ii * NPART / (NA / 2); k < (ii + 1) * NPART / (NA / 2); ++k) stat_part(k);
@@ -894,9 +911,8 @@ __device__ __forceinline__ void sd_step(const DenseParams &p, SdState<T, D> &S, 
   }
   sched_fence();
   {
-    float ds = 0.f;
 #pragma unroll
-    for (int u = 0; u < NU; ++u)
+    for (int u = 1; u < NU; ++u)
 #pragma unroll
       for (int r = 0; r < 16; ++r) ds = fmaf(pr[u][r], pacc[u][r], ds);
     S.st.l = fmaf(S.st.l, al, ls);
@@ -917,7 +933,6 @@ __device__ __forceinline__ void sd_step(const DenseParams &p, SdState<T, D> &S, 
   const float dh = l_tot > 0.f ? dl_tot * __builtin_amdgcn_rcpf(l_tot) : 0.f;
   const float shift = S.dh - dh;
   S.dh = dh;
-  F uf[NU][CS], pf[NU][CS];
 #pragma unroll
   for (int u = 0; u < NU; ++u)
 #pragma unroll
@@ -927,7 +942,6 @@ __device__ __forceinline__ void sd_step(const DenseParams &p, SdState<T, D> &S, 
       for (int e = 0; e < 16 / CS; ++e)
         pd[e] = pr[u][st * (16 / CS) + e] * (pacc[u][st * (16 / CS) + e] - dh);
       uf[u][st] = creuse<T>(pd, 0);
-      pf[u][st] = creuse<T>(pr[u], st);
     }
 
   constexpr int NC = NU * CS * NT;
