@@ -535,7 +535,7 @@ __global__ __launch_bounds__(256) void k_kv_bwd(const DenseParams p) {
     __syncthreads();
     char *lk = reinterpret_cast<char *>(Qs) + w * RS::BYTES;
     char *lv = reinterpret_cast<char *>(Gs) + w * RS::BYTES;
-    if (p.need_dk) RS::write_tiles(S.dk, -p.scale, lk, S.lane);  // dK was accumulated negated
+    if (p.need_dk) RS::template write_tiles<true>(S.dk, p.scale, lk, S.lane);  // dK was accumulated negated
     if (p.need_dv) RS::write_tiles(S.dv, 1.f, lv, S.lane);
     const int nvalid = max(0, min(32, p.Sk - S.jw));
     T *dk0 = (T *)p.dk + b * p.dks[0] + (int64_t)S.jw * p.dks[1] + g * p.dks[2];
@@ -551,10 +551,10 @@ __global__ __launch_bounds__(256) void k_kv_bwd(const DenseParams p) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * t + 8 * g + 4 * half;
-        const float sc = -p.scale;  // dK was accumulated negated
+        const float sc = p.scale;  // dK was accumulated negated: 0 - sc * x (a zero stays +0)
         if (p.need_dk)
-          store4<T>(dkrow + d0, sc * S.dk[t][4 * g], sc * S.dk[t][4 * g + 1], sc * S.dk[t][4 * g + 2],
-                    sc * S.dk[t][4 * g + 3]);
+          store4<T>(dkrow + d0, 0.f - sc * S.dk[t][4 * g], 0.f - sc * S.dk[t][4 * g + 1],
+                    0.f - sc * S.dk[t][4 * g + 2], 0.f - sc * S.dk[t][4 * g + 3]);
         if (p.need_dv)
           store4<T>(dvrow + d0, S.dv[t][4 * g], S.dv[t][4 * g + 1], S.dv[t][4 * g + 2],
                     S.dv[t][4 * g + 3]);

@@ -501,16 +501,19 @@ template <typename T, int D> struct RowStore {
   static constexpr int ES = sizeof(T), RB = D * ES + 16;  // padded row bytes
   static constexpr int BYTES = 32 * RB;
   static constexpr int LPR = D * ES / 16, RPI = 64 / LPR;  // lanes per row, rows per instruction
+  // NEG: the tiles hold the negated values; 0 - scale * acc restores them
+  // exactly and keeps a zero +0.
+  template <bool NEG = false>
   __device__ __forceinline__ static void write_tiles(const f32x16 *acc, float scale, char *lds,
                                                      int lane) {
     const int l32 = lane & 31, half = lane >> 5;
+    auto v = [&](int t, int r) { return NEG ? 0.f - scale * acc[t][r] : scale * acc[t][r]; };
 #pragma unroll
     for (int t = 0; t < D / 32; ++t)
 #pragma unroll
       for (int g = 0; g < 4; ++g)
         store4<T>(reinterpret_cast<T *>(lds + l32 * RB) + 32 * t + 8 * g + 4 * half,
-                  scale * acc[t][4 * g], scale * acc[t][4 * g + 1], scale * acc[t][4 * g + 2],
-                  scale * acc[t][4 * g + 3]);
+                  v(t, 4 * g), v(t, 4 * g + 1), v(t, 4 * g + 2), v(t, 4 * g + 3));
   }
   template <typename F>
   __device__ __forceinline__ static void store_rows(const char *lds, int nvalid, F rowptr, int lane) {

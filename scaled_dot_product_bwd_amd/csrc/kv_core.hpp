@@ -16,7 +16,8 @@
 // their first MFMA, so their loads go straight into the operand registers and
 // all of a tile's loads are in flight at once.  NEGV: the caller has negated V
 // once its loads landed (dP starts at +delta, the chain forms delta - dP, and
-// dS' and so dK^T come out negated, which the caller's store undoes) -- this
+// dS' and so dK^T come out negated, which the caller's store undoes as
+// 0 - scale * x, keeping a zero +0) -- this
 // saves the negation of delta in every chunk.  The matrix core's internal sum
 // is not exactly sign-symmetric, so dK may differ from the plain form in the
 // last bits (same arithmetic otherwise; dV is unchanged).

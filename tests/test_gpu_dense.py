@@ -134,6 +134,24 @@ def test_fully_masked_padding_batch():
     assert np.all(res["l"][1] == 0) and np.all(np.isneginf(res["m"][1]))
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_unseen_keys_get_positive_zero_gradients(dtype):
+    """Keys no row sees (hidden by key padding) get dK = dV = +0 exactly, sign
+    bit clear: the dK / dV pass accumulates dK negated and stores 0 - scale x."""
+    B, H, Sq, Sk, D = 2, 2, 130, 300, 128
+    q, k, v, dy, _ = sdpa_inputs.dense_inputs(B, Sq, Sk, H, D, seed=17, dtype=dtype)
+    valid = torch.ones(B, 1, 1, Sk)
+    valid[1] = 0.0
+    valid[0, ..., 200:] = 0.0
+    res = gpu_run(q, k, v, dy, mask_kind="keypad", mask=valid)
+    for n in ("dk", "dv"):
+        hidden = np.concatenate([res[n][0, 200:].ravel(), res[n][1].ravel()])
+        assert np.all(hidden == 0.0), n
+        assert not np.signbit(hidden).any(), f"{n}: a negative zero"
+    ref = oracle_run(q, k, v, dy, mask_kind="keypad", mask=valid)
+    assert_parity(res, ref, dtype)
+
+
 def test_empty_sequence_dims():
     q, k, v, dy, _ = sdpa_inputs.dense_inputs(1, 0, 40, 2, 32, seed=1, dtype=torch.float32)
     res = gpu_run(q, k, v, dy)
