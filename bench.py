@@ -48,9 +48,9 @@ fp32 row statistics; one step = one attn_bwd_paged call (plan built and
 uploaded beforehand).  Its roofline is HBM: algorithmic bytes (K / V history
 read once, dK / dV written over the listed pages, Q, dY and statistics read
 once) over the kernel time.  The line also times the query side (statistics
-and dQ on the GPU; split form, and the direct form beside it) and gives the
-whole chain's rate counted like the dense metric (10 D flops per visible
-triple).
+and dQ on the GPU, as two calls and as one fused call; split form, and the
+direct form beside it) and gives the whole chain's rate (fused query side plus
+dK / dV) counted like the dense metric (10 D flops per visible triple).
 
 --workload paged_mla measures the latent variant of the same kernel on the same
 page tables (16 query heads on one latent KV head of width 128 plus a position
@@ -382,10 +382,11 @@ def paged_measure(args, torch, sdb, dev, cpu=True):
     per = dist(time_calls(step, max(100, args.steps), torch))
     if not all(torch.isfinite(x[w["live_slots"].to(dev)]).all().item() for x in (dk, dv)):
         raise RuntimeError("non-finite gradients in the benchmark output")
-    # The query side (statistics and dQ on the GPU, attn_bwd_paged_row_stats /
-    # attn_bwd_paged_dq), timed the same way; reported beside the dK / dV line.
-    # Split form (each block's tokens in pieces of <= 1024, merged; the default)
-    # and the direct form (one workgroup per block).
+    # The query side (statistics and dQ on the GPU: attn_bwd_paged_row_stats and
+    # attn_bwd_paged_dq, and both in one call, attn_bwd_paged_stats_dq), timed
+    # the same way; reported beside the dK / dV line.  Split form (each block's
+    # tokens in pieces of <= 1024, merged; the default) and the direct form (one
+    # workgroup per block).  The full chain is the fused call plus dK / dV.
     st_gpu = torch.empty_like(stats)
     dq = torch.empty_like(q)
     qws = sdb.paged_q_workspace(plan, D, dev)
@@ -408,6 +409,34 @@ def paged_measure(args, torch, sdb, dev, cpu=True):
             t1.record()
             torch.cuda.synchronize()
             dst[name] = round(t0.elapsed_time(t1) / args.steps, 4)
+        # both in one call (attn_bwd_paged_stats_dq; with the workspace the
+        # library picks the form, a.q_form = 0)
+        def fstep():
+            rc = lib.attn_bwd_paged_stats_dq(ctypes.byref(a), ctypes.c_void_p(st_gpu.data_ptr()),
+                                             ctypes.c_void_p(dq.data_ptr()), handle)
+            if rc != 0:
+                raise RuntimeError(lib.attn_bwd_last_error().decode())
+        for _ in range(args.warmup):
+            fstep()
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(args.steps):
+            fstep()
+        t1.record()
+        torch.cuda.synchronize()
+        dst["stats_dq_fused"] = round(t0.elapsed_time(t1) / args.steps, 4)
+    # the fused call's split form, forced (for the record)
+    a.q_workspace, a.q_workspace_bytes, a.q_form = qws.data_ptr(), qws.numel(), 1
+    for _ in range(args.warmup):
+        fstep()
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        fstep()
+    t1.record()
+    torch.cuda.synchronize()
+    q_ms["stats_dq_fused_split_form"] = round(t0.elapsed_time(t1) / args.steps, 4)
+    a.q_form = 0
     nbytes = paged_bytes(w, plan)
     flops = paged_flops(w)
     gbs = nbytes / (ms / 1e3) / 1e9
@@ -433,8 +462,9 @@ def paged_measure(args, torch, sdb, dev, cpu=True):
                      "bytes_per_launch": nbytes},
         "query_side_ms": q_ms,
         "query_side_direct_ms": q_direct_ms,
-        "full_chain_ms": round(ms + sum(q_ms.values()), 4),
-        "full_chain_tflops": round(flops * 10.0 / 8.0 / ((ms + sum(q_ms.values())) / 1e3) / 1e12, 3),
+        "full_chain_ms": round(ms + q_ms["stats_dq_fused"], 4),
+        "full_chain_tflops": round(flops * 10.0 / 8.0 / ((ms + q_ms["stats_dq_fused"]) / 1e3) / 1e12, 3),
+        "full_chain_separate_ms": round(ms + q_ms["row_stats"] + q_ms["dq"], 4),
         "cpu_baseline": cpu_line,
     }
 

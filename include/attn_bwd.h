@@ -244,6 +244,16 @@ typedef struct attn_bwd_paged_args {
    * of 8, at least 8, at most the units rounded up to 8); -1: one workgroup
    * per unit.  Every form gives identical bits.  Below -1: ATTN_E_INVALID. */
   int32_t kv_workgroups;
+  /* Form of attn_bwd_paged_stats_dq (bf16; ignored by the other calls and for
+   * fp32).  0: chosen by the library: without q_workspace the direct form (one
+   * workgroup per (query block, KV head)); with it, the split form only where
+   * the plan's estimated time is lower (a few long sequences: the direct form
+   * waits for the longest block; many blocks: the split form pays a fixed
+   * cost per piece and the merge).  1: the split form (q_workspace required,
+   * else ATTN_E_WORKSPACE); 2: the direct form (q_workspace not used).  The
+   * forms differ in rounding order; each is bit-identical from run to run.
+   * Other values: ATTN_E_INVALID. */
+  int32_t q_form;
 } attn_bwd_paged_args;
 
 /* Enqueues the paged backward.  Every device pointer must be 16-byte aligned;
@@ -277,11 +287,27 @@ int attn_bwd_paged(const attn_bwd_paged_args *a, void *stream);
 int attn_bwd_paged_row_stats(const attn_bwd_paged_args *a, float *stats, void *stream);
 
 /* Bytes of q_workspace the split form of the query side needs for a plan
- * (host words) and head_dim: pieces * kv_heads * 128 rows * head_dim fp32
- * (the statistics use 4 of the head_dim floats per row).  0 for a buffer that
- * is not a plan. */
+ * (host words) and head_dim, for any of the three query-side calls:
+ * pieces * kv_heads * 128 rows * (2 head_dim + 8) fp32 (the fused call's
+ * partial statistics and two partial accumulators per row; the others use 4
+ * or head_dim of those floats).  0 for a buffer that is not a plan. */
 size_t attn_bwd_paged_q_workspace_bytes(const int32_t *plan_host, int32_t head_dim);
 int attn_bwd_paged_dq(const attn_bwd_paged_args *a, void *dq, void *stream);
+
+/* Both of the above in one call: `stats` as attn_bwd_paged_row_stats writes
+ * it and `dq` as attn_bwd_paged_dq would write it from those statistics
+ * (rlx-cpu `backward_dense_head_all` forms dS = P (dP - rowsum(P dP)) scale
+ * and dQ = dS K; ruDNN `history_backward` takes the statistics from a
+ * query-side kernel).  bf16: one pass over the tokens, accumulating
+ * A = sum P~ (dP - d) k and B = sum P~ k against the running statistics
+ * (P~ = exp(s - running max), d = the running estimate of delta), so that
+ * dq = scale (A + (d - delta) B) / denominator; the statistics equal
+ * attn_bwd_paged_row_stats's up to rounding, dq equals attn_bwd_paged_dq's
+ * from them up to rounding.  fp32: the two calls in sequence.  Outputs must
+ * not overlap each other or an input; with q_workspace (split form) the
+ * workspace needs attn_bwd_paged_q_workspace_bytes().  Reruns are
+ * bit-identical.  Errors as attn_bwd_paged; nothing is launched on error. */
+int attn_bwd_paged_stats_dq(const attn_bwd_paged_args *a, float *stats, void *dq, void *stream);
 
 /* The dense backward from what a forward pass saved, instead of recomputing
  * the row statistics: `lse` (device fp32 [B, H, Sq], contiguous) holds, per

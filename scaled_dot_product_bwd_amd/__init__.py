@@ -9,9 +9,8 @@ There is no CPU fallback: without the built library every call raises.
 
     plan = paged_plan(seq_lens, block_table, query_seq, query_pos, heads=32,
                       kv_heads=8, page_size=16, pool_pages=N, device="cuda")
-    stats = paged_row_stats(q, dy, k_pool, v_pool, plan)
+    stats, dq = paged_stats_dq(q, dy, k_pool, v_pool, plan)
     attn_bwd_paged(q, dy, k_pool, v_pool, stats, plan, dk_pool=dk, dv_pool=dv)
-    dq = attn_bwd_paged_dq(q, dy, k_pool, v_pool, stats, plan)
 
 Tensors are ``[B, S, H, D]`` (any strides with ``D`` contiguous; pass
 ``x.transpose(1, 2)`` for a ``[B, H, S, D]`` tensor), float32 or bfloat16, on the
@@ -36,7 +35,7 @@ __all__ = ["attn_bwd", "attn_bwd_noalloc", "attn_bwd_stage", "workspace_bytes", 
            "load_library", "library_path", "MASKS", "WRT", "PagedPlan", "paged_plan",
            "attn_bwd_paged", "attn_bwd_paged_mla", "make_paged_args", "paged_row_stats",
            "paged_q_workspace",
-           "attn_bwd_paged_dq"]
+           "attn_bwd_paged_dq", "paged_stats_dq"]
 
 MASKS = {"none": ATTN_MASK_NONE, "causal": ATTN_MASK_CAUSAL, "keypad": ATTN_MASK_KEYPAD,
          "window": ATTN_MASK_WINDOW, "bias": ATTN_MASK_BIAS}
@@ -587,3 +586,40 @@ def attn_bwd_paged_dq(q, dy, k_pool, v_pool, stats, plan, *, causal=True, scale=
                                             handle))
     _record(side, out, ws, plan.device_words)
     return out
+
+
+def paged_stats_dq(q, dy, k_pool, v_pool, plan, *, causal=True, scale=None, stats_out=None,
+                   dq_out=None, stream=None, form="auto", workspace=None):
+    """The statistics [nq, heads, 3] and dQ [nq, heads, D] of the paged layout in
+    one call (attn_bwd_paged_stats_dq: one pass over the tokens for bf16).
+    form: "auto" (a workspace is allocated unless one is given, and the library
+    picks the split or the direct form from the plan), "split" or "direct".
+    Returns (stats, dq)."""
+    torch = _torch()
+    dt = _io_dtype(q)
+    nq, heads, D = q.shape
+    forms = {"auto": 0, "split": 1, "direct": 2}
+    if form not in forms:
+        raise ValueError(f"form must be one of {sorted(forms)}")
+    if stats_out is not None:  # checked as the call's input statistics below
+        _check_float("stats_out", stats_out, torch.float32)
+    if plan.device_words is None:
+        plan.to(q.device)
+    if stats_out is None:
+        stats_out = torch.empty(nq, heads, 3, dtype=torch.float32, device=q.device)
+    if dq_out is None:
+        dq_out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    args = make_paged_args(q, dy, k_pool, v_pool, stats_out, plan, causal=causal, scale=scale,
+                           outs=[("dq", dq_out, tuple(q.shape), dt)])
+    args.q_form = forms[form]
+    ws = None
+    if form != "direct":
+        ws = workspace if workspace is not None else paged_q_workspace(plan, D, q.device)
+        _check_devices(q.device, [("workspace", ws)])
+        _set_q_workspace(args, ws)
+    handle, side = _launch_stream(stream, q.device)
+    _check(load_library().attn_bwd_paged_stats_dq(ctypes.byref(args),
+                                                  ctypes.c_void_p(stats_out.data_ptr()),
+                                                  ctypes.c_void_p(dq_out.data_ptr()), handle))
+    _record(side, stats_out, dq_out, ws, plan.device_words)
+    return stats_out, dq_out

@@ -25,7 +25,7 @@ EXPORTED = ["attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_row_stats", "attn_
             "attn_bwd_dq", "attn_bwd_stats_dq", "attn_bwd_paged_plan_words", "attn_bwd_paged_plan_build",
             "attn_bwd_paged", "attn_bwd_paged_row_stats", "attn_bwd_paged_dq",
             "attn_bwd_from_forward", "attn_bwd_paged_q_workspace_bytes",
-            "attn_bwd_last_error", "attn_bwd_noalloc"]
+            "attn_bwd_last_error", "attn_bwd_noalloc", "attn_bwd_paged_stats_dq"]
 
 # Plan header words (scaled_dot_product_bwd_amd/csrc/paged.hpp).
 PLAN_MAGIC = 0x32504241
@@ -86,7 +86,7 @@ class AttnBwdPagedArgs(ctypes.Structure):
         ("qp", ctypes.c_void_p), ("kp_pool", ctypes.c_void_p),
         ("dkp_pool", ctypes.c_void_p),
         ("q_workspace", ctypes.c_void_p), ("q_workspace_bytes", ctypes.c_size_t),
-        ("kv_workgroups", ctypes.c_int32),
+        ("kv_workgroups", ctypes.c_int32), ("q_form", ctypes.c_int32),
     ]
 
 
@@ -129,6 +129,9 @@ def load_library():
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [ctypes.POINTER(AttnBwdPagedArgs), ctypes.c_void_p, ctypes.c_void_p]
+    lib.attn_bwd_paged_stats_dq.restype = ctypes.c_int
+    lib.attn_bwd_paged_stats_dq.argtypes = [ctypes.POINTER(AttnBwdPagedArgs), ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_void_p]
     lib.attn_bwd_paged_q_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_bwd_paged_q_workspace_bytes.argtypes = [_p, _i32]
     lib.attn_bwd_last_error.restype = ctypes.c_char_p

@@ -7,6 +7,7 @@
 // path (rlx-cpu panics on a bad slice, rlx-metal `use_gpu` falls back to the
 // CPU, rlx-wgpu `attention_bwd` silently returns for head_dim > 128); here
 // every unsupported or inconsistent request is an explicit status.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -368,12 +369,12 @@ int run_from_forward(const attn_bwd_args *a, const float *lse, const void *out,
 // ---------------------------------------------------------------------------
 // Paged history backward.
 
-// What a paged call computes: dK / dV (attn_bwd_paged), the statistics or dQ
-// (the query side).
-enum PagedMode { PM_KV = 0, PM_STATS = 1, PM_DQ = 2 };
+// What a paged call computes: dK / dV (attn_bwd_paged), the statistics, dQ or
+// both (the query side).  PM_SDQ: out = the statistics, out2 = dQ.
+enum PagedMode { PM_KV = 0, PM_STATS = 1, PM_DQ = 2, PM_SDQ = 3 };
 
-int validate_paged(const attn_bwd_paged_args *a, int mode, void *out, attn::PagedParams &p,
-                   int &nblocks, bool &bf16) {
+int validate_paged(const attn_bwd_paged_args *a, int mode, void *out, void *out2,
+                   attn::PagedParams &p, int &nblocks, bool &bf16) {
   using namespace attn::plan;
   if (!a) return fail(ATTN_E_INVALID, "args is NULL");
   if (a->dtype != ATTN_F32 && a->dtype != ATTN_BF16)
@@ -401,6 +402,8 @@ int validate_paged(const attn_bwd_paged_args *a, int mode, void *out, attn::Page
     return fail(ATTN_E_UNSUPPORTED, "|scale| outside [2^-64, 2^64] (including 0) is not supported");
   if (a->causal != 0 && a->causal != 1) return fail(ATTN_E_INVALID, "causal must be 0 or 1");
   if (a->kv_workgroups < -1) return fail(ATTN_E_INVALID, "kv_workgroups is below -1");
+  if (mode == PM_SDQ && (a->q_form < 0 || a->q_form > 2))
+    return fail(ATTN_E_INVALID, "q_form %d is not 0, 1 or 2", a->q_form);
   const int32_t *w = a->plan_host;
   if (!w || !a->plan) return fail(ATTN_E_INVALID, "plan_host / plan is NULL");
   if (w[W_MAGIC] != kMagic) return fail(ATTN_E_INVALID, "plan_host is not a plan (bad magic)");
@@ -429,7 +432,8 @@ int validate_paged(const attn_bwd_paged_args *a, int mode, void *out, attn::Page
   const int64_t qrows = (int64_t)a->nq * a->heads;
   const int64_t pslots = (int64_t)a->pool_pages * a->page_size * a->kv_heads;
   const bool work = nblocks > 0, kv = mode == PM_KV;
-  constexpr int NT = 11, FIRST_OUT = 8;
+  constexpr int NT = 12, FIRST_OUT = 8;
+  const bool st_out = mode == PM_STATS || mode == PM_SDQ;
   struct T {
     const char *name;
     const void *ptr;
@@ -438,7 +442,7 @@ int validate_paged(const attn_bwd_paged_args *a, int mode, void *out, attn::Page
   } ts[NT] = {
       {"q", a->q, qrows * D * (int64_t)es, work && qrows > 0},
       {"dy", a->dy, qrows * D * (int64_t)es, work && qrows > 0},
-      {"stats", a->stats, qrows * 3 * (int64_t)sizeof(float), work && qrows > 0 && mode != PM_STATS},
+      {"stats", a->stats, qrows * 3 * (int64_t)sizeof(float), work && qrows > 0 && (mode == PM_KV || mode == PM_DQ)},
       {"k_pool", a->k_pool, pslots * D * (int64_t)es, work},
       {"v_pool", a->v_pool, pslots * D * (int64_t)es, work && !mla},
       {"qp", a->qp, qrows * P * (int64_t)es, work && qrows > 0 && P > 0},
@@ -446,10 +450,11 @@ int validate_paged(const attn_bwd_paged_args *a, int mode, void *out, attn::Page
       {"plan", a->plan, (int64_t)words * 4, work},
       {"dk_pool", a->dk_pool, pslots * D * (int64_t)es, work && kv && (a->need & 1)},
       {"dv_pool", a->dv_pool, pslots * D * (int64_t)es, work && kv && !mla && (a->need & 2)},
-      {kv ? "dkp_pool" : (mode == PM_STATS ? "stats_out" : "dq"), kv ? a->dkp_pool : out,
+      {kv ? "dkp_pool" : (st_out ? "stats_out" : "dq"), kv ? a->dkp_pool : out,
        kv ? pslots * P * (int64_t)es
-          : qrows * (mode == PM_STATS ? 3 * (int64_t)sizeof(float) : D * (int64_t)es),
+          : qrows * (st_out ? 3 * (int64_t)sizeof(float) : D * (int64_t)es),
        work && (kv ? mla && (a->need & 4) : true)},
+      {"dq", out2, qrows * D * (int64_t)es, work && mode == PM_SDQ},
   };
   Range rng[NT];
   for (int i = 0; i < NT; ++i) {
@@ -472,7 +477,8 @@ int validate_paged(const attn_bwd_paged_args *a, int mode, void *out, attn::Page
   float *qws = nullptr;
   if (mode != PM_KV && a->q_workspace && work) {
     const int64_t need = qpieces * a->kv_heads * attn::kQBlockRows *
-                         (mode == PM_STATS ? 4 : D) * (int64_t)sizeof(float);
+                         (mode == PM_STATS ? 4 : mode == PM_SDQ && bf16 ? 2 * D + 8 : D) *
+                         (int64_t)sizeof(float);
     if ((int64_t)a->q_workspace_bytes < need)
       return fail(ATTN_E_WORKSPACE, "q_workspace_bytes %zu < %lld needed", a->q_workspace_bytes,
                   (long long)need);
@@ -503,8 +509,9 @@ int validate_paged(const attn_bwd_paged_args *a, int mode, void *out, attn::Page
     p.dkp_pool = a->dkp_pool;
     p.need_dkp = (a->need >> 2) & 1;
   }
-  if (mode == PM_STATS) p.stats_out = (float *)out;
+  if (mode == PM_STATS || mode == PM_SDQ) p.stats_out = (float *)out;
   if (mode == PM_DQ) p.dq = out;
+  if (mode == PM_SDQ) p.dq = out2;
   p.stats = a->stats;
   p.plan = a->plan;
   p.heads = a->heads;
@@ -544,21 +551,78 @@ hipError_t launch_paged(bool bf16_in, int D, const PagedParams &p, int nblocks, 
                         hipStream_t stream);
 hipError_t launch_paged_q(int stage, bool bf16_in, int D, const PagedParams &p, int nblocks,
                           hipStream_t stream);
+int device_cus();
 }  // namespace attn
 
 namespace {
-int run_paged(const attn_bwd_paged_args *a, int mode, void *out, void *stream) {
+// The fused query pass (bf16) with a workspace: whether the split form's
+// estimated time is below the direct form's, from the host plan, in units of
+// one 64-token chunk step of one workgroup (one workgroup per compute unit).
+// A unit (a query block or a piece of one, per KV head) costs its visible
+// chunks plus kFixed steps (loading its rows and first chunks, storing its
+// results); a form takes at least its longest unit and its total over the
+// compute units; the split form adds one longest piece for the rounds'
+// granularity and the merge's traffic (each piece's partial results written
+// and read once).
+bool sdq_split_is_faster(const int32_t *w, int kv_heads, int causal, int D, int cus) {
+  using namespace attn::plan;
+  constexpr double kFixed = 5.0, kStepBytes = 7.6e6;  // HBM bytes moved per step time
+  const int64_t words = w[W_WORDS], nseq = w[W_NSEQ], nb = w[W_QBLK], np = w[W_QPIECES];
+  const int64_t ob = w[W_OFF_QBLK], otok = w[W_OFF_SEQ_TOK], omax = w[W_OFF_SEQ_MAXPOS];
+  const int64_t opc = w[W_OFF_QPIECE];
+  if (cus <= 0 || nseq < 0 || ob + 2 * nb > words || otok + nseq + 1 > words ||
+      omax + nseq > words || opc + 3 * np > words)
+    return false;
+  auto visible = [&](int64_t b) -> int64_t {  // tokens the block's rows see, -1 for a bad entry
+    if (b < 0 || b >= nb) return -1;
+    const int64_t s = w[ob + 2 * b];
+    if (s < 0 || s >= nseq) return -1;
+    const int64_t len = (int64_t)w[otok + s + 1] - w[otok + s];
+    return causal ? std::min<int64_t>(len, (int64_t)w[omax + s] + 1) : len;
+  };
+  auto chunks = [](int64_t t) { return t > 0 ? (double)((t + 63) / 64) : 0.0; };
+  double dmax = 0, dsum = 0, smax = 0, ssum = 0;
+  for (int64_t b = 0; b < nb; ++b) {
+    const int64_t v = visible(b);
+    if (v < 0) return false;
+    const double c = chunks(v) + kFixed;
+    dmax = std::max(dmax, c);
+    dsum += c;
+  }
+  for (int64_t k = 0; k < np; ++k) {
+    const int64_t v = visible(w[opc + 3 * k]);
+    if (v < 0) return false;
+    const double c = chunks(std::min<int64_t>(w[opc + 3 * k + 2], v) - w[opc + 3 * k + 1]) + kFixed;
+    smax = std::max(smax, c);
+    ssum += c;
+  }
+  const double direct = std::max(dmax, dsum * kv_heads / cus);
+  const double merge = 2.0 * np * kv_heads * attn::kQBlockRows * (2.0 * D + 8) * 4 / kStepBytes;
+  const double split = std::max(smax, ssum * kv_heads / cus) + smax + merge;
+  return split < direct;
+}
+
+int run_paged(const attn_bwd_paged_args *a, int mode, void *out, void *out2, void *stream) {
   attn::PagedParams p;
   int nblocks = 0;
   bool bf16 = false;
-  const int rc = validate_paged(a, mode, out, p, nblocks, bf16);
+  const int rc = validate_paged(a, mode, out, out2, p, nblocks, bf16);
   if (rc != ATTN_OK) return rc;
+  if (mode == PM_SDQ && bf16) {
+    if (a->q_form == 1 && !p.qws)
+      return fail(ATTN_E_WORKSPACE, "q_form 1 (split) needs q_workspace");
+    if (a->q_form == 2 ||
+        (a->q_form == 0 && p.qws &&
+         !sdq_split_is_faster(a->plan_host, a->kv_heads, a->causal, a->head_dim,
+                              attn::device_cus())))
+      p.qws = nullptr;  // the direct form
+  }
   if (nblocks == 0) return ATTN_OK;
   const hipError_t e =
       mode == PM_KV ? attn::launch_paged(bf16, a->head_dim, p, nblocks, a->kv_workgroups,
                                          (hipStream_t)stream)
-                    : attn::launch_paged_q(mode == PM_STATS ? 0 : 1, bf16, a->head_dim, p, nblocks,
-                                           (hipStream_t)stream);
+                    : attn::launch_paged_q(mode == PM_STATS ? 0 : mode == PM_DQ ? 1 : 2, bf16,
+                                           a->head_dim, p, nblocks, (hipStream_t)stream);
   if (e != hipSuccess) return fail(ATTN_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ATTN_OK;
 }
@@ -567,15 +631,19 @@ int run_paged(const attn_bwd_paged_args *a, int mode, void *out, void *stream) {
 extern "C" {
 
 int attn_bwd_paged(const attn_bwd_paged_args *a, void *stream) {
-  return run_paged(a, PM_KV, nullptr, stream);
+  return run_paged(a, PM_KV, nullptr, nullptr, stream);
 }
 
 int attn_bwd_paged_row_stats(const attn_bwd_paged_args *a, float *stats, void *stream) {
-  return run_paged(a, PM_STATS, stats, stream);
+  return run_paged(a, PM_STATS, stats, nullptr, stream);
 }
 
 int attn_bwd_paged_dq(const attn_bwd_paged_args *a, void *dq, void *stream) {
-  return run_paged(a, PM_DQ, dq, stream);
+  return run_paged(a, PM_DQ, dq, nullptr, stream);
+}
+
+int attn_bwd_paged_stats_dq(const attn_bwd_paged_args *a, float *stats, void *dq, void *stream) {
+  return run_paged(a, PM_SDQ, stats, dq, stream);
 }
 
 size_t attn_bwd_paged_q_workspace_bytes(const int32_t *plan_host, int32_t head_dim) {
@@ -586,7 +654,7 @@ size_t attn_bwd_paged_q_workspace_bytes(const int32_t *plan_host, int32_t head_d
     return 0;
   }
   return (size_t)plan_host[W_QPIECES] * (size_t)plan_host[W_KV_HEADS] * attn::kQBlockRows *
-         (size_t)(head_dim > 4 ? head_dim : 4) * sizeof(float);
+         (2 * (size_t)head_dim + 8) * sizeof(float);
 }
 
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq) {

@@ -821,7 +821,7 @@ static hipError_t launch_dtype(int D, const PagedParams &p, int nblocks, hipStre
 }
 
 // Compute units of the current device (0 if unknown), looked up once per device.
-static int device_cus() {
+int device_cus() {
   static std::atomic<int> cus[64];
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;

@@ -28,10 +28,11 @@
 #include "device_common.hpp"
 #include "paged.hpp"
 #include "q_core.hpp"
+#include "sd_core.hpp"
 
 namespace attn {
 
-enum { PQ_STATS = 0, PQ_DQ = 1 };
+enum { PQ_STATS = 0, PQ_DQ = 1, PQ_SDQ = 2 };
 
 constexpr int kPqRi = 4 * 64;  // rowinfo words per buffer: one 64-entry copy per wave
 
@@ -310,8 +311,310 @@ __global__ __launch_bounds__(256) void k_paged_q_merge(const PagedParams p) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Statistics and dQ in one pass (bf16): the fused query-major chunk step of
+// sd_core.hpp (A' = sum P~ (dP - dh) K and B = sum P~ K against the running
+// statistics, four contractions per visible triple) over the sequence's tokens
+// in chunks of 64, gathered through the token -> slot table.  Chunk c + 2's
+// K / V rows are requested under chunk c's phase A, from slot ids that a
+// one-dword-per-lane load brought into this wave's LDS copy a step earlier.
+// Direct form: the statistics and dQ rows are final.  Split form: each piece
+// writes, per row, its partial (mref, mtrue, l, delta', dh) and A', B
+// (log2-domain reference mref, unscaled) to the workspace; the merge combines
+// a block's pieces in token order.  Workspace of a (piece, KV head) unit,
+// planar so that a wave's rows are contiguous: 128 rows x kSdqRec floats of
+// statistics, then 128 rows of A' (D floats each), then 128 rows of B.
+
+constexpr int kSdqRec = 8;  // workspace floats of a row's partial statistics
+
+template <int D> struct PsdState {
+  typedef MT<bf16> M;
+  static constexpr int NSD = D / M::KS, NT = D / 32;
+  typename M::frag qf[NSD], gf[NSD];
+  f32x16 acc_a[NT], acc_b[NT];
+  RowStat st;
+  float dh;
+  int lane, half, wave;
+  int len, hi, c_last;  // hi: the last token the row sees (-1: none)
+  const int32_t *slots;
+  const bf16 *kbase, *vbase;
+  int64_t rs;  // elements between consecutive pool slots
+  ChunkIO<bf16, D, kSdKeys> io;  // (the lane's row and column of each load)
+};
+
+// Slot ids of chunk x's tokens (clamped to the sequence's last token) into
+// this wave's copy in buffer x & 1.
+template <int D>
+__device__ __forceinline__ void psd_rowinfo(PsdState<D> &S, int x, int (*ri)[kPqRi]) {
+  const int t = min(min(x, S.c_last) * kSdKeys + S.lane, S.len - 1);
+  dma_lds4(ri[x & 1] + 64 * S.wave, S.slots + t);
+}
+
+// Load j (K for j < L, V after) of chunk x into the tiles at LDS addresses
+// klds / vlds; sl[j]: the slot of the lane's row of load j.
+template <int D>
+__device__ __forceinline__ void psd_load(const PsdState<D> &S, int j, const int *sl, unsigned klds,
+                                         unsigned vlds) {
+  constexpr int L = ChunkIO<bf16, D, kSdKeys>::LOADS;
+  const int jj = j < L ? j : j - L;
+  int row, col;
+  S.io.slot_rc(jj, row, col);
+  const bf16 *src = (j < L ? S.kbase : S.vbase) + (int64_t)sl[jj] * S.rs + col;
+  dma_lds16_m0((j < L ? klds : vlds) + ((S.wave + 4 * jj) << 10), src);
+}
+
+template <int D>
+__device__ __forceinline__ void psd_slots(const PsdState<D> &S, int x, const int (*ri)[kPqRi],
+                                          int *sl) {
+  constexpr int L = ChunkIO<bf16, D, kSdKeys>::LOADS;
+  const int *mine = ri[x & 1] + 64 * S.wave;
+#pragma unroll
+  for (int j = 0; j < L; ++j) {
+    int row, col;
+    S.io.slot_rc(j, row, col);
+    sl[j] = mine[row];
+  }
+}
+
+// Chunk c (tokens 64 c ..), tiles in buffer bc; chunk c + 2 into the buffer
+// chunk c - 1 used (past c_last the last chunk again), slot ids of chunk c + 3.
+template <int D, bool MASKED>
+__device__ __forceinline__ void psd_step(const PagedParams &p, PsdState<D> &S, int c, int bc,
+                                         Tile<bf16, D, kSdKeys> *Ks, Tile<bf16, D, kSdKeys> *Vs,
+                                         int (*ri)[kPqRi]) {
+  constexpr int L = ChunkIO<bf16, D, kSdKeys>::LOADS;
+  const int bn = bc == 0 ? 2 : bc - 1;
+  psd_rowinfo(S, c + 3, ri);
+  int sl[L];
+  psd_slots(S, c + 2, ri, sl);
+  constexpr unsigned TB = sizeof(Tile<bf16, D, kSdKeys>);
+  const unsigned klds = lds_addr(Ks) + bn * TB, vlds = lds_addr(Vs) + bn * TB;
+  auto dma = [&](int k) { psd_load(S, k, sl, klds, vlds); };
+  const int half = S.half, t0 = c * kSdKeys;
+  auto adj_of = [&](int u, int r) {
+    return t0 + 32 * u + kr(r, half) > S.hi ? -INFINITY : 0.f;
+  };
+  sd_body<bf16, D, MASKED>(S, p.scale_log2, &Ks[bc], &Vs[bc], adj_of, dma);
+}
+
+template <int D, bool SPLIT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_paged_sdq(const PagedParams p) {
+  typedef bf16 T;
+  typedef MT<T> M;
+  constexpr int KS = M::KS, KL = M::KL, NSD = D / KS, NT = D / 32, KC = kSdKeys;
+  __shared__ Tile<T, D, KC> Ks[3], Vs[3];
+  __shared__ __attribute__((aligned(16))) int ri[2][kPqRi];
+
+  PsdState<D> S;
+  S.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  S.lane = threadIdx.x & 63;
+  S.half = S.lane >> 5;
+  const int l32 = S.lane & 31, half = S.half;
+  const int32_t *plan = p.plan;
+  const int L0 = xcd_remap(blockIdx.x, gridDim.x);
+  const int g = L0 % p.kv_heads;
+  int blk = L0 / p.kv_heads, piece = 0, tb0 = 0, te0 = INT32_MAX;
+  if constexpr (SPLIT) {
+    piece = plan[p.off_qpiece_order + blk];
+    blk = plan[p.off_qpiece + 3 * piece];
+    tb0 = plan[p.off_qpiece + 3 * piece + 1];
+    te0 = plan[p.off_qpiece + 3 * piece + 2];
+  }
+  const int seq = plan[p.off_qblk + 2 * blk], qh_begin = plan[p.off_qblk + 2 * blk + 1];
+  const int qs0 = plan[p.off_seq_qh + seq], nqh = plan[p.off_seq_qh + seq + 1] - qs0;
+  const int tb = plan[p.off_seq_tok + seq];
+  S.len = plan[p.off_seq_tok + seq + 1] - tb;
+  S.slots = plan + p.off_tok_slot + tb;
+
+  const int qh = qh_begin + 32 * S.wave + l32;
+  const bool valid = qh < nqh;
+  const int qhc = valid ? qh : 0;
+  const int64_t rh = (int64_t)plan[p.off_qh_rh + qs0 + qhc] + (int64_t)g * p.group;
+  const int pos = plan[p.off_qh_pos + qs0 + qhc];
+  S.hi = !valid ? -1 : p.causal ? min(S.len - 1, pos) : S.len - 1;
+  const T *qrow = (const T *)p.q + rh * D;
+  const T *grow = (const T *)p.dy + rh * D;
+#pragma unroll
+  for (int s = 0; s < NSD; ++s) {
+    S.qf[s] = load_frag<T>(qrow, s * KS + half * KL, valid);
+    S.gf[s] = load_frag<T>(grow, s * KS + half * KL, valid);
+  }
+  sd_init<NT>(S);
+  S.rs = (int64_t)p.kv_heads * D;
+  S.kbase = (const T *)p.k_pool + (int64_t)g * D;
+  S.vbase = (const T *)p.v_pool + (int64_t)g * D;
+  S.io.init(0);
+
+  // Tokens [tb0, tend) in chunks c0 .. c_last; chunks below tfull (seen by
+  // every row of the sequence) take the unmasked step when scale > 0.
+  const int maxpos = plan[p.off_seq_maxpos + seq], minpos = plan[p.off_seq_minpos + seq];
+  const int tend = min(p.causal ? min(S.len, maxpos + 1) : S.len, te0);
+  const int c0 = tb0 / KC;
+  S.c_last = tend > tb0 ? (tend - 1) / KC : c0 - 1;
+  const int tfull = p.causal ? min(S.len, minpos + 1) : S.len;
+  wait_vmem();
+  if (S.c_last >= c0) {
+    int sl[ChunkIO<T, D, KC>::LOADS];
+    constexpr int L2 = 2 * ChunkIO<T, D, KC>::LOADS;
+    constexpr unsigned TB = sizeof(Tile<T, D, KC>);
+    psd_rowinfo(S, c0, ri);
+    psd_rowinfo(S, c0 + 1, ri);
+    wait_vmem();
+    psd_slots(S, c0, ri, sl);
+#pragma unroll
+    for (int k = 0; k < L2; ++k) psd_load(S, k, sl, lds_addr(Ks), lds_addr(Vs));
+    psd_slots(S, c0 + 1, ri, sl);
+#pragma unroll
+    for (int k = 0; k < L2; ++k) psd_load(S, k, sl, lds_addr(Ks) + TB, lds_addr(Vs) + TB);
+    psd_rowinfo(S, c0 + 2, ri);  // into buffer c0 & 1, whose ids were read above
+    wait_vmem();
+    __syncthreads();
+    int cu = min(tfull / KC, S.c_last + 1);  // chunks [c0, cu) unmasked
+    if (!(p.scale_log2 > 0.f)) cu = c0;
+    int c = c0, bc = 0;
+    auto next = [&]() {
+      ++c;
+      bc = bc == 2 ? 0 : bc + 1;
+    };
+    for (; c < cu; next()) psd_step<D, false>(p, S, c, bc, Ks, Vs, ri);
+    for (; c <= S.c_last; next()) psd_step<D, true>(p, S, c, bc, Ks, Vs, ri);
+    wait_vmem();  // the repeated loads of the last steps land before the workgroup ends
+  }
+
+  if constexpr (SPLIT) {
+    // Partial results of rows 32 wave .. 32 wave + 31 of the unit (an invalid
+    // row's are never read).  A' and B go out as whole rows through LDS: the
+    // chunk tiles are free once every wave's repeated loads have landed.
+    float *u = p.qws + ((int64_t)piece * p.kv_heads + g) * kQBlockRows * (kSdqRec + 2 * D);
+    const int r0 = 32 * S.wave;
+    const float l_tot = halves_sum(S.st.l);
+    const float d_tot = halves_sum(S.st.dl);
+    if (half == 0) {
+      float *w = u + (r0 + l32) * kSdqRec;
+      store4<float>(w, S.st.mref, S.st.mtrue, l_tot, d_tot);
+      store4<float>(w + 4, S.dh, 0.f, 0.f, 0.f);
+    }
+    typedef RowStore<float, D> RS;
+    static_assert(2 * RS::BYTES <= sizeof(Ks) && 2 * RS::BYTES <= sizeof(Vs), "staging fits");
+    __syncthreads();
+    char *area = reinterpret_cast<char *>(S.wave < 2 ? (void *)Ks : (void *)Vs) + (S.wave & 1) * RS::BYTES;
+    float *wa = u + kQBlockRows * kSdqRec + (int64_t)r0 * D;
+    float *wb = wa + kQBlockRows * D;
+    RS::write_tiles(S.acc_a, 1.f, area, S.lane);
+    RS::store_rows(area, 32, [&](int n) { return wa + n * D; }, S.lane);
+    RS::write_tiles(S.acc_b, 1.f, area, S.lane);  // LDS operations of a wave complete in order
+    RS::store_rows(area, 32, [&](int n) { return wb + n * D; }, S.lane);
+    return;
+  }
+  if (!valid) return;
+  const RowStatOut o = row_stat_final(S.st, p.inv_scale_log2);
+  if (half == 0) {
+    float *st = p.stats_out + 3 * rh;
+    st[0] = o.m;
+    st[1] = o.l;
+    st[2] = o.delta;
+  }
+  sd_settle<NT>(S, o.delta);
+  T *dqrow = (T *)p.dq + rh * D;
+  const float sc = p.scale * o.inv_l;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      store4<T>(dqrow + 32 * t + 8 * q + 4 * half, sc * S.acc_a[t][4 * q],
+                sc * S.acc_a[t][4 * q + 1], sc * S.acc_a[t][4 * q + 2], sc * S.acc_a[t][4 * q + 3]);
+}
+
+// Merge of the fused split form: one thread per 4 columns of a (block, KV head,
+// row of the block).  Pieces in token order: the common reference M (largest
+// mref), l = sum 2^(mref_p - M) l_p and delta' likewise, delta = delta' / l,
+// dQ = scale / l * sum 2^(mref_p - M) (A'_p + (dh_p - delta) B_p).  The
+// statistics (written by each row's first thread) are (mtrue ln 2,
+// l 2^(M - mtrue), delta), as the direct form's.
+template <int D>
+__global__ __launch_bounds__(256) void k_paged_sdq_merge(const PagedParams p) {
+  typedef bf16 T;
+  constexpr int PER = D / 4, REC = kSdqRec + 2 * D;
+  const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (tid >= (int64_t)p.qblocks * p.kv_heads * kQBlockRows * PER) return;
+  const int dc = (int)(tid % PER);
+  int64_t r = tid / PER;
+  const int j = (int)(r % kQBlockRows);
+  r /= kQBlockRows;
+  const int g = (int)(r % p.kv_heads), b = (int)(r / p.kv_heads);
+  const int32_t *plan = p.plan;
+  const int seq = plan[p.off_qblk + 2 * b], qh = plan[p.off_qblk + 2 * b + 1] + j;
+  const int qs0 = plan[p.off_seq_qh + seq];
+  if (qh >= plan[p.off_seq_qh + seq + 1] - qs0) return;
+  const int64_t rh = (int64_t)plan[p.off_qh_rh + qs0 + qh] + (int64_t)g * p.group;
+  const int p0 = plan[p.off_qblk_piece + b], p1 = plan[p.off_qblk_piece + b + 1];
+  auto unit = [&](int pc) { return p.qws + ((int64_t)pc * p.kv_heads + g) * kQBlockRows * REC; };
+  auto rec = [&](int pc) { return unit(pc) + j * kSdqRec; };
+  float M = -INFINITY, mt = -INFINITY;
+  for (int pc = p0; pc < p1; ++pc) {
+    const f32x4 v = *reinterpret_cast<const f32x4 *>(rec(pc));
+    M = fmaxf(M, v[0]);
+    mt = fmaxf(mt, v[1]);
+  }
+  float l = 0.f, dl = 0.f;
+  if (M != -INFINITY) {
+    for (int pc = p0; pc < p1; ++pc) {
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(rec(pc));
+      const float a = fast_exp2(v[0] - M);  // 0 for a piece that saw nothing
+      l = fmaf(v[2], a, l);
+      dl = fmaf(v[3], a, dl);
+    }
+  }
+  const bool empty = !(l > 0.f);
+  const float delta = empty ? 0.f : dl / l;
+  if (dc == 0) {
+    float *st = p.stats_out + 3 * rh;
+    st[0] = empty ? -INFINITY : mt * kLn2;
+    st[1] = empty ? 0.f : l * fast_exp2(M - mt);
+    st[2] = delta;
+  }
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (!empty) {
+    for (int pc = p0; pc < p1; ++pc) {
+      const float *w = rec(pc);
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(w);
+      if (v[0] == -INFINITY) continue;  // nothing seen in this piece
+      const float a = fast_exp2(v[0] - M), sh = w[4] - delta;
+      const float *ra = unit(pc) + kQBlockRows * kSdqRec + (int64_t)j * D + 4 * dc;
+      const f32x4 A = *reinterpret_cast<const f32x4 *>(ra);
+      const f32x4 B = *reinterpret_cast<const f32x4 *>(ra + kQBlockRows * D);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(a, fmaf(sh, B[e], A[e]), acc[e]);
+    }
+  }
+  const float sc = empty ? 0.f : p.scale / l;
+  store4<T>((T *)p.dq + rh * D + 4 * dc, sc * acc[0], sc * acc[1], sc * acc[2], sc * acc[3]);
+}
+
 template <typename T, int D>
 static hipError_t launch_t(int stage, const PagedParams &p, int nblocks, hipStream_t stream) {
+  if (stage == PQ_SDQ) {
+    if constexpr (sizeof(T) == 2) {
+      if (!p.qws) {
+        hipLaunchKernelGGL((k_paged_sdq<D, false>), dim3(nblocks), dim3(256), 0, stream, p);
+        return hipGetLastError();
+      }
+      const int64_t mthreads = (int64_t)p.qblocks * p.kv_heads * kQBlockRows * (D / 4);
+      hipLaunchKernelGGL((k_paged_sdq<D, true>), dim3(p.qpieces * p.kv_heads), dim3(256), 0,
+                         stream, p);
+      hipLaunchKernelGGL((k_paged_sdq_merge<D>), dim3((int)((mthreads + 255) / 256)), dim3(256), 0,
+                         stream, p);
+      return hipGetLastError();
+    } else {
+      // fp32: the statistics, then dQ from them
+      const hipError_t e = launch_t<T, D>(PQ_STATS, p, nblocks, stream);
+      if (e != hipSuccess) return e;
+      PagedParams p2 = p;
+      p2.stats = p.stats_out;
+      return launch_t<T, D>(PQ_DQ, p2, nblocks, stream);
+    }
+  }
   if (!p.qws) {
     if (stage == PQ_STATS)
       hipLaunchKernelGGL((k_paged_q<T, D, PQ_STATS, false>), dim3(nblocks), dim3(256), 0, stream, p);

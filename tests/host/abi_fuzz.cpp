@@ -99,9 +99,12 @@ hipError_t launch_paged(bool, int D, const PagedParams &p, int nblocks, int work
   return hipSuccess;
 }
 
+int device_cus() { return 256; }
+
 hipError_t launch_paged_q(int stage, bool, int D, const PagedParams &p, int nblocks, hipStream_t) {
   ++n_launch;
-  if (stage != 0 && stage != 1) die("paged query stage");
+  if (stage != 0 && stage != 1 && stage != 2) die("paged query stage");
+  if (stage == 2 && (!p.stats_out || !p.dq)) die("paged fused outputs");
   if (nblocks <= 0 || (int64_t)nblocks != (int64_t)p.qblocks * p.kv_heads) die("paged query grid");
   if (D != 32 && D != 64 && D != 128) die("paged query head_dim");
   if (p.qws && p.qpieces < 0) die("paged query pieces");
@@ -366,6 +369,9 @@ void call_paged(const std::vector<int32_t> &plan, int32_t nq, int32_t heads, int
   a.mla = chance(10) ? 1 : 0;
   check_status(attn_bwd_paged_row_stats(&a, (float *)fake_ptr(), nullptr), "paged_row_stats");
   check_status(attn_bwd_paged_dq(&a, (void *)fake_ptr(), nullptr), "paged_dq");
+  a.q_form = (int32_t)pick({0, 1, 2, 3, -1});
+  check_status(attn_bwd_paged_stats_dq(&a, (float *)fake_ptr(), (void *)fake_ptr(), nullptr),
+               "paged_stats_dq");
 }
 
 void fuzz_paged(long iters) {

@@ -236,7 +236,8 @@ def test_paged_query_workspace_rules():
     lib = sdb.load_library()
     W = plan.words
     need_dq = int(W[_abi.W_QPIECES]) * 2 * 128 * 64 * 4  # pieces * kv_heads * rows * D * 4
-    assert lib.attn_bwd_paged_q_workspace_bytes(W.ctypes.data, 64) == need_dq
+    need_all = int(W[_abi.W_QPIECES]) * 2 * 128 * (2 * 64 + 8) * 4  # the fused call's records
+    assert lib.attn_bwd_paged_q_workspace_bytes(W.ctypes.data, 64) == need_all
     bad = W.copy()
     bad[0] = 7
     assert lib.attn_bwd_paged_q_workspace_bytes(bad.ctypes.data, 64) == 0
@@ -248,6 +249,14 @@ def test_paged_query_workspace_rules():
     a = _paged_args(plan, q_workspace=(1 << 24) * 1, q_workspace_bytes=need_dq)  # over q
     assert lib.attn_bwd_paged_dq(ctypes.byref(a), out, None) == _abi.ATTN_E_INVALID
     assert "q_workspace overlaps" in lib.attn_bwd_last_error().decode()
+    # the fused call (bf16) keeps 2 D + 8 floats per row and piece
+    st = ctypes.c_void_p((1 << 24) * 13)
+    a = _paged_args(plan, q_workspace=(1 << 24) * 12, q_workspace_bytes=need_all - 4)
+    assert lib.attn_bwd_paged_stats_dq(ctypes.byref(a), st, out, None) == _abi.ATTN_E_WORKSPACE
+    assert str(need_all) in lib.attn_bwd_last_error().decode()
+    a = _paged_args(plan, q_workspace=(1 << 24) * 13, q_workspace_bytes=need_all)  # over stats
+    assert lib.attn_bwd_paged_stats_dq(ctypes.byref(a), st, out, None) == _abi.ATTN_E_INVALID
+    assert "q_workspace overlaps" in lib.attn_bwd_last_error().decode()
 
 
 def test_paged_query_side_rejects_latent_variant():
@@ -257,6 +266,8 @@ def test_paged_query_side_rejects_latent_variant():
     for fn in (lib.attn_bwd_paged_row_stats, lib.attn_bwd_paged_dq):
         assert fn(ctypes.byref(a), ctypes.c_void_p(1 << 30), None) == _abi.ATTN_E_UNSUPPORTED
         assert "latent" in lib.attn_bwd_last_error().decode()
+    assert lib.attn_bwd_paged_stats_dq(ctypes.byref(a), ctypes.c_void_p(1 << 30),
+                                       ctypes.c_void_p(3 << 29), None) == _abi.ATTN_E_UNSUPPORTED
 
 
 def test_paged_rejects_foreign_plan():
@@ -302,6 +313,24 @@ def test_paged_query_side_rejections():
     assert "stats_out is NULL" in lib.attn_bwd_last_error().decode()
     assert lib.attn_bwd_paged_dq(ctypes.byref(a), ctypes.c_void_p(1 << 30), None) == _abi.ATTN_E_INVALID
     assert "stats is NULL" in lib.attn_bwd_last_error().decode()
+    # the fused call: two outputs, neither NULL, disjoint from each other and the inputs
+    fused = lib.attn_bwd_paged_stats_dq
+    st, dq = ctypes.c_void_p(1 << 30), ctypes.c_void_p(3 << 29)
+    assert fused(ctypes.byref(a), None, dq, None) == _abi.ATTN_E_INVALID
+    assert "stats_out is NULL" in lib.attn_bwd_last_error().decode()
+    assert fused(ctypes.byref(a), st, None, None) == _abi.ATTN_E_INVALID
+    assert "dq is NULL" in lib.attn_bwd_last_error().decode()
+    assert fused(ctypes.byref(a), st, st, None) == _abi.ATTN_E_INVALID
+    assert "overlaps" in lib.attn_bwd_last_error().decode()
+    assert fused(ctypes.byref(a), st, ctypes.c_void_p(a.dy), None) == _abi.ATTN_E_INVALID
+    assert "overlaps" in lib.attn_bwd_last_error().decode()
+    for bad in (3, -1):
+        a.q_form = bad
+        assert fused(ctypes.byref(a), st, dq, None) == _abi.ATTN_E_INVALID
+        assert "q_form" in lib.attn_bwd_last_error().decode()
+    a.q_form = 1  # the split form without a workspace
+    assert fused(ctypes.byref(a), st, dq, None) == _abi.ATTN_E_WORKSPACE
+    assert "q_workspace" in lib.attn_bwd_last_error().decode()
 
 
 def test_from_forward_rejections():

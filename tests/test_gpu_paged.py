@@ -299,7 +299,21 @@ def run_query_side(w, *, causal=True, label="", split=True):
     assert not np.isnan(g).any()
     e = rel_err(g, dq_ref)
     assert e <= tol, f"{label} dq: rel err {e:.3e} > {tol:g}"
-    return dict(plan=plan, stats=st_gpu, dq=dq_gpu, stats_err=errs, dq_err=e, st32=st32)
+    # Both in one call (attn_bwd_paged_stats_dq), against the same oracle values.
+    st_f, dq_f = sb.paged_stats_dq(q, dy, kp, vp, plan, causal=causal,
+                                   form="split" if split else "direct")
+    torch.cuda.synchronize()
+    errs_f = _stats_err(st_f.cpu().double().numpy(), st_ref)
+    for name, ef in zip(("max", "denominator", "delta"), errs_f):
+        assert ef <= tol, f"{label} fused stats {name}: rel err {ef:.3e} > {tol:g}"
+    gf = dq_f.double().cpu().numpy()
+    assert not np.isnan(gf).any()
+    empty = st_ref[..., 1] == 0
+    assert (gf[empty] == 0).all(), f"{label} fused dq: a row that sees nothing is not zero"
+    e_f = rel_err(gf, dq_ref)
+    assert e_f <= tol, f"{label} fused dq: rel err {e_f:.3e} > {tol:g}"
+    return dict(plan=plan, stats=st_gpu, dq=dq_gpu, stats_err=errs, dq_err=e, st32=st32,
+                fused_stats=st_f, fused_dq=dq_f, fused_stats_err=errs_f, fused_dq_err=e_f)
 
 
 # Sequences longer than a 1024-token piece, so the split form merges several
@@ -311,7 +325,7 @@ LONG_CASES = [
     dict(seed=110, nseq=2, len_lo=2100, len_hi=3300, q_per_seq=36, page_size=32, heads=4,
          kv_heads=1, D=128, dtype=torch.float32),
 ]
-Q_CASES = [CASES[0], CASES[1], CASES[3], CASES[4], CASES[5]] + LONG_CASES
+Q_CASES = [CASES[0], CASES[1], CASES[2], CASES[3], CASES[4], CASES[5]] + LONG_CASES
 
 
 def _middle_rows(w):
@@ -333,16 +347,39 @@ def test_paged_query_side_parity(case, causal, split):
 
 
 def test_paged_query_split_rerun_bitwise():
-    """The split form's merge runs in a fixed piece order: reruns are bit-identical."""
+    """The split form's merge runs in a fixed piece order: reruns are bit-identical
+    (the separate calls and the fused one)."""
     w = sdpa_inputs.paged_workload(**LONG_CASES[0])
     out = run_query_side(w, label="rerun")
     dev = torch.device("cuda:0")
     q, dy, kp, vp = (w[n].to(dev) for n in ("q", "dy", "k_pool", "v_pool"))
     st2 = sb.paged_row_stats(q, dy, kp, vp, out["plan"])
     dq2 = sb.attn_bwd_paged_dq(q, dy, kp, vp, out["st32"], out["plan"])
+    st3, dq3 = sb.paged_stats_dq(q, dy, kp, vp, out["plan"], form="split")
     torch.cuda.synchronize()
     assert torch.equal(st2.view(torch.int32), out["stats"].view(torch.int32))
     assert torch.equal(dq2.view(torch.int16), out["dq"].view(torch.int16))
+    assert torch.equal(st3.view(torch.int32), out["fused_stats"].view(torch.int32))
+    assert torch.equal(dq3.view(torch.int16), out["fused_dq"].view(torch.int16))
+
+
+@pytest.mark.parametrize("split", [True, False], ids=["split", "direct"])
+def test_paged_query_side_edges(split):
+    """A sequence of length 0 that has query rows (statistics (-inf, 0, 0), zero
+    dQ rows), rows at positions past their sequence's end (they see all of it),
+    a single-token sequence, bf16 and fp32."""
+    for dtype, D in ((torch.bfloat16, 64), (torch.float32, 32)):
+        w = sdpa_inputs.paged_workload(seed=114, nseq=4, len_lo=70, len_hi=260, q_per_seq=10,
+                                       page_size=16, heads=4, kv_heads=2, D=D, dtype=dtype)
+        lens = w["seq_lens"].clone()
+        lens[1] = 0
+        lens[3] = 1
+        w["seq_lens"] = lens
+        qp = w["query_pos"].clone()
+        qp[w["query_seq"] == 2] += 50
+        w["query_pos"] = qp
+        for causal in (True, False):
+            run_query_side(w, causal=causal, label=f"edges {dtype} causal={causal}", split=split)
 
 
 def test_paged_config5_gpu_chain():
@@ -350,6 +387,18 @@ def test_paged_config5_gpu_chain():
     GPU dQ, against the oracle run end to end in float64."""
     w = sdpa_inputs.paged_workload(seed=1005)
     out = run_query_side(w, label="config5")
-    print(f"[paged-q] config5 stats err {out['stats_err']} dq err {out['dq_err']:.3e}", flush=True)
+    print(f"[paged-q] config5 stats err {out['stats_err']} dq err {out['dq_err']:.3e} fused "
+          f"{out['fused_stats_err']} {out['fused_dq_err']:.3e}", flush=True)
+    # the fused call's library-picked form gives the bits of one of the two forms
+    dev = torch.device("cuda:0")
+    q, dy, kp, vp = (w[n].to(dev) for n in ("q", "dy", "k_pool", "v_pool"))
+    st_d, dq_d = sb.paged_stats_dq(q, dy, kp, vp, out["plan"], form="direct")
+    st_a, dq_a = sb.paged_stats_dq(q, dy, kp, vp, out["plan"], form="auto")
+    torch.cuda.synchronize()
+    same = [torch.equal(st_a.view(torch.int32), x.view(torch.int32)) and
+            torch.equal(dq_a.view(torch.int16), y.view(torch.int16))
+            for x, y in ((st_d, dq_d), (out["fused_stats"], out["fused_dq"]))]
+    assert any(same), "the picked form matches neither form bitwise"
+    print(f"[paged-q] config5 fused form picked: {'direct' if same[0] else 'split'}", flush=True)
     kv = run_case(w, gpu_stats=out["stats"], label="config5 gpu-stats")
     print(f"[paged-q] config5 chain dk {kv['dk_err']:.3e} dv {kv['dv_err']:.3e}", flush=True)
