@@ -38,7 +38,10 @@ Prints one JSON line.  Besides the contract fields it carries
   window256    the same tensors under the sliding window w = 256 (the parity
                workload of this shape), counted over its visible pairs;
   paged        the paged grouped-query history backward (below), its dK / dV
-               call against the HBM roofline and its query side.
+               call against the HBM roofline and its query side;
+  fp32_configs the fp32 dense workloads (configs 1, 2 and 4 with key padding
+               or bias under the causal rule) through attn_bwd, against the
+               fp32 MFMA peak.
 
 --workload paged measures the paged grouped-query history backward alone
 (ruDNN `history_backward`): bf16, 32 query / 8 KV heads, D 128, page 16, 16
@@ -89,6 +92,7 @@ KERNEL_SOURCES = ["scaled_dot_product_bwd_amd/csrc/dense_kernels.hip",
                   "scaled_dot_product_bwd_amd/csrc/device_common.hpp",
                   "scaled_dot_product_bwd_amd/csrc/kv_core.hpp",
                   "scaled_dot_product_bwd_amd/csrc/q_core.hpp",
+                  "scaled_dot_product_bwd_amd/csrc/sd_core.hpp",
                   "scaled_dot_product_bwd_amd/build.py"]
 PAGED_SOURCES = ["scaled_dot_product_bwd_amd/csrc/paged_kernels.hip",
                  "scaled_dot_product_bwd_amd/csrc/paged.hpp",
@@ -706,7 +710,61 @@ def main():
         line["paged"] = {k_: pm[k_] for k_ in ("ms_per_step", "value", "unit", "per_step",
                                                "pct_mfma_peak", "roofline", "query_side_ms",
                                                "full_chain_ms", "full_chain_tflops", "config")}
+        log("bench: fp32 dense workloads")
+        line["fp32_configs"] = fp32_config_records(args, torch, sdb, dev)
     print(json.dumps(line), flush=True)
+
+
+def fp32_config_records(args, torch, sdb, dev):
+    """The fp32 dense workloads (configs 1, 2 and 4: the parity cases of the
+    fp32 kernels k_row_stats, k_kv_bwd, k_dq_bwd), each timed through attn_bwd
+    over >= 100 calls (per-call median): TFLOP/s counted over the pairs the
+    index rule keeps (10 D flops each; key padding and bias hide or weight
+    pairs inside that set, which the kernels compute like any other), against
+    the fp32 MFMA peak.  Builder-side figures beside the bf16 headline."""
+    import ctypes
+    lib = sdb.load_library()
+    recs = {}
+    cases = [(1, "none", False), (2, "causal", False), (4, "keypad", True), (4, "bias", True)]
+    for k, kind, causal in cases:
+        d = sdpa_inputs_mod().dense_config_inputs(k)
+        q, kk, v, dy = (d[n].to(dev) for n in ("q", "k", "v", "dy"))
+        B, Sq, H, D = q.shape
+        Sk = kk.shape[1]
+        mask = None
+        if kind == "keypad":
+            mask = d["valid"].reshape(B, 1, 1, Sk).to(dev)
+        elif kind == "bias":
+            mask = d["bias"].to(dev)
+        dq, dk, dv = (torch.empty_like(x) for x in (q, kk, v))
+        ws = torch.empty(sdb.workspace_bytes(B, H, Sq), dtype=torch.uint8, device=dev)
+        a = sdb.make_args(q, kk, v, dy, dq, dk, dv, mask_kind=kind, causal=causal, mask=mask,
+                          workspace=ws)
+        handle = sdb._stream_handle(None)
+
+        def step():
+            rc = lib.attn_bwd(ctypes.byref(a), handle)
+            if rc != 0:
+                raise RuntimeError(lib.attn_bwd_last_error().decode())
+        for _ in range(max(args.warmup, 5)):
+            step()
+        per = dist(time_calls(step, max(100, args.steps), torch))
+        pairs = visible_pairs(Sq, Sk, "causal", 0) if (kind == "causal" or causal) else Sq * Sk
+        flops = 10.0 * D * B * H * pairs
+        tf = flops / (per["median_ms"] / 1e3) / 1e12
+        name = f"config{k}" + ("" if k != 4 else f"_{kind}_causal")
+        recs[name] = {"workload": f"B{B} H{H} Sq{Sq} Sk{Sk} D{D} fp32 {kind}"
+                                  + (" + causal" if causal else ""),
+                      "per_step": per, "counted_flops": flops, "tflops": round(tf, 3),
+                      "pct_fp32_mfma_peak": round(100.0 * tf / PEAK_TFLOPS["f32"], 3)}
+        del q, kk, v, dy, dq, dk, dv, ws, mask
+    torch.cuda.empty_cache()
+    return recs
+
+
+def sdpa_inputs_mod():
+    import sdpa_inputs
+    return sdpa_inputs
 
 
 def dense_measure(args, torch, sdb, dev, tensors, mask, window, full):
