@@ -221,7 +221,8 @@ typedef struct attn_bwd_paged_args {
    *   dk_pool[slot, g]  (the latent's gradient) += ds * q + p * dY,
    *   dkp_pool[slot, g] += ds * qp.
    * need: bit 0 the latent's gradient, bit 2 the position keys' (bit 1 is
-   * invalid).  head_dim in {64, 128}, position_dim in {0, 32, 64}.  The query
+   * invalid).  head_dim in {64, 128} (bf16 also 192 or 256, streamed in 32-row
+   * chunks), position_dim in {0, 32, 64}.  The query
    * side (row statistics, dQ) does not take the latent variant.  mla = 0: the
    * fields below are ignored. */
   int32_t mla, position_dim;

@@ -488,10 +488,10 @@ def attn_bwd_paged_mla(q, qp, dy, latent_pool, kp_pool, stats, plan, *, dlat_poo
     """Latent (MLA) variant of attn_bwd_paged: each slot's latent row is both its
     key and its value, and a position key adds qp . kp to the score.
     q, dy: [nq, heads, D]; qp: [nq, heads, P]; latent_pool: [slots, kv_heads, D];
-    kp_pool: [slots, kv_heads, P] (D in {64, 128}, P in {0, 32, 64}).  Writes the
-    latent's gradient (ds q + p dY, summed) into dlat_pool and the position
-    keys' (ds qp) into dkp_pool at the slots of listed pages; pools that are not
-    given are allocated zero-filled.  The default scale is 1/sqrt(D + P).
+    kp_pool: [slots, kv_heads, P] (D in {64, 128}, for bf16 also {192, 256};
+    P in {0, 32, 64}).  Writes the latent's gradient (ds q + p dY, summed) into
+    dlat_pool and the position keys' (ds qp) into dkp_pool at the slots of
+    listed pages; pools that are not given are allocated zero-filled.  The default scale is 1/sqrt(D + P).
     need: "dlat", "dkp" or "both".  Returns (dlat_pool, dkp_pool)."""
     torch = _torch()
     n = {"dlat": 1, "dkp": 4, "both": 5}[need] if isinstance(need, str) else int(need)

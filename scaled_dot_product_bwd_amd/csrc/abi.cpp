@@ -388,8 +388,10 @@ int validate_paged(const attn_bwd_paged_args *a, int mode, void *out, void *out2
   if (mode == PM_KV && mla && (a->need < 1 || a->need > 5 || (a->need & 2)))
     return fail(ATTN_E_INVALID, "latent variant: need %d is not 1, 4 or 5", a->need);
   if (mla) {
-    if (a->head_dim != 64 && a->head_dim != 128)
-      return fail(ATTN_E_UNSUPPORTED, "latent width %d is not 64 or 128", a->head_dim);
+    const bool wide = a->dtype == ATTN_BF16 && (a->head_dim == 192 || a->head_dim == 256);
+    if (a->head_dim != 64 && a->head_dim != 128 && !wide)
+      return fail(ATTN_E_UNSUPPORTED,
+                  "latent width %d is not 64 or 128 (or, for bf16, 192 or 256)", a->head_dim);
     if (a->position_dim != 0 && a->position_dim != 32 && a->position_dim != 64)
       return fail(ATTN_E_UNSUPPORTED, "position_dim %d is not 0, 32 or 64", a->position_dim);
     if ((a->need & 4) && a->position_dim == 0)

@@ -77,19 +77,20 @@ struct NoDma {
   __device__ __forceinline__ void operator()(int) const {}
 };
 
+// NSUB: 32-row sub-tiles per chunk (KvShape's by default; a wide latent key
+// takes one, so that three chunk buffers still fit in LDS).
 template <typename T, int DK, int DV, bool MASKED, bool MERGE, int NDMA = 0,
-          typename Adj, typename Dma = NoDma, bool NEGV = false>
+          typename Adj, typename Dma = NoDma, bool NEGV = false, int NSUB = KvShape<T>::NSUB>
 __device__ __forceinline__ void kv_chunk(const typename MT<T>::frag *kf,
                                          const typename MT<T>::frag *vf, f32x16 *dk, f32x16 *dv,
-                                         const Tile<T, DK, KvShape<T>::ROWS> *Qc,
-                                         const Tile<T, DV, KvShape<T>::ROWS> *Gc,
+                                         const Tile<T, DK, 32 * NSUB> *Qc,
+                                         const Tile<T, DV, 32 * NSUB> *Gc,
                                          const float *nls, const float *dst, float scale_log2,
                                          int lane, Adj adj, float ds_scale = 1.f, Dma dma = Dma()) {
   typedef MT<T> M;
   typedef typename M::frag F;
   static_assert(DV <= DK && DV % 32 == 0 && DK % 32 == 0, "widths");
   constexpr int NSD = DK / M::KS, NSV = DV / M::KS, NT = DK / 32, NTV = DV / 32, CS = M::CSTEPS;
-  constexpr int NSUB = KvShape<T>::NSUB;
   constexpr int NA = NSUB * NSD;    // phase-A steps (S, and dP while s < NSV)
   constexpr int NC = NSUB * CS * NT;  // phase-C steps (dK, and dV while t < NTV)
   constexpr int RING = 3;

@@ -47,13 +47,14 @@ constexpr int kStatWords = 4 * kStatWave;
 constexpr int kRiWords = 4 * 64;
 
 // D: value / latent width; P: position-key width (latent variant only, else 0).
+// A latent wider than 128 takes 32-row chunks (its Q / dY tiles are wide).
 template <typename T_, int D_, int P_, bool MLA_> struct PagedState {
   typedef T_ T;
   typedef MT<T> M;
   static constexpr int D = D_, P = P_, DK = D_ + P_;
   static constexpr bool MLA = MLA_;
   static constexpr int NSD = DK / M::KS, NSV = D / M::KS, NT = DK / 32, NTV = D / 32;
-  static constexpr int ROWS = KvShape<T>::ROWS;
+  static constexpr int ROWS = (MLA && D > 128) ? 32 : KvShape<T>::ROWS;
   typedef Tile<T, DK, ROWS> QTile;  // Q rows (latent variant: [q | qp])
   typedef Tile<T, D, ROWS> GTile;   // dY rows
   typename M::frag kf[NSD], vf[MLA ? 1 : NSV];
@@ -191,8 +192,9 @@ __device__ __forceinline__ void consume_chunk(const PagedParams &p, St &S, int c
     const bool vis = (tok >= 0) & (!causal | (tok <= pos));
     return vis ? 0.f : -INFINITY;
   };
-  kv_chunk<T, St::DK, St::D, MASKED, St::MLA>(S.kf, St::MLA ? S.kf : S.vf, S.dk, S.dv, Q, G, myst,
-                                              myst + 128, p.scale_log2, S.lane, adj, p.scale);
+  kv_chunk<T, St::DK, St::D, MASKED, St::MLA, 0, decltype(adj), NoDma, false, St::ROWS / 32>(
+      S.kf, St::MLA ? S.kf : S.vf, S.dk, S.dv, Q, G, myst, myst + 128, p.scale_log2, S.lane, adj,
+      p.scale);
 }
 
 // One chunk: request rowinfo of chunk c + 4 and the data of chunk c + 2,
@@ -810,13 +812,22 @@ static hipError_t launch_dtype(int D, const PagedParams &p, int nblocks, hipStre
     if (D == 128) return launch_t<T, 128, 0, false>(p, nblocks, stream);
     return hipErrorInvalidValue;
   }
-  // latent variant: latent width 64 or 128, position-key width 0, 32 or 64
+  // latent variant: latent width 64 or 128 (bf16 also 192, 256), position-key
+  // width 0, 32 or 64
   if (D == 64 && p.P == 0) return launch_t<T, 64, 0, true>(p, nblocks, stream);
   if (D == 64 && p.P == 32) return launch_t<T, 64, 32, true>(p, nblocks, stream);
   if (D == 64 && p.P == 64) return launch_t<T, 64, 64, true>(p, nblocks, stream);
   if (D == 128 && p.P == 0) return launch_t<T, 128, 0, true>(p, nblocks, stream);
   if (D == 128 && p.P == 32) return launch_t<T, 128, 32, true>(p, nblocks, stream);
   if (D == 128 && p.P == 64) return launch_t<T, 128, 64, true>(p, nblocks, stream);
+  if constexpr (sizeof(T) == 2) {  // wider latents: bf16 (32-row chunks)
+    if (D == 192 && p.P == 0) return launch_t<T, 192, 0, true>(p, nblocks, stream);
+    if (D == 192 && p.P == 32) return launch_t<T, 192, 32, true>(p, nblocks, stream);
+    if (D == 192 && p.P == 64) return launch_t<T, 192, 64, true>(p, nblocks, stream);
+    if (D == 256 && p.P == 0) return launch_t<T, 256, 0, true>(p, nblocks, stream);
+    if (D == 256 && p.P == 32) return launch_t<T, 256, 32, true>(p, nblocks, stream);
+    if (D == 256 && p.P == 64) return launch_t<T, 256, 64, true>(p, nblocks, stream);
+  }
   return hipErrorInvalidValue;
 }
 

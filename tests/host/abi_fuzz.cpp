@@ -88,12 +88,14 @@ hipError_t launch_dense_stage(int stage, bool, int D, int mode, const DenseParam
   return hipSuccess;
 }
 
-hipError_t launch_paged(bool, int D, const PagedParams &p, int nblocks, int workgroups,
+hipError_t launch_paged(bool bf16, int D, const PagedParams &p, int nblocks, int workgroups,
                         hipStream_t) {
   ++n_launch;
   if (workgroups < -1) die("paged kv_workgroups below -1 reached the launcher");
   if (nblocks <= 0 || (int64_t)nblocks != (int64_t)p.items * p.kv_heads) die("paged grid");
-  if (p.mla ? (D != 64 && D != 128) : (D != 32 && D != 64 && D != 128)) die("paged head_dim");
+  if (p.mla ? (D != 64 && D != 128 && !(bf16 && (D == 192 || D == 256)))
+            : (D != 32 && D != 64 && D != 128))
+    die("paged head_dim");
   if (p.group < 1 || p.group * p.kv_heads != p.heads) die("paged group");
   if (!p.plan) die("paged plan pointer");
   return hipSuccess;
@@ -337,7 +339,7 @@ void call_paged(const std::vector<int32_t> &plan, int32_t nq, int32_t heads, int
   a.need = (int32_t)pick({1, 2, 3, 3, 0, 4, 5});
   a.heads = chance(90) ? heads : heads + 1;
   a.kv_heads = kv_heads;
-  a.head_dim = (int32_t)pick({32, 64, 128, 128, 96});
+  a.head_dim = (int32_t)pick({32, 64, 128, 128, 96, 192, 256});
   a.page_size = page_size;
   a.causal = (int32_t)pick({0, 1, 1, 2});
   a.kv_workgroups = (int32_t)(chance(90) ? pick({0, 0, 8, 256, -1}) : pick({-2, INT32_MIN}));

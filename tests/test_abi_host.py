@@ -215,6 +215,9 @@ _MLA = dict(mla=1, need=5, position_dim=32, v_pool=0, dv_pool=0, qp=(1 << 24) * 
     (dict(_MLA, need=3), _abi.ATTN_E_INVALID, "need"),
     (dict(_MLA, need=8), _abi.ATTN_E_INVALID, "need"),
     (dict(_MLA, head_dim=32), _abi.ATTN_E_UNSUPPORTED, "latent width"),
+    (dict(_MLA, head_dim=320), _abi.ATTN_E_UNSUPPORTED, "latent width"),
+    (dict(_MLA, head_dim=192, dtype=0), _abi.ATTN_E_UNSUPPORTED, "latent width"),  # fp32: 64 / 128
+    (dict(_MLA, head_dim=256, dtype=0), _abi.ATTN_E_UNSUPPORTED, "latent width"),
     (dict(_MLA, position_dim=16), _abi.ATTN_E_UNSUPPORTED, "position_dim"),
     (dict(_MLA, position_dim=0), _abi.ATTN_E_INVALID, "position_dim is 0"),
     (dict(_MLA, qp=0), _abi.ATTN_E_INVALID, "qp is NULL"),

@@ -138,8 +138,30 @@ def test_mla_parity(case, causal):
     run_mla(sdpa_inputs.paged_workload(**case), causal=causal, label=f"seed{case['seed']}")
 
 
+# Latents wider than 128 (bf16; 32-row chunks): rows of several chunks, shared
+# prefixes, pages larger or smaller than an item, GQA.
+WIDE_CASES = [
+    dict(seed=310, nseq=3, len_lo=40, len_hi=300, q_per_seq=24, page_size=16, heads=8,
+         kv_heads=1, D=256, position_dim=64, dtype=torch.bfloat16, share_prefix_pages=2,
+         shuffle_rows=True),
+    dict(seed=311, nseq=2, len_lo=60, len_hi=200, q_per_seq=13, page_size=48, heads=4,
+         kv_heads=2, D=192, position_dim=32, dtype=torch.bfloat16),
+    dict(seed=312, nseq=2, len_lo=10, len_hi=90, q_per_seq=7, page_size=1, heads=4,
+         kv_heads=1, D=256, position_dim=32, dtype=torch.bfloat16),
+    dict(seed=313, nseq=2, len_lo=100, len_hi=300, q_per_seq=40, page_size=256, heads=8,
+         kv_heads=2, D=192, position_dim=64, dtype=torch.bfloat16, shuffle_rows=True),
+]
+
+
+@pytest.mark.parametrize("case", WIDE_CASES, ids=lambda c: f"seed{c['seed']}")
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "full"])
+def test_mla_wide_latent_parity(case, causal):
+    run_mla(sdpa_inputs.paged_workload(**case), causal=causal, label=f"seed{case['seed']}")
+
+
 @pytest.mark.parametrize("D,dtype", [(64, torch.bfloat16), (128, torch.float32),
-                                     (128, torch.bfloat16)])
+                                     (128, torch.bfloat16), (192, torch.bfloat16),
+                                     (256, torch.bfloat16)])
 def test_mla_without_position_keys(D, dtype):
     """P = 0: the latent alone is key and value."""
     w = sdpa_inputs.paged_workload(seed=307, nseq=2, len_lo=50, len_hi=160, q_per_seq=30,
@@ -185,6 +207,23 @@ def test_mla_full_size_sampled_and_rerun_bitwise():
     its sequence); a second GPU call must be bit-identical."""
     w = sdpa_inputs.paged_workload(seed=1005, heads=16, kv_heads=1, D=128, position_dim=64)
     out = run_mla(w, label="full", compare_seqs=[3, 11])
+    dev = torch.device("cuda:0")
+    q, qp, dy, lat, kpp = (w[n].to(dev) for n in ("q", "qp", "dy", "k_pool", "kp_pool"))
+    dl = _sentinel_pool(w["k_pool"]).to(dev)
+    dp = _sentinel_pool(w["kp_pool"]).to(dev)
+    sb.attn_bwd_paged_mla(q, qp, dy, lat, kpp, out["st32"], out["plan"], dlat_pool=dl,
+                          dkp_pool=dp, scale=_scale(w))
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(dl.cpu()), _bits(out["dlat"]))
+    assert np.array_equal(_bits(dp.cpu()), _bits(out["dkp"]))
+
+
+def test_mla_wide_full_size_sampled_and_rerun_bitwise():
+    """The paged workload's shape with 16 query heads on one latent KV head of
+    width 256 + 64 (bf16): two sampled sequences against the oracle, and a
+    second GPU call bit-identical."""
+    w = sdpa_inputs.paged_workload(seed=1005, heads=16, kv_heads=1, D=256, position_dim=64)
+    out = run_mla(w, label="full wide", compare_seqs=[5, 12])
     dev = torch.device("cuda:0")
     q, qp, dy, lat, kpp = (w[n].to(dev) for n in ("q", "qp", "dy", "k_pool", "kp_pool"))
     dl = _sentinel_pool(w["k_pool"]).to(dev)
