@@ -57,9 +57,9 @@ dK / dV) counted like the dense metric (10 D flops per visible triple).
 
 --workload paged_mla measures the latent variant of the same kernel on the same
 page tables (16 query heads on one latent KV head of width 128 plus a position
-key of width 64): TFLOP/s over the visible triples (4 (D + P) + 4 D flops each)
-against the MFMA peak, since at 16 query heads per latent row the kernel sits
-far above the HBM ridge.
+key of width 64; --latent-dim picks another latent width): TFLOP/s over the
+visible triples (4 (D + P) + 4 D flops each) against the MFMA peak, since at
+16 query heads per latent row the kernel sits far above the HBM ridge.
 
 --no-extras keeps only the headline measurement (for profiler runs, whose
 per-kernel averages then cover the headline's launches alone).
@@ -537,7 +537,8 @@ def main_paged_mla(args, torch, sdb, dev):
     import numpy as np
     import sdpa_inputs
     log("bench: generating the latent paged workload")
-    w = sdpa_inputs.paged_workload(seed=1005, heads=16, kv_heads=1, D=128, position_dim=64)
+    w = sdpa_inputs.paged_workload(seed=1005, heads=16, kv_heads=1, D=args.latent_dim,
+                                   position_dim=64)
     D, P = w["D"], w["P"]
     scale = float(torch.tensor(1.0 / (D + P) ** 0.5, dtype=torch.float32))
     plan = sdb.paged_plan(w["seq_lens"], w["block_table"], w["query_seq"], w["query_pos"],
@@ -633,6 +634,8 @@ def main():
                     help="only the headline measurement (no scrubbed, from_forward, window or "
                          "paged parts): for profiler runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--latent-dim", type=int, default=128, choices=[64, 128, 192, 256],
+                    help="latent width of --workload paged_mla")
     ap.add_argument("--preheat", type=float, default=0.1,
                     help="seconds of untimed steps before the warmup steps (clock ramp)")
     ap.add_argument("--copy-calibration", action="store_true",
