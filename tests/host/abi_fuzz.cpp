@@ -45,7 +45,7 @@ int64_t pick(std::initializer_list<int64_t> v) {
 bool chance(int percent) { return (int)(rng() % 100) < percent; }
 int64_t small(int64_t hi) { return (int64_t)(rng() % (uint64_t)(hi + 1)); }
 
-// a * b, saturated to int64 range (the driver itself must stay free of overflow).
+// a * b, saturated to int64 range (the fuzzer itself must stay free of overflow).
 int64_t smul(int64_t a, int64_t b) {
   __int128 r = (__int128)a * b;
   if (r > INT64_MAX) return INT64_MAX;
