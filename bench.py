@@ -740,7 +740,9 @@ def fp32_config_records(args, torch, sdb, dev):
         elif kind == "bias":
             mask = d["bias"].to(dev)
         dq, dk, dv = (torch.empty_like(x) for x in (q, kk, v))
-        ws = torch.empty(sdb.workspace_bytes(B, H, Sq), dtype=torch.uint8, device=dev)
+        # a workspace that allows the split form of the query-major passes
+        # (the library uses it where the blocks would leave the GPU idle)
+        ws = torch.empty(sdb.split_workspace_bytes(B, H, Sq, Sk, D), dtype=torch.uint8, device=dev)
         a = sdb.make_args(q, kk, v, dy, dq, dk, dv, mask_kind=kind, causal=causal, mask=mask,
                           workspace=ws)
         handle = sdb._stream_handle(None)

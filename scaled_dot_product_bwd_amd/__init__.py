@@ -31,7 +31,8 @@ from ._abi import (ATTN_BF16, ATTN_F32, ATTN_MASK_BIAS, ATTN_MASK_CAUSAL,
                    ATTN_WRT_ALL, ATTN_WRT_K, ATTN_WRT_Q, ATTN_WRT_V, AttnBwdArgs,
                    AttnBwdPagedArgs, AttnError, load_library, library_path)
 
-__all__ = ["attn_bwd", "attn_bwd_noalloc", "attn_bwd_stage", "workspace_bytes", "make_args", "AttnError",
+__all__ = ["attn_bwd", "attn_bwd_noalloc", "attn_bwd_stage", "workspace_bytes",
+           "split_workspace_bytes", "make_args", "AttnError",
            "load_library", "library_path", "MASKS", "WRT", "PagedPlan", "paged_plan",
            "attn_bwd_paged", "attn_bwd_paged_mla", "make_paged_args", "paged_row_stats",
            "paged_q_workspace",
@@ -49,6 +50,12 @@ def _torch():
 
 def workspace_bytes(B: int, H: int, Sq: int) -> int:
     return int(load_library().attn_bwd_workspace_bytes(B, H, Sq))
+
+
+def split_workspace_bytes(B: int, H: int, Sq: int, Sk: int, D: int) -> int:
+    """The workspace size that also enables the split form of the
+    query-major passes (attn_bwd_split_workspace_bytes)."""
+    return int(load_library().attn_bwd_split_workspace_bytes(B, H, Sq, Sk, D))
 
 
 def _strides3(t):
@@ -304,6 +311,14 @@ def attn_bwd(q, k, v, dy, *, wrt="all", mask_kind="none", causal=False, window=0
         dq, dk, dv = out
     if workspace is None:
         nbytes = workspace_bytes(B, H, Sq)
+        if q.dtype == torch.float32 and fwd_lse is None:
+            # the split form of the fp32 query-major passes pays when the
+            # (query block, head) workgroups fill at most half of the GPU (the
+            # library decides; a larger workspace only makes it possible)
+            blocks = B * H * ((Sq + 127) // 128)
+            cus = torch.cuda.get_device_properties(q.device).multi_processor_count
+            if 2 * blocks <= cus:
+                nbytes = max(nbytes, split_workspace_bytes(B, H, Sq, k.shape[1], D))
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
     args = make_args(q, k, v, dy, dq, dk, dv, wrt=w, mask_kind=mask_kind, causal=causal,
                      window=window, mask=mask, threshold=threshold, scale=scale,

@@ -25,7 +25,8 @@ EXPORTED = ["attn_bwd_workspace_bytes", "attn_bwd", "attn_bwd_row_stats", "attn_
             "attn_bwd_dq", "attn_bwd_stats_dq", "attn_bwd_paged_plan_words", "attn_bwd_paged_plan_build",
             "attn_bwd_paged", "attn_bwd_paged_row_stats", "attn_bwd_paged_dq",
             "attn_bwd_from_forward", "attn_bwd_paged_q_workspace_bytes",
-            "attn_bwd_last_error", "attn_bwd_noalloc", "attn_bwd_paged_stats_dq"]
+            "attn_bwd_last_error", "attn_bwd_noalloc", "attn_bwd_paged_stats_dq",
+            "attn_bwd_split_workspace_bytes"]
 
 # Plan header words (scaled_dot_product_bwd_amd/csrc/paged.hpp).
 PLAN_MAGIC = 0x32504241
@@ -108,6 +109,8 @@ def load_library():
     lib = ctypes.CDLL(path)
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_bwd_workspace_bytes.argtypes = [ctypes.c_int64] * 3
+    lib.attn_bwd_split_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_bwd_split_workspace_bytes.argtypes = [ctypes.c_int64] * 5
     for name in ("attn_bwd", "attn_bwd_row_stats", "attn_bwd_kv", "attn_bwd_dq",
                  "attn_bwd_stats_dq", "attn_bwd_noalloc"):
         fn = getattr(lib, name)

@@ -96,7 +96,35 @@ struct Checked {
   int mode;
   bool want_q, want_k, want_v;
   int nblk_q, nblk_k;
+  float *ws_split;  // the split form's region of the workspace, or nullptr
+  int split_max;    // pieces that region holds per row
 };
+}  // namespace
+
+namespace attn {
+int device_cus();
+}
+
+namespace {
+// Split form of the query-major row-statistics and dQ passes.  When the
+// (query block, head) workgroups would leave most compute units idle (a few
+// long rows of keys: few queries or heads), each block's keys are cut into
+// pieces of whole 32-key chunks, at least kSplitMinChunks each and at most
+// kSplitMaxPieces of them, and a merge combines the pieces' partial results.
+constexpr int64_t kSplitMinChunks = 4, kSplitMaxPieces = 16;
+
+int64_t split_max_pieces(int64_t Sk) {
+  const int64_t chunks = Sk / 32 + (Sk % 32 != 0);  // no overflow for any Sk >= 0
+  return std::min<int64_t>(kSplitMaxPieces, chunks / kSplitMinChunks);
+}
+
+// Pieces to use for a stage with `blocks` (query block, head) workgroups, or
+// 0 for the one-workgroup-per-block form: only when at most half of the
+// compute units would be busy.
+int split_pieces(int64_t blocks, int64_t Sk, int max_pieces, int cus) {
+  if (max_pieces < 2 || cus <= 0 || blocks <= 0 || 2 * blocks > cus) return 0;
+  return (int)std::min<int64_t>(max_pieces, std::max<int64_t>(2, cus / blocks));
+}
 
 int validate(const attn_bwd_args *a, Checked &c) {
   if (!a) return fail(ATTN_E_INVALID, "args is NULL");
@@ -203,6 +231,8 @@ int validate(const attn_bwd_args *a, Checked &c) {
 
   const size_t ws_need = attn_bwd_workspace_bytes(a->B, a->H, a->Sq);
   Range wrng;
+  c.ws_split = nullptr;
+  c.split_max = 0;
   if (ws_need) {
     if (!a->workspace) return fail(ATTN_E_WORKSPACE, "workspace is NULL (%zu bytes needed)", ws_need);
     if ((uintptr_t)a->workspace % 256)
@@ -211,6 +241,13 @@ int validate(const attn_bwd_args *a, Checked &c) {
       return fail(ATTN_E_WORKSPACE, "workspace has %zu bytes, %zu needed", a->workspace_bytes, ws_need);
     wrng.lo = (uintptr_t)a->workspace;
     wrng.hi = wrng.lo + ws_need;
+    // a workspace of attn_bwd_split_workspace_bytes() enables the split form
+    const size_t split_need = attn_bwd_split_workspace_bytes(a->B, a->H, a->Sq, a->Sk, a->D);
+    if (split_need > ws_need && a->workspace_bytes >= split_need) {
+      c.ws_split = (float *)((char *)a->workspace + ws_need);
+      c.split_max = (int)split_max_pieces(a->Sk);
+      wrng.hi = wrng.lo + split_need;
+    }
   }
 
   // No output may share memory with an input, another output or the workspace.
@@ -292,6 +329,17 @@ int run_stage(int stage, Checked &c, hipStream_t stream) {
     if (!c.want_q) p.dq = nullptr;
     p.nblk = c.nblk_q;
     nblocks = heads * c.nblk_q;
+  }
+  // Split form: row statistics and dQ only, and not with a forward's
+  // statistics (the dQ pass then also publishes them).
+  if (c.ws_split && p.fo == nullptr && (stage == attn::STAGE_ROW_STATS || stage == attn::STAGE_DQ)) {
+    const int np = split_pieces(nblocks, p.Sk, c.split_max, attn::device_cus());
+    if (np >= 2) {
+      const int chunks = (p.Sk + 31) / 32;
+      p.piece_chunks = (chunks + np - 1) / np;
+      p.npiece = (chunks + p.piece_chunks - 1) / p.piece_chunks;  // no empty tail piece
+      p.ws_split = c.ws_split;
+    }
   }
   const hipError_t e = attn::launch_dense_stage(stage, c.bf16, c.D, c.mode, p, nblocks, stream);
   if (e != hipSuccess)
@@ -663,6 +711,17 @@ size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq) {
   if (B < 0 || H < 0 || Sq < 0) return 0;
   if (stat_bytes(B, H, Sq) < 0) return SIZE_MAX;  // never satisfiable
   return 4 * plane_bytes(B, H, Sq);
+}
+
+size_t attn_bwd_split_workspace_bytes(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D) {
+  if (B < 0 || H < 0 || Sq < 0 || Sk < 0 || D <= 0 || D > 4096) return 0;
+  const size_t base = attn_bwd_workspace_bytes(B, H, Sq);
+  const int64_t np = split_max_pieces(Sk), rec = D > 4 ? D : 4;
+  int64_t n;
+  if (base == SIZE_MAX || np < 2 || __builtin_mul_overflow(stat_bytes(B, H, Sq), np * rec, &n) ||
+      n > kMaxBytes)
+    return base;
+  return base + (size_t)n;
 }
 
 }  // extern "C"

@@ -214,7 +214,18 @@ __device__ __forceinline__ void q_prologue(const DenseParams &p, ChunkIO<T, D> &
 // latency than a third buffer would.
 constexpr int kRsBuf = 2;
 
-template <typename T, int D, int MODE>
+// Key-axis piece of a split-form workgroup (piece 0 of the whole range
+// otherwise): its chunks [lo, hi] inside the block's visible chunks [c0, c1].
+struct QPiece {
+  int piece, lo, hi;
+};
+template <bool SPLIT>
+__device__ __forceinline__ QPiece q_piece(const DenseParams &p, int piece, int c0, int c1) {
+  if constexpr (!SPLIT) return QPiece{0, c0, c1};
+  return QPiece{piece, max(c0, piece * p.piece_chunks), min(c1, piece * p.piece_chunks + p.piece_chunks - 1)};
+}
+
+template <typename T, int D, int MODE, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_row_stats(const DenseParams p) {
   typedef MT<T> M;
   constexpr int KS = M::KS, KL = M::KL, NSD = D / KS, NQB = QShape<T>::NQB,
@@ -228,7 +239,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   const int l32 = S.lane & 31, half = S.half;
   const int nb = p.nblk;
   int bh, rank;
-  tile_order<kRsGroup>(blockIdx.x, gridDim.x, nb, bh, rank);
+  // split form: consecutive workgroups are the pieces of one (block, head)
+  const int np = SPLIT ? p.npiece : 1;
+  tile_order<kRsGroup>(blockIdx.x / np, gridDim.x / np, nb, bh, rank);
   const int blk = nb - 1 - rank;  // the heaviest causal blocks first
   S.h = bh % p.H;
   S.b = bh / p.H;
@@ -252,23 +265,66 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   S.kbase = (const T *)p.k + b * p.ks[0] + (h / p.G) * p.ks[2];  // the head's K / V head
   S.vbase = (const T *)p.v + b * p.vs[0] + (h / p.G) * p.vs[2];
   const QRange R = q_range(p, i0, QROWS, MODE == MODE_INDEX);
-  S.c_last = R.c_last;
+  const QPiece Pc = q_piece<SPLIT>(p, (int)(blockIdx.x % np), R.c_first, R.c_last);
+  S.c_last = Pc.hi;
   S.io_k.init(p.ks[1]);
   S.io_v.init(p.vs[1]);
-  q_prologue<T, D, kRsBuf>(p, S.io_k, S.io_v, S.kbase, S.vbase, R.c_first, R.c_last, Ks, Vs);
+  q_prologue<T, D, kRsBuf>(p, S.io_k, S.io_v, S.kbase, S.vbase, Pc.lo, Pc.hi, Ks, Vs);
   S.buf = 0;
   // Buffers rotate at run time here: unrolled by two (compile-time offsets)
   // the kernel spills at three waves per SIMD.
-  for (int c = R.c_first; c <= R.c_last; ++c)
+  for (int c = Pc.lo; c <= Pc.hi; ++c)
     rs_step<T, D, MODE, kRsBuf>(p, S, c, Ks, Vs, c < R.cu0 || c > R.cu1);
   wait_vmem();  // the repeated loads of the last step land before the workgroup ends
 
 #pragma unroll
   for (int q = 0; q < NQB; ++q) {
-    const RowStatOut o = row_stat_final(S.st[q], p.inv_scale_log2);
     const int qi = S.qi[q];
-    if (qi < p.Sq && half == 0) store_row_stat(p, ((int64_t)b * p.H + h) * p.Sq + qi, o);
+    const int64_t row = ((int64_t)b * p.H + h) * p.Sq + qi;
+    if constexpr (SPLIT) {
+      // this piece's (mref, true max, l, delta') of the row, log2 domain
+      const float l_tot = halves_sum(S.st[q].l);
+      const float d_tot = halves_sum(S.st[q].dl);
+      if (qi < p.Sq && half == 0)
+        store4<float>(p.ws_split + 4 * ((int64_t)Pc.piece * p.B * p.H * p.Sq + row), S.st[q].mref,
+                      S.st[q].mtrue, l_tot, d_tot);
+    } else {
+      const RowStatOut o = row_stat_final(S.st[q], p.inv_scale_log2);
+      if (qi < p.Sq && half == 0) store_row_stat(p, row, o);
+    }
   }
+}
+
+// Merge of the split row statistics: one thread per row, the pieces in order
+// rescaled to their common reference M (the largest mref): l = sum 2^(mref_k
+// - M) l_k and delta' likewise; then the statistics as row_stat_final forms
+// them with M as the reference.
+__global__ __launch_bounds__(256) void k_rs_merge(const DenseParams p) {
+  const int64_t rows = (int64_t)p.B * p.H * p.Sq;
+  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (row >= rows) return;
+  float M = -INFINITY, mt = -INFINITY;
+  for (int k = 0; k < p.npiece; ++k) {
+    const f32x4 v = *reinterpret_cast<const f32x4 *>(p.ws_split + 4 * (k * rows + row));
+    M = fmaxf(M, v[0]);
+    mt = fmaxf(mt, v[1]);
+  }
+  float l = 0.f, dl = 0.f;
+  if (M != -INFINITY) {
+    for (int k = 0; k < p.npiece; ++k) {
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(p.ws_split + 4 * (k * rows + row));
+      const float a = fast_exp2(v[0] - M);  // 0 for a piece that saw nothing
+      l = fmaf(v[2], a, l);
+      dl = fmaf(v[3], a, dl);
+    }
+  }
+  RowStatOut o;
+  o.empty = !(l > 0.f);
+  o.m = o.empty ? -INFINITY : mt * kLn2;
+  o.l = o.empty ? 0.f : l * fast_exp2(M - mt);
+  o.delta = o.empty ? 0.f : dl / l;
+  o.nls = (o.empty ? -INFINITY : -(M + __log2f(l))) * p.inv_scale_log2;
+  store_row_stat(p, row, o);
 }
 
 // ---------------------------------------------------------------------------
@@ -631,7 +687,7 @@ __device__ __forceinline__ void dq_step(const DenseParams &p, DqState<T, D> &S, 
   end_step<ChunkIO<T, D>::DIRECT, 2 * ChunkIO<T, D>::LOADS>(SPREAD || issued);
 }
 
-template <typename T, int D, int MODE>
+template <typename T, int D, int MODE, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_dq_bwd(const DenseParams p) {
   typedef MT<T> M;
   constexpr int KS = M::KS, KL = M::KL, NSD = D / KS, NT = D / 32, NQB = QShape<T>::NQB,
@@ -645,7 +701,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int l32 = S.lane & 31, half = S.half;
   const int nb = p.nblk;
   int bh, rank;
-  tile_order<kDqGroup>(blockIdx.x, gridDim.x, nb, bh, rank);
+  // split form (never with a forward's statistics): consecutive workgroups are
+  // the pieces of one (block, head)
+  const int np = SPLIT ? p.npiece : 1;
+  tile_order<kDqGroup>(blockIdx.x / np, gridDim.x / np, nb, bh, rank);
   const int blk = nb - 1 - rank;
   S.h = bh % p.H;
   S.b = bh / p.H;
@@ -699,21 +758,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   S.kbase = (const T *)p.k + b * p.ks[0] + (h / p.G) * p.ks[2];  // the head's K / V head
   S.vbase = (const T *)p.v + b * p.vs[0] + (h / p.G) * p.vs[2];
   const QRange R = q_range(p, i0, QROWS, MODE == MODE_INDEX);
-  S.c_last = R.c_last;
+  const QPiece Pc = q_piece<SPLIT>(p, (int)(blockIdx.x % np), R.c_first, R.c_last);
+  S.c_last = Pc.hi;
   S.io_k.init(p.ks[1]);
   S.io_v.init(p.vs[1]);
-  q_prologue<T, D>(p, S.io_k, S.io_v, S.kbase, S.vbase, R.c_first, R.c_last, Ks, Vs);
+  q_prologue<T, D>(p, S.io_k, S.io_v, S.kbase, S.vbase, Pc.lo, Pc.hi, Ks, Vs);
   auto masked = [&](int c) { return c < R.cu0 || c > R.cu1; };
-  int c = R.c_first;
-  for (; c + 2 <= R.c_last; c += 3) {  // unrolled by three: compile-time LDS offsets
+  int c = Pc.lo;
+  for (; c + 2 <= Pc.hi; c += 3) {  // unrolled by three: compile-time LDS offsets
     dq_step<T, D, MODE, 0>(p, S, c, Ks, Vs, masked(c));
     dq_step<T, D, MODE, 1>(p, S, c + 1, Ks, Vs, masked(c + 1));
     dq_step<T, D, MODE, 2>(p, S, c + 2, Ks, Vs, masked(c + 2));
   }
-  if (c <= R.c_last) dq_step<T, D, MODE, 0>(p, S, c, Ks, Vs, masked(c));
-  if (c + 1 <= R.c_last) dq_step<T, D, MODE, 1>(p, S, c + 1, Ks, Vs, masked(c + 1));
+  if (c <= Pc.hi) dq_step<T, D, MODE, 0>(p, S, c, Ks, Vs, masked(c));
+  if (c + 1 <= Pc.hi) dq_step<T, D, MODE, 1>(p, S, c + 1, Ks, Vs, masked(c + 1));
   wait_vmem();  // the repeated loads of the last steps land before the workgroup ends
 
+  if constexpr (SPLIT) {
+    // this piece's unscaled partial dQ rows (fp32), merged by k_dq_merge
+#pragma unroll
+    for (int q = 0; q < NQB; ++q) {
+      const int qi = S.qi[q];
+      if (qi >= p.Sq) continue;
+      float *wrow = p.ws_split + ((int64_t)Pc.piece * p.B * p.H * p.Sq +
+                                  ((int64_t)b * p.H + h) * p.Sq + qi) * D;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          store4<float>(wrow + 32 * t + 8 * g + 4 * half, S.dq[q][t][4 * g], S.dq[q][t][4 * g + 1],
+                        S.dq[q][t][4 * g + 2], S.dq[q][t][4 * g + 3]);
+    }
+    return;
+  }
   const float sc = p.scale;  // the factor of dS, applied once
   typedef RowStore<T, D> RS;
   if constexpr (NQB == 1 && 4 * RS::BYTES <= sizeof(Ks)) {
@@ -885,17 +962,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                  S.lane);
 }
 
+// Merge of the split dQ: one thread per 4 columns of a row, the pieces' partial
+// sums added in piece order, times `scale`, one store.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_dq_merge(const DenseParams p) {
+  const int64_t rows = (int64_t)p.B * p.H * p.Sq;
+  const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (tid >= rows * (D / 4)) return;
+  const int dc = (int)(tid % (D / 4));
+  const int64_t row = tid / (D / 4);
+  const int i = (int)(row % p.Sq);
+  const int64_t bh = row / p.Sq;
+  const int h = (int)(bh % p.H), b = (int)(bh / p.H);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < p.npiece; ++k)
+    acc += *reinterpret_cast<const f32x4 *>(p.ws_split + (k * rows + row) * D + 4 * dc);
+  const float sc = p.scale;
+  T *dst = (T *)p.dq + b * p.dqs[0] + (int64_t)i * p.dqs[1] + h * p.dqs[2] + 4 * dc;
+  store4<T>(dst, sc * acc[0], sc * acc[1], sc * acc[2], sc * acc[3]);
+}
+
 // ---------------------------------------------------------------------------
 // Launchers: one instantiation per (element type, head dim, mask mode).
 
+// Split form (p.ws_split set; row statistics and dQ only): nblocks * npiece
+// workgroups, then the merge over the B * H * Sq rows.
 template <typename T, int D, int MODE>
 static hipError_t launch_t(int stage, const DenseParams &p, int nblocks, hipStream_t stream) {
-  if (stage == STAGE_ROW_STATS)
-    hipLaunchKernelGGL((k_row_stats<T, D, MODE>), dim3(nblocks), dim3(256), 0, stream, p);
+  const bool split = p.ws_split != nullptr && (stage == STAGE_ROW_STATS || stage == STAGE_DQ);
+  const int64_t rows = (int64_t)p.B * p.H * p.Sq;
+  if (split && stage == STAGE_ROW_STATS) {
+    hipLaunchKernelGGL((k_row_stats<T, D, MODE, true>), dim3(nblocks * p.npiece), dim3(256), 0,
+                       stream, p);
+    hipLaunchKernelGGL(k_rs_merge, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, p);
+  } else if (split) {
+    hipLaunchKernelGGL((k_dq_bwd<T, D, MODE, true>), dim3(nblocks * p.npiece), dim3(256), 0,
+                       stream, p);
+    hipLaunchKernelGGL((k_dq_merge<T, D>), dim3((unsigned)((rows * (D / 4) + 255) / 256)),
+                       dim3(256), 0, stream, p);
+  } else if (stage == STAGE_ROW_STATS)
+    hipLaunchKernelGGL((k_row_stats<T, D, MODE, false>), dim3(nblocks), dim3(256), 0, stream, p);
   else if (stage == STAGE_KV)
     hipLaunchKernelGGL((k_kv_bwd<T, D, MODE>), dim3(nblocks), dim3(256), 0, stream, p);
   else if (stage == STAGE_DQ)
-    hipLaunchKernelGGL((k_dq_bwd<T, D, MODE>), dim3(nblocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((k_dq_bwd<T, D, MODE, false>), dim3(nblocks), dim3(256), 0, stream, p);
   else if constexpr (sizeof(T) == 2)
     hipLaunchKernelGGL((k_stats_dq<T, D, MODE>), dim3(nblocks), dim3(256), 0, stream, p);
   else

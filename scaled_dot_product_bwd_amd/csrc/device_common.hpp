@@ -69,6 +69,13 @@ struct DenseParams {
   const void *fo;
   const float *flse;
   int64_t fos[3];
+  // Split form of the row-statistics and dQ passes (ws_split != nullptr): the
+  // key axis in pieces of piece_chunks 32-key chunks, npiece of them, one
+  // workgroup per (query block, head, piece) writing partial results to
+  // ws_split ([npiece][B * H * Sq] records of 4 floats, or of D for dQ), which
+  // a merge kernel combines in piece order.
+  float *ws_split;
+  int npiece, piece_chunks;
 };
 
 __device__ __forceinline__ int kr(int r, int half) { return 8 * (r >> 2) + 4 * half + (r & 3); }

@@ -32,9 +32,17 @@ def rel_err(gpu, ref, zero_ref_scale=1.0) -> float:
 
 
 def gpu_run(q, k, v, dy, *, wrt="all", mask_kind="none", causal=False, window=0, mask=None,
-            threshold=0.5, scale=None, prefill_nan=True):
-    """Inputs are CPU tensors; returns CPU float64 numpy results and the stats."""
+            threshold=0.5, scale=None, prefill_nan=True, workspace=None):
+    """Inputs are CPU tensors; returns CPU float64 numpy results and the stats.
+    workspace: None (the binding's choice), "min" (attn_bwd_workspace_bytes:
+    never the split form) or "split" (attn_bwd_split_workspace_bytes)."""
     dev = torch.device("cuda:0")
+    ws_in = None
+    if workspace is not None:
+        B_, Sq_, H_, D_ = q.shape
+        n = (sdb.workspace_bytes(B_, H_, Sq_) if workspace == "min"
+             else sdb.split_workspace_bytes(B_, H_, Sq_, k.shape[1], D_))
+        ws_in = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
     qd, kd, vd, gd = (x.to(dev) for x in (q, k, v, dy))
     md = mask.to(dev) if mask is not None else None
     outs = []
@@ -48,7 +56,7 @@ def gpu_run(q, k, v, dy, *, wrt="all", mask_kind="none", causal=False, window=0,
             outs.append(None)
     (dq, dk, dv), ws = sdb.attn_bwd(qd, kd, vd, gd, wrt=wrt, mask_kind=mask_kind, causal=causal,
                                     window=window, mask=md, threshold=threshold, scale=scale,
-                                    out=tuple(outs), return_workspace=True)
+                                    out=tuple(outs), return_workspace=True, workspace=ws_in)
     torch.cuda.synchronize()
     B, Sq, H, _ = q.shape
     m, l, d = sdb.row_stats_views(ws, B, H, Sq)

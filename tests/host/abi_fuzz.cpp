@@ -85,6 +85,15 @@ hipError_t launch_dense_stage(int stage, bool, int D, int mode, const DenseParam
   if ((int64_t)nblocks != heads * p.nblk) die("dense grid size");
   if (!p.st_m || !p.st_l || !p.st_delta || !p.st_nls) die("dense workspace planes");
   if ((mode != MODE_INDEX) != (p.mask != nullptr)) die("dense mask pointer");
+  if (p.ws_split) {  // split form: row statistics / dQ, pieces covering the keys
+    if (stage != STAGE_ROW_STATS && stage != STAGE_DQ) die("split form on another stage");
+    if (p.fo) die("split form with a forward's statistics");
+    if (p.npiece < 2 || p.npiece > 16 || p.piece_chunks < 4) die("split pieces");
+    const int64_t chunks = (p.Sk + 31) / 32;
+    if ((int64_t)p.npiece * p.piece_chunks < chunks || (int64_t)(p.npiece - 1) * p.piece_chunks >= chunks)
+      die("split pieces do not tile the keys");
+    if ((char *)p.ws_split < (char *)p.st_nls) die("split region below the planes");
+  }
   return hipSuccess;
 }
 
@@ -101,7 +110,7 @@ hipError_t launch_paged(bool bf16, int D, const PagedParams &p, int nblocks, int
   return hipSuccess;
 }
 
-int device_cus() { return 256; }
+int device_cus() { return 256; }  // the split decisions see a 256-CU device
 
 hipError_t launch_paged_q(int stage, bool, int D, const PagedParams &p, int nblocks, hipStream_t) {
   ++n_launch;
@@ -237,7 +246,8 @@ void fuzz_dense(long iters) {
     static const float odd_scales[] = {0.f,       1e-30f,       -0.25f,          INFINITY,
                                        -INFINITY, std::nanf(""), 5.42101086e-20f, 3e38f};
     a.scale = chance(85) ? 0.125f : odd_scales[rng() % 8];
-    const size_t need = attn_bwd_workspace_bytes(a.B, a.H, a.Sq);
+    const size_t need = chance(50) ? attn_bwd_workspace_bytes(a.B, a.H, a.Sq)
+                                   : attn_bwd_split_workspace_bytes(a.B, a.H, a.Sq, a.Sk, a.D);
     a.workspace = (void *)fake_ptr();
     a.workspace_bytes = chance(80) ? need : (size_t)pick({0, 1, (int64_t)need - 1, INT64_MAX});
 

@@ -65,6 +65,77 @@ def test_config4_fp32_padding_and_bias(case):
     _rerun_bitwise(res, q, k, v, dy, mask_kind=kind, causal=causal, mask=mask)
 
 
+# The split form of the fp32 query-major passes (key pieces merged in order),
+# which a workspace of attn_bwd_split_workspace_bytes enables where the
+# (query block, head) workgroups would leave most of the GPU idle, against the
+# one-workgroup-per-block form and the oracle: configs 2 and 4, and a ragged
+# case (Sq not a multiple of the block, Sk not of the chunk, causal pieces that
+# see nothing).  Grouped-query shapes take the split form in test_gpu_gqa.py.
+SPLIT_CASES = {
+    "config2_causal": dict(cfg=2, kind="causal", causal=False),
+    "config4_keypad_causal": dict(cfg=4, kind="keypad", causal=True),
+    "config4_bias": dict(cfg=4, kind="bias", causal=False),
+    "ragged_causal": dict(cfg=None, kind="causal", causal=False),
+}
+
+
+def _split_inputs(c):
+    if c["cfg"] is None:
+        q, k, v, dy, _ = sdpa_inputs.dense_inputs(1, 200, 1000, 4, 32, seed=77)
+        return q, k, v, dy, None
+    d, q, k, v, dy = _cfg_inputs(c["cfg"])
+    B, Sk = q.shape[0], k.shape[1]
+    mask = None
+    if c["kind"] == "keypad":
+        mask = d["valid"].reshape(B, 1, 1, Sk)
+    elif c["kind"] == "bias":
+        mask = d["bias"]
+    return q, k, v, dy, mask
+
+
+@pytest.mark.parametrize("case", list(SPLIT_CASES))
+def test_fp32_split_form_against_oracle_and_direct_form(case):
+    c = SPLIT_CASES[case]
+    q, k, v, dy, mask = _split_inputs(c)
+    kw = dict(mask_kind=c["kind"], causal=c["causal"], mask=mask)
+    split = gpu_run(q, k, v, dy, workspace="split", **kw)
+    direct = gpu_run(q, k, v, dy, workspace="min", **kw)
+    ref = oracle_run(q, k, v, dy, **kw)
+    print(case, "split", assert_parity(split, ref, torch.float32, label=case + " split"))
+    print(case, "direct", assert_parity(direct, ref, torch.float32, label=case + " direct"))
+    _rerun_bitwise(split, q, k, v, dy, workspace="split", **kw)
+    # dK / dV read the statistics: the two forms' statistics agree to rounding,
+    # so everything stays within the fp32 tolerance of each other too
+    for n in ("dq", "dk", "dv"):
+        e = rel_err(split[n], direct[n])
+        assert e <= TOL[torch.float32], f"{case} {n}: split vs direct {e:.3e}"
+
+
+def test_split_form_through_the_stage_calls():
+    """attn_bwd_row_stats and attn_bwd_dq (bf16 and fp32) with a split-sized
+    workspace, against the oracle's statistics and dQ."""
+    import scaled_dot_product_bwd_amd as sdb
+    dev = torch.device("cuda:0")
+    for dtype in (torch.float32, torch.bfloat16):
+        q, k, v, dy, _ = sdpa_inputs.dense_inputs(2, 128, 2048, 2, 64, seed=78, dtype=dtype)
+        ref = oracle_run(q, k, v, dy, mask_kind="causal")
+        qd, kd, vd, gd = (x.to(dev) for x in (q, k, v, dy))
+        dq = torch.full_like(qd, float("nan"))
+        ws = torch.empty(sdb.split_workspace_bytes(2, 2, 128, 2048, 64), dtype=torch.uint8, device=dev)
+        a = sdb.make_args(qd, kd, vd, gd, dq, None, None, wrt="q", mask_kind="causal", workspace=ws)
+        sdb.attn_bwd_stage("row_stats", a)
+        sdb.attn_bwd_stage("dq", a)
+        torch.cuda.synchronize()
+        m, l, d = (x.cpu().double().numpy() for x in sdb.row_stats_views(ws, 2, 2, 128))
+        res = {"dq": dq.float().cpu().double().numpy(), "m": m, "l": l, "delta": d, "dv": None}
+        tol = TOL[dtype]
+        e = rel_err(res["dq"], ref["dq"])
+        assert e <= tol, f"{dtype} stage dq: {e:.3e}"
+        for n, t in (("m", 1e-5), ("l", 1e-4), ("delta", tol)):
+            e = rel_err(res[n], ref[n])
+            assert e <= t, f"{dtype} stage {n}: {e:.3e}"
+
+
 def _full_size_all_heads(mask_kind, window):
     """The full bf16 [4, 2048, 16, 128] workload: every element of dQ, dK, dV and
     of the statistics against the oracle over all 64 (batch, head) heads, the
