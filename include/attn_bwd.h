@@ -110,19 +110,20 @@ typedef struct attn_bwd_args {
  * exceed 2^60 bytes (sizes attn_bwd rejects). */
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq);
 
-/* A larger workspace that also holds the split form of the query-major
- * row-statistics and dQ passes (fp32 attn_bwd, and attn_bwd_row_stats /
- * attn_bwd_dq for either type; not with a forward's statistics): the four
- * planes above, then partial results of up to 16 key pieces per row (max(D, 4)
- * fp32 each).  With workspace_bytes >= this size the library cuts each query
- * block's keys into pieces of whole 32-key chunks (at least four each) when
- * the (query block, head) workgroups would leave most compute units idle (few
- * queries or heads against many keys), and merges the pieces' results in piece
- * order: the same sums in another order, so the outputs equal the
- * one-workgroup-per-block form's up to rounding, and reruns with the same
- * workspace size on the same device are bit-identical.  Returns
- * attn_bwd_workspace_bytes() where no split is possible (fewer than 256 keys),
- * 0 for negative sizes or D outside (0, 4096]. */
+/* A larger workspace that also holds the split form of the row-statistics,
+ * dQ and dK / dV passes (every pass but the fused bf16 statistics + dQ one,
+ * and not the dQ pass that forms a forward's statistics): the four planes
+ * above, then partial results of up to 16 pieces per row (max(D, 4) fp32 per
+ * query row for the query-major passes, 2 D per key row for dK / dV).  With
+ * workspace_bytes >= this size the library cuts a pass's streamed axis (keys
+ * for the query-major passes, queries for dK / dV) into pieces of whole chunks
+ * (at least four each) when its workgroups would leave most compute units
+ * idle (few queries against many keys, or the reverse), and merges the
+ * pieces' results in piece order: the same sums in another order, so the
+ * outputs equal the one-workgroup-per-block form's up to rounding, and reruns
+ * with the same workspace size on the same device are bit-identical.  Returns
+ * attn_bwd_workspace_bytes() where no split is possible (fewer than 256 keys
+ * and queries), 0 for negative sizes or D outside (0, 4096]. */
 size_t attn_bwd_split_workspace_bytes(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D);
 
 /* The whole dense backward, as `wrt` asks.  bf16: one query-major pass

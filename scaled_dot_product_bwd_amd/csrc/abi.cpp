@@ -97,7 +97,6 @@ struct Checked {
   bool want_q, want_k, want_v;
   int nblk_q, nblk_k;
   float *ws_split;  // the split form's region of the workspace, or nullptr
-  int split_max;    // pieces that region holds per row
 };
 }  // namespace
 
@@ -106,22 +105,25 @@ int device_cus();
 }
 
 namespace {
-// Split form of the query-major row-statistics and dQ passes.  When the
-// (query block, head) workgroups would leave most compute units idle (a few
-// long rows of keys: few queries or heads), each block's keys are cut into
-// pieces of whole 32-key chunks, at least kSplitMinChunks each and at most
-// kSplitMaxPieces of them, and a merge combines the pieces' partial results.
+// Split form of the row-statistics, dQ and dK / dV passes.  When a pass's
+// workgroups (one per query block and head, or per key block and K / V head)
+// would leave most compute units idle (few long rows: few queries against
+// many keys, or the reverse), each block's streamed axis is cut into pieces
+// of whole chunks (32 keys; 32 or 64 query rows for dK / dV), at least
+// kSplitMinChunks each and at most kSplitMaxPieces of them, and a merge
+// combines the pieces' partial results in piece order.
 constexpr int64_t kSplitMinChunks = 4, kSplitMaxPieces = 16;
 
-int64_t split_max_pieces(int64_t Sk) {
-  const int64_t chunks = Sk / 32 + (Sk % 32 != 0);  // no overflow for any Sk >= 0
+// Largest piece count over n rows streamed in chunks of `unit`.
+int64_t split_max_pieces(int64_t n, int64_t unit = 32) {
+  const int64_t chunks = n / unit + (n % unit != 0);  // no overflow for any n >= 0
   return std::min<int64_t>(kSplitMaxPieces, chunks / kSplitMinChunks);
 }
 
-// Pieces to use for a stage with `blocks` (query block, head) workgroups, or
-// 0 for the one-workgroup-per-block form: only when at most half of the
-// compute units would be busy.
-int split_pieces(int64_t blocks, int64_t Sk, int max_pieces, int cus) {
+// Pieces for a pass with `blocks` workgroups, or 0 for the
+// one-workgroup-per-block form: only when at most half of the compute units
+// would be busy.
+int split_pieces(int64_t blocks, int64_t max_pieces, int cus) {
   if (max_pieces < 2 || cus <= 0 || blocks <= 0 || 2 * blocks > cus) return 0;
   return (int)std::min<int64_t>(max_pieces, std::max<int64_t>(2, cus / blocks));
 }
@@ -232,7 +234,6 @@ int validate(const attn_bwd_args *a, Checked &c) {
   const size_t ws_need = attn_bwd_workspace_bytes(a->B, a->H, a->Sq);
   Range wrng;
   c.ws_split = nullptr;
-  c.split_max = 0;
   if (ws_need) {
     if (!a->workspace) return fail(ATTN_E_WORKSPACE, "workspace is NULL (%zu bytes needed)", ws_need);
     if ((uintptr_t)a->workspace % 256)
@@ -245,7 +246,6 @@ int validate(const attn_bwd_args *a, Checked &c) {
     const size_t split_need = attn_bwd_split_workspace_bytes(a->B, a->H, a->Sq, a->Sk, a->D);
     if (split_need > ws_need && a->workspace_bytes >= split_need) {
       c.ws_split = (float *)((char *)a->workspace + ws_need);
-      c.split_max = (int)split_max_pieces(a->Sk);
       wrng.hi = wrng.lo + split_need;
     }
   }
@@ -330,12 +330,15 @@ int run_stage(int stage, Checked &c, hipStream_t stream) {
     p.nblk = c.nblk_q;
     nblocks = heads * c.nblk_q;
   }
-  // Split form: row statistics and dQ only, and not with a forward's
-  // statistics (the dQ pass then also publishes them).
-  if (c.ws_split && p.fo == nullptr && (stage == attn::STAGE_ROW_STATS || stage == attn::STAGE_DQ)) {
-    const int np = split_pieces(nblocks, p.Sk, c.split_max, attn::device_cus());
+  // Split form: not for the fused bf16 pass, nor for the dQ pass that forms
+  // a forward's statistics (it also publishes them).
+  if (c.ws_split && stage != attn::STAGE_STATS_DQ && !(stage == attn::STAGE_DQ && p.fo)) {
+    const bool kv = stage == attn::STAGE_KV;
+    const int unit = kv ? (c.bf16 ? 64 : 32) : 32;  // the pass's chunk rows
+    const int64_t n = kv ? p.Sq : p.Sk;
+    const int np = split_pieces(nblocks, split_max_pieces(n, unit), attn::device_cus());
     if (np >= 2) {
-      const int chunks = (p.Sk + 31) / 32;
+      const int chunks = (int)((n + unit - 1) / unit);
       p.piece_chunks = (chunks + np - 1) / np;
       p.npiece = (chunks + p.piece_chunks - 1) / p.piece_chunks;  // no empty tail piece
       p.ws_split = c.ws_split;
@@ -716,11 +719,16 @@ size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq) {
 size_t attn_bwd_split_workspace_bytes(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D) {
   if (B < 0 || H < 0 || Sq < 0 || Sk < 0 || D <= 0 || D > 4096) return 0;
   const size_t base = attn_bwd_workspace_bytes(B, H, Sq);
-  const int64_t np = split_max_pieces(Sk), rec = D > 4 ? D : 4;
-  int64_t n;
-  if (base == SIZE_MAX || np < 2 || __builtin_mul_overflow(stat_bytes(B, H, Sq), np * rec, &n) ||
-      n > kMaxBytes)
+  if (base == SIZE_MAX) return base;
+  // query-major passes: pieces of the keys, max(D, 4) floats per query row;
+  // dK / dV: pieces of the queries, 2 D floats per key row (H bounds Hkv)
+  const int64_t npq = split_max_pieces(Sk), npk = split_max_pieces(Sq);
+  const int64_t rq = stat_bytes(B, H, Sq), rk = stat_bytes(B, H, Sk);
+  int64_t nq = 0, nk = 0;
+  if (rq < 0 || rk < 0 || __builtin_mul_overflow(rq, npq * (D > 4 ? D : 4), &nq) ||
+      __builtin_mul_overflow(rk, npk * 2 * D, &nk) || nq > kMaxBytes || nk > kMaxBytes)
     return base;
+  const int64_t n = std::max(npq >= 2 ? nq : 0, npk >= 2 ? nk : 0);
   return base + (size_t)n;
 }
 

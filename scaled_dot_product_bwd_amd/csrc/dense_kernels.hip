@@ -529,7 +529,7 @@ __device__ __forceinline__ void kv_run(const DenseParams &p, KvState<T, D> &S, i
   wait_vmem();  // the repeated loads of the last steps land before the workgroup ends
 }
 
-template <typename T, int D, int MODE>
+template <typename T, int D, int MODE, bool SPLIT>
 __global__ __launch_bounds__(256) void k_kv_bwd(const DenseParams p) {
   typedef MT<T> M;
   constexpr int KS = M::KS, KL = M::KL, NSD = D / KS, NT = D / 32, ROWS = KvShape<T>::ROWS;
@@ -544,7 +544,9 @@ __global__ __launch_bounds__(256) void k_kv_bwd(const DenseParams p) {
   S.half = S.lane >> 5;
   const int nb = p.nblk;
   int bg, blk;  // key block 0 sees the most queries under a causal mask: rank = block
-  tile_order<kKvGroup>(blockIdx.x, gridDim.x, nb, bg, blk);
+  // split form: consecutive workgroups are the query pieces of one key block
+  const int np = SPLIT ? p.npiece : 1;
+  tile_order<kKvGroup>(blockIdx.x / np, gridDim.x / np, nb, bg, blk);
   const int g = bg % p.Hkv;  // the K / V head; its query heads are g * G ... g * G + G - 1
   S.b = bg / p.Hkv;
   S.h0 = g * p.G;
@@ -575,7 +577,10 @@ __global__ __launch_bounds__(256) void k_kv_bwd(const DenseParams p) {
   const int ilo = max(0, (int)max((int64_t)j0b - p.hi_off, (int64_t)0));
   const int ihi = min(p.Sq - 1, (int)min((int64_t)jlast - p.lo_off, (int64_t)kBig));
   S.c_first = ilo / ROWS;
-  const int c_last = ihi >= ilo ? ihi / ROWS : S.c_first - 1;
+  int c_last = ihi >= ilo ? ihi / ROWS : S.c_first - 1;
+  const QPiece Pc = q_piece<SPLIT>(p, (int)(blockIdx.x % np), S.c_first, c_last);
+  S.c_first = Pc.lo;
+  c_last = Pc.hi;
   S.nch = c_last - S.c_first + 1;
   S.total = S.nch > 0 ? S.nch * p.G : 0;
 
@@ -584,6 +589,25 @@ __global__ __launch_bounds__(256) void k_kv_bwd(const DenseParams p) {
   S.io_q.init(p.qs[1]);
   S.io_g.init(p.dys[1]);
   kv_run<T, D, MODE>(p, S, c_last, j0b, Qs, Gs, st);
+
+  if constexpr (SPLIT) {
+    // this piece's raw accumulators of the wave's keys (dK negated and without
+    // its factor, dV), merged by k_kv_merge; 2 D floats per key row
+    if (!kvalid) return;
+    float *wrow = p.ws_split + ((int64_t)Pc.piece * p.B * p.Hkv * p.Sk +
+                                ((int64_t)b * p.Hkv + g) * p.Sk + kj) * (2 * D);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int d0 = 32 * t + 8 * q + 4 * half;
+        store4<float>(wrow + d0, S.dk[t][4 * q], S.dk[t][4 * q + 1], S.dk[t][4 * q + 2],
+                      S.dk[t][4 * q + 3]);
+        store4<float>(wrow + D + d0, S.dv[t][4 * q], S.dv[t][4 * q + 1], S.dv[t][4 * q + 2],
+                      S.dv[t][4 * q + 3]);
+      }
+    return;
+  }
 
   // dK (times the factor of dS, applied once) and dV of the wave's 32 keys.
   typedef RowStore<T, D> RS;
@@ -962,6 +986,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                  S.lane);
 }
 
+// Merge of the split dK / dV: one thread per 4 columns of a key row, the
+// pieces' accumulators added in piece order; dK = 0 - scale * sum (it was
+// accumulated negated; a key no row sees gets +0), dV = sum.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_kv_merge(const DenseParams p) {
+  const int64_t rows = (int64_t)p.B * p.Hkv * p.Sk;
+  const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (tid >= rows * (D / 4)) return;
+  const int dc = (int)(tid % (D / 4));
+  const int64_t row = tid / (D / 4);
+  const int j = (int)(row % p.Sk);
+  const int64_t bg = row / p.Sk;
+  const int g = (int)(bg % p.Hkv), b = (int)(bg / p.Hkv);
+  f32x4 ak = {0.f, 0.f, 0.f, 0.f}, av = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < p.npiece; ++k) {
+    const float *w = p.ws_split + (k * rows + row) * (2 * D) + 4 * dc;
+    ak += *reinterpret_cast<const f32x4 *>(w);
+    av += *reinterpret_cast<const f32x4 *>(w + D);
+  }
+  const float sc = p.scale;
+  if (p.need_dk)
+    store4<T>((T *)p.dk + b * p.dks[0] + (int64_t)j * p.dks[1] + g * p.dks[2] + 4 * dc,
+              0.f - sc * ak[0], 0.f - sc * ak[1], 0.f - sc * ak[2], 0.f - sc * ak[3]);
+  if (p.need_dv)
+    store4<T>((T *)p.dv + b * p.dvs[0] + (int64_t)j * p.dvs[1] + g * p.dvs[2] + 4 * dc, av[0],
+              av[1], av[2], av[3]);
+}
+
 // Merge of the split dQ: one thread per 4 columns of a row, the pieces' partial
 // sums added in piece order, times `scale`, one store.
 template <typename T, int D>
@@ -985,13 +1037,19 @@ __global__ __launch_bounds__(256) void k_dq_merge(const DenseParams p) {
 // ---------------------------------------------------------------------------
 // Launchers: one instantiation per (element type, head dim, mask mode).
 
-// Split form (p.ws_split set; row statistics and dQ only): nblocks * npiece
-// workgroups, then the merge over the B * H * Sq rows.
+// Split form (p.ws_split set; row statistics, dQ or dK / dV): nblocks * npiece
+// workgroups, then the merge over the rows.
 template <typename T, int D, int MODE>
 static hipError_t launch_t(int stage, const DenseParams &p, int nblocks, hipStream_t stream) {
-  const bool split = p.ws_split != nullptr && (stage == STAGE_ROW_STATS || stage == STAGE_DQ);
+  const bool split = p.ws_split != nullptr && stage != STAGE_STATS_DQ;
   const int64_t rows = (int64_t)p.B * p.H * p.Sq;
-  if (split && stage == STAGE_ROW_STATS) {
+  if (split && stage == STAGE_KV) {
+    const int64_t krows = (int64_t)p.B * p.Hkv * p.Sk;
+    hipLaunchKernelGGL((k_kv_bwd<T, D, MODE, true>), dim3(nblocks * p.npiece), dim3(256), 0,
+                       stream, p);
+    hipLaunchKernelGGL((k_kv_merge<T, D>), dim3((unsigned)((krows * (D / 4) + 255) / 256)),
+                       dim3(256), 0, stream, p);
+  } else if (split && stage == STAGE_ROW_STATS) {
     hipLaunchKernelGGL((k_row_stats<T, D, MODE, true>), dim3(nblocks * p.npiece), dim3(256), 0,
                        stream, p);
     hipLaunchKernelGGL(k_rs_merge, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, p);
@@ -1003,7 +1061,7 @@ static hipError_t launch_t(int stage, const DenseParams &p, int nblocks, hipStre
   } else if (stage == STAGE_ROW_STATS)
     hipLaunchKernelGGL((k_row_stats<T, D, MODE, false>), dim3(nblocks), dim3(256), 0, stream, p);
   else if (stage == STAGE_KV)
-    hipLaunchKernelGGL((k_kv_bwd<T, D, MODE>), dim3(nblocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((k_kv_bwd<T, D, MODE, false>), dim3(nblocks), dim3(256), 0, stream, p);
   else if (stage == STAGE_DQ)
     hipLaunchKernelGGL((k_dq_bwd<T, D, MODE, false>), dim3(nblocks), dim3(256), 0, stream, p);
   else if constexpr (sizeof(T) == 2)

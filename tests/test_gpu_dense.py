@@ -76,12 +76,16 @@ SPLIT_CASES = {
     "config4_keypad_causal": dict(cfg=4, kind="keypad", causal=True),
     "config4_bias": dict(cfg=4, kind="bias", causal=False),
     "ragged_causal": dict(cfg=None, kind="causal", causal=False),
+    "few_keys_many_queries": dict(cfg="fk", kind="causal", causal=False),
 }
 
 
 def _split_inputs(c):
     if c["cfg"] is None:
         q, k, v, dy, _ = sdpa_inputs.dense_inputs(1, 200, 1000, 4, 32, seed=77)
+        return q, k, v, dy, None
+    if c["cfg"] == "fk":  # 2 key blocks per head against 2000 queries: the dK / dV pass splits
+        q, k, v, dy, _ = sdpa_inputs.dense_inputs(1, 2000, 250, 2, 64, seed=79)
         return q, k, v, dy, None
     d, q, k, v, dy = _cfg_inputs(c["cfg"])
     B, Sk = q.shape[0], k.shape[1]
@@ -109,6 +113,33 @@ def test_fp32_split_form_against_oracle_and_direct_form(case):
     for n in ("dq", "dk", "dv"):
         e = rel_err(split[n], direct[n])
         assert e <= TOL[torch.float32], f"{case} {n}: split vs direct {e:.3e}"
+
+
+def test_bf16_kv_split_through_the_stage_calls():
+    """bf16: the fused statistics + dQ pass (never split), then the dK / dV pass
+    in split form (64-row query chunks) with a split-sized workspace, against
+    the oracle."""
+    import scaled_dot_product_bwd_amd as sdb
+    dev = torch.device("cuda:0")
+    q, k, v, dy, _ = sdpa_inputs.dense_inputs(2, 1500, 200, 2, 128, seed=80, dtype=torch.bfloat16)
+    ref = oracle_run(q, k, v, dy, mask_kind="causal")
+    qd, kd, vd, gd = (x.to(dev) for x in (q, k, v, dy))
+    outs = [torch.full_like(x, float("nan")) for x in (qd, kd, vd)]
+    ws = torch.empty(sdb.split_workspace_bytes(2, 2, 1500, 200, 128), dtype=torch.uint8, device=dev)
+    a = sdb.make_args(qd, kd, vd, gd, *outs, mask_kind="causal", workspace=ws)
+    sdb.attn_bwd_stage("stats_dq", a)
+    sdb.attn_bwd_stage("kv", a)
+    torch.cuda.synchronize()
+    first = [o.clone() for o in outs]
+    sdb.attn_bwd_stage("stats_dq", a)
+    sdb.attn_bwd_stage("kv", a)
+    torch.cuda.synchronize()
+    for n, o, f, r in zip(("dq", "dk", "dv"), outs, first, (ref["dq"], ref["dk"], ref["dv"])):
+        g = o.float().cpu().double().numpy()
+        assert not np.isnan(g).any(), n
+        e = rel_err(g, r, float(np.max(np.abs(ref["dv"]))))
+        assert e <= TOL[torch.bfloat16], f"{n}: {e:.3e}"
+        assert torch.equal(o.view(torch.int16), f.view(torch.int16)), f"{n}: rerun differs"
 
 
 def test_split_form_through_the_stage_calls():
