@@ -140,9 +140,9 @@ int attn_bwd(const attn_bwd_args *a, void *stream);
  * arguments and results, but `workspace` / `workspace_bytes` are ignored and
  * the row statistics live in a static device array the library holds on each
  * GPU (16 MiB, from the first use of the library's code on that GPU until the
- * process ends); where attn_bwd_split_workspace_bytes() fits in it, the split
- * form's partial results live there too (the form attn_bwd takes with a
- * workspace of that size).  B * H * Sq must be at most 2^20 rows, else ATTN_E_WORKSPACE
+ * process ends); it runs the form attn_bwd takes with a workspace of exactly
+ * attn_bwd_workspace_bytes() (never the split form), so the two give the same
+ * bits.  B * H * Sq must be at most 2^20 rows, else ATTN_E_WORKSPACE
  * (before any HIP call).  The array's device address is looked up once per
  * device, on the device current on the calling thread, which must be the
  * stream's device.  The call allocates and frees nothing.  All calls on one

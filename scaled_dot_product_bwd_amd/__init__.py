@@ -311,15 +311,14 @@ def attn_bwd(q, k, v, dy, *, wrt="all", mask_kind="none", causal=False, window=0
         dq, dk, dv = out
     if workspace is None:
         nbytes = workspace_bytes(B, H, Sq)
-        if q.dtype == torch.float32:
-            # the split form of the fp32 passes pays when a pass's workgroups
-            # (per query block and head, or per key block and K / V head) fill
-            # at most half of the GPU (the library decides; a larger workspace
-            # only makes it possible)
-            blocks = min(B * H * ((Sq + 127) // 128), B * k.shape[2] * ((k.shape[1] + 127) // 128))
-            cus = torch.cuda.get_device_properties(q.device).multi_processor_count
-            if 2 * blocks <= cus:
-                nbytes = max(nbytes, split_workspace_bytes(B, H, Sq, k.shape[1], D))
+        # the split form of the passes pays when a pass's workgroups (per
+        # query block and head, or per key block and K / V head) fill at most
+        # half of the GPU (the library decides; a larger workspace only makes
+        # it possible)
+        blocks = min(B * H * ((Sq + 127) // 128), B * k.shape[2] * ((k.shape[1] + 127) // 128))
+        cus = torch.cuda.get_device_properties(q.device).multi_processor_count
+        if 2 * blocks <= cus:
+            nbytes = max(nbytes, split_workspace_bytes(B, H, Sq, k.shape[1], D))
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
     args = make_args(q, k, v, dy, dq, dk, dv, wrt=w, mask_kind=mask_kind, causal=causal,
                      window=window, mask=mask, threshold=threshold, scale=scale,

@@ -330,11 +330,11 @@ int run_stage(int stage, Checked &c, hipStream_t stream) {
     p.nblk = c.nblk_q;
     nblocks = heads * c.nblk_q;
   }
-  // Split form: not for the fused bf16 pass, nor for the dQ pass that forms
-  // a forward's statistics (it also publishes them).
-  if (c.ws_split && stage != attn::STAGE_STATS_DQ && !(stage == attn::STAGE_DQ && p.fo)) {
+  // Split form: not for the dQ pass that forms a forward's statistics (it also
+  // publishes them).
+  if (c.ws_split && !(stage == attn::STAGE_DQ && p.fo)) {
     const bool kv = stage == attn::STAGE_KV;
-    const int unit = kv ? (c.bf16 ? 64 : 32) : 32;  // the pass's chunk rows
+    const int unit = kv ? (c.bf16 ? 64 : 32) : stage == attn::STAGE_STATS_DQ ? 64 : 32;  // chunk rows
     const int64_t n = kv ? p.Sq : p.Sk;
     const int np = split_pieces(nblocks, split_max_pieces(n, unit), attn::device_cus());
     if (np >= 2) {
@@ -720,15 +720,19 @@ size_t attn_bwd_split_workspace_bytes(int64_t B, int64_t H, int64_t Sq, int64_t 
   if (B < 0 || H < 0 || Sq < 0 || Sk < 0 || D <= 0 || D > 4096) return 0;
   const size_t base = attn_bwd_workspace_bytes(B, H, Sq);
   if (base == SIZE_MAX) return base;
-  // query-major passes: pieces of the keys, max(D, 4) floats per query row;
-  // dK / dV: pieces of the queries, 2 D floats per key row (H bounds Hkv)
-  const int64_t npq = split_max_pieces(Sk), npk = split_max_pieces(Sq);
+  // query-major passes: pieces of the keys, max(D, 4) floats per query row
+  // (the fused bf16 pass: pieces of 64 keys, 2 D + 8); dK / dV: pieces of the
+  // queries, 2 D floats per key row (H bounds Hkv)
+  const int64_t npq = split_max_pieces(Sk), npf = split_max_pieces(Sk, 64),
+                npk = split_max_pieces(Sq);
   const int64_t rq = stat_bytes(B, H, Sq), rk = stat_bytes(B, H, Sk);
-  int64_t nq = 0, nk = 0;
+  int64_t nq = 0, nf = 0, nk = 0;
   if (rq < 0 || rk < 0 || __builtin_mul_overflow(rq, npq * (D > 4 ? D : 4), &nq) ||
-      __builtin_mul_overflow(rk, npk * 2 * D, &nk) || nq > kMaxBytes || nk > kMaxBytes)
+      __builtin_mul_overflow(rq, npf * (2 * D + 8), &nf) ||
+      __builtin_mul_overflow(rk, npk * 2 * D, &nk) || nq > kMaxBytes || nf > kMaxBytes ||
+      nk > kMaxBytes)
     return base;
-  const int64_t n = std::max(npq >= 2 ? nq : 0, npk >= 2 ? nk : 0);
+  const int64_t n = std::max({npq >= 2 ? nq : 0, npf >= 2 ? nf : 0, npk >= 2 ? nk : 0});
   return base + (size_t)n;
 }
 

@@ -295,6 +295,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   }
 }
 
+// The statistics of a row whose pieces were combined: M the common reference,
+// mt the true max, l and dl (delta') relative to M; as row_stat_final forms
+// them with M as the reference.
+__device__ __forceinline__ RowStatOut merged_row_stat(float M, float mt, float l, float dl,
+                                                      float inv_scale_log2) {
+  RowStatOut o;
+  o.empty = !(l > 0.f);
+  o.m = o.empty ? -INFINITY : mt * kLn2;
+  o.l = o.empty ? 0.f : l * fast_exp2(M - mt);
+  o.delta = o.empty ? 0.f : dl / l;
+  o.nls = (o.empty ? -INFINITY : -(M + __log2f(l))) * inv_scale_log2;
+  o.inv_l = o.empty ? 0.f : 1.f / l;
+  return o;
+}
+
 // Merge of the split row statistics: one thread per row, the pieces in order
 // rescaled to their common reference M (the largest mref): l = sum 2^(mref_k
 // - M) l_k and delta' likewise; then the statistics as row_stat_final forms
@@ -318,13 +333,7 @@ __global__ __launch_bounds__(256) void k_rs_merge(const DenseParams p) {
       dl = fmaf(v[3], a, dl);
     }
   }
-  RowStatOut o;
-  o.empty = !(l > 0.f);
-  o.m = o.empty ? -INFINITY : mt * kLn2;
-  o.l = o.empty ? 0.f : l * fast_exp2(M - mt);
-  o.delta = o.empty ? 0.f : dl / l;
-  o.nls = (o.empty ? -INFINITY : -(M + __log2f(l))) * p.inv_scale_log2;
-  store_row_stat(p, row, o);
+  store_row_stat(p, row, merged_row_stat(M, mt, l, dl, p.inv_scale_log2));
 }
 
 // ---------------------------------------------------------------------------
@@ -891,7 +900,7 @@ __device__ __forceinline__ void sd_step(const DenseParams &p, SdState<T, D> &S, 
 }
 
 
-template <typename T, int D, int MODE>
+template <typename T, int D, int MODE, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_stats_dq(const DenseParams p) {
   typedef MT<T> M;
   constexpr int KS = M::KS, KL = M::KL, NSD = D / KS, NT = D / 32, QROWS = 128, KC = kSdKeys;
@@ -906,7 +915,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int l32 = S.lane & 31, half = S.half;
   const int nb = p.nblk;
   int bh, rank;
-  tile_order<kDqGroup>(blockIdx.x, gridDim.x, nb, bh, rank);
+  const int np = SPLIT ? p.npiece : 1;  // split form: consecutive workgroups are one block's pieces
+  tile_order<kDqGroup>(blockIdx.x / np, gridDim.x / np, nb, bh, rank);
   const int blk = nb - 1 - rank;  // the heaviest causal blocks first
   S.h = bh % p.H;
   S.b = bh / p.H;
@@ -929,41 +939,69 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   S.kbase = (const T *)p.k + b * p.ks[0] + (h / p.G) * p.ks[2];  // the head's K / V head
   S.vbase = (const T *)p.v + b * p.vs[0] + (h / p.G) * p.vs[2];
   const QRange R = q_range<KC>(p, i0, QROWS, MODE == MODE_INDEX);
-  S.c_last = R.c_last;
+  const QPiece Pc = q_piece<SPLIT>(p, (int)(blockIdx.x % np), R.c_first, R.c_last);
+  S.c_last = Pc.hi;
   S.io_k.init(p.ks[1]);
   S.io_v.init(p.vs[1]);
   // Chunk c_first into buffer 0 and landed (with the fragment loads above);
   // chunk c_first + 1 into buffer 1 stays in flight under chunk c_first's
   // compute (the first step waits for it at its end, as for every chunk).
-  if (R.c_first <= R.c_last) {
-    S.io_k.issue(S.kbase, p.ks[1], R.c_first * KC, p.Sk, Ks[0]);
-    S.io_v.issue(S.vbase, p.vs[1], R.c_first * KC, p.Sk, Vs[0]);
+  if (Pc.lo <= Pc.hi) {
+    S.io_k.issue(S.kbase, p.ks[1], Pc.lo * KC, p.Sk, Ks[0]);
+    S.io_v.issue(S.vbase, p.vs[1], Pc.lo * KC, p.Sk, Vs[0]);
   }
   wait_vmem();
   __syncthreads();
-  if (R.c_first <= R.c_last) {
-    const int c1 = min(R.c_first + 1, R.c_last);
+  if (Pc.lo <= Pc.hi) {
+    const int c1 = min(Pc.lo + 1, Pc.hi);
     S.io_k.issue(S.kbase, p.ks[1], c1 * KC, p.Sk, Ks[1]);
     S.io_v.issue(S.vbase, p.vs[1], c1 * KC, p.Sk, Vs[1]);
   }
   // Masked chunks before cu0 and after cu1, unmasked ones between (only for
   // the index rule with scale > 0: the unmasked step takes the max of the raw
   // scores); the buffers rotate at run time.
-  int cu0 = R.cu0, cu1 = R.cu1;
+  int cu0 = R.cu0, cu1 = SPLIT ? min(R.cu1, Pc.hi) : R.cu1;
   if (!(p.scale_log2 > 0.f)) {
-    cu0 = R.c_last + 1;
-    cu1 = R.c_last;
+    cu0 = Pc.hi + 1;
+    cu1 = Pc.hi;
   }
-  int c = R.c_first, bc = 0;
+  int c = Pc.lo, bc = 0;
   auto next = [&]() {
     ++c;
     bc = bc == 2 ? 0 : bc + 1;
   };
-  for (; c < cu0 && c <= R.c_last; next()) sd_step<T, D, MODE, true>(p, S, c, bc, Ks, Vs);
+  for (; c < cu0 && c <= Pc.hi; next()) sd_step<T, D, MODE, true>(p, S, c, bc, Ks, Vs);
   if constexpr (MODE == MODE_INDEX)
     for (; c <= cu1; next()) sd_step<T, D, MODE, false>(p, S, c, bc, Ks, Vs);
-  for (; c <= R.c_last; next()) sd_step<T, D, MODE, true>(p, S, c, bc, Ks, Vs);
+  for (; c <= Pc.hi; next()) sd_step<T, D, MODE, true>(p, S, c, bc, Ks, Vs);
   wait_vmem();  // the repeated loads of the last steps land before the workgroup ends
+
+  if constexpr (SPLIT) {
+    // This piece's partial results (merged by k_sdq_merge): per row (mref,
+    // true max, l, delta', dh), then A' and B as whole rows through LDS (the
+    // chunk tiles are free once every wave's repeated loads have landed).
+    const int64_t rows = (int64_t)p.B * p.H * p.Sq;
+    const int64_t row0 = ((int64_t)b * p.H + h) * p.Sq + i0 + 32 * w;  // the wave's first row
+    const float l_tot = halves_sum(S.st.l);
+    const float d_tot = halves_sum(S.st.dl);
+    if (S.qi < p.Sq && half == 0) {
+      float *r = p.ws_split + ((int64_t)Pc.piece * rows + row0 + l32) * 8;
+      store4<float>(r, S.st.mref, S.st.mtrue, l_tot, d_tot);
+      store4<float>(r + 4, S.dh, 0.f, 0.f, 0.f);
+    }
+    typedef RowStore<float, D> RSF;
+    static_assert(2 * RSF::BYTES <= sizeof(Ks) && 2 * RSF::BYTES <= sizeof(Vs), "staging fits");
+    __syncthreads();
+    char *area = reinterpret_cast<char *>(w < 2 ? (void *)Ks : (void *)Vs) + (w & 1) * RSF::BYTES;
+    const int nvalid = max(0, min(32, p.Sq - (i0 + 32 * w)));
+    float *wa = p.ws_split + (int64_t)p.npiece * rows * 8 + ((int64_t)Pc.piece * rows + row0) * D;
+    float *wb = wa + (int64_t)p.npiece * rows * D;
+    RSF::write_tiles(S.acc_a, 1.f, area, S.lane);
+    RSF::store_rows(area, nvalid, [&](int n) { return wa + (int64_t)n * D; }, S.lane);
+    RSF::write_tiles(S.acc_b, 1.f, area, S.lane);  // LDS operations of a wave complete in order
+    RSF::store_rows(area, nvalid, [&](int n) { return wb + (int64_t)n * D; }, S.lane);
+    return;
+  }
 
   const RowStatOut o = row_stat_final(S.st, p.inv_scale_log2);
   if (S.qi < p.Sq && half == 0) store_row_stat(p, ((int64_t)b * p.H + h) * p.Sq + S.qi, o);
@@ -1014,6 +1052,61 @@ __global__ __launch_bounds__(256) void k_kv_merge(const DenseParams p) {
               av[1], av[2], av[3]);
 }
 
+// Merge of the split statistics + dQ pass (bf16): one thread per 4 columns of
+// a row.  Pieces in order: the common reference M (largest mref), l = sum
+// 2^(mref_k - M) l_k and delta' likewise, delta = delta' / l, and dQ = scale /
+// l * sum 2^(mref_k - M) (A'_k + (dh_k - delta) B_k).  The row's first thread
+// writes the statistics.  Partial layout: [npiece][rows][8] records, then
+// [npiece][rows][D] of A', then of B.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_sdq_merge(const DenseParams p) {
+  const int64_t rows = (int64_t)p.B * p.H * p.Sq;
+  const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (tid >= rows * (D / 4)) return;
+  const int dc = (int)(tid % (D / 4));
+  const int64_t row = tid / (D / 4);
+  const int np = p.npiece;
+  auto rec = [&](int k) { return p.ws_split + ((int64_t)k * rows + row) * 8; };
+  float M = -INFINITY, mt = -INFINITY;
+  for (int k = 0; k < np; ++k) {
+    const f32x4 v = *reinterpret_cast<const f32x4 *>(rec(k));
+    M = fmaxf(M, v[0]);
+    mt = fmaxf(mt, v[1]);
+  }
+  float l = 0.f, dl = 0.f;
+  if (M != -INFINITY) {
+    for (int k = 0; k < np; ++k) {
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(rec(k));
+      const float a = fast_exp2(v[0] - M);  // 0 for a piece that saw nothing
+      l = fmaf(v[2], a, l);
+      dl = fmaf(v[3], a, dl);
+    }
+  }
+  const RowStatOut o = merged_row_stat(M, mt, l, dl, p.inv_scale_log2);
+  if (dc == 0) store_row_stat(p, row, o);
+  if (p.dq == nullptr) return;  // statistics only
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (!o.empty) {
+    const float *abase = p.ws_split + (int64_t)np * rows * 8;
+    const float *bbase = abase + (int64_t)np * rows * D;
+    for (int k = 0; k < np; ++k) {
+      const float *r = rec(k);
+      if (r[0] == -INFINITY) continue;  // nothing seen in this piece
+      const float a = fast_exp2(r[0] - M), sh = r[4] - o.delta;
+      const f32x4 A = *reinterpret_cast<const f32x4 *>(abase + ((int64_t)k * rows + row) * D + 4 * dc);
+      const f32x4 B = *reinterpret_cast<const f32x4 *>(bbase + ((int64_t)k * rows + row) * D + 4 * dc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(a, fmaf(sh, B[e], A[e]), acc[e]);
+    }
+  }
+  const int i = (int)(row % p.Sq);
+  const int64_t bh = row / p.Sq;
+  const int h = (int)(bh % p.H), b = (int)(bh / p.H);
+  const float sc = p.scale * o.inv_l;
+  T *dst = (T *)p.dq + b * p.dqs[0] + (int64_t)i * p.dqs[1] + h * p.dqs[2] + 4 * dc;
+  store4<T>(dst, sc * acc[0], sc * acc[1], sc * acc[2], sc * acc[3]);
+}
+
 // Merge of the split dQ: one thread per 4 columns of a row, the pieces' partial
 // sums added in piece order, times `scale`, one store.
 template <typename T, int D>
@@ -1037,12 +1130,21 @@ __global__ __launch_bounds__(256) void k_dq_merge(const DenseParams p) {
 // ---------------------------------------------------------------------------
 // Launchers: one instantiation per (element type, head dim, mask mode).
 
-// Split form (p.ws_split set; row statistics, dQ or dK / dV): nblocks * npiece
-// workgroups, then the merge over the rows.
+// Split form (p.ws_split set): nblocks * npiece workgroups, then the merge
+// over the rows.
 template <typename T, int D, int MODE>
 static hipError_t launch_t(int stage, const DenseParams &p, int nblocks, hipStream_t stream) {
-  const bool split = p.ws_split != nullptr && stage != STAGE_STATS_DQ;
+  const bool split = p.ws_split != nullptr;
   const int64_t rows = (int64_t)p.B * p.H * p.Sq;
+  if constexpr (sizeof(T) == 2) {
+    if (split && stage == STAGE_STATS_DQ) {
+      hipLaunchKernelGGL((k_stats_dq<T, D, MODE, true>), dim3(nblocks * p.npiece), dim3(256), 0,
+                         stream, p);
+      hipLaunchKernelGGL((k_sdq_merge<T, D>), dim3((unsigned)((rows * (D / 4) + 255) / 256)),
+                         dim3(256), 0, stream, p);
+      return hipGetLastError();
+    }
+  }
   if (split && stage == STAGE_KV) {
     const int64_t krows = (int64_t)p.B * p.Hkv * p.Sk;
     hipLaunchKernelGGL((k_kv_bwd<T, D, MODE, true>), dim3(nblocks * p.npiece), dim3(256), 0,
@@ -1065,7 +1167,7 @@ static hipError_t launch_t(int stage, const DenseParams &p, int nblocks, hipStre
   else if (stage == STAGE_DQ)
     hipLaunchKernelGGL((k_dq_bwd<T, D, MODE, false>), dim3(nblocks), dim3(256), 0, stream, p);
   else if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL((k_stats_dq<T, D, MODE>), dim3(nblocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((k_stats_dq<T, D, MODE, false>), dim3(nblocks), dim3(256), 0, stream, p);
   else
     return hipErrorInvalidValue;  // the fused pass is built for bf16 only
   return hipGetLastError();

@@ -94,6 +94,8 @@ extern "C" int attn_bwd_noalloc(const attn_bwd_args *a, void *stream) {
   if (rc != ATTN_OK) return rc;
   attn_bwd_args b = *a;
   b.workspace = ws;
-  b.workspace_bytes = kScratchBytes;
+  // exactly the statistics planes: the one-workgroup-per-block form, the one
+  // attn_bwd takes with a workspace of attn_bwd_workspace_bytes()
+  b.workspace_bytes = attn_bwd_workspace_bytes(a->B, a->H, a->Sq);
   return attn::run_dense_all(&b, stream);
 }

@@ -86,10 +86,9 @@ hipError_t launch_dense_stage(int stage, bool bf16, int D, int mode, const Dense
   if (!p.st_m || !p.st_l || !p.st_delta || !p.st_nls) die("dense workspace planes");
   if ((mode != MODE_INDEX) != (p.mask != nullptr)) die("dense mask pointer");
   if (p.ws_split) {  // split form: pieces covering the streamed axis
-    if (stage == STAGE_STATS_DQ) die("split form of the fused pass");
     if (stage == STAGE_DQ && p.fo) die("split dQ pass with a forward's statistics");
     if (p.npiece < 2 || p.npiece > 16 || p.piece_chunks < 4) die("split pieces");
-    const int64_t unit = stage == STAGE_KV ? (bf16 ? 64 : 32) : 32;
+    const int64_t unit = stage == STAGE_KV ? (bf16 ? 64 : 32) : stage == STAGE_STATS_DQ ? 64 : 32;
     const int64_t n = stage == STAGE_KV ? p.Sq : p.Sk;
     const int64_t chunks = (n + unit - 1) / unit;
     if ((int64_t)p.npiece * p.piece_chunks < chunks || (int64_t)(p.npiece - 1) * p.piece_chunks >= chunks)

@@ -115,6 +115,35 @@ def test_fp32_split_form_against_oracle_and_direct_form(case):
         assert e <= TOL[torch.float32], f"{case} {n}: split vs direct {e:.3e}"
 
 
+BF16_SPLIT_CASES = {
+    # few query blocks against many keys: the fused statistics + dQ pass splits
+    "causal_offset": dict(B=1, H=4, Sq=256, Sk=4096, D=128, kind="causal", causal=False, window=0),
+    "keypad_causal": dict(B=2, H=2, Sq=200, Sk=3000, D=64, kind="keypad", causal=True, window=0),
+    "bias": dict(B=1, H=2, Sq=130, Sk=2600, D=32, kind="bias", causal=False, window=0),
+    "window": dict(B=1, H=3, Sq=300, Sk=5000, D=128, kind="window", causal=False, window=700),
+}
+
+
+@pytest.mark.parametrize("case", list(BF16_SPLIT_CASES))
+def test_bf16_split_form_against_oracle_and_direct_form(case):
+    c = BF16_SPLIT_CASES[case]
+    q, k, v, dy, g = sdpa_inputs.dense_inputs(c["B"], c["Sq"], c["Sk"], c["H"], c["D"], seed=81,
+                                              dtype=torch.bfloat16)
+    mask = None
+    if c["kind"] == "keypad":
+        mask, _ = sdpa_inputs.keypad_valid(g, c["B"], c["Sk"], c["Sk"] // 4)
+        mask = mask.reshape(c["B"], 1, 1, c["Sk"])
+    elif c["kind"] == "bias":
+        mask = sdpa_inputs.bias_normal(g, c["B"], c["H"], c["Sq"], c["Sk"])
+    kw = dict(mask_kind=c["kind"], causal=c["causal"], window=c["window"], mask=mask)
+    split = gpu_run(q, k, v, dy, workspace="split", **kw)
+    direct = gpu_run(q, k, v, dy, workspace="min", **kw)
+    ref = oracle_run(q, k, v, dy, **kw)
+    print(case, "split", assert_parity(split, ref, torch.bfloat16, label=case + " split"))
+    print(case, "direct", assert_parity(direct, ref, torch.bfloat16, label=case + " direct"))
+    _rerun_bitwise(split, q, k, v, dy, workspace="split", **kw)
+
+
 def test_bf16_kv_split_through_the_stage_calls():
     """bf16: the fused statistics + dQ pass (never split), then the dK / dV pass
     in split form (64-row query chunks) with a split-sized workspace, against

@@ -31,7 +31,11 @@ def test_noalloc_equals_attn_bwd_on_two_calls_in_a_row():
     for B, H, S, D, dtype, mask, window, seed in CASES:
         q, k, v, dy, _ = sdpa_inputs.dense_inputs(B, S, S, H, D, seed=seed, dtype=dtype)
         qd, kd, vd, gd = (x.to(dev) for x in (q, k, v, dy))
-        ref = sdb.attn_bwd(qd, kd, vd, gd, mask_kind=mask, window=window)
+        # the reference on a workspace of exactly the statistics planes: the
+        # form attn_bwd_noalloc runs (a split-sized workspace would give the
+        # split form, equal only up to rounding)
+        ws = torch.empty(sdb.workspace_bytes(B, H, S), dtype=torch.uint8, device=dev)
+        ref = sdb.attn_bwd(qd, kd, vd, gd, mask_kind=mask, window=window, workspace=ws)
         outs = [torch.full_like(x, float("nan")) for x in (qd, kd, vd)]
         args = sdb.make_args(qd, kd, vd, gd, *outs, mask_kind=mask, window=window)
         assert not args.workspace  # no workspace is passed: the scratch is used
