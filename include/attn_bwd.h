@@ -110,11 +110,11 @@ typedef struct attn_bwd_args {
  * exceed 2^60 bytes (sizes attn_bwd rejects). */
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Sq);
 
-/* A larger workspace that also holds the split form of the row-statistics,
- * dQ and dK / dV passes (every pass but the fused bf16 statistics + dQ one,
- * and not the dQ pass that forms a forward's statistics): the four planes
- * above, then partial results of up to 16 pieces per row (max(D, 4) fp32 per
- * query row for the query-major passes, 2 D per key row for dK / dV).  With
+/* A larger workspace that also holds the split form of the passes (all but
+ * the dQ pass that forms a forward's statistics): the four planes above, then
+ * partial results of up to 16 pieces per row (max(D, 4) fp32 per query row for
+ * the row-statistics and dQ passes, 2 D + 8 for the fused bf16 statistics + dQ
+ * pass, 2 D per key row for dK / dV).  With
  * workspace_bytes >= this size the library cuts a pass's streamed axis (keys
  * for the query-major passes, queries for dK / dV) into pieces of whole chunks
  * (at least four each) when its workgroups would leave most compute units
