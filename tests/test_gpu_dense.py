@@ -144,6 +144,26 @@ def test_bf16_split_form_against_oracle_and_direct_form(case):
     _rerun_bitwise(split, q, k, v, dy, workspace="split", **kw)
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_split_form_fully_masked_rows(dtype):
+    """Key padding that hides every key of batch 1 (its rows see nothing: every
+    piece's partial is empty, the merge must give m = -inf, l = 0, delta = 0
+    and zero dQ rows) and most keys of batch 0 (pieces past the valid keys are
+    empty), in the split form, against the oracle."""
+    B, H, Sq, Sk, D = 2, 2, 100, 2000, 64
+    q, k, v, dy, _ = sdpa_inputs.dense_inputs(B, Sq, Sk, H, D, seed=82, dtype=dtype)
+    valid = torch.ones(B, Sk)
+    valid[0, 300:] = 0.0
+    valid[1, :] = 0.0
+    mask = valid.reshape(B, 1, 1, Sk)
+    kw = dict(mask_kind="keypad", mask=mask)
+    split = gpu_run(q, k, v, dy, workspace="split", **kw)
+    ref = oracle_run(q, k, v, dy, **kw)
+    print("fully masked", dtype, assert_parity(split, ref, dtype, label="fully masked split"))
+    assert np.all(split["dq"][1] == 0) and np.all(split["dk"][1] == 0) and np.all(split["dv"][1] == 0)
+    assert np.all(np.isneginf(split["m"].reshape(B, H, Sq)[1]))
+
+
 def test_bf16_kv_split_through_the_stage_calls():
     """bf16: the fused statistics + dQ pass (never split), then the dK / dV pass
     in split form (64-row query chunks) with a split-sized workspace, against
