@@ -218,7 +218,8 @@ int attn_bwd_paged_plan_build(int32_t nseq, const int32_t *seq_lens, const int32
 typedef struct attn_bwd_paged_args {
   int32_t dtype;      /* ATTN_F32 or ATTN_BF16: q, dy, pools and gradient pools */
   int32_t need;       /* bit 0: dK, bit 1: dV (at least one); latent variant: see below */
-  int32_t heads, kv_heads, head_dim, page_size, causal; /* head_dim in {32, 64, 128}; causal 0 / 1 */
+  int32_t heads, kv_heads, head_dim, page_size, causal; /* head_dim in {32, 64, 128} (latent
+                                                           variant: see below); causal 0 / 1 */
   int32_t nq, pool_pages;                /* must match the plan */
   float scale;                           /* 2^-64 <= |scale| <= 2^64 */
   const void *q, *dy;                    /* device [nq, heads, head_dim], contiguous */
