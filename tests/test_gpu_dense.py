@@ -164,6 +164,40 @@ def test_split_form_fully_masked_rows(dtype):
     assert np.all(np.isneginf(split["m"].reshape(B, H, Sq)[1]))
 
 
+def _random_case(seed):
+    """A seeded random dense case: shape, head size, dtype and mask."""
+    r = np.random.default_rng(seed)
+    B, H = int(r.integers(1, 3)), int(r.integers(1, 5))
+    Sq, Sk = int(r.integers(1, 400)), int(r.integers(1, 3000))
+    D = int(r.choice([32, 64, 128]))
+    dtype = torch.bfloat16 if r.integers(0, 2) else torch.float32
+    kind = str(r.choice(["none", "causal", "window", "keypad", "bias"]))
+    return dict(B=B, H=H, Sq=Sq, Sk=Sk, D=D, dtype=dtype, kind=kind,
+                window=int(r.integers(0, 600)) if kind == "window" else 0,
+                causal=bool(r.integers(0, 2)) if kind in ("keypad", "bias") else False)
+
+
+@pytest.mark.parametrize("seed", range(900, 912))
+def test_random_shapes_with_split_workspace(seed):
+    """Seeded random shapes, head sizes, types and masks, each with a
+    split-sized workspace (the split forms where the grid is small, the
+    one-workgroup-per-block forms elsewhere), against the oracle."""
+    c = _random_case(seed)
+    print(f"[random] seed {seed}: {c}", flush=True)
+    q, k, v, dy, g = sdpa_inputs.dense_inputs(c["B"], c["Sq"], c["Sk"], c["H"], c["D"], seed=seed,
+                                              dtype=c["dtype"])
+    mask = None
+    if c["kind"] == "keypad":
+        mask, _ = sdpa_inputs.keypad_valid(g, c["B"], c["Sk"], c["Sk"] // 3)
+        mask = mask.reshape(c["B"], 1, 1, c["Sk"])
+    elif c["kind"] == "bias":
+        mask = sdpa_inputs.bias_normal(g, c["B"], c["H"], c["Sq"], c["Sk"])
+    kw = dict(mask_kind=c["kind"], causal=c["causal"], window=c["window"], mask=mask)
+    res = gpu_run(q, k, v, dy, workspace="split", **kw)
+    ref = oracle_run(q, k, v, dy, nthreads=ORACLE_THREADS, **kw)
+    print(seed, assert_parity(res, ref, c["dtype"], label=f"random {seed}"))
+
+
 def test_bf16_kv_split_through_the_stage_calls():
     """bf16: the fused statistics + dQ pass (never split), then the dK / dV pass
     in split form (64-row query chunks) with a split-sized workspace, against
