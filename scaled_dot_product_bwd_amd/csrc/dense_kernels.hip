@@ -870,15 +870,17 @@ template <typename T, int D> struct SdState {
   int b, h, lane, half, c_last;
 };
 
-// Chunk c (keys 64 c .. 64 c + 63), whose tiles are in buffer bc; chunk
-// min(c + 2, c_last) goes to the buffer chunk c - 1 used, one load per
-// phase-A step (past the end the last chunk is loaded again: never read,
-// drained at the end).
-template <typename T, int D, int MODE, bool MASKED>
+// Chunk c (keys 64 c .. 64 c + 63), whose tiles are in buffer bc of four;
+// chunk min(c + 2, c_last) goes to buffer bc + 2 (chunk c - 2's, whose phase C
+// ran in step c - 1), one load per S step (past the end the last chunk is
+// loaded again: never read, drained at the end).  With PREV, chunk c - 1's
+// middle and phase C run in this step too (its K tile in buffer bc - 1).
+template <typename T, int D, int MODE, bool MASKED, bool PREV>
 __device__ __forceinline__ void sd_step(const DenseParams &p, SdState<T, D> &S, int c, int bc,
-                                        Tile<T, D, kSdKeys> *Ks, Tile<T, D, kSdKeys> *Vs) {
+                                        Tile<T, D, kSdKeys> *Ks, Tile<T, D, kSdKeys> *Vs,
+                                        SdCarry<T> &X) {
   constexpr int KC = kSdKeys, L = ChunkIO<T, D, KC>::LOADS;
-  const int bn = bc == 0 ? 2 : bc - 1;
+  const int bn = (bc + 2) & 3, bp = (bc + 3) & 3;
   const int half = S.half, j0 = c * KC;
   const int cn = min(c + 2, S.c_last);
   const T *kn = S.kbase + (int64_t)cn * KC * p.ks[1];
@@ -896,7 +898,7 @@ __device__ __forceinline__ void sd_step(const DenseParams &p, SdState<T, D> &S, 
   auto adj_of = [&](int u, int r) {
     return q_adj<MODE>(p, S.b, S.h, S.qi, j0 + 32 * u + kr(r, half), S.ks);
   };
-  sd_body<T, D, MASKED>(S, p.scale_log2, &Ks[bc], &Vs[bc], adj_of, dma);
+  sd_body_deferred<T, D, MASKED, PREV>(S, p.scale_log2, &Ks[bc], &Vs[bc], &Ks[bp], X, adj_of, dma);
 }
 
 
@@ -906,7 +908,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int KS = M::KS, KL = M::KL, NSD = D / KS, NT = D / 32, QROWS = 128, KC = kSdKeys;
   static_assert(sizeof(T) == 2, "bf16 only (direct-to-LDS chunk loads)");
   static_assert(QShape<T>::QROWS == QROWS, "one 32-query block per wave");
-  __shared__ Tile<T, D, KC> Ks[3], Vs[3];
+  __shared__ Tile<T, D, KC> Ks[4], Vs[4];
 
   SdState<T, D> S;
   const int tid = threadIdx.x, w = tid >> 6;
@@ -968,12 +970,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   int c = Pc.lo, bc = 0;
   auto next = [&]() {
     ++c;
-    bc = bc == 2 ? 0 : bc + 1;
+    bc = (bc + 1) & 3;
   };
-  for (; c < cu0 && c <= Pc.hi; next()) sd_step<T, D, MODE, true>(p, S, c, bc, Ks, Vs);
-  if constexpr (MODE == MODE_INDEX)
-    for (; c <= cu1; next()) sd_step<T, D, MODE, false>(p, S, c, bc, Ks, Vs);
-  for (; c <= Pc.hi; next()) sd_step<T, D, MODE, true>(p, S, c, bc, Ks, Vs);
+  SdCarry<T> X;
+  if (c <= Pc.hi) {  // the first chunk has no pending one
+    if (MODE == MODE_INDEX && c >= cu0 && c <= cu1)
+      sd_step<T, D, MODE, false, false>(p, S, c, bc, Ks, Vs, X);
+    else
+      sd_step<T, D, MODE, true, false>(p, S, c, bc, Ks, Vs, X);
+    next();
+    for (; c < cu0 && c <= Pc.hi; next()) sd_step<T, D, MODE, true, true>(p, S, c, bc, Ks, Vs, X);
+    if constexpr (MODE == MODE_INDEX)
+      for (; c <= cu1; next()) sd_step<T, D, MODE, false, true>(p, S, c, bc, Ks, Vs, X);
+    for (; c <= Pc.hi; next()) sd_step<T, D, MODE, true, true>(p, S, c, bc, Ks, Vs, X);
+    sd_finish<T, D>(S, &Ks[(bc + 3) & 3], X);  // the last chunk's phase C
+  }
   wait_vmem();  // the repeated loads of the last steps land before the workgroup ends
 
   if constexpr (SPLIT) {

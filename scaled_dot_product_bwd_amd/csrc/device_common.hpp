@@ -446,6 +446,7 @@ __device__ __forceinline__ int fresh(int x) {
 // formed before this point and the optimiser cannot sink its computation into
 // a later block (past a branch that follows it), where nothing would hide it.
 __device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(bf16x8 &x) { asm volatile("" : "+v"(x)); }
 
 
 // Workgroup id -> logical tile id.  The hardware hands workgroup i to XCD i % 8;
