@@ -377,25 +377,29 @@ __device__ __forceinline__ void psd_slots(const PsdState<D> &S, int x, const int
   }
 }
 
-// Chunk c (tokens 64 c ..), tiles in buffer bc; chunk c + 2 into the buffer
-// chunk c - 1 used (past c_last the last chunk again), slot ids of chunk c + 3.
-template <int D, bool MASKED>
-__device__ __forceinline__ void psd_step(const PagedParams &p, PsdState<D> &S, int c, int bc,
+// Chunk c (tokens 64 c ..), its K tile in buffer bk of four and its V tile in
+// buffer bv of three; chunk c + 2 into K buffer bk + 2 (chunk c - 2's, whose
+// phase C ran in step c - 1) and the V buffer chunk c - 1 used (past c_last
+// the last chunk again), slot ids of chunk c + 3.  With PREV, chunk c - 1's
+// middle and phase C run here too (its K tile in buffer bk - 1).
+template <int D, bool MASKED, bool PREV>
+__device__ __forceinline__ void psd_step(const PagedParams &p, PsdState<D> &S, int c, int bk, int bv,
                                          Tile<bf16, D, kSdKeys> *Ks, Tile<bf16, D, kSdKeys> *Vs,
-                                         int (*ri)[kPqRi]) {
+                                         int (*ri)[kPqRi], SdCarry<bf16> &X) {
   constexpr int L = ChunkIO<bf16, D, kSdKeys>::LOADS;
-  const int bn = bc == 0 ? 2 : bc - 1;
+  const int kn = (bk + 2) & 3, vn = bv == 0 ? 2 : bv - 1;
   psd_rowinfo(S, c + 3, ri);
   int sl[L];
   psd_slots(S, c + 2, ri, sl);
   constexpr unsigned TB = sizeof(Tile<bf16, D, kSdKeys>);
-  const unsigned klds = lds_addr(Ks) + bn * TB, vlds = lds_addr(Vs) + bn * TB;
+  const unsigned klds = lds_addr(Ks) + kn * TB, vlds = lds_addr(Vs) + vn * TB;
   auto dma = [&](int k) { psd_load(S, k, sl, klds, vlds); };
   const int half = S.half, t0 = c * kSdKeys;
   auto adj_of = [&](int u, int r) {
     return t0 + 32 * u + kr(r, half) > S.hi ? -INFINITY : 0.f;
   };
-  sd_body<bf16, D, MASKED>(S, p.scale_log2, &Ks[bc], &Vs[bc], adj_of, dma);
+  sd_body_deferred<bf16, D, MASKED, PREV>(S, p.scale_log2, &Ks[bk], &Vs[bv], &Ks[(bk + 3) & 3], X,
+                                          adj_of, dma);
 }
 
 template <int D, bool SPLIT>
@@ -403,7 +407,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   typedef bf16 T;
   typedef MT<T> M;
   constexpr int KS = M::KS, KL = M::KL, NSD = D / KS, NT = D / 32, KC = kSdKeys;
-  __shared__ Tile<T, D, KC> Ks[3], Vs[3];
+  __shared__ Tile<T, D, KC> Ks[4], Vs[3];
   __shared__ __attribute__((aligned(16))) int ri[2][kPqRi];
 
   PsdState<D> S;
@@ -472,13 +476,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     __syncthreads();
     int cu = min(tfull / KC, S.c_last + 1);  // chunks [c0, cu) unmasked
     if (!(p.scale_log2 > 0.f)) cu = c0;
-    int c = c0, bc = 0;
+    int c = c0, bk = 0, bv = 0;
     auto next = [&]() {
       ++c;
-      bc = bc == 2 ? 0 : bc + 1;
+      bk = (bk + 1) & 3;
+      bv = bv == 2 ? 0 : bv + 1;
     };
-    for (; c < cu; next()) psd_step<D, false>(p, S, c, bc, Ks, Vs, ri);
-    for (; c <= S.c_last; next()) psd_step<D, true>(p, S, c, bc, Ks, Vs, ri);
+    SdCarry<T> X;
+    if (c < cu)  // the first chunk has no pending one
+      psd_step<D, false, false>(p, S, c, bk, bv, Ks, Vs, ri, X);
+    else
+      psd_step<D, true, false>(p, S, c, bk, bv, Ks, Vs, ri, X);
+    next();
+    for (; c < cu; next()) psd_step<D, false, true>(p, S, c, bk, bv, Ks, Vs, ri, X);
+    for (; c <= S.c_last; next()) psd_step<D, true, true>(p, S, c, bk, bv, Ks, Vs, ri, X);
+    sd_finish<T, D>(S, &Ks[(bk + 3) & 3], X);  // the last chunk's phase C
     wait_vmem();  // the repeated loads of the last steps land before the workgroup ends
   }
 

@@ -53,187 +53,26 @@ template <int NT, typename St> __device__ __forceinline__ void sd_settle(St &S, 
     for (int r = 0; r < 16; ++r) S.acc_a[t][r] = fmaf(shift, S.acc_b[t][r], S.acc_a[t][r]);
 }
 
-// One chunk, whose tiles are Kc / Vc (LDS).  MASKED is fixed per loop by the
-// caller (no branch inside the step: a branch would split the step into blocks
-// and let the compiler move the exponentials out of the phase-A steps that
-// hide them); the unmasked step is for chunks whose every (row, key) pair is
-// visible, with cl > 0.  cl = scale log2 e; adj_of(u, r): the mask term (log2
-// domain: 0, -inf or a bias) of element r of sub-tile u (MASKED only);
-// dma(k), k < 2 LOADS: the caller's k-th direct-to-LDS load of a later chunk,
-// one per phase-A step.  The step ends by waiting for every vector-memory
-// operation but the 2 LOADS issued in it, then a barrier.
-//   Phase A: the S^T chains of both sub-tiles, then their dP^T chains (sub-tile
-//     0's, then sub-tile 1's) with the statistics in the steps: the max and
-//     the exponentials of S (one reference update per 64 keys, the
-//     row-statistics arithmetic over 32 scores per lane), their sum, the
-//     packed p~, and sub-tile 0's part of sum p~ dP.
-//   Then: the rest of the sums, the rescale (rare, wave-uniform), delta's new
-//     estimate dh, the packed operand p~ (dP - dh).
-//   Phase C: per tile t, A' += (dh_old - dh) B just before its first product
-//     (so each tile's shift overlaps the previous tile's MFMAs); then B and A'
+// ---------------------------------------------------------------------------
+// The chunk step.  Per 64-key chunk (two 32-key sub-tiles u) the arithmetic is
+//   S^T and dP^T chains (Q / dY fragments in registers, K / V from LDS);
+//   the statistics: the max and the reference update, the exponentials p~ and
+//     their sum, sum p~ dP, l and dl, the new estimate dh of delta;
+//   p~ and p~ (dP - dh) packed to bf16 for phase C;
+//   phase C: per tile t, A' += (dh_old - dh) B just before its first product
+//     (so each tile's shift overlaps the previous tile's MFMAs), then B and A'
 //     accumulate over the chunk's four 16-key steps, one transposed K fragment
 //     per pair of products.
-template <typename T, int D, bool MASKED, typename St, typename Adj, typename Dma>
-__device__ __forceinline__ void sd_body(St &S, float cl, const Tile<T, D, kSdKeys> *Kc,
-                                        const Tile<T, D, kSdKeys> *Vc, Adj adj_of, Dma dma) {
-  typedef MT<T> M;
-  typedef typename M::frag F;
-  constexpr int NT = D / 32, CS = M::CSTEPS, NSD = D / M::KS, RING = kSdRing;
-  constexpr int KC = kSdKeys, NU = KC / 32, L = ChunkIO<T, D, KC>::LOADS;
-  constexpr int NA = 2 * NU * NSD;  // phase-A steps (S, then dP)
-  static_assert(2 * L <= NA, "one load per phase-A step");
-  constexpr bool plain = !MASKED;
-  const int l32 = S.lane & 31, half = S.half;
-
-  // Phase A: the S chains of both sub-tiles interleaved (u = i % NU), then the
-  // dP chains one sub-tile after the other (sub-tile 0's completes halfway).
-  F fr[RING];
-  auto load = [&](int i) {  // step i < NA / 2: K of sub-tile i % NU, else V
-    const int half_a = NA / 2, ii = i < half_a ? i : i - half_a;
-    const int u = i < half_a ? ii % NU : ii / NSD, s = i < half_a ? ii / NU : ii % NSD;
-    fr[i % RING] = i < half_a ? Kc->frag(32 * u + l32, s, half) : Vc->frag(32 * u + l32, s, half);
-  };
-#pragma unroll
-  for (int i = 0; i < RING - 1; ++i) load(i);
-  f32x16 sacc[NU], pacc[NU];
-#pragma unroll
-  for (int u = 0; u < NU; ++u) sacc[u] = pacc[u] = f32x16{};
-  float s2[NU][16], pr[NU][16], mx = 0.f, mu = 0.f, al = 1.f, ls = 0.f, ds = 0.f;
-  bool moved = false;
-  F uf[NU][CS], pf[NU][CS];
-  // The statistics spread over the dP steps, part k:
-  //   k < NU: sub-tile k's scores and running max;  k = NU: the reference;
-  //   then the exponentials four at a time (their sum l as they come);
-  //   then each sub-tile's p~ packed for phase C;
-  //   then sum p~ dP over sub-tile 0 (its dP chain is done by then), in
-  //   three pieces.  Every sum runs in the order of the plain loop.
-  constexpr int KX = NU + 1, KP = KX + 4 * NU, KD = KP + NU, NPART = KD + 3;
-  auto stat_part = [&](int k) {
-    if (k < NU) {  // sub-tile k's scores and running max
-      const int u = k;
-      if constexpr (plain) {
-        if (u == 0) mx = sacc[0][0];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[u][r]);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s2[u][r] = fmaf(sacc[u][r], cl, adj_of(u, r));
-        if (u == 0) mx = s2[0][0];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s2[u][r]);
-      }
-    } else if (k == NU) {
-      mx = halves_max(mx);
-      if constexpr (plain) mx *= cl;
-      al = row_stat_ref(S.st, mx, moved, mu);
-    } else if (k < KP) {  // exponentials, four at a time, and their sum
-      const int q = k - KX, u = q / 4, r0 = 4 * (q % 4);
-#pragma unroll
-      for (int r = r0; r < r0 + 4; ++r) {
-        if constexpr (plain)
-          pr[u][r] = fast_exp2(fmaf(sacc[u][r], cl, -mu));
-        else
-          pr[u][r] = fast_exp2(s2[u][r] - mu);
-        ls += pr[u][r];
-      }
-      pin(ls);
-    } else if (k < KD) {  // sub-tile k - KP's p~ for phase C
-      const int u = k - KP;
-#pragma unroll
-      for (int st = 0; st < CS; ++st) pf[u][st] = creuse<T>(pr[u], st);
-    } else {  // sum p~ dP, sub-tile 0, piece k - KD
-      const int r0 = (k - KD) * 16 / 3, r1 = (k - KD + 1) * 16 / 3;
-#pragma unroll
-      for (int r = r0; r < r1; ++r) ds = fmaf(pr[0][r], pacc[0][r], ds);
-      pin(ds);
-    }
-  };
-#pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    sched_fence();
-    if (i + RING - 1 < NA) load(i + RING - 1);
-    if (i < 2 * L) dma(i);
-    if (i < NA / 2) {
-      const int u = i % NU, s = i / NU;
-      sacc[u] = M::mma(fr[i % RING], S.qf[s], sacc[u]);
-    } else {
-      const int ii = i - NA / 2, u = ii / NSD, s = ii % NSD;
-      pacc[u] = M::mma(fr[i % RING], S.gf[s], pacc[u]);
-#pragma unroll
-      for (int k = ii * NPART / (NA / 2); k < (ii + 1) * NPART / (NA / 2); ++k) stat_part(k);
-    }
-  }
-  sched_fence();
-  {
-#pragma unroll
-    for (int u = 1; u < NU; ++u)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) ds = fmaf(pr[u][r], pacc[u][r], ds);
-    S.st.l = fmaf(S.st.l, al, ls);
-    S.st.dl = fmaf(S.st.dl, al, ds);
-  }
-  if (__any(moved)) {  // rare after the first visible chunk: wave-uniform branch
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      S.acc_a[t] *= al;
-      S.acc_b[t] *= al;
-    }
-  }
-  // delta's running estimate, this chunk included, through the hardware
-  // reciprocal (l_tot >= 1 once a key is visible: the row's max term is
-  // 2^(mtrue - mref) >= 1).  The epilogue moves A' to delta itself.
-  const float l_tot = halves_sum(S.st.l);
-  const float dl_tot = halves_sum(S.st.dl);
-  const float dh = l_tot > 0.f ? dl_tot * __builtin_amdgcn_rcpf(l_tot) : 0.f;
-  const float shift = S.dh - dh;
-  S.dh = dh;
-#pragma unroll
-  for (int u = 0; u < NU; ++u)
-#pragma unroll
-    for (int st = 0; st < CS; ++st) {
-      float pd[16 / CS];
-#pragma unroll
-      for (int e = 0; e < 16 / CS; ++e)
-        pd[e] = pr[u][st * (16 / CS) + e] * (pacc[u][st * (16 / CS) + e] - dh);
-      uf[u][st] = creuse<T>(pd, 0);
-    }
-
-  constexpr int NC = NU * CS * NT;
-  F kt[RING];
-  auto loadc = [&](int k) {
-    const int t = k % NT, st = (k / NT) % CS, u = k / (NT * CS);
-    kt[k % RING] = Kc->tfrag(32 * t, st, S.lane, 32 * u);
-  };
-#pragma unroll
-  for (int k = 0; k < RING - 1 && k < NC; ++k) loadc(k);
-#pragma unroll
-  for (int k = 0; k < NC; ++k) {
-    const int t = k % NT, st = (k / NT) % CS, u = k / (NT * CS);
-    sched_fence();
-    if (k + RING - 1 < NC) loadc(k + RING - 1);
-    if (k < NT) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) S.acc_a[t][r] = fmaf(shift, S.acc_b[t][r], S.acc_a[t][r]);
-    }
-    S.acc_b[t] = M::mma(kt[k % RING], pf[u][st], S.acc_b[t]);
-    S.acc_a[t] = M::mma(kt[k % RING], uf[u][st], S.acc_a[t]);
-  }
-  sched_fence();
-  wait_vmem_le<2 * L>();  // the chunk requested a step ago has landed
-  __syncthreads();
-}
-
-// ---------------------------------------------------------------------------
-// The deferred form of the same step (dense kernel), which evens out the
-// VALU work over the step's MFMAs.  Step c runs
+// At one wave per SIMD only the wave's own instruction order overlaps VALU work
+// with MFMAs, so the step is deferred: step c runs
 //   chunk c's S chains, with chunk c - 1's middle (the rest of its sums, dh,
 //     its packed p~ (dP - dh)) in their shadows;
 //   chunk c - 1's phase C, with chunk c's statistics that need only S (the
 //     max, the reference, the exponentials and their sum, the packed p~);
 //   chunk c's dP chains, with its sum p~ dP over sub-tile 0.
-// Every row sees the same operations in the same order as in sd_body, so the
-// results are the same bits.  The caller keeps chunk c's K tile until step
-// c + 1 has run (four K buffers) and finishes the last chunk with sd_finish.
+// Every row sees the same operations in the same order as a step that runs
+// chunk c alone.  The caller keeps chunk c's K tile until step c + 1 has run
+// (four K buffers; V needs three) and finishes the last chunk with sd_finish.
 // What a step hands to the next:
 template <typename T> struct SdCarry {
   static constexpr int NU = kSdKeys / 32, CS = MT<T>::CSTEPS;
@@ -327,9 +166,16 @@ __device__ __forceinline__ void sd_phase_c(St &S, const Tile<T, D, kSdKeys> *Kp,
 }
 template <typename T, int D> constexpr int sd_ncsteps() { return (kSdKeys / 32) * MT<T>::CSTEPS * (D / 32); }
 
-// Chunk c (tiles Kc / Vc); with PREV, chunk c - 1's middle and phase C (its K
-// tile Kp, its carry X) run here too.  adj_of and dma as for sd_body.  X
-// leaves with chunk c's carry.
+// Chunk c (tiles Kc / Vc in LDS); with PREV, chunk c - 1's middle and phase C
+// (its K tile Kp, its carry X) run here too; X leaves with chunk c's carry.
+// MASKED is fixed per loop by the caller (a branch inside the step would split
+// it into blocks and let the compiler move work out of the MFMA shadows it was
+// placed in); the unmasked step is for chunks whose every (row, key) pair is
+// visible, with cl > 0.  cl = scale log2 e; adj_of(u, r): the mask term (log2
+// domain: 0, -inf or a bias) of element r of sub-tile u (MASKED only);
+// dma(k), k < 2 LOADS: the caller's k-th direct-to-LDS load of a later chunk,
+// one per S step.  The step ends by waiting for every vector-memory operation
+// but the 2 LOADS issued in it, then a barrier.
 template <typename T, int D, bool MASKED, bool PREV, typename St, typename Adj, typename Dma>
 __device__ __forceinline__ void sd_body_deferred(St &S, float cl, const Tile<T, D, kSdKeys> *Kc,
                                                  const Tile<T, D, kSdKeys> *Vc,
