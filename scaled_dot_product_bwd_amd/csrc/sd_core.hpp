@@ -30,7 +30,7 @@
 
 namespace attn {
 
-constexpr int kSdRing = 4;  // fragment ring of the fused pass (reads RING - 1 steps ahead)
+constexpr int kSdRing = 3;  // fragment ring of the fused pass (reads RING - 1 steps ahead)
 constexpr int kSdKeys = 64;  // keys per chunk: two 32-key sub-tiles per statistics update
 
 // A wave's state, as a struct with these members (each kernel adds its own):
