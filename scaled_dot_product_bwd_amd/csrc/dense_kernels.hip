@@ -242,7 +242,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   // split form: consecutive workgroups are the pieces of one (block, head)
   const int np = SPLIT ? p.npiece : 1;
   tile_order<kRsGroup>(blockIdx.x / np, gridDim.x / np, nb, bh, rank);
-  const int blk = nb - 1 - rank;  // the heaviest causal blocks first
+  // the heaviest causal blocks first; under a narrow band the short first ones
+  const int blk = narrow_band(p) ? rank : nb - 1 - rank;
   S.h = bh % p.H;
   S.b = bh / p.H;
   const int b = S.b, h = S.h;
@@ -556,6 +557,7 @@ __global__ __launch_bounds__(256) void k_kv_bwd(const DenseParams p) {
   // split form: consecutive workgroups are the query pieces of one key block
   const int np = SPLIT ? p.npiece : 1;
   tile_order<kKvGroup>(blockIdx.x / np, gridDim.x / np, nb, bg, blk);
+  if (narrow_band(p)) blk = nb - 1 - blk;  // the short last key blocks first
   const int g = bg % p.Hkv;  // the K / V head; its query heads are g * G ... g * G + G - 1
   S.b = bg / p.Hkv;
   S.h0 = g * p.G;
@@ -738,7 +740,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // the pieces of one (block, head)
   const int np = SPLIT ? p.npiece : 1;
   tile_order<kDqGroup>(blockIdx.x / np, gridDim.x / np, nb, bh, rank);
-  const int blk = nb - 1 - rank;
+  const int blk = narrow_band(p) ? rank : nb - 1 - rank;  // as in the statistics kernel
   S.h = bh % p.H;
   S.b = bh / p.H;
   const int b = S.b, h = S.h;
@@ -919,7 +921,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   int bh, rank;
   const int np = SPLIT ? p.npiece : 1;  // split form: consecutive workgroups are one block's pieces
   tile_order<kDqGroup>(blockIdx.x / np, gridDim.x / np, nb, bh, rank);
-  const int blk = nb - 1 - rank;  // the heaviest causal blocks first
+  // the heaviest causal blocks first; under a narrow band the short first ones
+  const int blk = narrow_band(p) ? rank : nb - 1 - rank;
   S.h = bh % p.H;
   S.b = bh / p.H;
   const int b = S.b, h = S.h;

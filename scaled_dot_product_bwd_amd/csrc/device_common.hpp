@@ -487,6 +487,17 @@ __device__ __forceinline__ void tile_order(int bid, int n, int nb, int &head, in
   tile_of_logical<GS>(xcd_remap(bid, n), n, nb, head, rank);
 }
 
+// A narrow band: a window rule whose visible span (hi_off - lo_off + 1 index
+// differences) is at most a quarter of the shorter sequence.  Then every block
+// but the few at the band's clipped end sees the same number of chunks, and
+// the heavy-first order starts every CU on an equal block: all of them load
+// their first operands and store their results at the same moments, round
+// after round.  Starting with the short end blocks puts part of each XCD's
+// CUs ahead of the rest for the whole kernel (the total work is unchanged).
+__device__ __forceinline__ bool narrow_band(const DenseParams &p) {
+  return p.lo_off > -kBig && 4 * ((int64_t)p.hi_off - p.lo_off + 1) <= (int64_t)min(p.Sq, p.Sk);
+}
+
 // Store 4 consecutive fp32 values as T.
 template <typename T> __device__ __forceinline__ void store4(T *dst, float a, float b, float c, float d);
 template <> __device__ __forceinline__ void store4<bf16>(bf16 *dst, float a, float b, float c, float d) {
