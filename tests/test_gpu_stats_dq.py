@@ -53,6 +53,22 @@ def test_peaked_rows(qscale, S, D):
         print(qscale, S, mask, assert_parity(res, ref, BF, label=f"peaked x{qscale} {mask} S={S}"))
 
 
+@pytest.mark.parametrize("Sk", [40, 64, 100, 192, 256, 300, 384])
+@pytest.mark.parametrize("mask", ["none", "causal", "window"])
+def test_chunk_counts(mask, Sk):
+    """Row blocks over one to six 64-key chunks.  Each chunk's phase C runs in
+    the next chunk's step, so this covers a block's first chunk (nothing
+    pending), the rotation of four K buffers, and the last chunk's phase C
+    after the loop, with the first chunk masked (window, ragged key end) or
+    not (no mask, causal with the query rows at the end of the keys)."""
+    B, H, Sq, D = 1, 2, 200, 64
+    q, k, v, dy, _ = sdpa_inputs.dense_inputs(B, Sq, Sk, H, D, seed=300 + Sk, dtype=BF)
+    window = 70 if mask == "window" else 0
+    res = gpu_run(q, k, v, dy, mask_kind=mask, window=window)
+    ref = oracle_run(q, k, v, dy, mask_kind=mask, window=window, nthreads=2)
+    print(mask, Sk, assert_parity(res, ref, BF, label=f"{mask} Sk={Sk}"))
+
+
 @pytest.mark.parametrize("mask,window", [("window", 40), ("keypad", 0), ("bias", 0)])
 def test_masks_bf16(mask, window):
     B, H, Sq, Sk, D = 2, 2, 150, 290, 128
