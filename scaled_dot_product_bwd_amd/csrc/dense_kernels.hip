@@ -920,9 +920,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int nb = p.nblk;
   int bh, rank;
   const int np = SPLIT ? p.npiece : 1;  // split form: consecutive workgroups are one block's pieces
-  tile_order<kDqGroup>(blockIdx.x / np, gridDim.x / np, nb, bh, rank);
-  // the heaviest causal blocks first; under a narrow band the short first ones
-  const int blk = narrow_band(p) ? rank : nb - 1 - rank;
+  // the heaviest causal blocks first; under a narrow band the short first ones,
+  // in groups of 8 heads (window-256: 76.8 -> 74.4 us against groups of
+  // kDqGroup, with which the causal workload runs 1.5 us faster)
+  const bool band = narrow_band(p);
+  if (band)
+    tile_order<8>(blockIdx.x / np, gridDim.x / np, nb, bh, rank);
+  else
+    tile_order<kDqGroup>(blockIdx.x / np, gridDim.x / np, nb, bh, rank);
+  const int blk = band ? rank : nb - 1 - rank;
   S.h = bh % p.H;
   S.b = bh / p.H;
   const int b = S.b, h = S.h;
